@@ -1,0 +1,229 @@
+/*
+ * spa.h -- C ABI of the sparse paged decode-attention library (libspa.so),
+ * written for AMD Instinct MI355X (gfx950).
+ *
+ * The library implements one decode step of LServe-style unified sparse
+ * attention over a hierarchical paged KV cache:
+ *   - streaming heads attend to the first `sink` tokens plus the last `window`
+ *     tokens (LServe write-up, bqwf.cn, "2.1 混合稀疏注意力机制", static
+ *     sparsity; the sink + local-window pattern is the StreamingLLM row of the
+ *     sparse-method table in the long-context survey, xllm-io.github.io,
+ *     "2.2" / sparse attention methods);
+ *   - dynamic heads score every logical page from its per-channel min/max key
+ *     summary, keep the best pages under a token budget, reuse that choice for
+ *     several decode steps and attend only to the chosen pages (LServe
+ *     write-up, "2.1" dynamic sparsity, and "3.2 解码阶段加速", reusable page
+ *     selector and dynamic budget);
+ *   - the KV cache lives in a pool of large physical pages, each holding
+ *     several small logical pages; a per-sequence page table maps logical
+ *     positions to physical pages (LServe write-up, "2.2 分层分页KV缓存").
+ *
+ * Conventions shared by every call
+ *   - All device pointers are owned by the caller. The library never
+ *     allocates, frees or synchronises device memory; every call only
+ *     enqueues kernels on `stream` and returns.
+ *   - Argument errors are found on the host, before anything is enqueued;
+ *     the call then returns a non-zero spa_status and spa_last_error() holds
+ *     a message (thread-local). A failed kernel launch returns SPA_ERR_HIP.
+ *   - bf16 tensors are IEEE bfloat16 bit patterns (uint16). Inputs must be
+ *     finite.
+ *   - Positions: sequence b holds tokens 0 .. L_b-1, where L_b = seq_lens[b]
+ *     counts the token appended in the current step. Token t of sequence b
+ *     lives in physical page page_table[b][t / P] at slot t % P.
+ *   - Query head i reads KV head i / G with G = H_q / H_kv (grouped-query
+ *     attention, long-context survey "2.3 分组查询注意力 (GQA)"; G = H_q is
+ *     multi-query attention, "2.4").
+ *   - Kernels never read or write outside the buffers described here, even
+ *     for bad device-side values: page ids outside [0, N) are skipped,
+ *     seq_lens are clamped to [0, max_pages * P], selected page ids outside
+ *     the sequence are skipped. Results for such inputs are unspecified.
+ *
+ * Pool layout in HBM (the method fixes only that logical pages sit inside
+ * physical pages; the in-page order is ours):
+ *   k_pool   bf16 [N][H_kv][P][D]        token-major: one logical page of one
+ *                                        head is p*D*2 contiguous bytes
+ *   v_pool   bf16 [N][H_kv][P/p][D][p]   channel-major inside each logical
+ *                                        page (the page is transposed), also
+ *                                        p*D*2 contiguous bytes
+ *   summary  bf16 [N][H_kv][P/p][2][D]   per logical page: [0] = channel-wise
+ *                                        minimum of its keys, [1] = maximum
+ */
+#ifndef SPA_H
+#define SPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum spa_status {
+  SPA_OK = 0,
+  SPA_ERR_INVALID = 1,        /* bad argument: null pointer, size out of range, shapes that disagree */
+  SPA_ERR_UNSUPPORTED = 2,    /* well-formed but not built: head_dim != 128, p not 16/32/64, G > 16 */
+  SPA_ERR_POOL_EXHAUSTED = 3, /* page allocator has fewer free pages than requested */
+  SPA_ERR_WORKSPACE = 4,      /* workspace missing or smaller than spa_workspace_bytes() */
+  SPA_ERR_HIP = 5             /* a HIP runtime call failed (kernel launch) */
+} spa_status;
+
+/* The physical-page pool of one attention layer. */
+typedef struct spa_pool {
+  int32_t num_kv_heads;   /* H_kv, 1..128 */
+  int32_t head_dim;       /* D, must be 128 */
+  int32_t logical_page;   /* p, tokens per logical page: 16, 32 or 64 (the write-up caps it at 64, "5.3") */
+  int32_t physical_page;  /* P, tokens per physical page: a multiple of p, P/p <= 64 */
+  int32_t num_phys_pages; /* N >= 1 */
+  void* k_pool;           /* device bf16 [N][H_kv][P][D] */
+  void* v_pool;           /* device bf16 [N][H_kv][P/p][D][p] */
+  void* summary;          /* device bf16 [N][H_kv][P/p][2][D]; may be NULL when no head is dynamic */
+} spa_pool;
+
+/* Which KV heads are streaming and which are dynamic, and the streaming
+ * pattern. The `kind` array is read on the host during the call only. */
+typedef struct spa_heads {
+  int32_t num_q_heads;    /* H_q: a multiple of H_kv with G = H_q / H_kv in {1, 2, 4, 8, 16} */
+  int32_t sink;           /* streaming heads attend tokens [0, min(sink, L)), sink >= 0 */
+  int32_t window;         /* ... and tokens [max(sink, L - window), L), window >= 1 */
+  const uint8_t* kind;    /* host [H_kv]: 0 = streaming head, 1 = dynamic head */
+} spa_heads;
+
+/* The decode batch: B sequences sharing one pool. */
+typedef struct spa_batch {
+  int32_t batch;              /* B >= 0; B == 0 makes every call a no-op */
+  int32_t max_pages;          /* columns of page_table (physical pages per sequence), >= 1 */
+  const int32_t* page_table;  /* device int32 [B][max_pages]: physical page ids in [0, N) */
+  const int32_t* seq_lens;    /* device int32 [B]: L_b, tokens in sequence b after this step's append */
+} spa_batch;
+
+/* ---- a1: append one token per sequence --------------------------------
+ * Writes the key and value of token L_b - 1 of every sequence b into its
+ * pool slot (physical page page_table[b][(L_b-1)/P], slot (L_b-1) % P).
+ *   k_new, v_new: device bf16 [B][H_kv][D], read only.
+ * Sequences with L_b < 1 are skipped. Summaries are not touched; call
+ * spa_page_summary_update afterwards for dynamic heads.
+ * LServe write-up "2.2 分层分页KV缓存" (pool of physical pages holding
+ * logical pages); paged store of the long-context survey "3.4 KV 缓存分页". */
+spa_status spa_kv_pool_append(const spa_pool* pool, const spa_batch* batch,
+                              const void* k_new, const void* v_new,
+                              hipStream_t stream);
+
+/* Bulk write of tokens [start, start + count) of ONE sequence (prefill).
+ *   page_table_row: device int32 [max_pages], that sequence's row;
+ *   k, v: device bf16 [H_kv][count][D] in logical (position) order.
+ * Requires 0 <= start, count >= 0, start + count <= max_pages * P. */
+spa_status spa_kv_pool_write(const spa_pool* pool, const int32_t* page_table_row,
+                             int32_t max_pages, int64_t start, int64_t count,
+                             const void* k, const void* v, hipStream_t stream);
+
+/* ---- a2: page summaries ------------------------------------------------
+ * For every dynamic KV head and every logical page j that overlaps positions
+ * [first_pos[b], L_b) of sequence b, recomputes the page's summary from the
+ * keys in the pool: channel-wise minimum and maximum over the page's valid
+ * tokens [j*p, min(j*p + p, L_b)). Min and max use IEEE totalOrder
+ * (-0 < +0), so the result is exact and independent of evaluation order.
+ * LServe write-up "2.1" (min-max pooling of each block's features).
+ *   first_pos: device int32 [B], or NULL meaning L_b - 1 (the decode case:
+ *              only the page holding the new token);
+ *   max_tokens: host bound, L_b - first_pos[b] <= max_tokens for every b
+ *              (1 when first_pos is NULL). Pages beyond the bound are not
+ *              refreshed. */
+spa_status spa_page_summary_update(const spa_pool* pool, const spa_heads* heads,
+                                   const spa_batch* batch, const int32_t* first_pos,
+                                   int32_t max_tokens, hipStream_t stream);
+
+/* ---- a3 + a4: page selection for dynamic heads --------------------------
+ * For sequence b and dynamic KV head h with query group g = 0..G-1, page j
+ * (0 <= j < n_b = ceil(L_b / p)) scores
+ *     s_j = max_g RN32( sum_c max(q[g][c] * kmax[j][c], q[g][c] * kmin[j][c]) ),
+ * the largest value q_g . k can take for any key inside the page's min/max
+ * box (LServe write-up "2.1": query-to-pooled-feature similarity; the
+ * upper-bound form is the Quest row of the long-context survey's sparse-method
+ * table). The sum is accumulated in fp64 from exact bf16 products and rounded
+ * once to fp32; no 1/sqrt(D) factor. Then
+ *     k_b = min(n_b, max(1, budget_tokens[b] / p), k_max)
+ * pages are kept: the first k_b in the order (score descending, page id
+ * ascending), written to sel_pages[b][h][0..k_b) in ascending page id, with
+ * sel_count[b][h] = k_b and sel_len[b] = L_b (the length the selection was
+ * made at). Rows of streaming heads are not written.
+ *   q:             device bf16 [B][H_q][D]
+ *   budget_tokens: device int32 [B], token budget per sequence (the write-up's
+ *                  rule min(4096, L/32) is spa_default_budget)
+ *   k_max:         host int, capacity of a sel_pages row, >= 1
+ *   sel_pages:     device int32 [B][H_kv][k_max]  (written)
+ *   sel_count:     device int32 [B][H_kv]         (written)
+ *   sel_len:       device int32 [B]               (written)
+ *   scores:        device fp32 [B][H_kv][max_pages * P / p] or NULL; when
+ *                  given, receives s_j for dynamic heads (entries j >= n_b
+ *                  unspecified)
+ *   ws, ws_bytes:  device workspace of at least spa_workspace_bytes() bytes
+ * Reuse across steps (write-up "3.2": rerun selection every C tokens) is the
+ * caller's: call this only on steps that select and keep the outputs. */
+spa_status spa_select_pages(const spa_pool* pool, const spa_heads* heads,
+                            const spa_batch* batch, const void* q,
+                            const int32_t* budget_tokens, int32_t k_max,
+                            int32_t* sel_pages, int32_t* sel_count, int32_t* sel_len,
+                            float* scores, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/* ---- a6 + a7 + a8: unified sparse decode attention ----------------------
+ * For every sequence b and query head i (KV head h = i / G):
+ *     out[b][i] = sum_{t in T} softmax_t(q_i . K_t / sqrt(D)) V_t,
+ *     lse[b][i] = natural log of sum_{t in T} exp(q_i . K_t / sqrt(D)),
+ * with the attended token set T
+ *   streaming head: [0, min(sink, L)) U [max(sink, L - window), L);
+ *   dynamic head:   { t < L : t / p in sel_pages[b][h][0..sel_count) }
+ *                   U [sel_len[b], L)   (tokens appended since the selection).
+ * bf16 inputs, fp32 accumulation. Work is split over the attended tokens and
+ * the split results are merged with the running-max / running-sum rule of
+ * online softmax (FlashAttention, long-context survey "2.1"; the max and sum
+ * outputs of the Novita vLLM article, "2. 注意力机制修改").
+ *   out: device fp32 [B][H_q][D]; lse: device fp32 [B][H_q] or NULL.
+ *   sel_*: as written by spa_select_pages (not read for streaming heads);
+ *   k_max: capacity of a sel_pages row.
+ * A sequence with L_b < 1 gets out = 0 and lse = -inf. */
+spa_status spa_sparse_decode_attn(const spa_pool* pool, const spa_heads* heads,
+                                  const spa_batch* batch, const void* q,
+                                  const int32_t* sel_pages, const int32_t* sel_count,
+                                  const int32_t* sel_len, int32_t k_max,
+                                  float* out, float* lse, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
+/* Workspace bytes needed by spa_select_pages and spa_sparse_decode_attn for
+ * these shapes (one buffer serves both). Returns 0 for invalid arguments. */
+size_t spa_workspace_bytes(const spa_pool* pool, const spa_heads* heads,
+                           int32_t batch, int32_t max_pages, int32_t k_max);
+
+/* The write-up's dynamic budget rule ("3.2"): min(4096, L / 32) tokens,
+ * integer division; 0 for L < 32. */
+int32_t spa_default_budget(int64_t context_len);
+
+/* ---- physical-page allocator (host) -------------------------------------
+ * A free list over page ids 0..N-1 (LServe write-up "2.2": free list of
+ * physical pages; long-context survey "3.4": allocate_page raises when no
+ * page is free). Pages are handed out lowest id first from a fresh
+ * allocator. Not thread-safe. */
+typedef struct spa_allocator spa_allocator;
+
+/* num_pages >= 1; *out receives the handle. */
+spa_status spa_alloc_create(int32_t num_pages, spa_allocator** out);
+/* All-or-nothing: either `count` ids are written to ids_out (host int32
+ * [count]) or SPA_ERR_POOL_EXHAUSTED is returned and nothing changes. */
+spa_status spa_alloc_pages(spa_allocator* a, int32_t count, int32_t* ids_out);
+/* Returns pages to the free list. An id out of range or not allocated makes
+ * the whole call fail with SPA_ERR_INVALID and nothing changes. */
+spa_status spa_alloc_free(spa_allocator* a, int32_t count, const int32_t* ids);
+/* Number of free pages, or -1 for a NULL handle. */
+int32_t spa_alloc_num_free(const spa_allocator* a);
+void spa_alloc_destroy(spa_allocator* a);
+
+/* Static text for a status code. */
+const char* spa_status_string(spa_status s);
+/* Message of the last failing call on this thread ("" if none). */
+const char* spa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPA_H */

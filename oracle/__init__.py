@@ -1,0 +1,230 @@
+"""CPU oracle for sparse paged decode attention -- test infrastructure only.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` import this package. The product (``sparse_paged_attention_amd``)
+never does, and the two share no code.
+
+This module is a thin ctypes layer over ``spa_oracle.c`` (plain C, fp64
+attention, exact page scores). Each wrapper takes and returns numpy arrays in
+logical (position) order; bf16 values travel as uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "spa_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+ORC_OK, ORC_ERR_ARG, ORC_ERR_NONFINITE, ORC_ERR_RANGE = 0, 1, 2, 3
+
+
+def build(force: bool = False) -> str:
+    """Compile spa_oracle.c with gcc (OpenMP) into oracle/liboracle.so."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=gnu11", "-fopenmp", "-fPIC", "-shared",
+                               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class OrcJob(ctypes.Structure):
+    _fields_ = [
+        ("K", ctypes.c_void_p), ("V", ctypes.c_void_p), ("q", ctypes.c_void_p),
+        ("L", ctypes.c_int64),
+        ("D", ctypes.c_int32), ("G", ctypes.c_int32), ("dynamic", ctypes.c_int32),
+        ("sink", ctypes.c_int32), ("window", ctypes.c_int32), ("p", ctypes.c_int32),
+        ("budget", ctypes.c_int64),
+        ("do_select", ctypes.c_int32),
+        ("sel", ctypes.c_void_p), ("sel_cap", ctypes.c_int64),
+        ("nsel", ctypes.c_void_p), ("Ls", ctypes.c_void_p),
+        ("scores", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("rc", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = build()
+        L = ctypes.CDLL(path)
+        i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+        L.orc_bf16_value.argtypes = [ctypes.c_uint16]
+        L.orc_bf16_value.restype = ctypes.c_double
+        L.orc_budget_tokens.argtypes = [i64]
+        L.orc_budget_tokens.restype = i32
+        L.orc_pages_to_select.argtypes = [i64, i64, i32]
+        L.orc_pages_to_select.restype = i64
+        L.orc_page_summary.argtypes = [vp, i64, i32, i32, vp, vp]
+        L.orc_page_scores.argtypes = [vp, i32, i32, vp, vp, i64, vp]
+        L.orc_topk.argtypes = [vp, i64, i64, vp]
+        L.orc_attended_set.argtypes = [i32, i64, i32, i32, i32, vp, i64, i64, vp]
+        L.orc_attended_set.restype = i64
+        L.orc_attend.argtypes = [vp, vp, vp, i64, i32, vp, vp, vp]
+        L.orc_decode_head.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, i64,
+                                      i32, vp, i64, vp, vp, vp, vp, vp]
+        L.orc_decode_heads.argtypes = [i32, ctypes.POINTER(OrcJob)]
+        L.orc_decode_heads.restype = i32
+        L.orc_num_threads.restype = i32
+        for name in ("orc_page_summary", "orc_page_scores", "orc_topk", "orc_attend",
+                     "orc_decode_head"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != ORC_OK:
+        raise OracleError(f"{what} failed with oracle status {rc}")
+
+
+def _u16(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("bf16 arrays travel as uint16 bit patterns")
+    return a
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def bf16_value(bits: int) -> float:
+    return lib().orc_bf16_value(bits)
+
+
+def budget_tokens(L: int) -> int:
+    return lib().orc_budget_tokens(L)
+
+
+def pages_to_select(n: int, budget: int, p: int) -> int:
+    return lib().orc_pages_to_select(n, budget, p)
+
+
+def page_summary(K: np.ndarray, p: int):
+    """K: uint16 [L][D] -> (kmin, kmax) uint16 [ceil(L/p)][D]."""
+    K = _u16(K)
+    L, D = K.shape
+    n = -(-L // p)
+    kmin = np.empty((n, D), np.uint16)
+    kmax = np.empty((n, D), np.uint16)
+    _check(lib().orc_page_summary(_ptr(K), L, D, p, _ptr(kmin), _ptr(kmax)), "page_summary")
+    return kmin, kmax
+
+
+def page_scores(q: np.ndarray, kmin: np.ndarray, kmax: np.ndarray) -> np.ndarray:
+    """q: uint16 [G][D]; kmin/kmax: uint16 [n][D] -> float32 [n]."""
+    q, kmin, kmax = _u16(q), _u16(kmin), _u16(kmax)
+    G, D = q.shape
+    n = kmin.shape[0]
+    s = np.empty(n, np.float32)
+    _check(lib().orc_page_scores(_ptr(q), G, D, _ptr(kmin), _ptr(kmax), n, _ptr(s)), "page_scores")
+    return s
+
+
+def topk(scores: np.ndarray, k: int) -> np.ndarray:
+    s = np.ascontiguousarray(scores, dtype=np.float32)
+    ids = np.empty(max(k, 1), np.int32)
+    _check(lib().orc_topk(_ptr(s), s.size, k, _ptr(ids)), "topk")
+    return ids[:k].copy()
+
+
+def attended_set(dynamic: bool, L: int, sink: int, window: int, p: int,
+                 sel=None, Ls: int | None = None) -> np.ndarray:
+    sel = np.ascontiguousarray(sel if sel is not None else np.zeros(0), dtype=np.int32)
+    mask = np.empty(max(L, 1), np.uint8)
+    cnt = lib().orc_attended_set(int(dynamic), L, sink, window, p, _ptr(sel), sel.size,
+                                 L if Ls is None else Ls, _ptr(mask))
+    if cnt < 0:
+        raise OracleError("attended_set failed")
+    return mask[:L].astype(bool)
+
+
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, mask) -> tuple[np.ndarray, float]:
+    """q: uint16 [D]; K, V: uint16 [L][D]; mask: bool [L] -> (out fp64 [D], lse)."""
+    q, K, V = _u16(q), _u16(K), _u16(V)
+    L, D = K.shape
+    m = np.ascontiguousarray(mask, dtype=np.uint8)
+    out = np.empty(D, np.float64)
+    lse = np.empty(1, np.float64)
+    _check(lib().orc_attend(_ptr(q), _ptr(K), _ptr(V), L, D, _ptr(m), _ptr(out), _ptr(lse)), "attend")
+    return out, float(lse[0])
+
+
+class HeadState:
+    """Selection carried between decode steps for one dynamic (sequence, KV head)."""
+
+    def __init__(self, cap: int):
+        self.sel = np.zeros(max(cap, 1), np.int32)
+        self.nsel = np.zeros(1, np.int64)
+        self.Ls = np.zeros(1, np.int64)
+
+    @property
+    def pages(self) -> np.ndarray:
+        return self.sel[: int(self.nsel[0])].copy()
+
+
+def decode_head(K, V, q, *, dynamic: bool, sink: int, window: int, p: int, budget: int,
+                do_select: bool, state: HeadState | None = None, want_scores: bool = False):
+    """One decode step for one (sequence, KV head); K, V [L][D], q [G][D] (uint16).
+
+    Returns (out fp64 [G][D], lse fp64 [G], scores or None)."""
+    K, V, q = _u16(K), _u16(V), _u16(q)
+    L, D = K.shape
+    G = q.shape[0]
+    n = -(-L // p)
+    if state is None:
+        state = HeadState(n)
+    scores = np.full(n, np.nan, np.float32) if (want_scores and dynamic and do_select) else None
+    out = np.empty((G, D), np.float64)
+    lse = np.empty(G, np.float64)
+    rc = lib().orc_decode_head(_ptr(K), _ptr(V), _ptr(q), L, D, G, int(dynamic), sink, window, p,
+                               budget, int(do_select), _ptr(state.sel), state.sel.size,
+                               _ptr(state.nsel), _ptr(state.Ls),
+                               _ptr(scores) if scores is not None else None,
+                               _ptr(out), _ptr(lse))
+    _check(rc, "decode_head")
+    return out, lse, scores
+
+
+def decode_heads(jobs: list[dict]) -> list[tuple[np.ndarray, np.ndarray]]:
+    """Runs many independent decode_head jobs in parallel (OpenMP).
+
+    Each job dict holds K, V, q, dynamic, sink, window, p, budget, do_select,
+    state (HeadState). Returns [(out, lse)] in job order."""
+    arr = (OrcJob * len(jobs))()
+    keep = []
+    results = []
+    for i, j in enumerate(jobs):
+        K, V, q = _u16(j["K"]), _u16(j["V"]), _u16(j["q"])
+        L, D = K.shape
+        G = q.shape[0]
+        st = j["state"]
+        out = np.empty((G, D), np.float64)
+        lse = np.empty(G, np.float64)
+        keep += [K, V, q, out, lse]
+        results.append((out, lse))
+        arr[i] = OrcJob(_ptr(K), _ptr(V), _ptr(q), L, D, G, int(j["dynamic"]), j["sink"],
+                        j["window"], j["p"], j["budget"], int(j["do_select"]), _ptr(st.sel),
+                        st.sel.size, _ptr(st.nsel), _ptr(st.Ls), None, _ptr(out), _ptr(lse), 0)
+    failed = lib().orc_decode_heads(len(jobs), arr)
+    if failed:
+        bad = [(i, arr[i].rc) for i in range(len(jobs)) if arr[i].rc]
+        raise OracleError(f"{failed} oracle jobs failed: {bad[:4]}")
+    return results
+
+
+def num_threads() -> int:
+    return lib().orc_num_threads()

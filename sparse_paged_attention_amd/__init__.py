@@ -1,0 +1,330 @@
+"""Python binding of libspa.so, the sparse paged decode-attention library for
+MI355X (gfx950).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels. PyTorch provides device memory and the current HIP stream. The C ABI
+is documented in include/spa.h; the functions here take the same arguments as
+its entry points, with torch tensors in place of device pointers.
+
+The library must be built (``python __graft_entry__.py`` or
+``sparse_paged_attention_amd._build.build_library()``); importing this module
+fails loudly when it is not.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspa.so")
+
+SPA_OK, SPA_ERR_INVALID, SPA_ERR_UNSUPPORTED, SPA_ERR_POOL_EXHAUSTED, SPA_ERR_WORKSPACE, SPA_ERR_HIP = range(6)
+
+HEAD_DIM = 128
+
+
+class SpaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+        self.message = message
+
+
+class PoolExhausted(SpaError):
+    pass
+
+
+class c_pool(ctypes.Structure):
+    _fields_ = [("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("logical_page", ctypes.c_int32), ("physical_page", ctypes.c_int32),
+                ("num_phys_pages", ctypes.c_int32), ("k_pool", ctypes.c_void_p),
+                ("v_pool", ctypes.c_void_p), ("summary", ctypes.c_void_p)]
+
+
+class c_heads(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("sink", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("kind", ctypes.POINTER(ctypes.c_uint8))]
+
+
+class c_batch(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+                ("page_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p)]
+
+
+EXPORTS = ("spa_kv_pool_append", "spa_kv_pool_write", "spa_page_summary_update",
+           "spa_select_pages", "spa_sparse_decode_attn", "spa_workspace_bytes",
+           "spa_default_budget", "spa_alloc_create", "spa_alloc_pages", "spa_alloc_free",
+           "spa_alloc_num_free", "spa_alloc_destroy", "spa_status_string", "spa_last_error")
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libspa.so; raises if it was never built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build the HIP library first "
+                              "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        P, H, B = ctypes.POINTER(c_pool), ctypes.POINTER(c_heads), ctypes.POINTER(c_batch)
+        sig = {
+            "spa_kv_pool_append": ([P, B, vp, vp, vp], ctypes.c_int),
+            "spa_kv_pool_write": ([P, vp, i32, i64, i64, vp, vp, vp], ctypes.c_int),
+            "spa_page_summary_update": ([P, H, B, vp, i32, vp], ctypes.c_int),
+            "spa_select_pages": ([P, H, B, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+            "spa_sparse_decode_attn": ([P, H, B, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp], ctypes.c_int),
+            "spa_workspace_bytes": ([P, H, i32, i32, i32], sz),
+            "spa_default_budget": ([i64], i32),
+            "spa_alloc_create": ([i32, ctypes.POINTER(vp)], ctypes.c_int),
+            "spa_alloc_pages": ([vp, i32, vp], ctypes.c_int),
+            "spa_alloc_free": ([vp, i32, vp], ctypes.c_int),
+            "spa_alloc_num_free": ([vp], i32),
+            "spa_alloc_destroy": ([vp], None),
+            "spa_status_string": ([ctypes.c_int], ctypes.c_char_p),
+            "spa_last_error": ([], ctypes.c_char_p),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != SPA_OK:
+        msg = lib().spa_last_error().decode()
+        cls = PoolExhausted if status == SPA_ERR_POOL_EXHAUSTED else SpaError
+        raise cls(status, msg)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+_DT = {"bf16": "torch.bfloat16", "f32": "torch.float32", "i32": "torch.int32", "u8": "torch.uint8"}
+
+
+def _need(t, shape, dtype: str, name: str, optional: bool = False) -> None:
+    """Checks a device tensor argument: shape (None = any extent), dtype,
+    contiguity. The C ABI cannot see buffer extents, so they are checked here."""
+    if t is None:
+        if optional:
+            return
+        raise SpaError(SPA_ERR_INVALID, f"{name} is None")
+    if str(t.dtype) != _DT[dtype]:
+        raise SpaError(SPA_ERR_INVALID, f"{name}: dtype {t.dtype}, expected {_DT[dtype]}")
+    if not t.is_contiguous():
+        raise SpaError(SPA_ERR_INVALID, f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise SpaError(SPA_ERR_INVALID, f"{name} must be a device tensor")
+    if len(t.shape) != len(shape) or any(e is not None and e != a for e, a in zip(shape, t.shape)):
+        raise SpaError(SPA_ERR_INVALID, f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _heads_for(heads, pool):
+    if len(heads.kind) != pool.num_kv_heads:
+        raise SpaError(SPA_ERR_INVALID, f"heads.kind has {len(heads.kind)} entries, pool has "
+                                        f"{pool.num_kv_heads} KV heads")
+    return heads.c()
+
+
+def _stream(stream=None) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+# ------------------------------------------------------------------ objects
+
+@dataclass
+class Pool:
+    """A physical-page pool of one attention layer (device tensors).
+
+    k: bf16 [N][H_kv][P][D]; v: bf16 [N][H_kv][P/p][D][p];
+    summary: bf16 [N][H_kv][P/p][2][D] or None."""
+    num_kv_heads: int
+    logical_page: int
+    physical_page: int
+    num_phys_pages: int
+    k: object
+    v: object
+    summary: object = None
+    head_dim: int = HEAD_DIM
+
+    @classmethod
+    def empty(cls, num_kv_heads: int, logical_page: int, physical_page: int, num_phys_pages: int,
+              with_summary: bool = True, device="cuda", zero: bool = True) -> "Pool":
+        import torch
+        mk = torch.zeros if zero else torch.empty
+        r = physical_page // logical_page
+        k = mk((num_phys_pages, num_kv_heads, physical_page, HEAD_DIM), dtype=torch.bfloat16, device=device)
+        v = mk((num_phys_pages, num_kv_heads, r, HEAD_DIM, logical_page), dtype=torch.bfloat16, device=device)
+        s = mk((num_phys_pages, num_kv_heads, r, 2, HEAD_DIM), dtype=torch.bfloat16, device=device) \
+            if with_summary else None
+        return cls(num_kv_heads, logical_page, physical_page, num_phys_pages, k, v, s)
+
+    def check(self) -> None:
+        r = self.physical_page // max(self.logical_page, 1)
+        N, H, P, p = self.num_phys_pages, self.num_kv_heads, self.physical_page, self.logical_page
+        _need(self.k, (N, H, P, HEAD_DIM), "bf16", "pool.k")
+        _need(self.v, (N, H, r, HEAD_DIM, p), "bf16", "pool.v")
+        _need(self.summary, (N, H, r, 2, HEAD_DIM), "bf16", "pool.summary", optional=True)
+
+    def c(self) -> c_pool:
+        self.check()
+        return c_pool(self.num_kv_heads, self.head_dim, self.logical_page, self.physical_page,
+                      self.num_phys_pages, _ptr(self.k), _ptr(self.v), _ptr(self.summary))
+
+
+@dataclass
+class Heads:
+    """Head kinds (0 streaming, 1 dynamic per KV head) and the streaming pattern."""
+    num_q_heads: int
+    kind: tuple
+    sink: int
+    window: int
+
+    def c(self) -> c_heads:
+        if len(self.kind) < 1:
+            raise SpaError(SPA_ERR_INVALID, "heads.kind is empty")
+        arr = (ctypes.c_uint8 * len(self.kind))(*[int(k) for k in self.kind])
+        h = c_heads(self.num_q_heads, self.sink, self.window,
+                    ctypes.cast(arr, ctypes.POINTER(ctypes.c_uint8)))
+        h._keep = arr
+        return h
+
+
+@dataclass
+class Batch:
+    """page_table: int32 [B][max_pages] (device); seq_lens: int32 [B] (device)."""
+    page_table: object
+    seq_lens: object
+
+    def c(self) -> c_batch:
+        _need(self.page_table, (None, None), "i32", "page_table")
+        B, mp = self.page_table.shape
+        _need(self.seq_lens, (B,), "i32", "seq_lens")
+        return c_batch(B, mp, _ptr(self.page_table), _ptr(self.seq_lens))
+
+
+# ------------------------------------------------------------ entry points
+
+def kv_pool_append(pool: Pool, batch: Batch, k_new, v_new, stream=None) -> None:
+    """spa_kv_pool_append: k_new, v_new bf16 [B][H_kv][D]."""
+    p, b = pool.c(), batch.c()
+    shape = (b.batch, pool.num_kv_heads, HEAD_DIM)
+    _need(k_new, shape, "bf16", "k_new")
+    _need(v_new, shape, "bf16", "v_new")
+    _check(lib().spa_kv_pool_append(ctypes.byref(p), ctypes.byref(b), _ptr(k_new), _ptr(v_new),
+                                    _stream(stream)))
+
+
+def kv_pool_write(pool: Pool, page_table_row, start: int, k, v, stream=None) -> None:
+    """spa_kv_pool_write: k, v bf16 [H_kv][count][D] for positions [start, start+count)."""
+    p = pool.c()
+    _need(page_table_row, (None,), "i32", "page_table_row")
+    _need(k, (pool.num_kv_heads, None, HEAD_DIM), "bf16", "k")
+    count = k.shape[1]
+    _need(v, (pool.num_kv_heads, count, HEAD_DIM), "bf16", "v")
+    _check(lib().spa_kv_pool_write(ctypes.byref(p), _ptr(page_table_row), page_table_row.shape[0],
+                                   start, count, _ptr(k), _ptr(v), _stream(stream)))
+
+
+def page_summary_update(pool: Pool, heads: Heads, batch: Batch, first_pos=None, max_tokens: int = 1,
+                        stream=None) -> None:
+    """spa_page_summary_update (first_pos None: the page of the newest token)."""
+    p, h, b = pool.c(), _heads_for(heads, pool), batch.c()
+    _need(first_pos, (b.batch,), "i32", "first_pos", optional=True)
+    _check(lib().spa_page_summary_update(ctypes.byref(p), ctypes.byref(h), ctypes.byref(b),
+                                         _ptr(first_pos), max_tokens, _stream(stream)))
+
+
+def workspace_bytes(pool: Pool, heads: Heads, batch: int, max_pages: int, k_max: int) -> int:
+    p, h = pool.c(), _heads_for(heads, pool)
+    n = lib().spa_workspace_bytes(ctypes.byref(p), ctypes.byref(h), batch, max_pages, k_max)
+    if n == 0:
+        raise SpaError(SPA_ERR_INVALID, "workspace_bytes: invalid shapes")
+    return n
+
+
+def select_pages(pool: Pool, heads: Heads, batch: Batch, q, budget_tokens, k_max: int,
+                 sel_pages, sel_count, sel_len, scores=None, workspace=None, stream=None) -> None:
+    """spa_select_pages: q bf16 [B][H_q][D]; budget_tokens int32 [B];
+    writes sel_pages int32 [B][H_kv][k_max], sel_count int32 [B][H_kv], sel_len int32 [B]."""
+    p, h, b = pool.c(), _heads_for(heads, pool), batch.c()
+    B, H = b.batch, pool.num_kv_heads
+    _need(q, (B, heads.num_q_heads, HEAD_DIM), "bf16", "q")
+    _need(budget_tokens, (B,), "i32", "budget_tokens")
+    _need(sel_pages, (B, H, k_max), "i32", "sel_pages")
+    _need(sel_count, (B, H), "i32", "sel_count")
+    _need(sel_len, (B,), "i32", "sel_len")
+    n_max = b.max_pages * (pool.physical_page // pool.logical_page)
+    _need(scores, (B, H, n_max), "f32", "scores", optional=True)
+    _need(workspace, (None,), "u8", "workspace", optional=True)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().spa_select_pages(ctypes.byref(p), ctypes.byref(h), ctypes.byref(b), _ptr(q),
+                                  _ptr(budget_tokens), k_max, _ptr(sel_pages), _ptr(sel_count),
+                                  _ptr(sel_len), _ptr(scores), _ptr(workspace), ws_bytes,
+                                  _stream(stream)))
+
+
+def sparse_decode_attn(pool: Pool, heads: Heads, batch: Batch, q, sel_pages, sel_count, sel_len,
+                       k_max: int, out, lse=None, workspace=None, stream=None) -> None:
+    """spa_sparse_decode_attn: out fp32 [B][H_q][D], lse fp32 [B][H_q] or None."""
+    p, h, b = pool.c(), _heads_for(heads, pool), batch.c()
+    B, H, HQ = b.batch, pool.num_kv_heads, heads.num_q_heads
+    _need(q, (B, HQ, HEAD_DIM), "bf16", "q")
+    dyn = any(heads.kind)
+    _need(sel_pages, (B, H, k_max), "i32", "sel_pages", optional=not dyn)
+    _need(sel_count, (B, H), "i32", "sel_count", optional=not dyn)
+    _need(sel_len, (B,), "i32", "sel_len", optional=not dyn)
+    _need(out, (B, HQ, HEAD_DIM), "f32", "out")
+    _need(lse, (B, HQ), "f32", "lse", optional=True)
+    _need(workspace, (None,), "u8", "workspace", optional=True)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().spa_sparse_decode_attn(ctypes.byref(p), ctypes.byref(h), ctypes.byref(b), _ptr(q),
+                                        _ptr(sel_pages), _ptr(sel_count), _ptr(sel_len), k_max,
+                                        _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                                        _stream(stream)))
+
+
+def default_budget(context_len: int) -> int:
+    """min(4096, L // 32): the write-up's dynamic budget rule."""
+    return lib().spa_default_budget(context_len)
+
+
+class Allocator:
+    """Host free list of physical page ids (spa_alloc_*)."""
+
+    def __init__(self, num_pages: int):
+        h = ctypes.c_void_p()
+        _check(lib().spa_alloc_create(num_pages, ctypes.byref(h)))
+        self._h = h
+
+    def alloc(self, count: int) -> list:
+        ids = (ctypes.c_int32 * max(count, 1))()
+        _check(lib().spa_alloc_pages(self._h, count, ids))
+        return list(ids[:count])
+
+    def free(self, ids) -> None:
+        arr = (ctypes.c_int32 * max(len(ids), 1))(*ids)
+        _check(lib().spa_alloc_free(self._h, len(ids), arr))
+
+    @property
+    def num_free(self) -> int:
+        return lib().spa_alloc_num_free(self._h)
+
+    def close(self) -> None:
+        if self._h:
+            lib().spa_alloc_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,42 @@
+"""Builds libspa.so (HIP, gfx950) in-tree with hipcc."""
+from __future__ import annotations
+
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+ROOT = os.path.dirname(PKG)
+LIB = os.path.join(PKG, "libspa.so")
+SOURCES = ["api.cpp", "pool.hip", "select.hip", "attn.hip"]
+ARCH = "gfx950"
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+# Packed fp32 instructions are kept out of every kernel.
+FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         f"-I{os.path.join(ROOT, 'include')}"]
+
+
+def _compile(src: str, out_dir: str) -> str:
+    obj = os.path.join(out_dir, src + ".o")
+    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    subprocess.check_call([HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj],
+                          stderr=subprocess.STDOUT if os.environ.get("SPA_BUILD_VERBOSE") else subprocess.DEVNULL)
+    return obj
+
+
+def build_library() -> str:
+    out_dir = os.path.join(PKG, "_build")
+    os.makedirs(out_dir, exist_ok=True)
+    with ThreadPoolExecutor(len(SOURCES)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, out_dir), SOURCES))
+    tmp = LIB + ".tmp"
+    subprocess.check_call([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build_library())

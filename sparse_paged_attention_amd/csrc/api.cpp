@@ -1,0 +1,374 @@
+// C ABI of libspa.so: argument checks on the host, launch planning, and the
+// host-side physical-page allocator. Every check runs before anything is
+// enqueued; kernels only see arguments that passed them.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/spa.h"
+#include "spa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+spa_status fail(spa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+spa_status ok() {
+  g_last_error.clear();
+  return SPA_OK;
+}
+
+spa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SPA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Attention blocks per work item (16 tokens each).
+constexpr int32_t kBlocksPerItem = 8;
+// Largest page count a selection row can score (top-k keeps 64 keys per thread).
+constexpr int64_t kMaxScoredPages = 65536;
+
+spa_status check_pool(const spa_pool* pool, spa::PoolArgs* out) {
+  if (!pool) return fail(SPA_ERR_INVALID, "pool is NULL");
+  if (pool->num_kv_heads < 1 || pool->num_kv_heads > spa::kMaxKvHeads)
+    return fail(SPA_ERR_INVALID, "num_kv_heads %d outside [1, %d]", pool->num_kv_heads, spa::kMaxKvHeads);
+  if (pool->head_dim != spa::kHeadDim)
+    return fail(pool->head_dim < 1 ? SPA_ERR_INVALID : SPA_ERR_UNSUPPORTED,
+                "head_dim %d: only 128 is built", pool->head_dim);
+  const int32_t p = pool->logical_page, P = pool->physical_page;
+  if (p < 1 || p > 64) return fail(SPA_ERR_INVALID, "logical_page %d outside [1, 64]", p);
+  if (p != 16 && p != 32 && p != 64)
+    return fail(SPA_ERR_UNSUPPORTED, "logical_page %d: only 16, 32 and 64 are built", p);
+  if (P < p || P % p != 0) return fail(SPA_ERR_INVALID, "physical_page %d is not a multiple of logical_page %d", P, p);
+  if (P / p > 64) return fail(SPA_ERR_INVALID, "physical_page / logical_page = %d exceeds 64", P / p);
+  if (pool->num_phys_pages < 1) return fail(SPA_ERR_INVALID, "num_phys_pages %d < 1", pool->num_phys_pages);
+  if (!pool->k_pool || !pool->v_pool) return fail(SPA_ERR_INVALID, "k_pool / v_pool is NULL");
+  out->hkv = pool->num_kv_heads;
+  out->p = p;
+  out->P = P;
+  out->r = P / p;
+  out->N = pool->num_phys_pages;
+  out->k = static_cast<uint16_t*>(pool->k_pool);
+  out->v = static_cast<uint16_t*>(pool->v_pool);
+  out->summ = static_cast<uint16_t*>(pool->summary);
+  return SPA_OK;
+}
+
+spa_status check_heads(const spa_heads* heads, const spa::PoolArgs& pl, int32_t* G,
+                       spa::HeadList* dyn, uint8_t* kind) {
+  if (!heads) return fail(SPA_ERR_INVALID, "heads is NULL");
+  if (heads->num_q_heads < 1 || heads->num_q_heads % pl.hkv != 0)
+    return fail(SPA_ERR_INVALID, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                heads->num_q_heads, pl.hkv);
+  const int32_t g = heads->num_q_heads / pl.hkv;
+  if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16)
+    return fail(SPA_ERR_UNSUPPORTED, "query group size %d: only 1, 2, 4, 8, 16 are built", g);
+  if (heads->sink < 0) return fail(SPA_ERR_INVALID, "sink %d < 0", heads->sink);
+  if (heads->window < 1) return fail(SPA_ERR_INVALID, "window %d < 1", heads->window);
+  if (!heads->kind) return fail(SPA_ERR_INVALID, "heads->kind is NULL");
+  dyn->n = 0;
+  for (int32_t h = 0; h < pl.hkv; ++h) {
+    const uint8_t k = heads->kind[h];
+    if (k > 1) return fail(SPA_ERR_INVALID, "kind[%d] = %u is neither 0 nor 1", h, (unsigned)k);
+    if (kind) kind[h] = k;
+    if (k) dyn->id[dyn->n++] = (int16_t)h;
+  }
+  if (dyn->n > 0 && !pl.summ) return fail(SPA_ERR_INVALID, "dynamic heads need pool->summary");
+  *G = g;
+  return SPA_OK;
+}
+
+spa_status check_batch(const spa_batch* batch, const spa::PoolArgs& pl, spa::BatchArgs* out) {
+  if (!batch) return fail(SPA_ERR_INVALID, "batch is NULL");
+  if (batch->batch < 0) return fail(SPA_ERR_INVALID, "batch %d < 0", batch->batch);
+  if (batch->batch > 65535) return fail(SPA_ERR_INVALID, "batch %d > 65535", batch->batch);
+  if (batch->max_pages < 1) return fail(SPA_ERR_INVALID, "max_pages %d < 1", batch->max_pages);
+  if ((int64_t)batch->max_pages * pl.P > INT32_MAX)
+    return fail(SPA_ERR_INVALID, "max_pages * physical_page exceeds 2^31 - 1 tokens");
+  if (batch->batch > 0 && (!batch->page_table || !batch->seq_lens))
+    return fail(SPA_ERR_INVALID, "page_table / seq_lens is NULL");
+  out->B = batch->batch;
+  out->max_pp = batch->max_pages;
+  out->pt = batch->page_table;
+  out->lens = batch->seq_lens;
+  return SPA_OK;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+int32_t n_max_pages(const spa::PoolArgs& pl, int32_t max_pp) {
+  return (int32_t)((int64_t)max_pp * pl.r);   // logical pages a page-table row can address
+}
+
+void plan_attention(const spa::PoolArgs& pl, const spa_heads* heads, int32_t k_max,
+                    const uint8_t* kind, spa::AttnPlan* plan) {
+  std::memset(plan, 0, sizeof *plan);
+  const int32_t bpi = kBlocksPerItem;
+  // streaming blocks: sink blocks + window blocks (+1 when the window is unaligned)
+  const int64_t nb_stream = (heads->sink + 15) / 16 + (heads->window + 15) / 16 + 1;
+  const int64_t nb_dyn = (int64_t)k_max * (pl.p / 16);
+  plan->blocks_per_item = bpi;
+  plan->items_stream = (int32_t)((nb_stream + bpi - 1) / bpi);
+  plan->items_dyn = (int32_t)((nb_dyn + bpi - 1) / bpi) + 1;       // + the tail item
+  plan->item_stride = std::max(plan->items_stream, plan->items_dyn);
+  plan->sink = heads->sink;
+  plan->window = heads->window;
+  plan->k_max = k_max;
+  int32_t at = 0;
+  for (int32_t h = 0; h < pl.hkv; ++h) {
+    plan->kind[h] = kind[h];
+    plan->item_base[h] = at;
+    at += kind[h] ? plan->items_dyn : plan->items_stream;
+  }
+  plan->item_base[pl.hkv] = at;
+  plan->items_per_seq = at;
+}
+
+size_t attn_bytes(const spa::PoolArgs& pl, const spa::AttnPlan& plan, int32_t B, int32_t G, size_t* ml_off) {
+  const size_t slots = (size_t)B * pl.hkv * plan.item_stride * G;
+  const size_t o = align_up(slots * spa::kHeadDim * sizeof(float));
+  *ml_off = o;
+  return o + align_up(slots * 2 * sizeof(float));
+}
+
+size_t select_bytes(const spa::PoolArgs& pl, int32_t B, int32_t max_pp) {
+  return align_up((size_t)B * pl.hkv * n_max_pages(pl, max_pp) * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* spa_status_string(spa_status s) {
+  switch (s) {
+    case SPA_OK: return "ok";
+    case SPA_ERR_INVALID: return "invalid argument";
+    case SPA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SPA_ERR_POOL_EXHAUSTED: return "page pool exhausted";
+    case SPA_ERR_WORKSPACE: return "workspace missing or too small";
+    case SPA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* spa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t spa_default_budget(int64_t context_len) {
+  if (context_len < 0) return 0;
+  const int64_t b = context_len / 32;
+  return (int32_t)std::min<int64_t>(b, 4096);
+}
+
+spa_status spa_kv_pool_append(const spa_pool* pool, const spa_batch* batch, const void* k_new,
+                              const void* v_new, hipStream_t stream) {
+  spa::PoolArgs pl;
+  spa::BatchArgs bt;
+  spa_status s;
+  if ((s = check_pool(pool, &pl)) != SPA_OK) return s;
+  if ((s = check_batch(batch, pl, &bt)) != SPA_OK) return s;
+  if (bt.B == 0) return ok();
+  if (!k_new || !v_new) return fail(SPA_ERR_INVALID, "k_new / v_new is NULL");
+  return hip_status(spa::launch_append(pl, bt, static_cast<const uint16_t*>(k_new),
+                                       static_cast<const uint16_t*>(v_new), stream),
+                    "kv_pool_append launch");
+}
+
+spa_status spa_kv_pool_write(const spa_pool* pool, const int32_t* page_table_row, int32_t max_pages,
+                             int64_t start, int64_t count, const void* k, const void* v,
+                             hipStream_t stream) {
+  spa::PoolArgs pl;
+  spa_status s;
+  if ((s = check_pool(pool, &pl)) != SPA_OK) return s;
+  if (max_pages < 1) return fail(SPA_ERR_INVALID, "max_pages %d < 1", max_pages);
+  if (start < 0 || count < 0) return fail(SPA_ERR_INVALID, "start %lld / count %lld negative",
+                                          (long long)start, (long long)count);
+  if (start + count > (int64_t)max_pages * pl.P)
+    return fail(SPA_ERR_INVALID, "tokens [%lld, %lld) exceed max_pages * physical_page = %lld",
+                (long long)start, (long long)(start + count), (long long)max_pages * pl.P);
+  if (count == 0) return ok();
+  if (count > (int64_t)UINT32_MAX * 4) return fail(SPA_ERR_INVALID, "count too large");
+  if (!page_table_row || !k || !v) return fail(SPA_ERR_INVALID, "page_table_row / k / v is NULL");
+  return hip_status(spa::launch_write(pl, page_table_row, max_pages, start, count,
+                                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                                      stream),
+                    "kv_pool_write launch");
+}
+
+spa_status spa_page_summary_update(const spa_pool* pool, const spa_heads* heads, const spa_batch* batch,
+                                   const int32_t* first_pos, int32_t max_tokens, hipStream_t stream) {
+  spa::PoolArgs pl;
+  spa::BatchArgs bt;
+  spa::HeadList dyn;
+  int32_t G;
+  spa_status s;
+  if ((s = check_pool(pool, &pl)) != SPA_OK) return s;
+  if ((s = check_heads(heads, pl, &G, &dyn, nullptr)) != SPA_OK) return s;
+  if ((s = check_batch(batch, pl, &bt)) != SPA_OK) return s;
+  if (max_tokens < 1) return fail(SPA_ERR_INVALID, "max_tokens %d < 1", max_tokens);
+  if (!first_pos && max_tokens != 1) return fail(SPA_ERR_INVALID, "first_pos NULL requires max_tokens == 1");
+  if ((int64_t)max_tokens > (int64_t)bt.max_pp * pl.P)
+    return fail(SPA_ERR_INVALID, "max_tokens %d exceeds max_pages * physical_page", max_tokens);
+  if (bt.B == 0 || dyn.n == 0) return ok();
+  return hip_status(spa::launch_summary(pl, bt, dyn, first_pos, max_tokens, stream), "page_summary_update launch");
+}
+
+size_t spa_workspace_bytes(const spa_pool* pool, const spa_heads* heads, int32_t batch, int32_t max_pages,
+                           int32_t k_max) {
+  spa::PoolArgs pl;
+  spa::HeadList dyn;
+  int32_t G;
+  uint8_t kind[spa::kMaxKvHeads];
+  const std::string keep = g_last_error;
+  size_t bytes = 0;
+  if (check_pool(pool, &pl) == SPA_OK && check_heads(heads, pl, &G, &dyn, kind) == SPA_OK &&
+      batch >= 0 && max_pages >= 1 && k_max >= 1) {
+    spa::AttnPlan plan;
+    plan_attention(pl, heads, k_max, kind, &plan);
+    size_t ml_off;
+    bytes = std::max(attn_bytes(pl, plan, batch, G, &ml_off), select_bytes(pl, batch, max_pages));
+    bytes = std::max<size_t>(bytes, 256);
+  }
+  g_last_error = keep;
+  return bytes;
+}
+
+spa_status spa_select_pages(const spa_pool* pool, const spa_heads* heads, const spa_batch* batch,
+                            const void* q, const int32_t* budget_tokens, int32_t k_max,
+                            int32_t* sel_pages, int32_t* sel_count, int32_t* sel_len, float* scores,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+  spa::PoolArgs pl;
+  spa::BatchArgs bt;
+  spa::HeadList dyn;
+  int32_t G;
+  spa_status s;
+  if ((s = check_pool(pool, &pl)) != SPA_OK) return s;
+  if ((s = check_heads(heads, pl, &G, &dyn, nullptr)) != SPA_OK) return s;
+  if ((s = check_batch(batch, pl, &bt)) != SPA_OK) return s;
+  if (k_max < 1) return fail(SPA_ERR_INVALID, "k_max %d < 1", k_max);
+  const int32_t n_max = n_max_pages(pl, bt.max_pp);
+  if (n_max > kMaxScoredPages)
+    return fail(SPA_ERR_UNSUPPORTED, "max_pages * P / p = %d logical pages exceeds %lld", n_max,
+                (long long)kMaxScoredPages);
+  if ((int64_t)bt.B * dyn.n > 2147483647LL / 1) return fail(SPA_ERR_INVALID, "too many heads");
+  if (bt.B == 0 || dyn.n == 0) return ok();
+  if (!q || !budget_tokens || !sel_pages || !sel_count || !sel_len)
+    return fail(SPA_ERR_INVALID, "q / budget_tokens / sel_pages / sel_count / sel_len is NULL");
+  float* sc = scores;
+  if (!sc) {
+    if (!ws || ws_bytes < select_bytes(pl, bt.B, bt.max_pp))
+      return fail(SPA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes,
+                  select_bytes(pl, bt.B, bt.max_pp));
+    sc = static_cast<float*>(ws);
+  }
+  return hip_status(spa::launch_select(pl, bt, dyn, G, static_cast<const uint16_t*>(q), budget_tokens, k_max,
+                                       sel_pages, sel_count, sel_len, sc, n_max, stream),
+                    "select_pages launch");
+}
+
+spa_status spa_sparse_decode_attn(const spa_pool* pool, const spa_heads* heads, const spa_batch* batch,
+                                  const void* q, const int32_t* sel_pages, const int32_t* sel_count,
+                                  const int32_t* sel_len, int32_t k_max, float* out, float* lse, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  spa::PoolArgs pl;
+  spa::BatchArgs bt;
+  spa::HeadList dyn;
+  int32_t G;
+  uint8_t kind[spa::kMaxKvHeads];
+  spa_status s;
+  if ((s = check_pool(pool, &pl)) != SPA_OK) return s;
+  if ((s = check_heads(heads, pl, &G, &dyn, kind)) != SPA_OK) return s;
+  if ((s = check_batch(batch, pl, &bt)) != SPA_OK) return s;
+  if (k_max < 1) return fail(SPA_ERR_INVALID, "k_max %d < 1", k_max);
+  if (bt.B == 0) return ok();
+  if (!q || !out) return fail(SPA_ERR_INVALID, "q / out is NULL");
+  if (dyn.n > 0 && (!sel_pages || !sel_count || !sel_len))
+    return fail(SPA_ERR_INVALID, "dynamic heads need sel_pages / sel_count / sel_len");
+  spa::AttnPlan plan;
+  plan_attention(pl, heads, k_max, kind, &plan);
+  if ((int64_t)bt.B * plan.items_per_seq > INT32_MAX) return fail(SPA_ERR_INVALID, "grid too large");
+  size_t ml_off;
+  const size_t need = attn_bytes(pl, plan, bt.B, G, &ml_off);
+  if (!ws || ws_bytes < need) return fail(SPA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
+  float* part_o = static_cast<float*>(ws);
+  float* part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + ml_off);
+  return hip_status(spa::launch_attn(pl, bt, plan, G, static_cast<const uint16_t*>(q), sel_pages, sel_count,
+                                     sel_len, out, lse, part_o, part_ml, stream),
+                    "sparse_decode_attn launch");
+}
+
+// ------------------------------------------------------------- allocator
+
+struct spa_allocator {
+  std::vector<int32_t> free_list;    // stack: back() is handed out next
+  std::vector<uint8_t> in_use;
+};
+
+spa_status spa_alloc_create(int32_t num_pages, spa_allocator** out) {
+  if (!out) return fail(SPA_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  if (num_pages < 1) return fail(SPA_ERR_INVALID, "num_pages %d < 1", num_pages);
+  spa_allocator* a = new (std::nothrow) spa_allocator;
+  if (!a) return fail(SPA_ERR_INVALID, "out of host memory");
+  a->free_list.resize(num_pages);
+  for (int32_t i = 0; i < num_pages; ++i) a->free_list[i] = num_pages - 1 - i;   // lowest id on top
+  a->in_use.assign(num_pages, 0);
+  *out = a;
+  return ok();
+}
+
+spa_status spa_alloc_pages(spa_allocator* a, int32_t count, int32_t* ids_out) {
+  if (!a) return fail(SPA_ERR_INVALID, "allocator is NULL");
+  if (count < 0) return fail(SPA_ERR_INVALID, "count %d < 0", count);
+  if (count > 0 && !ids_out) return fail(SPA_ERR_INVALID, "ids_out is NULL");
+  if ((size_t)count > a->free_list.size())
+    return fail(SPA_ERR_POOL_EXHAUSTED, "No free pages available: %d requested, %zu free", count,
+                a->free_list.size());
+  for (int32_t i = 0; i < count; ++i) {
+    const int32_t id = a->free_list.back();
+    a->free_list.pop_back();
+    a->in_use[id] = 1;
+    ids_out[i] = id;
+  }
+  return ok();
+}
+
+spa_status spa_alloc_free(spa_allocator* a, int32_t count, const int32_t* ids) {
+  if (!a) return fail(SPA_ERR_INVALID, "allocator is NULL");
+  if (count < 0) return fail(SPA_ERR_INVALID, "count %d < 0", count);
+  if (count > 0 && !ids) return fail(SPA_ERR_INVALID, "ids is NULL");
+  std::vector<uint8_t> seen;
+  for (int32_t i = 0; i < count; ++i) {
+    const int32_t id = ids[i];
+    if (id < 0 || (size_t)id >= a->in_use.size()) return fail(SPA_ERR_INVALID, "page id %d out of range", id);
+    if (!a->in_use[id]) return fail(SPA_ERR_INVALID, "page %d is not allocated", id);
+    if (seen.empty()) seen.assign(a->in_use.size(), 0);
+    if (seen[id]) return fail(SPA_ERR_INVALID, "page %d freed twice in one call", id);
+    seen[id] = 1;
+  }
+  for (int32_t i = 0; i < count; ++i) {
+    a->in_use[ids[i]] = 0;
+    a->free_list.push_back(ids[i]);
+  }
+  return ok();
+}
+
+int32_t spa_alloc_num_free(const spa_allocator* a) { return a ? (int32_t)a->free_list.size() : -1; }
+
+void spa_alloc_destroy(spa_allocator* a) { delete a; }
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Internal declarations shared by the host dispatch (api.cpp) and the kernel
+// files. Not part of the public ABI (include/spa.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spa {
+
+constexpr int kHeadDim = 128;       // D
+constexpr int kBlockTokens = 16;    // tokens per attention block (MFMA M/K tile)
+constexpr int kMaxKvHeads = 128;
+
+// Pool geometry and base pointers, passed by value to every kernel.
+struct PoolArgs {
+  int32_t hkv;      // KV heads
+  int32_t p;        // logical page (tokens)
+  int32_t P;        // physical page (tokens)
+  int32_t r;        // P / p
+  int32_t N;        // physical pages
+  uint16_t* k;      // [N][hkv][P][D]
+  uint16_t* v;      // [N][hkv][r][D][p]
+  uint16_t* summ;   // [N][hkv][r][2][D]
+};
+
+struct BatchArgs {
+  int32_t B;
+  int32_t max_pp;
+  const int32_t* pt;    // [B][max_pp]
+  const int32_t* lens;  // [B]
+};
+
+// A list of KV-head ids (dynamic heads for selection / summaries).
+struct HeadList {
+  int32_t n;
+  int16_t id[kMaxKvHeads];
+};
+
+// Work plan of the attention launch. Items are numbered per sequence: the
+// items of KV head h are [item_base[h], item_base[h+1]).
+struct AttnPlan {
+  int32_t items_per_seq;        // item_base[hkv]
+  int32_t items_stream;         // items per streaming head
+  int32_t items_dyn;            // items per dynamic head (the last one is the tail item)
+  int32_t blocks_per_item;      // 16-token blocks per item
+  int32_t item_stride;          // max(items_stream, items_dyn): partial slots per head
+  int32_t sink, window;
+  int32_t k_max;
+  uint8_t kind[kMaxKvHeads];
+  int32_t item_base[kMaxKvHeads + 1];
+};
+
+// ---- launchers (return hipError_t of the launch) -------------------------
+hipError_t launch_append(const PoolArgs& pool, const BatchArgs& batch,
+                         const uint16_t* k_new, const uint16_t* v_new, hipStream_t s);
+hipError_t launch_write(const PoolArgs& pool, const int32_t* pt_row, int32_t max_pp,
+                        int64_t start, int64_t count, const uint16_t* k,
+                        const uint16_t* v, hipStream_t s);
+hipError_t launch_summary(const PoolArgs& pool, const BatchArgs& batch, const HeadList& dyn,
+                          const int32_t* first_pos, int32_t max_tokens, hipStream_t s);
+hipError_t launch_select(const PoolArgs& pool, const BatchArgs& batch, const HeadList& dyn,
+                         int32_t G, const uint16_t* q, const int32_t* budget, int32_t k_max,
+                         int32_t* sel_pages, int32_t* sel_count, int32_t* sel_len,
+                         float* scores, int32_t n_max, hipStream_t s);
+hipError_t launch_attn(const PoolArgs& pool, const BatchArgs& batch, const AttnPlan& plan,
+                       int32_t G, const uint16_t* q, const int32_t* sel_pages,
+                       const int32_t* sel_count, const int32_t* sel_len, float* out,
+                       float* lse, float* part_o, float* part_ml, hipStream_t s);
+
+}  // namespace spa

@@ -1,0 +1,156 @@
+"""GPU-vs-oracle parity harness (imported by the GPU tests and the smoke check).
+
+Runs a workload's decode steps through the library (DecodeLayer over the C
+ABI) and the same steps through the CPU oracle on the same seeded inputs, and
+compares
+  - selected page ids: bit-exact, except where the oracle's k-th and
+    (k+1)-th page scores are within 1e-6 relative (a near tie); then the
+    oracle's attention is recomputed with the GPU's selection so the output
+    check still runs;
+  - page scores: bit-exact fp32 (both are the rounded exact bound);
+  - outputs: max |gpu - oracle| <= 2e-3 (bf16 inputs, fp32 accumulation);
+  - lse: max |gpu - oracle| <= 1e-3.
+"""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+import torch
+
+import oracle
+import workloads as W
+from sparse_paged_attention_amd.runner import DecodeLayer
+
+OUT_TOL = 2e-3
+LSE_TOL = 1e-3
+TIE_REL = 1e-6
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def bits_to_bf16(a: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+class ParityRun:
+    """A workload on the GPU plus the oracle state needed to check it."""
+
+    def __init__(self, wl: W.Workload, check_heads=None, threads: int = 16):
+        self.wl = wl
+        self.check = check_heads if check_heads is not None else \
+            [(b, h) for b in range(wl.batch) for h in range(wl.hkv)]
+        pt = W.page_table(wl)
+        self.layer = DecodeLayer(hq=wl.hq, hkv=wl.hkv, p=wl.p, P=wl.P, kind=wl.kind, sink=wl.sink,
+                                 window=wl.window, page_table=pt, num_phys_pages=wl.num_phys_pages,
+                                 k_max=wl.k_max)
+        self.K, self.V = {}, {}          # host bits of the checked (b, h) slices
+        self.new_k, self.new_v = [], []  # per sequence: [H_kv][steps][D] appended tokens
+        need = {(b, h) for b, h in self.check}
+        for b in range(wl.batch):
+            Kb = W.kv_all(wl, b, "k", threads)
+            Vb = W.kv_all(wl, b, "v", threads)
+            pre = wl.contexts[b] - 1
+            if pre > 0:
+                self.layer.write_tokens(b, 0, bits_to_bf16(Kb[:, :pre]), bits_to_bf16(Vb[:, :pre]))
+            self.new_k.append(Kb[:, pre:pre + wl.steps].copy())
+            self.new_v.append(Vb[:, pre:pre + wl.steps].copy())
+            for h in range(wl.hkv):
+                if (b, h) in need:
+                    self.K[(b, h)] = Kb[h]
+                    self.V[(b, h)] = Vb[h]
+            del Kb, Vb
+        self.layer.set_lengths([c - 1 for c in wl.contexts])
+        if any(wl.kind):
+            self.layer.rebuild_summaries()
+        torch.cuda.synchronize()
+        self.state = {(b, h): oracle.HeadState(wl.k_max) for b, h in self.check}
+        self.scores = torch.full((wl.batch, wl.hkv, pt.shape[1] * (wl.P // wl.p)), float("nan"),
+                                 dtype=torch.float32, device="cuda")
+
+    def step_inputs(self, i: int):
+        wl = self.wl
+        q = np.stack([W.query(wl, b, i) for b in range(wl.batch)])
+        kn = np.stack([self.new_k[b][:, i] for b in range(wl.batch)])
+        vn = np.stack([self.new_v[b][:, i] for b in range(wl.batch)])
+        return q, kn, vn
+
+    def run_step(self, i: int) -> dict:
+        wl, layer = self.wl, self.layer
+        q, kn, vn = self.step_inputs(i)
+        lens = np.array([wl.seq_len(b, i) for b in range(wl.batch)], np.int32)
+        layer.set_lengths(lens)
+        layer.set_budget([wl.budget_at(int(L)) for L in lens])
+        qd = bits_to_bf16(q)
+        layer.append(bits_to_bf16(kn), bits_to_bf16(vn))
+        select = wl.selects_at(i)
+        if select:
+            layer.select(qd, scores=self.scores)
+        layer.attend(qd)
+        torch.cuda.synchronize()
+        out = layer.out.cpu().numpy().astype(np.float64)
+        lse = layer.lse.cpu().numpy().astype(np.float64)
+        sel = layer.sel_pages.cpu().numpy()
+        cnt = layer.sel_count.cpu().numpy()
+        scores = self.scores.cpu().numpy() if select else None
+        report = dict(step=i, select=select, max_err=0.0, max_lse_err=0.0, ties=0, sel_checked=0,
+                      score_mismatch=0)
+        G = wl.G
+        for b, h in self.check:
+            L = int(lens[b])
+            dyn = bool(wl.kind[h])
+            st = self.state[(b, h)]
+            qg = q[b, h * G:(h + 1) * G]
+            K, V = self.K[(b, h)][:L], self.V[(b, h)][:L]
+            o_out, o_lse, o_scores = oracle.decode_head(
+                K, V, qg, dynamic=dyn, sink=wl.sink, window=wl.window, p=wl.p,
+                budget=wl.budget_at(L), do_select=select, state=st, want_scores=True)
+            if dyn and select:
+                n = -(-L // wl.p)
+                gs = scores[b, h, :n]
+                report["score_mismatch"] += int((gs.view(np.uint32) != o_scores.view(np.uint32)).sum())
+                gsel = sel[b, h, :cnt[b, h]]
+                osel = st.pages
+                report["sel_checked"] += 1
+                if not np.array_equal(gsel, osel):
+                    k = osel.size
+                    srt = np.sort(o_scores)[::-1]
+                    near_tie = k < srt.size and abs(srt[k - 1] - srt[k]) <= TIE_REL * abs(srt[k - 1])
+                    if not near_tie:
+                        raise AssertionError(
+                            f"{wl.name} step {i} b{b} h{h}: selection differs "
+                            f"(gpu {gsel.size} pages, oracle {osel.size}; "
+                            f"first diff {np.setdiff1d(gsel, osel)[:5]} vs {np.setdiff1d(osel, gsel)[:5]})")
+                    report["ties"] += 1
+                    st.sel[:gsel.size] = gsel
+                    st.nsel[0] = gsel.size
+                    o_out, o_lse, _ = oracle.decode_head(
+                        K, V, qg, dynamic=True, sink=wl.sink, window=wl.window, p=wl.p,
+                        budget=wl.budget_at(L), do_select=False, state=st)
+            err = float(np.abs(out[b, h * G:(h + 1) * G] - o_out).max())
+            lerr = float(np.abs(lse[b, h * G:(h + 1) * G] - o_lse).max())
+            report["max_err"] = max(report["max_err"], err)
+            report["max_lse_err"] = max(report["max_lse_err"], lerr)
+        return report
+
+    def run(self, steps: int | None = None) -> list:
+        reps = []
+        for i in range(self.wl.steps if steps is None else steps):
+            t = time.time()
+            r = self.run_step(i)
+            log(f"  {self.wl.name} step {i}: select={r['select']} max_err={r['max_err']:.2e} "
+                f"lse_err={r['max_lse_err']:.2e} ties={r['ties']} score_mismatch={r['score_mismatch']} "
+                f"({time.time() - t:.1f}s)")
+            reps.append(r)
+        return reps
+
+
+def assert_reports(reps: list) -> None:
+    for r in reps:
+        assert r["score_mismatch"] == 0, r
+        assert r["max_err"] <= OUT_TOL, r
+        assert r["max_lse_err"] <= LSE_TOL, r

@@ -1,0 +1,171 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry
+point declared in include/spa.h, and rejects bad arguments on the host before
+anything is launched (every call below fails validation, so no kernel runs and
+no device memory is touched, with or without a GPU)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def spa():
+    import sparse_paged_attention_amd as spa
+    if not os.path.exists(spa.LIB_PATH):
+        from sparse_paged_attention_amd import _build
+        _build.build_library()
+    spa.lib()
+    return spa
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "spa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(spa_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function(spa):
+    names = header_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(spa.lib(), n), n
+    assert set(names) == set(spa.EXPORTS)
+
+
+def test_default_budget_matches_page_rule(spa):
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "budget_rule.json")))
+    for L, b in g["pairs"]:
+        assert spa.default_budget(L) == b
+    assert spa.default_budget(-5) == 0
+
+
+def test_status_strings(spa):
+    for s in range(6):
+        assert spa.lib().spa_status_string(s)
+
+
+def test_allocator_free_list(spa):
+    a = spa.Allocator(8)
+    assert a.num_free == 8
+    ids = a.alloc(3)
+    assert ids == [0, 1, 2]
+    assert a.num_free == 5
+    with pytest.raises(spa.PoolExhausted) as e:
+        a.alloc(6)
+    assert "No free pages" in str(e.value)
+    assert a.num_free == 5                      # all-or-nothing
+    a.free([1])
+    assert a.alloc(1) == [1]                    # last freed is handed out first
+    with pytest.raises(spa.SpaError):
+        a.free([7])                             # not allocated
+    with pytest.raises(spa.SpaError):
+        a.free([0, 0])                          # twice in one call
+    assert a.num_free == 5
+    with pytest.raises(spa.SpaError):
+        a.free([99])
+    a.free([0, 1, 2])
+    assert a.num_free == 8
+    assert sorted(a.alloc(8)) == list(range(8))
+    with pytest.raises(spa.SpaError):
+        spa.Allocator(0)
+
+
+FAKE = 0x1000   # never dereferenced: every call below fails validation first
+
+
+def mkpool(spa, **kw):
+    d = dict(num_kv_heads=8, head_dim=128, logical_page=16, physical_page=64, num_phys_pages=10,
+             k_pool=FAKE, v_pool=FAKE, summary=FAKE)
+    d.update(kw)
+    return spa.c_pool(**d)
+
+
+def mkheads(spa, hq=32, sink=64, window=1024, kind=(0, 0, 0, 0, 1, 1, 1, 1)):
+    arr = (ctypes.c_uint8 * len(kind))(*kind)
+    h = spa.c_heads(hq, sink, window, ctypes.cast(arr, ctypes.POINTER(ctypes.c_uint8)))
+    h._keep = arr
+    return h
+
+
+def mkbatch(spa, B=1, mp=4, pt=FAKE, lens=FAKE):
+    return spa.c_batch(B, mp, pt, lens)
+
+
+def attn(spa, pool, heads, batch, q=FAKE, sel=FAKE, k_max=8, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return spa.lib().spa_sparse_decode_attn(ctypes.byref(pool), ctypes.byref(heads), ctypes.byref(batch),
+                                            q, sel, sel, sel, k_max, out, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(head_dim=64), 2), (dict(head_dim=0), 1), (dict(logical_page=8), 2),
+    (dict(logical_page=128, physical_page=256), 1), (dict(physical_page=40), 1),
+    (dict(logical_page=16, physical_page=16 * 65), 1), (dict(num_phys_pages=0), 1),
+    (dict(k_pool=None), 1), (dict(num_kv_heads=0), 1), (dict(num_kv_heads=200), 1),
+    (dict(summary=None), 1),
+])
+def test_pool_validation(spa, bad, status):
+    pool = mkpool(spa, **bad)
+    kind = (0,) * pool.num_kv_heads if pool.num_kv_heads in (0, 200) else (0, 0, 0, 0, 1, 1, 1, 1)
+    heads = mkheads(spa, kind=kind[:8] if len(kind) >= 8 else kind)
+    assert attn(spa, pool, heads, mkbatch(spa)) == status
+    assert spa.lib().spa_last_error()
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(hq=20), 1), (dict(hq=8 * 3), 2), (dict(hq=8 * 32), 2), (dict(hq=0), 1), (dict(sink=-1), 1),
+    (dict(window=0), 1), (dict(kind=(0, 0, 0, 0, 1, 1, 1, 2)), 1),
+])
+def test_heads_validation(spa, bad, status):
+    assert attn(spa, mkpool(spa), mkheads(spa, **bad), mkbatch(spa)) == status
+
+
+def test_batch_and_buffer_validation(spa):
+    pool, heads = mkpool(spa), mkheads(spa)
+    assert attn(spa, pool, heads, mkbatch(spa, B=-1)) == 1
+    assert attn(spa, pool, heads, mkbatch(spa, mp=0)) == 1
+    assert attn(spa, pool, heads, mkbatch(spa, pt=None)) == 1
+    assert attn(spa, pool, heads, mkbatch(spa), q=None) == 1
+    assert attn(spa, pool, heads, mkbatch(spa), out=None) == 1
+    assert attn(spa, pool, heads, mkbatch(spa), sel=None) == 1
+    assert attn(spa, pool, heads, mkbatch(spa), k_max=0) == 1
+    assert attn(spa, pool, heads, mkbatch(spa), ws_bytes=16) == 4
+    assert attn(spa, pool, heads, mkbatch(spa), ws=None) == 4
+    # an empty batch is a no-op that succeeds without touching anything
+    assert attn(spa, pool, heads, mkbatch(spa, B=0, pt=None, lens=None)) == 0
+
+
+def test_workspace_bytes(spa):
+    pool, heads = mkpool(spa), mkheads(spa)
+    n = spa.lib().spa_workspace_bytes(ctypes.byref(pool), ctypes.byref(heads), 4, 2049, 256)
+    assert n >= 4 * 8 * 2049 * 4 * 4          # page scores of every head
+    assert n % 256 == 0
+    bad = mkpool(spa, head_dim=64)
+    assert spa.lib().spa_workspace_bytes(ctypes.byref(bad), ctypes.byref(heads), 4, 2049, 256) == 0
+
+
+def test_select_and_summary_validation(spa):
+    L = spa.lib()
+    pool, heads, batch = mkpool(spa), mkheads(spa), mkbatch(spa)
+    args = lambda **o: [ctypes.byref(o.get("pool", pool)), ctypes.byref(heads), ctypes.byref(batch),
+                        o.get("q", FAKE), o.get("budget", FAKE), o.get("k_max", 8), FAKE, FAKE, FAKE,
+                        None, o.get("ws", FAKE), o.get("ws_bytes", 1 << 30), None]
+    assert L.spa_select_pages(*args(k_max=0)) == 1
+    assert L.spa_select_pages(*args(q=None)) == 1
+    assert L.spa_select_pages(*args(budget=None)) == 1
+    assert L.spa_select_pages(*args(ws_bytes=8)) == 4
+    big = mkbatch(spa, mp=20000)
+    assert L.spa_select_pages(ctypes.byref(pool), ctypes.byref(heads), ctypes.byref(big), FAKE, FAKE, 8,
+                              FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None) == 2
+    assert L.spa_page_summary_update(ctypes.byref(pool), ctypes.byref(heads), ctypes.byref(batch),
+                                     None, 5, None) == 1
+    assert L.spa_page_summary_update(ctypes.byref(pool), ctypes.byref(heads), ctypes.byref(batch),
+                                     FAKE, 0, None) == 1
+    assert L.spa_kv_pool_append(ctypes.byref(pool), ctypes.byref(batch), None, FAKE, None) == 1
+    assert L.spa_kv_pool_write(ctypes.byref(pool), FAKE, 4, 250, 10, FAKE, FAKE, None) == 1
+    assert L.spa_kv_pool_write(ctypes.byref(pool), FAKE, 4, -1, 1, FAKE, FAKE, None) == 1
+    assert L.spa_kv_pool_write(ctypes.byref(pool), None, 4, 0, 1, FAKE, FAKE, None) == 1
+    assert L.spa_kv_pool_write(ctypes.byref(pool), FAKE, 4, 0, 0, FAKE, FAKE, None) == 0

@@ -1,0 +1,118 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs. Every test here needs an MI355X and the built library."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity import ParityRun, assert_reports, bits_to_bf16, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_paged_attention_amd as spa
+    spa.lib()
+    oracle.build()
+
+
+def run(wl, steps=None, check=None):
+    log(f"[parity] {wl.name} B={wl.batch} hq={wl.hq} hkv={wl.hkv} p={wl.p} P={wl.P} "
+        f"contexts={wl.contexts[:4]} steps={wl.steps if steps is None else steps}")
+    pr = ParityRun(wl, check_heads=check)
+    reps = pr.run(steps)
+    assert_reports(reps)
+    return pr, reps
+
+
+# ------------------------------------------------------------ pool layout
+
+def test_pool_write_append_and_summaries_bit_exact():
+    wl = W.WORKLOADS["toy_4k"].scaled(contexts=(300, 77, 1), batch=3, steps=3, permute=True,
+                                      kind=(1, 1), planted=None)
+    pr = ParityRun(wl, check_heads=[])
+    layer = pr.layer
+    for i in range(wl.steps):
+        q, kn, vn = pr.step_inputs(i)
+        layer.set_lengths([wl.seq_len(b, i) for b in range(wl.batch)])
+        layer.append(bits_to_bf16(kn), bits_to_bf16(vn))
+    torch.cuda.synchronize()
+    kp = layer.pool.k.view(torch.int16).cpu().numpy().view(np.uint16)
+    vp = layer.pool.v.view(torch.int16).cpu().numpy().view(np.uint16)
+    sp = layer.pool.summary.view(torch.int16).cpu().numpy().view(np.uint16)
+    pt = W.page_table(wl)
+    p, P, r = wl.p, wl.P, wl.P // wl.p
+    for b in range(wl.batch):
+        L = wl.final_len(b)
+        for h in range(wl.hkv):
+            K = W.kv(wl, b, h, "k")[:L]
+            V = W.kv(wl, b, h, "v")[:L]
+            t = np.arange(L)
+            phys = pt[b, t // P]
+            slot = t % P
+            np.testing.assert_array_equal(kp[phys, h, slot], K)
+            np.testing.assert_array_equal(vp[phys, h, slot // p, :, slot % p], V)
+            kmin, kmax = oracle.page_summary(K, p)
+            j = np.arange(kmin.shape[0])
+            np.testing.assert_array_equal(sp[pt[b, j // r], h, j % r, 0], kmin)
+            np.testing.assert_array_equal(sp[pt[b, j // r], h, j % r, 1], kmax)
+
+
+# ------------------------------------------------------ the five workloads
+
+def test_toy_4k():
+    run(W.WORKLOADS["toy_4k"])
+
+
+def test_llama3_32k_massive_activations():
+    run(W.WORKLOADS["llama3_32k"])
+
+
+def test_single_256k_p32():
+    run(W.WORKLOADS["single_256k"])
+
+
+def test_llama3_128k_reuse_small():
+    """The 128K workload's shape and step schedule at small contexts: batch 4,
+    shuffled pool, selection every 4 steps, 9 steps (tail of up to 3 tokens)."""
+    wl = W.WORKLOADS["llama3_128k"].scaled(contexts=(4100, 3001, 1000, 17), steps=9, budget=512,
+                                           window=300)
+    run(wl)
+
+
+def test_ragged_mha_small():
+    wl = W.WORKLOADS["ragged_mha"].scaled(contexts=(2500, 40, 1800, 3333, 700, 16, 1, 2049),
+                                          batch=8, steps=6)
+    run(wl)
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 8), (64, 8), (32, 2)])
+def test_group_sizes(hq, hkv):
+    kind = tuple(h % 2 for h in range(hkv))
+    wl = W.Workload(f"g{hq // hkv}", 2000 + hq, 2, hq, hkv, 16, 64, (1500, 999), 5, 2, kind, 32, 200,
+                    256, True)
+    run(wl)
+
+
+def test_p64_and_dense_budget():
+    """p = 64 pages; the budget covers the context, so the dynamic head is dense."""
+    wl = W.Workload("p64", 2100, 2, 8, 2, 64, 256, (700, 300), 3, 1, (0, 1), 8, 5000, 8192, True)
+    run(wl)
+
+
+def test_short_sequences_streaming_dense():
+    """L <= sink + window: streaming heads attend everything."""
+    wl = W.Workload("short", 2200, 3, 32, 8, 16, 64, (1, 30, 65), 4, 2, (0, 1) * 4, 64, 1024, 4096,
+                    False)
+    run(wl)
+
+
+def test_llama3_128k_full_size_sampled():
+    """The configuration the benchmark times, at full size: 4 x 131072 + 16
+    steps, shuffled pool, reuse every 4 steps; checked on sampled heads."""
+    wl = W.WORKLOADS["llama3_128k"]
+    run(wl, check=[(0, 0), (0, 4), (1, 5), (2, 3), (3, 7)])

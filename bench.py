@@ -1,0 +1,284 @@
+"""Benchmark: sparse paged decode attention at 128K context on one MI355X.
+
+Workload (the 128K decode configuration of the LServe write-up's latency
+table, bqwf.cn "3.2", at Llama-3-8B attention shape): 4 sequences of 131072
+tokens, 32 query / 8 KV heads, head_dim 128, logical pages of 16 inside
+physical pages of 64 shuffled over the pool, KV heads 0-3 streaming (sink 64 +
+window 2048), 4-7 dynamic with a 4096-token budget, page selection every 4
+decode steps. Inputs are synthetic (seeded N(0,1) bf16) and resident in HBM.
+
+A step is one pass of the whole hot path for one attention layer: append the
+new token, refresh its page summary, select pages (every 4th decode step),
+sparse decode attention for all heads. To keep the timing honest about HBM
+(a step touches 51-118 MB, less than the 256 MB last-level cache), the layer
+is replicated R times with separate pools and consecutive steps cycle through
+the replicas, as the layers of a model do; the timed steps are replayed from
+a HIP graph.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse decode-attn µs/step + achieved HBM GB/s (% peak) at 128K ctx"
+PEAK_GBPS = 8000.0
+WORKLOAD = "llama3_128k"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(wl, L: int, select: bool) -> dict:
+    """Bytes the method must move in one layer-step, per part (all sequences
+    at length L). K/V rows are 256 B each, summaries 512 B per page."""
+    D2 = wl.d * 2
+    n_dyn = sum(wl.kind)
+    n_str = wl.hkv - n_dyn
+    B = wl.batch
+    s0 = min(wl.sink, L)
+    w0 = max(wl.sink, L - wl.window)
+    t_stream = s0 + max(0, L - w0)
+    n = -(-L // wl.p)
+    k = min(n, max(1, wl.budget_at(L) // wl.p))
+    t_dyn = k * wl.p                        # selected pages are full pages here
+    q_bytes = B * wl.hq * D2
+    out_bytes = B * wl.hq * (wl.d * 4 + 4)
+    attn = B * (n_str * t_stream + n_dyn * t_dyn) * 2 * D2 + q_bytes + out_bytes \
+        + B * n_dyn * k * 4 + B * (L // wl.P + 1) * 4
+    append = B * wl.hkv * D2 * 2 * 2                       # read new rows, write them
+    summary = B * n_dyn * (D2 + 2 * 2 * D2)                 # new key + read/write min/max
+    sel = 0
+    if select:
+        sel = B * n_dyn * n * 2 * D2 + q_bytes + B * n_dyn * n * 4 * 2 + B * n_dyn * k * 4
+    return dict(attn=attn, append=append, summary=summary, select=sel,
+                total=attn + append + summary + sel)
+
+
+def cpu_baseline(wl, host_kv, sample_steps: int = 4) -> dict:
+    """The CPU oracle on a bounded sample: `sample_steps` decode steps
+    (one selection + reuse) of every sequence and KV head of one layer,
+    scaled to microseconds per layer-step."""
+    import oracle
+    import workloads as W
+    oracle.build()
+    G = wl.G
+    states = {(b, h): oracle.HeadState(wl.k_max) for b in range(wl.batch) for h in range(wl.hkv)}
+    t0 = time.perf_counter()
+    for i in range(sample_steps):
+        jobs = []
+        for b in range(wl.batch):
+            L = wl.seq_len(b, i)
+            q = W.query(wl, b, i)
+            K, V = host_kv[b]
+            for h in range(wl.hkv):
+                jobs.append(dict(K=K[h, :L], V=V[h, :L], q=q[h * G:(h + 1) * G], dynamic=bool(wl.kind[h]),
+                                 sink=wl.sink, window=wl.window, p=wl.p, budget=wl.budget_at(L),
+                                 do_select=wl.selects_at(i), state=states[(b, h)]))
+        oracle.decode_heads(jobs)
+    dt = time.perf_counter() - t0
+    return {"value": round(dt / sample_steps * 1e6, 1), "unit": "us/step", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{sample_steps} decode steps (1 selection + {sample_steps - 1} reuse) of all "
+                      f"{wl.batch} sequences x {wl.hkv} KV heads of one layer, fp64 oracle, "
+                      f"{dt:.1f} s total"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64, help="timed layer-steps")
+    ap.add_argument("--warmup", type=int, default=16, help="untimed layer-steps before")
+    ap.add_argument("--replicas", type=int, default=8, help="layer replicas the steps cycle over")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--threads", type=int, default=16)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path keeps every "
+              f"head on its own GPU and has no multi-GPU run.", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads as W
+    import sparse_paged_attention_amd as spa
+    from sparse_paged_attention_amd.runner import DecodeLayer
+
+    spa.lib()
+    torch.cuda.set_device(0)
+    wl = W.WORKLOADS[WORKLOAD]
+    R = args.replicas
+    total_steps = args.warmup + args.steps
+    n_decode = -(-total_steps // R)
+    if n_decode > wl.steps:
+        raise SystemExit(f"at most {wl.steps * R} layer-steps with {R} replicas")
+
+    t_setup = time.time()
+    pt = W.page_table(wl)
+    layers = [DecodeLayer(hq=wl.hq, hkv=wl.hkv, p=wl.p, P=wl.P, kind=wl.kind, sink=wl.sink,
+                          window=wl.window, page_table=pt, num_phys_pages=wl.num_phys_pages,
+                          k_max=wl.k_max) for _ in range(R)]
+    host_kv = []
+    newk = np.zeros((wl.steps, wl.batch, wl.hkv, wl.d), np.uint16)
+    newv = np.zeros_like(newk)
+    for b in range(wl.batch):
+        K = W.kv_all(wl, b, "k", args.threads)
+        V = W.kv_all(wl, b, "v", args.threads)
+        pre = wl.contexts[b] - 1
+        Kd = torch.from_numpy(K[:, :pre].view(np.int16)).cuda().view(torch.bfloat16)
+        Vd = torch.from_numpy(V[:, :pre].view(np.int16)).cuda().view(torch.bfloat16)
+        for layer in layers:
+            layer.write_tokens(b, 0, Kd, Vd)
+        del Kd, Vd
+        newk[:, b] = K[:, pre:pre + wl.steps].transpose(1, 0, 2)
+        newv[:, b] = V[:, pre:pre + wl.steps].transpose(1, 0, 2)
+        host_kv.append((K, V))
+        log(f"[bench] sequence {b} written to {R} pools")
+    for layer in layers:
+        layer.set_lengths([c - 1 for c in wl.contexts])
+        layer.rebuild_summaries()
+        layer.set_budget([wl.budget_at(c) for c in wl.contexts])
+    torch.cuda.synchronize()
+
+    def dev(a, dtype=torch.bfloat16):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(dtype)
+
+    # per decode step: lengths, new tokens; per layer-step: q
+    lens = [torch.tensor([wl.seq_len(b, t) for b in range(wl.batch)], dtype=torch.int32, device="cuda")
+            for t in range(n_decode)]
+    kn = [dev(newk[t]) for t in range(n_decode)]
+    vn = [dev(newv[t]) for t in range(n_decode)]
+    qs = [dev(np.stack([W.query(wl, b, t * R + r) for b in range(wl.batch)]))
+          for t in range(n_decode) for r in range(R)]
+    log(f"[bench] setup {time.time() - t_setup:.1f}s; {R} replicas x "
+        f"{layers[0].pool.k.numel() * 2 * 2 / 2**30:.2f} GiB K+V")
+
+    def layer_step(s: int, timed_attn=None):
+        t, r = divmod(s, R)
+        layer = layers[r]
+        layer.use_lengths(lens[t])
+        layer.append(kn[t], vn[t])
+        if wl.selects_at(t):
+            layer.select(qs[s])
+        if timed_attn is not None:
+            timed_attn[0].record()
+        layer.attend(qs[s])
+        if timed_attn is not None:
+            timed_attn[1].record()
+
+    # warm-up (eager, also compiles nothing: kernels are prebuilt)
+    for s in range(args.warmup):
+        layer_step(s)
+    torch.cuda.synchronize()
+
+    # capture the timed steps once; replays are idempotent (same tokens are
+    # re-appended at the same positions, selections recomputed identically)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for s in range(args.warmup, total_steps):
+            layer_step(s)
+    g.replay()                                  # one untimed replay
+    torch.cuda.synchronize()
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record()
+    g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = gpu_ms / args.steps
+
+    # per-launch time of the attention call over the same steps, events on
+    # its stream; a sleep kernel keeps the GPU behind the CPU so launches
+    # queue back to back
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    torch.cuda._sleep(int(60e6))
+    for i, s in enumerate(range(args.warmup, total_steps)):
+        layer_step(s, pairs[i])
+    torch.cuda.synchronize()
+    attn_ms = [a.elapsed_time(b) for a, b in pairs]
+    attn_avg_us = 1e3 * sum(attn_ms) / len(attn_ms)
+
+    # algorithmic bytes over the timed steps
+    tot = 0
+    attn_bytes = 0
+    for s in range(args.warmup, total_steps):
+        t = s // R
+        L = wl.seq_len(0, t)
+        ab = algorithmic_bytes(wl, L, wl.selects_at(t))
+        tot += ab["total"]
+        attn_bytes += ab["attn"]
+    bytes_per_step = tot / args.steps
+    attn_bytes_avg = attn_bytes / args.steps
+    gbps = bytes_per_step / (ms_per_step * 1e-3) / 1e9
+    attn_gbps = attn_bytes_avg / (attn_avg_us * 1e-6) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, host_kv)
+
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "attn_llama3_128k_traffic.json")
+    if os.path.exists(tpath):
+        try:
+            tr = json.load(open(tpath))
+            traffic = tr.get("bytes_per_launch") if tr.get("kernel_source_hash") == _attn_hash() else None
+        except Exception:
+            traffic = None
+
+    res = {
+        "metric": METRIC,
+        "value": round(ms_per_step * 1e3, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{WORKLOAD}: batch 4 x 131072 ctx (+1 token/step), 32 q / 8 kv heads, "
+                               f"d 128, logical page 16 / physical 64 shuffled, kv 0-3 streaming "
+                               f"(sink 64 + window 2048), kv 4-7 dynamic budget 4096, select every 4 "
+                               f"steps, {R} layer replicas",
+                   "batch": wl.batch, "context": wl.contexts[0], "replicas": R},
+        "achieved_GBps": round(gbps, 1),
+        "hbm_frac": round(gbps / PEAK_GBPS, 4),
+        "bytes_per_step": int(bytes_per_step),
+        "wall_s_timed": round(wall, 4),
+        "roofline": {"bound": "hbm", "kernel": "spa_sparse_decode_attn (attn_kernel + combine_kernel)",
+                     "achieved": round(attn_gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(attn_gbps / PEAK_GBPS, 4), "traffic": traffic,
+                     "avg_launch_us": round(attn_avg_us, 2), "bytes_per_launch": int(attn_bytes_avg)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def _attn_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("attn.hip", "spa_internal.h"):
+        h.update(open(os.path.join(ROOT, "sparse_paged_attention_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -191,7 +191,10 @@ spa_status spa_sparse_decode_attn(const spa_pool* pool, const spa_heads* heads,
                                   hipStream_t stream);
 
 /* Workspace bytes needed by spa_select_pages and spa_sparse_decode_attn for
- * these shapes (one buffer serves both). Returns 0 for invalid arguments. */
+ * these shapes (one buffer serves both). Returns 0 for invalid arguments.
+ * The workspace must be zero-filled once before its first use (its first
+ * bytes hold per-head counters; every call leaves them at zero again). Calls
+ * that share a workspace must not run concurrently. */
 size_t spa_workspace_bytes(const spa_pool* pool, const spa_heads* heads,
                            int32_t batch, int32_t max_pages, int32_t k_max);
 

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -38,8 +39,16 @@ spa_status hip_status(hipError_t e, const char* what) {
   return fail(SPA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Attention blocks per work item (16 tokens each).
-constexpr int32_t kBlocksPerItem = 8;
+// Attention blocks per work item (16 tokens each): 4, 8 or 16; the
+// SPA_ATTN_BLOCKS_PER_ITEM environment variable overrides the default.
+int32_t blocks_per_item() {
+  static const int32_t v = [] {
+    const char* e = std::getenv("SPA_ATTN_BLOCKS_PER_ITEM");
+    const int32_t x = e ? std::atoi(e) : 0;
+    return (x == 4 || x == 8 || x == 16) ? x : 8;
+  }();
+  return v;
+}
 // Largest page count a selection row can score (top-k keeps 64 keys per thread).
 constexpr int64_t kMaxScoredPages = 65536;
 
@@ -118,7 +127,7 @@ int32_t n_max_pages(const spa::PoolArgs& pl, int32_t max_pp) {
 void plan_attention(const spa::PoolArgs& pl, const spa_heads* heads, int32_t k_max,
                     const uint8_t* kind, spa::AttnPlan* plan) {
   std::memset(plan, 0, sizeof *plan);
-  const int32_t bpi = kBlocksPerItem;
+  const int32_t bpi = blocks_per_item();
   // streaming blocks: sink blocks + window blocks (+1 when the window is unaligned)
   const int64_t nb_stream = (heads->sink + 15) / 16 + (heads->window + 15) / 16 + 1;
   const int64_t nb_dyn = (int64_t)k_max * (pl.p / 16);
@@ -137,6 +146,13 @@ void plan_attention(const spa::PoolArgs& pl, const spa_heads* heads, int32_t k_m
   }
   plan->item_base[pl.hkv] = at;
   plan->items_per_seq = at;
+}
+
+// Workspace layout: [ticket counters: B * H_kv int32, kept zero between calls]
+// then a scratch area shared by selection (page scores) and attention
+// (per-item partials).
+size_t ticket_bytes(const spa::PoolArgs& pl, int32_t B) {
+  return align_up((size_t)B * pl.hkv * sizeof(int32_t));
 }
 
 size_t attn_bytes(const spa::PoolArgs& pl, const spa::AttnPlan& plan, int32_t B, int32_t G, size_t* ml_off) {
@@ -240,7 +256,8 @@ size_t spa_workspace_bytes(const spa_pool* pool, const spa_heads* heads, int32_t
     spa::AttnPlan plan;
     plan_attention(pl, heads, k_max, kind, &plan);
     size_t ml_off;
-    bytes = std::max(attn_bytes(pl, plan, batch, G, &ml_off), select_bytes(pl, batch, max_pages));
+    bytes = ticket_bytes(pl, batch) +
+            std::max(attn_bytes(pl, plan, batch, G, &ml_off), select_bytes(pl, batch, max_pages));
     bytes = std::max<size_t>(bytes, 256);
   }
   g_last_error = keep;
@@ -270,10 +287,10 @@ spa_status spa_select_pages(const spa_pool* pool, const spa_heads* heads, const 
     return fail(SPA_ERR_INVALID, "q / budget_tokens / sel_pages / sel_count / sel_len is NULL");
   float* sc = scores;
   if (!sc) {
-    if (!ws || ws_bytes < select_bytes(pl, bt.B, bt.max_pp))
-      return fail(SPA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes,
-                  select_bytes(pl, bt.B, bt.max_pp));
-    sc = static_cast<float*>(ws);
+    const size_t need = ticket_bytes(pl, bt.B) + select_bytes(pl, bt.B, bt.max_pp);
+    if (!ws || ws_bytes < need)
+      return fail(SPA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
+    sc = reinterpret_cast<float*>(static_cast<char*>(ws) + ticket_bytes(pl, bt.B));
   }
   return hip_status(spa::launch_select(pl, bt, dyn, G, static_cast<const uint16_t*>(q), budget_tokens, k_max,
                                        sel_pages, sel_count, sel_len, sc, n_max, stream),
@@ -301,13 +318,18 @@ spa_status spa_sparse_decode_attn(const spa_pool* pool, const spa_heads* heads, 
   spa::AttnPlan plan;
   plan_attention(pl, heads, k_max, kind, &plan);
   if ((int64_t)bt.B * plan.items_per_seq > INT32_MAX) return fail(SPA_ERR_INVALID, "grid too large");
+  if ((int64_t)plan.item_stride * G > spa::kMaxPartialsPerHead)
+    return fail(SPA_ERR_UNSUPPORTED, "k_max %d with %d query heads per KV head needs %lld partials per head "
+                "(at most %d)", k_max, G, (long long)plan.item_stride * G, spa::kMaxPartialsPerHead);
   size_t ml_off;
-  const size_t need = attn_bytes(pl, plan, bt.B, G, &ml_off);
+  const size_t tb = ticket_bytes(pl, bt.B);
+  const size_t need = tb + attn_bytes(pl, plan, bt.B, G, &ml_off);
   if (!ws || ws_bytes < need) return fail(SPA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
-  float* part_o = static_cast<float*>(ws);
-  float* part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + ml_off);
+  int32_t* tickets = static_cast<int32_t*>(ws);
+  float* part_o = reinterpret_cast<float*>(static_cast<char*>(ws) + tb);
+  float* part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + tb + ml_off);
   return hip_status(spa::launch_attn(pl, bt, plan, G, static_cast<const uint16_t*>(q), sel_pages, sel_count,
-                                     sel_len, out, lse, part_o, part_ml, stream),
+                                     sel_len, out, lse, part_o, part_ml, tickets, stream),
                     "sparse_decode_attn launch");
 }
 

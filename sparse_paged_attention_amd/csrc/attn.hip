@@ -45,9 +45,10 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// A 16-token block: absolute positions [t0, t0 + 16), of which [lo, hi) count.
+// A 16-token block: absolute positions [t0, t0 + 16), of which [lo, hi) count,
+// in physical page `phys` (already validated) at logical slot `lp`.
 struct Block {
-  int32_t t0, lo, hi;
+  int32_t t0, lo, hi, phys, lp;
 };
 
 // Operand registers of one block.
@@ -56,34 +57,21 @@ struct Tile {
   uint2 v[8];     // V^T: channel 16c + (lane & 15), tokens 4*(lane>>4) .. +3
 };
 
-struct Ctx {
-  PoolArgs pl;
-  int32_t b, h;
-  const int32_t* pt_row;
-  int32_t max_pp;
-};
-
-// Loads the tile of block `blk`; returns false when its physical page is
-// not valid (the block then contributes nothing).
-__device__ __forceinline__ bool load_tile(const Ctx& c, const Block& blk, Tile& t) {
-  const int32_t j = blk.t0 / c.pl.p;
-  const int32_t slot_in_page = blk.t0 % c.pl.p;
-  if (j < 0 || j / c.pl.r >= c.max_pp) return false;
-  const int32_t phys = c.pt_row[j / c.pl.r];
-  if (phys < 0 || phys >= c.pl.N) return false;
-  const int32_t lp = j % c.pl.r;
+// Issues the loads of a block's tile. Empty blocks load from page 0 of the
+// pool (always mapped), so the loads never depend on control flow.
+template <int PG>
+__device__ __forceinline__ void issue_tile(const PoolArgs& pl, int32_t h, const Block& blk, Tile& t) {
   const int lane = threadIdx.x & 63;
   const int row = lane & 15, quad = lane >> 4;
-  const int64_t head = (int64_t)phys * c.pl.hkv + c.h;
-  const uint16_t* kp = c.pl.k + ((head * c.pl.P + lp * c.pl.p + slot_in_page + row) * kHeadDim + 32 * quad);
-  const uint4* k4 = reinterpret_cast<const uint4*>(kp);
+  const int64_t head = (int64_t)blk.phys * pl.hkv + h;
+  const int32_t in_page = blk.t0 & (PG - 1);
+  const uint4* k4 = reinterpret_cast<const uint4*>(
+      pl.k + ((head * pl.P + blk.lp * PG + in_page + row) * kHeadDim + 32 * quad));
 #pragma unroll
   for (int i = 0; i < 4; ++i) t.k[i] = k4[i];
-  const uint16_t* vp = c.pl.v + ((head * c.pl.r + lp) * kHeadDim + row) * c.pl.p + slot_in_page + 4 * quad;
+  const uint16_t* vp = pl.v + ((head * pl.r + blk.lp) * kHeadDim + row) * PG + in_page + 4 * quad;
 #pragma unroll
-  for (int ch = 0; ch < 8; ++ch)
-    t.v[ch] = *reinterpret_cast<const uint2*>(vp + (int64_t)16 * ch * c.pl.p);
-  return true;
+  for (int ch = 0; ch < 8; ++ch) t.v[ch] = *reinterpret_cast<const uint2*>(vp + 16 * ch * PG);
 }
 
 struct State {
@@ -116,7 +104,7 @@ __device__ __forceinline__ void process_tile(const Block& blk, const Tile& t, co
   }
   bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
   bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-  if (bm == -INFINITY) return;                    // no valid token (same for every lane)
+  // a non-empty block has a valid token, so bm is finite
   const float m_new = fmaxf(st.m, bm);
   const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
   float pr[4];
@@ -140,12 +128,14 @@ __device__ __forceinline__ void process_tile(const Block& blk, const Tile& t, co
     plo[r] = (short)bf16_rne(rest);
   }
   const bool full = blk.lo <= blk.t0 && blk.hi >= blk.t0 + kBlockTokens;
+  const uint32_t mx = (valid[0] ? 0x0000FFFFu : 0u) | (valid[1] ? 0xFFFF0000u : 0u);
+  const uint32_t my = (valid[2] ? 0x0000FFFFu : 0u) | (valid[3] ? 0xFFFF0000u : 0u);
 #pragma unroll
   for (int ch = 0; ch < 8; ++ch) {
     uint2 w = t.v[ch];
     if (!full) {                                   // stale pool bytes must not reach the MFMA
-      w.x &= (valid[0] ? 0x0000FFFFu : 0u) | (valid[1] ? 0xFFFF0000u : 0u);
-      w.y &= (valid[2] ? 0x0000FFFFu : 0u) | (valid[3] ? 0xFFFF0000u : 0u);
+      w.x &= mx;
+      w.y &= my;
     }
     s16x4 a;
     __builtin_memcpy(&a, &w, 8);
@@ -154,33 +144,7 @@ __device__ __forceinline__ void process_tile(const Block& blk, const Tile& t, co
   }
 }
 
-// Number of 16-token blocks of the streaming set and the block at index v.
-struct StreamSet {
-  int32_t s0, w0, nb_sink, first_w, total;
-  __device__ StreamSet(int32_t L, int32_t sink, int32_t window) {
-    s0 = min(sink, L);
-    w0 = max(sink, L - window);
-    nb_sink = (s0 + kBlockTokens - 1) / kBlockTokens;
-    first_w = w0 / kBlockTokens;
-    const int32_t nb_win = L > w0 ? (L - 1) / kBlockTokens - first_w + 1 : 0;
-    total = nb_sink + nb_win;
-  }
-  __device__ Block at(int32_t v, int32_t L) const {
-    Block b;
-    if (v < nb_sink) {
-      b.t0 = v * kBlockTokens;
-      b.lo = b.t0;
-      b.hi = min(b.t0 + kBlockTokens, s0);
-    } else {
-      b.t0 = (first_w + v - nb_sink) * kBlockTokens;
-      b.lo = max(b.t0, w0);
-      b.hi = min(b.t0 + kBlockTokens, L);
-    }
-    return b;
-  }
-};
-
-__device__ bool page_selected(const int32_t* sel, int32_t cnt, int32_t j) {
+__device__ __forceinline__ bool page_selected(const int32_t* sel, int32_t cnt, int32_t j) {
   int32_t lo = 0, hi = cnt;                        // ascending ids
   while (lo < hi) {
     const int32_t mid = (lo + hi) >> 1;
@@ -191,7 +155,73 @@ __device__ bool page_selected(const int32_t* sel, int32_t cnt, int32_t j) {
   return false;
 }
 
-template <int BPI>
+// Which blocks an item covers. Blocks are numbered per head:
+//   streaming: the sink blocks, then the window blocks;
+//   dynamic:   block (i, s) = 16-token block s of the i-th selected page;
+//   tail:      16-token blocks of [floor16(L_s), L) outside selected pages.
+struct BlockSource {
+  int32_t kind;          // 0 streaming, 1 dynamic, 2 tail
+  int32_t L, PG;
+  int32_t s0, w0, nb_sink, first_w;          // streaming
+  const int32_t* sel;
+  int32_t cnt;                               // dynamic / tail
+  int32_t ls_floor, ls;                      // tail
+  int32_t n_pages;
+
+  // token range of block v (lo == hi: empty); t0 is 16-aligned
+  __device__ __forceinline__ void range(int32_t v, int32_t& t0, int32_t& lo, int32_t& hi) const {
+    if (kind == 0) {
+      if (v < nb_sink) {
+        t0 = v * kBlockTokens; lo = t0; hi = min(t0 + kBlockTokens, s0);
+      } else {
+        t0 = (first_w + v - nb_sink) * kBlockTokens; lo = max(t0, w0); hi = min(t0 + kBlockTokens, L);
+      }
+    } else if (kind == 1) {
+      const int32_t sb = PG / kBlockTokens;
+      const int32_t j = sel[v / sb];
+      if (j < 0 || j >= n_pages) { t0 = 0; lo = 0; hi = 0; return; }
+      t0 = j * PG + (v % sb) * kBlockTokens; lo = t0; hi = min(t0 + kBlockTokens, L);
+    } else {
+      t0 = ls_floor + v * kBlockTokens;
+      lo = max(t0, ls); hi = min(t0 + kBlockTokens, L);
+      if (page_selected(sel, cnt, t0 / PG)) hi = lo;
+    }
+  }
+};
+
+// Resolves blocks [v0, v0 + BPI) (those at or past v_end are empty) to pool
+// locations, then runs them through a two-tile software pipeline: the loads
+// of block u+1 are in flight while block u is computed.
+template <int PG, int BPI>
+__device__ __forceinline__ void run_blocks(const PoolArgs& pl, const int32_t* pt_row, int32_t max_pp,
+                                           int32_t h, const BlockSource& src, int32_t v0, int32_t v_end,
+                                           const bf16x8 (&qb)[4], State& st) {
+  Block blk[BPI];
+#pragma unroll
+  for (int u = 0; u < BPI; ++u) {
+    int32_t t0 = 0, lo = 0, hi = 0;
+    if (v0 + u < v_end) src.range(v0 + u, t0, lo, hi);
+    const int32_t j = t0 / PG;
+    const int32_t slot = j / (pl.P / PG);
+    int32_t phys = (lo < hi && slot < max_pp) ? pt_row[slot] : -1;
+    if (phys < 0 || phys >= pl.N) { phys = 0; hi = lo; t0 = 0; }
+    blk[u] = Block{t0, lo, hi, phys, j % (pl.P / PG)};
+    if (hi <= lo) blk[u].lp = 0;
+  }
+  Tile ta, tb;
+  issue_tile<PG>(pl, h, blk[0], ta);
+#pragma unroll
+  for (int u = 0; u < BPI; u += 2) {
+    if (u + 1 < BPI) issue_tile<PG>(pl, h, blk[u + 1], tb);
+    if (blk[u].lo < blk[u].hi) process_tile(blk[u], ta, qb, st);
+    if (u + 2 < BPI) issue_tile<PG>(pl, h, blk[u + 2], ta);
+    if (u + 1 < BPI && blk[u + 1].lo < blk[u + 1].hi) process_tile(blk[u + 1], tb, qb, st);
+  }
+}
+
+// One item of one (sequence, KV head): the online softmax over its blocks and
+// a partial (max, sum, unnormalised output) per query head.
+template <int PG, int BPI>
 __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, AttnPlan plan, int32_t G,
                                                   const uint16_t* __restrict__ q,
                                                   const int32_t* __restrict__ sel_pages,
@@ -207,19 +237,20 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
   const int32_t L = clamp_len(bt, b, pl.P);
   const int lane = threadIdx.x & 63;
   const int g = lane & 15, quad = lane >> 4;
-
-  Ctx c{pl, b, h, bt.pt + (int64_t)b * bt.max_pp, bt.max_pp};
+  const int32_t* pt_row = bt.pt + (int64_t)b * bt.max_pp;
 
   // query operand: Q[g][32*quad + 8*i .. +8], zero for g >= G
   bf16x8 qb[4];
   const int32_t hq = pl.hkv * G;
-  if (g < G) {
-    const uint4* q4 = reinterpret_cast<const uint4*>(q + ((int64_t)b * hq + h * G + g) * kHeadDim + 32 * quad);
+  {
+    const int32_t gq = g < G ? g : 0;
+    const uint4* q4 = reinterpret_cast<const uint4*>(q + ((int64_t)b * hq + h * G + gq) * kHeadDim + 32 * quad);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { uint4 w = q4[i]; __builtin_memcpy(&qb[i], &w, 16); }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { uint4 w = {0, 0, 0, 0}; __builtin_memcpy(&qb[i], &w, 16); }
+    for (int i = 0; i < 4; ++i) {
+      uint4 w = q4[i];
+      if (g >= G) w = uint4{0, 0, 0, 0};
+      __builtin_memcpy(&qb[i], &w, 16);
+    }
   }
 
   State st;
@@ -229,65 +260,44 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
   for (int ch = 0; ch < 8; ++ch) st.o[ch] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const bool dynamic = plan.kind[h] != 0;
-  const int32_t* sel = sel_pages + ((int64_t)b * pl.hkv + h) * plan.k_max;
-  if (dynamic && it == plan.items_dyn - 1) {
-    // tail item: tokens appended since the selection, outside selected pages
-    const int32_t cnt = min(max(sel_count[(int64_t)b * pl.hkv + h], 0), plan.k_max);
-    const int32_t ls = max(sel_len[b], 0);
-    for (int32_t t0 = (ls / kBlockTokens) * kBlockTokens; t0 < L; t0 += kBlockTokens) {
-      if (page_selected(sel, cnt, t0 / pl.p)) continue;
-      Block blk{t0, max(t0, ls), min(t0 + kBlockTokens, L)};
-      Tile t;
-      if (load_tile(c, blk, t)) process_tile(blk, t, qb, st);
-    }
-  } else if (L > 0) {
-    int32_t total, v0 = it * BPI;
-    StreamSet ss(L, plan.sink, plan.window);
-    const int32_t sb = pl.p / kBlockTokens;
-    const int32_t n_pages = (L + pl.p - 1) / pl.p;
-    int32_t cnt = 0;
-    if (dynamic) {
-      cnt = min(max(sel_count[(int64_t)b * pl.hkv + h], 0), plan.k_max);
-      total = cnt * sb;
+  const int32_t n_items = dynamic ? plan.items_dyn : plan.items_stream;
+  BlockSource src;
+  src.L = L;
+  src.PG = PG;
+  src.n_pages = (L + PG - 1) / PG;
+  src.sel = sel_pages + ((int64_t)b * pl.hkv + h) * plan.k_max;
+  src.cnt = 0;
+  if (L > 0) {
+    if (!dynamic) {
+      src.kind = 0;
+      src.s0 = min(plan.sink, L);
+      src.w0 = max(plan.sink, L - plan.window);
+      src.nb_sink = (src.s0 + kBlockTokens - 1) / kBlockTokens;
+      src.first_w = src.w0 / kBlockTokens;
+      const int32_t nb_win = L > src.w0 ? (L - 1) / kBlockTokens - src.first_w + 1 : 0;
+      run_blocks<PG, BPI>(pl, pt_row, bt.max_pp, h, src, it * BPI, src.nb_sink + nb_win, qb, st);
     } else {
-      total = ss.total;
-    }
-    const int32_t v1 = min(total, v0 + BPI);
-    auto block_at = [&](int32_t v) -> Block {
-      if (!dynamic) return ss.at(v, L);
-      const int32_t j = sel[v / sb];
-      Block blk{0, 0, 0};
-      if (j < 0 || j >= n_pages) return blk;          // out of range: empty block
-      blk.t0 = j * pl.p + (v % sb) * kBlockTokens;
-      blk.lo = blk.t0;
-      blk.hi = min(blk.t0 + kBlockTokens, L);
-      return blk;
-    };
-    if (v0 < v1) {
-      Block cur = block_at(v0);
-      Tile tc;
-      bool okc = cur.lo < cur.hi && load_tile(c, cur, tc);
-      for (int32_t v = v0; v < v1; ++v) {
-        Block nxt;
-        Tile tn;
-        bool okn = false;
-        if (v + 1 < v1) {
-          nxt = block_at(v + 1);
-          okn = nxt.lo < nxt.hi && load_tile(c, nxt, tn);
-        }
-        if (okc) process_tile(cur, tc, qb, st);
-        cur = nxt;
-        tc = tn;
-        okc = okn;
+      src.cnt = min(max(sel_count[(int64_t)b * pl.hkv + h], 0), plan.k_max);
+      if (it < n_items - 1) {
+        src.kind = 1;
+        run_blocks<PG, BPI>(pl, pt_row, bt.max_pp, h, src, it * BPI, src.cnt * (PG / kBlockTokens), qb, st);
+      } else {
+        src.kind = 2;
+        src.ls = min(max(sel_len[b], 0), L);
+        src.ls_floor = (src.ls / kBlockTokens) * kBlockTokens;
+        const int32_t nb = (L - src.ls_floor + kBlockTokens - 1) / kBlockTokens;
+        for (int32_t v0 = 0; v0 < nb; v0 += BPI)
+          run_blocks<PG, BPI>(pl, pt_row, bt.max_pp, h, src, v0, nb, qb, st);
       }
     }
   }
 
-  // fold the four token quads of the running sum
+  // fold the four token quads of the running sum, store the partial
   st.l += __shfl_xor(st.l, 16, 64);
   st.l += __shfl_xor(st.l, 32, 64);
+  const int64_t slot0 = ((int64_t)b * pl.hkv + h) * plan.item_stride * G;
   if (g < G) {
-    const int64_t slot = (((int64_t)b * pl.hkv + h) * plan.item_stride + it) * G + g;
+    const int64_t slot = slot0 + (int64_t)it * G + g;
     float* o = part_o + slot * kHeadDim + 4 * quad;
 #pragma unroll
     for (int ch = 0; ch < 8; ++ch) *reinterpret_cast<f32x4*>(o + 16 * ch) = st.o[ch];
@@ -296,45 +306,83 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
       part_ml[slot * 2 + 1] = st.l;
     }
   }
+
 }
 
-// Merge of the item partials of one query head: thread d owns channel d.
-__global__ void __launch_bounds__(128) combine_kernel(int32_t hkv, AttnPlan plan, int32_t G,
-                                                      const float* __restrict__ part_o,
-                                                      const float* __restrict__ part_ml,
-                                                      float* __restrict__ out,
-                                                      float* __restrict__ lse) {
-  const int32_t hq = hkv * G;
-  const int32_t b = blockIdx.x / hq, i = blockIdx.x % hq;
-  const int32_t h = i / G, g = i % G;
+// Merge of the item partials of one (sequence, KV head): the running-max /
+// running-sum rule of online softmax applied across items. Thread (g, d) owns
+// channel d of query g; the items' (max, sum) pairs are staged in LDS first so
+// every output channel's loads are independent and in flight together.
+constexpr int kCombineThreads = 512;
+constexpr int kMaxItemsLds = kMaxPartialsPerHead;
+
+__global__ void __launch_bounds__(kCombineThreads) combine_kernel(int32_t hkv, AttnPlan plan, int32_t G,
+                                                                  const float* __restrict__ part_o,
+                                                                  const float* __restrict__ part_ml,
+                                                                  float* __restrict__ out,
+                                                                  float* __restrict__ lse) {
+  __shared__ float sm[kMaxItemsLds], sl[kMaxItemsLds];
+  __shared__ float sM[16];
+  const int32_t b = blockIdx.x / hkv, h = blockIdx.x % hkv;
   const int32_t n_items = plan.kind[h] ? plan.items_dyn : plan.items_stream;
-  const int64_t slot0 = ((int64_t)b * hkv + h) * plan.item_stride;
-  float M = -INFINITY;
-  for (int32_t it = 0; it < n_items; ++it) M = fmaxf(M, part_ml[((slot0 + it) * G + g) * 2]);
-  const int d = threadIdx.x;
-  float num = 0.f, den = 0.f;
-  if (M != -INFINITY) {
-    for (int32_t it = 0; it < n_items; ++it) {
-      const int64_t slot = (slot0 + it) * G + g;
-      const float w = __builtin_amdgcn_exp2f(part_ml[slot * 2] - M);
-      den += w * part_ml[slot * 2 + 1];
-      num += w * part_o[slot * kHeadDim + d];
-    }
+  const int64_t slot0 = ((int64_t)b * hkv + h) * plan.item_stride * G;   // slot(i, g) = slot0 + i*G + g
+  const int32_t n_ml = n_items * G;                                     // <= kMaxItemsLds (host check)
+  for (int32_t k = threadIdx.x; k < n_ml; k += kCombineThreads) {
+    sm[k] = part_ml[(slot0 + k) * 2];
+    sl[k] = part_ml[(slot0 + k) * 2 + 1];
   }
-  const int64_t oi = (int64_t)b * hq + i;
-  out[oi * kHeadDim + d] = M == -INFINITY ? 0.f : num / den;
-  if (lse && d == 0) lse[oi] = M == -INFINITY ? -INFINITY : (M + log2f(den)) * kLn2;
+  __syncthreads();
+  if (threadIdx.x < G) {
+    float M = -INFINITY;
+    for (int32_t i = 0; i < n_items; ++i) M = fmaxf(M, sm[i * G + threadIdx.x]);
+    sM[threadIdx.x] = M;
+  }
+  __syncthreads();
+  const int32_t hq = hkv * G;
+  for (int32_t gd = threadIdx.x; gd < G * kHeadDim; gd += kCombineThreads) {
+    const int32_t g = gd / kHeadDim, d = gd % kHeadDim;
+    const float M = sM[g];
+    float num = 0.f, den = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll 8
+      for (int32_t i = 0; i < n_items; ++i) {
+        const float w = __builtin_amdgcn_exp2f(sm[i * G + g] - M);
+        den += w * sl[i * G + g];
+        num += w * part_o[(slot0 + (int64_t)i * G + g) * kHeadDim + d];
+      }
+    }
+    const int64_t oi = (int64_t)b * hq + h * G + g;
+    out[oi * kHeadDim + d] = M == -INFINITY ? 0.f : num / den;
+    if (lse && d == 0) lse[oi] = M == -INFINITY ? -INFINITY : (M + log2f(den)) * kLn2;
+  }
 }
 
-template <int BPI>
-hipError_t launch_attn_bpi(const PoolArgs& pool, const BatchArgs& batch, const AttnPlan& plan,
-                           int32_t G, const uint16_t* q, const int32_t* sel_pages,
-                           const int32_t* sel_count, const int32_t* sel_len, float* part_o,
-                           float* part_ml, hipStream_t s) {
+template <int PG, int BPI>
+hipError_t launch_attn_t(const PoolArgs& pool, const BatchArgs& batch, const AttnPlan& plan, int32_t G,
+                         const uint16_t* q, const int32_t* sel_pages, const int32_t* sel_count,
+                         const int32_t* sel_len, float* part_o, float* part_ml, int32_t* tickets,
+                         float* out, float* lse, hipStream_t s) {
   const int64_t grid = (int64_t)batch.B * plan.items_per_seq;
-  hipLaunchKernelGGL(attn_kernel<BPI>, dim3((unsigned)grid), dim3(64), 0, s, pool, batch, plan, G, q,
+  hipLaunchKernelGGL((attn_kernel<PG, BPI>), dim3((unsigned)grid), dim3(64), 0, s, pool, batch, plan, G, q,
                      sel_pages, sel_count, sel_len, part_o, part_ml);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(combine_kernel, dim3(batch.B * pool.hkv), dim3(kCombineThreads), 0, s, pool.hkv, plan, G,
+                     part_o, part_ml, out, lse);
   return hipGetLastError();
+}
+
+template <int PG>
+hipError_t launch_attn_p(const PoolArgs& pool, const BatchArgs& batch, const AttnPlan& plan, int32_t G,
+                         const uint16_t* q, const int32_t* sel_pages, const int32_t* sel_count,
+                         const int32_t* sel_len, float* part_o, float* part_ml, int32_t* tickets,
+                         float* out, float* lse, hipStream_t s) {
+  switch (plan.blocks_per_item) {
+    case 4: return launch_attn_t<PG, 4>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, part_o, part_ml, tickets, out, lse, s);
+    case 8: return launch_attn_t<PG, 8>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, part_o, part_ml, tickets, out, lse, s);
+    case 16: return launch_attn_t<PG, 16>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, part_o, part_ml, tickets, out, lse, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -342,19 +390,14 @@ hipError_t launch_attn_bpi(const PoolArgs& pool, const BatchArgs& batch, const A
 hipError_t launch_attn(const PoolArgs& pool, const BatchArgs& batch, const AttnPlan& plan, int32_t G,
                        const uint16_t* q, const int32_t* sel_pages, const int32_t* sel_count,
                        const int32_t* sel_len, float* out, float* lse, float* part_o,
-                       float* part_ml, hipStream_t s) {
+                       float* part_ml, int32_t* tickets, hipStream_t s) {
   if (batch.B == 0) return hipSuccess;
-  hipError_t e;
-  switch (plan.blocks_per_item) {
-    case 4: e = launch_attn_bpi<4>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, part_o, part_ml, s); break;
-    case 8: e = launch_attn_bpi<8>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, part_o, part_ml, s); break;
-    case 16: e = launch_attn_bpi<16>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, part_o, part_ml, s); break;
+  switch (pool.p) {
+    case 16: return launch_attn_p<16>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, part_o, part_ml, tickets, out, lse, s);
+    case 32: return launch_attn_p<32>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, part_o, part_ml, tickets, out, lse, s);
+    case 64: return launch_attn_p<64>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, part_o, part_ml, tickets, out, lse, s);
     default: return hipErrorInvalidValue;
   }
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(batch.B * pool.hkv * G), dim3(128), 0, s, pool.hkv, plan, G,
-                     part_o, part_ml, out, lse);
-  return hipGetLastError();
 }
 
 }  // namespace spa

@@ -10,6 +10,7 @@ namespace spa {
 constexpr int kHeadDim = 128;       // D
 constexpr int kBlockTokens = 16;    // tokens per attention block (MFMA M/K tile)
 constexpr int kMaxKvHeads = 128;
+constexpr int kMaxPartialsPerHead = 2048;   // items x query heads merged per KV head
 
 // Pool geometry and base pointers, passed by value to every kernel.
 struct PoolArgs {
@@ -65,6 +66,7 @@ hipError_t launch_select(const PoolArgs& pool, const BatchArgs& batch, const Hea
 hipError_t launch_attn(const PoolArgs& pool, const BatchArgs& batch, const AttnPlan& plan,
                        int32_t G, const uint16_t* q, const int32_t* sel_pages,
                        const int32_t* sel_count, const int32_t* sel_len, float* out,
-                       float* lse, float* part_o, float* part_ml, hipStream_t s);
+                       float* lse, float* part_o, float* part_ml, int32_t* tickets,
+                       hipStream_t s);
 
 }  // namespace spa

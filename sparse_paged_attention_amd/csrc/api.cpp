@@ -138,14 +138,15 @@ void plan_attention(const spa::PoolArgs& pl, const spa_heads* heads, int32_t k_m
   plan->sink = heads->sink;
   plan->window = heads->window;
   plan->k_max = k_max;
-  int32_t at = 0;
   for (int32_t h = 0; h < pl.hkv; ++h) {
     plan->kind[h] = kind[h];
-    plan->item_base[h] = at;
-    at += kind[h] ? plan->items_dyn : plan->items_stream;
+    if (kind[h]) plan->dyn_ids[plan->n_dyn++] = (uint8_t)h;
+    else plan->stream_ids[plan->n_stream++] = (uint8_t)h;
   }
-  plan->item_base[pl.hkv] = at;
-  plan->items_per_seq = at;
+}
+
+int64_t attn_items_per_seq(const spa::AttnPlan& plan) {
+  return (int64_t)plan.n_stream * plan.items_stream + (int64_t)plan.n_dyn * plan.items_dyn;
 }
 
 // Workspace layout: [ticket counters: B * H_kv int32, kept zero between calls]
@@ -317,7 +318,7 @@ spa_status spa_sparse_decode_attn(const spa_pool* pool, const spa_heads* heads, 
     return fail(SPA_ERR_INVALID, "dynamic heads need sel_pages / sel_count / sel_len");
   spa::AttnPlan plan;
   plan_attention(pl, heads, k_max, kind, &plan);
-  if ((int64_t)bt.B * plan.items_per_seq > INT32_MAX) return fail(SPA_ERR_INVALID, "grid too large");
+  if ((int64_t)bt.B * attn_items_per_seq(plan) > INT32_MAX) return fail(SPA_ERR_INVALID, "grid too large");
   if ((int64_t)plan.item_stride * G > spa::kMaxPartialsPerHead)
     return fail(SPA_ERR_UNSUPPORTED, "k_max %d with %d query heads per KV head needs %lld partials per head "
                 "(at most %d)", k_max, G, (long long)plan.item_stride * G, spa::kMaxPartialsPerHead);

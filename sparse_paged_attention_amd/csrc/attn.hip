@@ -80,10 +80,16 @@ struct State {
   f32x4 o[8];       // O^T: channels 16c + 4*quad + r of query (lane & 15)
 };
 
-__device__ __forceinline__ void process_tile(const Block& blk, const Tile& t, const bf16x8 (&qb)[4],
-                                             State& st) {
-  const int lane = threadIdx.x & 63;
-  const int quad = lane >> 4;
+// Cross-lane max over the four 16-lane rows (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float max_over_rows(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
+// Scores S^T[16 tok][16 q] of one block: 4 chained 16x16x32 MFMAs over D.
+__device__ __forceinline__ f32x4 qk_block(const Tile& t, const bf16x8 (&qb)[4]) {
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -91,56 +97,78 @@ __device__ __forceinline__ void process_tile(const Block& blk, const Tile& t, co
     __builtin_memcpy(&a, &t.k[i], 16);
     s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[i], s, 0, 0, 0);
   }
-  // lane holds scores of tokens t0 + 4*quad + r for query (lane & 15)
-  float x[4];
-  bool valid[4];
+  return s;
+}
+
+// Two blocks (32 tokens) at once. The PV product contracts over 32 tokens
+// with one 16x16x32 MFMA per 16 channels: K-slot j of lane row q holds token
+// 4q + j of block a (j < 4) or token 4q + j - 4 of block b (j >= 4), which is
+// exactly where the QK products left this lane's probabilities.
+__device__ __forceinline__ void process_pair(const Block& ba, const Tile& ta, const Block& bb,
+                                             const Tile& tb, const bf16x8 (&qb)[4], State& st) {
+  const int lane = threadIdx.x & 63;
+  const int quad = lane >> 4;
+  const f32x4 sa = qk_block(ta, qb);
+  const f32x4 sb = qk_block(tb, qb);
+  float x[8];
+  bool valid[8];
   float bm = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int32_t tok = blk.t0 + 4 * quad + r;
-    valid[r] = tok >= blk.lo && tok < blk.hi;
-    x[r] = valid[r] ? s[r] * kScaleLog2 : -INFINITY;
-    bm = fmaxf(bm, x[r]);
+    const int32_t tka = ba.t0 + 4 * quad + r, tkb = bb.t0 + 4 * quad + r;
+    valid[r] = tka >= ba.lo && tka < ba.hi;
+    valid[4 + r] = tkb >= bb.lo && tkb < bb.hi;
+    x[r] = valid[r] ? sa[r] * kScaleLog2 : -INFINITY;
+    x[4 + r] = valid[4 + r] ? sb[r] * kScaleLog2 : -INFINITY;
+    bm = fmaxf(bm, fmaxf(x[r], x[4 + r]));
   }
-  bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-  bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-  // a non-empty block has a valid token, so bm is finite
+  bm = max_over_rows(bm);
+  if (bm == -INFINITY) return;                    // no valid token (same for every lane)
   const float m_new = fmaxf(st.m, bm);
   const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-  float pr[4];
+  float pr[8];
   float psum = 0.f;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    pr[r] = valid[r] ? __builtin_amdgcn_exp2f(x[r] - m_new) : 0.f;
+  for (int r = 0; r < 8; ++r) {
+    pr[r] = __builtin_amdgcn_exp2f(x[r] - m_new);  // 0 for masked tokens
     psum += pr[r];
   }
   st.l = st.l * alpha + psum;
   st.m = m_new;
+  if (__any(alpha != 1.f)) {
 #pragma unroll
-  for (int ch = 0; ch < 8; ++ch) st.o[ch] *= alpha;
-
-  s16x4 phi, plo;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint16_t hb = bf16_rne(pr[r]);
-    const float rest = pr[r] - __uint_as_float((uint32_t)hb << 16);
-    phi[r] = (short)hb;
-    plo[r] = (short)bf16_rne(rest);
+    for (int ch = 0; ch < 8; ++ch) st.o[ch] *= alpha;
   }
-  const bool full = blk.lo <= blk.t0 && blk.hi >= blk.t0 + kBlockTokens;
-  const uint32_t mx = (valid[0] ? 0x0000FFFFu : 0u) | (valid[1] ? 0xFFFF0000u : 0u);
-  const uint32_t my = (valid[2] ? 0x0000FFFFu : 0u) | (valid[3] ? 0xFFFF0000u : 0u);
+  bf16x8 phi, plo;
+  {
+    uint16_t hb[8], lb[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      hb[r] = bf16_rne(pr[r]);
+      lb[r] = bf16_rne(pr[r] - __uint_as_float((uint32_t)hb[r] << 16));
+    }
+    __builtin_memcpy(&phi, hb, 16);
+    __builtin_memcpy(&plo, lb, 16);
+  }
+  const bool full = ba.lo <= ba.t0 && ba.hi >= ba.t0 + kBlockTokens &&
+                    bb.lo <= bb.t0 && bb.hi >= bb.t0 + kBlockTokens;
+  uint32_t mk[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    mk[w] = (valid[2 * w] ? 0x0000FFFFu : 0u) | (valid[2 * w + 1] ? 0xFFFF0000u : 0u);
 #pragma unroll
   for (int ch = 0; ch < 8; ++ch) {
-    uint2 w = t.v[ch];
+    uint4 w = {ta.v[ch].x, ta.v[ch].y, tb.v[ch].x, tb.v[ch].y};
     if (!full) {                                   // stale pool bytes must not reach the MFMA
-      w.x &= mx;
-      w.y &= my;
+      w.x &= mk[0];
+      w.y &= mk[1];
+      w.z &= mk[2];
+      w.w &= mk[3];
     }
-    s16x4 a;
-    __builtin_memcpy(&a, &w, 8);
-    st.o[ch] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, phi, st.o[ch], 0, 0, 0);
-    st.o[ch] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, plo, st.o[ch], 0, 0, 0);
+    bf16x8 a;
+    __builtin_memcpy(&a, &w, 16);
+    st.o[ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, st.o[ch], 0, 0, 0);
+    st.o[ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, st.o[ch], 0, 0, 0);
   }
 }
 
@@ -161,67 +189,101 @@ __device__ __forceinline__ bool page_selected(const int32_t* sel, int32_t cnt, i
 //   tail:      16-token blocks of [floor16(L_s), L) outside selected pages.
 struct BlockSource {
   int32_t kind;          // 0 streaming, 1 dynamic, 2 tail
-  int32_t L, PG;
+  int32_t L;
   int32_t s0, w0, nb_sink, first_w;          // streaming
   const int32_t* sel;
-  int32_t cnt;                               // dynamic / tail
+  int32_t cnt, k_max;                        // dynamic / tail
   int32_t ls_floor, ls;                      // tail
-  int32_t n_pages;
-
-  // token range of block v (lo == hi: empty); t0 is 16-aligned
-  __device__ __forceinline__ void range(int32_t v, int32_t& t0, int32_t& lo, int32_t& hi) const {
-    if (kind == 0) {
-      if (v < nb_sink) {
-        t0 = v * kBlockTokens; lo = t0; hi = min(t0 + kBlockTokens, s0);
-      } else {
-        t0 = (first_w + v - nb_sink) * kBlockTokens; lo = max(t0, w0); hi = min(t0 + kBlockTokens, L);
-      }
-    } else if (kind == 1) {
-      const int32_t sb = PG / kBlockTokens;
-      const int32_t j = sel[v / sb];
-      if (j < 0 || j >= n_pages) { t0 = 0; lo = 0; hi = 0; return; }
-      t0 = j * PG + (v % sb) * kBlockTokens; lo = t0; hi = min(t0 + kBlockTokens, L);
-    } else {
-      t0 = ls_floor + v * kBlockTokens;
-      lo = max(t0, ls); hi = min(t0 + kBlockTokens, L);
-      if (page_selected(sel, cnt, t0 / PG)) hi = lo;
-    }
-  }
 };
 
 // Resolves blocks [v0, v0 + BPI) (those at or past v_end are empty) to pool
-// locations, then runs them through a two-tile software pipeline: the loads
-// of block u+1 are in flight while block u is computed.
-template <int PG, int BPI>
-__device__ __forceinline__ void run_blocks(const PoolArgs& pl, const int32_t* pt_row, int32_t max_pp,
-                                           int32_t h, const BlockSource& src, int32_t v0, int32_t v_end,
-                                           const bf16x8 (&qb)[4], State& st) {
+// locations, then streams them through a ring of DEPTH operand tiles: the
+// first DEPTH blocks' loads are issued together, and each tile is refilled
+// with block u + DEPTH as soon as block u has been computed. Every lookup
+// (selected page ids, page-table entries) is issued unconditionally with a
+// clamped index, so each level of the lookup costs one memory round trip for
+// the whole item. The kernel has a single call site, so one copy of the
+// pipeline serves every kind of item (instruction-cache footprint).
+template <int PG, int BPI, int DEPTH>
+__device__ __forceinline__ void run_blocks(const PoolArgs& pl, const int32_t* pt_row,
+                                           int32_t max_pp, int32_t h, const BlockSource& src,
+                                           int32_t v0, int32_t v_end, const bf16x8 (&qb)[4],
+                                           State& st) {
+  constexpr int SB = PG / kBlockTokens;           // blocks per logical page
+  const int32_t L = src.L;
+  const int32_t n_pages = (L + PG - 1) / PG;
   Block blk[BPI];
+  if (src.kind == 1) {
+    int32_t page[BPI];
+#pragma unroll
+    for (int u = 0; u < BPI; ++u) {
+      const int32_t i = min((v0 + u) / SB, src.k_max - 1);
+      page[u] = src.sel[i];
+    }
+#pragma unroll
+    for (int u = 0; u < BPI; ++u) {
+      const int32_t j = page[u];
+      const bool ok = v0 + u < v_end && j >= 0 && j < n_pages;
+      const int32_t t0 = ok ? j * PG + ((v0 + u) % SB) * kBlockTokens : 0;
+      blk[u] = Block{t0, t0, ok ? min(t0 + kBlockTokens, L) : t0, 0, 0};
+    }
+  } else if (src.kind == 0) {
+#pragma unroll
+    for (int u = 0; u < BPI; ++u) {
+      const int32_t v = v0 + u;
+      int32_t t0, lo, hi;
+      if (v < src.nb_sink) {
+        t0 = v * kBlockTokens; lo = t0; hi = min(t0 + kBlockTokens, src.s0);
+      } else {
+        t0 = (src.first_w + v - src.nb_sink) * kBlockTokens; lo = max(t0, src.w0); hi = min(t0 + kBlockTokens, L);
+      }
+      if (v >= v_end) { t0 = 0; lo = 0; hi = 0; }
+      blk[u] = Block{t0, lo, hi, 0, 0};
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < BPI; ++u) {
+      const int32_t t0 = src.ls_floor + (v0 + u) * kBlockTokens;
+      int32_t lo = max(t0, src.ls), hi = min(t0 + kBlockTokens, L);
+      if (v0 + u >= v_end || page_selected(src.sel, src.cnt, t0 / PG)) hi = lo;
+      blk[u] = Block{hi > lo ? t0 : 0, lo, hi, 0, 0};
+    }
+  }
+  int32_t ptv[BPI];
 #pragma unroll
   for (int u = 0; u < BPI; ++u) {
-    int32_t t0 = 0, lo = 0, hi = 0;
-    if (v0 + u < v_end) src.range(v0 + u, t0, lo, hi);
-    const int32_t j = t0 / PG;
-    const int32_t slot = j / (pl.P / PG);
-    int32_t phys = (lo < hi && slot < max_pp) ? pt_row[slot] : -1;
-    if (phys < 0 || phys >= pl.N) { phys = 0; hi = lo; t0 = 0; }
-    blk[u] = Block{t0, lo, hi, phys, j % (pl.P / PG)};
-    if (hi <= lo) blk[u].lp = 0;
+    const int32_t slot = min((blk[u].t0 / PG) / (pl.P / PG), max_pp - 1);
+    ptv[u] = pt_row[slot];
   }
-  Tile ta, tb;
-  issue_tile<PG>(pl, h, blk[0], ta);
+#pragma unroll
+  for (int u = 0; u < BPI; ++u) {
+    const int32_t j = blk[u].t0 / PG;
+    int32_t phys = ptv[u];
+    if (phys < 0 || phys >= pl.N || blk[u].hi <= blk[u].lo) { phys = 0; blk[u].hi = blk[u].lo; blk[u].t0 = 0; }
+    blk[u].phys = phys;
+    blk[u].lp = blk[u].hi > blk[u].lo ? j % (pl.P / PG) : 0;
+  }
+  // blocks go in pairs; DEPTH (even) tiles are in flight
+  static_assert(BPI % 2 == 0 && DEPTH % 2 == 0, "blocks are processed in pairs");
+  constexpr int D = DEPTH < BPI ? DEPTH : BPI;
+  Tile t[D];
+#pragma unroll
+  for (int u = 0; u < D; ++u) issue_tile<PG>(pl, h, blk[u], t[u]);
 #pragma unroll
   for (int u = 0; u < BPI; u += 2) {
-    if (u + 1 < BPI) issue_tile<PG>(pl, h, blk[u + 1], tb);
-    if (blk[u].lo < blk[u].hi) process_tile(blk[u], ta, qb, st);
-    if (u + 2 < BPI) issue_tile<PG>(pl, h, blk[u + 2], ta);
-    if (u + 1 < BPI && blk[u + 1].lo < blk[u + 1].hi) process_tile(blk[u + 1], tb, qb, st);
+    if (blk[u].lo < blk[u].hi || blk[u + 1].lo < blk[u + 1].hi)
+      process_pair(blk[u], t[u % D], blk[u + 1], t[(u + 1) % D], qb, st);
+    if (u + D < BPI) {
+      issue_tile<PG>(pl, h, blk[u + D], t[u % D]);
+      issue_tile<PG>(pl, h, blk[u + 1 + D], t[(u + 1) % D]);
+    }
   }
 }
 
 // One item of one (sequence, KV head): the online softmax over its blocks and
-// a partial (max, sum, unnormalised output) per query head.
-template <int PG, int BPI>
+// a partial (max, sum, unnormalised output) per query head. Items are laid
+// out as [streaming: B x n_stream x items_stream][dynamic: B x n_dyn x items_dyn].
+template <int PG, int BPI, int DEPTH>
 __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, AttnPlan plan, int32_t G,
                                                   const uint16_t* __restrict__ q,
                                                   const int32_t* __restrict__ sel_pages,
@@ -229,12 +291,32 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
                                                   const int32_t* __restrict__ sel_len,
                                                   float* __restrict__ part_o,
                                                   float* __restrict__ part_ml) {
-  const int32_t b = blockIdx.x / plan.items_per_seq;
-  const int32_t rem = blockIdx.x % plan.items_per_seq;
-  int32_t h = 0;
-  while (plan.item_base[h + 1] <= rem) ++h;
-  const int32_t it = rem - plan.item_base[h];
+  int32_t idx = blockIdx.x;
+  const int32_t n_stream_items = bt.B * plan.n_stream * plan.items_stream;
+  const bool dynamic = idx >= n_stream_items;
+  int32_t b, h, it;
+  if (!dynamic) {
+    const int32_t per_b = plan.n_stream * plan.items_stream;
+    b = idx / per_b;
+    const int32_t r = idx % per_b;
+    h = plan.stream_ids[r / plan.items_stream];
+    it = r % plan.items_stream;
+  } else {
+    idx -= n_stream_items;
+    const int32_t per_b = plan.n_dyn * plan.items_dyn;
+    b = idx / per_b;
+    const int32_t r = idx % per_b;
+    h = plan.dyn_ids[r / plan.items_dyn];
+    it = r % plan.items_dyn;
+  }
+  const int32_t n_items = dynamic ? plan.items_dyn : plan.items_stream;
+  // independent loads first: length, selection count / length, query
   const int32_t L = clamp_len(bt, b, pl.P);
+  int32_t cnt = 0, ls = 0;
+  if (dynamic) {
+    cnt = min(max(sel_count[(int64_t)b * pl.hkv + h], 0), plan.k_max);
+    ls = sel_len[b];
+  }
   const int lane = threadIdx.x & 63;
   const int g = lane & 15, quad = lane >> 4;
   const int32_t* pt_row = bt.pt + (int64_t)b * bt.max_pp;
@@ -259,15 +341,13 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
 #pragma unroll
   for (int ch = 0; ch < 8; ++ch) st.o[ch] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const bool dynamic = plan.kind[h] != 0;
-  const int32_t n_items = dynamic ? plan.items_dyn : plan.items_stream;
   BlockSource src;
   src.L = L;
-  src.PG = PG;
-  src.n_pages = (L + PG - 1) / PG;
   src.sel = sel_pages + ((int64_t)b * pl.hkv + h) * plan.k_max;
-  src.cnt = 0;
+  src.cnt = cnt;
+  src.k_max = plan.k_max;
   if (L > 0) {
+    int32_t v_begin = it * BPI, v_end;
     if (!dynamic) {
       src.kind = 0;
       src.s0 = min(plan.sink, L);
@@ -275,21 +355,19 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
       src.nb_sink = (src.s0 + kBlockTokens - 1) / kBlockTokens;
       src.first_w = src.w0 / kBlockTokens;
       const int32_t nb_win = L > src.w0 ? (L - 1) / kBlockTokens - src.first_w + 1 : 0;
-      run_blocks<PG, BPI>(pl, pt_row, bt.max_pp, h, src, it * BPI, src.nb_sink + nb_win, qb, st);
+      v_end = min(src.nb_sink + nb_win, v_begin + BPI);
+    } else if (it < n_items - 1) {
+      src.kind = 1;
+      v_end = min(cnt * (PG / kBlockTokens), v_begin + BPI);
     } else {
-      src.cnt = min(max(sel_count[(int64_t)b * pl.hkv + h], 0), plan.k_max);
-      if (it < n_items - 1) {
-        src.kind = 1;
-        run_blocks<PG, BPI>(pl, pt_row, bt.max_pp, h, src, it * BPI, src.cnt * (PG / kBlockTokens), qb, st);
-      } else {
-        src.kind = 2;
-        src.ls = min(max(sel_len[b], 0), L);
-        src.ls_floor = (src.ls / kBlockTokens) * kBlockTokens;
-        const int32_t nb = (L - src.ls_floor + kBlockTokens - 1) / kBlockTokens;
-        for (int32_t v0 = 0; v0 < nb; v0 += BPI)
-          run_blocks<PG, BPI>(pl, pt_row, bt.max_pp, h, src, v0, nb, qb, st);
-      }
+      src.kind = 2;
+      src.ls = min(max(ls, 0), L);
+      src.ls_floor = (src.ls / kBlockTokens) * kBlockTokens;
+      v_begin = 0;
+      v_end = (L - src.ls_floor + kBlockTokens - 1) / kBlockTokens;   // any length: chunks of BPI
     }
+    for (int32_t v0 = v_begin; v0 < v_end; v0 += BPI)
+      run_blocks<PG, BPI, DEPTH>(pl, pt_row, bt.max_pp, h, src, v0, v_end, qb, st);
   }
 
   // fold the four token quads of the running sum, store the partial
@@ -357,13 +435,13 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(int32_t hkv, A
   }
 }
 
-template <int PG, int BPI>
+template <int PG, int BPI, int DEPTH = 4>
 hipError_t launch_attn_t(const PoolArgs& pool, const BatchArgs& batch, const AttnPlan& plan, int32_t G,
                          const uint16_t* q, const int32_t* sel_pages, const int32_t* sel_count,
                          const int32_t* sel_len, float* part_o, float* part_ml, int32_t* tickets,
                          float* out, float* lse, hipStream_t s) {
-  const int64_t grid = (int64_t)batch.B * plan.items_per_seq;
-  hipLaunchKernelGGL((attn_kernel<PG, BPI>), dim3((unsigned)grid), dim3(64), 0, s, pool, batch, plan, G, q,
+  const int64_t grid = (int64_t)batch.B * (plan.n_stream * plan.items_stream + plan.n_dyn * plan.items_dyn);
+  hipLaunchKernelGGL((attn_kernel<PG, BPI, DEPTH>), dim3((unsigned)grid), dim3(64), 0, s, pool, batch, plan, G, q,
                      sel_pages, sel_count, sel_len, part_o, part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

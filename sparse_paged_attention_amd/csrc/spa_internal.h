@@ -37,18 +37,20 @@ struct HeadList {
   int16_t id[kMaxKvHeads];
 };
 
-// Work plan of the attention launch. Items are numbered per sequence: the
-// items of KV head h are [item_base[h], item_base[h+1]).
+// Work plan of the attention launch: every streaming head is cut into
+// items_stream items and every dynamic head into items_dyn items (the last of
+// which covers the tokens appended since the selection).
 struct AttnPlan {
-  int32_t items_per_seq;        // item_base[hkv]
+  int32_t n_stream, n_dyn;      // streaming / dynamic KV heads
   int32_t items_stream;         // items per streaming head
-  int32_t items_dyn;            // items per dynamic head (the last one is the tail item)
+  int32_t items_dyn;            // items per dynamic head
   int32_t blocks_per_item;      // 16-token blocks per item
   int32_t item_stride;          // max(items_stream, items_dyn): partial slots per head
   int32_t sink, window;
   int32_t k_max;
   uint8_t kind[kMaxKvHeads];
-  int32_t item_base[kMaxKvHeads + 1];
+  uint8_t stream_ids[kMaxKvHeads];
+  uint8_t dyn_ids[kMaxKvHeads];
 };
 
 // ---- launchers (return hipError_t of the launch) -------------------------

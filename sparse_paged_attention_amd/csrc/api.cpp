@@ -49,8 +49,8 @@ int32_t blocks_per_item() {
   }();
   return v;
 }
-// Largest page count a selection row can score (top-k keeps 64 keys per thread).
-constexpr int64_t kMaxScoredPages = 65536;
+// Largest page count a selection row can score (top-k keeps 32 keys per thread).
+constexpr int64_t kMaxScoredPages = 32768;
 
 spa_status check_pool(const spa_pool* pool, spa::PoolArgs* out) {
   if (!pool) return fail(SPA_ERR_INVALID, "pool is NULL");

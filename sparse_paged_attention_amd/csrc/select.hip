@@ -34,11 +34,15 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 // ---------------------------------------------------------------- scoring
 //
-// A group of LPP lanes scores NP pages; each lane owns CPL = 128 / LPP
-// channels of every page, so its q+ / q- values stay in registers (fp64) and
-// its summary loads are contiguous. The V = NP * G partial sums of a group
-// are reduce-scattered over the group's lanes (R = LPP / V lanes end up
-// sharing each total), rounded to fp32 and max-reduced over the query group.
+// One wave scores a range of consecutive logical pages of one (sequence,
+// dynamic head). Inside the wave, a group of LPP lanes scores NP pages at a
+// time; each lane owns CPL = 128 / LPP channels of every page, so its q+ / q-
+// values stay in registers (fp64) and its summary loads are contiguous. The
+// V = NP * G partial sums of a group are reduce-scattered over the group's
+// lanes (R = LPP / V lanes end up sharing each total), rounded to fp32 and
+// max-reduced over the query group. The range's page-table entries are read
+// once into LDS; summary loads run one pass ahead of the arithmetic and are
+// issued unconditionally (an invalid page reads page 0 and is masked).
 template <int G>
 struct ScoreShape {
   static constexpr int LPP = G <= 4 ? 16 : 4 * G;   // lanes per page
@@ -47,128 +51,186 @@ struct ScoreShape {
   static constexpr int V = NP * G;                  // partial sums per lane
   static constexpr int R = LPP / V;                 // lanes holding each total
   static constexpr int GPW = 64 / LPP;              // groups per wave
-  static constexpr int GPB = 4 * GPW;               // groups per 256-thread block
-  static constexpr int PAGES = GPB * NP;            // pages per block
+  static constexpr int PASS = GPW * NP;             // pages per pass
+  static constexpr int PASSES = 8;
+  static constexpr int RANGE = PASS * PASSES;       // pages per wave (<= 128)
 };
 
 template <int CPL>
-__device__ __forceinline__ void load_chunk(const uint16_t* p, double (&out)[CPL]) {
+struct Raw {
+  uint32_t w[CPL / 2];
+};
+
+template <int CPL>
+__device__ __forceinline__ void load_raw(const uint16_t* p, Raw<CPL>& r) {
   if constexpr (CPL == 8) {
     const uint4 w = *reinterpret_cast<const uint4*>(p);
-    out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x); out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
-    out[4] = bf16_lo(w.z); out[5] = bf16_hi(w.z); out[6] = bf16_lo(w.w); out[7] = bf16_hi(w.w);
+    r.w[0] = w.x; r.w[1] = w.y; r.w[2] = w.z; r.w[3] = w.w;
   } else if constexpr (CPL == 4) {
     const uint2 w = *reinterpret_cast<const uint2*>(p);
-    out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x); out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
+    r.w[0] = w.x; r.w[1] = w.y;
   } else {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-    out[0] = bf16_lo(w); out[1] = bf16_hi(w);
+    r.w[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+}
+
+template <int CPL>
+__device__ __forceinline__ void widen(const Raw<CPL>& r, double (&out)[CPL]) {
+#pragma unroll
+  for (int i = 0; i < CPL / 2; ++i) {
+    out[2 * i] = bf16_lo(r.w[i]);
+    out[2 * i + 1] = bf16_hi(r.w[i]);
   }
 }
 
 template <int G>
-__global__ void __launch_bounds__(256) score_kernel(PoolArgs pl, BatchArgs bt, HeadList dyn,
-                                                    const uint16_t* __restrict__ q,
-                                                    float* __restrict__ scores, int32_t n_max) {
+__global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, HeadList dyn,
+                                                   const uint16_t* __restrict__ q,
+                                                   float* __restrict__ scores, int32_t n_max) {
   using S = ScoreShape<G>;
+  __shared__ int32_t pts[2 * 64];
   const int32_t b = blockIdx.y / dyn.n, h = dyn.id[blockIdx.y % dyn.n];
   const int32_t L = clamp_len(bt, b, pl.P);
   const int32_t n = (L + pl.p - 1) / pl.p;
-  const int32_t base = blockIdx.x * S::PAGES;
+  const int32_t base = blockIdx.x * S::RANGE;
   if (base >= n) return;
 
   const int lane = threadIdx.x & 63;
   const int sub = lane % S::LPP;                          // position inside the group
-  const int group = (threadIdx.x >> 6) * S::GPW + lane / S::LPP;
+  const int group = lane / S::LPP;
   const int c0 = sub * S::CPL;
+
+  // page-table entries covering the range (at most 128: two per lane)
+  const int32_t* pt_row = bt.pt + (int64_t)b * bt.max_pp;
+  const int32_t e0 = base / pl.r;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int32_t e = min(e0 + lane + 64 * k, bt.max_pp - 1);
+    pts[lane + 64 * k] = pt_row[e];
+  }
 
   // q+ and q- of this lane's channels, fp64 (exact for bf16)
   double qp[G][S::CPL], qn[G][S::CPL];
   const int32_t hq = pl.hkv * G;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
+    Raw<S::CPL> rq;
+    load_raw<S::CPL>(q + ((int64_t)b * hq + h * G + g) * kHeadDim + c0, rq);
     double qv[S::CPL];
-    load_chunk<S::CPL>(q + ((int64_t)b * hq + h * G + g) * kHeadDim + c0, qv);
+    widen<S::CPL>(rq, qv);
 #pragma unroll
     for (int i = 0; i < S::CPL; ++i) {
       qp[g][i] = qv[i] > 0.0 ? qv[i] : 0.0;
       qn[g][i] = qv[i] < 0.0 ? qv[i] : 0.0;
     }
   }
+  __syncthreads();
 
-  double v[S::V];                                         // [page slot][query]
-#pragma unroll
-  for (int pp = 0; pp < S::NP; ++pp) {
-    const int32_t j = base + pp * S::GPB + group;
-    double kmin[S::CPL], kmax[S::CPL];
-    bool ok = j < n;
-    int32_t phys = 0;
-    if (ok) {
-      phys = bt.pt[(int64_t)b * bt.max_pp + j / pl.r];
-      ok = phys >= 0 && phys < pl.N;
-    }
-    if (ok) {
-      const uint16_t* s = pl.summ + ((((int64_t)phys * pl.hkv + h) * pl.r + j % pl.r) * 2) * kHeadDim + c0;
-      load_chunk<S::CPL>(s, kmin);
-      load_chunk<S::CPL>(s + kHeadDim, kmax);
-    } else {
-#pragma unroll
-      for (int i = 0; i < S::CPL; ++i) { kmin[i] = 0.0; kmax[i] = 0.0; }
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      double acc = 0.0;
-#pragma unroll
-      for (int i = 0; i < S::CPL; ++i) {
-        acc = fma(qp[g][i], kmax[i], acc);
-        acc = fma(qn[g][i], kmin[i], acc);
-      }
-      v[pp * G + g] = acc;
-    }
-  }
+  // summary location of page slot pp of pass it (page 0 of the pool if invalid)
+  auto locate = [&](int it, int pp, bool& ok) -> const uint16_t* {
+    const int32_t j = base + it * S::PASS + pp * S::GPW + group;
+    int32_t phys = pts[min(j / pl.r - e0, 127)];
+    ok = j < n && phys >= 0 && phys < pl.N;
+    if (!ok) phys = 0;
+    return pl.summ + ((((int64_t)phys * pl.hkv + h) * pl.r + (ok ? j % pl.r : 0)) * 2) * kHeadDim + c0;
+  };
 
-  // reduce-scatter over the high lane bits of the group, then sum over the
-  // R lanes that share a total
+  // one pass worth of loaded summaries
+  struct Pass {
+    Raw<S::CPL> mn[S::NP], mx[S::NP];
+    bool ok[S::NP];
+  };
+  auto issue = [&](int it, Pass& ps) {
 #pragma unroll
-  for (int m = S::LPP / 2; m >= 1; m /= 2) {
-    if (m >= S::R) {
-      const bool upper = (sub & m) != 0;
-      const int half = m / S::R;
-#pragma unroll
-      for (int i = 0; i < half; ++i) {
-        const double send = upper ? v[i] : v[i + half];
-        const double keep = upper ? v[i + half] : v[i];
-        v[i] = keep + __shfl_xor(send, m, 64);
-      }
-    } else {
-      v[0] += __shfl_xor(v[0], m, 64);
+    for (int pp = 0; pp < S::NP; ++pp) {
+      const uint16_t* sp = locate(it, pp, ps.ok[pp]);
+      load_raw<S::CPL>(sp, ps.mn[pp]);
+      load_raw<S::CPL>(sp + kHeadDim, ps.mx[pp]);
     }
-  }
-  // lane `sub` now holds the total of index sub / R = page_slot * G + query
-  float s = (float)v[0];
-  s = s == 0.0f ? 0.0f : s;                               // one zero: +0
+  };
+  float* out_row = scores + ((int64_t)b * pl.hkv + h) * n_max;
+  auto compute = [&](int it, const Pass& ps) {
+    double v[S::V];                                       // [page slot][query]
 #pragma unroll
-  for (int m = 1; m < G; m *= 2) s = fmaxf(s, __shfl_xor(s, m * S::R, 64));
-  const int idx = sub / S::R;
-  const int pp = idx / G;
-  const int32_t j = base + pp * S::GPB + group;
-  if (sub % (S::R * G) == 0 && j < n) {
-    bool ok = true;
-    const int32_t phys = bt.pt[(int64_t)b * bt.max_pp + j / pl.r];
-    ok = phys >= 0 && phys < pl.N;
-    scores[((int64_t)b * pl.hkv + h) * n_max + j] = ok ? s : -INFINITY;
+    for (int pp = 0; pp < S::NP; ++pp) {
+      double kmin[S::CPL], kmax[S::CPL];
+      widen<S::CPL>(ps.mn[pp], kmin);
+      widen<S::CPL>(ps.mx[pp], kmax);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        double acc = 0.0;
+#pragma unroll
+        for (int i = 0; i < S::CPL; ++i) {
+          acc = fma(qp[g][i], kmax[i], acc);
+          acc = fma(qn[g][i], kmin[i], acc);
+        }
+        v[pp * G + g] = acc;
+      }
+    }
+    // reduce-scatter over the high lane bits of the group, then sum over the
+    // R lanes that share a total
+#pragma unroll
+    for (int m = S::LPP / 2; m >= 1; m /= 2) {
+      if (m >= S::R) {
+        const bool upper = (sub & m) != 0;
+        const int half = m / S::R;
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+          const double send = upper ? v[i] : v[i + half];
+          const double keep = upper ? v[i + half] : v[i];
+          v[i] = keep + __shfl_xor(send, m, 64);
+        }
+      } else {
+        v[0] += __shfl_xor(v[0], m, 64);
+      }
+    }
+    // lane `sub` now holds the total of index sub / R = page_slot * G + query
+    float sc = (float)v[0];
+    sc = sc == 0.0f ? 0.0f : sc;                          // one zero: +0
+#pragma unroll
+    for (int m = 1; m < G; m *= 2) sc = fmaxf(sc, __shfl_xor(sc, m * S::R, 64));
+    const int pp = (sub / S::R) / G;
+    bool ok = false;
+#pragma unroll
+    for (int k = 0; k < S::NP; ++k) ok = k == pp ? ps.ok[k] : ok;
+    const int32_t j = base + it * S::PASS + pp * S::GPW + group;
+    if (sub % (S::R * G) == 0 && j < n) out_row[j] = ok ? sc : -INFINITY;
+  };
+
+  // two passes in flight: the loads of pass it + 1 run under the arithmetic
+  // of pass it (explicit double buffer, no register indexing by pass)
+  static_assert(S::PASSES % 2 == 0, "passes go in pairs");
+  Pass pa, pb;
+  issue(0, pa);
+  for (int it = 0; it < S::PASSES; it += 2) {
+    issue(it + 1, pb);
+    compute(it, pa);
+    if (it + 2 < S::PASSES) issue(it + 2, pa);
+    compute(it + 1, pb);
   }
 }
 
 // ------------------------------------------------------------------ top-k
+//
+// One 512-thread block per (sequence, dynamic head). Element e of thread t is
+// page e * 512 + t (coalesced loads), held in a register as the 32-bit
+// order-preserving image of its fp32 score. Rounds of a 512-bin histogram
+// over the remaining candidates' key range find the bin holding the k-th
+// largest key: keys above it are kept, keys below dropped, the bin's keys stay
+// candidates. When every candidate has the same key, the ones with the lowest
+// page ids are kept (ties go to the lower page id). Kept ids are written in
+// ascending order; both id-order ranks come from one block-wide prefix sum
+// over per-(element, wave) counts.
 
-constexpr int kTopkThreads = 1024;
-constexpr int kBins = 1024;
+constexpr int kTopkThreads = 512;
+constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kBins = kTopkThreads;                 // one bin per thread
+constexpr int kBinBits = 9;
+static_assert(kBins == (1 << kBinBits), "bins");
 
-__device__ __forceinline__ uint64_t page_key(const float* s, int32_t j) {
-  const uint32_t u = __float_as_uint(s[j]);
-  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+__device__ __forceinline__ uint32_t order32(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 // Inclusive sum over the block of one value per thread; every thread gets its
@@ -183,7 +245,8 @@ __device__ int32_t block_inclusive_scan(int32_t x, int32_t* sh_wave, int32_t& to
   if (lane == 63) sh_wave[wave] = x;
   __syncthreads();
   int32_t before = 0, all = 0;
-  for (int w = 0; w < kTopkThreads / 64; ++w) {
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
     const int32_t t = sh_wave[w];
     before += w < wave ? t : 0;
     all += t;
@@ -193,6 +256,39 @@ __device__ int32_t block_inclusive_scan(int32_t x, int32_t* sh_wave, int32_t& to
   return x + before;
 }
 
+// For a per-thread element mask, the number of set elements with a smaller
+// page id than element e of this thread (ids: e * kTopkThreads + thread),
+// written to `rank` for every set element; returns the total.
+template <int E>
+__device__ int32_t id_order_ranks(uint64_t mask, int32_t (&rank)[E], int32_t* table, int32_t* sh_wave) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint64_t ball = __ballot((mask >> e) & 1);
+    if (lane == 0) table[e * kTopkWaves + wave] = __popcll(ball);
+  }
+  __syncthreads();
+  int32_t total = 0;
+  for (int32_t base = 0; base < E * kTopkWaves; base += kTopkThreads) {
+    const int32_t idx = base + tid;
+    const int32_t x = idx < E * kTopkWaves ? table[idx] : 0;
+    int32_t t2;
+    const int32_t incl = block_inclusive_scan(x, sh_wave, t2);
+    if (idx < E * kTopkWaves) table[idx] = incl - x + total;
+    total += t2;
+  }
+  __syncthreads();
+  const uint64_t below = (1ull << lane) - 1;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint64_t ball = __ballot((mask >> e) & 1);
+    rank[e] = table[e * kTopkWaves + wave] + __popcll(ball & below);
+  }
+  __syncthreads();
+  return total;
+}
+
+template <int E>   // elements per thread: n <= E * kTopkThreads
 __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_t p, int32_t P,
                                                             int32_t hkv, HeadList dyn,
                                                             const float* __restrict__ scores,
@@ -201,9 +297,10 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
                                                             int32_t k_max, int32_t* sel_pages,
                                                             int32_t* sel_count, int32_t* sel_len) {
   __shared__ int32_t hist[kBins];
-  __shared__ int32_t sh_wave[kTopkThreads / 64];
-  __shared__ uint64_t sh_min[kTopkThreads / 64], sh_max[kTopkThreads / 64];
+  __shared__ int32_t sh_wave[kTopkWaves];
+  __shared__ uint32_t sh_min[kTopkWaves], sh_max[kTopkWaves];
   __shared__ int32_t sh_pick[2];
+  __shared__ int32_t table[E * kTopkWaves];
 
   const int32_t b = blockIdx.x / dyn.n, h = dyn.id[blockIdx.x % dyn.n];
   const int32_t L = clamp_len(bt, b, P);
@@ -213,46 +310,53 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
   k = k > n ? n : k;
   k = k > k_max ? k_max : k;
   const float* s = scores + ((int64_t)b * hkv + h) * n_max;
-  const int tid = threadIdx.x;
-  const int32_t per = (n + kTopkThreads - 1) / kTopkThreads;   // <= kMaxPerThread
-  const int32_t first = tid * per;
-  const int32_t mine = max(0, min(per, n - first));
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  uint64_t cand = mine >= 64 ? ~0ull : ((1ull << mine) - 1);
-  uint64_t sel = 0;
+  uint32_t ord[E];
+  uint64_t cand = 0, sel = 0;                       // bit e: element e
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int32_t j = e * kTopkThreads + tid;
+    ord[e] = order32(s[min(j, n_max - 1)]);
+    if (j < n) cand |= 1ull << e;
+  }
   int32_t need = k;
+  int32_t rank[E];
 
-  for (int round = 0; round < 16 && need > 0; ++round) {
-    // candidate count and key range
+  for (int round = 0; round < 8 && need > 0; ++round) {
     int32_t total;
     block_inclusive_scan(__popcll(cand), sh_wave, total);
     if (total <= need) { sel |= cand; cand = 0; break; }
-    uint64_t lo = ~0ull, hi = 0;
-    for (int32_t e = 0; e < mine; ++e)
-      if (cand >> e & 1) {
-        const uint64_t key = page_key(s, first + e);
-        lo = key < lo ? key : lo;
-        hi = key > hi ? key : hi;
-      }
+    uint32_t lo = 0xFFFFFFFFu, hi = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (cand >> e & 1) { lo = min(lo, ord[e]); hi = max(hi, ord[e]); }
     for (int d = 32; d >= 1; d /= 2) {
-      const uint64_t l2 = __shfl_xor(lo, d, 64), h2 = __shfl_xor(hi, d, 64);
-      lo = l2 < lo ? l2 : lo;
-      hi = h2 > hi ? h2 : hi;
+      lo = min(lo, (uint32_t)__shfl_xor((int)lo, d, 64));
+      hi = max(hi, (uint32_t)__shfl_xor((int)hi, d, 64));
     }
-    if ((tid & 63) == 0) { sh_min[tid >> 6] = lo; sh_max[tid >> 6] = hi; }
+    if (lane == 0) { sh_min[wave] = lo; sh_max[wave] = hi; }
     hist[tid] = 0;
     __syncthreads();
-    lo = ~0ull;
+    lo = 0xFFFFFFFFu;
     hi = 0;
-    for (int w = 0; w < kTopkThreads / 64; ++w) {
-      lo = sh_min[w] < lo ? sh_min[w] : lo;
-      hi = sh_max[w] > hi ? sh_max[w] : hi;
+#pragma unroll
+    for (int w = 0; w < kTopkWaves; ++w) { lo = min(lo, sh_min[w]); hi = max(hi, sh_max[w]); }
+    if (lo == hi) {
+      // all candidates tie: keep the `need` lowest page ids
+      id_order_ranks<E>(cand, rank, table, sh_wave);
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if ((cand >> e & 1) && rank[e] < need) sel |= 1ull << e;
+      cand = 0;
+      break;
     }
-    const uint64_t span = hi - lo;
-    const int bits = span == 0 ? 0 : 64 - __clzll((long long)span);
-    const int shift = bits > 10 ? bits - 10 : 0;               // (span >> shift) < kBins
-    for (int32_t e = 0; e < mine; ++e)
-      if (cand >> e & 1) atomicAdd(&hist[(page_key(s, first + e) - lo) >> shift], 1);
+    const uint32_t span = hi - lo;
+    const int bits = 32 - __clz((int)span);
+    const int shift = bits > kBinBits ? bits - kBinBits : 0;   // (span >> shift) < kBins
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (cand >> e & 1) atomicAdd(&hist[(ord[e] - lo) >> shift], 1);
     __syncthreads();
     // bins in descending order: thread t looks at bin kBins-1-t
     const int32_t cnt = hist[kBins - 1 - tid];
@@ -260,25 +364,24 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
     const int32_t incl = block_inclusive_scan(cnt, sh_wave, tot2);
     if (incl - cnt < need && incl >= need) { sh_pick[0] = kBins - 1 - tid; sh_pick[1] = incl - cnt; }
     __syncthreads();
-    const int32_t pick = sh_pick[0], above = sh_pick[1];
-    for (int32_t e = 0; e < mine; ++e)
+    const uint32_t pick = (uint32_t)sh_pick[0];
+    const int32_t above = sh_pick[1];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
       if (cand >> e & 1) {
-        const int32_t bin = (int32_t)((page_key(s, first + e) - lo) >> shift);
+        const uint32_t bin = (ord[e] - lo) >> shift;
         if (bin > pick) { sel |= 1ull << e; cand &= ~(1ull << e); }
         else if (bin < pick) cand &= ~(1ull << e);
       }
     need -= above;
-    __syncthreads();
   }
 
-  // compaction in id order
-  int32_t total;
-  const int32_t cnt = __popcll(sel);
-  const int32_t at = block_inclusive_scan(cnt, sh_wave, total) - cnt;
+  // kept ids in ascending order
+  const int32_t total = id_order_ranks<E>(sel, rank, table, sh_wave);
   int32_t* out = sel_pages + ((int64_t)b * hkv + h) * k_max;
-  int32_t w = at;
-  for (int32_t e = 0; e < mine; ++e)
-    if (sel >> e & 1) out[w++] = first + e;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if ((sel >> e) & 1) out[rank[e]] = e * kTopkThreads + tid;
   if (tid == 0) {
     sel_count[(int64_t)b * hkv + h] = total;
     sel_len[b] = L;
@@ -289,8 +392,8 @@ template <int G>
 hipError_t launch_score_g(const PoolArgs& pool, const BatchArgs& batch, const HeadList& dyn,
                           const uint16_t* q, float* scores, int32_t n_max, hipStream_t s) {
   using S = ScoreShape<G>;
-  dim3 grid((n_max + S::PAGES - 1) / S::PAGES, batch.B * dyn.n);
-  hipLaunchKernelGGL(score_kernel<G>, grid, dim3(256), 0, s, pool, batch, dyn, q, scores, n_max);
+  dim3 grid((n_max + S::RANGE - 1) / S::RANGE, batch.B * dyn.n);
+  hipLaunchKernelGGL(score_kernel<G>, grid, dim3(64), 0, s, pool, batch, dyn, q, scores, n_max);
   return hipGetLastError();
 }
 
@@ -311,9 +414,12 @@ hipError_t launch_select(const PoolArgs& pool, const BatchArgs& batch, const Hea
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_kernel, dim3(batch.B * dyn.n), dim3(kTopkThreads), 0, s, batch, pool.p,
-                     pool.P, pool.hkv, dyn, scores, n_max, budget, k_max, sel_pages, sel_count,
-                     sel_len);
+  if (n_max <= 32 * kTopkThreads)
+    hipLaunchKernelGGL(topk_kernel<32>, dim3(batch.B * dyn.n), dim3(kTopkThreads), 0, s, batch, pool.p,
+                       pool.P, pool.hkv, dyn, scores, n_max, budget, k_max, sel_pages, sel_count, sel_len);
+  else
+    hipLaunchKernelGGL(topk_kernel<64>, dim3(batch.B * dyn.n), dim3(kTopkThreads), 0, s, batch, pool.p,
+                       pool.P, pool.hkv, dyn, scores, n_max, budget, k_max, sel_pages, sel_count, sel_len);
   return hipGetLastError();
 }
 

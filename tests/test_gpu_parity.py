@@ -116,3 +116,13 @@ def test_llama3_128k_full_size_sampled():
     steps, shuffled pool, reuse every 4 steps; checked on sampled heads."""
     wl = W.WORKLOADS["llama3_128k"]
     run(wl, check=[(0, 0), (0, 4), (1, 5), (2, 3), (3, 7)])
+
+
+def test_selection_exact_ties_go_to_lowest_page_id():
+    """Integer-valued keys and queries: many pages share a score exactly, and
+    the selection must still match the oracle id for id (lowest ids win)."""
+    wl = W.Workload("ties", 2300, 3, 32, 8, 16, 64, (3000, 777, 5000), 3, 1, (0, 1) * 4, 16, 128, 512,
+                    True, quantized=True)
+    log(f"[parity] {wl.name}")
+    pr = ParityRun(wl, strict_ties=True)
+    assert_reports(pr.run())

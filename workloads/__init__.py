@@ -54,6 +54,7 @@ class Workload:
     permute: bool            # shuffle physical pages across the pool
     planted: str | None = None   # "aligned3" or "rho05x32"
     outliers: bool = False
+    quantized: bool = False  # keys, values and queries rounded to integers in [-2, 2] (many exact score ties)
     d: int = 128
 
     @property
@@ -139,6 +140,8 @@ def query(wl: Workload, b: int, step: int) -> np.ndarray:
     """q of sequence b at decode step `step`: uint16 [H_q][D]."""
     g = _gen(wl.seed, _Q, b, step)
     x = g.standard_normal((wl.hq, wl.d), dtype=np.float32)
+    if wl.quantized:
+        x = np.clip(np.rint(x), -2, 2).astype(np.float32)
     return to_bf16_bits(x)
 
 
@@ -182,6 +185,8 @@ def kv_f32(wl: Workload, b: int, h: int, which: str, out: np.ndarray | None = No
             else:
                 qbar = q.sum(axis=0) / math.sqrt(wl.G)
                 rows[:] = 0.5 * qbar + math.sqrt(0.75) * rows
+    if wl.quantized:
+        np.clip(np.rint(out, out=out), -2, 2, out=out)
     if wl.outliers:
         for t in outlier_positions(wl, b):
             if t < L:

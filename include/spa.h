@@ -97,17 +97,21 @@ typedef struct spa_batch {
   const int32_t* seq_lens;    /* device int32 [B]: L_b, tokens in sequence b after this step's append */
 } spa_batch;
 
-/* ---- a1: append one token per sequence --------------------------------
+/* ---- a1 (+ a2): append one token per sequence -------------------------
  * Writes the key and value of token L_b - 1 of every sequence b into its
  * pool slot (physical page page_table[b][(L_b-1)/P], slot (L_b-1) % P).
+ *   heads: NULL, or the head kinds; when given, the same launch also rebuilds
+ *          the summary of the logical page receiving the token for every
+ *          dynamic head (the same result as spa_page_summary_update with
+ *          first_pos NULL afterwards);
  *   k_new, v_new: device bf16 [B][H_kv][D], read only.
- * Sequences with L_b < 1 are skipped. Summaries are not touched; call
- * spa_page_summary_update afterwards for dynamic heads.
+ * Sequences with L_b < 1 are skipped.
  * LServe write-up "2.2 分层分页KV缓存" (pool of physical pages holding
- * logical pages); paged store of the long-context survey "3.4 KV 缓存分页". */
-spa_status spa_kv_pool_append(const spa_pool* pool, const spa_batch* batch,
-                              const void* k_new, const void* v_new,
-                              hipStream_t stream);
+ * logical pages); paged store of the long-context survey "3.4 KV 缓存分页";
+ * min-max page summaries, write-up "2.1". */
+spa_status spa_kv_pool_append(const spa_pool* pool, const spa_heads* heads,
+                              const spa_batch* batch, const void* k_new,
+                              const void* v_new, hipStream_t stream);
 
 /* Bulk write of tokens [start, start + count) of ONE sequence (prefill).
  *   page_table_row: device int32 [max_pages], that sequence's row;

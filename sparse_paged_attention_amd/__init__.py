@@ -71,7 +71,7 @@ def lib() -> ctypes.CDLL:
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         P, H, B = ctypes.POINTER(c_pool), ctypes.POINTER(c_heads), ctypes.POINTER(c_batch)
         sig = {
-            "spa_kv_pool_append": ([P, B, vp, vp, vp], ctypes.c_int),
+            "spa_kv_pool_append": ([P, H, B, vp, vp, vp], ctypes.c_int),
             "spa_kv_pool_write": ([P, vp, i32, i64, i64, vp, vp, vp], ctypes.c_int),
             "spa_page_summary_update": ([P, H, B, vp, i32, vp], ctypes.c_int),
             "spa_select_pages": ([P, H, B, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
@@ -213,14 +213,17 @@ class Batch:
 
 # ------------------------------------------------------------ entry points
 
-def kv_pool_append(pool: Pool, batch: Batch, k_new, v_new, stream=None) -> None:
-    """spa_kv_pool_append: k_new, v_new bf16 [B][H_kv][D]."""
+def kv_pool_append(pool: Pool, batch: Batch, k_new, v_new, heads: "Heads | None" = None,
+                   stream=None) -> None:
+    """spa_kv_pool_append: k_new, v_new bf16 [B][H_kv][D]; with `heads`, the
+    summaries of the dynamic heads' receiving pages are rebuilt in the same launch."""
     p, b = pool.c(), batch.c()
+    h = _heads_for(heads, pool) if heads is not None else None
     shape = (b.batch, pool.num_kv_heads, HEAD_DIM)
     _need(k_new, shape, "bf16", "k_new")
     _need(v_new, shape, "bf16", "v_new")
-    _check(lib().spa_kv_pool_append(ctypes.byref(p), ctypes.byref(b), _ptr(k_new), _ptr(v_new),
-                                    _stream(stream)))
+    _check(lib().spa_kv_pool_append(ctypes.byref(p), ctypes.byref(h) if h is not None else None,
+                                    ctypes.byref(b), _ptr(k_new), _ptr(v_new), _stream(stream)))
 
 
 def kv_pool_write(pool: Pool, page_table_row, start: int, k, v, stream=None) -> None:

@@ -191,17 +191,20 @@ int32_t spa_default_budget(int64_t context_len) {
   return (int32_t)std::min<int64_t>(b, 4096);
 }
 
-spa_status spa_kv_pool_append(const spa_pool* pool, const spa_batch* batch, const void* k_new,
-                              const void* v_new, hipStream_t stream) {
+spa_status spa_kv_pool_append(const spa_pool* pool, const spa_heads* heads, const spa_batch* batch,
+                              const void* k_new, const void* v_new, hipStream_t stream) {
   spa::PoolArgs pl;
   spa::BatchArgs bt;
+  spa::HeadList dyn;
+  int32_t G;
   spa_status s;
   if ((s = check_pool(pool, &pl)) != SPA_OK) return s;
+  if (heads && (s = check_heads(heads, pl, &G, &dyn, nullptr)) != SPA_OK) return s;
   if ((s = check_batch(batch, pl, &bt)) != SPA_OK) return s;
   if (bt.B == 0) return ok();
   if (!k_new || !v_new) return fail(SPA_ERR_INVALID, "k_new / v_new is NULL");
   return hip_status(spa::launch_append(pl, bt, static_cast<const uint16_t*>(k_new),
-                                       static_cast<const uint16_t*>(v_new), stream),
+                                       static_cast<const uint16_t*>(v_new), heads ? &dyn : nullptr, stream),
                     "kv_pool_append launch");
 }
 

@@ -214,19 +214,19 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
 //
 // One 512-thread block per (sequence, dynamic head). Element e of thread t is
 // page e * 512 + t (coalesced loads), held in a register as the 32-bit
-// order-preserving image of its fp32 score. Rounds of a 512-bin histogram
+// order-preserving image of its fp32 score. Rounds of a 4096-bin histogram
 // over the remaining candidates' key range find the bin holding the k-th
 // largest key: keys above it are kept, keys below dropped, the bin's keys stay
-// candidates. When every candidate has the same key, the ones with the lowest
-// page ids are kept (ties go to the lower page id). Kept ids are written in
+// candidates. At most 64 candidates left are ranked exactly by (key
+// descending, page id ascending); if more than 64 share one key, the ones with
+// the lowest page ids are kept (ties go to the lower page id). Kept ids are written in
 // ascending order; both id-order ranks come from one block-wide prefix sum
 // over per-(element, wave) counts.
 
 constexpr int kTopkThreads = 512;
 constexpr int kTopkWaves = kTopkThreads / 64;
-constexpr int kBins = kTopkThreads;                 // one bin per thread
-constexpr int kBinBits = 9;
-static_assert(kBins == (1 << kBinBits), "bins");
+constexpr int kHistBits = 12;
+constexpr int kHistBins = 1 << kHistBits;           // 8 per thread
 
 __device__ __forceinline__ uint32_t order32(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -296,10 +296,13 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
                                                             const int32_t* __restrict__ budget,
                                                             int32_t k_max, int32_t* sel_pages,
                                                             int32_t* sel_count, int32_t* sel_len) {
-  __shared__ int32_t hist[kBins];
+  constexpr int BINS = kHistBins, PER = BINS / kTopkThreads;
+  __shared__ int32_t hist[BINS];
   __shared__ int32_t sh_wave[kTopkWaves];
   __shared__ uint32_t sh_min[kTopkWaves], sh_max[kTopkWaves];
   __shared__ int32_t sh_pick[2];
+  __shared__ int32_t sh_ncand;
+  __shared__ uint64_t cand_key[64];
   __shared__ int32_t table[E * kTopkWaves];
 
   const int32_t b = blockIdx.x / dyn.n, h = dyn.id[blockIdx.x % dyn.n];
@@ -324,26 +327,51 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
   int32_t rank[E];
 
   for (int round = 0; round < 8 && need > 0; ++round) {
-    int32_t total;
-    block_inclusive_scan(__popcll(cand), sh_wave, total);
-    if (total <= need) { sel |= cand; cand = 0; break; }
+    // candidate count and key range in one pass
     uint32_t lo = 0xFFFFFFFFu, hi = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e)
       if (cand >> e & 1) { lo = min(lo, ord[e]); hi = max(hi, ord[e]); }
+    int32_t c = __popcll(cand);
     for (int d = 32; d >= 1; d /= 2) {
       lo = min(lo, (uint32_t)__shfl_xor((int)lo, d, 64));
       hi = max(hi, (uint32_t)__shfl_xor((int)hi, d, 64));
+      c += __shfl_xor(c, d, 64);
     }
-    if (lane == 0) { sh_min[wave] = lo; sh_max[wave] = hi; }
-    hist[tid] = 0;
+    if (lane == 0) { sh_min[wave] = lo; sh_max[wave] = hi; sh_wave[wave] = c; }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) hist[tid * PER + i] = 0;
+    if (tid == 0) sh_ncand = 0;
     __syncthreads();
     lo = 0xFFFFFFFFu;
     hi = 0;
+    int32_t total = 0;
 #pragma unroll
-    for (int w = 0; w < kTopkWaves; ++w) { lo = min(lo, sh_min[w]); hi = max(hi, sh_max[w]); }
+    for (int w = 0; w < kTopkWaves; ++w) { lo = min(lo, sh_min[w]); hi = max(hi, sh_max[w]); total += sh_wave[w]; }
+    if (total <= need) { sel |= cand; cand = 0; break; }
+    if (total <= 64) {
+      // exact ranks by (key descending, page id ascending) among the few left
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (cand >> e & 1) {
+          const int32_t at = atomicAdd(&sh_ncand, 1);
+          cand_key[at] = ((uint64_t)ord[e] << 32) | (0xFFFFFFFFu - (uint32_t)(e * kTopkThreads + tid));
+        }
+      __syncthreads();
+      const int32_t nc = sh_ncand;
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (cand >> e & 1) {
+          const uint64_t key = ((uint64_t)ord[e] << 32) | (0xFFFFFFFFu - (uint32_t)(e * kTopkThreads + tid));
+          int32_t r = 0;
+          for (int32_t i = 0; i < nc; ++i) r += cand_key[i] > key;
+          if (r < need) sel |= 1ull << e;
+        }
+      cand = 0;
+      break;
+    }
     if (lo == hi) {
-      // all candidates tie: keep the `need` lowest page ids
+      // more than 64 candidates share one key: keep the `need` lowest page ids
       id_order_ranks<E>(cand, rank, table, sh_wave);
 #pragma unroll
       for (int e = 0; e < E; ++e)
@@ -353,16 +381,22 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
     }
     const uint32_t span = hi - lo;
     const int bits = 32 - __clz((int)span);
-    const int shift = bits > kBinBits ? bits - kBinBits : 0;   // (span >> shift) < kBins
+    const int shift = bits > kHistBits ? bits - kHistBits : 0;   // (span >> shift) < BINS
 #pragma unroll
     for (int e = 0; e < E; ++e)
       if (cand >> e & 1) atomicAdd(&hist[(ord[e] - lo) >> shift], 1);
     __syncthreads();
-    // bins in descending order: thread t looks at bin kBins-1-t
-    const int32_t cnt = hist[kBins - 1 - tid];
+    // bins in descending order: thread t owns bins BINS-1-t*PER .. BINS-PER-t*PER
+    int32_t cnt[PER], sum = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) { cnt[i] = hist[BINS - 1 - (tid * PER + i)]; sum += cnt[i]; }
     int32_t tot2;
-    const int32_t incl = block_inclusive_scan(cnt, sh_wave, tot2);
-    if (incl - cnt < need && incl >= need) { sh_pick[0] = kBins - 1 - tid; sh_pick[1] = incl - cnt; }
+    int32_t run = block_inclusive_scan(sum, sh_wave, tot2) - sum;   // keys in higher bins
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (run < need && run + cnt[i] >= need) { sh_pick[0] = BINS - 1 - (tid * PER + i); sh_pick[1] = run; }
+      run += cnt[i];
+    }
     __syncthreads();
     const uint32_t pick = (uint32_t)sh_pick[0];
     const int32_t above = sh_pick[1];

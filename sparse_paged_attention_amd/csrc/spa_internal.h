@@ -55,7 +55,8 @@ struct AttnPlan {
 
 // ---- launchers (return hipError_t of the launch) -------------------------
 hipError_t launch_append(const PoolArgs& pool, const BatchArgs& batch,
-                         const uint16_t* k_new, const uint16_t* v_new, hipStream_t s);
+                         const uint16_t* k_new, const uint16_t* v_new,
+                         const HeadList* dyn, hipStream_t s);
 hipError_t launch_write(const PoolArgs& pool, const int32_t* pt_row, int32_t max_pp,
                         int64_t start, int64_t count, const uint16_t* k,
                         const uint16_t* v, hipStream_t s);

@@ -71,8 +71,7 @@ class DecodeLayer:
     def append(self, k_new: torch.Tensor, v_new: torch.Tensor) -> None:
         """Appends one token to every sequence: k_new, v_new bf16 [B][H_kv][D].
         seq_lens must already count the new token (see use_lengths / set_lengths)."""
-        kv_pool_append(self.pool, self.batch, k_new, v_new)
-        page_summary_update(self.pool, self.heads, self.batch)
+        kv_pool_append(self.pool, self.batch, k_new, v_new, heads=self.heads)
 
     def select(self, q: torch.Tensor, scores=None) -> None:
         select_pages(self.pool, self.heads, self.batch, q, self.budget, self.k_max, self.sel_pages,

@@ -164,7 +164,10 @@ def test_select_and_summary_validation(spa):
                                      None, 5, None) == 1
     assert L.spa_page_summary_update(ctypes.byref(pool), ctypes.byref(heads), ctypes.byref(batch),
                                      FAKE, 0, None) == 1
-    assert L.spa_kv_pool_append(ctypes.byref(pool), ctypes.byref(batch), None, FAKE, None) == 1
+    assert L.spa_kv_pool_append(ctypes.byref(pool), None, ctypes.byref(batch), None, FAKE, None) == 1
+    bad_heads = mkheads(spa, kind=(0, 0, 0, 0, 1, 1, 1, 3))
+    assert L.spa_kv_pool_append(ctypes.byref(pool), ctypes.byref(bad_heads), ctypes.byref(batch), FAKE,
+                                FAKE, None) == 1
     assert L.spa_kv_pool_write(ctypes.byref(pool), FAKE, 4, 250, 10, FAKE, FAKE, None) == 1
     assert L.spa_kv_pool_write(ctypes.byref(pool), FAKE, 4, -1, 1, FAKE, FAKE, None) == 1
     assert L.spa_kv_pool_write(ctypes.byref(pool), None, 4, 0, 1, FAKE, FAKE, None) == 1

@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sparse decode-attn µs/step + achieved HBM GB/s (% peak) at 128K ctx"
 PEAK_GBPS = 8000.0
+COPY_BYTES = 1 << 30          # calibration copy for the HBM byte counters
 WORKLOAD = "llama3_128k"
 
 
@@ -103,6 +104,9 @@ def main() -> int:
     ap.add_argument("--replicas", type=int, default=8, help="layer replicas the steps cycle over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--threads", type=int, default=16)
+    ap.add_argument("--probe", action="store_true",
+                    help="counter-collection mode: run the steps eagerly, then a plain copy of "
+                         "COPY_BYTES for calibration; prints no result line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path keeps every "
@@ -113,6 +117,7 @@ def main() -> int:
     import workloads as W
     import sparse_paged_attention_amd as spa
     from sparse_paged_attention_amd.runner import DecodeLayer
+    from sparse_paged_attention_amd.profiling import attn_source_hash
 
     spa.lib()
     torch.cuda.set_device(0)
@@ -181,6 +186,16 @@ def main() -> int:
         layer_step(s)
     torch.cuda.synchronize()
 
+    if args.probe:
+        for s in range(args.warmup, total_steps):
+            layer_step(s)
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] probe done: {args.steps} steps, copy of {COPY_BYTES} bytes")
+        return 0
+
     # capture the timed steps once; replays are idempotent (same tokens are
     # re-appended at the same positions, selections recomputed identically)
     g = torch.cuda.CUDAGraph()
@@ -236,7 +251,7 @@ def main() -> int:
     if os.path.exists(tpath):
         try:
             tr = json.load(open(tpath))
-            traffic = tr.get("bytes_per_launch") if tr.get("kernel_source_hash") == _attn_hash() else None
+            traffic = tr.get("bytes_per_launch") if tr.get("kernel_source_hash") == attn_source_hash() else None
         except Exception:
             traffic = None
 
@@ -270,14 +285,6 @@ def main() -> int:
     }
     print(json.dumps(res), flush=True)
     return 0
-
-
-def _attn_hash() -> str:
-    import hashlib
-    h = hashlib.sha256()
-    for f in ("attn.hip", "spa_internal.h"):
-        h.update(open(os.path.join(ROOT, "sparse_paged_attention_amd", "csrc", f), "rb").read())
-    return h.hexdigest()[:16]
 
 
 if __name__ == "__main__":

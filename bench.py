@@ -67,32 +67,37 @@ def algorithmic_bytes(wl, L: int, select: bool) -> dict:
                 total=attn + append + summary + sel)
 
 
-def cpu_baseline(wl, host_kv, sample_steps: int = 4) -> dict:
-    """The CPU oracle on a bounded sample: `sample_steps` decode steps
-    (one selection + reuse) of every sequence and KV head of one layer,
+def cpu_baseline(wl, host_kv, replicas: int, sample_steps: int = 16) -> dict:
+    """The CPU oracle on a bounded sample of the same job: the first
+    `sample_steps` decode steps (selections and reuse as scheduled) of every
+    layer replica, sequence and KV head, with the queries the GPU steps use,
     scaled to microseconds per layer-step."""
     import oracle
     import workloads as W
     oracle.build()
     G = wl.G
-    states = {(b, h): oracle.HeadState(wl.k_max) for b in range(wl.batch) for h in range(wl.hkv)}
+    states = {(r, b, h): oracle.HeadState(wl.k_max)
+              for r in range(replicas) for b in range(wl.batch) for h in range(wl.hkv)}
     t0 = time.perf_counter()
     for i in range(sample_steps):
-        jobs = []
-        for b in range(wl.batch):
-            L = wl.seq_len(b, i)
-            q = W.query(wl, b, i)
-            K, V = host_kv[b]
-            for h in range(wl.hkv):
-                jobs.append(dict(K=K[h, :L], V=V[h, :L], q=q[h * G:(h + 1) * G], dynamic=bool(wl.kind[h]),
-                                 sink=wl.sink, window=wl.window, p=wl.p, budget=wl.budget_at(L),
-                                 do_select=wl.selects_at(i), state=states[(b, h)]))
-        oracle.decode_heads(jobs)
+        for r in range(replicas):
+            jobs = []
+            for b in range(wl.batch):
+                L = wl.seq_len(b, i)
+                q = W.query(wl, b, i * replicas + r)
+                K, V = host_kv[b]
+                for h in range(wl.hkv):
+                    jobs.append(dict(K=K[h, :L], V=V[h, :L], q=q[h * G:(h + 1) * G], dynamic=bool(wl.kind[h]),
+                                     sink=wl.sink, window=wl.window, p=wl.p, budget=wl.budget_at(L),
+                                     do_select=wl.selects_at(i), state=states[(r, b, h)]))
+            oracle.decode_heads(jobs)
     dt = time.perf_counter() - t0
-    return {"value": round(dt / sample_steps * 1e6, 1), "unit": "us/step", "cores": oracle.num_threads(),
+    n = sample_steps * replicas
+    n_sel = sum(1 for i in range(sample_steps) if wl.selects_at(i))
+    return {"value": round(dt / n * 1e6, 1), "unit": "us/step", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{sample_steps} decode steps (1 selection + {sample_steps - 1} reuse) of all "
-                      f"{wl.batch} sequences x {wl.hkv} KV heads of one layer, fp64 oracle, "
+            "sample": f"{sample_steps} decode steps ({n_sel} with selection) x {replicas} layer replicas = "
+                      f"{n} layer-steps over all {wl.batch} sequences x {wl.hkv} KV heads, fp64 oracle, "
                       f"{dt:.1f} s total"}
 
 
@@ -168,18 +173,14 @@ def main() -> int:
     log(f"[bench] setup {time.time() - t_setup:.1f}s; {R} replicas x "
         f"{layers[0].pool.k.numel() * 2 * 2 / 2**30:.2f} GiB K+V")
 
-    def layer_step(s: int, timed_attn=None):
+    def layer_step(s: int):
         t, r = divmod(s, R)
         layer = layers[r]
         layer.use_lengths(lens[t])
         layer.append(kn[t], vn[t])
         if wl.selects_at(t):
             layer.select(qs[s])
-        if timed_attn is not None:
-            timed_attn[0].record()
         layer.attend(qs[s])
-        if timed_attn is not None:
-            timed_attn[1].record()
 
     # warm-up (eager, also compiles nothing: kernels are prebuilt)
     for s in range(args.warmup):
@@ -216,35 +217,39 @@ def main() -> int:
     gpu_ms = ev0.elapsed_time(ev1)
     ms_per_step = gpu_ms / args.steps
 
-    # per-launch time of the attention call over the same steps, events on
-    # its stream; a sleep kernel keeps the GPU behind the CPU so launches
-    # queue back to back
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(args.steps)]
-    torch.cuda._sleep(int(60e6))
-    for i, s in enumerate(range(args.warmup, total_steps)):
-        layer_step(s, pairs[i])
+    # per-call time of the attention entry point (attn_kernel + combine_kernel):
+    # a graph of `steps` attention calls cycling over the replicas at the
+    # state the timed steps left (last decode step's lengths and selections),
+    # replayed between two events on the capturing stream
+    t_last = (total_steps - 1) // R
+    ga = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(ga):
+        for i in range(args.steps):
+            r = i % R
+            layers[r].use_lengths(lens[t_last])
+            layers[r].attend(qs[t_last * R + r])
+    ga.replay()
     torch.cuda.synchronize()
-    attn_ms = [a.elapsed_time(b) for a, b in pairs]
-    attn_avg_us = 1e3 * sum(attn_ms) / len(attn_ms)
+    ea0, ea1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ea0.record()
+    ga.replay()
+    ea1.record()
+    torch.cuda.synchronize()
+    attn_avg_us = 1e3 * ea0.elapsed_time(ea1) / args.steps
+    attn_bytes_call = algorithmic_bytes(wl, wl.seq_len(0, t_last), False)["attn"]
 
     # algorithmic bytes over the timed steps
     tot = 0
-    attn_bytes = 0
     for s in range(args.warmup, total_steps):
         t = s // R
-        L = wl.seq_len(0, t)
-        ab = algorithmic_bytes(wl, L, wl.selects_at(t))
-        tot += ab["total"]
-        attn_bytes += ab["attn"]
+        tot += algorithmic_bytes(wl, wl.seq_len(0, t), wl.selects_at(t))["total"]
     bytes_per_step = tot / args.steps
-    attn_bytes_avg = attn_bytes / args.steps
     gbps = bytes_per_step / (ms_per_step * 1e-3) / 1e9
-    attn_gbps = attn_bytes_avg / (attn_avg_us * 1e-6) / 1e9
+    attn_gbps = attn_bytes_call / (attn_avg_us * 1e-6) / 1e9
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, host_kv)
+        cpu = cpu_baseline(wl, host_kv, R)
 
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "attn_llama3_128k_traffic.json")
@@ -280,7 +285,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "kernel": "spa_sparse_decode_attn (attn_kernel + combine_kernel)",
                      "achieved": round(attn_gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attn_gbps / PEAK_GBPS, 4), "traffic": traffic,
-                     "avg_launch_us": round(attn_avg_us, 2), "bytes_per_launch": int(attn_bytes_avg)},
+                     "avg_launch_us": round(attn_avg_us, 2), "bytes_per_launch": int(attn_bytes_call)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -184,7 +184,8 @@ spa_status spa_select_pages(const spa_pool* pool, const spa_heads* heads,
  * online softmax (FlashAttention, long-context survey "2.1"; the max and sum
  * outputs of the Novita vLLM article, "2. 注意力机制修改").
  *   out: device fp32 [B][H_q][D]; lse: device fp32 [B][H_q] or NULL.
- *   sel_*: as written by spa_select_pages (not read for streaming heads);
+ *   sel_*: as written by spa_select_pages (page ids distinct; not read for
+ *          streaming heads);
  *   k_max: capacity of a sel_pages row.
  * A sequence with L_b < 1 gets out = 0 and lse = -inf. */
 spa_status spa_sparse_decode_attn(const spa_pool* pool, const spa_heads* heads,
@@ -196,11 +197,20 @@ spa_status spa_sparse_decode_attn(const spa_pool* pool, const spa_heads* heads,
 
 /* Workspace bytes needed by spa_select_pages and spa_sparse_decode_attn for
  * these shapes (one buffer serves both). Returns 0 for invalid arguments.
- * The workspace must be zero-filled once before its first use (its first
- * bytes hold per-head counters; every call leaves them at zero again). Calls
- * that share a workspace must not run concurrently. */
+ * The workspace needs no initialisation and holds nothing between calls;
+ * calls that share a workspace must not run concurrently. */
 size_t spa_workspace_bytes(const spa_pool* pool, const spa_heads* heads,
                            int32_t batch, int32_t max_pages, int32_t k_max);
+
+/* Tuning of spa_sparse_decode_attn's work split (no effect on results
+ * beyond floating-point summation order): the attended tokens of a head are
+ * cut into items of `blocks` 16-token blocks, one work-group per item, and
+ * the item partials are merged afterwards. 0 (the default) picks the size
+ * per call so that the busiest compute unit has the fewest blocks; 4, 5, 6,
+ * 7, 8, 9, 10, 12 or 16 fixes it (as does the SPA_ATTN_BLOCKS_PER_ITEM
+ * environment variable, read once). Any other value: SPA_ERR_INVALID.
+ * Process-wide; takes effect from the next call. */
+spa_status spa_set_attn_blocks_per_item(int32_t blocks);
 
 /* The write-up's dynamic budget rule ("3.2"): min(4096, L / 32) tokens,
  * integer division; 0 for L < 32. */

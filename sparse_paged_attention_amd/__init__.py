@@ -55,7 +55,8 @@ class c_batch(ctypes.Structure):
 EXPORTS = ("spa_kv_pool_append", "spa_kv_pool_write", "spa_page_summary_update",
            "spa_select_pages", "spa_sparse_decode_attn", "spa_workspace_bytes",
            "spa_default_budget", "spa_alloc_create", "spa_alloc_pages", "spa_alloc_free",
-           "spa_alloc_num_free", "spa_alloc_destroy", "spa_status_string", "spa_last_error")
+           "spa_alloc_num_free", "spa_alloc_destroy", "spa_status_string", "spa_last_error",
+           "spa_set_attn_blocks_per_item")
 
 _lib = None
 
@@ -78,6 +79,7 @@ def lib() -> ctypes.CDLL:
             "spa_sparse_decode_attn": ([P, H, B, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp], ctypes.c_int),
             "spa_workspace_bytes": ([P, H, i32, i32, i32], sz),
             "spa_default_budget": ([i64], i32),
+            "spa_set_attn_blocks_per_item": ([i32], ctypes.c_int),
             "spa_alloc_create": ([i32, ctypes.POINTER(vp)], ctypes.c_int),
             "spa_alloc_pages": ([vp, i32, vp], ctypes.c_int),
             "spa_alloc_free": ([vp, i32, vp], ctypes.c_int),
@@ -293,6 +295,12 @@ def sparse_decode_attn(pool: Pool, heads: Heads, batch: Batch, q, sel_pages, sel
                                         _ptr(sel_pages), _ptr(sel_count), _ptr(sel_len), k_max,
                                         _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                         _stream(stream)))
+
+
+def set_attn_blocks_per_item(blocks: int) -> None:
+    """Fix the attention work-item size (16-token blocks per item), or 0 for
+    the per-call automatic choice (spa_set_attn_blocks_per_item)."""
+    _check(lib().spa_set_attn_blocks_per_item(blocks))
 
 
 def default_budget(context_len: int) -> int:

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -39,16 +40,48 @@ spa_status hip_status(hipError_t e, const char* what) {
   return fail(SPA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Attention blocks per work item (16 tokens each): 4, 8 or 16; the
-// SPA_ATTN_BLOCKS_PER_ITEM environment variable overrides the default.
-int32_t blocks_per_item() {
-  static const int32_t v = [] {
+// Attention blocks per work item (16 tokens each). All work-groups of a
+// launch are resident at once and the dispatcher spreads them evenly over
+// the compute units, so the launch lasts as long as the busiest unit: the
+// item size is picked to minimise ceil(items / CUs) * blocks per item.
+// spa_set_attn_blocks_per_item() or the SPA_ATTN_BLOCKS_PER_ITEM environment
+// variable (one of kBpiChoices) fixes it instead.
+constexpr int32_t kBpiChoices[] = {4, 5, 6, 7, 8, 9, 10, 12, 16};
+constexpr int32_t kBpiMin = 4;
+
+bool valid_bpi(int32_t x) {
+  for (int32_t c : kBpiChoices)
+    if (x == c) return true;
+  return false;
+}
+
+std::atomic<int32_t> g_forced_bpi{-1};   // -1: not read yet, 0: automatic
+
+int32_t forced_blocks_per_item() {
+  int32_t v = g_forced_bpi.load(std::memory_order_relaxed);
+  if (v < 0) {
     const char* e = std::getenv("SPA_ATTN_BLOCKS_PER_ITEM");
     const int32_t x = e ? std::atoi(e) : 0;
-    return (x == 4 || x == 8 || x == 16) ? x : 8;
-  }();
+    v = valid_bpi(x) ? x : 0;
+    int32_t expect = -1;
+    if (!g_forced_bpi.compare_exchange_strong(expect, v)) v = expect;
+  }
   return v;
 }
+
+// Compute units of the current device (queried once per device).
+int32_t device_cus() {
+  static int32_t cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 // Largest page count a selection row can score (top-k keeps 32 keys per thread).
 constexpr int64_t kMaxScoredPages = 32768;
 
@@ -124,38 +157,58 @@ int32_t n_max_pages(const spa::PoolArgs& pl, int32_t max_pp) {
   return (int32_t)((int64_t)max_pp * pl.r);   // logical pages a page-table row can address
 }
 
-void plan_attention(const spa::PoolArgs& pl, const spa_heads* heads, int32_t k_max,
-                    const uint8_t* kind, spa::AttnPlan* plan) {
-  std::memset(plan, 0, sizeof *plan);
-  const int32_t bpi = blocks_per_item();
-  // streaming blocks: sink blocks + window blocks (+1 when the window is unaligned)
+// Items per head for a given item size: streaming heads cover the sink and
+// window blocks (+1 when the window is unaligned), dynamic heads k_max pages
+// plus one item for the tokens appended since the selection.
+void size_items(const spa::PoolArgs& pl, const spa_heads* heads, int32_t k_max, int32_t bpi,
+                spa::AttnPlan* plan) {
   const int64_t nb_stream = (heads->sink + 15) / 16 + (heads->window + 15) / 16 + 1;
   const int64_t nb_dyn = (int64_t)k_max * (pl.p / 16);
   plan->blocks_per_item = bpi;
   plan->items_stream = (int32_t)((nb_stream + bpi - 1) / bpi);
-  plan->items_dyn = (int32_t)((nb_dyn + bpi - 1) / bpi) + 1;       // + the tail item
+  plan->items_dyn = (int32_t)((nb_dyn + bpi - 1) / bpi) + 1;
   plan->item_stride = std::max(plan->items_stream, plan->items_dyn);
+}
+
+// batch < 0: size for the largest item count any batch size can use
+// (workspace sizing); otherwise pick the item size for this batch.
+void plan_attention(const spa::PoolArgs& pl, const spa_heads* heads, int32_t k_max, const uint8_t* kind,
+                    int32_t batch, spa::AttnPlan* plan) {
+  std::memset(plan, 0, sizeof *plan);
+  int32_t n_dyn = 0;
+  for (int32_t h = 0; h < pl.hkv; ++h)
+    if (kind[h]) {
+      plan->dyn_mask[h / 32] |= 1u << (h % 32);
+      ++n_dyn;
+    }
+  const int32_t n_str = pl.hkv - n_dyn;
+  int32_t bpi = forced_blocks_per_item();
+  if (batch < 0) {
+    bpi = kBpiMin;
+  } else if (bpi == 0) {
+    const int64_t cus = device_cus();
+    int64_t best = -1;
+    for (int32_t c : kBpiChoices) {
+      spa::AttnPlan t;
+      size_items(pl, heads, k_max, c, &t);
+      const int64_t items = (int64_t)std::max(batch, 1) * (n_str * (int64_t)t.items_stream +
+                                                           n_dyn * (int64_t)(t.items_dyn - 1));
+      const int64_t cost = (items + cus - 1) / cus * c;
+      if (best < 0 || cost <= best) {      // ties go to the larger item
+        best = cost;
+        bpi = c;
+      }
+    }
+  }
+  size_items(pl, heads, k_max, bpi, plan);
+  plan->items_per_seq = n_str * plan->items_stream + n_dyn * plan->items_dyn;
   plan->sink = heads->sink;
   plan->window = heads->window;
   plan->k_max = k_max;
-  for (int32_t h = 0; h < pl.hkv; ++h) {
-    plan->kind[h] = kind[h];
-    if (kind[h]) plan->dyn_ids[plan->n_dyn++] = (uint8_t)h;
-    else plan->stream_ids[plan->n_stream++] = (uint8_t)h;
-  }
 }
 
-int64_t attn_items_per_seq(const spa::AttnPlan& plan) {
-  return (int64_t)plan.n_stream * plan.items_stream + (int64_t)plan.n_dyn * plan.items_dyn;
-}
-
-// Workspace layout: [ticket counters: B * H_kv int32, kept zero between calls]
-// then a scratch area shared by selection (page scores) and attention
-// (per-item partials).
-size_t ticket_bytes(const spa::PoolArgs& pl, int32_t B) {
-  return align_up((size_t)B * pl.hkv * sizeof(int32_t));
-}
-
+// Workspace: a scratch area used by selection (page scores) and by attention
+// (per-item partials); nothing in it lives from one call to the next.
 size_t attn_bytes(const spa::PoolArgs& pl, const spa::AttnPlan& plan, int32_t B, int32_t G, size_t* ml_off) {
   const size_t slots = (size_t)B * pl.hkv * plan.item_stride * G;
   const size_t o = align_up(slots * spa::kHeadDim * sizeof(float));
@@ -184,6 +237,13 @@ const char* spa_status_string(spa_status s) {
 }
 
 const char* spa_last_error(void) { return g_last_error.c_str(); }
+
+spa_status spa_set_attn_blocks_per_item(int32_t blocks) {
+  if (blocks != 0 && !valid_bpi(blocks))
+    return fail(SPA_ERR_INVALID, "blocks per item %d: use 0 or one of 4, 5, 6, 7, 8, 9, 10, 12, 16", blocks);
+  g_forced_bpi.store(blocks, std::memory_order_relaxed);
+  return ok();
+}
 
 int32_t spa_default_budget(int64_t context_len) {
   if (context_len < 0) return 0;
@@ -258,10 +318,9 @@ size_t spa_workspace_bytes(const spa_pool* pool, const spa_heads* heads, int32_t
   if (check_pool(pool, &pl) == SPA_OK && check_heads(heads, pl, &G, &dyn, kind) == SPA_OK &&
       batch >= 0 && max_pages >= 1 && k_max >= 1) {
     spa::AttnPlan plan;
-    plan_attention(pl, heads, k_max, kind, &plan);
+    plan_attention(pl, heads, k_max, kind, -1, &plan);
     size_t ml_off;
-    bytes = ticket_bytes(pl, batch) +
-            std::max(attn_bytes(pl, plan, batch, G, &ml_off), select_bytes(pl, batch, max_pages));
+    bytes = std::max(attn_bytes(pl, plan, batch, G, &ml_off), select_bytes(pl, batch, max_pages));
     bytes = std::max<size_t>(bytes, 256);
   }
   g_last_error = keep;
@@ -291,10 +350,10 @@ spa_status spa_select_pages(const spa_pool* pool, const spa_heads* heads, const 
     return fail(SPA_ERR_INVALID, "q / budget_tokens / sel_pages / sel_count / sel_len is NULL");
   float* sc = scores;
   if (!sc) {
-    const size_t need = ticket_bytes(pl, bt.B) + select_bytes(pl, bt.B, bt.max_pp);
+    const size_t need = select_bytes(pl, bt.B, bt.max_pp);
     if (!ws || ws_bytes < need)
       return fail(SPA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
-    sc = reinterpret_cast<float*>(static_cast<char*>(ws) + ticket_bytes(pl, bt.B));
+    sc = static_cast<float*>(ws);
   }
   return hip_status(spa::launch_select(pl, bt, dyn, G, static_cast<const uint16_t*>(q), budget_tokens, k_max,
                                        sel_pages, sel_count, sel_len, sc, n_max, stream),
@@ -320,20 +379,21 @@ spa_status spa_sparse_decode_attn(const spa_pool* pool, const spa_heads* heads, 
   if (dyn.n > 0 && (!sel_pages || !sel_count || !sel_len))
     return fail(SPA_ERR_INVALID, "dynamic heads need sel_pages / sel_count / sel_len");
   spa::AttnPlan plan;
-  plan_attention(pl, heads, k_max, kind, &plan);
-  if ((int64_t)bt.B * attn_items_per_seq(plan) > INT32_MAX) return fail(SPA_ERR_INVALID, "grid too large");
-  if ((int64_t)plan.item_stride * G > spa::kMaxPartialsPerHead)
-    return fail(SPA_ERR_UNSUPPORTED, "k_max %d with %d query heads per KV head needs %lld partials per head "
-                "(at most %d)", k_max, G, (long long)plan.item_stride * G, spa::kMaxPartialsPerHead);
+  plan_attention(pl, heads, k_max, kind, bt.B, &plan);
+  if ((int64_t)bt.B * plan.items_per_seq > INT32_MAX) return fail(SPA_ERR_INVALID, "grid too large");
+  plan.sel_mask = dyn.n > 0 ? ~int64_t(0) : 0;
+  if (dyn.n == 0) {                 // never used; read at index 0 to keep the loads branch-free
+    sel_pages = bt.lens;
+    sel_count = bt.lens;
+    sel_len = bt.lens;
+  }
   size_t ml_off;
-  const size_t tb = ticket_bytes(pl, bt.B);
-  const size_t need = tb + attn_bytes(pl, plan, bt.B, G, &ml_off);
+  const size_t need = attn_bytes(pl, plan, bt.B, G, &ml_off);
   if (!ws || ws_bytes < need) return fail(SPA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
-  int32_t* tickets = static_cast<int32_t*>(ws);
-  float* part_o = reinterpret_cast<float*>(static_cast<char*>(ws) + tb);
-  float* part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + tb + ml_off);
+  float* part_o = static_cast<float*>(ws);
+  float* part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + ml_off);
   return hip_status(spa::launch_attn(pl, bt, plan, G, static_cast<const uint16_t*>(q), sel_pages, sel_count,
-                                     sel_len, out, lse, part_o, part_ml, tickets, stream),
+                                     sel_len, out, lse, part_o, part_ml, stream),
                     "sparse_decode_attn launch");
 }
 

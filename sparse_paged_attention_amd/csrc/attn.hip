@@ -28,6 +28,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // log2(e) / sqrt(128): scores are kept in the log2 domain
 constexpr float kScaleLog2 = 0.12751743074602467f;
@@ -39,10 +41,12 @@ __device__ __forceinline__ int32_t clamp_len(const BatchArgs& bt, int32_t b, int
   return L < 0 ? 0 : (L > cap ? cap : L);
 }
 
-__device__ __forceinline__ uint16_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// The same memory seen through the constant address space: wave-uniform
+// loads from it are scalar loads. Only for data no kernel of the launch
+// writes (lengths, selections, page table).
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T* as_scalar(const T* p) {
+  return (const __attribute__((address_space(4))) T*)p;
 }
 
 // A 16-token block: absolute positions [t0, t0 + 16), of which [lo, hi) count,
@@ -58,24 +62,40 @@ struct Tile {
 };
 
 // Issues the loads of a block's tile. Empty blocks load from page 0 of the
-// pool (always mapped), so the loads never depend on control flow.
+// pool (always mapped), so the loads never depend on control flow. The block
+// base is wave-uniform and each lane adds a fixed 32-bit offset, so every
+// load is a scalar-base + vector-offset access with no 64-bit address math.
 template <int PG>
 __device__ __forceinline__ void issue_tile(const PoolArgs& pl, int32_t h, const Block& blk, Tile& t) {
   const int lane = threadIdx.x & 63;
   const int row = lane & 15, quad = lane >> 4;
   const int64_t head = (int64_t)blk.phys * pl.hkv + h;
   const int32_t in_page = blk.t0 & (PG - 1);
-  const uint4* k4 = reinterpret_cast<const uint4*>(
-      pl.k + ((head * pl.P + blk.lp * PG + in_page + row) * kHeadDim + 32 * quad));
+  const uint16_t* kb = pl.k + (head * pl.P + blk.lp * PG + in_page) * kHeadDim;
+  const uint16_t* vb = pl.v + (head * pl.r + blk.lp) * (int64_t)(kHeadDim * PG) + in_page;
+  const uint32_t koff = row * kHeadDim + 32 * quad, voff = row * PG + 4 * quad;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) t.k[i] = k4[i];
-  const uint16_t* vp = pl.v + ((head * pl.r + blk.lp) * kHeadDim + row) * PG + in_page + 4 * quad;
+  for (int i = 0; i < 4; ++i) t.k[i] = *reinterpret_cast<const uint4*>(kb + koff + 8 * i);
 #pragma unroll
-  for (int ch = 0; ch < 8; ++ch) t.v[ch] = *reinterpret_cast<const uint2*>(vp + 16 * ch * PG);
+  for (int ch = 0; ch < 8; ++ch) t.v[ch] = *reinterpret_cast<const uint2*>(vb + voff + 16 * ch * PG);
+}
+
+// A pipeline slot: a real block's loads, or zeros for the padding slot
+// (`real` is a constant once the pipeline loop is unrolled).
+template <int PG>
+__device__ __forceinline__ void fill_tile(const PoolArgs& pl, int32_t h, const Block& blk, Tile& t, bool real) {
+  if (real) {
+    issue_tile<PG>(pl, h, blk, t);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t.k[i] = uint4{0, 0, 0, 0};
+#pragma unroll
+    for (int ch = 0; ch < 8; ++ch) t.v[ch] = uint2{0, 0};
+  }
 }
 
 struct State {
-  float m;          // running max of this lane's query, log2 domain
+  float m;          // running reference (near the maximum) of this lane's query, log2 units
   float l;          // running sum over this lane's tokens
   f32x4 o[8];       // O^T: channels 16c + 4*quad + r of query (lane & 15)
 };
@@ -100,6 +120,13 @@ __device__ __forceinline__ f32x4 qk_block(const Tile& t, const bf16x8 (&qb)[4]) 
   return s;
 }
 
+// The running reference of the online softmax is raised only when a block's
+// maximum exceeds it by more than this (log2 units): probabilities then stay
+// below 2^kRescaleSlack, and the rescale of the accumulators (which live in
+// accumulation registers) is rare instead of happening on most blocks.
+// out = o / l and lse = ref + log2(l) are unchanged by the choice of reference.
+constexpr float kRescaleSlack = 8.f;
+
 // Two blocks (32 tokens) at once. The PV product contracts over 32 tokens
 // with one 16x16x32 MFMA per 16 channels: K-slot j of lane row q holds token
 // 4q + j of block a (j < 4) or token 4q + j - 4 of block b (j >= 4), which is
@@ -110,215 +137,256 @@ __device__ __forceinline__ void process_pair(const Block& ba, const Tile& ta, co
   const int quad = lane >> 4;
   const f32x4 sa = qk_block(ta, qb);
   const f32x4 sb = qk_block(tb, qb);
-  float x[8];
+  const bool full = ba.lo <= ba.t0 && ba.hi >= ba.t0 + kBlockTokens &&
+                    bb.lo <= bb.t0 && bb.hi >= bb.t0 + kBlockTokens;
   bool valid[8];
+  float s[8];
   float bm = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int32_t tka = ba.t0 + 4 * quad + r, tkb = bb.t0 + 4 * quad + r;
-    valid[r] = tka >= ba.lo && tka < ba.hi;
-    valid[4 + r] = tkb >= bb.lo && tkb < bb.hi;
-    x[r] = valid[r] ? sa[r] * kScaleLog2 : -INFINITY;
-    x[4 + r] = valid[4 + r] ? sb[r] * kScaleLog2 : -INFINITY;
-    bm = fmaxf(bm, fmaxf(x[r], x[4 + r]));
+    valid[r] = full || (tka >= ba.lo && tka < ba.hi);
+    valid[4 + r] = full || (tkb >= bb.lo && tkb < bb.hi);
+    s[r] = valid[r] ? sa[r] : -INFINITY;
+    s[4 + r] = valid[4 + r] ? sb[r] : -INFINITY;
+    bm = fmaxf(bm, fmaxf(s[r], s[4 + r]));
   }
-  bm = max_over_rows(bm);
+  bm = max_over_rows(bm) * kScaleLog2;            // this query's maximum over the pair, log2 units
   if (bm == -INFINITY) return;                    // no valid token (same for every lane)
-  const float m_new = fmaxf(st.m, bm);
-  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+  const bool first = st.m == -INFINITY;
+  const bool raise = bm > st.m + kRescaleSlack;   // always true on the first block
+  const float m_new = raise ? bm : st.m;
+  if (__any(raise && !first)) {                   // o and l are still zero before the first block
+    const float alpha = raise && !first ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.f;
+    st.l *= alpha;
+#pragma unroll
+    for (int ch = 0; ch < 8; ++ch) st.o[ch] *= alpha;
+  }
+  st.m = m_new;
   float pr[8];
   float psum = 0.f;
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
-    pr[r] = __builtin_amdgcn_exp2f(x[r] - m_new);  // 0 for masked tokens
+    pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], kScaleLog2, -m_new));   // 0 for masked tokens
     psum += pr[r];
   }
-  st.l = st.l * alpha + psum;
-  st.m = m_new;
-  if (__any(alpha != 1.f)) {
-#pragma unroll
-    for (int ch = 0; ch < 8; ++ch) st.o[ch] *= alpha;
-  }
+  st.l += psum;
+  // P split into bf16 high and low parts (native round-to-nearest-even conversions)
   bf16x8 phi, plo;
-  {
-    uint16_t hb[8], lb[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      hb[r] = bf16_rne(pr[r]);
-      lb[r] = bf16_rne(pr[r] - __uint_as_float((uint32_t)hb[r] << 16));
-    }
-    __builtin_memcpy(&phi, hb, 16);
-    __builtin_memcpy(&plo, lb, 16);
+  for (int r = 0; r < 8; r += 2) {
+    const f32x2 v = {pr[r], pr[r + 1]};
+    const bf16x2 h = __builtin_convertvector(v, bf16x2);
+    const f32x2 rest = v - __builtin_convertvector(h, f32x2);
+    const bf16x2 lo = __builtin_convertvector(rest, bf16x2);
+    phi[r] = h[0]; phi[r + 1] = h[1];
+    plo[r] = lo[0]; plo[r + 1] = lo[1];
   }
-  const bool full = ba.lo <= ba.t0 && ba.hi >= ba.t0 + kBlockTokens &&
-                    bb.lo <= bb.t0 && bb.hi >= bb.t0 + kBlockTokens;
-  uint32_t mk[4];
+  uint4 w[8];
 #pragma unroll
-  for (int w = 0; w < 4; ++w)
-    mk[w] = (valid[2 * w] ? 0x0000FFFFu : 0u) | (valid[2 * w + 1] ? 0xFFFF0000u : 0u);
+  for (int ch = 0; ch < 8; ++ch) w[ch] = uint4{ta.v[ch].x, ta.v[ch].y, tb.v[ch].x, tb.v[ch].y};
+  if (!full) {                                     // stale pool bytes must not reach the MFMA
+    asm volatile("" ::: "memory");                 // keep this a branch: full blocks skip it
+    uint32_t mk[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      mk[i] = (valid[2 * i] ? 0x0000FFFFu : 0u) | (valid[2 * i + 1] ? 0xFFFF0000u : 0u);
+#pragma unroll
+    for (int ch = 0; ch < 8; ++ch) {
+      w[ch].x &= mk[0];
+      w[ch].y &= mk[1];
+      w[ch].z &= mk[2];
+      w[ch].w &= mk[3];
+    }
+  }
 #pragma unroll
   for (int ch = 0; ch < 8; ++ch) {
-    uint4 w = {ta.v[ch].x, ta.v[ch].y, tb.v[ch].x, tb.v[ch].y};
-    if (!full) {                                   // stale pool bytes must not reach the MFMA
-      w.x &= mk[0];
-      w.y &= mk[1];
-      w.z &= mk[2];
-      w.w &= mk[3];
-    }
     bf16x8 a;
-    __builtin_memcpy(&a, &w, 16);
+    __builtin_memcpy(&a, &w[ch], 16);
     st.o[ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, st.o[ch], 0, 0, 0);
     st.o[ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, st.o[ch], 0, 0, 0);
   }
 }
 
-__device__ __forceinline__ bool page_selected(const int32_t* sel, int32_t cnt, int32_t j) {
-  int32_t lo = 0, hi = cnt;                        // ascending ids
-  while (lo < hi) {
-    const int32_t mid = (lo + hi) >> 1;
-    const int32_t x = sel[mid];
-    if (x == j) return true;
-    if (x < j) lo = mid + 1; else hi = mid;
-  }
-  return false;
-}
-
 // Which blocks an item covers. Blocks are numbered per head:
 //   streaming: the sink blocks, then the window blocks;
-//   dynamic:   block (i, s) = 16-token block s of the i-th selected page;
-//   tail:      16-token blocks of [floor16(L_s), L) outside selected pages.
+//   dynamic:   block (i, s) = 16-token block s of the i-th selected page,
+//              limited to positions below L_s (the length at selection);
+//   tail:      16-token blocks of [floor16(L_s), L), limited to [L_s, L).
+// Selected pages below L_s plus all of [L_s, L) is the same token set as
+// selected pages below L plus the part of [L_s, L) outside them, and needs
+// no membership test.
 struct BlockSource {
   int32_t kind;          // 0 streaming, 1 dynamic, 2 tail
-  int32_t L;
+  int32_t L, ls;         // ls: L_s clamped to [0, L]
   int32_t s0, w0, nb_sink, first_w;          // streaming
-  const int32_t* sel;
-  int32_t cnt, k_max;                        // dynamic / tail
-  int32_t ls_floor, ls;                      // tail
+  int32_t ls_floor;                          // tail
 };
 
 // Resolves blocks [v0, v0 + BPI) (those at or past v_end are empty) to pool
 // locations, then streams them through a ring of DEPTH operand tiles: the
 // first DEPTH blocks' loads are issued together, and each tile is refilled
-// with block u + DEPTH as soon as block u has been computed. Every lookup
-// (selected page ids, page-table entries) is issued unconditionally with a
-// clamped index, so each level of the lookup costs one memory round trip for
-// the whole item. The kernel has a single call site, so one copy of the
-// pipeline serves every kind of item (instruction-cache footprint).
+// with block u + DEPTH as soon as block u has been computed. The look-ups
+// (selected page ids, page-table entries) are wave-uniform scalar loads:
+// they travel on the scalar-memory path, so they never queue behind the
+// tile loads other waves of the compute unit have in flight, and every
+// level of look-up costs one round trip for the whole item. For selected
+// pages the page-table entry depends only on the page id (`page`, loaded by
+// the caller before the lengths arrive). The kernel has a single call site,
+// so one copy of the pipeline serves every kind of item (instruction-cache
+// footprint).
 template <int PG, int BPI, int DEPTH>
 __device__ __forceinline__ void run_blocks(const PoolArgs& pl, const int32_t* pt_row,
                                            int32_t max_pp, int32_t h, const BlockSource& src,
-                                           int32_t v0, int32_t v_end, const bf16x8 (&qb)[4],
-                                           State& st) {
+                                           const int32_t (&page)[(BPI + 1) & ~1], int32_t v0, int32_t v_end,
+                                           const bf16x8 (&qb)[4], State& st) {
   constexpr int SB = PG / kBlockTokens;           // blocks per logical page
+  constexpr int NB = (BPI + 1) & ~1;              // pipeline slots: BPI rounded up to pairs
+  const int32_t r = pl.P / PG;
   const int32_t L = src.L;
-  const int32_t n_pages = (L + PG - 1) / PG;
-  Block blk[BPI];
+  const auto pt = as_scalar(pt_row);
+  Block blk[NB];
+  int32_t ptv[NB];
   if (src.kind == 1) {
-    int32_t page[BPI];
 #pragma unroll
-    for (int u = 0; u < BPI; ++u) {
-      const int32_t i = min((v0 + u) / SB, src.k_max - 1);
-      page[u] = src.sel[i];
-    }
+    for (int u = 0; u < NB; ++u) ptv[u] = pt[min(max(page[u], 0) / r, max_pp - 1)];
+    const int32_t n_pages_s = (src.ls + PG - 1) / PG;
 #pragma unroll
-    for (int u = 0; u < BPI; ++u) {
+    for (int u = 0; u < NB; ++u) {
       const int32_t j = page[u];
-      const bool ok = v0 + u < v_end && j >= 0 && j < n_pages;
+      const bool ok = v0 + u < v_end && j >= 0 && j < n_pages_s;
       const int32_t t0 = ok ? j * PG + ((v0 + u) % SB) * kBlockTokens : 0;
-      blk[u] = Block{t0, t0, ok ? min(t0 + kBlockTokens, L) : t0, 0, 0};
-    }
-  } else if (src.kind == 0) {
-#pragma unroll
-    for (int u = 0; u < BPI; ++u) {
-      const int32_t v = v0 + u;
-      int32_t t0, lo, hi;
-      if (v < src.nb_sink) {
-        t0 = v * kBlockTokens; lo = t0; hi = min(t0 + kBlockTokens, src.s0);
-      } else {
-        t0 = (src.first_w + v - src.nb_sink) * kBlockTokens; lo = max(t0, src.w0); hi = min(t0 + kBlockTokens, L);
-      }
-      if (v >= v_end) { t0 = 0; lo = 0; hi = 0; }
-      blk[u] = Block{t0, lo, hi, 0, 0};
+      blk[u] = Block{t0, t0, ok ? min(t0 + kBlockTokens, src.ls) : t0, 0, 0};
     }
   } else {
+    if (src.kind == 0) {
 #pragma unroll
-    for (int u = 0; u < BPI; ++u) {
-      const int32_t t0 = src.ls_floor + (v0 + u) * kBlockTokens;
-      int32_t lo = max(t0, src.ls), hi = min(t0 + kBlockTokens, L);
-      if (v0 + u >= v_end || page_selected(src.sel, src.cnt, t0 / PG)) hi = lo;
-      blk[u] = Block{hi > lo ? t0 : 0, lo, hi, 0, 0};
+      for (int u = 0; u < NB; ++u) {
+        const int32_t v = v0 + u;
+        int32_t t0, lo, hi;
+        if (v < src.nb_sink) {
+          t0 = v * kBlockTokens; lo = t0; hi = min(t0 + kBlockTokens, src.s0);
+        } else {
+          t0 = (src.first_w + v - src.nb_sink) * kBlockTokens; lo = max(t0, src.w0); hi = min(t0 + kBlockTokens, L);
+        }
+        if (v >= v_end) { t0 = 0; lo = 0; hi = 0; }
+        blk[u] = Block{t0, lo, hi, 0, 0};
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int32_t t0 = src.ls_floor + (v0 + u) * kBlockTokens;
+        const int32_t lo = max(t0, src.ls), hi = v0 + u < v_end ? min(t0 + kBlockTokens, L) : lo;
+        blk[u] = Block{hi > lo ? t0 : 0, lo, hi, 0, 0};
+      }
     }
-  }
-  int32_t ptv[BPI];
 #pragma unroll
-  for (int u = 0; u < BPI; ++u) {
-    const int32_t slot = min((blk[u].t0 / PG) / (pl.P / PG), max_pp - 1);
-    ptv[u] = pt_row[slot];
+    for (int u = 0; u < NB; ++u) ptv[u] = pt[min(blk[u].t0 / pl.P, max_pp - 1)];
   }
 #pragma unroll
-  for (int u = 0; u < BPI; ++u) {
+  for (int u = 0; u < NB; ++u) {
     const int32_t j = blk[u].t0 / PG;
     int32_t phys = ptv[u];
     if (phys < 0 || phys >= pl.N || blk[u].hi <= blk[u].lo) { phys = 0; blk[u].hi = blk[u].lo; blk[u].t0 = 0; }
     blk[u].phys = phys;
-    blk[u].lp = blk[u].hi > blk[u].lo ? j % (pl.P / PG) : 0;
+    blk[u].lp = blk[u].hi > blk[u].lo ? j % r : 0;
   }
-  // blocks go in pairs; DEPTH (even) tiles are in flight
-  static_assert(BPI % 2 == 0 && DEPTH % 2 == 0, "blocks are processed in pairs");
-  constexpr int D = DEPTH < BPI ? DEPTH : BPI;
+  // blocks go in pairs; DEPTH (even) tiles are in flight; the padding slot
+  // of an odd BPI is empty and loads nothing
+  static_assert(DEPTH % 2 == 0, "blocks are processed in pairs");
+  constexpr int D = DEPTH < NB ? DEPTH : NB;
   Tile t[D];
 #pragma unroll
-  for (int u = 0; u < D; ++u) issue_tile<PG>(pl, h, blk[u], t[u]);
+  for (int u = 0; u < D; ++u) fill_tile<PG>(pl, h, blk[u], t[u], u < BPI);
 #pragma unroll
-  for (int u = 0; u < BPI; u += 2) {
+  for (int u = 0; u < NB; u += 2) {
     if (blk[u].lo < blk[u].hi || blk[u + 1].lo < blk[u + 1].hi)
       process_pair(blk[u], t[u % D], blk[u + 1], t[(u + 1) % D], qb, st);
-    if (u + D < BPI) {
-      issue_tile<PG>(pl, h, blk[u + D], t[u % D]);
-      issue_tile<PG>(pl, h, blk[u + 1 + D], t[(u + 1) % D]);
+    if (u + D < NB) {
+      fill_tile<PG>(pl, h, blk[u + D], t[u % D], u + D < BPI);
+      fill_tile<PG>(pl, h, blk[u + 1 + D], t[(u + 1) % D], u + 1 + D < BPI);
     }
   }
 }
 
+// The dynamic-head mask as opaque register values, so that nothing below
+// turns into an indexed reload of the launch arguments (one more memory
+// round trip).
+struct HeadMask {
+  uint32_t w0, w1, w2, w3;
+  __device__ __forceinline__ explicit HeadMask(const AttnPlan& plan)
+      : w0(plan.dyn_mask[0]), w1(plan.dyn_mask[1]), w2(plan.dyn_mask[2]), w3(plan.dyn_mask[3]) {
+    asm volatile("" : "+s"(w0), "+s"(w1), "+s"(w2), "+s"(w3));
+  }
+  // (written with counts only: a select among the words gets turned back
+  // into an indexed array read)
+  __device__ __forceinline__ bool dynamic(int32_t h) const { return below(h + 1) != below(h); }
+  // dynamic heads among [0, h)
+  __device__ __forceinline__ int32_t below(int32_t h) const {
+    return part(w0, h) + part(w1, h - 32) + part(w2, h - 64) + part(w3, h - 96);
+  }
+  __device__ __forceinline__ static int32_t part(uint32_t w, int32_t k) {
+    return k <= 0 ? 0 : __popc(k >= 32 ? w : w & ((1u << k) - 1u));
+  }
+};
+
 // One item of one (sequence, KV head): the online softmax over its blocks and
-// a partial (max, sum, unnormalised output) per query head. Items are laid
-// out as [streaming: B x n_stream x items_stream][dynamic: B x n_dyn x items_dyn].
+// a partial (max, sum, unnormalised output) per query head.
 template <int PG, int BPI, int DEPTH>
 __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, AttnPlan plan, int32_t G,
-                                                  const uint16_t* __restrict__ q,
-                                                  const int32_t* __restrict__ sel_pages,
-                                                  const int32_t* __restrict__ sel_count,
-                                                  const int32_t* __restrict__ sel_len,
-                                                  float* __restrict__ part_o,
-                                                  float* __restrict__ part_ml) {
-  int32_t idx = blockIdx.x;
-  const int32_t n_stream_items = bt.B * plan.n_stream * plan.items_stream;
-  const bool dynamic = idx >= n_stream_items;
-  int32_t b, h, it;
-  if (!dynamic) {
-    const int32_t per_b = plan.n_stream * plan.items_stream;
-    b = idx / per_b;
-    const int32_t r = idx % per_b;
-    h = plan.stream_ids[r / plan.items_stream];
-    it = r % plan.items_stream;
-  } else {
-    idx -= n_stream_items;
-    const int32_t per_b = plan.n_dyn * plan.items_dyn;
-    b = idx / per_b;
-    const int32_t r = idx % per_b;
-    h = plan.dyn_ids[r / plan.items_dyn];
-    it = r % plan.items_dyn;
+                                                  const uint16_t* q, const int32_t* sel_pages,
+                                                  const int32_t* sel_count, const int32_t* sel_len,
+                                                  float* part_o, float* part_ml) {
+  constexpr int SB = PG / kBlockTokens;
+  // Every launch argument the kernel uses, read into registers in one round:
+  // left to itself the compiler fetches each argument just before its first
+  // use, one dependent scalar-memory round trip at a time.
+  asm volatile("" ::"s"(pl.hkv), "s"(pl.P), "s"(pl.N), "s"(bt.max_pp), "s"(plan.items_stream),
+               "s"(plan.items_dyn), "s"(plan.item_stride), "s"(plan.items_per_seq), "s"(plan.sink),
+               "s"(plan.window), "s"(plan.k_max),
+               "s"(G), "s"(plan.dyn_mask[0]), "s"(plan.dyn_mask[1]), "s"(plan.dyn_mask[2]),
+               "s"(plan.dyn_mask[3]), "s"(plan.sel_mask));
+  asm volatile("" ::"s"(pl.k), "s"(pl.v), "s"(bt.pt), "s"(bt.lens), "s"(sel_pages), "s"(sel_count),
+               "s"(sel_len), "s"(q), "s"(part_o), "s"(part_ml));
+  // work-group -> (sequence, head, item): head h's first item within the
+  // sequence is h * items_stream + (dynamic heads below h) * (items_dyn - items_stream)
+  const HeadMask mask(plan);
+  const int32_t b = blockIdx.x / plan.items_per_seq;
+  const int32_t rem = blockIdx.x - b * plan.items_per_seq;
+  const int32_t extra = plan.items_dyn - plan.items_stream;
+  int32_t h = 0;
+  for (int32_t hi = pl.hkv; hi - h > 1;) {
+    const int32_t mid = (h + hi) >> 1;
+    if (mid * plan.items_stream + mask.below(mid) * extra <= rem) h = mid; else hi = mid;
   }
+  const int32_t it = rem - (h * plan.items_stream + mask.below(h) * extra);
+  const bool dynamic = mask.dynamic(h);
   const int32_t n_items = dynamic ? plan.items_dyn : plan.items_stream;
-  // independent loads first: length, selection count / length, query
-  const int32_t L = clamp_len(bt, b, pl.P);
-  int32_t cnt = 0, ls = 0;
-  if (dynamic) {
-    cnt = min(max(sel_count[(int64_t)b * pl.hkv + h], 0), plan.k_max);
-    ls = sel_len[b];
-  }
+  const int32_t kind = !dynamic ? 0 : (it < n_items - 1 ? 1 : 2);
   const int lane = threadIdx.x & 63;
   const int g = lane & 15, quad = lane >> 4;
+
+  // one round of independent loads: length, selection count and length, the
+  // selected page ids of the item's blocks, the query
+  const int64_t bh = (int64_t)b * pl.hkv + h;
+  // (sel_mask is 0 when no head is dynamic: the selection pointers then
+  // alias the lengths and every index collapses to 0)
+  constexpr int NB = (BPI + 1) & ~1;
+  const int32_t L_raw = as_scalar(bt.lens)[b];
+  const int32_t cnt_raw = as_scalar(sel_count)[bh & plan.sel_mask];
+  const int32_t ls_raw = as_scalar(sel_len)[b & plan.sel_mask];
+  int32_t page[NB];
+  {
+    const auto sp = as_scalar(sel_pages);
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      page[u] = sp[(bh * plan.k_max + min((it * BPI + u) / SB, plan.k_max - 1)) & plan.sel_mask];
+  }
+  // all of the round in flight together, waited for once (the compiler would
+  // otherwise sink each load to its first use, behind the branches)
+  asm volatile("" ::"s"(L_raw), "s"(cnt_raw), "s"(ls_raw));
+#pragma unroll
+  for (int u = 0; u < NB; ++u) asm volatile("" ::"s"(page[u]));
   const int32_t* pt_row = bt.pt + (int64_t)b * bt.max_pp;
 
   // query operand: Q[g][32*quad + 8*i .. +8], zero for g >= G
@@ -341,41 +409,36 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
 #pragma unroll
   for (int ch = 0; ch < 8; ++ch) st.o[ch] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  const int32_t cap = bt.max_pp * pl.P;
+  const int32_t L = L_raw < 0 ? 0 : (L_raw > cap ? cap : L_raw);
   BlockSource src;
+  src.kind = kind;
   src.L = L;
-  src.sel = sel_pages + ((int64_t)b * pl.hkv + h) * plan.k_max;
-  src.cnt = cnt;
-  src.k_max = plan.k_max;
-  if (L > 0) {
-    int32_t v_begin = it * BPI, v_end;
-    if (!dynamic) {
-      src.kind = 0;
-      src.s0 = min(plan.sink, L);
-      src.w0 = max(plan.sink, L - plan.window);
-      src.nb_sink = (src.s0 + kBlockTokens - 1) / kBlockTokens;
-      src.first_w = src.w0 / kBlockTokens;
-      const int32_t nb_win = L > src.w0 ? (L - 1) / kBlockTokens - src.first_w + 1 : 0;
-      v_end = min(src.nb_sink + nb_win, v_begin + BPI);
-    } else if (it < n_items - 1) {
-      src.kind = 1;
-      v_end = min(cnt * (PG / kBlockTokens), v_begin + BPI);
-    } else {
-      src.kind = 2;
-      src.ls = min(max(ls, 0), L);
-      src.ls_floor = (src.ls / kBlockTokens) * kBlockTokens;
-      v_begin = 0;
-      v_end = (L - src.ls_floor + kBlockTokens - 1) / kBlockTokens;   // any length: chunks of BPI
-    }
-    for (int32_t v0 = v_begin; v0 < v_end; v0 += BPI)
-      run_blocks<PG, BPI, DEPTH>(pl, pt_row, bt.max_pp, h, src, v0, v_end, qb, st);
+  src.ls = min(max(ls_raw, 0), L);
+  int32_t v_begin = it * BPI, v_end = 0;
+  if (kind == 0) {
+    src.s0 = min(plan.sink, L);
+    src.w0 = max(plan.sink, L - plan.window);
+    src.nb_sink = (src.s0 + kBlockTokens - 1) / kBlockTokens;
+    src.first_w = src.w0 / kBlockTokens;
+    const int32_t nb_win = L > src.w0 ? (L - 1) / kBlockTokens - src.first_w + 1 : 0;
+    v_end = min(src.nb_sink + nb_win, v_begin + BPI);
+  } else if (kind == 1) {
+    const int32_t cnt = min(max(cnt_raw, 0), plan.k_max);
+    v_end = min(cnt * SB, v_begin + BPI);
+  } else {
+    src.ls_floor = (src.ls / kBlockTokens) * kBlockTokens;
+    v_begin = 0;
+    v_end = (L - src.ls_floor + kBlockTokens - 1) / kBlockTokens;   // any length: chunks of BPI
   }
+  for (int32_t v0 = v_begin; v0 < v_end; v0 += BPI)
+    run_blocks<PG, BPI, DEPTH>(pl, pt_row, bt.max_pp, h, src, page, v0, v_end, qb, st);
 
   // fold the four token quads of the running sum, store the partial
   st.l += __shfl_xor(st.l, 16, 64);
   st.l += __shfl_xor(st.l, 32, 64);
-  const int64_t slot0 = ((int64_t)b * pl.hkv + h) * plan.item_stride * G;
   if (g < G) {
-    const int64_t slot = slot0 + (int64_t)it * G + g;
+    const int64_t slot = (bh * plan.item_stride + it) * G + g;
     float* o = part_o + slot * kHeadDim + 4 * quad;
 #pragma unroll
     for (int ch = 0; ch < 8; ++ch) *reinterpret_cast<f32x4*>(o + 16 * ch) = st.o[ch];
@@ -384,68 +447,89 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
       part_ml[slot * 2 + 1] = st.l;
     }
   }
-
 }
 
-// Merge of the item partials of one (sequence, KV head): the running-max /
-// running-sum rule of online softmax applied across items. Thread (g, d) owns
-// channel d of query g; the items' (max, sum) pairs are staged in LDS first so
-// every output channel's loads are independent and in flight together.
-constexpr int kCombineThreads = 512;
-constexpr int kMaxItemsLds = kMaxPartialsPerHead;
+// Merge of the item partials of one (sequence, KV head, query head): the
+// running-max / running-sum rule of online softmax applied across items.
+// Thread (slice, c4) folds channels 4*c4 .. +3 over the items slice,
+// slice + kCombineSlices, ...; the loads of a chunk of items are all issued
+// before any is used. The slices are then folded through LDS.
+constexpr int kCombineSlices = 8;
+constexpr int kCombineThreads = kCombineSlices * (kHeadDim / 4);
+constexpr int kCombineChunk = 8;
+
+__device__ __forceinline__ void fold_partial(float m_i, float l_i, const f32x4& o_i, float& M, float& l,
+                                             f32x4& o) {
+  if (m_i == -INFINITY) return;                  // empty item
+  const float Mn = fmaxf(M, m_i);
+  const float a = __builtin_amdgcn_exp2f(M - Mn), c = __builtin_amdgcn_exp2f(m_i - Mn);
+  l = l * a + l_i * c;
+  o = o * a + o_i * c;
+  M = Mn;
+}
 
 __global__ void __launch_bounds__(kCombineThreads) combine_kernel(int32_t hkv, AttnPlan plan, int32_t G,
                                                                   const float* __restrict__ part_o,
                                                                   const float* __restrict__ part_ml,
                                                                   float* __restrict__ out,
                                                                   float* __restrict__ lse) {
-  __shared__ float sm[kMaxItemsLds], sl[kMaxItemsLds];
-  __shared__ float sM[16];
-  const int32_t b = blockIdx.x / hkv, h = blockIdx.x % hkv;
-  const int32_t n_items = plan.kind[h] ? plan.items_dyn : plan.items_stream;
-  const int64_t slot0 = ((int64_t)b * hkv + h) * plan.item_stride * G;   // slot(i, g) = slot0 + i*G + g
-  const int32_t n_ml = n_items * G;                                     // <= kMaxItemsLds (host check)
-  for (int32_t k = threadIdx.x; k < n_ml; k += kCombineThreads) {
-    sm[k] = part_ml[(slot0 + k) * 2];
-    sl[k] = part_ml[(slot0 + k) * 2 + 1];
-  }
-  __syncthreads();
-  if (threadIdx.x < G) {
-    float M = -INFINITY;
-    for (int32_t i = 0; i < n_items; ++i) M = fmaxf(M, sm[i * G + threadIdx.x]);
-    sM[threadIdx.x] = M;
-  }
-  __syncthreads();
-  const int32_t hq = hkv * G;
-  for (int32_t gd = threadIdx.x; gd < G * kHeadDim; gd += kCombineThreads) {
-    const int32_t g = gd / kHeadDim, d = gd % kHeadDim;
-    const float M = sM[g];
-    float num = 0.f, den = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll 8
-      for (int32_t i = 0; i < n_items; ++i) {
-        const float w = __builtin_amdgcn_exp2f(sm[i * G + g] - M);
-        den += w * sl[i * G + g];
-        num += w * part_o[(slot0 + (int64_t)i * G + g) * kHeadDim + d];
-      }
+  __shared__ f32x4 so[kCombineThreads];
+  __shared__ float sM[kCombineThreads], sl[kCombineThreads];
+  // all launch arguments in one scalar-memory round trip (see attn_kernel)
+  asm volatile("" ::"s"(hkv), "s"(G), "s"(plan.items_stream), "s"(plan.items_dyn), "s"(plan.item_stride),
+               "s"(plan.dyn_mask[0]), "s"(plan.dyn_mask[1]), "s"(plan.dyn_mask[2]), "s"(plan.dyn_mask[3]),
+               "s"(part_o), "s"(part_ml), "s"(out), "s"(lse));
+  const HeadMask mask(plan);
+  const int32_t bh = blockIdx.x / G, g = blockIdx.x - bh * G;
+  const int32_t h = bh % hkv;
+  const int32_t n_items = mask.dynamic(h) ? plan.items_dyn : plan.items_stream;
+  const int64_t slot0 = (int64_t)bh * plan.item_stride * G + g;     // slot(i) = slot0 + i * G
+  const int32_t tid = threadIdx.x;
+  const int32_t sl_id = tid / (kHeadDim / 4), c4 = tid % (kHeadDim / 4);
+  float M = -INFINITY, l = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int32_t i0 = sl_id; i0 < n_items; i0 += kCombineSlices * kCombineChunk) {
+    f32x4 ov[kCombineChunk];
+    float2 mlv[kCombineChunk];
+#pragma unroll
+    for (int k = 0; k < kCombineChunk; ++k) {
+      const int32_t i = min(i0 + k * kCombineSlices, n_items - 1);
+      const int64_t slot = slot0 + (int64_t)i * G;
+      ov[k] = *reinterpret_cast<const f32x4*>(part_o + slot * kHeadDim + 4 * c4);
+      mlv[k] = *reinterpret_cast<const float2*>(part_ml + slot * 2);
     }
-    const int64_t oi = (int64_t)b * hq + h * G + g;
-    out[oi * kHeadDim + d] = M == -INFINITY ? 0.f : num / den;
-    if (lse && d == 0) lse[oi] = M == -INFINITY ? -INFINITY : (M + log2f(den)) * kLn2;
+#pragma unroll
+    for (int k = 0; k < kCombineChunk; ++k)
+      if (i0 + k * kCombineSlices < n_items) fold_partial(mlv[k].x, mlv[k].y, ov[k], M, l, o);
   }
+  so[tid] = o;
+  sM[tid] = M;
+  sl[tid] = l;
+  __syncthreads();
+  if (sl_id != 0) return;
+#pragma unroll
+  for (int32_t s = 1; s < kCombineSlices; ++s) {
+    const int32_t j = s * (kHeadDim / 4) + c4;
+    fold_partial(sM[j], sl[j], so[j], M, l, o);
+  }
+  const int64_t oi = (int64_t)bh * G + g;          // = b * H_q + h * G + g
+  f32x4 res = {0.f, 0.f, 0.f, 0.f};
+  if (M != -INFINITY) res = o / l;
+  *reinterpret_cast<f32x4*>(out + oi * kHeadDim + 4 * c4) = res;
+  if (lse && c4 == 0) lse[oi] = M == -INFINITY ? -INFINITY : (M + log2f(l)) * kLn2;
 }
 
 template <int PG, int BPI, int DEPTH = 4>
 hipError_t launch_attn_t(const PoolArgs& pool, const BatchArgs& batch, const AttnPlan& plan, int32_t G,
                          const uint16_t* q, const int32_t* sel_pages, const int32_t* sel_count,
-                         const int32_t* sel_len, float* part_o, float* part_ml, int32_t* tickets,
+                         const int32_t* sel_len, float* part_o, float* part_ml,
                          float* out, float* lse, hipStream_t s) {
-  const int64_t grid = (int64_t)batch.B * (plan.n_stream * plan.items_stream + plan.n_dyn * plan.items_dyn);
+  const int64_t grid = (int64_t)batch.B * plan.items_per_seq;
   hipLaunchKernelGGL((attn_kernel<PG, BPI, DEPTH>), dim3((unsigned)grid), dim3(64), 0, s, pool, batch, plan, G, q,
                      sel_pages, sel_count, sel_len, part_o, part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(batch.B * pool.hkv), dim3(kCombineThreads), 0, s, pool.hkv, plan, G,
+  hipLaunchKernelGGL(combine_kernel, dim3(batch.B * pool.hkv * G), dim3(kCombineThreads), 0, s, pool.hkv, plan, G,
                      part_o, part_ml, out, lse);
   return hipGetLastError();
 }
@@ -453,12 +537,14 @@ hipError_t launch_attn_t(const PoolArgs& pool, const BatchArgs& batch, const Att
 template <int PG>
 hipError_t launch_attn_p(const PoolArgs& pool, const BatchArgs& batch, const AttnPlan& plan, int32_t G,
                          const uint16_t* q, const int32_t* sel_pages, const int32_t* sel_count,
-                         const int32_t* sel_len, float* part_o, float* part_ml, int32_t* tickets,
+                         const int32_t* sel_len, float* part_o, float* part_ml,
                          float* out, float* lse, hipStream_t s) {
   switch (plan.blocks_per_item) {
-    case 4: return launch_attn_t<PG, 4>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, part_o, part_ml, tickets, out, lse, s);
-    case 8: return launch_attn_t<PG, 8>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, part_o, part_ml, tickets, out, lse, s);
-    case 16: return launch_attn_t<PG, 16>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, part_o, part_ml, tickets, out, lse, s);
+#define SPA_BPI_CASE(n) \
+    case n: return launch_attn_t<PG, n>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, part_o, part_ml, out, lse, s);
+    SPA_BPI_CASE(4) SPA_BPI_CASE(5) SPA_BPI_CASE(6) SPA_BPI_CASE(7) SPA_BPI_CASE(8) SPA_BPI_CASE(9)
+    SPA_BPI_CASE(10) SPA_BPI_CASE(12) SPA_BPI_CASE(16)
+#undef SPA_BPI_CASE
     default: return hipErrorInvalidValue;
   }
 }
@@ -468,12 +554,12 @@ hipError_t launch_attn_p(const PoolArgs& pool, const BatchArgs& batch, const Att
 hipError_t launch_attn(const PoolArgs& pool, const BatchArgs& batch, const AttnPlan& plan, int32_t G,
                        const uint16_t* q, const int32_t* sel_pages, const int32_t* sel_count,
                        const int32_t* sel_len, float* out, float* lse, float* part_o,
-                       float* part_ml, int32_t* tickets, hipStream_t s) {
+                       float* part_ml, hipStream_t s) {
   if (batch.B == 0) return hipSuccess;
   switch (pool.p) {
-    case 16: return launch_attn_p<16>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, part_o, part_ml, tickets, out, lse, s);
-    case 32: return launch_attn_p<32>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, part_o, part_ml, tickets, out, lse, s);
-    case 64: return launch_attn_p<64>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, part_o, part_ml, tickets, out, lse, s);
+    case 16: return launch_attn_p<16>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, part_o, part_ml, out, lse, s);
+    case 32: return launch_attn_p<32>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, part_o, part_ml, out, lse, s);
+    case 64: return launch_attn_p<64>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, part_o, part_ml, out, lse, s);
     default: return hipErrorInvalidValue;
   }
 }

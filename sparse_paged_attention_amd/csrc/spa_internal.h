@@ -10,7 +10,6 @@ namespace spa {
 constexpr int kHeadDim = 128;       // D
 constexpr int kBlockTokens = 16;    // tokens per attention block (MFMA M/K tile)
 constexpr int kMaxKvHeads = 128;
-constexpr int kMaxPartialsPerHead = 2048;   // items x query heads merged per KV head
 
 // Pool geometry and base pointers, passed by value to every kernel.
 struct PoolArgs {
@@ -39,18 +38,19 @@ struct HeadList {
 
 // Work plan of the attention launch: every streaming head is cut into
 // items_stream items and every dynamic head into items_dyn items (the last of
-// which covers the tokens appended since the selection).
+// which covers the tokens appended since the selection). Work-groups are
+// numbered [sequence][KV head][item], each head holding as many items as its
+// kind needs; partials are stored item_stride slots per head.
 struct AttnPlan {
-  int32_t n_stream, n_dyn;      // streaming / dynamic KV heads
   int32_t items_stream;         // items per streaming head
   int32_t items_dyn;            // items per dynamic head
-  int32_t blocks_per_item;      // 16-token blocks per item
   int32_t item_stride;          // max(items_stream, items_dyn): partial slots per head
+  int32_t items_per_seq;        // sum over the KV heads of their item counts
+  int32_t blocks_per_item;      // 16-token blocks per item
   int32_t sink, window;
   int32_t k_max;
-  uint8_t kind[kMaxKvHeads];
-  uint8_t stream_ids[kMaxKvHeads];
-  uint8_t dyn_ids[kMaxKvHeads];
+  uint32_t dyn_mask[kMaxKvHeads / 32];   // bit h set: KV head h is dynamic
+  int64_t sel_mask;                      // ~0 with dynamic heads, 0 without (selection unused)
 };
 
 // ---- launchers (return hipError_t of the launch) -------------------------
@@ -69,7 +69,7 @@ hipError_t launch_select(const PoolArgs& pool, const BatchArgs& batch, const Hea
 hipError_t launch_attn(const PoolArgs& pool, const BatchArgs& batch, const AttnPlan& plan,
                        int32_t G, const uint16_t* q, const int32_t* sel_pages,
                        const int32_t* sel_count, const int32_t* sel_len, float* out,
-                       float* lse, float* part_o, float* part_ml, int32_t* tickets,
+                       float* lse, float* part_o, float* part_ml,
                        hipStream_t s);
 
 }  // namespace spa

@@ -7,7 +7,8 @@
         per-kernel average of every collected counter, summed over the
         counter's hardware instances for each dispatch;
     python -m sparse_paged_attention_amd.profiling traffic <fetch.db> <write.db> <kernels> <copy_bytes>
-        HBM bytes per launch of the comma-separated <kernels> (one call of the
+        HBM bytes per launch of the comma-separated <kernels> (name parts, each
+        matching one kernel; together one call of the
         entry point that launches them, summed) from a FETCH_SIZE run and a
         WRITE_SIZE run, each scaled by what the same counter reads for the
         plain copy kernel of <copy_bytes> bytes (the largest copy dispatch) in
@@ -85,7 +86,11 @@ def traffic(fetch_db: str, write_db: str, kernels: str, copy_bytes: float) -> di
     f_scale = copy_bytes / f_copy
     w_scale = copy_bytes / w_copy
     per = {}
-    for kernel in kernels.split(","):
+    for part in kernels.split(","):
+        match = [k for k in f if part in k]
+        if len(match) != 1:
+            raise SystemExit(f"'{part}' names {len(match)} kernels in the FETCH_SIZE run: {match}")
+        kernel = match[0]
         fk = [v * 1024.0 * f_scale for v in f[kernel]["FETCH_SIZE"]]
         wk = [v * 1024.0 * w_scale for v in w[kernel]["WRITE_SIZE"]]
         per[kernel] = dict(launches=len(fk), fetch_bytes=sum(fk) / len(fk), write_bytes=sum(wk) / len(wk))

@@ -40,8 +40,7 @@ class DecodeLayer:
         self.sel_len = torch.zeros(self.B, dtype=torch.int32, device=device)
         self.budget = torch.zeros(self.B, dtype=torch.int32, device=device)
         nbytes = workspace_bytes(self.pool, self.heads, self.B, self.max_pages, self.k_max)
-        # zero-filled once: the library's ticket counters live at its start
-        self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.out = torch.empty((self.B, hq, 128), dtype=torch.float32, device=device)
         self.lse = torch.empty((self.B, hq), dtype=torch.float32, device=device)
 

@@ -172,3 +172,14 @@ def test_select_and_summary_validation(spa):
     assert L.spa_kv_pool_write(ctypes.byref(pool), FAKE, 4, -1, 1, FAKE, FAKE, None) == 1
     assert L.spa_kv_pool_write(ctypes.byref(pool), None, 4, 0, 1, FAKE, FAKE, None) == 1
     assert L.spa_kv_pool_write(ctypes.byref(pool), FAKE, 4, 0, 0, FAKE, FAKE, None) == 0
+
+
+def test_attn_blocks_per_item_setting(spa):
+    """Accepted item sizes round-trip; anything else is rejected up front."""
+    lib = spa.lib()
+    for ok in (0, 4, 5, 6, 7, 8, 9, 10, 12, 16, 0):
+        assert lib.spa_set_attn_blocks_per_item(ok) == 0
+    for bad in (-1, 1, 2, 3, 11, 13, 17, 64):
+        assert lib.spa_set_attn_blocks_per_item(bad) == 1
+        assert b"blocks per item" in lib.spa_last_error()
+    assert lib.spa_set_attn_blocks_per_item(0) == 0

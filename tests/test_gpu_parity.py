@@ -118,6 +118,21 @@ def test_llama3_128k_full_size_sampled():
     run(wl, check=[(0, 0), (0, 4), (1, 5), (2, 3), (3, 7)])
 
 
+@pytest.mark.parametrize("bpi", [4, 5, 6, 7, 8, 9, 10, 12, 16])
+def test_every_item_size(bpi):
+    """Each attention work-item size (odd sizes pad the last block pair):
+    the 128K shape at small contexts with a 3-token tail, and p = 64 pages."""
+    import sparse_paged_attention_amd as spa
+    spa.set_attn_blocks_per_item(bpi)
+    try:
+        run(W.WORKLOADS["llama3_128k"].scaled(contexts=(4100, 3001, 1000, 17), steps=5, budget=512,
+                                              window=300))
+        run(W.Workload(f"p64_bpi{bpi}", 2400 + bpi, 2, 8, 2, 64, 256, (2000, 700), 3, 2, (0, 1), 8, 600,
+                       512, True))
+    finally:
+        spa.set_attn_blocks_per_item(0)
+
+
 def test_selection_exact_ties_go_to_lowest_page_id():
     """Integer-valued keys and queries: many pages share a score exactly, and
     the selection must still match the oracle id for id (lowest ids win)."""

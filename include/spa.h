@@ -158,6 +158,10 @@ spa_status spa_page_summary_update(const spa_pool* pool, const spa_heads* heads,
  *   sel_pages:     device int32 [B][H_kv][k_max]  (written)
  *   sel_count:     device int32 [B][H_kv]         (written)
  *   sel_len:       device int32 [B]               (written)
+ *   sel_phys:      device int32 [B][H_kv][k_max] or NULL; when given,
+ *                  receives page_table[b][id / (P / p)] for each selected id
+ *                  (the physical page holding it), which lets
+ *                  spa_sparse_decode_attn skip the page-table look-up
  *   scores:        device fp32 [B][H_kv][max_pages * P / p] or NULL; when
  *                  given, receives s_j for dynamic heads (entries j >= n_b
  *                  unspecified)
@@ -168,7 +172,7 @@ spa_status spa_select_pages(const spa_pool* pool, const spa_heads* heads,
                             const spa_batch* batch, const void* q,
                             const int32_t* budget_tokens, int32_t k_max,
                             int32_t* sel_pages, int32_t* sel_count, int32_t* sel_len,
-                            float* scores, void* ws, size_t ws_bytes,
+                            int32_t* sel_phys, float* scores, void* ws, size_t ws_bytes,
                             hipStream_t stream);
 
 /* ---- a6 + a7 + a8: unified sparse decode attention ----------------------
@@ -184,14 +188,18 @@ spa_status spa_select_pages(const spa_pool* pool, const spa_heads* heads,
  * online softmax (FlashAttention, long-context survey "2.1"; the max and sum
  * outputs of the Novita vLLM article, "2. 注意力机制修改").
  *   out: device fp32 [B][H_q][D]; lse: device fp32 [B][H_q] or NULL.
- *   sel_*: as written by spa_select_pages (page ids distinct; not read for
- *          streaming heads);
+ *   sel_pages / sel_count / sel_len: as written by spa_select_pages (page
+ *          ids distinct; not read for streaming heads);
+ *   sel_phys: as written by the same spa_select_pages call, or NULL to look
+ *          the selected pages up in the page table here. When given, the
+ *          page-table entries of the selected pages must not have changed
+ *          since the selection (pages are only ever added at the end);
  *   k_max: capacity of a sel_pages row.
  * A sequence with L_b < 1 gets out = 0 and lse = -inf. */
 spa_status spa_sparse_decode_attn(const spa_pool* pool, const spa_heads* heads,
                                   const spa_batch* batch, const void* q,
                                   const int32_t* sel_pages, const int32_t* sel_count,
-                                  const int32_t* sel_len, int32_t k_max,
+                                  const int32_t* sel_len, const int32_t* sel_phys, int32_t k_max,
                                   float* out, float* lse, void* ws, size_t ws_bytes,
                                   hipStream_t stream);
 

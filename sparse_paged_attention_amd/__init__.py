@@ -75,8 +75,8 @@ def lib() -> ctypes.CDLL:
             "spa_kv_pool_append": ([P, H, B, vp, vp, vp], ctypes.c_int),
             "spa_kv_pool_write": ([P, vp, i32, i64, i64, vp, vp, vp], ctypes.c_int),
             "spa_page_summary_update": ([P, H, B, vp, i32, vp], ctypes.c_int),
-            "spa_select_pages": ([P, H, B, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
-            "spa_sparse_decode_attn": ([P, H, B, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp], ctypes.c_int),
+            "spa_select_pages": ([P, H, B, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+            "spa_sparse_decode_attn": ([P, H, B, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp], ctypes.c_int),
             "spa_workspace_bytes": ([P, H, i32, i32, i32], sz),
             "spa_default_budget": ([i64], i32),
             "spa_set_attn_blocks_per_item": ([i32], ctypes.c_int),
@@ -257,9 +257,11 @@ def workspace_bytes(pool: Pool, heads: Heads, batch: int, max_pages: int, k_max:
 
 
 def select_pages(pool: Pool, heads: Heads, batch: Batch, q, budget_tokens, k_max: int,
-                 sel_pages, sel_count, sel_len, scores=None, workspace=None, stream=None) -> None:
+                 sel_pages, sel_count, sel_len, scores=None, workspace=None, stream=None,
+                 sel_phys=None) -> None:
     """spa_select_pages: q bf16 [B][H_q][D]; budget_tokens int32 [B];
-    writes sel_pages int32 [B][H_kv][k_max], sel_count int32 [B][H_kv], sel_len int32 [B]."""
+    writes sel_pages int32 [B][H_kv][k_max], sel_count int32 [B][H_kv], sel_len int32 [B],
+    and, when given, sel_phys int32 [B][H_kv][k_max] (physical page of each selected page)."""
     p, h, b = pool.c(), _heads_for(heads, pool), batch.c()
     B, H = b.batch, pool.num_kv_heads
     _need(q, (B, heads.num_q_heads, HEAD_DIM), "bf16", "q")
@@ -267,19 +269,21 @@ def select_pages(pool: Pool, heads: Heads, batch: Batch, q, budget_tokens, k_max
     _need(sel_pages, (B, H, k_max), "i32", "sel_pages")
     _need(sel_count, (B, H), "i32", "sel_count")
     _need(sel_len, (B,), "i32", "sel_len")
+    _need(sel_phys, (B, H, k_max), "i32", "sel_phys", optional=True)
     n_max = b.max_pages * (pool.physical_page // pool.logical_page)
     _need(scores, (B, H, n_max), "f32", "scores", optional=True)
     _need(workspace, (None,), "u8", "workspace", optional=True)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().spa_select_pages(ctypes.byref(p), ctypes.byref(h), ctypes.byref(b), _ptr(q),
                                   _ptr(budget_tokens), k_max, _ptr(sel_pages), _ptr(sel_count),
-                                  _ptr(sel_len), _ptr(scores), _ptr(workspace), ws_bytes,
+                                  _ptr(sel_len), _ptr(sel_phys), _ptr(scores), _ptr(workspace), ws_bytes,
                                   _stream(stream)))
 
 
 def sparse_decode_attn(pool: Pool, heads: Heads, batch: Batch, q, sel_pages, sel_count, sel_len,
-                       k_max: int, out, lse=None, workspace=None, stream=None) -> None:
-    """spa_sparse_decode_attn: out fp32 [B][H_q][D], lse fp32 [B][H_q] or None."""
+                       k_max: int, out, lse=None, workspace=None, stream=None, sel_phys=None) -> None:
+    """spa_sparse_decode_attn: out fp32 [B][H_q][D], lse fp32 [B][H_q] or None; sel_phys as
+    written by the selection that produced sel_pages, or None to use the page table."""
     p, h, b = pool.c(), _heads_for(heads, pool), batch.c()
     B, H, HQ = b.batch, pool.num_kv_heads, heads.num_q_heads
     _need(q, (B, HQ, HEAD_DIM), "bf16", "q")
@@ -287,12 +291,13 @@ def sparse_decode_attn(pool: Pool, heads: Heads, batch: Batch, q, sel_pages, sel
     _need(sel_pages, (B, H, k_max), "i32", "sel_pages", optional=not dyn)
     _need(sel_count, (B, H), "i32", "sel_count", optional=not dyn)
     _need(sel_len, (B,), "i32", "sel_len", optional=not dyn)
+    _need(sel_phys, (B, H, k_max), "i32", "sel_phys", optional=True)
     _need(out, (B, HQ, HEAD_DIM), "f32", "out")
     _need(lse, (B, HQ), "f32", "lse", optional=True)
     _need(workspace, (None,), "u8", "workspace", optional=True)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().spa_sparse_decode_attn(ctypes.byref(p), ctypes.byref(h), ctypes.byref(b), _ptr(q),
-                                        _ptr(sel_pages), _ptr(sel_count), _ptr(sel_len), k_max,
+                                        _ptr(sel_pages), _ptr(sel_count), _ptr(sel_len), _ptr(sel_phys), k_max,
                                         _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                         _stream(stream)))
 

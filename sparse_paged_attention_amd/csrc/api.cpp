@@ -329,8 +329,8 @@ size_t spa_workspace_bytes(const spa_pool* pool, const spa_heads* heads, int32_t
 
 spa_status spa_select_pages(const spa_pool* pool, const spa_heads* heads, const spa_batch* batch,
                             const void* q, const int32_t* budget_tokens, int32_t k_max,
-                            int32_t* sel_pages, int32_t* sel_count, int32_t* sel_len, float* scores,
-                            void* ws, size_t ws_bytes, hipStream_t stream) {
+                            int32_t* sel_pages, int32_t* sel_count, int32_t* sel_len, int32_t* sel_phys,
+                            float* scores, void* ws, size_t ws_bytes, hipStream_t stream) {
   spa::PoolArgs pl;
   spa::BatchArgs bt;
   spa::HeadList dyn;
@@ -356,14 +356,14 @@ spa_status spa_select_pages(const spa_pool* pool, const spa_heads* heads, const 
     sc = static_cast<float*>(ws);
   }
   return hip_status(spa::launch_select(pl, bt, dyn, G, static_cast<const uint16_t*>(q), budget_tokens, k_max,
-                                       sel_pages, sel_count, sel_len, sc, n_max, stream),
+                                       sel_pages, sel_count, sel_len, sel_phys, sc, n_max, stream),
                     "select_pages launch");
 }
 
 spa_status spa_sparse_decode_attn(const spa_pool* pool, const spa_heads* heads, const spa_batch* batch,
                                   const void* q, const int32_t* sel_pages, const int32_t* sel_count,
-                                  const int32_t* sel_len, int32_t k_max, float* out, float* lse, void* ws,
-                                  size_t ws_bytes, hipStream_t stream) {
+                                  const int32_t* sel_len, const int32_t* sel_phys, int32_t k_max, float* out,
+                                  float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
   spa::PoolArgs pl;
   spa::BatchArgs bt;
   spa::HeadList dyn;
@@ -382,18 +382,20 @@ spa_status spa_sparse_decode_attn(const spa_pool* pool, const spa_heads* heads, 
   plan_attention(pl, heads, k_max, kind, bt.B, &plan);
   if ((int64_t)bt.B * plan.items_per_seq > INT32_MAX) return fail(SPA_ERR_INVALID, "grid too large");
   plan.sel_mask = dyn.n > 0 ? ~int64_t(0) : 0;
+  plan.use_phys = dyn.n > 0 && sel_phys != nullptr;
   if (dyn.n == 0) {                 // never used; read at index 0 to keep the loads branch-free
     sel_pages = bt.lens;
     sel_count = bt.lens;
     sel_len = bt.lens;
   }
+  if (!plan.use_phys) sel_phys = sel_pages;     // read alongside the ids, never used
   size_t ml_off;
   const size_t need = attn_bytes(pl, plan, bt.B, G, &ml_off);
   if (!ws || ws_bytes < need) return fail(SPA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
   float* part_o = static_cast<float*>(ws);
   float* part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + ml_off);
   return hip_status(spa::launch_attn(pl, bt, plan, G, static_cast<const uint16_t*>(q), sel_pages, sel_count,
-                                     sel_len, out, lse, part_o, part_ml, stream),
+                                     sel_len, sel_phys, out, lse, part_o, part_ml, stream),
                     "sparse_decode_attn launch");
 }
 

@@ -55,42 +55,45 @@ struct Block {
   int32_t t0, lo, hi, phys, lp;
 };
 
-// Operand registers of one block.
-struct Tile {
-  uint4 k[4];     // K rows: this lane's 64 bytes of token (lane & 15)
-  uint2 v[8];     // V^T: channel 16c + (lane & 15), tokens 4*(lane>>4) .. +3
+// Operand registers of a pair of blocks (a, b). V is kept the way the PV
+// MFMA consumes it: v[c] = {block a's 4 tokens, block b's 4 tokens} of
+// channel 16c + (lane & 15), so the loads land in place.
+struct PairTile {
+  uint4 ka[4], kb[4];   // K rows: this lane's 64 bytes of token (lane & 15) of a / b
+  uint4 v[8];
 };
 
-// Issues the loads of a block's tile. Empty blocks load from page 0 of the
-// pool (always mapped), so the loads never depend on control flow. The block
-// base is wave-uniform and each lane adds a fixed 32-bit offset, so every
-// load is a scalar-base + vector-offset access with no 64-bit address math.
+// Issues the loads of block `blk` into the a (half = 0) or b (half = 1) half
+// of a pair tile. Empty blocks load from page 0 of the pool (always mapped),
+// so the loads never depend on control flow; the padding slot of an odd
+// item loads nothing and is zero. The block base is wave-uniform and each
+// lane adds a fixed 32-bit offset (scalar base + vector offset addressing).
 template <int PG>
-__device__ __forceinline__ void issue_tile(const PoolArgs& pl, int32_t h, const Block& blk, Tile& t) {
+__device__ __forceinline__ void issue_half(const PoolArgs& pl, int32_t h, const Block& blk, PairTile& t,
+                                           int half, bool real) {
+  uint4* kd = half ? t.kb : t.ka;
+  if (!real) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kd[i] = uint4{0, 0, 0, 0};
+#pragma unroll
+    for (int ch = 0; ch < 8; ++ch) {
+      if (half) { t.v[ch].z = 0; t.v[ch].w = 0; } else { t.v[ch].x = 0; t.v[ch].y = 0; }
+    }
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int row = lane & 15, quad = lane >> 4;
   const int64_t head = (int64_t)blk.phys * pl.hkv + h;
   const int32_t in_page = blk.t0 & (PG - 1);
-  const uint16_t* kb = pl.k + (head * pl.P + blk.lp * PG + in_page) * kHeadDim;
-  const uint16_t* vb = pl.v + (head * pl.r + blk.lp) * (int64_t)(kHeadDim * PG) + in_page;
+  const uint16_t* kbase = pl.k + (head * pl.P + blk.lp * PG + in_page) * kHeadDim;
+  const uint16_t* vbase = pl.v + (head * pl.r + blk.lp) * (int64_t)(kHeadDim * PG) + in_page;
   const uint32_t koff = row * kHeadDim + 32 * quad, voff = row * PG + 4 * quad;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) t.k[i] = *reinterpret_cast<const uint4*>(kb + koff + 8 * i);
+  for (int i = 0; i < 4; ++i) kd[i] = *reinterpret_cast<const uint4*>(kbase + koff + 8 * i);
 #pragma unroll
-  for (int ch = 0; ch < 8; ++ch) t.v[ch] = *reinterpret_cast<const uint2*>(vb + voff + 16 * ch * PG);
-}
-
-// A pipeline slot: a real block's loads, or zeros for the padding slot
-// (`real` is a constant once the pipeline loop is unrolled).
-template <int PG>
-__device__ __forceinline__ void fill_tile(const PoolArgs& pl, int32_t h, const Block& blk, Tile& t, bool real) {
-  if (real) {
-    issue_tile<PG>(pl, h, blk, t);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) t.k[i] = uint4{0, 0, 0, 0};
-#pragma unroll
-    for (int ch = 0; ch < 8; ++ch) t.v[ch] = uint2{0, 0};
+  for (int ch = 0; ch < 8; ++ch) {
+    const uint2 w = *reinterpret_cast<const uint2*>(vbase + voff + 16 * ch * PG);
+    if (half) { t.v[ch].z = w.x; t.v[ch].w = w.y; } else { t.v[ch].x = w.x; t.v[ch].y = w.y; }
   }
 }
 
@@ -109,12 +112,12 @@ __device__ __forceinline__ float max_over_rows(float x) {
 }
 
 // Scores S^T[16 tok][16 q] of one block: 4 chained 16x16x32 MFMAs over D.
-__device__ __forceinline__ f32x4 qk_block(const Tile& t, const bf16x8 (&qb)[4]) {
+__device__ __forceinline__ f32x4 qk_block(const uint4 (&k)[4], const bf16x8 (&qb)[4]) {
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     bf16x8 a;
-    __builtin_memcpy(&a, &t.k[i], 16);
+    __builtin_memcpy(&a, &k[i], 16);
     s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[i], s, 0, 0, 0);
   }
   return s;
@@ -127,32 +130,46 @@ __device__ __forceinline__ f32x4 qk_block(const Tile& t, const bf16x8 (&qb)[4]) 
 // out = o / l and lse = ref + log2(l) are unchanged by the choice of reference.
 constexpr float kRescaleSlack = 8.f;
 
-// Two blocks (32 tokens) at once. The PV product contracts over 32 tokens
-// with one 16x16x32 MFMA per 16 channels: K-slot j of lane row q holds token
-// 4q + j of block a (j < 4) or token 4q + j - 4 of block b (j >= 4), which is
-// exactly where the QK products left this lane's probabilities.
-__device__ __forceinline__ void process_pair(const Block& ba, const Tile& ta, const Block& bb,
-                                             const Tile& tb, const bf16x8 (&qb)[4], State& st) {
-  const int lane = threadIdx.x & 63;
-  const int quad = lane >> 4;
-  const f32x4 sa = qk_block(ta, qb);
-  const f32x4 sb = qk_block(tb, qb);
-  const bool full = ba.lo <= ba.t0 && ba.hi >= ba.t0 + kBlockTokens &&
-                    bb.lo <= bb.t0 && bb.hi >= bb.t0 + kBlockTokens;
-  bool valid[8];
+// Probabilities of a pair of blocks, in the form the PV MFMA consumes.
+struct PairProbs {
+  bf16x8 hi, lo;       // P split into bf16 high and low parts
+  uint32_t mk[4];      // V masks (token validity) when the pair is not full
+  bool full, any;      // every token valid / at least one valid token
+};
+
+// Online-softmax step for two blocks (32 tokens) given their scores: updates
+// the running reference and sum, rescales the accumulators when the
+// reference rises, and returns this lane's 8 probabilities (K-slot j of lane
+// row q: token 4q + j of block a for j < 4, token 4q + j - 4 of block b).
+__device__ __forceinline__ PairProbs softmax_pair(const Block& ba, const Block& bb, const f32x4& sa,
+                                                  const f32x4& sb, State& st) {
+  PairProbs pp;
+  const int quad = (threadIdx.x & 63) >> 4;
+  pp.full = ba.lo <= ba.t0 && ba.hi >= ba.t0 + kBlockTokens && bb.lo <= bb.t0 && bb.hi >= bb.t0 + kBlockTokens;
   float s[8];
-  float bm = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int32_t tka = ba.t0 + 4 * quad + r, tkb = bb.t0 + 4 * quad + r;
-    valid[r] = full || (tka >= ba.lo && tka < ba.hi);
-    valid[4 + r] = full || (tkb >= bb.lo && tkb < bb.hi);
-    s[r] = valid[r] ? sa[r] : -INFINITY;
-    s[4 + r] = valid[4 + r] ? sb[r] : -INFINITY;
-    bm = fmaxf(bm, fmaxf(s[r], s[4 + r]));
+    s[r] = sa[r];
+    s[4 + r] = sb[r];
   }
+  if (!pp.full) {                                  // mask the invalid tokens (uniform branch)
+    bool valid[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int32_t tka = ba.t0 + 4 * quad + r, tkb = bb.t0 + 4 * quad + r;
+      valid[r] = tka >= ba.lo && tka < ba.hi;
+      valid[4 + r] = tkb >= bb.lo && tkb < bb.hi;
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) s[r] = valid[r] ? s[r] : -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      pp.mk[i] = (valid[2 * i] ? 0x0000FFFFu : 0u) | (valid[2 * i + 1] ? 0xFFFF0000u : 0u);
+  }
+  float bm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
   bm = max_over_rows(bm) * kScaleLog2;            // this query's maximum over the pair, log2 units
-  if (bm == -INFINITY) return;                    // no valid token (same for every lane)
+  pp.any = bm != -INFINITY;                       // same for every lane
+  if (!pp.any) return pp;
   const bool first = st.m == -INFINITY;
   const bool raise = bm > st.m + kRescaleSlack;   // always true on the first block
   const float m_new = raise ? bm : st.m;
@@ -171,40 +188,34 @@ __device__ __forceinline__ void process_pair(const Block& ba, const Tile& ta, co
     psum += pr[r];
   }
   st.l += psum;
-  // P split into bf16 high and low parts (native round-to-nearest-even conversions)
-  bf16x8 phi, plo;
 #pragma unroll
-  for (int r = 0; r < 8; r += 2) {
+  for (int r = 0; r < 8; r += 2) {                // native round-to-nearest-even conversions
     const f32x2 v = {pr[r], pr[r + 1]};
     const bf16x2 h = __builtin_convertvector(v, bf16x2);
     const f32x2 rest = v - __builtin_convertvector(h, f32x2);
     const bf16x2 lo = __builtin_convertvector(rest, bf16x2);
-    phi[r] = h[0]; phi[r + 1] = h[1];
-    plo[r] = lo[0]; plo[r + 1] = lo[1];
+    pp.hi[r] = h[0]; pp.hi[r + 1] = h[1];
+    pp.lo[r] = lo[0]; pp.lo[r + 1] = lo[1];
   }
-  uint4 w[8];
-#pragma unroll
-  for (int ch = 0; ch < 8; ++ch) w[ch] = uint4{ta.v[ch].x, ta.v[ch].y, tb.v[ch].x, tb.v[ch].y};
-  if (!full) {                                     // stale pool bytes must not reach the MFMA
-    asm volatile("" ::: "memory");                 // keep this a branch: full blocks skip it
-    uint32_t mk[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      mk[i] = (valid[2 * i] ? 0x0000FFFFu : 0u) | (valid[2 * i + 1] ? 0xFFFF0000u : 0u);
-#pragma unroll
-    for (int ch = 0; ch < 8; ++ch) {
-      w[ch].x &= mk[0];
-      w[ch].y &= mk[1];
-      w[ch].z &= mk[2];
-      w[ch].w &= mk[3];
-    }
-  }
+  return pp;
+}
+
+// O^T[128][16 q] += V^T[128][32 tok] . P^T: one 16x16x32 MFMA per 16
+// channels for each of the two parts of P.
+__device__ __forceinline__ void pv_pair(const PairTile& t, const PairProbs& pp, State& st) {
 #pragma unroll
   for (int ch = 0; ch < 8; ++ch) {
+    uint4 w = t.v[ch];
+    if (!pp.full) {                                // stale pool bytes must not reach the MFMA
+      w.x &= pp.mk[0];
+      w.y &= pp.mk[1];
+      w.z &= pp.mk[2];
+      w.w &= pp.mk[3];
+    }
     bf16x8 a;
-    __builtin_memcpy(&a, &w[ch], 16);
-    st.o[ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, st.o[ch], 0, 0, 0);
-    st.o[ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, st.o[ch], 0, 0, 0);
+    __builtin_memcpy(&a, &w, 16);
+    st.o[ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pp.hi, st.o[ch], 0, 0, 0);
+    st.o[ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pp.lo, st.o[ch], 0, 0, 0);
   }
 }
 
@@ -238,8 +249,9 @@ struct BlockSource {
 template <int PG, int BPI, int DEPTH>
 __device__ __forceinline__ void run_blocks(const PoolArgs& pl, const int32_t* pt_row,
                                            int32_t max_pp, int32_t h, const BlockSource& src,
-                                           const int32_t (&page)[(BPI + 1) & ~1], int32_t v0, int32_t v_end,
-                                           const bf16x8 (&qb)[4], State& st) {
+                                           const int32_t (&page)[(BPI + 1) & ~1],
+                                           const int32_t (&page_phys)[(BPI + 1) & ~1], bool use_phys,
+                                           int32_t v0, int32_t v_end, const bf16x8 (&qb)[4], State& st) {
   constexpr int SB = PG / kBlockTokens;           // blocks per logical page
   constexpr int NB = (BPI + 1) & ~1;              // pipeline slots: BPI rounded up to pairs
   const int32_t r = pl.P / PG;
@@ -248,8 +260,13 @@ __device__ __forceinline__ void run_blocks(const PoolArgs& pl, const int32_t* pt
   Block blk[NB];
   int32_t ptv[NB];
   if (src.kind == 1) {
+    if (use_phys) {                                // resolved when the pages were selected
 #pragma unroll
-    for (int u = 0; u < NB; ++u) ptv[u] = pt[min(max(page[u], 0) / r, max_pp - 1)];
+      for (int u = 0; u < NB; ++u) ptv[u] = page_phys[u];
+    } else {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) ptv[u] = pt[min(max(page[u], 0) / r, max_pp - 1)];
+    }
     const int32_t n_pages_s = (src.ls + PG - 1) / PG;
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
@@ -291,20 +308,31 @@ __device__ __forceinline__ void run_blocks(const PoolArgs& pl, const int32_t* pt
     blk[u].phys = phys;
     blk[u].lp = blk[u].hi > blk[u].lo ? j % r : 0;
   }
-  // blocks go in pairs; DEPTH (even) tiles are in flight; the padding slot
-  // of an odd BPI is empty and loads nothing
+  // Blocks go in pairs through a ring of DEPTH / 2 pair tiles. The scores of
+  // the next pair are computed before the current pair's PV product, so its
+  // MFMAs queue behind the current ones while the VALU works on the softmax.
   static_assert(DEPTH % 2 == 0, "blocks are processed in pairs");
   constexpr int D = DEPTH < NB ? DEPTH : NB;
-  Tile t[D];
+  constexpr int NT = D / 2;
+  PairTile t[NT];
 #pragma unroll
-  for (int u = 0; u < D; ++u) fill_tile<PG>(pl, h, blk[u], t[u], u < BPI);
+  for (int u = 0; u < D; u += 2) {
+    issue_half<PG>(pl, h, blk[u], t[u / 2], 0, u < BPI);
+    issue_half<PG>(pl, h, blk[u + 1], t[u / 2], 1, u + 1 < BPI);
+  }
+  f32x4 sa = qk_block(t[0].ka, qb), sb = qk_block(t[0].kb, qb);
 #pragma unroll
   for (int u = 0; u < NB; u += 2) {
-    if (blk[u].lo < blk[u].hi || blk[u + 1].lo < blk[u + 1].hi)
-      process_pair(blk[u], t[u % D], blk[u + 1], t[(u + 1) % D], qb, st);
+    const PairProbs pp = softmax_pair(blk[u], blk[u + 1], sa, sb, st);
+    if (u + 2 < NB) {
+      const PairTile& tn = t[((u + 2) / 2) % NT];
+      sa = qk_block(tn.ka, qb);
+      sb = qk_block(tn.kb, qb);
+    }
+    if (pp.any) pv_pair(t[(u / 2) % NT], pp, st);
     if (u + D < NB) {
-      fill_tile<PG>(pl, h, blk[u + D], t[u % D], u + D < BPI);
-      fill_tile<PG>(pl, h, blk[u + 1 + D], t[(u + 1) % D], u + 1 + D < BPI);
+      issue_half<PG>(pl, h, blk[u + D], t[(u / 2) % NT], 0, u + D < BPI);
+      issue_half<PG>(pl, h, blk[u + 1 + D], t[(u / 2) % NT], 1, u + 1 + D < BPI);
     }
   }
 }
@@ -336,7 +364,7 @@ template <int PG, int BPI, int DEPTH>
 __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, AttnPlan plan, int32_t G,
                                                   const uint16_t* q, const int32_t* sel_pages,
                                                   const int32_t* sel_count, const int32_t* sel_len,
-                                                  float* part_o, float* part_ml) {
+                                                  const int32_t* sel_phys, float* part_o, float* part_ml) {
   constexpr int SB = PG / kBlockTokens;
   // Every launch argument the kernel uses, read into registers in one round:
   // left to itself the compiler fetches each argument just before its first
@@ -347,7 +375,7 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
                "s"(G), "s"(plan.dyn_mask[0]), "s"(plan.dyn_mask[1]), "s"(plan.dyn_mask[2]),
                "s"(plan.dyn_mask[3]), "s"(plan.sel_mask));
   asm volatile("" ::"s"(pl.k), "s"(pl.v), "s"(bt.pt), "s"(bt.lens), "s"(sel_pages), "s"(sel_count),
-               "s"(sel_len), "s"(q), "s"(part_o), "s"(part_ml));
+               "s"(sel_len), "s"(sel_phys), "s"(q), "s"(part_o), "s"(part_ml), "s"(plan.use_phys));
   // work-group -> (sequence, head, item): head h's first item within the
   // sequence is h * items_stream + (dynamic heads below h) * (items_dyn - items_stream)
   const HeadMask mask(plan);
@@ -375,18 +403,22 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
   const int32_t L_raw = as_scalar(bt.lens)[b];
   const int32_t cnt_raw = as_scalar(sel_count)[bh & plan.sel_mask];
   const int32_t ls_raw = as_scalar(sel_len)[b & plan.sel_mask];
-  int32_t page[NB];
+  int32_t page[NB], page_phys[NB];
   {
     const auto sp = as_scalar(sel_pages);
+    const auto sq = as_scalar(sel_phys);          // aliases sel_pages when not in use
 #pragma unroll
-    for (int u = 0; u < NB; ++u)
-      page[u] = sp[(bh * plan.k_max + min((it * BPI + u) / SB, plan.k_max - 1)) & plan.sel_mask];
+    for (int u = 0; u < NB; ++u) {
+      const int64_t i = (bh * plan.k_max + min((it * BPI + u) / SB, plan.k_max - 1)) & plan.sel_mask;
+      page[u] = sp[i];
+      page_phys[u] = sq[i];
+    }
   }
   // all of the round in flight together, waited for once (the compiler would
   // otherwise sink each load to its first use, behind the branches)
   asm volatile("" ::"s"(L_raw), "s"(cnt_raw), "s"(ls_raw));
 #pragma unroll
-  for (int u = 0; u < NB; ++u) asm volatile("" ::"s"(page[u]));
+  for (int u = 0; u < NB; ++u) asm volatile("" ::"s"(page[u]), "s"(page_phys[u]));
   const int32_t* pt_row = bt.pt + (int64_t)b * bt.max_pp;
 
   // query operand: Q[g][32*quad + 8*i .. +8], zero for g >= G
@@ -432,7 +464,8 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
     v_end = (L - src.ls_floor + kBlockTokens - 1) / kBlockTokens;   // any length: chunks of BPI
   }
   for (int32_t v0 = v_begin; v0 < v_end; v0 += BPI)
-    run_blocks<PG, BPI, DEPTH>(pl, pt_row, bt.max_pp, h, src, page, v0, v_end, qb, st);
+    run_blocks<PG, BPI, DEPTH>(pl, pt_row, bt.max_pp, h, src, page, page_phys, plan.use_phys != 0, v0, v_end,
+                               qb, st);
 
   // fold the four token quads of the running sum, store the partial
   st.l += __shfl_xor(st.l, 16, 64);
@@ -522,11 +555,11 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(int32_t hkv, A
 template <int PG, int BPI, int DEPTH = 4>
 hipError_t launch_attn_t(const PoolArgs& pool, const BatchArgs& batch, const AttnPlan& plan, int32_t G,
                          const uint16_t* q, const int32_t* sel_pages, const int32_t* sel_count,
-                         const int32_t* sel_len, float* part_o, float* part_ml,
+                         const int32_t* sel_len, const int32_t* sel_phys, float* part_o, float* part_ml,
                          float* out, float* lse, hipStream_t s) {
   const int64_t grid = (int64_t)batch.B * plan.items_per_seq;
   hipLaunchKernelGGL((attn_kernel<PG, BPI, DEPTH>), dim3((unsigned)grid), dim3(64), 0, s, pool, batch, plan, G, q,
-                     sel_pages, sel_count, sel_len, part_o, part_ml);
+                     sel_pages, sel_count, sel_len, sel_phys, part_o, part_ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(combine_kernel, dim3(batch.B * pool.hkv * G), dim3(kCombineThreads), 0, s, pool.hkv, plan, G,
@@ -537,11 +570,11 @@ hipError_t launch_attn_t(const PoolArgs& pool, const BatchArgs& batch, const Att
 template <int PG>
 hipError_t launch_attn_p(const PoolArgs& pool, const BatchArgs& batch, const AttnPlan& plan, int32_t G,
                          const uint16_t* q, const int32_t* sel_pages, const int32_t* sel_count,
-                         const int32_t* sel_len, float* part_o, float* part_ml,
+                         const int32_t* sel_len, const int32_t* sel_phys, float* part_o, float* part_ml,
                          float* out, float* lse, hipStream_t s) {
   switch (plan.blocks_per_item) {
 #define SPA_BPI_CASE(n) \
-    case n: return launch_attn_t<PG, n>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, part_o, part_ml, out, lse, s);
+    case n: return launch_attn_t<PG, n>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, sel_phys, part_o, part_ml, out, lse, s);
     SPA_BPI_CASE(4) SPA_BPI_CASE(5) SPA_BPI_CASE(6) SPA_BPI_CASE(7) SPA_BPI_CASE(8) SPA_BPI_CASE(9)
     SPA_BPI_CASE(10) SPA_BPI_CASE(12) SPA_BPI_CASE(16)
 #undef SPA_BPI_CASE
@@ -553,13 +586,13 @@ hipError_t launch_attn_p(const PoolArgs& pool, const BatchArgs& batch, const Att
 
 hipError_t launch_attn(const PoolArgs& pool, const BatchArgs& batch, const AttnPlan& plan, int32_t G,
                        const uint16_t* q, const int32_t* sel_pages, const int32_t* sel_count,
-                       const int32_t* sel_len, float* out, float* lse, float* part_o,
-                       float* part_ml, hipStream_t s) {
+                       const int32_t* sel_len, const int32_t* sel_phys, float* out, float* lse,
+                       float* part_o, float* part_ml, hipStream_t s) {
   if (batch.B == 0) return hipSuccess;
   switch (pool.p) {
-    case 16: return launch_attn_p<16>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, part_o, part_ml, out, lse, s);
-    case 32: return launch_attn_p<32>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, part_o, part_ml, out, lse, s);
-    case 64: return launch_attn_p<64>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, part_o, part_ml, out, lse, s);
+    case 16: return launch_attn_p<16>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, sel_phys, part_o, part_ml, out, lse, s);
+    case 32: return launch_attn_p<32>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, sel_phys, part_o, part_ml, out, lse, s);
+    case 64: return launch_attn_p<64>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, sel_phys, part_o, part_ml, out, lse, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -295,7 +295,8 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
                                                             int32_t n_max,
                                                             const int32_t* __restrict__ budget,
                                                             int32_t k_max, int32_t* sel_pages,
-                                                            int32_t* sel_count, int32_t* sel_len) {
+                                                            int32_t* sel_count, int32_t* sel_len,
+                                                            int32_t* sel_phys) {
   constexpr int BINS = kHistBins, PER = BINS / kTopkThreads;
   __shared__ int32_t hist[BINS];
   __shared__ int32_t sh_wave[kTopkWaves];
@@ -416,6 +417,14 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
 #pragma unroll
   for (int e = 0; e < E; ++e)
     if ((sel >> e) & 1) out[rank[e]] = e * kTopkThreads + tid;
+  if (sel_phys) {                                 // physical page of each kept page, through the page table
+    int32_t* ph = sel_phys + ((int64_t)b * hkv + h) * k_max;
+    const int32_t* pt_row = bt.pt + (int64_t)b * bt.max_pp;
+    const int32_t r = P / p;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if ((sel >> e) & 1) ph[rank[e]] = pt_row[(e * kTopkThreads + tid) / r];
+  }
   if (tid == 0) {
     sel_count[(int64_t)b * hkv + h] = total;
     sel_len[b] = L;
@@ -435,8 +444,8 @@ hipError_t launch_score_g(const PoolArgs& pool, const BatchArgs& batch, const He
 
 hipError_t launch_select(const PoolArgs& pool, const BatchArgs& batch, const HeadList& dyn,
                          int32_t G, const uint16_t* q, const int32_t* budget, int32_t k_max,
-                         int32_t* sel_pages, int32_t* sel_count, int32_t* sel_len, float* scores,
-                         int32_t n_max, hipStream_t s) {
+                         int32_t* sel_pages, int32_t* sel_count, int32_t* sel_len, int32_t* sel_phys,
+                         float* scores, int32_t n_max, hipStream_t s) {
   if (batch.B == 0 || dyn.n == 0) return hipSuccess;
   hipError_t e;
   switch (G) {
@@ -450,10 +459,12 @@ hipError_t launch_select(const PoolArgs& pool, const BatchArgs& batch, const Hea
   if (e != hipSuccess) return e;
   if (n_max <= 32 * kTopkThreads)
     hipLaunchKernelGGL(topk_kernel<32>, dim3(batch.B * dyn.n), dim3(kTopkThreads), 0, s, batch, pool.p,
-                       pool.P, pool.hkv, dyn, scores, n_max, budget, k_max, sel_pages, sel_count, sel_len);
+                       pool.P, pool.hkv, dyn, scores, n_max, budget, k_max, sel_pages, sel_count, sel_len,
+                       sel_phys);
   else
     hipLaunchKernelGGL(topk_kernel<64>, dim3(batch.B * dyn.n), dim3(kTopkThreads), 0, s, batch, pool.p,
-                       pool.P, pool.hkv, dyn, scores, n_max, budget, k_max, sel_pages, sel_count, sel_len);
+                       pool.P, pool.hkv, dyn, scores, n_max, budget, k_max, sel_pages, sel_count, sel_len,
+                       sel_phys);
   return hipGetLastError();
 }
 

@@ -51,6 +51,7 @@ struct AttnPlan {
   int32_t k_max;
   uint32_t dyn_mask[kMaxKvHeads / 32];   // bit h set: KV head h is dynamic
   int64_t sel_mask;                      // ~0 with dynamic heads, 0 without (selection unused)
+  int32_t use_phys;                      // selected pages' physical pages come with the selection
 };
 
 // ---- launchers (return hipError_t of the launch) -------------------------
@@ -65,10 +66,11 @@ hipError_t launch_summary(const PoolArgs& pool, const BatchArgs& batch, const He
 hipError_t launch_select(const PoolArgs& pool, const BatchArgs& batch, const HeadList& dyn,
                          int32_t G, const uint16_t* q, const int32_t* budget, int32_t k_max,
                          int32_t* sel_pages, int32_t* sel_count, int32_t* sel_len,
-                         float* scores, int32_t n_max, hipStream_t s);
+                         int32_t* sel_phys, float* scores, int32_t n_max, hipStream_t s);
 hipError_t launch_attn(const PoolArgs& pool, const BatchArgs& batch, const AttnPlan& plan,
                        int32_t G, const uint16_t* q, const int32_t* sel_pages,
-                       const int32_t* sel_count, const int32_t* sel_len, float* out,
+                       const int32_t* sel_count, const int32_t* sel_len,
+                       const int32_t* sel_phys, float* out,
                        float* lse, float* part_o, float* part_ml,
                        hipStream_t s);
 

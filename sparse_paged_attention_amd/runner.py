@@ -23,7 +23,8 @@ from . import (Batch, Heads, Pool, kv_pool_append, kv_pool_write, page_summary_u
 
 class DecodeLayer:
     def __init__(self, *, hq: int, hkv: int, p: int, P: int, kind, sink: int, window: int,
-                 page_table: np.ndarray, num_phys_pages: int, k_max: int, device="cuda"):
+                 page_table: np.ndarray, num_phys_pages: int, k_max: int, device="cuda",
+                 resolve_at_selection: bool = True):
         self.hq, self.hkv, self.p, self.P = hq, hkv, p, P
         self.k_max = int(k_max)
         self.device = device
@@ -38,6 +39,10 @@ class DecodeLayer:
         self.sel_pages = torch.zeros((self.B, hkv, self.k_max), dtype=torch.int32, device=device)
         self.sel_count = torch.zeros((self.B, hkv), dtype=torch.int32, device=device)
         self.sel_len = torch.zeros(self.B, dtype=torch.int32, device=device)
+        # physical pages of the selection, resolved once by the selection call
+        # (None: attention looks the selected pages up in the page table)
+        self.sel_phys = torch.zeros((self.B, hkv, self.k_max), dtype=torch.int32, device=device) \
+            if resolve_at_selection else None
         self.budget = torch.zeros(self.B, dtype=torch.int32, device=device)
         nbytes = workspace_bytes(self.pool, self.heads, self.B, self.max_pages, self.k_max)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
@@ -74,11 +79,13 @@ class DecodeLayer:
 
     def select(self, q: torch.Tensor, scores=None) -> None:
         select_pages(self.pool, self.heads, self.batch, q, self.budget, self.k_max, self.sel_pages,
-                     self.sel_count, self.sel_len, scores=scores, workspace=self.workspace)
+                     self.sel_count, self.sel_len, scores=scores, workspace=self.workspace,
+                     sel_phys=self.sel_phys)
 
     def attend(self, q: torch.Tensor) -> None:
         sparse_decode_attn(self.pool, self.heads, self.batch, q, self.sel_pages, self.sel_count,
-                           self.sel_len, self.k_max, self.out, self.lse, workspace=self.workspace)
+                           self.sel_len, self.k_max, self.out, self.lse, workspace=self.workspace,
+                           sel_phys=self.sel_phys)
 
     def step(self, q, k_new, v_new, do_select: bool) -> None:
         """One decode step; seq_lens must already hold the lengths after the append."""

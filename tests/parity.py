@@ -40,7 +40,8 @@ def bits_to_bf16(a: np.ndarray, device="cuda") -> torch.Tensor:
 class ParityRun:
     """A workload on the GPU plus the oracle state needed to check it."""
 
-    def __init__(self, wl: W.Workload, check_heads=None, threads: int = 16, strict_ties: bool = False):
+    def __init__(self, wl: W.Workload, check_heads=None, threads: int = 16, strict_ties: bool = False,
+                 resolve_at_selection: bool = True):
         self.wl = wl
         self.strict_ties = strict_ties
         self.check = check_heads if check_heads is not None else \
@@ -48,7 +49,7 @@ class ParityRun:
         pt = W.page_table(wl)
         self.layer = DecodeLayer(hq=wl.hq, hkv=wl.hkv, p=wl.p, P=wl.P, kind=wl.kind, sink=wl.sink,
                                  window=wl.window, page_table=pt, num_phys_pages=wl.num_phys_pages,
-                                 k_max=wl.k_max)
+                                 k_max=wl.k_max, resolve_at_selection=resolve_at_selection)
         self.K, self.V = {}, {}          # host bits of the checked (b, h) slices
         self.new_k, self.new_v = [], []  # per sequence: [H_kv][steps][D] appended tokens
         need = {(b, h) for b, h in self.check}

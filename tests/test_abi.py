@@ -97,7 +97,7 @@ def mkbatch(spa, B=1, mp=4, pt=FAKE, lens=FAKE):
 
 def attn(spa, pool, heads, batch, q=FAKE, sel=FAKE, k_max=8, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
     return spa.lib().spa_sparse_decode_attn(ctypes.byref(pool), ctypes.byref(heads), ctypes.byref(batch),
-                                            q, sel, sel, sel, k_max, out, None, ws, ws_bytes, None)
+                                            q, sel, sel, sel, None, k_max, out, None, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("bad,status", [
@@ -152,14 +152,14 @@ def test_select_and_summary_validation(spa):
     pool, heads, batch = mkpool(spa), mkheads(spa), mkbatch(spa)
     args = lambda **o: [ctypes.byref(o.get("pool", pool)), ctypes.byref(heads), ctypes.byref(batch),
                         o.get("q", FAKE), o.get("budget", FAKE), o.get("k_max", 8), FAKE, FAKE, FAKE,
-                        None, o.get("ws", FAKE), o.get("ws_bytes", 1 << 30), None]
+                        None, None, o.get("ws", FAKE), o.get("ws_bytes", 1 << 30), None]
     assert L.spa_select_pages(*args(k_max=0)) == 1
     assert L.spa_select_pages(*args(q=None)) == 1
     assert L.spa_select_pages(*args(budget=None)) == 1
     assert L.spa_select_pages(*args(ws_bytes=8)) == 4
     big = mkbatch(spa, mp=20000)
     assert L.spa_select_pages(ctypes.byref(pool), ctypes.byref(heads), ctypes.byref(big), FAKE, FAKE, 8,
-                              FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None) == 2
+                              FAKE, FAKE, FAKE, None, None, FAKE, 1 << 40, None) == 2
     assert L.spa_page_summary_update(ctypes.byref(pool), ctypes.byref(heads), ctypes.byref(batch),
                                      None, 5, None) == 1
     assert L.spa_page_summary_update(ctypes.byref(pool), ctypes.byref(heads), ctypes.byref(batch),

@@ -133,6 +133,14 @@ def test_every_item_size(bpi):
         spa.set_attn_blocks_per_item(0)
 
 
+def test_attention_resolving_pages_through_the_page_table():
+    """spa_sparse_decode_attn without the selection's physical pages (looks the
+    selected pages up in the page table itself): same results."""
+    wl = W.WORKLOADS["llama3_128k"].scaled(contexts=(4100, 3001, 1000, 17), steps=6, budget=512, window=300)
+    log(f"[parity] {wl.name} through the page table")
+    assert_reports(ParityRun(wl, resolve_at_selection=False).run())
+
+
 def test_selection_exact_ties_go_to_lowest_page_id():
     """Integer-valued keys and queries: many pages share a score exactly, and
     the selection must still match the oracle id for id (lowest ids win)."""

@@ -100,6 +100,9 @@ spa_status check_pool(const spa_pool* pool, spa::PoolArgs* out) {
   if (P / p > 64) return fail(SPA_ERR_INVALID, "physical_page / logical_page = %d exceeds 64", P / p);
   if (pool->num_phys_pages < 1) return fail(SPA_ERR_INVALID, "num_phys_pages %d < 1", pool->num_phys_pages);
   if (!pool->k_pool || !pool->v_pool) return fail(SPA_ERR_INVALID, "k_pool / v_pool is NULL");
+  if ((int64_t)pool->num_phys_pages * pool->num_kv_heads * (P / p) >= (int64_t)UINT32_MAX)
+    return fail(SPA_ERR_UNSUPPORTED, "pool of %d pages x %d heads x %d logical pages has 2^32 or more summary "
+                "records", pool->num_phys_pages, pool->num_kv_heads, P / p);
   out->hkv = pool->num_kv_heads;
   out->p = p;
   out->P = P;

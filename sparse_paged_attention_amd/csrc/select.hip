@@ -40,9 +40,10 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // values stay in registers (fp64) and its summary loads are contiguous. The
 // V = NP * G partial sums of a group are reduce-scattered over the group's
 // lanes (R = LPP / V lanes end up sharing each total), rounded to fp32 and
-// max-reduced over the query group. The range's page-table entries are read
-// once into LDS; summary loads run one pass ahead of the arithmetic and are
-// issued unconditionally (an invalid page reads page 0 and is masked).
+// max-reduced over the query group. The pool offset of each page of the
+// range's summary is computed once into LDS; summary loads run one pass ahead
+// of the arithmetic and are issued unconditionally (an invalid page reads
+// page 0 and is masked).
 template <int G>
 struct ScoreShape {
   static constexpr int LPP = G <= 4 ? 16 : 4 * G;   // lanes per page
@@ -88,7 +89,8 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
                                                    const uint16_t* __restrict__ q,
                                                    float* __restrict__ scores, int32_t n_max) {
   using S = ScoreShape<G>;
-  __shared__ int32_t pts[2 * 64];
+  static_assert(S::RANGE <= 128, "two page offsets per lane");
+  __shared__ uint32_t offs[128];
   const int32_t b = blockIdx.y / dyn.n, h = dyn.id[blockIdx.y % dyn.n];
   const int32_t L = clamp_len(bt, b, pl.P);
   const int32_t n = (L + pl.p - 1) / pl.p;
@@ -100,13 +102,17 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
   const int group = lane / S::LPP;
   const int c0 = sub * S::CPL;
 
-  // page-table entries covering the range (at most 128: two per lane)
+  // summary record (512 B) of every page of the range through the page
+  // table, or ~0 for pages past the length or unmapped
   const int32_t* pt_row = bt.pt + (int64_t)b * bt.max_pp;
-  const int32_t e0 = base / pl.r;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    const int32_t e = min(e0 + lane + 64 * k, bt.max_pp - 1);
-    pts[lane + 64 * k] = pt_row[e];
+    const int32_t i = lane + 64 * k, j = base + i;
+    if (i < S::RANGE) {
+      const int32_t phys = pt_row[min(j / pl.r, bt.max_pp - 1)];
+      const bool ok = j < n && phys >= 0 && phys < pl.N;
+      offs[i] = ok ? (uint32_t)(((int64_t)phys * pl.hkv + h) * pl.r + j % pl.r) : ~0u;
+    }
   }
 
   // q+ and q- of this lane's channels, fp64 (exact for bf16)
@@ -128,11 +134,9 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
 
   // summary location of page slot pp of pass it (page 0 of the pool if invalid)
   auto locate = [&](int it, int pp, bool& ok) -> const uint16_t* {
-    const int32_t j = base + it * S::PASS + pp * S::GPW + group;
-    int32_t phys = pts[min(j / pl.r - e0, 127)];
-    ok = j < n && phys >= 0 && phys < pl.N;
-    if (!ok) phys = 0;
-    return pl.summ + ((((int64_t)phys * pl.hkv + h) * pl.r + (ok ? j % pl.r : 0)) * 2) * kHeadDim + c0;
+    const uint32_t o = offs[it * S::PASS + pp * S::GPW + group];
+    ok = o != ~0u;
+    return pl.summ + (uint64_t)(ok ? o : 0u) * (2 * kHeadDim) + c0;
   };
 
   // one pass worth of loaded summaries

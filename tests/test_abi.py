@@ -105,7 +105,7 @@ def attn(spa, pool, heads, batch, q=FAKE, sel=FAKE, k_max=8, out=FAKE, ws=FAKE, 
     (dict(logical_page=128, physical_page=256), 1), (dict(physical_page=40), 1),
     (dict(logical_page=16, physical_page=16 * 65), 1), (dict(num_phys_pages=0), 1),
     (dict(k_pool=None), 1), (dict(num_kv_heads=0), 1), (dict(num_kv_heads=200), 1),
-    (dict(summary=None), 1),
+    (dict(summary=None), 1), (dict(num_phys_pages=2**31 - 1), 2),
 ])
 def test_pool_validation(spa, bad, status):
     pool = mkpool(spa, **bad)

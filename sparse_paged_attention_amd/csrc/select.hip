@@ -216,37 +216,39 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
 
 // ------------------------------------------------------------------ top-k
 //
-// One 512-thread block per (sequence, dynamic head). Element e of thread t is
-// page e * 512 + t (coalesced loads), held in a register as the 32-bit
+// One 1024-thread block per (sequence, dynamic head). Element e of thread t is
+// page e * 1024 + t (coalesced loads), held in a register as the 32-bit
 // order-preserving image of its fp32 score. Rounds of a 4096-bin histogram
 // over the remaining candidates' key range find the bin holding the k-th
 // largest key: keys above it are kept, keys below dropped, the bin's keys stay
-// candidates. At most 64 candidates left are ranked exactly by (key
-// descending, page id ascending); if more than 64 share one key, the ones with
-// the lowest page ids are kept (ties go to the lower page id). Kept ids are written in
-// ascending order; both id-order ranks come from one block-wide prefix sum
-// over per-(element, wave) counts.
+// candidates. Once at most kMaxCand candidates are left they are ranked
+// exactly by (key descending, page id ascending); if more share one key, the
+// ones with the lowest page ids are kept (ties go to the lower page id). Kept
+// ids are written in ascending order: a block-wide prefix sum over
+// per-(element, wave) counts gives each its position; the ids are also staged
+// in LDS so the physical-page look-ups go out as one coalesced round.
 
-constexpr int kTopkThreads = 512;
+constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
-constexpr int kHistBits = 12;
-constexpr int kHistBins = 1 << kHistBits;           // 8 per thread
+constexpr int kHistBins = 4096;                     // 4 per thread
+constexpr int kMaxCand = 128;
+constexpr int kOutStage = 4096;                     // kept ids staged in LDS
 
 __device__ __forceinline__ uint32_t order32(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Inclusive sum over the block of one value per thread; every thread gets its
-// own inclusive prefix and `total`.
-__device__ int32_t block_inclusive_scan(int32_t x, int32_t* sh_wave, int32_t& total) {
+// Exclusive prefix over the block (thread order) of one value per thread.
+__device__ int32_t block_exclusive_scan(int32_t x, int32_t* sh_wave, int32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t incl = x;
 #pragma unroll
   for (int d = 1; d < 64; d *= 2) {
-    const int32_t y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
+    const int32_t y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
   }
-  if (lane == 63) sh_wave[wave] = x;
+  if (lane == 63) sh_wave[wave] = incl;
   __syncthreads();
   int32_t before = 0, all = 0;
 #pragma unroll
@@ -257,14 +259,14 @@ __device__ int32_t block_inclusive_scan(int32_t x, int32_t* sh_wave, int32_t& to
   }
   __syncthreads();
   total = all;
-  return x + before;
+  return incl - x + before;
 }
 
-// For a per-thread element mask, the number of set elements with a smaller
-// page id than element e of this thread (ids: e * kTopkThreads + thread),
-// written to `rank` for every set element; returns the total.
+// For a per-thread element mask: the position of every set element among all
+// set elements in page-id order (ids e * kTopkThreads + thread); returns the
+// number of set elements.
 template <int E>
-__device__ int32_t id_order_ranks(uint64_t mask, int32_t (&rank)[E], int32_t* table, int32_t* sh_wave) {
+__device__ int32_t id_order_ranks(uint32_t mask, int32_t (&rank)[E], int32_t* table, int32_t* sh_wave) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -272,15 +274,11 @@ __device__ int32_t id_order_ranks(uint64_t mask, int32_t (&rank)[E], int32_t* ta
     if (lane == 0) table[e * kTopkWaves + wave] = __popcll(ball);
   }
   __syncthreads();
-  int32_t total = 0;
-  for (int32_t base = 0; base < E * kTopkWaves; base += kTopkThreads) {
-    const int32_t idx = base + tid;
-    const int32_t x = idx < E * kTopkWaves ? table[idx] : 0;
-    int32_t t2;
-    const int32_t incl = block_inclusive_scan(x, sh_wave, t2);
-    if (idx < E * kTopkWaves) table[idx] = incl - x + total;
-    total += t2;
-  }
+  static_assert(E * kTopkWaves <= kTopkThreads, "one table entry per thread");
+  const int32_t x = tid < E * kTopkWaves ? table[tid] : 0;
+  int32_t total;
+  const int32_t excl = block_exclusive_scan(x, sh_wave, total);
+  if (tid < E * kTopkWaves) table[tid] = excl;
   __syncthreads();
   const uint64_t below = (1ull << lane) - 1;
 #pragma unroll
@@ -292,7 +290,7 @@ __device__ int32_t id_order_ranks(uint64_t mask, int32_t (&rank)[E], int32_t* ta
   return total;
 }
 
-template <int E>   // elements per thread: n <= E * kTopkThreads
+template <int E>   // elements per thread: n_max <= E * kTopkThreads
 __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_t p, int32_t P,
                                                             int32_t hkv, HeadList dyn,
                                                             const float* __restrict__ scores,
@@ -301,14 +299,17 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
                                                             int32_t k_max, int32_t* sel_pages,
                                                             int32_t* sel_count, int32_t* sel_len,
                                                             int32_t* sel_phys) {
+  static_assert(E <= 32, "32-bit element masks");
   constexpr int BINS = kHistBins, PER = BINS / kTopkThreads;
   __shared__ int32_t hist[BINS];
   __shared__ int32_t sh_wave[kTopkWaves];
   __shared__ uint32_t sh_min[kTopkWaves], sh_max[kTopkWaves];
+  __shared__ int32_t sh_cnt[kTopkWaves];
   __shared__ int32_t sh_pick[2];
-  __shared__ int32_t sh_ncand;
-  __shared__ uint64_t cand_key[64];
+  __shared__ int32_t sh_nc;
+  __shared__ uint64_t cand_key[kMaxCand];
   __shared__ int32_t table[E * kTopkWaves];
+  __shared__ int32_t staged[kOutStage];
 
   const int32_t b = blockIdx.x / dyn.n, h = dyn.id[blockIdx.x % dyn.n];
   const int32_t L = clamp_len(bt, b, P);
@@ -321,72 +322,73 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   uint32_t ord[E];
-  uint64_t cand = 0, sel = 0;                       // bit e: element e
+  uint32_t cand = 0, sel = 0;                       // bit e: element e
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int32_t j = e * kTopkThreads + tid;
     ord[e] = order32(s[min(j, n_max - 1)]);
-    if (j < n) cand |= 1ull << e;
+    if (j < n) cand |= 1u << e;
   }
   int32_t need = k;
   int32_t rank[E];
 
   for (int round = 0; round < 8 && need > 0; ++round) {
-    // candidate count and key range in one pass
+    // candidate count and key range; the histogram is cleared meanwhile
     uint32_t lo = 0xFFFFFFFFu, hi = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e)
       if (cand >> e & 1) { lo = min(lo, ord[e]); hi = max(hi, ord[e]); }
-    int32_t c = __popcll(cand);
+    int32_t c = __popc(cand);
+#pragma unroll
     for (int d = 32; d >= 1; d /= 2) {
       lo = min(lo, (uint32_t)__shfl_xor((int)lo, d, 64));
       hi = max(hi, (uint32_t)__shfl_xor((int)hi, d, 64));
       c += __shfl_xor(c, d, 64);
     }
-    if (lane == 0) { sh_min[wave] = lo; sh_max[wave] = hi; sh_wave[wave] = c; }
+    if (lane == 0) { sh_min[wave] = lo; sh_max[wave] = hi; sh_cnt[wave] = c; }
 #pragma unroll
     for (int i = 0; i < PER; ++i) hist[tid * PER + i] = 0;
-    if (tid == 0) sh_ncand = 0;
+    if (tid == 0) sh_nc = 0;
     __syncthreads();
     lo = 0xFFFFFFFFu;
     hi = 0;
     int32_t total = 0;
 #pragma unroll
-    for (int w = 0; w < kTopkWaves; ++w) { lo = min(lo, sh_min[w]); hi = max(hi, sh_max[w]); total += sh_wave[w]; }
+    for (int w = 0; w < kTopkWaves; ++w) { lo = min(lo, sh_min[w]); hi = max(hi, sh_max[w]); total += sh_cnt[w]; }
     if (total <= need) { sel |= cand; cand = 0; break; }
-    if (total <= 64) {
+    if (total <= kMaxCand) {
       // exact ranks by (key descending, page id ascending) among the few left
 #pragma unroll
       for (int e = 0; e < E; ++e)
         if (cand >> e & 1) {
-          const int32_t at = atomicAdd(&sh_ncand, 1);
+          const int32_t at = atomicAdd(&sh_nc, 1);
           cand_key[at] = ((uint64_t)ord[e] << 32) | (0xFFFFFFFFu - (uint32_t)(e * kTopkThreads + tid));
         }
       __syncthreads();
-      const int32_t nc = sh_ncand;
+      const int32_t nc = sh_nc;
 #pragma unroll
       for (int e = 0; e < E; ++e)
         if (cand >> e & 1) {
           const uint64_t key = ((uint64_t)ord[e] << 32) | (0xFFFFFFFFu - (uint32_t)(e * kTopkThreads + tid));
           int32_t r = 0;
           for (int32_t i = 0; i < nc; ++i) r += cand_key[i] > key;
-          if (r < need) sel |= 1ull << e;
+          if (r < need) sel |= 1u << e;
         }
       cand = 0;
       break;
     }
     if (lo == hi) {
-      // more than 64 candidates share one key: keep the `need` lowest page ids
+      // more than kMaxCand candidates share one key: keep the `need` lowest page ids
       id_order_ranks<E>(cand, rank, table, sh_wave);
 #pragma unroll
       for (int e = 0; e < E; ++e)
-        if ((cand >> e & 1) && rank[e] < need) sel |= 1ull << e;
+        if ((cand >> e & 1) && rank[e] < need) sel |= 1u << e;
       cand = 0;
       break;
     }
     const uint32_t span = hi - lo;
     const int bits = 32 - __clz((int)span);
-    const int shift = bits > kHistBits ? bits - kHistBits : 0;   // (span >> shift) < BINS
+    const int shift = bits > 12 ? bits - 12 : 0;    // (span >> shift) < BINS
 #pragma unroll
     for (int e = 0; e < E; ++e)
       if (cand >> e & 1) atomicAdd(&hist[(ord[e] - lo) >> shift], 1);
@@ -396,7 +398,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
 #pragma unroll
     for (int i = 0; i < PER; ++i) { cnt[i] = hist[BINS - 1 - (tid * PER + i)]; sum += cnt[i]; }
     int32_t tot2;
-    int32_t run = block_inclusive_scan(sum, sh_wave, tot2) - sum;   // keys in higher bins
+    int32_t run = block_exclusive_scan(sum, sh_wave, tot2);       // keys in higher bins
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       if (run < need && run + cnt[i] >= need) { sh_pick[0] = BINS - 1 - (tid * PER + i); sh_pick[1] = run; }
@@ -409,8 +411,8 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
     for (int e = 0; e < E; ++e)
       if (cand >> e & 1) {
         const uint32_t bin = (ord[e] - lo) >> shift;
-        if (bin > pick) { sel |= 1ull << e; cand &= ~(1ull << e); }
-        else if (bin < pick) cand &= ~(1ull << e);
+        if (bin > pick) { sel |= 1u << e; cand &= ~(1u << e); }
+        else if (bin < pick) cand &= ~(1u << e);
       }
     need -= above;
   }
@@ -420,18 +422,24 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
   int32_t* out = sel_pages + ((int64_t)b * hkv + h) * k_max;
 #pragma unroll
   for (int e = 0; e < E; ++e)
-    if ((sel >> e) & 1) out[rank[e]] = e * kTopkThreads + tid;
-  if (sel_phys) {                                 // physical page of each kept page, through the page table
-    int32_t* ph = sel_phys + ((int64_t)b * hkv + h) * k_max;
-    const int32_t* pt_row = bt.pt + (int64_t)b * bt.max_pp;
-    const int32_t r = P / p;
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      if ((sel >> e) & 1) ph[rank[e]] = pt_row[(e * kTopkThreads + tid) / r];
-  }
+    if ((sel >> e) & 1) {
+      const int32_t id = e * kTopkThreads + tid;
+      out[rank[e]] = id;
+      if (rank[e] < kOutStage) staged[rank[e]] = id;
+    }
   if (tid == 0) {
     sel_count[(int64_t)b * hkv + h] = total;
     sel_len[b] = L;
+  }
+  if (sel_phys) {                                 // physical page of each kept page, through the page table
+    __syncthreads();
+    int32_t* ph = sel_phys + ((int64_t)b * hkv + h) * k_max;
+    const int32_t* pt_row = bt.pt + (int64_t)b * bt.max_pp;
+    const int32_t r = P / p;
+    for (int32_t i = tid; i < min(total, kOutStage); i += kTopkThreads) ph[i] = pt_row[staged[i] / r];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (((sel >> e) & 1) && rank[e] >= kOutStage) ph[rank[e]] = pt_row[(e * kTopkThreads + tid) / r];
   }
 }
 
@@ -461,14 +469,13 @@ hipError_t launch_select(const PoolArgs& pool, const BatchArgs& batch, const Hea
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  if (n_max <= 32 * kTopkThreads)
-    hipLaunchKernelGGL(topk_kernel<32>, dim3(batch.B * dyn.n), dim3(kTopkThreads), 0, s, batch, pool.p,
-                       pool.P, pool.hkv, dyn, scores, n_max, budget, k_max, sel_pages, sel_count, sel_len,
-                       sel_phys);
-  else
-    hipLaunchKernelGGL(topk_kernel<64>, dim3(batch.B * dyn.n), dim3(kTopkThreads), 0, s, batch, pool.p,
-                       pool.P, pool.hkv, dyn, scores, n_max, budget, k_max, sel_pages, sel_count, sel_len,
-                       sel_phys);
+#define SPA_TOPK(E)                                                                                     \
+  hipLaunchKernelGGL(topk_kernel<E>, dim3(batch.B * dyn.n), dim3(kTopkThreads), 0, s, batch, pool.p, pool.P, \
+                     pool.hkv, dyn, scores, n_max, budget, k_max, sel_pages, sel_count, sel_len, sel_phys)
+  if (n_max <= 8 * kTopkThreads) SPA_TOPK(8);
+  else if (n_max <= 16 * kTopkThreads) SPA_TOPK(16);
+  else SPA_TOPK(32);
+#undef SPA_TOPK
   return hipGetLastError();
 }
 

@@ -239,6 +239,29 @@ __device__ __forceinline__ uint32_t order32(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Wave-wide reductions on the VALU: DPP within each 16-lane row (swap
+// neighbours, pairs, then mirror halves and rows), then the cross-row lane
+// swaps; every lane ends with the result.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));   // row_mirror
+  auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op(a[0], a[1]);
+  auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return op(c[0], c[1]);
+}
+
+// Sum over the 8-lane group holding this lane (lanes 8m .. 8m + 7).
+__device__ __forceinline__ int32_t group8_sum(int32_t v) {
+  v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
+  v += __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);
+  return v;
+}
+
 // Exclusive prefix over the block (thread order) of one value per thread.
 __device__ int32_t block_exclusive_scan(int32_t x, int32_t* sh_wave, int32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -308,6 +331,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
   __shared__ int32_t sh_pick[2];
   __shared__ int32_t sh_nc;
   __shared__ uint64_t cand_key[kMaxCand];
+  __shared__ uint32_t sel_bits[kTopkThreads];
   __shared__ int32_t table[E * kTopkWaves];
   __shared__ int32_t staged[kOutStage];
 
@@ -338,16 +362,13 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
 #pragma unroll
     for (int e = 0; e < E; ++e)
       if (cand >> e & 1) { lo = min(lo, ord[e]); hi = max(hi, ord[e]); }
-    int32_t c = __popc(cand);
-#pragma unroll
-    for (int d = 32; d >= 1; d /= 2) {
-      lo = min(lo, (uint32_t)__shfl_xor((int)lo, d, 64));
-      hi = max(hi, (uint32_t)__shfl_xor((int)hi, d, 64));
-      c += __shfl_xor(c, d, 64);
-    }
+    lo = wave_reduce(lo, [](uint32_t x, uint32_t y) { return min(x, y); });
+    hi = wave_reduce(hi, [](uint32_t x, uint32_t y) { return max(x, y); });
+    const int32_t c = (int32_t)wave_reduce((uint32_t)__popc(cand), [](uint32_t x, uint32_t y) { return x + y; });
     if (lane == 0) { sh_min[wave] = lo; sh_max[wave] = hi; sh_cnt[wave] = c; }
 #pragma unroll
     for (int i = 0; i < PER; ++i) hist[tid * PER + i] = 0;
+    sel_bits[tid] = 0;
     if (tid == 0) sh_nc = 0;
     __syncthreads();
     lo = 0xFFFFFFFFu;
@@ -365,15 +386,26 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
           cand_key[at] = ((uint64_t)ord[e] << 32) | (0xFFFFFFFFu - (uint32_t)(e * kTopkThreads + tid));
         }
       __syncthreads();
+      // thread (i, part): how many of candidates part*16 .. +15 outrank
+      // candidate i; the 8 parts are summed within the 8-lane group
       const int32_t nc = sh_nc;
+      const int32_t i = tid >> 3, part = tid & 7;
+      int32_t r = 0;
+      if (i < nc) {
+        const uint64_t key = cand_key[i];
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-        if (cand >> e & 1) {
-          const uint64_t key = ((uint64_t)ord[e] << 32) | (0xFFFFFFFFu - (uint32_t)(e * kTopkThreads + tid));
-          int32_t r = 0;
-          for (int32_t i = 0; i < nc; ++i) r += cand_key[i] > key;
-          if (r < need) sel |= 1u << e;
+        for (int x = 0; x < kMaxCand / 8; ++x) {
+          const int32_t jj = part * (kMaxCand / 8) + x;
+          r += jj < nc && cand_key[jj] > key;
         }
+      }
+      r = group8_sum(r);
+      if (part == 0 && i < nc && r < need) {
+        const uint32_t id = 0xFFFFFFFFu - (uint32_t)cand_key[i];
+        atomicOr(&sel_bits[id % kTopkThreads], 1u << (id / kTopkThreads));
+      }
+      __syncthreads();
+      sel |= sel_bits[tid];
       cand = 0;
       break;
     }

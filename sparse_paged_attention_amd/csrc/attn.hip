@@ -421,7 +421,12 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
   for (int u = 0; u < NB; ++u) asm volatile("" ::"s"(page[u]), "s"(page_phys[u]));
   const int32_t* pt_row = bt.pt + (int64_t)b * bt.max_pp;
 
-  // query operand: Q[g][32*quad + 8*i .. +8], zero for g >= G
+  // query operand: Q[g][32*quad + 8*i .. +8]. Columns g >= G carry a copy of
+  // query 0: every column of the scores, of the softmax (its reductions run
+  // over tokens, within a column) and of the PV product is independent of the
+  // others, and those columns are never stored, so they need no zeroing --
+  // zeroing them would make the wave wait for this load before issuing any
+  // tile load.
   bf16x8 qb[4];
   const int32_t hq = pl.hkv * G;
   {
@@ -429,8 +434,7 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
     const uint4* q4 = reinterpret_cast<const uint4*>(q + ((int64_t)b * hq + h * G + gq) * kHeadDim + 32 * quad);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint4 w = q4[i];
-      if (g >= G) w = uint4{0, 0, 0, 0};
+      const uint4 w = q4[i];
       __builtin_memcpy(&qb[i], &w, 16);
     }
   }

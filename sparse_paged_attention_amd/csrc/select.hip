@@ -54,6 +54,7 @@ struct ScoreShape {
   static constexpr int GPW = 64 / LPP;              // groups per wave
   static constexpr int PASS = GPW * NP;             // pages per pass
   static constexpr int PASSES = 8;
+  static constexpr int RING = 2;                    // passes in flight
   static constexpr int RANGE = PASS * PASSES;       // pages per wave (<= 128)
 };
 
@@ -201,16 +202,21 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
     if (sub % (S::R * G) == 0 && j < n) out_row[j] = ok ? sc : -INFINITY;
   };
 
-  // two passes in flight: the loads of pass it + 1 run under the arithmetic
-  // of pass it (explicit double buffer, no register indexing by pass)
-  static_assert(S::PASSES % 2 == 0, "passes go in pairs");
-  Pass pa, pb;
-  issue(0, pa);
-  for (int it = 0; it < S::PASSES; it += 2) {
-    issue(it + 1, pb);
-    compute(it, pa);
-    if (it + 2 < S::PASSES) issue(it + 2, pa);
-    compute(it + 1, pb);
+  // a ring of S::RING passes in flight: the loads of pass it + 1 run under
+  // the arithmetic of pass it (fully unrolled, so the ring is never indexed
+  // at run time; deeper rings measured slower)
+  // Passes past the head's last page are skipped (wave-uniform): the last
+  // range of a head is often nearly empty.
+  const int32_t live = min(S::PASSES, (n - base + S::PASS - 1) / S::PASS);
+  Pass ring[S::RING];
+#pragma unroll
+  for (int it = 0; it < S::RING; ++it)
+    if (it < live) issue(it, ring[it]);
+#pragma unroll
+  for (int it = 0; it < S::PASSES; ++it) {
+    if (it >= live) break;
+    compute(it, ring[it % S::RING]);
+    if (it + S::RING < live) issue(it + S::RING, ring[it % S::RING]);
   }
 }
 

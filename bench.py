@@ -9,7 +9,9 @@ decode steps. Inputs are synthetic (seeded N(0,1) bf16) and resident in HBM.
 
 A step is one pass of the whole hot path for one attention layer: append the
 new token, refresh its page summary, select pages (every 4th decode step),
-sparse decode attention for all heads. To keep the timing honest about HBM
+sparse decode attention for all heads. Steps without selection append inside
+the attention launch (spa_append_decode_attn); selecting steps append first,
+since the selection reads the new token's page summary. To keep the timing honest about HBM
 (a step touches 51-118 MB, less than the 256 MB last-level cache), the layer
 is replicated R times with separate pools and consecutive steps cycle through
 the replicas, as the layers of a model do; the timed steps are replayed from
@@ -177,10 +179,12 @@ def main() -> int:
         t, r = divmod(s, R)
         layer = layers[r]
         layer.use_lengths(lens[t])
-        layer.append(kn[t], vn[t])
-        if wl.selects_at(t):
+        if wl.selects_at(t):                    # the selection reads the new token's summary
+            layer.append(kn[t], vn[t])
             layer.select(qs[s])
-        layer.attend(qs[s])
+            layer.attend(qs[s])
+        else:                                   # append inside the attention launch
+            layer.append_attend(qs[s], kn[t], vn[t])
 
     # warm-up (eager, also compiles nothing: kernels are prebuilt)
     for s in range(args.warmup):

@@ -203,6 +203,24 @@ spa_status spa_sparse_decode_attn(const spa_pool* pool, const spa_heads* heads,
                                   float* out, float* lse, void* ws, size_t ws_bytes,
                                   hipStream_t stream);
 
+/* ---- a1 + a2 + a6 + a7 + a8 in one launch -------------------------------
+ * The same pool state and outputs as spa_kv_pool_append(pool, heads, batch,
+ * k_new, v_new) followed by spa_sparse_decode_attn with the other arguments:
+ * token L_b - 1 of every sequence (k_new, v_new: device bf16 [B][H_kv][D],
+ * read only) is written into its pool slot, the summary of the logical page
+ * receiving it is rebuilt for every dynamic head, and the attention takes that
+ * token from k_new / v_new instead of the pool (the step order of the LServe
+ * write-up "3.2 解码阶段加速": the new token is appended, then attended).
+ * For steps that do not select: the selection passed in must have been made
+ * before this token, i.e. sel_len[b] <= L_b - 1 (a larger sel_len is read as
+ * L_b - 1). Same workspace as spa_sparse_decode_attn. */
+spa_status spa_append_decode_attn(const spa_pool* pool, const spa_heads* heads,
+                                  const spa_batch* batch, const void* k_new, const void* v_new,
+                                  const void* q, const int32_t* sel_pages,
+                                  const int32_t* sel_count, const int32_t* sel_len,
+                                  const int32_t* sel_phys, int32_t k_max, float* out, float* lse,
+                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Workspace bytes needed by spa_select_pages and spa_sparse_decode_attn for
  * these shapes (one buffer serves both). Returns 0 for invalid arguments.
  * The workspace needs no initialisation and holds nothing between calls;

@@ -53,7 +53,7 @@ class c_batch(ctypes.Structure):
 
 
 EXPORTS = ("spa_kv_pool_append", "spa_kv_pool_write", "spa_page_summary_update",
-           "spa_select_pages", "spa_sparse_decode_attn", "spa_workspace_bytes",
+           "spa_select_pages", "spa_sparse_decode_attn", "spa_append_decode_attn", "spa_workspace_bytes",
            "spa_default_budget", "spa_alloc_create", "spa_alloc_pages", "spa_alloc_free",
            "spa_alloc_num_free", "spa_alloc_destroy", "spa_status_string", "spa_last_error",
            "spa_set_attn_blocks_per_item")
@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
             "spa_page_summary_update": ([P, H, B, vp, i32, vp], ctypes.c_int),
             "spa_select_pages": ([P, H, B, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "spa_sparse_decode_attn": ([P, H, B, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp], ctypes.c_int),
+            "spa_append_decode_attn": ([P, H, B, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp],
+                                       ctypes.c_int),
             "spa_workspace_bytes": ([P, H, i32, i32, i32], sz),
             "spa_default_budget": ([i64], i32),
             "spa_set_attn_blocks_per_item": ([i32], ctypes.c_int),
@@ -281,9 +283,12 @@ def select_pages(pool: Pool, heads: Heads, batch: Batch, q, budget_tokens, k_max
 
 
 def sparse_decode_attn(pool: Pool, heads: Heads, batch: Batch, q, sel_pages, sel_count, sel_len,
-                       k_max: int, out, lse=None, workspace=None, stream=None, sel_phys=None) -> None:
+                       k_max: int, out, lse=None, workspace=None, stream=None, sel_phys=None,
+                       k_new=None, v_new=None) -> None:
     """spa_sparse_decode_attn: out fp32 [B][H_q][D], lse fp32 [B][H_q] or None; sel_phys as
-    written by the selection that produced sel_pages, or None to use the page table."""
+    written by the selection that produced sel_pages, or None to use the page table.
+    With k_new / v_new (bf16 [B][H_kv][D]): spa_append_decode_attn, which also appends the
+    step's token in the same launch."""
     p, h, b = pool.c(), _heads_for(heads, pool), batch.c()
     B, H, HQ = b.batch, pool.num_kv_heads, heads.num_q_heads
     _need(q, (B, HQ, HEAD_DIM), "bf16", "q")
@@ -296,9 +301,17 @@ def sparse_decode_attn(pool: Pool, heads: Heads, batch: Batch, q, sel_pages, sel
     _need(lse, (B, HQ), "f32", "lse", optional=True)
     _need(workspace, (None,), "u8", "workspace", optional=True)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().spa_sparse_decode_attn(ctypes.byref(p), ctypes.byref(h), ctypes.byref(b), _ptr(q),
-                                        _ptr(sel_pages), _ptr(sel_count), _ptr(sel_len), _ptr(sel_phys), k_max,
-                                        _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+    if k_new is None and v_new is None:
+        _check(lib().spa_sparse_decode_attn(ctypes.byref(p), ctypes.byref(h), ctypes.byref(b), _ptr(q),
+                                            _ptr(sel_pages), _ptr(sel_count), _ptr(sel_len), _ptr(sel_phys),
+                                            k_max, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                                            _stream(stream)))
+        return
+    _need(k_new, (B, H, HEAD_DIM), "bf16", "k_new")
+    _need(v_new, (B, H, HEAD_DIM), "bf16", "v_new")
+    _check(lib().spa_append_decode_attn(ctypes.byref(p), ctypes.byref(h), ctypes.byref(b), _ptr(k_new),
+                                        _ptr(v_new), _ptr(q), _ptr(sel_pages), _ptr(sel_count), _ptr(sel_len),
+                                        _ptr(sel_phys), k_max, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                         _stream(stream)))
 
 

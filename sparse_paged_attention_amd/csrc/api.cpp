@@ -363,10 +363,13 @@ spa_status spa_select_pages(const spa_pool* pool, const spa_heads* heads, const 
                     "select_pages launch");
 }
 
-spa_status spa_sparse_decode_attn(const spa_pool* pool, const spa_heads* heads, const spa_batch* batch,
-                                  const void* q, const int32_t* sel_pages, const int32_t* sel_count,
-                                  const int32_t* sel_len, const int32_t* sel_phys, int32_t k_max, float* out,
-                                  float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+namespace {
+
+// Shared by the attention entry points; k_new / v_new NULL: no token appended.
+spa_status decode_attn(const spa_pool* pool, const spa_heads* heads, const spa_batch* batch, const void* k_new,
+                       const void* v_new, const void* q, const int32_t* sel_pages, const int32_t* sel_count,
+                       const int32_t* sel_len, const int32_t* sel_phys, int32_t k_max, float* out, float* lse,
+                       void* ws, size_t ws_bytes, hipStream_t stream, const char* what) {
   spa::PoolArgs pl;
   spa::BatchArgs bt;
   spa::HeadList dyn;
@@ -383,7 +386,8 @@ spa_status spa_sparse_decode_attn(const spa_pool* pool, const spa_heads* heads, 
     return fail(SPA_ERR_INVALID, "dynamic heads need sel_pages / sel_count / sel_len");
   spa::AttnPlan plan;
   plan_attention(pl, heads, k_max, kind, bt.B, &plan);
-  if ((int64_t)bt.B * plan.items_per_seq > INT32_MAX) return fail(SPA_ERR_INVALID, "grid too large");
+  if ((int64_t)bt.B * plan.items_per_seq + (int64_t)bt.B * pl.hkv > INT32_MAX)
+    return fail(SPA_ERR_INVALID, "grid too large");
   plan.sel_mask = dyn.n > 0 ? ~int64_t(0) : 0;
   plan.use_phys = dyn.n > 0 && sel_phys != nullptr;
   if (dyn.n == 0) {                 // never used; read at index 0 to keep the loads branch-free
@@ -398,8 +402,30 @@ spa_status spa_sparse_decode_attn(const spa_pool* pool, const spa_heads* heads, 
   float* part_o = static_cast<float*>(ws);
   float* part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + ml_off);
   return hip_status(spa::launch_attn(pl, bt, plan, G, static_cast<const uint16_t*>(q), sel_pages, sel_count,
-                                     sel_len, sel_phys, out, lse, part_o, part_ml, stream),
-                    "sparse_decode_attn launch");
+                                     sel_len, sel_phys, out, lse, part_o, part_ml,
+                                     static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                                     stream),
+                    what);
+}
+
+}  // namespace
+
+spa_status spa_sparse_decode_attn(const spa_pool* pool, const spa_heads* heads, const spa_batch* batch,
+                                  const void* q, const int32_t* sel_pages, const int32_t* sel_count,
+                                  const int32_t* sel_len, const int32_t* sel_phys, int32_t k_max, float* out,
+                                  float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return decode_attn(pool, heads, batch, nullptr, nullptr, q, sel_pages, sel_count, sel_len, sel_phys, k_max, out,
+                     lse, ws, ws_bytes, stream, "sparse_decode_attn launch");
+}
+
+spa_status spa_append_decode_attn(const spa_pool* pool, const spa_heads* heads, const spa_batch* batch,
+                                  const void* k_new, const void* v_new, const void* q, const int32_t* sel_pages,
+                                  const int32_t* sel_count, const int32_t* sel_len, const int32_t* sel_phys,
+                                  int32_t k_max, float* out, float* lse, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  if (batch && batch->batch > 0 && (!k_new || !v_new)) return fail(SPA_ERR_INVALID, "k_new / v_new is NULL");
+  return decode_attn(pool, heads, batch, k_new, v_new, q, sel_pages, sel_count, sel_len, sel_phys, k_max, out,
+                     lse, ws, ws_bytes, stream, "append_decode_attn launch");
 }
 
 // ------------------------------------------------------------- allocator

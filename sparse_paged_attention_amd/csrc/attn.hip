@@ -20,7 +20,7 @@
 // into bf16 high and low parts so the products keep ~16 significant bits.
 // Keys are stored token-major and values channel-major per logical page, so
 // both tiles load straight from HBM into operand registers.
-#include "spa_internal.h"
+#include "pool_rows.h"
 
 namespace spa {
 namespace {
@@ -34,12 +34,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // log2(e) / sqrt(128): scores are kept in the log2 domain
 constexpr float kScaleLog2 = 0.12751743074602467f;
 constexpr float kLn2 = 0.69314718055994531f;
-
-__device__ __forceinline__ int32_t clamp_len(const BatchArgs& bt, int32_t b, int32_t P) {
-  int32_t L = bt.lens[b];
-  int32_t cap = bt.max_pp * P;
-  return L < 0 ? 0 : (L > cap ? cap : L);
-}
 
 // The same memory seen through the constant address space: wave-uniform
 // loads from it are scalar loads. Only for data no kernel of the launch
@@ -109,6 +103,14 @@ __device__ __forceinline__ float max_over_rows(float x) {
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
   auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
+// Cross-lane sum over the four 16-lane rows.
+__device__ __forceinline__ float sum_over_rows(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
 // Scores S^T[16 tok][16 q] of one block: 4 chained 16x16x32 MFMAs over D.
@@ -219,6 +221,30 @@ __device__ __forceinline__ void pv_pair(const PairTile& t, const PairProbs& pp, 
   }
 }
 
+// The token appended in the same launch comes from the caller's buffers, not
+// the pool: the head's last item starts its running state with it (reference
+// = its score, sum = 1, output = its value row), before any block. Lane
+// (g, quad) holds q channels 32*quad + 8*i .. +8 in qb[i] and output channels
+// 16c + 4*quad + r in o[c][r]; kw / vw are the matching key and value words.
+__device__ __forceinline__ void start_with_token(const uint4 (&kw)[4], const uint2 (&vw)[8],
+                                                 const bf16x8 (&qb)[4], State& st) {
+  const int quad = (threadIdx.x & 63) >> 4;
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    bf16x8 kb;
+    __builtin_memcpy(&kb, &kw[i], 16);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s = __builtin_fmaf((float)qb[i][j], (float)kb[j], s);
+  }
+  st.m = sum_over_rows(s) * kScaleLog2;
+  st.l = quad == 0 ? 1.f : 0.f;                    // the sum is folded over the quads at the end
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    st.o[c] = f32x4{__uint_as_float(vw[c].x << 16), __uint_as_float(vw[c].x & 0xFFFF0000u),
+                    __uint_as_float(vw[c].y << 16), __uint_as_float(vw[c].y & 0xFFFF0000u)};
+}
+
 // Which blocks an item covers. Blocks are numbered per head:
 //   streaming: the sink blocks, then the window blocks;
 //   dynamic:   block (i, s) = 16-token block s of the i-th selected page,
@@ -229,7 +255,8 @@ __device__ __forceinline__ void pv_pair(const PairTile& t, const PairProbs& pp, 
 // no membership test.
 struct BlockSource {
   int32_t kind;          // 0 streaming, 1 dynamic, 2 tail
-  int32_t L, ls;         // ls: L_s clamped to [0, L]
+  int32_t L, ls;         // ls: L_s clamped to [0, lim]
+  int32_t lim;           // pool rows below lim are read (L, or L - 1 when the last token is appended in this launch)
   int32_t s0, w0, nb_sink, first_w;          // streaming
   int32_t ls_floor;                          // tail
 };
@@ -282,9 +309,10 @@ __device__ __forceinline__ void run_blocks(const PoolArgs& pl, const int32_t* pt
         const int32_t v = v0 + u;
         int32_t t0, lo, hi;
         if (v < src.nb_sink) {
-          t0 = v * kBlockTokens; lo = t0; hi = min(t0 + kBlockTokens, src.s0);
+          t0 = v * kBlockTokens; lo = t0; hi = min(t0 + kBlockTokens, min(src.s0, src.lim));
         } else {
-          t0 = (src.first_w + v - src.nb_sink) * kBlockTokens; lo = max(t0, src.w0); hi = min(t0 + kBlockTokens, L);
+          t0 = (src.first_w + v - src.nb_sink) * kBlockTokens; lo = max(t0, src.w0);
+          hi = min(t0 + kBlockTokens, src.lim);
         }
         if (v >= v_end) { t0 = 0; lo = 0; hi = 0; }
         blk[u] = Block{t0, lo, hi, 0, 0};
@@ -293,7 +321,7 @@ __device__ __forceinline__ void run_blocks(const PoolArgs& pl, const int32_t* pt
 #pragma unroll
       for (int u = 0; u < NB; ++u) {
         const int32_t t0 = src.ls_floor + (v0 + u) * kBlockTokens;
-        const int32_t lo = max(t0, src.ls), hi = v0 + u < v_end ? min(t0 + kBlockTokens, L) : lo;
+        const int32_t lo = max(t0, src.ls), hi = v0 + u < v_end ? min(t0 + kBlockTokens, src.lim) : lo;
         blk[u] = Block{hi > lo ? t0 : 0, lo, hi, 0, 0};
       }
     }
@@ -360,11 +388,15 @@ struct HeadMask {
 
 // One item of one (sequence, KV head): the online softmax over its blocks and
 // a partial (max, sum, unnormalised output) per query head.
-template <int PG, int BPI, int DEPTH>
+// FRESH: the step's token is appended in this launch (k_new / v_new given);
+// a separate instantiation, so plain attention carries none of its code.
+template <int PG, int BPI, int DEPTH, bool FRESH>
 __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, AttnPlan plan, int32_t G,
                                                   const uint16_t* q, const int32_t* sel_pages,
                                                   const int32_t* sel_count, const int32_t* sel_len,
-                                                  const int32_t* sel_phys, float* part_o, float* part_ml) {
+                                                  const int32_t* sel_phys, float* part_o, float* part_ml,
+                                                  const uint32_t* k_new, const uint16_t* v_new,
+                                                  int32_t n_append) {
   constexpr int SB = PG / kBlockTokens;
   // Every launch argument the kernel uses, read into registers in one round:
   // left to itself the compiler fetches each argument just before its first
@@ -375,12 +407,21 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
                "s"(G), "s"(plan.dyn_mask[0]), "s"(plan.dyn_mask[1]), "s"(plan.dyn_mask[2]),
                "s"(plan.dyn_mask[3]), "s"(plan.sel_mask));
   asm volatile("" ::"s"(pl.k), "s"(pl.v), "s"(bt.pt), "s"(bt.lens), "s"(sel_pages), "s"(sel_count),
-               "s"(sel_len), "s"(sel_phys), "s"(q), "s"(part_o), "s"(part_ml), "s"(plan.use_phys));
+               "s"(sel_len), "s"(sel_phys), "s"(q), "s"(part_o), "s"(part_ml), "s"(plan.use_phys),
+               "s"(k_new), "s"(v_new), "s"(n_append));
   // work-group -> (sequence, head, item): head h's first item within the
   // sequence is h * items_stream + (dynamic heads below h) * (items_dyn - items_stream)
   const HeadMask mask(plan);
-  const int32_t b = blockIdx.x / plan.items_per_seq;
-  const int32_t rem = blockIdx.x - b * plan.items_per_seq;
+  // the first n_append work-groups write the step's token into the pool (one
+  // per sequence and KV head); no item reads that row from the pool
+  if (FRESH && (int32_t)blockIdx.x < n_append) {
+    const int32_t ab = (int32_t)blockIdx.x / pl.hkv, ah = (int32_t)blockIdx.x - ab * pl.hkv;
+    append_token(pl, bt, ab, ah, k_new, v_new, mask.dynamic(ah));
+    return;
+  }
+  const int32_t item = (int32_t)blockIdx.x - (FRESH ? n_append : 0);
+  const int32_t b = item / plan.items_per_seq;
+  const int32_t rem = item - b * plan.items_per_seq;
   const int32_t extra = plan.items_dyn - plan.items_stream;
   int32_t h = 0;
   for (int32_t hi = pl.hkv; hi - h > 1;) {
@@ -439,6 +480,19 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
     }
   }
 
+  // the step's token, when appended in this launch, is the last item's
+  const bool fresh = FRESH;
+  const bool owner = fresh && it == n_items - 1;
+  uint4 kw[4];
+  uint2 vw[8];
+  if (owner) {
+    const uint4* k4 = reinterpret_cast<const uint4*>(k_new + bh * (kHeadDim / 2) + 16 * quad);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kw[i] = k4[i];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) vw[c] = *reinterpret_cast<const uint2*>(v_new + bh * kHeadDim + 16 * c + 4 * quad);
+  }
+
   State st;
   st.m = -INFINITY;
   st.l = 0.f;
@@ -447,10 +501,14 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
 
   const int32_t cap = bt.max_pp * pl.P;
   const int32_t L = L_raw < 0 ? 0 : (L_raw > cap ? cap : L_raw);
+  // with the step's token appended in this launch, pool rows are read below
+  // L - 1 only
+  if (owner && L >= 1) start_with_token(kw, vw, qb, st);
   BlockSource src;
   src.kind = kind;
   src.L = L;
-  src.ls = min(max(ls_raw, 0), L);
+  src.lim = fresh ? max(L - 1, 0) : L;
+  src.ls = min(max(ls_raw, 0), src.lim);
   int32_t v_begin = it * BPI, v_end = 0;
   if (kind == 0) {
     src.s0 = min(plan.sink, L);
@@ -560,10 +618,16 @@ template <int PG, int BPI, int DEPTH = 4>
 hipError_t launch_attn_t(const PoolArgs& pool, const BatchArgs& batch, const AttnPlan& plan, int32_t G,
                          const uint16_t* q, const int32_t* sel_pages, const int32_t* sel_count,
                          const int32_t* sel_len, const int32_t* sel_phys, float* part_o, float* part_ml,
-                         float* out, float* lse, hipStream_t s) {
-  const int64_t grid = (int64_t)batch.B * plan.items_per_seq;
-  hipLaunchKernelGGL((attn_kernel<PG, BPI, DEPTH>), dim3((unsigned)grid), dim3(64), 0, s, pool, batch, plan, G, q,
-                     sel_pages, sel_count, sel_len, sel_phys, part_o, part_ml);
+                         float* out, float* lse, const uint16_t* k_new, const uint16_t* v_new, hipStream_t s) {
+  const int32_t n_append = k_new ? batch.B * pool.hkv : 0;
+  const int64_t grid = n_append + (int64_t)batch.B * plan.items_per_seq;
+  if (k_new)
+    hipLaunchKernelGGL((attn_kernel<PG, BPI, DEPTH, true>), dim3((unsigned)grid), dim3(64), 0, s, pool, batch, plan,
+                       G, q, sel_pages, sel_count, sel_len, sel_phys, part_o, part_ml,
+                       reinterpret_cast<const uint32_t*>(k_new), v_new, n_append);
+  else
+    hipLaunchKernelGGL((attn_kernel<PG, BPI, DEPTH, false>), dim3((unsigned)grid), dim3(64), 0, s, pool, batch,
+                       plan, G, q, sel_pages, sel_count, sel_len, sel_phys, part_o, part_ml, nullptr, nullptr, 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(combine_kernel, dim3(batch.B * pool.hkv * G), dim3(kCombineThreads), 0, s, pool.hkv, plan, G,
@@ -575,10 +639,10 @@ template <int PG>
 hipError_t launch_attn_p(const PoolArgs& pool, const BatchArgs& batch, const AttnPlan& plan, int32_t G,
                          const uint16_t* q, const int32_t* sel_pages, const int32_t* sel_count,
                          const int32_t* sel_len, const int32_t* sel_phys, float* part_o, float* part_ml,
-                         float* out, float* lse, hipStream_t s) {
+                         float* out, float* lse, const uint16_t* k_new, const uint16_t* v_new, hipStream_t s) {
   switch (plan.blocks_per_item) {
 #define SPA_BPI_CASE(n) \
-    case n: return launch_attn_t<PG, n>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, sel_phys, part_o, part_ml, out, lse, s);
+    case n: return launch_attn_t<PG, n>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, sel_phys, part_o, part_ml, out, lse, k_new, v_new, s);
     SPA_BPI_CASE(4) SPA_BPI_CASE(5) SPA_BPI_CASE(6) SPA_BPI_CASE(7) SPA_BPI_CASE(8) SPA_BPI_CASE(9)
     SPA_BPI_CASE(10) SPA_BPI_CASE(12) SPA_BPI_CASE(16)
 #undef SPA_BPI_CASE
@@ -591,12 +655,13 @@ hipError_t launch_attn_p(const PoolArgs& pool, const BatchArgs& batch, const Att
 hipError_t launch_attn(const PoolArgs& pool, const BatchArgs& batch, const AttnPlan& plan, int32_t G,
                        const uint16_t* q, const int32_t* sel_pages, const int32_t* sel_count,
                        const int32_t* sel_len, const int32_t* sel_phys, float* out, float* lse,
-                       float* part_o, float* part_ml, hipStream_t s) {
+                       float* part_o, float* part_ml, const uint16_t* k_new, const uint16_t* v_new,
+                       hipStream_t s) {
   if (batch.B == 0) return hipSuccess;
   switch (pool.p) {
-    case 16: return launch_attn_p<16>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, sel_phys, part_o, part_ml, out, lse, s);
-    case 32: return launch_attn_p<32>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, sel_phys, part_o, part_ml, out, lse, s);
-    case 64: return launch_attn_p<64>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, sel_phys, part_o, part_ml, out, lse, s);
+    case 16: return launch_attn_p<16>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, sel_phys, part_o, part_ml, out, lse, k_new, v_new, s);
+    case 32: return launch_attn_p<32>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, sel_phys, part_o, part_ml, out, lse, k_new, v_new, s);
+    case 64: return launch_attn_p<64>(pool, batch, plan, G, q, sel_pages, sel_count, sel_len, sel_phys, part_o, part_ml, out, lse, k_new, v_new, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -72,6 +72,7 @@ hipError_t launch_attn(const PoolArgs& pool, const BatchArgs& batch, const AttnP
                        const int32_t* sel_count, const int32_t* sel_len,
                        const int32_t* sel_phys, float* out,
                        float* lse, float* part_o, float* part_ml,
+                       const uint16_t* k_new, const uint16_t* v_new,   // NULL: no token appended
                        hipStream_t s);
 
 }  // namespace spa

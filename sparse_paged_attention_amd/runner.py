@@ -87,9 +87,19 @@ class DecodeLayer:
                            self.sel_len, self.k_max, self.out, self.lse, workspace=self.workspace,
                            sel_phys=self.sel_phys)
 
+    def append_attend(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor) -> None:
+        """append + attend in one launch (steps that reuse an earlier selection)."""
+        sparse_decode_attn(self.pool, self.heads, self.batch, q, self.sel_pages, self.sel_count,
+                           self.sel_len, self.k_max, self.out, self.lse, workspace=self.workspace,
+                           sel_phys=self.sel_phys, k_new=k_new, v_new=v_new)
+
     def step(self, q, k_new, v_new, do_select: bool) -> None:
-        """One decode step; seq_lens must already hold the lengths after the append."""
-        self.append(k_new, v_new)
+        """One decode step; seq_lens must already hold the lengths after the append.
+        A selecting step appends first (the selection reads the new summary); the
+        others append inside the attention launch."""
         if do_select:
+            self.append(k_new, v_new)
             self.select(q)
-        self.attend(q)
+            self.attend(q)
+        else:
+            self.append_attend(q, k_new, v_new)

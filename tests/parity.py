@@ -41,8 +41,9 @@ class ParityRun:
     """A workload on the GPU plus the oracle state needed to check it."""
 
     def __init__(self, wl: W.Workload, check_heads=None, threads: int = 16, strict_ties: bool = False,
-                 resolve_at_selection: bool = True):
+                 resolve_at_selection: bool = True, fused: bool = False):
         self.wl = wl
+        self.fused = fused               # steps without selection append inside the attention launch
         self.strict_ties = strict_ties
         self.check = check_heads if check_heads is not None else \
             [(b, h) for b in range(wl.batch) for h in range(wl.hkv)]
@@ -88,11 +89,14 @@ class ParityRun:
         layer.set_lengths(lens)
         layer.set_budget([wl.budget_at(int(L)) for L in lens])
         qd = bits_to_bf16(q)
-        layer.append(bits_to_bf16(kn), bits_to_bf16(vn))
         select = wl.selects_at(i)
-        if select:
-            layer.select(qd, scores=self.scores)
-        layer.attend(qd)
+        if self.fused and not select:
+            layer.append_attend(qd, bits_to_bf16(kn), bits_to_bf16(vn))
+        else:
+            layer.append(bits_to_bf16(kn), bits_to_bf16(vn))
+            if select:
+                layer.select(qd, scores=self.scores)
+            layer.attend(qd)
         torch.cuda.synchronize()
         out = layer.out.cpu().numpy().astype(np.float64)
         lse = layer.lse.cpu().numpy().astype(np.float64)

@@ -183,3 +183,23 @@ def test_attn_blocks_per_item_setting(spa):
         assert lib.spa_set_attn_blocks_per_item(bad) == 1
         assert b"blocks per item" in lib.spa_last_error()
     assert lib.spa_set_attn_blocks_per_item(0) == 0
+
+
+def test_append_decode_attn_validation(spa):
+    """The append-and-attend entry point checks its own inputs and then the
+    attention's, before anything is launched."""
+    L = spa.lib()
+    pool, heads = mkpool(spa), mkheads(spa)
+
+    def call(batch, k_new=FAKE, v_new=FAKE, q=FAKE, k_max=8, ws_bytes=1 << 30):
+        return L.spa_append_decode_attn(ctypes.byref(pool), ctypes.byref(heads), ctypes.byref(batch), k_new,
+                                        v_new, q, FAKE, FAKE, FAKE, None, k_max, FAKE, None, FAKE, ws_bytes,
+                                        None)
+    assert call(mkbatch(spa), k_new=None) == 1
+    assert call(mkbatch(spa), v_new=None) == 1
+    assert call(mkbatch(spa), q=None) == 1
+    assert call(mkbatch(spa), k_max=0) == 1
+    assert call(mkbatch(spa), ws_bytes=16) == 4
+    assert call(mkbatch(spa, B=-1)) == 1
+    assert call(mkbatch(spa, B=0, pt=None, lens=None), k_new=None, v_new=None) == 0
+

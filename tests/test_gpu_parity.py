@@ -20,10 +20,10 @@ def gpu():
     oracle.build()
 
 
-def run(wl, steps=None, check=None):
+def run(wl, steps=None, check=None, fused=False):
     log(f"[parity] {wl.name} B={wl.batch} hq={wl.hq} hkv={wl.hkv} p={wl.p} P={wl.P} "
         f"contexts={wl.contexts[:4]} steps={wl.steps if steps is None else steps}")
-    pr = ParityRun(wl, check_heads=check)
+    pr = ParityRun(wl, check_heads=check, fused=fused)
     reps = pr.run(steps)
     assert_reports(reps)
     return pr, reps
@@ -129,6 +129,73 @@ def test_every_item_size(bpi):
                                               window=300))
         run(W.Workload(f"p64_bpi{bpi}", 2400 + bpi, 2, 8, 2, 64, 256, (2000, 700), 3, 2, (0, 1), 8, 600,
                        512, True))
+    finally:
+        spa.set_attn_blocks_per_item(0)
+
+
+def test_append_inside_attention_pool_bit_exact():
+    """spa_append_decode_attn writes the same pool (keys, values, summaries)
+    as spa_kv_pool_append: three steps, new pages opened on the way."""
+    wl = W.WORKLOADS["toy_4k"].scaled(contexts=(300, 77, 1, 33), batch=4, steps=3, permute=True,
+                                      kind=(1, 0), planted=None)
+    pr = ParityRun(wl, check_heads=[])
+    layer = pr.layer
+    for i in range(wl.steps):
+        q, kn, vn = pr.step_inputs(i)
+        layer.set_lengths([wl.seq_len(b, i) for b in range(wl.batch)])
+        layer.append_attend(bits_to_bf16(q), bits_to_bf16(kn), bits_to_bf16(vn))
+    torch.cuda.synchronize()
+    kp = layer.pool.k.view(torch.int16).cpu().numpy().view(np.uint16)
+    vp = layer.pool.v.view(torch.int16).cpu().numpy().view(np.uint16)
+    sp = layer.pool.summary.view(torch.int16).cpu().numpy().view(np.uint16)
+    pt = W.page_table(wl)
+    p, P, r = wl.p, wl.P, wl.P // wl.p
+    for b in range(wl.batch):
+        L = wl.final_len(b)
+        for h in range(wl.hkv):
+            K = W.kv(wl, b, h, "k")[:L]
+            V = W.kv(wl, b, h, "v")[:L]
+            t = np.arange(L)
+            phys = pt[b, t // P]
+            slot = t % P
+            np.testing.assert_array_equal(kp[phys, h, slot], K)
+            np.testing.assert_array_equal(vp[phys, h, slot // p, :, slot % p], V)
+            if wl.kind[h]:
+                kmin, kmax = oracle.page_summary(K, p)
+                j = np.arange(kmin.shape[0])
+                np.testing.assert_array_equal(sp[pt[b, j // r], h, j % r, 0], kmin)
+                np.testing.assert_array_equal(sp[pt[b, j // r], h, j % r, 1], kmax)
+
+
+def test_append_inside_attention_128k_small():
+    """The 128K shape at small contexts, steps without selection appending in
+    the attention launch (selection every 4 steps, tails of up to 3 tokens)."""
+    wl = W.WORKLOADS["llama3_128k"].scaled(contexts=(4100, 3001, 1000, 17), steps=9, budget=512,
+                                           window=300)
+    run(wl, fused=True)
+
+
+def test_append_inside_attention_edges():
+    """Appending in the attention launch: a second token (the dynamic heads'
+    tail is the new token alone), tokens inside the sink, tokens opening a
+    new block and a new page, ragged MHA heads, p = 64 pages."""
+    wl = W.Workload("fused_edges", 2700, 6, 16, 4, 16, 64, (1, 2, 16, 33, 64, 1090), 4, 3, (0, 1, 1, 0),
+                    32, 64, 256, True)
+    run(wl, fused=True)
+    run(W.WORKLOADS["ragged_mha"].scaled(contexts=(2500, 40, 1800, 3333, 700, 16, 1, 2049), batch=8,
+                                         steps=5), fused=True)
+    run(W.Workload("fused_p64", 2800, 2, 8, 2, 64, 256, (2000, 700), 5, 2, (0, 1), 8, 600, 512, True),
+        fused=True)
+
+
+@pytest.mark.parametrize("bpi", [4, 5, 7, 16])
+def test_append_inside_attention_item_sizes(bpi):
+    """Every head's last item carries the appended token, whatever the item size."""
+    import sparse_paged_attention_amd as spa
+    spa.set_attn_blocks_per_item(bpi)
+    try:
+        run(W.WORKLOADS["llama3_128k"].scaled(contexts=(4100, 3001, 1000, 17), steps=5, budget=512,
+                                              window=300), fused=True)
     finally:
         spa.set_attn_blocks_per_item(0)
 

@@ -170,7 +170,9 @@ void size_items(const spa::PoolArgs& pl, const spa_heads* heads, int32_t k_max, 
   plan->blocks_per_item = bpi;
   plan->items_stream = (int32_t)((nb_stream + bpi - 1) / bpi);
   plan->items_dyn = (int32_t)((nb_dyn + bpi - 1) / bpi) + 1;
-  plan->item_stride = std::max(plan->items_stream, plan->items_dyn);
+  // one slot more: the partial of a token appended inside the attention launch
+  plan->item_stride = std::max(plan->items_stream, plan->items_dyn) + 1;
+  plan->extra_partial = 0;
 }
 
 // batch < 0: size for the largest item count any batch size can use

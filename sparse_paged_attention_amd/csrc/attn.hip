@@ -221,28 +221,55 @@ __device__ __forceinline__ void pv_pair(const PairTile& t, const PairProbs& pp, 
   }
 }
 
-// The token appended in the same launch comes from the caller's buffers, not
-// the pool: the head's last item starts its running state with it (reference
-// = its score, sum = 1, output = its value row), before any block. Lane
-// (g, quad) holds q channels 32*quad + 8*i .. +8 in qb[i] and output channels
-// 16c + 4*quad + r in o[c][r]; kw / vw are the matching key and value words.
-__device__ __forceinline__ void start_with_token(const uint4 (&kw)[4], const uint2 (&vw)[8],
-                                                 const bf16x8 (&qb)[4], State& st) {
-  const int quad = (threadIdx.x & 63) >> 4;
+// The partial of the token appended in the same launch, taken from the
+// caller's buffers (the pool row is being written by this very wave): for
+// each query g of the group, reference = its score q_g . k / sqrt(D) (log2
+// units), sum = 1, output = the value row; an empty partial when the token
+// has no pool slot (no token, or an unmapped page: such a token is not
+// attended). Written to slot `it` of the head like an item's partial. Lane
+// (g, quad) covers q channels 32*quad .. +32 and output channels
+// 16c + 4*quad + r, as in the items.
+__device__ __forceinline__ void token_partial(const PoolArgs& pl, const BatchArgs& bt, int32_t b, int32_t h,
+                                              int32_t G, int32_t item_stride, int32_t it, const uint16_t* q,
+                                              const uint16_t* k_new, const uint16_t* v_new, float* part_o,
+                                              float* part_ml) {
+  const int lane = threadIdx.x & 63, g = lane & 15, quad = lane >> 4;
+  const int32_t L = clamp_len(bt, b, pl.P);
+  bool valid = L >= 1;
+  if (valid) {
+    const int32_t phys = bt.pt[(int64_t)b * bt.max_pp + (L - 1) / pl.P];
+    valid = phys >= 0 && phys < pl.N;
+  }
+  const int64_t bh = (int64_t)b * pl.hkv + h;
+  const int32_t gq = g < G ? g : 0;
+  const uint4* q4 = reinterpret_cast<const uint4*>(q + (bh * G + gq) * kHeadDim + 32 * quad);
+  const uint4* k4 = reinterpret_cast<const uint4*>(k_new + bh * kHeadDim + 32 * quad);
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    bf16x8 kb;
-    __builtin_memcpy(&kb, &kw[i], 16);
+    const uint4 qw = q4[i], kw = k4[i];
+    bf16x8 qv, kv;
+    __builtin_memcpy(&qv, &qw, 16);
+    __builtin_memcpy(&kv, &kw, 16);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) s = __builtin_fmaf((float)qb[i][j], (float)kb[j], s);
+    for (int j = 0; j < 8; ++j) s = __builtin_fmaf((float)qv[j], (float)kv[j], s);
   }
-  st.m = sum_over_rows(s) * kScaleLog2;
-  st.l = quad == 0 ? 1.f : 0.f;                    // the sum is folded over the quads at the end
+  const float t = sum_over_rows(s) * kScaleLog2;
+  if (g >= G) return;
+  const int64_t slot = (bh * item_stride + it) * G + g;
+  float* o = part_o + slot * kHeadDim + 4 * quad;
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
-    st.o[c] = f32x4{__uint_as_float(vw[c].x << 16), __uint_as_float(vw[c].x & 0xFFFF0000u),
-                    __uint_as_float(vw[c].y << 16), __uint_as_float(vw[c].y & 0xFFFF0000u)};
+  for (int c = 0; c < 8; ++c) {
+    const uint2 w = *reinterpret_cast<const uint2*>(v_new + bh * kHeadDim + 16 * c + 4 * quad);
+    f32x4 v = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
+               __uint_as_float(w.y & 0xFFFF0000u)};
+    if (!valid) v = f32x4{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f32x4*>(o + 16 * c) = v;
+  }
+  if (quad == 0) {
+    part_ml[slot * 2 + 0] = valid ? t : -INFINITY;
+    part_ml[slot * 2 + 1] = valid ? 1.f : 0.f;
+  }
 }
 
 // Which blocks an item covers. Blocks are numbered per head:
@@ -405,21 +432,27 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
                "s"(plan.items_dyn), "s"(plan.item_stride), "s"(plan.items_per_seq), "s"(plan.sink),
                "s"(plan.window), "s"(plan.k_max),
                "s"(G), "s"(plan.dyn_mask[0]), "s"(plan.dyn_mask[1]), "s"(plan.dyn_mask[2]),
-               "s"(plan.dyn_mask[3]), "s"(plan.sel_mask));
+               "s"(plan.dyn_mask[3]), "s"(plan.sel_mask), "s"(plan.use_phys));
   asm volatile("" ::"s"(pl.k), "s"(pl.v), "s"(bt.pt), "s"(bt.lens), "s"(sel_pages), "s"(sel_count),
-               "s"(sel_len), "s"(sel_phys), "s"(q), "s"(part_o), "s"(part_ml), "s"(plan.use_phys),
-               "s"(k_new), "s"(v_new), "s"(n_append));
+               "s"(sel_len), "s"(sel_phys), "s"(q), "s"(part_o), "s"(part_ml),
+               "s"(k_new), "s"(v_new), "s"(n_append), "s"(bt.B));
   // work-group -> (sequence, head, item): head h's first item within the
   // sequence is h * items_stream + (dynamic heads below h) * (items_dyn - items_stream)
   const HeadMask mask(plan);
-  // the first n_append work-groups write the step's token into the pool (one
-  // per sequence and KV head); no item reads that row from the pool
-  if (FRESH && (int32_t)blockIdx.x < n_append) {
-    const int32_t ab = (int32_t)blockIdx.x / pl.hkv, ah = (int32_t)blockIdx.x - ab * pl.hkv;
+  // the last n_append work-groups (after every item, so the items keep their
+  // places on the compute units) write the step's token into the pool, one
+  // per sequence and KV head, and its partial; no item reads that row
+  const int32_t n_items_all = bt.B * plan.items_per_seq;
+  if (FRESH && (int32_t)blockIdx.x >= n_items_all) {
+    const int32_t w = (int32_t)blockIdx.x - n_items_all;
+    const int32_t ab = w / pl.hkv, ah = w - ab * pl.hkv;
+    const int32_t n_it = mask.dynamic(ah) ? plan.items_dyn : plan.items_stream;
+    token_partial(pl, bt, ab, ah, G, plan.item_stride, n_it, q, reinterpret_cast<const uint16_t*>(k_new), v_new,
+                  part_o, part_ml);
     append_token(pl, bt, ab, ah, k_new, v_new, mask.dynamic(ah));
     return;
   }
-  const int32_t item = (int32_t)blockIdx.x - (FRESH ? n_append : 0);
+  const int32_t item = (int32_t)blockIdx.x;
   const int32_t b = item / plan.items_per_seq;
   const int32_t rem = item - b * plan.items_per_seq;
   const int32_t extra = plan.items_dyn - plan.items_stream;
@@ -480,19 +513,6 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
     }
   }
 
-  // the step's token, when appended in this launch, is the last item's
-  const bool fresh = FRESH;
-  const bool owner = fresh && it == n_items - 1;
-  uint4 kw[4];
-  uint2 vw[8];
-  if (owner) {
-    const uint4* k4 = reinterpret_cast<const uint4*>(k_new + bh * (kHeadDim / 2) + 16 * quad);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) kw[i] = k4[i];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) vw[c] = *reinterpret_cast<const uint2*>(v_new + bh * kHeadDim + 16 * c + 4 * quad);
-  }
-
   State st;
   st.m = -INFINITY;
   st.l = 0.f;
@@ -502,12 +522,11 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
   const int32_t cap = bt.max_pp * pl.P;
   const int32_t L = L_raw < 0 ? 0 : (L_raw > cap ? cap : L_raw);
   // with the step's token appended in this launch, pool rows are read below
-  // L - 1 only
-  if (owner && L >= 1) start_with_token(kw, vw, qb, st);
+  // L - 1 only (the token has a partial of its own)
   BlockSource src;
   src.kind = kind;
   src.L = L;
-  src.lim = fresh ? max(L - 1, 0) : L;
+  src.lim = FRESH ? max(L - 1, 0) : L;
   src.ls = min(max(ls_raw, 0), src.lim);
   int32_t v_begin = it * BPI, v_end = 0;
   if (kind == 0) {
@@ -572,12 +591,14 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(int32_t hkv, A
   __shared__ float sM[kCombineThreads], sl[kCombineThreads];
   // all launch arguments in one scalar-memory round trip (see attn_kernel)
   asm volatile("" ::"s"(hkv), "s"(G), "s"(plan.items_stream), "s"(plan.items_dyn), "s"(plan.item_stride),
+               "s"(plan.extra_partial),
                "s"(plan.dyn_mask[0]), "s"(plan.dyn_mask[1]), "s"(plan.dyn_mask[2]), "s"(plan.dyn_mask[3]),
                "s"(part_o), "s"(part_ml), "s"(out), "s"(lse));
   const HeadMask mask(plan);
   const int32_t bh = blockIdx.x / G, g = blockIdx.x - bh * G;
   const int32_t h = bh % hkv;
-  const int32_t n_items = mask.dynamic(h) ? plan.items_dyn : plan.items_stream;
+  // (+1: the partial of a token appended in the attention launch)
+  const int32_t n_items = (mask.dynamic(h) ? plan.items_dyn : plan.items_stream) + plan.extra_partial;
   const int64_t slot0 = (int64_t)bh * plan.item_stride * G + g;     // slot(i) = slot0 + i * G
   const int32_t tid = threadIdx.x;
   const int32_t sl_id = tid / (kHeadDim / 4), c4 = tid % (kHeadDim / 4);
@@ -630,7 +651,9 @@ hipError_t launch_attn_t(const PoolArgs& pool, const BatchArgs& batch, const Att
                        plan, G, q, sel_pages, sel_count, sel_len, sel_phys, part_o, part_ml, nullptr, nullptr, 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(batch.B * pool.hkv * G), dim3(kCombineThreads), 0, s, pool.hkv, plan, G,
+  AttnPlan cplan = plan;
+  cplan.extra_partial = k_new ? 1 : 0;
+  hipLaunchKernelGGL(combine_kernel, dim3(batch.B * pool.hkv * G), dim3(kCombineThreads), 0, s, pool.hkv, cplan, G,
                      part_o, part_ml, out, lse);
   return hipGetLastError();
 }

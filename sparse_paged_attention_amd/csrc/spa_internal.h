@@ -50,8 +50,9 @@ struct AttnPlan {
   int32_t sink, window;
   int32_t k_max;
   uint32_t dyn_mask[kMaxKvHeads / 32];   // bit h set: KV head h is dynamic
-  int64_t sel_mask;                      // ~0 with dynamic heads, 0 without (selection unused)
   int32_t use_phys;                      // selected pages' physical pages come with the selection
+  int32_t extra_partial;                 // 1: slot items_* of each head holds an appended token's partial
+  int64_t sel_mask;                      // ~0 with dynamic heads, 0 without (selection unused)
 };
 
 // ---- launchers (return hipError_t of the launch) -------------------------

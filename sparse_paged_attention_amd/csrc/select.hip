@@ -55,7 +55,14 @@ struct ScoreShape {
   static constexpr int PASS = GPW * NP;             // pages per pass
   static constexpr int PASSES = 8;
   static constexpr int RING = 2;                    // passes in flight
-  static constexpr int RANGE = PASS * PASSES;       // pages per wave (<= 128)
+  static constexpr int RANGE = PASS * PASSES;       // pages per wave
+  // the last range of a head takes up to one pass more, so that a length just
+  // past a multiple of RANGE needs no extra wave (which would wait for a free
+  // slot until every other wave of the launch has finished); not for G > 4,
+  // whose registers the extra pass would push past two waves per SIMD
+  static constexpr int XPASS = G <= 4 ? 1 : 0;
+  static constexpr int MAXP = PASSES + XPASS;
+  static constexpr int OFFS = PASS * MAXP;          // pages of the longest range
 };
 
 template <int CPL>
@@ -90,8 +97,8 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
                                                    const uint16_t* __restrict__ q,
                                                    float* __restrict__ scores, int32_t n_max) {
   using S = ScoreShape<G>;
-  static_assert(S::RANGE <= 128, "two page offsets per lane");
-  __shared__ uint32_t offs[128];
+  static_assert(S::OFFS <= 192, "three page offsets per lane");
+  __shared__ uint32_t offs[S::OFFS];
   const int32_t b = blockIdx.y / dyn.n, h = dyn.id[blockIdx.y % dyn.n];
   const int32_t L = clamp_len(bt, b, pl.P);
   const int32_t n = (L + pl.p - 1) / pl.p;
@@ -107,9 +114,9 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
   // table, or ~0 for pages past the length or unmapped
   const int32_t* pt_row = bt.pt + (int64_t)b * bt.max_pp;
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < 3; ++k) {
     const int32_t i = lane + 64 * k, j = base + i;
-    if (i < S::RANGE) {
+    if (i < S::OFFS) {
       const int32_t phys = pt_row[min(j / pl.r, bt.max_pp - 1)];
       const bool ok = j < n && phys >= 0 && phys < pl.N;
       offs[i] = ok ? (uint32_t)(((int64_t)phys * pl.hkv + h) * pl.r + j % pl.r) : ~0u;
@@ -207,7 +214,8 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
   // at run time; deeper rings measured slower)
   // Passes past the head's last page are skipped (wave-uniform): the last
   // range of a head is often nearly empty.
-  const int32_t live = min(S::PASSES, (n - base + S::PASS - 1) / S::PASS);
+  const int32_t cap = blockIdx.x + 1 == gridDim.x ? S::MAXP : S::PASSES;
+  const int32_t live = min(cap, (n - base + S::PASS - 1) / S::PASS);
   Pass ring[S::RING];
 #pragma unroll
   for (int it = 0; it < S::RING; ++it)
@@ -218,6 +226,9 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
     compute(it, ring[it % S::RING]);
     if (it + S::RING < live) issue(it + S::RING, ring[it % S::RING]);
   }
+  // the extra pass of a head's last range (issued by the loop above)
+  if constexpr (S::XPASS > 0)
+    if (live > S::PASSES) compute(S::PASSES, ring[S::PASSES % S::RING]);
 }
 
 // ------------------------------------------------------------------ top-k
@@ -485,7 +496,9 @@ template <int G>
 hipError_t launch_score_g(const PoolArgs& pool, const BatchArgs& batch, const HeadList& dyn,
                           const uint16_t* q, float* scores, int32_t n_max, hipStream_t s) {
   using S = ScoreShape<G>;
-  dim3 grid((n_max + S::RANGE - 1) / S::RANGE, batch.B * dyn.n);
+  // ranges of RANGE pages; the last one also takes up to PASS more
+  const int32_t ranges = std::max(1, (n_max - S::XPASS * S::PASS + S::RANGE - 1) / S::RANGE);
+  dim3 grid(ranges, batch.B * dyn.n);
   hipLaunchKernelGGL(score_kernel<G>, grid, dim3(64), 0, s, pool, batch, dyn, q, scores, n_max);
   return hipGetLastError();
 }

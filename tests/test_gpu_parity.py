@@ -201,10 +201,11 @@ def test_append_inside_attention_item_sizes(bpi):
 
 
 def test_score_ranges_of_every_fill():
-    """Scoring works on ranges of 128 pages in passes of 16: contexts whose
-    last range holds 1, 17, 33, 113 and 128 pages (1 to 8 live passes) and
-    one that ends inside a page."""
-    n_pages = (129, 145, 161, 241, 256, 227)
+    """Scoring works on ranges of 128 pages in passes of 16, a head's last
+    range taking one pass more: contexts whose last range holds 1, 17, 33,
+    113, 128 and 132 pages (1 to 9 live passes) and one that ends inside a
+    page."""
+    n_pages = (129, 145, 161, 241, 256, 260, 227)
     ctx = tuple(16 * n for n in n_pages[:-1]) + (16 * n_pages[-1] - 5,)
     wl = W.Workload("score_fill", 2600, len(ctx), 16, 4, 16, 64, ctx, 2, 1, (1, 0, 1, 1), 16, 100, 512,
                     True)

@@ -9,9 +9,9 @@ decode steps. Inputs are synthetic (seeded N(0,1) bf16) and resident in HBM.
 
 A step is one pass of the whole hot path for one attention layer: append the
 new token, refresh its page summary, select pages (every 4th decode step),
-sparse decode attention for all heads. Steps without selection append inside
-the attention launch (spa_append_decode_attn); selecting steps append first,
-since the selection reads the new token's page summary. To keep the timing honest about HBM
+sparse decode attention for all heads. The append runs inside the attention
+launch on steps without selection (spa_append_decode_attn) and inside the
+selection's scoring launch on the others (spa_append_select_pages). To keep the timing honest about HBM
 (a step touches 51-118 MB, less than the 256 MB last-level cache), the layer
 is replicated R times with separate pools and consecutive steps cycle through
 the replicas, as the layers of a model do; the timed steps are replayed from
@@ -179,9 +179,8 @@ def main() -> int:
         t, r = divmod(s, R)
         layer = layers[r]
         layer.use_lengths(lens[t])
-        if wl.selects_at(t):                    # the selection reads the new token's summary
-            layer.append(kn[t], vn[t])
-            layer.select(qs[s])
+        if wl.selects_at(t):                    # append inside the scoring launch
+            layer.append_select(qs[s], kn[t], vn[t])
             layer.attend(qs[s])
         else:                                   # append inside the attention launch
             layer.append_attend(qs[s], kn[t], vn[t])

@@ -175,6 +175,23 @@ spa_status spa_select_pages(const spa_pool* pool, const spa_heads* heads,
                             int32_t* sel_phys, float* scores, void* ws, size_t ws_bytes,
                             hipStream_t stream);
 
+/* ---- a1 + a2 + a3 + a4 in one launch pair -----------------------------
+ * The same pool state and outputs as spa_kv_pool_append(pool, heads, batch,
+ * k_new, v_new) followed by spa_select_pages with the other arguments: the
+ * scoring launch also writes token L_b - 1 (k_new, v_new: device bf16
+ * [B][H_kv][D], read only) into its pool slot and rebuilds the summary of its
+ * logical page for every dynamic head, and scores that page with the new key
+ * merged into its summary (the step order of the LServe write-up "3.2
+ * 解码阶段加速": append, then select on the updated summaries). For steps that
+ * select; the pool rows it writes are read by spa_sparse_decode_attn
+ * afterwards. Same workspace as spa_select_pages. */
+spa_status spa_append_select_pages(const spa_pool* pool, const spa_heads* heads,
+                                   const spa_batch* batch, const void* k_new, const void* v_new,
+                                   const void* q, const int32_t* budget_tokens, int32_t k_max,
+                                   int32_t* sel_pages, int32_t* sel_count, int32_t* sel_len,
+                                   int32_t* sel_phys, float* scores, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
 /* ---- a6 + a7 + a8: unified sparse decode attention ----------------------
  * For every sequence b and query head i (KV head h = i / G):
  *     out[b][i] = sum_{t in T} softmax_t(q_i . K_t / sqrt(D)) V_t,

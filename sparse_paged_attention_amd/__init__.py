@@ -53,7 +53,8 @@ class c_batch(ctypes.Structure):
 
 
 EXPORTS = ("spa_kv_pool_append", "spa_kv_pool_write", "spa_page_summary_update",
-           "spa_select_pages", "spa_sparse_decode_attn", "spa_append_decode_attn", "spa_workspace_bytes",
+           "spa_select_pages", "spa_append_select_pages", "spa_sparse_decode_attn", "spa_append_decode_attn",
+           "spa_workspace_bytes",
            "spa_default_budget", "spa_alloc_create", "spa_alloc_pages", "spa_alloc_free",
            "spa_alloc_num_free", "spa_alloc_destroy", "spa_status_string", "spa_last_error",
            "spa_set_attn_blocks_per_item")
@@ -76,6 +77,8 @@ def lib() -> ctypes.CDLL:
             "spa_kv_pool_write": ([P, vp, i32, i64, i64, vp, vp, vp], ctypes.c_int),
             "spa_page_summary_update": ([P, H, B, vp, i32, vp], ctypes.c_int),
             "spa_select_pages": ([P, H, B, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+            "spa_append_select_pages": ([P, H, B, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp],
+                                        ctypes.c_int),
             "spa_sparse_decode_attn": ([P, H, B, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp], ctypes.c_int),
             "spa_append_decode_attn": ([P, H, B, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp],
                                        ctypes.c_int),
@@ -260,10 +263,12 @@ def workspace_bytes(pool: Pool, heads: Heads, batch: int, max_pages: int, k_max:
 
 def select_pages(pool: Pool, heads: Heads, batch: Batch, q, budget_tokens, k_max: int,
                  sel_pages, sel_count, sel_len, scores=None, workspace=None, stream=None,
-                 sel_phys=None) -> None:
+                 sel_phys=None, k_new=None, v_new=None) -> None:
     """spa_select_pages: q bf16 [B][H_q][D]; budget_tokens int32 [B];
     writes sel_pages int32 [B][H_kv][k_max], sel_count int32 [B][H_kv], sel_len int32 [B],
-    and, when given, sel_phys int32 [B][H_kv][k_max] (physical page of each selected page)."""
+    and, when given, sel_phys int32 [B][H_kv][k_max] (physical page of each selected page).
+    With k_new / v_new (bf16 [B][H_kv][D]): spa_append_select_pages, which also appends the
+    step's token in the same launches."""
     p, h, b = pool.c(), _heads_for(heads, pool), batch.c()
     B, H = b.batch, pool.num_kv_heads
     _need(q, (B, heads.num_q_heads, HEAD_DIM), "bf16", "q")
@@ -276,10 +281,18 @@ def select_pages(pool: Pool, heads: Heads, batch: Batch, q, budget_tokens, k_max
     _need(scores, (B, H, n_max), "f32", "scores", optional=True)
     _need(workspace, (None,), "u8", "workspace", optional=True)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().spa_select_pages(ctypes.byref(p), ctypes.byref(h), ctypes.byref(b), _ptr(q),
-                                  _ptr(budget_tokens), k_max, _ptr(sel_pages), _ptr(sel_count),
-                                  _ptr(sel_len), _ptr(sel_phys), _ptr(scores), _ptr(workspace), ws_bytes,
-                                  _stream(stream)))
+    if k_new is None and v_new is None:
+        _check(lib().spa_select_pages(ctypes.byref(p), ctypes.byref(h), ctypes.byref(b), _ptr(q),
+                                      _ptr(budget_tokens), k_max, _ptr(sel_pages), _ptr(sel_count),
+                                      _ptr(sel_len), _ptr(sel_phys), _ptr(scores), _ptr(workspace), ws_bytes,
+                                      _stream(stream)))
+        return
+    _need(k_new, (B, H, HEAD_DIM), "bf16", "k_new")
+    _need(v_new, (B, H, HEAD_DIM), "bf16", "v_new")
+    _check(lib().spa_append_select_pages(ctypes.byref(p), ctypes.byref(h), ctypes.byref(b), _ptr(k_new),
+                                         _ptr(v_new), _ptr(q), _ptr(budget_tokens), k_max, _ptr(sel_pages),
+                                         _ptr(sel_count), _ptr(sel_len), _ptr(sel_phys), _ptr(scores),
+                                         _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def sparse_decode_attn(pool: Pool, heads: Heads, batch: Batch, q, sel_pages, sel_count, sel_len,

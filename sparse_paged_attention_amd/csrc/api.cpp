@@ -332,10 +332,13 @@ size_t spa_workspace_bytes(const spa_pool* pool, const spa_heads* heads, int32_t
   return bytes;
 }
 
-spa_status spa_select_pages(const spa_pool* pool, const spa_heads* heads, const spa_batch* batch,
-                            const void* q, const int32_t* budget_tokens, int32_t k_max,
-                            int32_t* sel_pages, int32_t* sel_count, int32_t* sel_len, int32_t* sel_phys,
-                            float* scores, void* ws, size_t ws_bytes, hipStream_t stream) {
+namespace {
+
+// Shared by the selection entry points; k_new / v_new NULL: no token appended.
+spa_status select_pages(const spa_pool* pool, const spa_heads* heads, const spa_batch* batch, const void* k_new,
+                        const void* v_new, const void* q, const int32_t* budget_tokens, int32_t k_max,
+                        int32_t* sel_pages, int32_t* sel_count, int32_t* sel_len, int32_t* sel_phys,
+                        float* scores, void* ws, size_t ws_bytes, hipStream_t stream, const char* what) {
   spa::PoolArgs pl;
   spa::BatchArgs bt;
   spa::HeadList dyn;
@@ -350,7 +353,16 @@ spa_status spa_select_pages(const spa_pool* pool, const spa_heads* heads, const 
     return fail(SPA_ERR_UNSUPPORTED, "max_pages * P / p = %d logical pages exceeds %lld", n_max,
                 (long long)kMaxScoredPages);
   if ((int64_t)bt.B * dyn.n > 2147483647LL / 1) return fail(SPA_ERR_INVALID, "too many heads");
-  if (bt.B == 0 || dyn.n == 0) return ok();
+  if (bt.B == 0) return ok();
+  const bool fresh = k_new != nullptr || v_new != nullptr;
+  if (fresh && (!k_new || !v_new)) return fail(SPA_ERR_INVALID, "k_new / v_new is NULL");
+  if (dyn.n == 0)                   // nothing to select: the append alone
+    return fresh ? hip_status(spa::launch_select(pl, bt, dyn, G, nullptr, nullptr, k_max, nullptr, nullptr,
+                                                 nullptr, nullptr, nullptr, n_max,
+                                                 static_cast<const uint16_t*>(k_new),
+                                                 static_cast<const uint16_t*>(v_new), stream),
+                              what)
+                 : ok();
   if (!q || !budget_tokens || !sel_pages || !sel_count || !sel_len)
     return fail(SPA_ERR_INVALID, "q / budget_tokens / sel_pages / sel_count / sel_len is NULL");
   float* sc = scores;
@@ -361,8 +373,30 @@ spa_status spa_select_pages(const spa_pool* pool, const spa_heads* heads, const 
     sc = static_cast<float*>(ws);
   }
   return hip_status(spa::launch_select(pl, bt, dyn, G, static_cast<const uint16_t*>(q), budget_tokens, k_max,
-                                       sel_pages, sel_count, sel_len, sel_phys, sc, n_max, stream),
-                    "select_pages launch");
+                                       sel_pages, sel_count, sel_len, sel_phys, sc, n_max,
+                                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                                       stream),
+                    what);
+}
+
+}  // namespace
+
+spa_status spa_select_pages(const spa_pool* pool, const spa_heads* heads, const spa_batch* batch,
+                            const void* q, const int32_t* budget_tokens, int32_t k_max,
+                            int32_t* sel_pages, int32_t* sel_count, int32_t* sel_len, int32_t* sel_phys,
+                            float* scores, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return select_pages(pool, heads, batch, nullptr, nullptr, q, budget_tokens, k_max, sel_pages, sel_count, sel_len,
+                      sel_phys, scores, ws, ws_bytes, stream, "select_pages launch");
+}
+
+spa_status spa_append_select_pages(const spa_pool* pool, const spa_heads* heads, const spa_batch* batch,
+                                   const void* k_new, const void* v_new, const void* q,
+                                   const int32_t* budget_tokens, int32_t k_max, int32_t* sel_pages,
+                                   int32_t* sel_count, int32_t* sel_len, int32_t* sel_phys, float* scores,
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (batch && batch->batch > 0 && (!k_new || !v_new)) return fail(SPA_ERR_INVALID, "k_new / v_new is NULL");
+  return select_pages(pool, heads, batch, k_new, v_new, q, budget_tokens, k_max, sel_pages, sel_count, sel_len,
+                      sel_phys, scores, ws, ws_bytes, stream, "append_select_pages launch");
 }
 
 namespace {

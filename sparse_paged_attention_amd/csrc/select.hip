@@ -18,16 +18,11 @@
 // order by an exact bucket select on unique 64-bit keys
 //     key = order(score) << 32 | (0xFFFFFFFF - page id),
 // then writes the kept ids in ascending order.
-#include "spa_internal.h"
+#include "pool_rows.h"
 
 namespace spa {
 namespace {
 
-__device__ __forceinline__ int32_t clamp_len(const BatchArgs& bt, int32_t b, int32_t P) {
-  int32_t L = bt.lens[b];
-  int32_t cap = bt.max_pp * P;
-  return L < 0 ? 0 : (L > cap ? cap : L);
-}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -92,11 +87,51 @@ __device__ __forceinline__ void widen(const Raw<CPL>& r, double (&out)[CPL]) {
   }
 }
 
-template <int G>
+// The summary of the page receiving a token appended in the same launch, as
+// the append leaves it: the channel-wise min / max of the stored summary and
+// the new key, or the new key alone when it opens the page. Taking min / max
+// with the new key again changes nothing, so the stored record may be read
+// before or after the append wave rewrites it.
+template <int CPL>
+__device__ __forceinline__ void merge_new_key(Raw<CPL>& mn, Raw<CPL>& mx, const Raw<CPL>& kn, bool opens) {
+#pragma unroll
+  for (int w = 0; w < CPL / 2; ++w) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const uint16_t a = (uint16_t)(mn.w[w] >> (16 * half)), c = (uint16_t)(mx.w[w] >> (16 * half));
+      const uint16_t k = (uint16_t)(kn.w[w] >> (16 * half));
+      const uint32_t ka = order_key(a), kc = order_key(c), kk = order_key(k);
+      const uint16_t l = opens ? k : from_key(min(ka, kk));
+      const uint16_t u = opens ? k : from_key(max(kc, kk));
+      lo |= (uint32_t)l << (16 * half);
+      hi |= (uint32_t)u << (16 * half);
+    }
+    mn.w[w] = lo;
+    mx.w[w] = hi;
+  }
+}
+
+// FRESH: the step's token is appended in this launch (k_new / v_new given):
+// B * H_kv extra work-groups in rows past the heads' rows write it into the
+// pool and rebuild its page summary, and the waves scoring that page use the
+// summary with the new key merged in.
+template <int G, bool FRESH>
 __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, HeadList dyn,
                                                    const uint16_t* __restrict__ q,
-                                                   float* __restrict__ scores, int32_t n_max) {
+                                                   float* __restrict__ scores, int32_t n_max,
+                                                   const uint32_t* __restrict__ k_new,
+                                                   const uint16_t* __restrict__ v_new) {
   using S = ScoreShape<G>;
+  if (FRESH && (int32_t)blockIdx.y >= bt.B * dyn.n) {
+    const int32_t w = ((int32_t)blockIdx.y - bt.B * dyn.n) * (int32_t)gridDim.x + (int32_t)blockIdx.x;
+    if (w >= bt.B * pl.hkv) return;
+    const int32_t ab = w / pl.hkv, ah = w - ab * pl.hkv;
+    bool is_dyn = false;
+    for (int32_t d = 0; d < dyn.n; ++d) is_dyn |= dyn.id[d] == ah;
+    append_token(pl, bt, ab, ah, k_new, v_new, is_dyn);
+    return;
+  }
   static_assert(S::OFFS <= 192, "three page offsets per lane");
   __shared__ uint32_t offs[S::OFFS];
   const int32_t b = blockIdx.y / dyn.n, h = dyn.id[blockIdx.y % dyn.n];
@@ -138,6 +173,11 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
       qn[g][i] = qv[i] < 0.0 ? qv[i] : 0.0;
     }
   }
+  // the new key's channels of this lane, and where the token lands
+  Raw<S::CPL> kn;
+  const int32_t j_new = FRESH && L >= 1 ? (L - 1) / pl.p : -1;
+  const bool opens = FRESH && L >= 1 && (L - 1) % pl.p == 0;
+  if (FRESH) load_raw<S::CPL>(reinterpret_cast<const uint16_t*>(k_new) + ((int64_t)b * pl.hkv + h) * kHeadDim + c0, kn);
   __syncthreads();
 
   // summary location of page slot pp of pass it (page 0 of the pool if invalid)
@@ -161,7 +201,12 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
     }
   };
   float* out_row = scores + ((int64_t)b * pl.hkv + h) * n_max;
-  auto compute = [&](int it, const Pass& ps) {
+  auto compute = [&](int it, Pass& ps) {
+    if (FRESH && j_new >= base + it * S::PASS && j_new < base + (it + 1) * S::PASS) {
+#pragma unroll
+      for (int pp = 0; pp < S::NP; ++pp)
+        if (base + it * S::PASS + pp * S::GPW + group == j_new) merge_new_key<S::CPL>(ps.mn[pp], ps.mx[pp], kn, opens);
+    }
     double v[S::V];                                       // [page slot][query]
 #pragma unroll
     for (int pp = 0; pp < S::NP; ++pp) {
@@ -494,12 +539,19 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
 
 template <int G>
 hipError_t launch_score_g(const PoolArgs& pool, const BatchArgs& batch, const HeadList& dyn,
-                          const uint16_t* q, float* scores, int32_t n_max, hipStream_t s) {
+                          const uint16_t* q, float* scores, int32_t n_max, const uint16_t* k_new,
+                          const uint16_t* v_new, hipStream_t s) {
   using S = ScoreShape<G>;
   // ranges of RANGE pages; the last one also takes up to PASS more
   const int32_t ranges = std::max(1, (n_max - S::XPASS * S::PASS + S::RANGE - 1) / S::RANGE);
-  dim3 grid(ranges, batch.B * dyn.n);
-  hipLaunchKernelGGL(score_kernel<G>, grid, dim3(64), 0, s, pool, batch, dyn, q, scores, n_max);
+  if (k_new) {          // extra rows for the append waves
+    const int32_t rows = (batch.B * pool.hkv + ranges - 1) / ranges;
+    hipLaunchKernelGGL((score_kernel<G, true>), dim3(ranges, batch.B * dyn.n + rows), dim3(64), 0, s, pool, batch,
+                       dyn, q, scores, n_max, reinterpret_cast<const uint32_t*>(k_new), v_new);
+  } else {
+    hipLaunchKernelGGL((score_kernel<G, false>), dim3(ranges, batch.B * dyn.n), dim3(64), 0, s, pool, batch, dyn,
+                       q, scores, n_max, nullptr, nullptr);
+  }
   return hipGetLastError();
 }
 
@@ -508,15 +560,21 @@ hipError_t launch_score_g(const PoolArgs& pool, const BatchArgs& batch, const He
 hipError_t launch_select(const PoolArgs& pool, const BatchArgs& batch, const HeadList& dyn,
                          int32_t G, const uint16_t* q, const int32_t* budget, int32_t k_max,
                          int32_t* sel_pages, int32_t* sel_count, int32_t* sel_len, int32_t* sel_phys,
-                         float* scores, int32_t n_max, hipStream_t s) {
-  if (batch.B == 0 || dyn.n == 0) return hipSuccess;
+                         float* scores, int32_t n_max, const uint16_t* k_new, const uint16_t* v_new,
+                         hipStream_t s) {
+  if (batch.B == 0) return hipSuccess;
+  if (dyn.n == 0) return k_new ? launch_append(pool, batch, k_new, v_new, nullptr, s) : hipSuccess;
   hipError_t e;
+  if (k_new && G >= 8) {      // no room in those scoring kernels' registers: append first
+    if ((e = launch_append(pool, batch, k_new, v_new, &dyn, s)) != hipSuccess) return e;
+    k_new = v_new = nullptr;
+  }
   switch (G) {
-    case 1: e = launch_score_g<1>(pool, batch, dyn, q, scores, n_max, s); break;
-    case 2: e = launch_score_g<2>(pool, batch, dyn, q, scores, n_max, s); break;
-    case 4: e = launch_score_g<4>(pool, batch, dyn, q, scores, n_max, s); break;
-    case 8: e = launch_score_g<8>(pool, batch, dyn, q, scores, n_max, s); break;
-    case 16: e = launch_score_g<16>(pool, batch, dyn, q, scores, n_max, s); break;
+    case 1: e = launch_score_g<1>(pool, batch, dyn, q, scores, n_max, k_new, v_new, s); break;
+    case 2: e = launch_score_g<2>(pool, batch, dyn, q, scores, n_max, k_new, v_new, s); break;
+    case 4: e = launch_score_g<4>(pool, batch, dyn, q, scores, n_max, k_new, v_new, s); break;
+    case 8: e = launch_score_g<8>(pool, batch, dyn, q, scores, n_max, k_new, v_new, s); break;
+    case 16: e = launch_score_g<16>(pool, batch, dyn, q, scores, n_max, k_new, v_new, s); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;

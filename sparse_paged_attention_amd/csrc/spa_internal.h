@@ -67,7 +67,9 @@ hipError_t launch_summary(const PoolArgs& pool, const BatchArgs& batch, const He
 hipError_t launch_select(const PoolArgs& pool, const BatchArgs& batch, const HeadList& dyn,
                          int32_t G, const uint16_t* q, const int32_t* budget, int32_t k_max,
                          int32_t* sel_pages, int32_t* sel_count, int32_t* sel_len,
-                         int32_t* sel_phys, float* scores, int32_t n_max, hipStream_t s);
+                         int32_t* sel_phys, float* scores, int32_t n_max,
+                         const uint16_t* k_new, const uint16_t* v_new,   // NULL: no token appended
+                         hipStream_t s);
 hipError_t launch_attn(const PoolArgs& pool, const BatchArgs& batch, const AttnPlan& plan,
                        int32_t G, const uint16_t* q, const int32_t* sel_pages,
                        const int32_t* sel_count, const int32_t* sel_len,

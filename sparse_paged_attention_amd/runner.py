@@ -87,6 +87,12 @@ class DecodeLayer:
                            self.sel_len, self.k_max, self.out, self.lse, workspace=self.workspace,
                            sel_phys=self.sel_phys)
 
+    def append_select(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, scores=None) -> None:
+        """append + select, the append inside the selection's scoring launch."""
+        select_pages(self.pool, self.heads, self.batch, q, self.budget, self.k_max, self.sel_pages,
+                     self.sel_count, self.sel_len, scores=scores, workspace=self.workspace,
+                     sel_phys=self.sel_phys, k_new=k_new, v_new=v_new)
+
     def append_attend(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor) -> None:
         """append + attend in one launch (steps that reuse an earlier selection)."""
         sparse_decode_attn(self.pool, self.heads, self.batch, q, self.sel_pages, self.sel_count,
@@ -95,11 +101,10 @@ class DecodeLayer:
 
     def step(self, q, k_new, v_new, do_select: bool) -> None:
         """One decode step; seq_lens must already hold the lengths after the append.
-        A selecting step appends first (the selection reads the new summary); the
-        others append inside the attention launch."""
+        The append runs inside the selection's scoring launch on selecting steps and
+        inside the attention launch on the others."""
         if do_select:
-            self.append(k_new, v_new)
-            self.select(q)
+            self.append_select(q, k_new, v_new)
             self.attend(q)
         else:
             self.append_attend(q, k_new, v_new)

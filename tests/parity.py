@@ -43,7 +43,7 @@ class ParityRun:
     def __init__(self, wl: W.Workload, check_heads=None, threads: int = 16, strict_ties: bool = False,
                  resolve_at_selection: bool = True, fused: bool = False):
         self.wl = wl
-        self.fused = fused               # steps without selection append inside the attention launch
+        self.fused = fused               # the append runs inside the selection / attention launches
         self.strict_ties = strict_ties
         self.check = check_heads if check_heads is not None else \
             [(b, h) for b in range(wl.batch) for h in range(wl.hkv)]
@@ -92,6 +92,9 @@ class ParityRun:
         select = wl.selects_at(i)
         if self.fused and not select:
             layer.append_attend(qd, bits_to_bf16(kn), bits_to_bf16(vn))
+        elif self.fused:
+            layer.append_select(qd, bits_to_bf16(kn), bits_to_bf16(vn), scores=self.scores)
+            layer.attend(qd)
         else:
             layer.append(bits_to_bf16(kn), bits_to_bf16(vn))
             if select:

@@ -203,3 +203,20 @@ def test_append_decode_attn_validation(spa):
     assert call(mkbatch(spa, B=-1)) == 1
     assert call(mkbatch(spa, B=0, pt=None, lens=None), k_new=None, v_new=None) == 0
 
+
+def test_append_select_pages_validation(spa):
+    L = spa.lib()
+    pool, heads = mkpool(spa), mkheads(spa)
+
+    def call(batch, k_new=FAKE, v_new=FAKE, q=FAKE, k_max=8, ws_bytes=1 << 30):
+        return L.spa_append_select_pages(ctypes.byref(pool), ctypes.byref(heads), ctypes.byref(batch), k_new,
+                                         v_new, q, FAKE, k_max, FAKE, FAKE, FAKE, None, None, FAKE, ws_bytes,
+                                         None)
+    assert call(mkbatch(spa), k_new=None) == 1
+    assert call(mkbatch(spa), v_new=None) == 1
+    assert call(mkbatch(spa), q=None) == 1
+    assert call(mkbatch(spa), k_max=0) == 1
+    assert call(mkbatch(spa), ws_bytes=8) == 4
+    assert call(mkbatch(spa, mp=20000), ws_bytes=1 << 40) == 2
+    assert call(mkbatch(spa, B=0, pt=None, lens=None), k_new=None, v_new=None) == 0
+

@@ -134,16 +134,21 @@ def test_every_item_size(bpi):
 
 
 def test_append_inside_attention_pool_bit_exact():
-    """spa_append_decode_attn writes the same pool (keys, values, summaries)
-    as spa_kv_pool_append: three steps, new pages opened on the way."""
-    wl = W.WORKLOADS["toy_4k"].scaled(contexts=(300, 77, 1, 33), batch=4, steps=3, permute=True,
+    """spa_append_decode_attn and spa_append_select_pages write the same pool
+    (keys, values, summaries) as spa_kv_pool_append: four steps alternating
+    the two, new pages opened on the way."""
+    wl = W.WORKLOADS["toy_4k"].scaled(contexts=(300, 77, 1, 33), batch=4, steps=4, permute=True,
                                       kind=(1, 0), planted=None)
     pr = ParityRun(wl, check_heads=[])
     layer = pr.layer
+    layer.set_budget([256] * wl.batch)
     for i in range(wl.steps):
         q, kn, vn = pr.step_inputs(i)
         layer.set_lengths([wl.seq_len(b, i) for b in range(wl.batch)])
-        layer.append_attend(bits_to_bf16(q), bits_to_bf16(kn), bits_to_bf16(vn))
+        if i % 2 == 0:
+            layer.append_select(bits_to_bf16(q), bits_to_bf16(kn), bits_to_bf16(vn))
+        else:
+            layer.append_attend(bits_to_bf16(q), bits_to_bf16(kn), bits_to_bf16(vn))
     torch.cuda.synchronize()
     kp = layer.pool.k.view(torch.int16).cpu().numpy().view(np.uint16)
     vp = layer.pool.v.view(torch.int16).cpu().numpy().view(np.uint16)

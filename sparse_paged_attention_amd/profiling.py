@@ -7,7 +7,7 @@
         per-kernel average of every collected counter, summed over the
         counter's hardware instances for each dispatch;
     python -m sparse_paged_attention_amd.profiling traffic <fetch.db> <write.db> <kernels> <copy_bytes>
-        HBM bytes per launch of the comma-separated <kernels> (name parts, each
+        HBM bytes per launch of the |-separated <kernels> (name parts, each
         matching one kernel; together one call of the
         entry point that launches them, summed) from a FETCH_SIZE run and a
         WRITE_SIZE run, each scaled by what the same counter reads for the
@@ -68,7 +68,7 @@ def attn_source_hash() -> str:
     """Hash of the sources the attention kernels are built from; a stored
     traffic figure is only valid for the kernels it was measured on."""
     h = hashlib.sha256()
-    for f in ("attn.hip", "spa_internal.h"):
+    for f in ("attn.hip", "pool_rows.h", "spa_internal.h"):
         with open(os.path.join(_CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -86,7 +86,7 @@ def traffic(fetch_db: str, write_db: str, kernels: str, copy_bytes: float) -> di
     f_scale = copy_bytes / f_copy
     w_scale = copy_bytes / w_copy
     per = {}
-    for part in kernels.split(","):
+    for part in kernels.split("|"):
         match = [k for k in f if part in k]
         if len(match) != 1:
             raise SystemExit(f"'{part}' names {len(match)} kernels in the FETCH_SIZE run: {match}")

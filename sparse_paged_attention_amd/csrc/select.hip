@@ -39,8 +39,38 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // range's summary is computed once into LDS; summary loads run one pass ahead
 // of the arithmetic and are issued unconditionally (an invalid page reads
 // page 0 and is masked).
-template <int G>
+// Exchange with the partner lane of butterfly level M (M < 16: inside each
+// 16-lane row). DPP pairings stand in for lane ^ M: row_mirror (i <-> 15 - i)
+// for M = 8, row_half_mirror (i <-> 7 - i in each half row) for M = 4,
+// quad_perm for M = 2, 1. Each partner differs from the lane in bit M and in
+// no higher bit, which is all a reduce-scatter over the bits M, M/2, ... 1
+// needs: the halves kept and the lane that ends with each total are those of
+// lane ^ M. The moves need no LDS round trip (the score kernel runs one wave
+// per SIMD, so such latency is not hidden).
+template <int M>
+__device__ __forceinline__ uint32_t xchg32(uint32_t x) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M >= 16, "butterfly level");
+  if constexpr (M >= 16) {
+    return (uint32_t)__shfl_xor((int)x, M, 64);
+  } else {
+    constexpr int ctrl = M == 8 ? 0x140 : M == 4 ? 0x141 : M == 2 ? 0x4E : 0xB1;
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, ctrl, 0xF, 0xF, false);
+  }
+}
+template <int M>
+__device__ __forceinline__ double xchg(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint64_t lo = xchg32<M>((uint32_t)u), hi = xchg32<M>((uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, lo | (hi << 32));
+}
+template <int M>
+__device__ __forceinline__ float xchg(float x) {
+  return __uint_as_float(xchg32<M>(__float_as_uint(x)));
+}
+
+template <int G_>
 struct ScoreShape {
+  static constexpr int G = G_;
   static constexpr int LPP = G <= 4 ? 16 : 4 * G;   // lanes per page
   static constexpr int CPL = kHeadDim / LPP;        // channels per lane
   static constexpr int NP = 4;                      // pages per group per pass
@@ -109,6 +139,45 @@ __device__ __forceinline__ void merge_new_key(Raw<CPL>& mn, Raw<CPL>& mx, const 
     }
     mn.w[w] = lo;
     mx.w[w] = hi;
+  }
+}
+
+// The exchange used by the score reduction: DPP moves, except for groups of a
+// whole wave (G = 16), whose kernel has no register room for them.
+template <class S, int M, class T>
+__device__ __forceinline__ T exch(T x) {
+  if constexpr (S::LPP >= 64) return __shfl_xor(x, M, 64);
+  else return xchg<M>(x);
+}
+
+// One butterfly level M of the reduce-scatter of the V partial sums over the
+// LPP lanes of a group (levels M >= R halve the values kept; below R the R
+// lanes sharing a total add it up), then the next level.
+template <class S, int M>
+__device__ __forceinline__ void reduce_level(double (&v)[S::V], int sub) {
+  if constexpr (M >= 1) {
+    if constexpr (M >= S::R) {
+      const bool upper = (sub & M) != 0;
+      constexpr int half = M / S::R;
+#pragma unroll
+      for (int i = 0; i < half; ++i) {
+        const double send = upper ? v[i] : v[i + half];
+        const double keep = upper ? v[i + half] : v[i];
+        v[i] = keep + exch<S, M>(send);
+      }
+    } else {
+      v[0] += exch<S, M>(v[0]);
+    }
+    reduce_level<S, M / 2>(v, sub);
+  }
+}
+
+// Max over the G query totals of a page slot (lanes M * R apart).
+template <class S, int M>
+__device__ __forceinline__ void max_over_group(float& sc) {
+  if constexpr (M < S::G) {
+    sc = fmaxf(sc, exch<S, M * S::R>(sc));
+    max_over_group<S, M * 2>(sc);
   }
 }
 
@@ -226,26 +295,11 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
     }
     // reduce-scatter over the high lane bits of the group, then sum over the
     // R lanes that share a total
-#pragma unroll
-    for (int m = S::LPP / 2; m >= 1; m /= 2) {
-      if (m >= S::R) {
-        const bool upper = (sub & m) != 0;
-        const int half = m / S::R;
-#pragma unroll
-        for (int i = 0; i < half; ++i) {
-          const double send = upper ? v[i] : v[i + half];
-          const double keep = upper ? v[i + half] : v[i];
-          v[i] = keep + __shfl_xor(send, m, 64);
-        }
-      } else {
-        v[0] += __shfl_xor(v[0], m, 64);
-      }
-    }
+    reduce_level<S, S::LPP / 2>(v, sub);
     // lane `sub` now holds the total of index sub / R = page_slot * G + query
     float sc = (float)v[0];
     sc = sc == 0.0f ? 0.0f : sc;                          // one zero: +0
-#pragma unroll
-    for (int m = 1; m < G; m *= 2) sc = fmaxf(sc, __shfl_xor(sc, m * S::R, 64));
+    max_over_group<S, 1>(sc);
     const int pp = (sub / S::R) / G;
     bool ok = false;
 #pragma unroll

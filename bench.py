@@ -69,6 +69,15 @@ def algorithmic_bytes(wl, L: int, select: bool) -> dict:
                 total=attn + append + summary + sel)
 
 
+def bulk_write_bytes(wl, count: int) -> int:
+    """Bytes one prompt write of `count` tokens must move: read the caller's
+    K and V rows, write them into the pool, write the min/max summary of every
+    logical page of the dynamic heads, read the page-table row."""
+    n_dyn = sum(wl.kind)
+    rows = wl.hkv * count * wl.d * 2
+    return 2 * 2 * rows + n_dyn * (-(-count // wl.p)) * 2 * wl.d * 2 + (-(-count // wl.P)) * 4
+
+
 def cpu_baseline(wl, host_kv, replicas: int, sample_steps: int = 16) -> dict:
     """The CPU oracle on a bounded sample of the same job: the first
     `sample_steps` decode steps (selections and reuse as scheduled) of every
@@ -141,6 +150,7 @@ def main() -> int:
                           window=wl.window, page_table=pt, num_phys_pages=wl.num_phys_pages,
                           k_max=wl.k_max) for _ in range(R)]
     host_kv = []
+    write_events = []
     newk = np.zeros((wl.steps, wl.batch, wl.hkv, wl.d), np.uint16)
     newv = np.zeros_like(newk)
     for b in range(wl.batch):
@@ -149,8 +159,13 @@ def main() -> int:
         pre = wl.contexts[b] - 1
         Kd = torch.from_numpy(K[:, :pre].view(np.int16)).cuda().view(torch.bfloat16)
         Vd = torch.from_numpy(V[:, :pre].view(np.int16)).cuda().view(torch.bfloat16)
-        for layer in layers:
+        torch.cuda.synchronize()
+        for layer in layers:                    # prompt write + summaries of the dynamic heads, one pass
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
             layer.write_tokens(b, 0, Kd, Vd)
+            e1.record()
+            write_events.append((e0, e1, pre))
         del Kd, Vd
         newk[:, b] = K[:, pre:pre + wl.steps].transpose(1, 0, 2)
         newv[:, b] = V[:, pre:pre + wl.steps].transpose(1, 0, 2)
@@ -158,9 +173,11 @@ def main() -> int:
         log(f"[bench] sequence {b} written to {R} pools")
     for layer in layers:
         layer.set_lengths([c - 1 for c in wl.contexts])
-        layer.rebuild_summaries()
         layer.set_budget([wl.budget_at(c) for c in wl.contexts])
     torch.cuda.synchronize()
+    write_us = sorted(1e3 * e0.elapsed_time(e1) for e0, e1, _ in write_events)
+    write_med = write_us[len(write_us) // 2]
+    write_bytes = bulk_write_bytes(wl, write_events[0][2])
 
     def dev(a, dtype=torch.bfloat16):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(dtype)
@@ -290,6 +307,12 @@ def main() -> int:
                      "frac": round(attn_gbps / PEAK_GBPS, 4), "traffic": traffic,
                      "avg_launch_us": round(attn_avg_us, 2), "bytes_per_launch": int(attn_bytes_call)},
         "cpu_baseline": cpu,
+        "bulk_write": {"what": f"spa_kv_pool_write of one {write_events[0][2]}-token prompt (all {wl.hkv} KV heads, "
+                               f"summaries of the {sum(wl.kind)} dynamic heads in the same pass)",
+                       "median_us": round(write_med, 1), "bytes": int(write_bytes),
+                       "achieved": round(write_bytes / (write_med * 1e-6) / 1e9, 1), "unit": "GB/s",
+                       "frac": round(write_bytes / (write_med * 1e-6) / 1e9 / PEAK_GBPS, 4),
+                       "calls": len(write_us)},
     }
     print(json.dumps(res), flush=True)
     return 0

@@ -113,13 +113,24 @@ spa_status spa_kv_pool_append(const spa_pool* pool, const spa_heads* heads,
                               const spa_batch* batch, const void* k_new,
                               const void* v_new, hipStream_t stream);
 
-/* Bulk write of tokens [start, start + count) of ONE sequence (prefill).
+/* Bulk write of tokens [start, start + count) of ONE sequence (prefill, or a
+ * chunk of it).
+ *   heads: NULL, or the head kinds; when given, the same pass also builds the
+ *          summary of every logical page it writes into, for every dynamic
+ *          head, over the page's tokens below start + count (tokens of the
+ *          page before `start` are read from the pool): the same result as
+ *          spa_page_summary_update with first_pos = start and
+ *          L = start + count afterwards;
  *   page_table_row: device int32 [max_pages], that sequence's row;
  *   k, v: device bf16 [H_kv][count][D] in logical (position) order.
- * Requires 0 <= start, count >= 0, start + count <= max_pages * P. */
-spa_status spa_kv_pool_write(const spa_pool* pool, const int32_t* page_table_row,
-                             int32_t max_pages, int64_t start, int64_t count,
-                             const void* k, const void* v, hipStream_t stream);
+ * Tokens of the pool outside the range are left as they are.
+ * Requires 0 <= start, count >= 0, start + count <= max_pages * P.
+ * LServe write-up "2.1" (min-max pooling of the keys at prefill) and "2.2"
+ * (pages of the pool through the page table). */
+spa_status spa_kv_pool_write(const spa_pool* pool, const spa_heads* heads,
+                             const int32_t* page_table_row, int32_t max_pages,
+                             int64_t start, int64_t count, const void* k, const void* v,
+                             hipStream_t stream);
 
 /* ---- a2: page summaries ------------------------------------------------
  * For every dynamic KV head and every logical page j that overlaps positions

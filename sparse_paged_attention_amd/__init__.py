@@ -74,7 +74,7 @@ def lib() -> ctypes.CDLL:
         P, H, B = ctypes.POINTER(c_pool), ctypes.POINTER(c_heads), ctypes.POINTER(c_batch)
         sig = {
             "spa_kv_pool_append": ([P, H, B, vp, vp, vp], ctypes.c_int),
-            "spa_kv_pool_write": ([P, vp, i32, i64, i64, vp, vp, vp], ctypes.c_int),
+            "spa_kv_pool_write": ([P, H, vp, i32, i64, i64, vp, vp, vp], ctypes.c_int),
             "spa_page_summary_update": ([P, H, B, vp, i32, vp], ctypes.c_int),
             "spa_select_pages": ([P, H, B, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "spa_append_select_pages": ([P, H, B, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp],
@@ -233,14 +233,17 @@ def kv_pool_append(pool: Pool, batch: Batch, k_new, v_new, heads: "Heads | None"
                                     ctypes.byref(b), _ptr(k_new), _ptr(v_new), _stream(stream)))
 
 
-def kv_pool_write(pool: Pool, page_table_row, start: int, k, v, stream=None) -> None:
-    """spa_kv_pool_write: k, v bf16 [H_kv][count][D] for positions [start, start+count)."""
+def kv_pool_write(pool: Pool, page_table_row, start: int, k, v, heads=None, stream=None) -> None:
+    """spa_kv_pool_write: k, v bf16 [H_kv][count][D] for positions [start, start+count);
+    with `heads`, the dynamic heads' summaries of the written pages are built in the same pass."""
     p = pool.c()
+    h = _heads_for(heads, pool) if heads is not None else None
     _need(page_table_row, (None,), "i32", "page_table_row")
     _need(k, (pool.num_kv_heads, None, HEAD_DIM), "bf16", "k")
     count = k.shape[1]
     _need(v, (pool.num_kv_heads, count, HEAD_DIM), "bf16", "v")
-    _check(lib().spa_kv_pool_write(ctypes.byref(p), _ptr(page_table_row), page_table_row.shape[0],
+    _check(lib().spa_kv_pool_write(ctypes.byref(p), ctypes.byref(h) if h is not None else None,
+                                   _ptr(page_table_row), page_table_row.shape[0],
                                    start, count, _ptr(k), _ptr(v), _stream(stream)))
 
 

@@ -273,12 +273,15 @@ spa_status spa_kv_pool_append(const spa_pool* pool, const spa_heads* heads, cons
                     "kv_pool_append launch");
 }
 
-spa_status spa_kv_pool_write(const spa_pool* pool, const int32_t* page_table_row, int32_t max_pages,
-                             int64_t start, int64_t count, const void* k, const void* v,
+spa_status spa_kv_pool_write(const spa_pool* pool, const spa_heads* heads, const int32_t* page_table_row,
+                             int32_t max_pages, int64_t start, int64_t count, const void* k, const void* v,
                              hipStream_t stream) {
   spa::PoolArgs pl;
+  spa::HeadList dyn;
+  int32_t G;
   spa_status s;
   if ((s = check_pool(pool, &pl)) != SPA_OK) return s;
+  if (heads && (s = check_heads(heads, pl, &G, &dyn, nullptr)) != SPA_OK) return s;
   if (max_pages < 1) return fail(SPA_ERR_INVALID, "max_pages %d < 1", max_pages);
   if (start < 0 || count < 0) return fail(SPA_ERR_INVALID, "start %lld / count %lld negative",
                                           (long long)start, (long long)count);
@@ -286,11 +289,9 @@ spa_status spa_kv_pool_write(const spa_pool* pool, const int32_t* page_table_row
     return fail(SPA_ERR_INVALID, "tokens [%lld, %lld) exceed max_pages * physical_page = %lld",
                 (long long)start, (long long)(start + count), (long long)max_pages * pl.P);
   if (count == 0) return ok();
-  if (count > (int64_t)UINT32_MAX * 4) return fail(SPA_ERR_INVALID, "count too large");
   if (!page_table_row || !k || !v) return fail(SPA_ERR_INVALID, "page_table_row / k / v is NULL");
-  return hip_status(spa::launch_write(pl, page_table_row, max_pages, start, count,
-                                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                                      stream),
+  return hip_status(spa::launch_write(pl, page_table_row, start, count, static_cast<const uint16_t*>(k),
+                                      static_cast<const uint16_t*>(v), heads ? &dyn : nullptr, stream),
                     "kv_pool_write launch");
 }
 

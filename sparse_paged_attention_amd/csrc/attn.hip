@@ -309,7 +309,6 @@ __device__ __forceinline__ void run_blocks(const PoolArgs& pl, const int32_t* pt
   constexpr int SB = PG / kBlockTokens;           // blocks per logical page
   constexpr int NB = (BPI + 1) & ~1;              // pipeline slots: BPI rounded up to pairs
   const int32_t r = pl.P / PG;
-  const int32_t L = src.L;
   const auto pt = as_scalar(pt_row);
   Block blk[NB];
   int32_t ptv[NB];

@@ -27,31 +27,93 @@ __global__ void __launch_bounds__(64) append_kernel(PoolArgs pl, BatchArgs bt,
   append_token(pl, bt, b, h, k_new, v_new, with_summary && is_dyn);
 }
 
-// Bulk write of one sequence: grid (ceil(count / 4), hkv), 256 threads =
-// 4 tokens x 64 lanes of 2 channels.
-__global__ void __launch_bounds__(256) write_kernel(PoolArgs pl, const int32_t* __restrict__ pt,
-                                                    int32_t max_pp, int64_t start, int64_t count,
-                                                    const uint32_t* __restrict__ k,
-                                                    const uint16_t* __restrict__ v) {
+// Bulk write of tokens [start, start + count) of one sequence (prefill), one
+// wave per (logical page, KV head). Lane l owns channels 2l and 2l + 1 of each
+// of the page's PG tokens, so every load instruction reads one whole 256-byte
+// row of the caller's [H_kv][count][D] arrays. Keys are stored row by row;
+// values channel-major, each channel's PG tokens as one contiguous run built
+// in registers. For dynamic heads (bit h of `dyn`) the lane's minimum and
+// maximum over the page are its part of the page summary, written in the same
+// pass: the summary covers the page's tokens below start + count, those
+// before `start` (a page only partly inside the range) read from the pool.
+struct DynMask {
+  uint32_t w[kMaxKvHeads / 32];
+};
+
+template <int PG>
+__global__ void __launch_bounds__(64) write_kernel(PoolArgs pl, const int32_t* __restrict__ pt, int64_t start,
+                                                   int64_t count, const uint32_t* __restrict__ k,
+                                                   const uint32_t* __restrict__ v, DynMask dyn) {
   const int32_t h = blockIdx.y;
-  const int64_t n = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
-  if (n >= count) return;
-  const int64_t t = start + n;
-  const int32_t phys = pt[t / pl.P];
+  const int64_t j = start / PG + blockIdx.x;       // logical page
+  const int64_t t0 = j * PG, end = start + count;
+  const int64_t lo = t0 > start ? t0 : start, hi = t0 + PG < end ? t0 + PG : end;
+  if (lo >= hi) return;
+  const int32_t phys = pt[j / pl.r];
   if (phys < 0 || phys >= pl.N) return;
-  const int32_t slot = (int32_t)(t % pl.P), lp = slot / pl.p, i = slot % pl.p;
-  const int lane = threadIdx.x % 64;
-  const int64_t src = ((int64_t)h * count + n) * kHeadDim;
-  reinterpret_cast<uint32_t*>(pl.k + k_row(pl, phys, h, slot) * kHeadDim)[lane] = k[src / 2 + lane];
-  uint16_t* vp = pl.v + v_page(pl, phys, h, lp);
-  vp[(2 * lane) * pl.p + i] = v[src + 2 * lane];
-  vp[(2 * lane + 1) * pl.p + i] = v[src + 2 * lane + 1];
+  const int32_t lp = (int32_t)(j % pl.r);
+  const int lane = threadIdx.x;
+  uint32_t kw[PG], vw[PG];
+#pragma unroll
+  for (int u = 0; u < PG; ++u) {                   // rows outside the range re-read row lo
+    const int64_t t = t0 + u;
+    const int64_t row = (int64_t)h * count + ((t >= lo && t < hi) ? t : lo) - start;
+    kw[u] = k[row * 64 + lane];
+    vw[u] = v[row * 64 + lane];
+  }
+  uint32_t* kd = reinterpret_cast<uint32_t*>(pl.k + k_row(pl, phys, h, lp * PG) * kHeadDim) + lane;
+  uint16_t* vd = pl.v + v_page(pl, phys, h, lp);   // [D][PG]
+  if (lo == t0 && hi == t0 + PG) {
+#pragma unroll
+    for (int u = 0; u < PG; ++u) kd[u * 64] = kw[u];
+    uint32_t a[PG / 2], c[PG / 2];                   // channel 2l / 2l + 1, tokens 2i and 2i + 1
+#pragma unroll
+    for (int i = 0; i < PG / 2; ++i) {
+      a[i] = (vw[2 * i] & 0xFFFFu) | (vw[2 * i + 1] << 16);
+      c[i] = (vw[2 * i] >> 16) | (vw[2 * i + 1] & 0xFFFF0000u);
+    }
+    uint4* d0 = reinterpret_cast<uint4*>(vd + (2 * lane) * PG);
+    uint4* d1 = reinterpret_cast<uint4*>(vd + (2 * lane + 1) * PG);
+#pragma unroll
+    for (int i = 0; i < PG / 8; ++i) {
+      d0[i] = uint4{a[4 * i], a[4 * i + 1], a[4 * i + 2], a[4 * i + 3]};
+      d1[i] = uint4{c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]};
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < PG; ++u) {
+      const int64_t t = t0 + u;
+      if (t >= lo && t < hi) {
+        kd[u * 64] = kw[u];
+        vd[(2 * lane) * PG + u] = (uint16_t)vw[u];
+        vd[(2 * lane + 1) * PG + u] = (uint16_t)(vw[u] >> 16);
+      }
+    }
+  }
+  if (!((dyn.w[h >> 5] >> (h & 31)) & 1u)) return;
+  uint32_t lo0 = 0xFFFFFFFFu, hi0 = 0u, lo1 = 0xFFFFFFFFu, hi1 = 0u;
+#pragma unroll
+  for (int u = 0; u < PG; ++u) {
+    const int64_t t = t0 + u;
+    if (t < hi) {                                   // tokens before `start` are already in the pool
+      const uint32_t w = t >= lo ? kw[u] : kd[u * 64];
+      const uint32_t x = order_key((uint16_t)w), y = order_key((uint16_t)(w >> 16));
+      lo0 = min(lo0, x); hi0 = max(hi0, x);
+      lo1 = min(lo1, y); hi1 = max(hi1, y);
+    }
+  }
+  uint32_t* sp = reinterpret_cast<uint32_t*>(pl.summ + summ_page(pl, phys, h, lp));
+  sp[lane] = (uint32_t)from_key(lo0) | ((uint32_t)from_key(lo1) << 16);
+  sp[kHeadDim / 2 + lane] = (uint32_t)from_key(hi0) | ((uint32_t)from_key(hi1) << 16);
 }
 
-// grid (pages in range, B * dyn.n), 128 threads = one channel each.
-__global__ void __launch_bounds__(128) summary_kernel(PoolArgs pl, BatchArgs bt, HeadList dyn,
-                                                      const int32_t* __restrict__ first_pos,
-                                                      int32_t max_tokens) {
+// Summaries rebuilt from the pool: grid (pages in range, B * dyn.n), one wave
+// per (logical page, dynamic head); lane l takes channels 2l and 2l + 1 of the
+// page's valid tokens, each load instruction one 256-byte key row.
+template <int PG>
+__global__ void __launch_bounds__(64) summary_kernel(PoolArgs pl, BatchArgs bt, HeadList dyn,
+                                                     const int32_t* __restrict__ first_pos,
+                                                     int32_t max_tokens) {
   const int32_t b = blockIdx.y / dyn.n, h = dyn.id[blockIdx.y % dyn.n];
   const int32_t L = clamp_len(bt, b, pl.P);
   if (L < 1) return;
@@ -59,23 +121,27 @@ __global__ void __launch_bounds__(128) summary_kernel(PoolArgs pl, BatchArgs bt,
   if (f < 0) f = 0;
   if (f < L - max_tokens) f = L - max_tokens;      // pages beyond the bound are not refreshed
   if (f >= L) return;
-  const int32_t j = f / pl.p + blockIdx.x;          // logical page to rebuild
-  if ((int64_t)j * pl.p >= L) return;
+  const int32_t j = f / PG + blockIdx.x;            // logical page to rebuild
+  if ((int64_t)j * PG >= L) return;
   const int32_t phys = bt.pt[(int64_t)b * bt.max_pp + j / pl.r];
   if (phys < 0 || phys >= pl.N) return;
   const int32_t lp = j % pl.r;
-  const int32_t t0 = j * pl.p, t1 = min(t0 + pl.p, L);
-  const int c = threadIdx.x;
-  const uint16_t* kr = pl.k + k_row(pl, phys, h, lp * pl.p) * kHeadDim + c;
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-  for (int32_t t = 0; t < t1 - t0; ++t) {
-    const uint32_t key = order_key(kr[(int64_t)t * kHeadDim]);
-    lo = min(lo, key);
-    hi = max(hi, key);
+  const int32_t n = min(PG, L - j * PG);            // valid tokens of the page
+  const int lane = threadIdx.x;
+  const uint32_t* kr = reinterpret_cast<const uint32_t*>(pl.k + k_row(pl, phys, h, lp * PG) * kHeadDim) + lane;
+  uint32_t w[PG];
+#pragma unroll
+  for (int u = 0; u < PG; ++u) w[u] = kr[min(u, n - 1) * 64];   // rows past the valid ones repeat the last
+  uint32_t lo0 = 0xFFFFFFFFu, hi0 = 0u, lo1 = 0xFFFFFFFFu, hi1 = 0u;
+#pragma unroll
+  for (int u = 0; u < PG; ++u) {
+    const uint32_t x = order_key((uint16_t)w[u]), y = order_key((uint16_t)(w[u] >> 16));
+    lo0 = min(lo0, x); hi0 = max(hi0, x);
+    lo1 = min(lo1, y); hi1 = max(hi1, y);
   }
-  uint16_t* s = pl.summ + summ_page(pl, phys, h, lp);
-  s[c] = from_key(lo);
-  s[kHeadDim + c] = from_key(hi);
+  uint32_t* sp = reinterpret_cast<uint32_t*>(pl.summ + summ_page(pl, phys, h, lp));
+  sp[lane] = (uint32_t)from_key(lo0) | ((uint32_t)from_key(lo1) << 16);
+  sp[kHeadDim / 2 + lane] = (uint32_t)from_key(hi0) | ((uint32_t)from_key(hi1) << 16);
 }
 
 }  // namespace
@@ -91,12 +157,22 @@ hipError_t launch_append(const PoolArgs& pool, const BatchArgs& batch, const uin
   return hipGetLastError();
 }
 
-hipError_t launch_write(const PoolArgs& pool, const int32_t* pt_row, int32_t max_pp, int64_t start,
-                        int64_t count, const uint16_t* k, const uint16_t* v, hipStream_t s) {
+hipError_t launch_write(const PoolArgs& pool, const int32_t* pt_row, int64_t start, int64_t count,
+                        const uint16_t* k, const uint16_t* v, const HeadList* dyn, hipStream_t s) {
   if (count == 0) return hipSuccess;
-  dim3 grid((unsigned)((count + 3) / 4), pool.hkv);
-  hipLaunchKernelGGL(write_kernel, grid, dim3(256), 0, s, pool, pt_row, max_pp, start, count,
-                     reinterpret_cast<const uint32_t*>(k), v);
+  DynMask m = {};
+  if (dyn)
+    for (int32_t d = 0; d < dyn->n; ++d) m.w[dyn->id[d] >> 5] |= 1u << (dyn->id[d] & 31);
+  const int64_t pages = (start + count - 1) / pool.p - start / pool.p + 1;
+  const dim3 grid((unsigned)pages, pool.hkv);
+  const uint32_t* k32 = reinterpret_cast<const uint32_t*>(k);
+  const uint32_t* v32 = reinterpret_cast<const uint32_t*>(v);
+  switch (pool.p) {
+    case 16: hipLaunchKernelGGL(write_kernel<16>, grid, dim3(64), 0, s, pool, pt_row, start, count, k32, v32, m); break;
+    case 32: hipLaunchKernelGGL(write_kernel<32>, grid, dim3(64), 0, s, pool, pt_row, start, count, k32, v32, m); break;
+    case 64: hipLaunchKernelGGL(write_kernel<64>, grid, dim3(64), 0, s, pool, pt_row, start, count, k32, v32, m); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -105,8 +181,13 @@ hipError_t launch_summary(const PoolArgs& pool, const BatchArgs& batch, const He
   if (batch.B == 0 || dyn.n == 0 || max_tokens < 1) return hipSuccess;
   // pages overlapping a range of max_tokens positions
   const int32_t pages = (max_tokens + pool.p - 1) / pool.p + 1;
-  dim3 grid(pages, batch.B * dyn.n);
-  hipLaunchKernelGGL(summary_kernel, grid, dim3(128), 0, s, pool, batch, dyn, first_pos, max_tokens);
+  const dim3 grid(pages, batch.B * dyn.n);
+  switch (pool.p) {
+    case 16: hipLaunchKernelGGL(summary_kernel<16>, grid, dim3(64), 0, s, pool, batch, dyn, first_pos, max_tokens); break;
+    case 32: hipLaunchKernelGGL(summary_kernel<32>, grid, dim3(64), 0, s, pool, batch, dyn, first_pos, max_tokens); break;
+    case 64: hipLaunchKernelGGL(summary_kernel<64>, grid, dim3(64), 0, s, pool, batch, dyn, first_pos, max_tokens); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

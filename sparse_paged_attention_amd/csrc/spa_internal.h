@@ -59,9 +59,10 @@ struct AttnPlan {
 hipError_t launch_append(const PoolArgs& pool, const BatchArgs& batch,
                          const uint16_t* k_new, const uint16_t* v_new,
                          const HeadList* dyn, hipStream_t s);
-hipError_t launch_write(const PoolArgs& pool, const int32_t* pt_row, int32_t max_pp,
-                        int64_t start, int64_t count, const uint16_t* k,
-                        const uint16_t* v, hipStream_t s);
+hipError_t launch_write(const PoolArgs& pool, const int32_t* pt_row, int64_t start,
+                        int64_t count, const uint16_t* k, const uint16_t* v,
+                        const HeadList* dyn,                  // NULL or dynamic heads: summaries too
+                        hipStream_t s);
 hipError_t launch_summary(const PoolArgs& pool, const BatchArgs& batch, const HeadList& dyn,
                           const int32_t* first_pos, int32_t max_tokens, hipStream_t s);
 hipError_t launch_select(const PoolArgs& pool, const BatchArgs& batch, const HeadList& dyn,

@@ -50,9 +50,11 @@ class DecodeLayer:
         self.lse = torch.empty((self.B, hq), dtype=torch.float32, device=device)
 
     # ----------------------------------------------------------- set-up
-    def write_tokens(self, b: int, start: int, K: torch.Tensor, V: torch.Tensor) -> None:
-        """Positions [start, start + K.shape[1]) of sequence b; K, V bf16 [H_kv][n][D] on device."""
-        kv_pool_write(self.pool, self.page_table[b], start, K.contiguous(), V.contiguous())
+    def write_tokens(self, b: int, start: int, K: torch.Tensor, V: torch.Tensor, summaries: bool = True) -> None:
+        """Positions [start, start + K.shape[1]) of sequence b; K, V bf16 [H_kv][n][D] on device.
+        With `summaries`, the dynamic heads' page summaries are built in the same pass."""
+        kv_pool_write(self.pool, self.page_table[b], start, K.contiguous(), V.contiguous(),
+                      heads=self.heads if summaries else None)
 
     def set_lengths(self, lens) -> None:
         self.lens_host = np.asarray(lens, np.int32).copy()

@@ -168,10 +168,12 @@ def test_select_and_summary_validation(spa):
     bad_heads = mkheads(spa, kind=(0, 0, 0, 0, 1, 1, 1, 3))
     assert L.spa_kv_pool_append(ctypes.byref(pool), ctypes.byref(bad_heads), ctypes.byref(batch), FAKE,
                                 FAKE, None) == 1
-    assert L.spa_kv_pool_write(ctypes.byref(pool), FAKE, 4, 250, 10, FAKE, FAKE, None) == 1
-    assert L.spa_kv_pool_write(ctypes.byref(pool), FAKE, 4, -1, 1, FAKE, FAKE, None) == 1
-    assert L.spa_kv_pool_write(ctypes.byref(pool), None, 4, 0, 1, FAKE, FAKE, None) == 1
-    assert L.spa_kv_pool_write(ctypes.byref(pool), FAKE, 4, 0, 0, FAKE, FAKE, None) == 0
+    assert L.spa_kv_pool_write(ctypes.byref(pool), None, FAKE, 4, 250, 10, FAKE, FAKE, None) == 1
+    assert L.spa_kv_pool_write(ctypes.byref(pool), None, FAKE, 4, -1, 1, FAKE, FAKE, None) == 1
+    assert L.spa_kv_pool_write(ctypes.byref(pool), None, None, 4, 0, 1, FAKE, FAKE, None) == 1
+    assert L.spa_kv_pool_write(ctypes.byref(pool), None, FAKE, 4, 0, 0, FAKE, FAKE, None) == 0
+    assert L.spa_kv_pool_write(ctypes.byref(pool), ctypes.byref(bad_heads), FAKE, 4, 0, 1, FAKE, FAKE, None) == 1
+    assert L.spa_kv_pool_write(ctypes.byref(pool), ctypes.byref(heads), FAKE, 4, 0, 0, FAKE, FAKE, None) == 0
 
 
 def test_attn_blocks_per_item_setting(spa):

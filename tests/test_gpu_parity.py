@@ -62,6 +62,60 @@ def test_pool_write_append_and_summaries_bit_exact():
             np.testing.assert_array_equal(sp[pt[b, j // r], h, j % r, 1], kmax)
 
 
+@pytest.mark.parametrize("p,P", [(16, 64), (32, 256), (64, 128)])
+def test_bulk_write_in_chunks_builds_summaries(p, P):
+    """spa_kv_pool_write with the head kinds, in chunks whose edges fall inside
+    logical pages: the pool holds every token where the page table puts it,
+    each dynamic head's summaries equal the oracle's min/max pooling of its
+    keys (LServe write-up "2.1"), bit for bit, streaming heads' summaries are
+    not touched, and rebuilding the summaries from the pool changes nothing."""
+    from sparse_paged_attention_amd.runner import DecodeLayer
+    wl = W.WORKLOADS["toy_4k"].scaled(contexts=(300, 77, 1, 2 * P + 3), batch=4, steps=1, permute=True,
+                                      p=p, P=P, hkv=4, hq=8, kind=(1, 0, 1, 0), planted=None, name="bulk_write")
+    log(f"[parity] bulk write p={p} P={P} contexts={wl.contexts}")
+    pt = W.page_table(wl)
+    layer = DecodeLayer(hq=wl.hq, hkv=wl.hkv, p=p, P=P, kind=wl.kind, sink=wl.sink, window=wl.window,
+                        page_table=pt, num_phys_pages=wl.num_phys_pages, k_max=wl.k_max)
+    layer.pool.summary.view(torch.int16).fill_(0x7F7F)           # a pattern no write produces here
+    src = []
+    for b in range(wl.batch):
+        L = wl.contexts[b]
+        K = np.stack([W.kv(wl, b, h, "k")[:L] for h in range(wl.hkv)])
+        V = np.stack([W.kv(wl, b, h, "v")[:L] for h in range(wl.hkv)])
+        src.append((K, V))
+        edges = sorted({0, L, *[e for e in (37, 38, 38 + p, 2 * P + 1) if e < L]})
+        for a, e in zip(edges[:-1], edges[1:]):
+            layer.write_tokens(b, a, bits_to_bf16(np.ascontiguousarray(K[:, a:e])).cuda(),
+                               bits_to_bf16(np.ascontiguousarray(V[:, a:e])).cuda())
+    layer.set_lengths(list(wl.contexts))
+    torch.cuda.synchronize()
+
+    def host(t):
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    kp, vp, sp = host(layer.pool.k), host(layer.pool.v), host(layer.pool.summary)
+    r = P // p
+    for b in range(wl.batch):
+        K, V = src[b]
+        L = wl.contexts[b]
+        t = np.arange(L)
+        phys, slot = pt[b, t // P], t % P
+        j = np.arange(-(-L // p))
+        for h in range(wl.hkv):
+            np.testing.assert_array_equal(kp[phys, h, slot], K[h])
+            np.testing.assert_array_equal(vp[phys, h, slot // p, :, slot % p], V[h])
+            got = sp[pt[b, j // r], h, j % r]
+            if wl.kind[h]:
+                kmin, kmax = oracle.page_summary(K[h], p)
+                np.testing.assert_array_equal(got[:, 0], kmin)
+                np.testing.assert_array_equal(got[:, 1], kmax)
+            else:
+                assert (got == 0x7F7F).all()
+    layer.rebuild_summaries()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(layer.pool.summary), sp)
+
+
 # ------------------------------------------------------ the five workloads
 
 def test_toy_4k():

@@ -37,6 +37,8 @@ METRIC = "sparse decode-attn µs/step + achieved HBM GB/s (% peak) at 128K ctx"
 PEAK_GBPS = 8000.0
 COPY_BYTES = 1 << 30          # calibration copy for the HBM byte counters
 WORKLOAD = "llama3_128k"
+ATTN_KERNELS = "attn_kernel<16, 5, 4, false>|combine_kernel"    # one spa_sparse_decode_attn call
+WRITE_KERNELS = "write_kernel<16>"                               # one spa_kv_pool_write call
 
 
 def log(*a):
@@ -133,7 +135,7 @@ def main() -> int:
     import workloads as W
     import sparse_paged_attention_amd as spa
     from sparse_paged_attention_amd.runner import DecodeLayer
-    from sparse_paged_attention_amd.profiling import attn_source_hash
+    from sparse_paged_attention_amd.profiling import source_hash
 
     spa.lib()
     torch.cuda.set_device(0)
@@ -271,14 +273,17 @@ def main() -> int:
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, host_kv, R)
 
-    traffic = None
-    tpath = os.path.join(ROOT, "profiles", "attn_llama3_128k_traffic.json")
-    if os.path.exists(tpath):
-        try:
-            tr = json.load(open(tpath))
-            traffic = tr.get("bytes_per_launch") if tr.get("kernel_source_hash") == attn_source_hash() else None
-        except Exception:
-            traffic = None
+    def stored_traffic(name: str, kernels: str):
+        """HBM bytes per launch from a committed counter summary, if it was
+        taken on the kernels as they are now built."""
+        tpath = os.path.join(ROOT, "profiles", name)
+        if not os.path.exists(tpath):
+            return None
+        tr = json.load(open(tpath))
+        return tr.get("bytes_per_launch") if tr.get("kernel_source_hash") == source_hash(kernels) else None
+
+    traffic = stored_traffic("attn_llama3_128k_traffic.json", ATTN_KERNELS)
+    write_traffic = stored_traffic("bulk_write_llama3_128k_traffic.json", WRITE_KERNELS)
 
     res = {
         "metric": METRIC,
@@ -312,7 +317,7 @@ def main() -> int:
                        "median_us": round(write_med, 1), "bytes": int(write_bytes),
                        "achieved": round(write_bytes / (write_med * 1e-6) / 1e9, 1), "unit": "GB/s",
                        "frac": round(write_bytes / (write_med * 1e-6) / 1e9 / PEAK_GBPS, 4),
-                       "calls": len(write_us)},
+                       "traffic": write_traffic, "calls": len(write_us)},
     }
     print(json.dumps(res), flush=True)
     return 0

@@ -12,8 +12,8 @@
         entry point that launches them, summed) from a FETCH_SIZE run and a
         WRITE_SIZE run, each scaled by what the same counter reads for the
         plain copy kernel of <copy_bytes> bytes (the largest copy dispatch) in
-        that run; the JSON carries the hash of the attention sources it was
-        taken on.
+        that run; the JSON carries the hash of the sources of those kernels
+        it was taken on.
 
 rocprofv3 writes SQLite databases; only the standard `kernels` and
 `pmc_events` views are read.
@@ -64,11 +64,27 @@ def pmc_per_dispatch(db_path: str) -> dict:
     return out
 
 
-def attn_source_hash() -> str:
-    """Hash of the sources the attention kernels are built from; a stored
+# Sources each kernel is built from (name part -> files).
+_KERNEL_SOURCES = (
+    (("attn_kernel", "combine_kernel"), ("attn.hip", "pool_rows.h", "spa_internal.h")),
+    (("write_kernel", "summary_kernel", "append_kernel"), ("pool.hip", "pool_rows.h", "spa_internal.h")),
+    (("score_kernel", "topk_kernel"), ("select.hip", "pool_rows.h", "spa_internal.h")),
+)
+
+
+def source_hash(kernels: str) -> str:
+    """Hash of the sources the |-separated kernels are built from; a stored
     traffic figure is only valid for the kernels it was measured on."""
+    files = []
+    for part in kernels.split("|"):
+        for names, srcs in _KERNEL_SOURCES:
+            if any(n in part for n in names):
+                files.extend(f for f in srcs if f not in files)
+                break
+        else:
+            raise ValueError(f"no sources known for kernel '{part}'")
     h = hashlib.sha256()
-    for f in ("attn.hip", "pool_rows.h", "spa_internal.h"):
+    for f in sorted(files):
         with open(os.path.join(_CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -98,7 +114,7 @@ def traffic(fetch_db: str, write_db: str, kernels: str, copy_bytes: float) -> di
     write = sum(v["write_bytes"] for v in per.values())
     return dict(kernels=per, fetch_bytes_per_launch=fetch, write_bytes_per_launch=write,
                 bytes_per_launch=fetch + write, fetch_scale=f_scale, write_scale=w_scale,
-                copy_kernel=ck, copy_bytes=copy_bytes, kernel_source_hash=attn_source_hash())
+                copy_kernel=ck, copy_bytes=copy_bytes, kernel_source_hash=source_hash(kernels))
 
 
 def _print_stats(db: str) -> None:

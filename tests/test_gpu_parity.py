@@ -176,6 +176,16 @@ def test_llama3_128k_full_size_sampled(fused):
     run(wl, check=[(0, 0), (0, 4), (1, 5), (2, 3), (3, 7)], fused=fused)
 
 
+def test_ragged_mha_full_size_sampled():
+    """The ragged continuous batch at full size: 16 sequences of 24842 ..
+    127144 tokens, 32 KV heads (MHA) over one shuffled 20.5 GB pool, 16 steps
+    with selection every 4, the benchmark's launches; checked on sampled
+    heads of the shortest and the longest sequences and others, streaming
+    (0-15) and dynamic (16-31)."""
+    wl = W.WORKLOADS["ragged_mha"]
+    run(wl, check=[(6, 0), (6, 31), (0, 15), (0, 16), (9, 3), (13, 24), (15, 30)], fused=True)
+
+
 @pytest.mark.parametrize("bpi", [4, 5, 6, 7, 8, 9, 10, 12, 16])
 def test_every_item_size(bpi):
     """Each attention work-item size (odd sizes pad the last block pair):

@@ -562,13 +562,14 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
   }
 }
 
-// Merge of the item partials of one (sequence, KV head, query head): the
-// running-max / running-sum rule of online softmax applied across items.
-// Thread (slice, c4) folds channels 4*c4 .. +3 over the items slice,
-// slice + kCombineSlices, ...; the loads of a chunk of items are all issued
-// before any is used. The slices are then folded through LDS.
+// Merge of the item partials of one query head: the running-max /
+// running-sum rule of online softmax applied across items (long-context
+// survey "2.1"; Novita article "2."). One wave per (sequence, query head,
+// quarter of the channels): lane (slice, c4) folds channels
+// 32*quarter + 4*c4 .. +3 over items slice, slice + 8, ..., all of a chunk's
+// loads issued before any is used; the eight slices are then folded across
+// lanes.
 constexpr int kCombineSlices = 8;
-constexpr int kCombineThreads = kCombineSlices * (kHeadDim / 4);
 constexpr int kCombineChunk = 8;
 
 __device__ __forceinline__ void fold_partial(float m_i, float l_i, const f32x4& o_i, float& M, float& l,
@@ -581,57 +582,52 @@ __device__ __forceinline__ void fold_partial(float m_i, float l_i, const f32x4& 
   M = Mn;
 }
 
-__global__ void __launch_bounds__(kCombineThreads) combine_kernel(int32_t hkv, AttnPlan plan, int32_t G,
-                                                                  const float* __restrict__ part_o,
-                                                                  const float* __restrict__ part_ml,
-                                                                  float* __restrict__ out,
-                                                                  float* __restrict__ lse) {
-  __shared__ f32x4 so[kCombineThreads];
-  __shared__ float sM[kCombineThreads], sl[kCombineThreads];
+__global__ void __launch_bounds__(64) combine_kernel(int32_t hkv, AttnPlan plan, int32_t G,
+                                                     const float* __restrict__ part_o,
+                                                     const float* __restrict__ part_ml, float* __restrict__ out,
+                                                     float* __restrict__ lse) {
   // all launch arguments in one scalar-memory round trip (see attn_kernel)
   asm volatile("" ::"s"(hkv), "s"(G), "s"(plan.items_stream), "s"(plan.items_dyn), "s"(plan.item_stride),
                "s"(plan.extra_partial),
                "s"(plan.dyn_mask[0]), "s"(plan.dyn_mask[1]), "s"(plan.dyn_mask[2]), "s"(plan.dyn_mask[3]),
                "s"(part_o), "s"(part_ml), "s"(out), "s"(lse));
   const HeadMask mask(plan);
-  const int32_t bh = blockIdx.x / G, g = blockIdx.x - bh * G;
+  const int32_t quarter = blockIdx.x & 3, oi = blockIdx.x >> 2;    // oi = b * H_q + h * G + g
+  const int32_t bh = oi / G, g = oi - bh * G;
   const int32_t h = bh % hkv;
   // (+1: the partial of a token appended in the attention launch)
   const int32_t n_items = (mask.dynamic(h) ? plan.items_dyn : plan.items_stream) + plan.extra_partial;
+  const int lane = threadIdx.x, slice = lane >> 3, c4 = lane & 7;
+  const int32_t ch = 32 * quarter + 4 * c4;
   const int64_t slot0 = (int64_t)bh * plan.item_stride * G + g;     // slot(i) = slot0 + i * G
-  const int32_t tid = threadIdx.x;
-  const int32_t sl_id = tid / (kHeadDim / 4), c4 = tid % (kHeadDim / 4);
   float M = -INFINITY, l = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int32_t i0 = sl_id; i0 < n_items; i0 += kCombineSlices * kCombineChunk) {
+  for (int32_t i0 = slice; i0 < n_items; i0 += kCombineSlices * kCombineChunk) {
     f32x4 ov[kCombineChunk];
     float2 mlv[kCombineChunk];
 #pragma unroll
     for (int k = 0; k < kCombineChunk; ++k) {
-      const int32_t i = min(i0 + k * kCombineSlices, n_items - 1);
-      const int64_t slot = slot0 + (int64_t)i * G;
-      ov[k] = *reinterpret_cast<const f32x4*>(part_o + slot * kHeadDim + 4 * c4);
+      const int64_t slot = slot0 + (int64_t)min(i0 + k * kCombineSlices, n_items - 1) * G;
+      ov[k] = *reinterpret_cast<const f32x4*>(part_o + slot * kHeadDim + ch);
       mlv[k] = *reinterpret_cast<const float2*>(part_ml + slot * 2);
     }
 #pragma unroll
     for (int k = 0; k < kCombineChunk; ++k)
       if (i0 + k * kCombineSlices < n_items) fold_partial(mlv[k].x, mlv[k].y, ov[k], M, l, o);
   }
-  so[tid] = o;
-  sM[tid] = M;
-  sl[tid] = l;
-  __syncthreads();
-  if (sl_id != 0) return;
 #pragma unroll
-  for (int32_t s = 1; s < kCombineSlices; ++s) {
-    const int32_t j = s * (kHeadDim / 4) + c4;
-    fold_partial(sM[j], sl[j], so[j], M, l, o);
+  for (int x = 8; x < 64; x <<= 1) {
+    const float M2 = __shfl_xor(M, x, 64), l2 = __shfl_xor(l, x, 64);
+    f32x4 o2;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o2[r] = __shfl_xor(o[r], x, 64);
+    fold_partial(M2, l2, o2, M, l, o);
   }
-  const int64_t oi = (int64_t)bh * G + g;          // = b * H_q + h * G + g
+  if (slice != 0) return;
   f32x4 res = {0.f, 0.f, 0.f, 0.f};
   if (M != -INFINITY) res = o / l;
-  *reinterpret_cast<f32x4*>(out + oi * kHeadDim + 4 * c4) = res;
-  if (lse && c4 == 0) lse[oi] = M == -INFINITY ? -INFINITY : (M + log2f(l)) * kLn2;
+  *reinterpret_cast<f32x4*>(out + (int64_t)oi * kHeadDim + ch) = res;
+  if (lse && lane == 0 && quarter == 0) lse[oi] = M == -INFINITY ? -INFINITY : (M + log2f(l)) * kLn2;
 }
 
 template <int PG, int BPI, int DEPTH = 4>
@@ -652,7 +648,7 @@ hipError_t launch_attn_t(const PoolArgs& pool, const BatchArgs& batch, const Att
   if (e != hipSuccess) return e;
   AttnPlan cplan = plan;
   cplan.extra_partial = k_new ? 1 : 0;
-  hipLaunchKernelGGL(combine_kernel, dim3(batch.B * pool.hkv * G), dim3(kCombineThreads), 0, s, pool.hkv, cplan, G,
+  hipLaunchKernelGGL(combine_kernel, dim3(batch.B * pool.hkv * G * 4), dim3(64), 0, s, pool.hkv, cplan, G,
                      part_o, part_ml, out, lse);
   return hipGetLastError();
 }

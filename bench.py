@@ -219,8 +219,11 @@ def main() -> int:
         log(f"[bench] probe done: {args.steps} steps, copy of {COPY_BYTES} bytes")
         return 0
 
-    # capture the timed steps once; replays are idempotent (same tokens are
-    # re-appended at the same positions, selections recomputed identically)
+    # capture the timed steps once; a replay re-appends the same tokens at the
+    # same positions and does the same work per step (a selection can differ
+    # where a scoring wave reads the summary of the page receiving the token,
+    # which an earlier run already filled further; the attention reads k
+    # pages per dynamic head whichever they are)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for s in range(args.warmup, total_steps):

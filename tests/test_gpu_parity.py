@@ -186,6 +186,73 @@ def test_ragged_mha_full_size_sampled():
     run(wl, check=[(6, 0), (6, 31), (0, 15), (0, 16), (9, 3), (13, 24), (15, 30)], fused=True)
 
 
+def test_graph_replay_matches_eager():
+    """The benchmark's path: decode steps (the append inside the selection /
+    attention launches, selection every 4 steps) captured in a HIP graph and
+    replayed. From the same pool state, every replay gives the eager run's
+    outputs, lse and selections bit for bit; eager work and synchronisations
+    run between the replays. (The pool is restored before each run: a replay
+    re-appends the same tokens, but the summary of the page receiving a token
+    may be read before its rewrite, and after an earlier run it already holds
+    later tokens.)"""
+    wl = W.WORKLOADS["llama3_128k"].scaled(contexts=(4100, 3001, 1000, 17), steps=8, budget=512, window=300)
+    log(f"[parity] graph replay {wl.name} contexts={wl.contexts} steps={wl.steps}")
+    pr = ParityRun(wl, check_heads=[])
+    layer = pr.layer
+    layer.set_budget([wl.budget_at(wl.seq_len(b, 0)) for b in range(wl.batch)])
+    pool = [layer.pool.k, layer.pool.v, layer.pool.summary]
+    snap = [t.clone() for t in pool]
+    steps = []
+    for i in range(wl.steps):
+        q, kn, vn = pr.step_inputs(i)
+        lens = torch.tensor([wl.seq_len(b, i) for b in range(wl.batch)], dtype=torch.int32, device="cuda")
+        steps.append((lens, bits_to_bf16(q), bits_to_bf16(kn), bits_to_bf16(vn), wl.selects_at(i)))
+
+    def buffers():
+        return [(torch.empty_like(layer.out), torch.empty_like(layer.lse), torch.empty_like(layer.sel_pages),
+                 torch.empty_like(layer.sel_count)) for _ in steps]
+
+    def run_steps(rec):
+        for (lens, q, kn, vn, sel), (o, l, sp, sc) in zip(steps, rec):
+            layer.use_lengths(lens)
+            if sel:
+                layer.append_select(q, kn, vn)
+                layer.attend(q)
+            else:
+                layer.append_attend(q, kn, vn)
+            o.copy_(layer.out)
+            l.copy_(layer.lse)
+            sp.copy_(layer.sel_pages)
+            sc.copy_(layer.sel_count)
+
+    def restore():
+        for t, s0 in zip(pool, snap):
+            t.copy_(s0)
+        torch.cuda.synchronize()
+
+    eager = buffers()
+    restore()
+    run_steps(eager)
+    torch.cuda.synchronize()
+    replayed = buffers()
+    g = torch.cuda.CUDAGraph()
+    restore()
+    with torch.cuda.graph(g):
+        run_steps(replayed)
+    for rep in range(3):
+        restore()
+        noise = torch.randn(1 << 20, device="cuda").sum()        # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(noise)
+        for i, (a, b) in enumerate(zip(eager, replayed)):
+            for x, y, what in zip(a, b, ("out", "lse", "sel_pages", "sel_count")):
+                assert torch.equal(x, y), f"replay {rep} step {i}: {what} differs from the eager run"
+    # and the eager run itself is the oracle's (same steps, same state)
+    pr2 = ParityRun(wl, fused=True)
+    assert_reports(pr2.run())
+
+
 @pytest.mark.parametrize("bpi", [4, 5, 6, 7, 8, 9, 10, 12, 16])
 def test_every_item_size(bpi):
     """Each attention work-item size (odd sizes pad the last block pair):

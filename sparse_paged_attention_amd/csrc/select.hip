@@ -547,10 +547,22 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
     for (int i = 0; i < PER; ++i) { cnt[i] = hist[BINS - 1 - (tid * PER + i)]; sum += cnt[i]; }
     int32_t tot2;
     int32_t run = block_exclusive_scan(sum, sh_wave, tot2);       // keys in higher bins
+    int32_t hit = -1, hit_run = 0;                // the owned bin where the count reaches `need`
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      if (run < need && run + cnt[i] >= need) { sh_pick[0] = BINS - 1 - (tid * PER + i); sh_pick[1] = run; }
+      const bool here = run < need && run + cnt[i] >= need;
+      hit = here ? i : hit;
+      hit_run = here ? run : hit_run;
       run += cnt[i];
+    }
+    if (hit >= 0) {
+      // recomputed here: left to itself the compiler keeps the bin numbers in
+      // registers from the start, spills them, and this one thread then waits
+      // on a scratch load before the barrier
+      int32_t t = tid;
+      asm volatile("" : "+v"(t));
+      sh_pick[0] = BINS - 1 - (t * PER + hit);
+      sh_pick[1] = hit_run;
     }
     __syncthreads();
     const uint32_t pick = (uint32_t)sh_pick[0];

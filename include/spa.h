@@ -95,6 +95,22 @@ typedef struct spa_batch {
   int32_t max_pages;          /* columns of page_table (physical pages per sequence), >= 1 */
   const int32_t* page_table;  /* device int32 [B][max_pages]: physical page ids in [0, N) */
   const int32_t* seq_lens;    /* device int32 [B]: L_b, tokens in sequence b after this step's append */
+  /* NULL, or device int32 [B]: window-only storage of the streaming heads.
+   * Sequence b keeps its streaming heads' rows in the R consecutive physical
+   * pages stream_pages[b] .. stream_pages[b] + R - 1 (R from
+   * spa_stream_ring_pages), not in the page table's pages: position t lives in
+   * ring slot t/P while t/P < S = ceil(sink / P) (the sink's pages), else in
+   * slot S + (t/P - S) mod (R - S); the window's pages reuse the slots in turn.
+   * Only tokens a step can still attend are kept (the sink, and the window),
+   * so a sequence's streaming heads need R pages whatever its length; the
+   * page table then serves the dynamic heads only. A ring outside the pool
+   * leaves the streaming heads' tokens unmapped (not attended, not written).
+   * Needs the head kinds in every call that takes them (calls without them
+   * return SPA_ERR_INVALID). LServe write-up "2.1" (streaming heads attend
+   * the sink and a local window only); the rolling ring of a window's
+   * keys and values, long-text article at lshu.cn, section "4.3"
+   * (StreamingLLM rolling cache). */
+  const int32_t* stream_pages;
 } spa_batch;
 
 /* ---- a1 (+ a2): append one token per sequence -------------------------
@@ -115,6 +131,10 @@ spa_status spa_kv_pool_append(const spa_pool* pool, const spa_heads* heads,
 
 /* Bulk write of tokens [start, start + count) of ONE sequence (prefill, or a
  * chunk of it).
+ *   stream_base: -1, or the first page of the sequence's ring (its
+ *          stream_pages entry, see spa_batch; needs `heads`): the streaming
+ *          heads then keep only the sink's pages and the last R - S pages of
+ *          the range, in their ring slots;
  *   heads: NULL, or the head kinds; when given, the same pass also builds the
  *          summary of every logical page it writes into, for every dynamic
  *          head, over the page's tokens below start + count (tokens of the
@@ -129,8 +149,8 @@ spa_status spa_kv_pool_append(const spa_pool* pool, const spa_heads* heads,
  * (pages of the pool through the page table). */
 spa_status spa_kv_pool_write(const spa_pool* pool, const spa_heads* heads,
                              const int32_t* page_table_row, int32_t max_pages,
-                             int64_t start, int64_t count, const void* k, const void* v,
-                             hipStream_t stream);
+                             int32_t stream_base, int64_t start, int64_t count,
+                             const void* k, const void* v, hipStream_t stream);
 
 /* ---- a2: page summaries ------------------------------------------------
  * For every dynamic KV head and every logical page j that overlaps positions
@@ -269,6 +289,11 @@ spa_status spa_set_attn_blocks_per_item(int32_t blocks);
 /* The write-up's dynamic budget rule ("3.2"): min(4096, L / 32) tokens,
  * integer division; 0 for L < 32. */
 int32_t spa_default_budget(int64_t context_len);
+
+/* Pages of one sequence's ring for window-only storage of the streaming
+ * heads (spa_batch.stream_pages): ceil(sink / P) + ceil(window / P) + 1.
+ * Returns 0 for invalid arguments. */
+int32_t spa_stream_ring_pages(const spa_pool* pool, const spa_heads* heads);
 
 /* ---- physical-page allocator (host) -------------------------------------
  * A free list over page ids 0..N-1 (LServe write-up "2.2": free list of

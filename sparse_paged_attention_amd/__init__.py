@@ -49,13 +49,14 @@ class c_heads(ctypes.Structure):
 
 class c_batch(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("max_pages", ctypes.c_int32),
-                ("page_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p)]
+                ("page_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("stream_pages", ctypes.c_void_p)]
 
 
 EXPORTS = ("spa_kv_pool_append", "spa_kv_pool_write", "spa_page_summary_update",
            "spa_select_pages", "spa_append_select_pages", "spa_sparse_decode_attn", "spa_append_decode_attn",
            "spa_workspace_bytes",
-           "spa_default_budget", "spa_alloc_create", "spa_alloc_pages", "spa_alloc_free",
+           "spa_default_budget", "spa_stream_ring_pages", "spa_alloc_create", "spa_alloc_pages", "spa_alloc_free",
            "spa_alloc_num_free", "spa_alloc_destroy", "spa_status_string", "spa_last_error",
            "spa_set_attn_blocks_per_item")
 
@@ -74,7 +75,7 @@ def lib() -> ctypes.CDLL:
         P, H, B = ctypes.POINTER(c_pool), ctypes.POINTER(c_heads), ctypes.POINTER(c_batch)
         sig = {
             "spa_kv_pool_append": ([P, H, B, vp, vp, vp], ctypes.c_int),
-            "spa_kv_pool_write": ([P, H, vp, i32, i64, i64, vp, vp, vp], ctypes.c_int),
+            "spa_kv_pool_write": ([P, H, vp, i32, i32, i64, i64, vp, vp, vp], ctypes.c_int),
             "spa_page_summary_update": ([P, H, B, vp, i32, vp], ctypes.c_int),
             "spa_select_pages": ([P, H, B, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "spa_append_select_pages": ([P, H, B, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp],
@@ -84,6 +85,7 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_int),
             "spa_workspace_bytes": ([P, H, i32, i32, i32], sz),
             "spa_default_budget": ([i64], i32),
+            "spa_stream_ring_pages": ([P, H], i32),
             "spa_set_attn_blocks_per_item": ([i32], ctypes.c_int),
             "spa_alloc_create": ([i32, ctypes.POINTER(vp)], ctypes.c_int),
             "spa_alloc_pages": ([vp, i32, vp], ctypes.c_int),
@@ -207,15 +209,19 @@ class Heads:
 
 @dataclass
 class Batch:
-    """page_table: int32 [B][max_pages] (device); seq_lens: int32 [B] (device)."""
+    """page_table: int32 [B][max_pages] (device); seq_lens: int32 [B] (device);
+    stream_pages: None or int32 [B] (device), the first page of each sequence's
+    ring for window-only storage of the streaming heads."""
     page_table: object
     seq_lens: object
+    stream_pages: object = None
 
     def c(self) -> c_batch:
         _need(self.page_table, (None, None), "i32", "page_table")
         B, mp = self.page_table.shape
         _need(self.seq_lens, (B,), "i32", "seq_lens")
-        return c_batch(B, mp, _ptr(self.page_table), _ptr(self.seq_lens))
+        _need(self.stream_pages, (B,), "i32", "stream_pages", optional=True)
+        return c_batch(B, mp, _ptr(self.page_table), _ptr(self.seq_lens), _ptr(self.stream_pages))
 
 
 # ------------------------------------------------------------ entry points
@@ -233,9 +239,11 @@ def kv_pool_append(pool: Pool, batch: Batch, k_new, v_new, heads: "Heads | None"
                                     ctypes.byref(b), _ptr(k_new), _ptr(v_new), _stream(stream)))
 
 
-def kv_pool_write(pool: Pool, page_table_row, start: int, k, v, heads=None, stream=None) -> None:
+def kv_pool_write(pool: Pool, page_table_row, start: int, k, v, heads=None, stream_base: int = -1,
+                  stream=None) -> None:
     """spa_kv_pool_write: k, v bf16 [H_kv][count][D] for positions [start, start+count);
-    with `heads`, the dynamic heads' summaries of the written pages are built in the same pass."""
+    with `heads`, the dynamic heads' summaries of the written pages are built in the same pass;
+    stream_base >= 0: the streaming heads go to the sequence's ring starting at that page."""
     p = pool.c()
     h = _heads_for(heads, pool) if heads is not None else None
     _need(page_table_row, (None,), "i32", "page_table_row")
@@ -243,8 +251,17 @@ def kv_pool_write(pool: Pool, page_table_row, start: int, k, v, heads=None, stre
     count = k.shape[1]
     _need(v, (pool.num_kv_heads, count, HEAD_DIM), "bf16", "v")
     _check(lib().spa_kv_pool_write(ctypes.byref(p), ctypes.byref(h) if h is not None else None,
-                                   _ptr(page_table_row), page_table_row.shape[0],
+                                   _ptr(page_table_row), page_table_row.shape[0], int(stream_base),
                                    start, count, _ptr(k), _ptr(v), _stream(stream)))
+
+
+def stream_ring_pages(pool: Pool, heads: "Heads") -> int:
+    """spa_stream_ring_pages: pages of one sequence's ring for window-only storage."""
+    p, h = pool.c(), _heads_for(heads, pool)
+    n = lib().spa_stream_ring_pages(ctypes.byref(p), ctypes.byref(h))
+    if n <= 0:
+        raise SpaError(SPA_ERR_INVALID, "stream_ring_pages: invalid shapes")
+    return n
 
 
 def page_summary_update(pool: Pool, heads: Heads, batch: Batch, first_pos=None, max_tokens: int = 1,

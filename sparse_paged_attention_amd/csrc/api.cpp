@@ -151,6 +151,28 @@ spa_status check_batch(const spa_batch* batch, const spa::PoolArgs& pl, spa::Bat
   out->max_pp = batch->max_pages;
   out->pt = batch->page_table;
   out->lens = batch->seq_lens;
+  out->ring = batch->stream_pages;
+  out->ring_sink = 0;
+  out->ring_win = 1;
+  return SPA_OK;
+}
+
+// Pages of the ring that keeps a sequence's streaming heads: the sink's pages
+// and the pages a window of `window` tokens can touch at once (one more than
+// it fills when it is not aligned to a page).
+void ring_geometry(const spa_heads* heads, int32_t P, int32_t* sink_pages, int32_t* win_pages) {
+  *sink_pages = (int32_t)(((int64_t)heads->sink + P - 1) / P);
+  *win_pages = (int32_t)(((int64_t)heads->window + P - 1) / P) + 1;
+}
+
+// Completes the batch's ring geometry (streaming heads kept in a ring when
+// stream_pages is given), which needs the head kinds.
+spa_status set_ring(const spa_heads* heads, const spa::PoolArgs& pl, spa::BatchArgs* bt) {
+  if (!bt->ring) return SPA_OK;
+  if (!heads) return fail(SPA_ERR_INVALID, "stream_pages needs the head kinds (heads is NULL)");
+  ring_geometry(heads, pl.P, &bt->ring_sink, &bt->ring_win);
+  if ((int64_t)bt->ring_sink + bt->ring_win > pl.N)
+    return fail(SPA_ERR_INVALID, "a ring of %d pages does not fit a pool of %d", bt->ring_sink + bt->ring_win, pl.N);
   return SPA_OK;
 }
 
@@ -250,6 +272,21 @@ spa_status spa_set_attn_blocks_per_item(int32_t blocks) {
   return ok();
 }
 
+int32_t spa_stream_ring_pages(const spa_pool* pool, const spa_heads* heads) {
+  spa::PoolArgs pl;
+  spa::HeadList dyn;
+  int32_t G;
+  const std::string keep = g_last_error;
+  int32_t n = 0;
+  if (check_pool(pool, &pl) == SPA_OK && check_heads(heads, pl, &G, &dyn, nullptr) == SPA_OK) {
+    int32_t a, b;
+    ring_geometry(heads, pl.P, &a, &b);
+    n = a + b;
+  }
+  g_last_error = keep;
+  return n;
+}
+
 int32_t spa_default_budget(int64_t context_len) {
   if (context_len < 0) return 0;
   const int64_t b = context_len / 32;
@@ -266,6 +303,7 @@ spa_status spa_kv_pool_append(const spa_pool* pool, const spa_heads* heads, cons
   if ((s = check_pool(pool, &pl)) != SPA_OK) return s;
   if (heads && (s = check_heads(heads, pl, &G, &dyn, nullptr)) != SPA_OK) return s;
   if ((s = check_batch(batch, pl, &bt)) != SPA_OK) return s;
+  if ((s = set_ring(heads, pl, &bt)) != SPA_OK) return s;
   if (bt.B == 0) return ok();
   if (!k_new || !v_new) return fail(SPA_ERR_INVALID, "k_new / v_new is NULL");
   return hip_status(spa::launch_append(pl, bt, static_cast<const uint16_t*>(k_new),
@@ -274,8 +312,8 @@ spa_status spa_kv_pool_append(const spa_pool* pool, const spa_heads* heads, cons
 }
 
 spa_status spa_kv_pool_write(const spa_pool* pool, const spa_heads* heads, const int32_t* page_table_row,
-                             int32_t max_pages, int64_t start, int64_t count, const void* k, const void* v,
-                             hipStream_t stream) {
+                             int32_t max_pages, int32_t stream_base, int64_t start, int64_t count, const void* k,
+                             const void* v, hipStream_t stream) {
   spa::PoolArgs pl;
   spa::HeadList dyn;
   int32_t G;
@@ -288,10 +326,19 @@ spa_status spa_kv_pool_write(const spa_pool* pool, const spa_heads* heads, const
   if (start + count > (int64_t)max_pages * pl.P)
     return fail(SPA_ERR_INVALID, "tokens [%lld, %lld) exceed max_pages * physical_page = %lld",
                 (long long)start, (long long)(start + count), (long long)max_pages * pl.P);
+  int32_t ring_sink = 0, ring_win = 1;
+  if (stream_base >= 0) {
+    if (!heads) return fail(SPA_ERR_INVALID, "stream_base needs the head kinds (heads is NULL)");
+    ring_geometry(heads, pl.P, &ring_sink, &ring_win);
+    if ((int64_t)stream_base + ring_sink + ring_win > pl.N)
+      return fail(SPA_ERR_INVALID, "ring [%d, %d) exceeds the pool's %d pages", stream_base,
+                  stream_base + ring_sink + ring_win, pl.N);
+  }
   if (count == 0) return ok();
   if (!page_table_row || !k || !v) return fail(SPA_ERR_INVALID, "page_table_row / k / v is NULL");
   return hip_status(spa::launch_write(pl, page_table_row, start, count, static_cast<const uint16_t*>(k),
-                                      static_cast<const uint16_t*>(v), heads ? &dyn : nullptr, stream),
+                                      static_cast<const uint16_t*>(v), heads ? &dyn : nullptr,
+                                      stream_base >= 0 ? stream_base : -1, ring_sink, ring_win, stream),
                     "kv_pool_write launch");
 }
 
@@ -305,6 +352,7 @@ spa_status spa_page_summary_update(const spa_pool* pool, const spa_heads* heads,
   if ((s = check_pool(pool, &pl)) != SPA_OK) return s;
   if ((s = check_heads(heads, pl, &G, &dyn, nullptr)) != SPA_OK) return s;
   if ((s = check_batch(batch, pl, &bt)) != SPA_OK) return s;
+  if ((s = set_ring(heads, pl, &bt)) != SPA_OK) return s;
   if (max_tokens < 1) return fail(SPA_ERR_INVALID, "max_tokens %d < 1", max_tokens);
   if (!first_pos && max_tokens != 1) return fail(SPA_ERR_INVALID, "first_pos NULL requires max_tokens == 1");
   if ((int64_t)max_tokens > (int64_t)bt.max_pp * pl.P)
@@ -348,6 +396,7 @@ spa_status select_pages(const spa_pool* pool, const spa_heads* heads, const spa_
   if ((s = check_pool(pool, &pl)) != SPA_OK) return s;
   if ((s = check_heads(heads, pl, &G, &dyn, nullptr)) != SPA_OK) return s;
   if ((s = check_batch(batch, pl, &bt)) != SPA_OK) return s;
+  if ((s = set_ring(heads, pl, &bt)) != SPA_OK) return s;
   if (k_max < 1) return fail(SPA_ERR_INVALID, "k_max %d < 1", k_max);
   const int32_t n_max = n_max_pages(pl, bt.max_pp);
   if (n_max > kMaxScoredPages)
@@ -416,6 +465,7 @@ spa_status decode_attn(const spa_pool* pool, const spa_heads* heads, const spa_b
   if ((s = check_pool(pool, &pl)) != SPA_OK) return s;
   if ((s = check_heads(heads, pl, &G, &dyn, kind)) != SPA_OK) return s;
   if ((s = check_batch(batch, pl, &bt)) != SPA_OK) return s;
+  if ((s = set_ring(heads, pl, &bt)) != SPA_OK) return s;
   if (k_max < 1) return fail(SPA_ERR_INVALID, "k_max %d < 1", k_max);
   if (bt.B == 0) return ok();
   if (!q || !out) return fail(SPA_ERR_INVALID, "q / out is NULL");

@@ -232,12 +232,13 @@ __device__ __forceinline__ void pv_pair(const PairTile& t, const PairProbs& pp, 
 __device__ __forceinline__ void token_partial(const PoolArgs& pl, const BatchArgs& bt, int32_t b, int32_t h,
                                               int32_t G, int32_t item_stride, int32_t it, const uint16_t* q,
                                               const uint16_t* k_new, const uint16_t* v_new, float* part_o,
-                                              float* part_ml) {
+                                              float* part_ml, bool in_ring) {
   const int lane = threadIdx.x & 63, g = lane & 15, quad = lane >> 4;
   const int32_t L = clamp_len(bt, b, pl.P);
   bool valid = L >= 1;
   if (valid) {
-    const int32_t phys = bt.pt[(int64_t)b * bt.max_pp + (L - 1) / pl.P];
+    const int32_t phys = in_ring ? ring_page(bt, bt.ring[b], L - 1, pl.P, pl.N)
+                                 : bt.pt[(int64_t)b * bt.max_pp + (L - 1) / pl.P];
     valid = phys >= 0 && phys < pl.N;
   }
   const int64_t bh = (int64_t)b * pl.hkv + h;
@@ -285,6 +286,7 @@ struct BlockSource {
   int32_t L, ls;         // ls: L_s clamped to [0, lim]
   int32_t lim;           // pool rows below lim are read (L, or L - 1 when the last token is appended in this launch)
   int32_t s0, w0, nb_sink, first_w;          // streaming
+  int32_t ring_base;                         // streaming: first page of the sequence's ring, if kept in one
   int32_t ls_floor;                          // tail
 };
 
@@ -301,7 +303,7 @@ struct BlockSource {
 // so one copy of the pipeline serves every kind of item (instruction-cache
 // footprint).
 template <int PG, int BPI, int DEPTH>
-__device__ __forceinline__ void run_blocks(const PoolArgs& pl, const int32_t* pt_row,
+__device__ __forceinline__ void run_blocks(const PoolArgs& pl, const BatchArgs& bt, const int32_t* pt_row,
                                            int32_t max_pp, int32_t h, const BlockSource& src,
                                            const int32_t (&page)[(BPI + 1) & ~1],
                                            const int32_t (&page_phys)[(BPI + 1) & ~1], bool use_phys,
@@ -310,6 +312,7 @@ __device__ __forceinline__ void run_blocks(const PoolArgs& pl, const int32_t* pt
   constexpr int NB = (BPI + 1) & ~1;              // pipeline slots: BPI rounded up to pairs
   const int32_t r = pl.P / PG;
   const auto pt = as_scalar(pt_row);
+  const bool bt_ring = bt.ring != nullptr;
   Block blk[NB];
   int32_t ptv[NB];
   if (src.kind == 1) {
@@ -351,8 +354,13 @@ __device__ __forceinline__ void run_blocks(const PoolArgs& pl, const int32_t* pt
         blk[u] = Block{hi > lo ? t0 : 0, lo, hi, 0, 0};
       }
     }
+    if (src.kind == 0 && bt_ring) {            // the ring's pages follow from the position alone
 #pragma unroll
-    for (int u = 0; u < NB; ++u) ptv[u] = pt[min(blk[u].t0 / pl.P, max_pp - 1)];
+      for (int u = 0; u < NB; ++u) ptv[u] = ring_page(bt, src.ring_base, blk[u].t0, pl.P, pl.N);
+    } else {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) ptv[u] = pt[min(blk[u].t0 / pl.P, max_pp - 1)];
+    }
   }
 #pragma unroll
   for (int u = 0; u < NB; ++u) {
@@ -434,7 +442,7 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
                "s"(plan.dyn_mask[3]), "s"(plan.sel_mask), "s"(plan.use_phys));
   asm volatile("" ::"s"(pl.k), "s"(pl.v), "s"(bt.pt), "s"(bt.lens), "s"(sel_pages), "s"(sel_count),
                "s"(sel_len), "s"(sel_phys), "s"(q), "s"(part_o), "s"(part_ml),
-               "s"(k_new), "s"(v_new), "s"(n_append), "s"(bt.B));
+               "s"(k_new), "s"(v_new), "s"(n_append), "s"(bt.B), "s"(bt.ring), "s"(bt.ring_sink), "s"(bt.ring_win));
   // work-group -> (sequence, head, item): head h's first item within the
   // sequence is h * items_stream + (dynamic heads below h) * (items_dyn - items_stream)
   const HeadMask mask(plan);
@@ -447,8 +455,8 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
     const int32_t ab = w / pl.hkv, ah = w - ab * pl.hkv;
     const int32_t n_it = mask.dynamic(ah) ? plan.items_dyn : plan.items_stream;
     token_partial(pl, bt, ab, ah, G, plan.item_stride, n_it, q, reinterpret_cast<const uint16_t*>(k_new), v_new,
-                  part_o, part_ml);
-    append_token(pl, bt, ab, ah, k_new, v_new, mask.dynamic(ah));
+                  part_o, part_ml, bt.ring != nullptr && !mask.dynamic(ah));
+    append_token(pl, bt, ab, ah, k_new, v_new, mask.dynamic(ah), bt.ring != nullptr && !mask.dynamic(ah));
     return;
   }
   const int32_t item = (int32_t)blockIdx.x;
@@ -476,6 +484,7 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
   const int32_t L_raw = as_scalar(bt.lens)[b];
   const int32_t cnt_raw = as_scalar(sel_count)[bh & plan.sel_mask];
   const int32_t ls_raw = as_scalar(sel_len)[b & plan.sel_mask];
+  const int32_t ring_raw = as_scalar(bt.ring ? bt.ring : bt.lens)[b];   // (read, never used, without a ring)
   int32_t page[NB], page_phys[NB];
   {
     const auto sp = as_scalar(sel_pages);
@@ -489,7 +498,7 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
   }
   // all of the round in flight together, waited for once (the compiler would
   // otherwise sink each load to its first use, behind the branches)
-  asm volatile("" ::"s"(L_raw), "s"(cnt_raw), "s"(ls_raw));
+  asm volatile("" ::"s"(L_raw), "s"(cnt_raw), "s"(ls_raw), "s"(ring_raw));
 #pragma unroll
   for (int u = 0; u < NB; ++u) asm volatile("" ::"s"(page[u]), "s"(page_phys[u]));
   const int32_t* pt_row = bt.pt + (int64_t)b * bt.max_pp;
@@ -527,6 +536,7 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
   src.L = L;
   src.lim = FRESH ? max(L - 1, 0) : L;
   src.ls = min(max(ls_raw, 0), src.lim);
+  src.ring_base = ring_raw;
   int32_t v_begin = it * BPI, v_end = 0;
   if (kind == 0) {
     src.s0 = min(plan.sink, L);
@@ -544,7 +554,7 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
     v_end = (L - src.ls_floor + kBlockTokens - 1) / kBlockTokens;   // any length: chunks of BPI
   }
   for (int32_t v0 = v_begin; v0 < v_end; v0 += BPI)
-    run_blocks<PG, BPI, DEPTH>(pl, pt_row, bt.max_pp, h, src, page, page_phys, plan.use_phys != 0, v0, v_end,
+    run_blocks<PG, BPI, DEPTH>(pl, bt, pt_row, bt.max_pp, h, src, page, page_phys, plan.use_phys != 0, v0, v_end,
                                qb, st);
 
   // fold the four token quads of the running sum, store the partial

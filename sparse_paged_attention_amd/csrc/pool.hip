@@ -24,7 +24,7 @@ __global__ void __launch_bounds__(64) append_kernel(PoolArgs pl, BatchArgs bt,
   const int32_t b = blockIdx.x / pl.hkv, h = blockIdx.x % pl.hkv;
   bool is_dyn = false;
   for (int32_t d = 0; d < dyn.n; ++d) is_dyn |= dyn.id[d] == h;
-  append_token(pl, bt, b, h, k_new, v_new, with_summary && is_dyn);
+  append_token(pl, bt, b, h, k_new, v_new, with_summary && is_dyn, bt.ring != nullptr && !is_dyn);
 }
 
 // Bulk write of tokens [start, start + count) of one sequence (prefill), one
@@ -36,6 +36,9 @@ __global__ void __launch_bounds__(64) append_kernel(PoolArgs pl, BatchArgs bt,
 // maximum over the page are its part of the page summary, written in the same
 // pass: the summary covers the page's tokens below start + count, those
 // before `start` (a page only partly inside the range) read from the pool.
+// With a ring (ring_base >= 0), streaming heads keep only what a later step
+// can attend: the sink's pages and the last ring_win pages of the range, at
+// their ring slots.
 struct DynMask {
   uint32_t w[kMaxKvHeads / 32];
 };
@@ -43,13 +46,22 @@ struct DynMask {
 template <int PG>
 __global__ void __launch_bounds__(64) write_kernel(PoolArgs pl, const int32_t* __restrict__ pt, int64_t start,
                                                    int64_t count, const uint32_t* __restrict__ k,
-                                                   const uint32_t* __restrict__ v, DynMask dyn) {
+                                                   const uint32_t* __restrict__ v, DynMask dyn,
+                                                   int32_t ring_base, int32_t ring_sink, int32_t ring_win) {
   const int32_t h = blockIdx.y;
   const int64_t j = start / PG + blockIdx.x;       // logical page
   const int64_t t0 = j * PG, end = start + count;
   const int64_t lo = t0 > start ? t0 : start, hi = t0 + PG < end ? t0 + PG : end;
   if (lo >= hi) return;
-  const int32_t phys = pt[j / pl.r];
+  const bool dynamic = (dyn.w[h >> 5] >> (h & 31)) & 1u;
+  int32_t phys;
+  if (ring_base >= 0 && !dynamic) {
+    const int64_t pg = j / pl.r, last = (end - 1) / pl.P;
+    if (pg >= ring_sink && pg < last - (ring_win - 1)) return;   // overwritten later in this range
+    phys = ring_base + (int32_t)(pg < ring_sink ? pg : ring_sink + (pg - ring_sink) % ring_win);
+  } else {
+    phys = pt[j / pl.r];
+  }
   if (phys < 0 || phys >= pl.N) return;
   const int32_t lp = (int32_t)(j % pl.r);
   const int lane = threadIdx.x;
@@ -90,7 +102,7 @@ __global__ void __launch_bounds__(64) write_kernel(PoolArgs pl, const int32_t* _
       }
     }
   }
-  if (!((dyn.w[h >> 5] >> (h & 31)) & 1u)) return;
+  if (!dynamic) return;
   uint32_t lo0 = 0xFFFFFFFFu, hi0 = 0u, lo1 = 0xFFFFFFFFu, hi1 = 0u;
 #pragma unroll
   for (int u = 0; u < PG; ++u) {
@@ -158,7 +170,8 @@ hipError_t launch_append(const PoolArgs& pool, const BatchArgs& batch, const uin
 }
 
 hipError_t launch_write(const PoolArgs& pool, const int32_t* pt_row, int64_t start, int64_t count,
-                        const uint16_t* k, const uint16_t* v, const HeadList* dyn, hipStream_t s) {
+                        const uint16_t* k, const uint16_t* v, const HeadList* dyn, int32_t ring_base,
+                        int32_t ring_sink, int32_t ring_win, hipStream_t s) {
   if (count == 0) return hipSuccess;
   DynMask m = {};
   if (dyn)
@@ -168,9 +181,9 @@ hipError_t launch_write(const PoolArgs& pool, const int32_t* pt_row, int64_t sta
   const uint32_t* k32 = reinterpret_cast<const uint32_t*>(k);
   const uint32_t* v32 = reinterpret_cast<const uint32_t*>(v);
   switch (pool.p) {
-    case 16: hipLaunchKernelGGL(write_kernel<16>, grid, dim3(64), 0, s, pool, pt_row, start, count, k32, v32, m); break;
-    case 32: hipLaunchKernelGGL(write_kernel<32>, grid, dim3(64), 0, s, pool, pt_row, start, count, k32, v32, m); break;
-    case 64: hipLaunchKernelGGL(write_kernel<64>, grid, dim3(64), 0, s, pool, pt_row, start, count, k32, v32, m); break;
+    case 16: hipLaunchKernelGGL(write_kernel<16>, grid, dim3(64), 0, s, pool, pt_row, start, count, k32, v32, m, ring_base, ring_sink, ring_win); break;
+    case 32: hipLaunchKernelGGL(write_kernel<32>, grid, dim3(64), 0, s, pool, pt_row, start, count, k32, v32, m, ring_base, ring_sink, ring_win); break;
+    case 64: hipLaunchKernelGGL(write_kernel<64>, grid, dim3(64), 0, s, pool, pt_row, start, count, k32, v32, m, ring_base, ring_sink, ring_win); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -31,6 +31,16 @@ __device__ __forceinline__ int32_t clamp_len(const BatchArgs& bt, int32_t b, int
   return L < 0 ? 0 : (L > cap ? cap : L);
 }
 
+// Physical page of position t of a streaming head in the ring that starts at
+// `base` (the sink's pages, then the window's pages reused in turn: the
+// window spans at most ring_win pages, so the pages it covers never share a
+// slot), or -1 when the ring does not lie inside the pool.
+__device__ __forceinline__ int32_t ring_page(const BatchArgs& bt, int32_t base, int32_t t, int32_t P, int32_t N) {
+  const int32_t pg = t / P;
+  const int32_t slot = pg < bt.ring_sink ? pg : bt.ring_sink + (pg - bt.ring_sink) % bt.ring_win;
+  return base >= 0 && base <= N - (bt.ring_sink + bt.ring_win) ? base + slot : -1;
+}
+
 // bf16 bit pattern -> unsigned key that orders like IEEE totalOrder (finite
 // values; -0 below +0), and back.
 __device__ __forceinline__ uint32_t order_key(uint16_t x) {
@@ -44,14 +54,15 @@ __device__ __forceinline__ uint16_t from_key(uint32_t k) {
 // l owns channels 2l and 2l+1. With `summary`, the same wave rebuilds the
 // summary of the logical page receiving the token: min and max over the
 // page's earlier tokens (read from the pool, 16 rows per batch of loads) and
-// the new key. k_new / v_new: bf16 [B][H_kv][D].
+// the new key. `in_ring`: a streaming head kept in the sequence's ring.
+// k_new / v_new: bf16 [B][H_kv][D].
 __device__ __forceinline__ void append_token(const PoolArgs& pl, const BatchArgs& bt, int32_t b, int32_t h,
                                              const uint32_t* __restrict__ k_new,
-                                             const uint16_t* __restrict__ v_new, bool summary) {
+                                             const uint16_t* __restrict__ v_new, bool summary, bool in_ring) {
   const int32_t L = clamp_len(bt, b, pl.P);
   if (L < 1) return;
   const int32_t t = L - 1;
-  const int32_t phys = bt.pt[(int64_t)b * bt.max_pp + t / pl.P];
+  const int32_t phys = in_ring ? ring_page(bt, bt.ring[b], t, pl.P, pl.N) : bt.pt[(int64_t)b * bt.max_pp + t / pl.P];
   if (phys < 0 || phys >= pl.N) return;
   const int32_t slot = t % pl.P, lp = slot / pl.p, i = slot % pl.p;
   const int lane = threadIdx.x & 63;

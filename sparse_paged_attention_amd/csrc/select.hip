@@ -198,7 +198,7 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
     const int32_t ab = w / pl.hkv, ah = w - ab * pl.hkv;
     bool is_dyn = false;
     for (int32_t d = 0; d < dyn.n; ++d) is_dyn |= dyn.id[d] == ah;
-    append_token(pl, bt, ab, ah, k_new, v_new, is_dyn);
+    append_token(pl, bt, ab, ah, k_new, v_new, is_dyn, bt.ring != nullptr && !is_dyn);
     return;
   }
   static_assert(S::OFFS <= 192, "three page offsets per lane");

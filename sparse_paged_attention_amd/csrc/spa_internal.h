@@ -28,6 +28,12 @@ struct BatchArgs {
   int32_t max_pp;
   const int32_t* pt;    // [B][max_pp]
   const int32_t* lens;  // [B]
+  // Streaming heads kept in a ring of physical pages per sequence (NULL: in
+  // the pages of the page table like dynamic heads): ring[b] is the first of
+  // ring_sink + ring_win consecutive pages; position t of a streaming head is
+  // in page ring[b] + (t/P < ring_sink ? t/P : ring_sink + (t/P - ring_sink) % ring_win).
+  const int32_t* ring;
+  int32_t ring_sink, ring_win;
 };
 
 // A list of KV-head ids (dynamic heads for selection / summaries).
@@ -62,7 +68,8 @@ hipError_t launch_append(const PoolArgs& pool, const BatchArgs& batch,
 hipError_t launch_write(const PoolArgs& pool, const int32_t* pt_row, int64_t start,
                         int64_t count, const uint16_t* k, const uint16_t* v,
                         const HeadList* dyn,                  // NULL or dynamic heads: summaries too
-                        hipStream_t s);
+                        int32_t ring_base, int32_t ring_sink,  // ring_base < 0: no ring
+                        int32_t ring_win, hipStream_t s);
 hipError_t launch_summary(const PoolArgs& pool, const BatchArgs& batch, const HeadList& dyn,
                           const int32_t* first_pos, int32_t max_tokens, hipStream_t s);
 hipError_t launch_select(const PoolArgs& pool, const BatchArgs& batch, const HeadList& dyn,

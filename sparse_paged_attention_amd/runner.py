@@ -18,24 +18,36 @@ import numpy as np
 import torch
 
 from . import (Batch, Heads, Pool, kv_pool_append, kv_pool_write, page_summary_update,
-               select_pages, sparse_decode_attn, workspace_bytes)
+               select_pages, sparse_decode_attn, stream_ring_pages, workspace_bytes)
 
 
 class DecodeLayer:
     def __init__(self, *, hq: int, hkv: int, p: int, P: int, kind, sink: int, window: int,
                  page_table: np.ndarray, num_phys_pages: int, k_max: int, device="cuda",
-                 resolve_at_selection: bool = True):
+                 resolve_at_selection: bool = True, window_only: bool = False):
         self.hq, self.hkv, self.p, self.P = hq, hkv, p, P
         self.k_max = int(k_max)
         self.device = device
         self.heads = Heads(hq, tuple(int(k) for k in kind), sink, window)
-        self.pool = Pool.empty(hkv, p, P, num_phys_pages, with_summary=any(kind), device=device)
         pt = np.ascontiguousarray(page_table, dtype=np.int32)
         self.B, self.max_pages = pt.shape
+        # window-only storage: each sequence's streaming heads live in a ring of
+        # R pages placed after the page table's pages
+        self.ring_pages = 0
+        n_pages = num_phys_pages
+        if window_only:
+            probe = Pool.empty(hkv, p, P, 1, with_summary=any(kind), device=device)   # sizes only
+            self.ring_pages = stream_ring_pages(probe, self.heads)
+            n_pages += self.B * self.ring_pages
+        self.pool = Pool.empty(hkv, p, P, n_pages, with_summary=any(kind), device=device)
+        self.stream_pages = None
+        if window_only:
+            self.stream_pages = torch.arange(self.B, dtype=torch.int32, device=device) * self.ring_pages \
+                + num_phys_pages
         self.page_table = torch.from_numpy(pt).to(device)
         self.lens_host = np.zeros(self.B, np.int32)
         self.seq_lens = torch.zeros(self.B, dtype=torch.int32, device=device)
-        self.batch = Batch(self.page_table, self.seq_lens)
+        self.batch = Batch(self.page_table, self.seq_lens, self.stream_pages)
         self.sel_pages = torch.zeros((self.B, hkv, self.k_max), dtype=torch.int32, device=device)
         self.sel_count = torch.zeros((self.B, hkv), dtype=torch.int32, device=device)
         self.sel_len = torch.zeros(self.B, dtype=torch.int32, device=device)
@@ -53,8 +65,9 @@ class DecodeLayer:
     def write_tokens(self, b: int, start: int, K: torch.Tensor, V: torch.Tensor, summaries: bool = True) -> None:
         """Positions [start, start + K.shape[1]) of sequence b; K, V bf16 [H_kv][n][D] on device.
         With `summaries`, the dynamic heads' page summaries are built in the same pass."""
+        base = -1 if self.stream_pages is None else int(self.stream_pages[b])
         kv_pool_write(self.pool, self.page_table[b], start, K.contiguous(), V.contiguous(),
-                      heads=self.heads if summaries else None)
+                      heads=self.heads if (summaries or base >= 0) else None, stream_base=base)
 
     def set_lengths(self, lens) -> None:
         self.lens_host = np.asarray(lens, np.int32).copy()
@@ -72,7 +85,7 @@ class DecodeLayer:
     def use_lengths(self, seq_lens: torch.Tensor) -> None:
         """Points the batch at a device int32 [B] tensor of lengths prepared by the caller."""
         self.seq_lens = seq_lens
-        self.batch = Batch(self.page_table, seq_lens)
+        self.batch = Batch(self.page_table, seq_lens, self.stream_pages)
 
     def append(self, k_new: torch.Tensor, v_new: torch.Tensor) -> None:
         """Appends one token to every sequence: k_new, v_new bf16 [B][H_kv][D].

@@ -168,12 +168,36 @@ def test_select_and_summary_validation(spa):
     bad_heads = mkheads(spa, kind=(0, 0, 0, 0, 1, 1, 1, 3))
     assert L.spa_kv_pool_append(ctypes.byref(pool), ctypes.byref(bad_heads), ctypes.byref(batch), FAKE,
                                 FAKE, None) == 1
-    assert L.spa_kv_pool_write(ctypes.byref(pool), None, FAKE, 4, 250, 10, FAKE, FAKE, None) == 1
-    assert L.spa_kv_pool_write(ctypes.byref(pool), None, FAKE, 4, -1, 1, FAKE, FAKE, None) == 1
-    assert L.spa_kv_pool_write(ctypes.byref(pool), None, None, 4, 0, 1, FAKE, FAKE, None) == 1
-    assert L.spa_kv_pool_write(ctypes.byref(pool), None, FAKE, 4, 0, 0, FAKE, FAKE, None) == 0
-    assert L.spa_kv_pool_write(ctypes.byref(pool), ctypes.byref(bad_heads), FAKE, 4, 0, 1, FAKE, FAKE, None) == 1
-    assert L.spa_kv_pool_write(ctypes.byref(pool), ctypes.byref(heads), FAKE, 4, 0, 0, FAKE, FAKE, None) == 0
+    assert L.spa_kv_pool_write(ctypes.byref(pool), None, FAKE, 4, -1, 250, 10, FAKE, FAKE, None) == 1
+    assert L.spa_kv_pool_write(ctypes.byref(pool), None, FAKE, 4, -1, -1, 1, FAKE, FAKE, None) == 1
+    assert L.spa_kv_pool_write(ctypes.byref(pool), None, None, 4, -1, 0, 1, FAKE, FAKE, None) == 1
+    assert L.spa_kv_pool_write(ctypes.byref(pool), None, FAKE, 4, -1, 0, 0, FAKE, FAKE, None) == 0
+    assert L.spa_kv_pool_write(ctypes.byref(pool), ctypes.byref(bad_heads), FAKE, 4, -1, 0, 1, FAKE, FAKE,
+                               None) == 1
+    assert L.spa_kv_pool_write(ctypes.byref(pool), ctypes.byref(heads), FAKE, 4, -1, 0, 0, FAKE, FAKE, None) == 0
+
+
+def test_window_only_storage_validation(spa):
+    """Rings of the streaming heads: ceil(sink / P) + ceil(window / P) + 1 pages,
+    checked against the pool, and only usable together with the head kinds."""
+    L = spa.lib()
+    ring = lambda pool, heads: L.spa_stream_ring_pages(ctypes.byref(pool), ctypes.byref(heads))
+    big_pool = mkpool(spa, num_phys_pages=1000)
+    assert ring(big_pool, mkheads(spa, sink=64, window=1024)) == 1 + 16 + 1
+    assert ring(big_pool, mkheads(spa, sink=65, window=1025)) == 2 + 17 + 1
+    assert ring(big_pool, mkheads(spa, sink=0, window=1)) == 0 + 1 + 1
+    assert ring(mkpool(spa, physical_page=256), mkheads(spa, sink=64, window=4096)) == 1 + 16 + 1
+    assert ring(mkpool(spa, num_kv_heads=0), mkheads(spa)) == 0
+    heads = mkheads(spa)                                     # ring of 18 pages
+    small = mkpool(spa, num_phys_pages=17)
+    ringed = spa.c_batch(1, 4, FAKE, FAKE, FAKE)
+    assert attn(spa, small, heads, ringed) == 1              # the ring does not fit the pool
+    assert L.spa_kv_pool_append(ctypes.byref(big_pool), None, ctypes.byref(ringed), FAKE, FAKE, None) == 1
+    assert L.spa_kv_pool_write(ctypes.byref(big_pool), None, FAKE, 4, 0, 0, 1, FAKE, FAKE, None) == 1
+    assert L.spa_kv_pool_write(ctypes.byref(big_pool), ctypes.byref(heads), FAKE, 4, 1000 - 17, 0, 1, FAKE,
+                               FAKE, None) == 1
+    assert L.spa_kv_pool_write(ctypes.byref(big_pool), ctypes.byref(heads), FAKE, 4, 1000 - 18, 0, 0, FAKE,
+                               FAKE, None) == 0
 
 
 def test_attn_blocks_per_item_setting(spa):

@@ -20,10 +20,10 @@ def gpu():
     oracle.build()
 
 
-def run(wl, steps=None, check=None, fused=False):
+def run(wl, steps=None, check=None, fused=False, window_only=False):
     log(f"[parity] {wl.name} B={wl.batch} hq={wl.hq} hkv={wl.hkv} p={wl.p} P={wl.P} "
-        f"contexts={wl.contexts[:4]} steps={wl.steps if steps is None else steps}")
-    pr = ParityRun(wl, check_heads=check, fused=fused)
+        f"contexts={wl.contexts[:4]} steps={wl.steps if steps is None else steps} window_only={window_only}")
+    pr = ParityRun(wl, check_heads=check, fused=fused, window_only=window_only)
     reps = pr.run(steps)
     assert_reports(reps)
     return pr, reps
@@ -251,6 +251,59 @@ def test_graph_replay_matches_eager():
     # and the eager run itself is the oracle's (same steps, same state)
     pr2 = ParityRun(wl, fused=True)
     assert_reports(pr2.run())
+
+
+# ------------------------------------------ window-only streaming storage
+
+WINDOW_ONLY_CASES = {
+    "toy_4k": lambda: W.WORKLOADS["toy_4k"].scaled(steps=6, reuse=2),
+    "128k_small": lambda: W.WORKLOADS["llama3_128k"].scaled(contexts=(4100, 3001, 1000, 17), steps=9,
+                                                           budget=512, window=300),
+    "ragged_small": lambda: W.WORKLOADS["ragged_mha"].scaled(contexts=(2500, 40, 1800, 3333, 700, 16, 1, 2049),
+                                                             batch=8, steps=6),
+    "p32_P256": lambda: W.WORKLOADS["single_256k"].scaled(contexts=(9000,), steps=5, window=700, sink=40),
+    "p64": lambda: W.Workload("p64_ring", 2480, 2, 8, 2, 64, 256, (2000, 700), 6, 2, (0, 1), 8, 600, 512, True),
+}
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("case", list(WINDOW_ONLY_CASES))
+def test_window_only_storage(case, fused):
+    """Streaming heads kept in a ring of sink + window pages per sequence
+    (the window's pages reused as it moves; LServe write-up "2.1": streaming
+    heads attend the sink and the window only): the same results as the
+    oracle, on the separate entry points and on the benchmark's launches."""
+    run(WINDOW_ONLY_CASES[case](), fused=fused, window_only=True)
+
+
+def test_window_only_matches_page_table_layout():
+    """The ring changes where streaming heads' rows live, nothing else: step
+    by step, outputs, lse and selections are bit-identical to the page-table
+    layout, and no streaming head's row is ever written into a page of the
+    page table (those pages stay zero there)."""
+    wl = W.WORKLOADS["llama3_128k"].scaled(contexts=(4100, 3001, 1000, 17), steps=9, budget=512, window=300)
+    log(f"[parity] ring vs page table {wl.name} contexts={wl.contexts}")
+    a = ParityRun(wl, check_heads=[], fused=True)
+    b = ParityRun(wl, check_heads=[], fused=True, window_only=True)
+    for i in range(wl.steps):
+        a.run_step(i)
+        b.run_step(i)
+        for x, y, what in ((a.layer.out, b.layer.out, "out"), (a.layer.lse, b.layer.lse, "lse"),
+                           (a.layer.sel_pages, b.layer.sel_pages, "sel_pages"),
+                           (a.layer.sel_count, b.layer.sel_count, "sel_count")):
+            assert torch.equal(x, y), f"step {i}: {what} differs"
+    pt = W.page_table(wl)
+    used = np.unique(pt[pt >= 0])
+    stream = [h for h in range(wl.hkv) if not wl.kind[h]]
+    k = b.layer.pool.k[torch.from_numpy(used).cuda()][:, stream]
+    v = b.layer.pool.v[torch.from_numpy(used).cuda()][:, stream]
+    assert not k.view(torch.int16).any() and not v.view(torch.int16).any()
+
+
+def test_window_only_128k_full_size_sampled():
+    """The benchmark's configuration at full size with the streaming heads in
+    rings (4 x 131072 + 16 steps, the benchmark's launches), sampled heads."""
+    run(W.WORKLOADS["llama3_128k"], check=[(0, 0), (1, 3), (2, 5), (3, 2)], fused=True, window_only=True)
 
 
 @pytest.mark.parametrize("bpi", [4, 5, 6, 7, 8, 9, 10, 12, 16])

@@ -37,7 +37,7 @@ METRIC = "sparse decode-attn µs/step + achieved HBM GB/s (% peak) at 128K ctx"
 PEAK_GBPS = 8000.0
 COPY_BYTES = 1 << 30          # calibration copy for the HBM byte counters
 WORKLOAD = "llama3_128k"
-ATTN_KERNELS = "attn_kernel<16, 5, 4, false>|combine_kernel"    # one spa_sparse_decode_attn call
+ATTN_KERNELS = "attn_kernel<16, 5, 4, false, false>|combine_kernel"    # one spa_sparse_decode_attn call
 WRITE_KERNELS = "write_kernel<16>"                               # one spa_kv_pool_write call
 
 

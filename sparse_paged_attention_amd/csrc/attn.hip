@@ -302,7 +302,7 @@ struct BlockSource {
 // the caller before the lengths arrive). The kernel has a single call site,
 // so one copy of the pipeline serves every kind of item (instruction-cache
 // footprint).
-template <int PG, int BPI, int DEPTH>
+template <int PG, int BPI, int DEPTH, bool RING>
 __device__ __forceinline__ void run_blocks(const PoolArgs& pl, const BatchArgs& bt, const int32_t* pt_row,
                                            int32_t max_pp, int32_t h, const BlockSource& src,
                                            const int32_t (&page)[(BPI + 1) & ~1],
@@ -312,7 +312,6 @@ __device__ __forceinline__ void run_blocks(const PoolArgs& pl, const BatchArgs& 
   constexpr int NB = (BPI + 1) & ~1;              // pipeline slots: BPI rounded up to pairs
   const int32_t r = pl.P / PG;
   const auto pt = as_scalar(pt_row);
-  const bool bt_ring = bt.ring != nullptr;
   Block blk[NB];
   int32_t ptv[NB];
   if (src.kind == 1) {
@@ -354,7 +353,7 @@ __device__ __forceinline__ void run_blocks(const PoolArgs& pl, const BatchArgs& 
         blk[u] = Block{hi > lo ? t0 : 0, lo, hi, 0, 0};
       }
     }
-    if (src.kind == 0 && bt_ring) {            // the ring's pages follow from the position alone
+    if (RING && src.kind == 0) {               // the ring's pages follow from the position alone
 #pragma unroll
       for (int u = 0; u < NB; ++u) ptv[u] = ring_page(bt, src.ring_base, blk[u].t0, pl.P, pl.N);
     } else {
@@ -424,7 +423,7 @@ struct HeadMask {
 // a partial (max, sum, unnormalised output) per query head.
 // FRESH: the step's token is appended in this launch (k_new / v_new given);
 // a separate instantiation, so plain attention carries none of its code.
-template <int PG, int BPI, int DEPTH, bool FRESH>
+template <int PG, int BPI, int DEPTH, bool FRESH, bool RING>
 __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, AttnPlan plan, int32_t G,
                                                   const uint16_t* q, const int32_t* sel_pages,
                                                   const int32_t* sel_count, const int32_t* sel_len,
@@ -442,7 +441,8 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
                "s"(plan.dyn_mask[3]), "s"(plan.sel_mask), "s"(plan.use_phys));
   asm volatile("" ::"s"(pl.k), "s"(pl.v), "s"(bt.pt), "s"(bt.lens), "s"(sel_pages), "s"(sel_count),
                "s"(sel_len), "s"(sel_phys), "s"(q), "s"(part_o), "s"(part_ml),
-               "s"(k_new), "s"(v_new), "s"(n_append), "s"(bt.B), "s"(bt.ring), "s"(bt.ring_sink), "s"(bt.ring_win));
+               "s"(k_new), "s"(v_new), "s"(n_append), "s"(bt.B));
+  if (RING) asm volatile("" ::"s"(bt.ring), "s"(bt.ring_sink), "s"(bt.ring_win));
   // work-group -> (sequence, head, item): head h's first item within the
   // sequence is h * items_stream + (dynamic heads below h) * (items_dyn - items_stream)
   const HeadMask mask(plan);
@@ -455,8 +455,8 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
     const int32_t ab = w / pl.hkv, ah = w - ab * pl.hkv;
     const int32_t n_it = mask.dynamic(ah) ? plan.items_dyn : plan.items_stream;
     token_partial(pl, bt, ab, ah, G, plan.item_stride, n_it, q, reinterpret_cast<const uint16_t*>(k_new), v_new,
-                  part_o, part_ml, bt.ring != nullptr && !mask.dynamic(ah));
-    append_token(pl, bt, ab, ah, k_new, v_new, mask.dynamic(ah), bt.ring != nullptr && !mask.dynamic(ah));
+                  part_o, part_ml, RING && !mask.dynamic(ah));
+    append_token(pl, bt, ab, ah, k_new, v_new, mask.dynamic(ah), RING && !mask.dynamic(ah));
     return;
   }
   const int32_t item = (int32_t)blockIdx.x;
@@ -484,7 +484,7 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
   const int32_t L_raw = as_scalar(bt.lens)[b];
   const int32_t cnt_raw = as_scalar(sel_count)[bh & plan.sel_mask];
   const int32_t ls_raw = as_scalar(sel_len)[b & plan.sel_mask];
-  const int32_t ring_raw = as_scalar(bt.ring ? bt.ring : bt.lens)[b];   // (read, never used, without a ring)
+  const int32_t ring_raw = RING ? as_scalar(bt.ring)[b] : -1;
   int32_t page[NB], page_phys[NB];
   {
     const auto sp = as_scalar(sel_pages);
@@ -554,7 +554,7 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
     v_end = (L - src.ls_floor + kBlockTokens - 1) / kBlockTokens;   // any length: chunks of BPI
   }
   for (int32_t v0 = v_begin; v0 < v_end; v0 += BPI)
-    run_blocks<PG, BPI, DEPTH>(pl, bt, pt_row, bt.max_pp, h, src, page, page_phys, plan.use_phys != 0, v0, v_end,
+    run_blocks<PG, BPI, DEPTH, RING>(pl, bt, pt_row, bt.max_pp, h, src, page, page_phys, plan.use_phys != 0, v0, v_end,
                                qb, st);
 
   // fold the four token quads of the running sum, store the partial
@@ -647,13 +647,20 @@ hipError_t launch_attn_t(const PoolArgs& pool, const BatchArgs& batch, const Att
                          float* out, float* lse, const uint16_t* k_new, const uint16_t* v_new, hipStream_t s) {
   const int32_t n_append = k_new ? batch.B * pool.hkv : 0;
   const int64_t grid = n_append + (int64_t)batch.B * plan.items_per_seq;
-  if (k_new)
-    hipLaunchKernelGGL((attn_kernel<PG, BPI, DEPTH, true>), dim3((unsigned)grid), dim3(64), 0, s, pool, batch, plan,
-                       G, q, sel_pages, sel_count, sel_len, sel_phys, part_o, part_ml,
-                       reinterpret_cast<const uint32_t*>(k_new), v_new, n_append);
-  else
-    hipLaunchKernelGGL((attn_kernel<PG, BPI, DEPTH, false>), dim3((unsigned)grid), dim3(64), 0, s, pool, batch,
-                       plan, G, q, sel_pages, sel_count, sel_len, sel_phys, part_o, part_ml, nullptr, nullptr, 0);
+  // kernel variants: the token appended in the launch (FRESH) and streaming
+  // heads kept in rings (RING) are template flags, so launches without them
+  // carry none of their code
+#define SPA_ATTN_LAUNCH(FRESH, RING)                                                                         \
+  hipLaunchKernelGGL((attn_kernel<PG, BPI, DEPTH, FRESH, RING>), dim3((unsigned)grid), dim3(64), 0, s, pool, \
+                     batch, plan, G, q, sel_pages, sel_count, sel_len, sel_phys, part_o, part_ml,           \
+                     reinterpret_cast<const uint32_t*>(k_new), v_new, n_append)
+  const bool ring = batch.ring != nullptr;
+  if (k_new) {
+    if (ring) SPA_ATTN_LAUNCH(true, true); else SPA_ATTN_LAUNCH(true, false);
+  } else {
+    if (ring) SPA_ATTN_LAUNCH(false, true); else SPA_ATTN_LAUNCH(false, false);
+  }
+#undef SPA_ATTN_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   AttnPlan cplan = plan;

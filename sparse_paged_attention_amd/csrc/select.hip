@@ -647,8 +647,13 @@ hipError_t launch_select(const PoolArgs& pool, const BatchArgs& batch, const Hea
 #define SPA_TOPK(E)                                                                                     \
   hipLaunchKernelGGL(topk_kernel<E>, dim3(batch.B * dyn.n), dim3(kTopkThreads), 0, s, batch, pool.p, pool.P, \
                      pool.hkv, dyn, scores, n_max, budget, k_max, sel_pages, sel_count, sel_len, sel_phys)
+  // the fewest scores per thread that hold the row: each phase of the
+  // selection costs VALU work per element, on one compute unit per problem
   if (n_max <= 8 * kTopkThreads) SPA_TOPK(8);
+  else if (n_max <= 9 * kTopkThreads) SPA_TOPK(9);
+  else if (n_max <= 12 * kTopkThreads) SPA_TOPK(12);
   else if (n_max <= 16 * kTopkThreads) SPA_TOPK(16);
+  else if (n_max <= 24 * kTopkThreads) SPA_TOPK(24);
   else SPA_TOPK(32);
 #undef SPA_TOPK
   return hipGetLastError();

@@ -75,9 +75,18 @@ typedef struct spa_pool {
   int32_t logical_page;   /* p, tokens per logical page: 16, 32 or 64 (the write-up caps it at 64, "5.3") */
   int32_t physical_page;  /* P, tokens per physical page: a multiple of p, P/p <= 64 */
   int32_t num_phys_pages; /* N >= 1 */
-  void* k_pool;           /* device bf16 [N][H_kv][P][D] */
-  void* v_pool;           /* device bf16 [N][H_kv][P/p][D][p] */
-  void* summary;          /* device bf16 [N][H_kv][P/p][2][D]; may be NULL when no head is dynamic */
+  void* k_pool;           /* device bf16 [N][S][P][D] */
+  void* v_pool;           /* device bf16 [N][S][P/p][D][p] */
+  void* summary;          /* device bf16 [N][S][P/p][2][D]; may be NULL when no head is dynamic */
+  /* S, head slots per physical page. 0 (or H_kv): every page holds every KV
+   * head, head h in slot h. Fewer (at least the number of dynamic and of
+   * streaming heads): the compact layout of window-only storage -- the page
+   * table's pages hold the dynamic heads, head h in slot (dynamic heads below
+   * h), and the rings of spa_batch.stream_pages hold the streaming heads, in
+   * slot (streaming heads below h); every call then needs the head kinds, and
+   * the rings whenever a head is streaming. With half the heads streaming this
+   * halves the pool. */
+  int32_t head_slots;
 } spa_pool;
 
 /* Which KV heads are streaming and which are dynamic, and the streaming

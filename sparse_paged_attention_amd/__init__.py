@@ -39,7 +39,8 @@ class c_pool(ctypes.Structure):
     _fields_ = [("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("logical_page", ctypes.c_int32), ("physical_page", ctypes.c_int32),
                 ("num_phys_pages", ctypes.c_int32), ("k_pool", ctypes.c_void_p),
-                ("v_pool", ctypes.c_void_p), ("summary", ctypes.c_void_p)]
+                ("v_pool", ctypes.c_void_p), ("summary", ctypes.c_void_p),
+                ("head_slots", ctypes.c_int32)]
 
 
 class c_heads(ctypes.Structure):
@@ -153,8 +154,8 @@ def _stream(stream=None) -> int:
 class Pool:
     """A physical-page pool of one attention layer (device tensors).
 
-    k: bf16 [N][H_kv][P][D]; v: bf16 [N][H_kv][P/p][D][p];
-    summary: bf16 [N][H_kv][P/p][2][D] or None."""
+    k: bf16 [N][S][P][D]; v: bf16 [N][S][P/p][D][p];
+    summary: bf16 [N][S][P/p][2][D] or None; S = head_slots or H_kv."""
     num_kv_heads: int
     logical_page: int
     physical_page: int
@@ -163,30 +164,32 @@ class Pool:
     v: object
     summary: object = None
     head_dim: int = HEAD_DIM
+    head_slots: int = 0
 
     @classmethod
     def empty(cls, num_kv_heads: int, logical_page: int, physical_page: int, num_phys_pages: int,
-              with_summary: bool = True, device="cuda", zero: bool = True) -> "Pool":
+              with_summary: bool = True, device="cuda", zero: bool = True, head_slots: int = 0) -> "Pool":
         import torch
         mk = torch.zeros if zero else torch.empty
         r = physical_page // logical_page
-        k = mk((num_phys_pages, num_kv_heads, physical_page, HEAD_DIM), dtype=torch.bfloat16, device=device)
-        v = mk((num_phys_pages, num_kv_heads, r, HEAD_DIM, logical_page), dtype=torch.bfloat16, device=device)
-        s = mk((num_phys_pages, num_kv_heads, r, 2, HEAD_DIM), dtype=torch.bfloat16, device=device) \
+        S = head_slots or num_kv_heads
+        k = mk((num_phys_pages, S, physical_page, HEAD_DIM), dtype=torch.bfloat16, device=device)
+        v = mk((num_phys_pages, S, r, HEAD_DIM, logical_page), dtype=torch.bfloat16, device=device)
+        s = mk((num_phys_pages, S, r, 2, HEAD_DIM), dtype=torch.bfloat16, device=device) \
             if with_summary else None
-        return cls(num_kv_heads, logical_page, physical_page, num_phys_pages, k, v, s)
+        return cls(num_kv_heads, logical_page, physical_page, num_phys_pages, k, v, s, head_slots=head_slots)
 
     def check(self) -> None:
         r = self.physical_page // max(self.logical_page, 1)
-        N, H, P, p = self.num_phys_pages, self.num_kv_heads, self.physical_page, self.logical_page
-        _need(self.k, (N, H, P, HEAD_DIM), "bf16", "pool.k")
-        _need(self.v, (N, H, r, HEAD_DIM, p), "bf16", "pool.v")
-        _need(self.summary, (N, H, r, 2, HEAD_DIM), "bf16", "pool.summary", optional=True)
+        N, S, P, p = self.num_phys_pages, self.head_slots or self.num_kv_heads, self.physical_page, self.logical_page
+        _need(self.k, (N, S, P, HEAD_DIM), "bf16", "pool.k")
+        _need(self.v, (N, S, r, HEAD_DIM, p), "bf16", "pool.v")
+        _need(self.summary, (N, S, r, 2, HEAD_DIM), "bf16", "pool.summary", optional=True)
 
     def c(self) -> c_pool:
         self.check()
         return c_pool(self.num_kv_heads, self.head_dim, self.logical_page, self.physical_page,
-                      self.num_phys_pages, _ptr(self.k), _ptr(self.v), _ptr(self.summary))
+                      self.num_phys_pages, _ptr(self.k), _ptr(self.v), _ptr(self.summary), self.head_slots)
 
 
 @dataclass

@@ -100,10 +100,15 @@ spa_status check_pool(const spa_pool* pool, spa::PoolArgs* out) {
   if (P / p > 64) return fail(SPA_ERR_INVALID, "physical_page / logical_page = %d exceeds 64", P / p);
   if (pool->num_phys_pages < 1) return fail(SPA_ERR_INVALID, "num_phys_pages %d < 1", pool->num_phys_pages);
   if (!pool->k_pool || !pool->v_pool) return fail(SPA_ERR_INVALID, "k_pool / v_pool is NULL");
-  if ((int64_t)pool->num_phys_pages * pool->num_kv_heads * (P / p) >= (int64_t)UINT32_MAX)
-    return fail(SPA_ERR_UNSUPPORTED, "pool of %d pages x %d heads x %d logical pages has 2^32 or more summary "
-                "records", pool->num_phys_pages, pool->num_kv_heads, P / p);
+  const int32_t hs = pool->head_slots == 0 ? pool->num_kv_heads : pool->head_slots;
+  if (hs < 1 || hs > pool->num_kv_heads)
+    return fail(SPA_ERR_INVALID, "head_slots %d outside [1, num_kv_heads = %d] (0: num_kv_heads)", pool->head_slots,
+                pool->num_kv_heads);
+  if ((int64_t)pool->num_phys_pages * hs * (P / p) >= (int64_t)UINT32_MAX)
+    return fail(SPA_ERR_UNSUPPORTED, "pool of %d pages x %d head slots x %d logical pages has 2^32 or more "
+                "summary records", pool->num_phys_pages, hs, P / p);
   out->hkv = pool->num_kv_heads;
+  out->hs = hs;
   out->p = p;
   out->P = P;
   out->r = P / p;
@@ -134,6 +139,9 @@ spa_status check_heads(const spa_heads* heads, const spa::PoolArgs& pl, int32_t*
     if (k) dyn->id[dyn->n++] = (int16_t)h;
   }
   if (dyn->n > 0 && !pl.summ) return fail(SPA_ERR_INVALID, "dynamic heads need pool->summary");
+  if (pl.hs < pl.hkv && (dyn->n > pl.hs || pl.hkv - dyn->n > pl.hs))
+    return fail(SPA_ERR_INVALID, "head_slots %d holds neither the %d dynamic nor the %d streaming heads", pl.hs,
+                dyn->n, pl.hkv - dyn->n);
   *G = g;
   return SPA_OK;
 }
@@ -167,7 +175,21 @@ void ring_geometry(const spa_heads* heads, int32_t P, int32_t* sink_pages, int32
 
 // Completes the batch's ring geometry (streaming heads kept in a ring when
 // stream_pages is given), which needs the head kinds.
+// A compact pool (fewer head slots than heads) keeps streaming heads in rings
+// only, so its calls need the head kinds and, with streaming heads, the rings.
+bool has_streaming(const spa_heads* heads, int32_t hkv) {
+  for (int32_t h = 0; h < hkv; ++h)
+    if (!heads->kind[h]) return true;
+  return false;
+}
+
 spa_status set_ring(const spa_heads* heads, const spa::PoolArgs& pl, spa::BatchArgs* bt) {
+  if (pl.hs < pl.hkv) {
+    if (!heads) return fail(SPA_ERR_INVALID, "a pool with head_slots < num_kv_heads needs the head kinds");
+    if (!bt->ring && has_streaming(heads, pl.hkv))
+      return fail(SPA_ERR_INVALID, "a pool with head_slots < num_kv_heads keeps streaming heads in rings: "
+                  "stream_pages is NULL");
+  }
   if (!bt->ring) return SPA_OK;
   if (!heads) return fail(SPA_ERR_INVALID, "stream_pages needs the head kinds (heads is NULL)");
   ring_geometry(heads, pl.P, &bt->ring_sink, &bt->ring_win);
@@ -327,6 +349,12 @@ spa_status spa_kv_pool_write(const spa_pool* pool, const spa_heads* heads, const
     return fail(SPA_ERR_INVALID, "tokens [%lld, %lld) exceed max_pages * physical_page = %lld",
                 (long long)start, (long long)(start + count), (long long)max_pages * pl.P);
   int32_t ring_sink = 0, ring_win = 1;
+  if (pl.hs < pl.hkv) {
+    if (!heads) return fail(SPA_ERR_INVALID, "a pool with head_slots < num_kv_heads needs the head kinds");
+    if (stream_base < 0 && has_streaming(heads, pl.hkv))
+      return fail(SPA_ERR_INVALID, "a pool with head_slots < num_kv_heads keeps streaming heads in rings: "
+                  "stream_base < 0");
+  }
   if (stream_base >= 0) {
     if (!heads) return fail(SPA_ERR_INVALID, "stream_base needs the head kinds (heads is NULL)");
     ring_geometry(heads, pl.P, &ring_sink, &ring_win);

@@ -77,7 +77,7 @@ __device__ __forceinline__ void issue_half(const PoolArgs& pl, int32_t h, const 
   }
   const int lane = threadIdx.x & 63;
   const int row = lane & 15, quad = lane >> 4;
-  const int64_t head = (int64_t)blk.phys * pl.hkv + h;
+  const int64_t head = (int64_t)blk.phys * pl.hs + h;     // h: the head's slot in its page
   const int32_t in_page = blk.t0 & (PG - 1);
   const uint16_t* kbase = pl.k + (head * pl.P + blk.lp * PG + in_page) * kHeadDim;
   const uint16_t* vbase = pl.v + (head * pl.r + blk.lp) * (int64_t)(kHeadDim * PG) + in_page;
@@ -434,7 +434,7 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
   // Every launch argument the kernel uses, read into registers in one round:
   // left to itself the compiler fetches each argument just before its first
   // use, one dependent scalar-memory round trip at a time.
-  asm volatile("" ::"s"(pl.hkv), "s"(pl.P), "s"(pl.N), "s"(bt.max_pp), "s"(plan.items_stream),
+  asm volatile("" ::"s"(pl.hkv), "s"(pl.hs), "s"(pl.P), "s"(pl.N), "s"(bt.max_pp), "s"(plan.items_stream),
                "s"(plan.items_dyn), "s"(plan.item_stride), "s"(plan.items_per_seq), "s"(plan.sink),
                "s"(plan.window), "s"(plan.k_max),
                "s"(G), "s"(plan.dyn_mask[0]), "s"(plan.dyn_mask[1]), "s"(plan.dyn_mask[2]),
@@ -456,7 +456,8 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
     const int32_t n_it = mask.dynamic(ah) ? plan.items_dyn : plan.items_stream;
     token_partial(pl, bt, ab, ah, G, plan.item_stride, n_it, q, reinterpret_cast<const uint16_t*>(k_new), v_new,
                   part_o, part_ml, RING && !mask.dynamic(ah));
-    append_token(pl, bt, ab, ah, k_new, v_new, mask.dynamic(ah), RING && !mask.dynamic(ah));
+    append_token(pl, bt, ab, ah, head_slot(pl, ah, mask.below(ah), mask.dynamic(ah)), k_new, v_new,
+                 mask.dynamic(ah), RING && !mask.dynamic(ah));
     return;
   }
   const int32_t item = (int32_t)blockIdx.x;
@@ -554,7 +555,7 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
     v_end = (L - src.ls_floor + kBlockTokens - 1) / kBlockTokens;   // any length: chunks of BPI
   }
   for (int32_t v0 = v_begin; v0 < v_end; v0 += BPI)
-    run_blocks<PG, BPI, DEPTH, RING>(pl, bt, pt_row, bt.max_pp, h, src, page, page_phys, plan.use_phys != 0, v0, v_end,
+    run_blocks<PG, BPI, DEPTH, RING>(pl, bt, pt_row, bt.max_pp, head_slot(pl, h, mask.below(h), dynamic), src, page, page_phys, plan.use_phys != 0, v0, v_end,
                                qb, st);
 
   // fold the four token quads of the running sum, store the partial

@@ -24,7 +24,8 @@ __global__ void __launch_bounds__(64) append_kernel(PoolArgs pl, BatchArgs bt,
   const int32_t b = blockIdx.x / pl.hkv, h = blockIdx.x % pl.hkv;
   bool is_dyn = false;
   for (int32_t d = 0; d < dyn.n; ++d) is_dyn |= dyn.id[d] == h;
-  append_token(pl, bt, b, h, k_new, v_new, with_summary && is_dyn, bt.ring != nullptr && !is_dyn);
+  append_token(pl, bt, b, h, head_slot(pl, h, dyn_rank(dyn, h), is_dyn), k_new, v_new, with_summary && is_dyn,
+               bt.ring != nullptr && !is_dyn);
 }
 
 // Bulk write of tokens [start, start + count) of one sequence (prefill), one
@@ -64,6 +65,10 @@ __global__ void __launch_bounds__(64) write_kernel(PoolArgs pl, const int32_t* _
   }
   if (phys < 0 || phys >= pl.N) return;
   const int32_t lp = (int32_t)(j % pl.r);
+  int32_t below = 0;
+#pragma unroll
+  for (int w = 0; w < kMaxKvHeads / 32; ++w) below += __popc(dyn.w[w] & (32 * w + 32 <= h ? ~0u : 32 * w >= h ? 0u : (1u << (h - 32 * w)) - 1u));
+  const int32_t hsl = head_slot(pl, h, below, dynamic);
   const int lane = threadIdx.x;
   uint32_t kw[PG], vw[PG];
 #pragma unroll
@@ -73,8 +78,8 @@ __global__ void __launch_bounds__(64) write_kernel(PoolArgs pl, const int32_t* _
     kw[u] = k[row * 64 + lane];
     vw[u] = v[row * 64 + lane];
   }
-  uint32_t* kd = reinterpret_cast<uint32_t*>(pl.k + k_row(pl, phys, h, lp * PG) * kHeadDim) + lane;
-  uint16_t* vd = pl.v + v_page(pl, phys, h, lp);   // [D][PG]
+  uint32_t* kd = reinterpret_cast<uint32_t*>(pl.k + k_row(pl, phys, hsl, lp * PG) * kHeadDim) + lane;
+  uint16_t* vd = pl.v + v_page(pl, phys, hsl, lp);   // [D][PG]
   if (lo == t0 && hi == t0 + PG) {
 #pragma unroll
     for (int u = 0; u < PG; ++u) kd[u * 64] = kw[u];
@@ -114,7 +119,7 @@ __global__ void __launch_bounds__(64) write_kernel(PoolArgs pl, const int32_t* _
       lo1 = min(lo1, y); hi1 = max(hi1, y);
     }
   }
-  uint32_t* sp = reinterpret_cast<uint32_t*>(pl.summ + summ_page(pl, phys, h, lp));
+  uint32_t* sp = reinterpret_cast<uint32_t*>(pl.summ + summ_page(pl, phys, hsl, lp));
   sp[lane] = (uint32_t)from_key(lo0) | ((uint32_t)from_key(lo1) << 16);
   sp[kHeadDim / 2 + lane] = (uint32_t)from_key(hi0) | ((uint32_t)from_key(hi1) << 16);
 }
@@ -126,7 +131,8 @@ template <int PG>
 __global__ void __launch_bounds__(64) summary_kernel(PoolArgs pl, BatchArgs bt, HeadList dyn,
                                                      const int32_t* __restrict__ first_pos,
                                                      int32_t max_tokens) {
-  const int32_t b = blockIdx.y / dyn.n, h = dyn.id[blockIdx.y % dyn.n];
+  const int32_t b = blockIdx.y / dyn.n, k = blockIdx.y % dyn.n, h = dyn.id[k];
+  const int32_t hsl = head_slot(pl, h, k, true);     // (the list is in ascending head order)
   const int32_t L = clamp_len(bt, b, pl.P);
   if (L < 1) return;
   int32_t f = first_pos ? first_pos[b] : L - 1;
@@ -140,7 +146,7 @@ __global__ void __launch_bounds__(64) summary_kernel(PoolArgs pl, BatchArgs bt, 
   const int32_t lp = j % pl.r;
   const int32_t n = min(PG, L - j * PG);            // valid tokens of the page
   const int lane = threadIdx.x;
-  const uint32_t* kr = reinterpret_cast<const uint32_t*>(pl.k + k_row(pl, phys, h, lp * PG) * kHeadDim) + lane;
+  const uint32_t* kr = reinterpret_cast<const uint32_t*>(pl.k + k_row(pl, phys, hsl, lp * PG) * kHeadDim) + lane;
   uint32_t w[PG];
 #pragma unroll
   for (int u = 0; u < PG; ++u) w[u] = kr[min(u, n - 1) * 64];   // rows past the valid ones repeat the last
@@ -151,7 +157,7 @@ __global__ void __launch_bounds__(64) summary_kernel(PoolArgs pl, BatchArgs bt, 
     lo0 = min(lo0, x); hi0 = max(hi0, x);
     lo1 = min(lo1, y); hi1 = max(hi1, y);
   }
-  uint32_t* sp = reinterpret_cast<uint32_t*>(pl.summ + summ_page(pl, phys, h, lp));
+  uint32_t* sp = reinterpret_cast<uint32_t*>(pl.summ + summ_page(pl, phys, hsl, lp));
   sp[lane] = (uint32_t)from_key(lo0) | ((uint32_t)from_key(lo1) << 16);
   sp[kHeadDim / 2 + lane] = (uint32_t)from_key(hi0) | ((uint32_t)from_key(hi1) << 16);
 }

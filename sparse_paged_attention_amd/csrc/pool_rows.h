@@ -16,14 +16,27 @@
 namespace spa {
 namespace {
 
-__device__ __forceinline__ int64_t k_row(const PoolArgs& pl, int32_t phys, int32_t h, int32_t slot) {
-  return ((int64_t)phys * pl.hkv + h) * pl.P + slot;                 // row of D elements
+// hsl: the head's slot in its physical page (head_slot)
+__device__ __forceinline__ int64_t k_row(const PoolArgs& pl, int32_t phys, int32_t hsl, int32_t row) {
+  return ((int64_t)phys * pl.hs + hsl) * pl.P + row;                  // row of D elements
 }
-__device__ __forceinline__ int64_t v_page(const PoolArgs& pl, int32_t phys, int32_t h, int32_t lp) {
-  return (((int64_t)phys * pl.hkv + h) * pl.r + lp) * (int64_t)kHeadDim * pl.p;
+__device__ __forceinline__ int64_t v_page(const PoolArgs& pl, int32_t phys, int32_t hsl, int32_t lp) {
+  return (((int64_t)phys * pl.hs + hsl) * pl.r + lp) * (int64_t)kHeadDim * pl.p;
 }
-__device__ __forceinline__ int64_t summ_page(const PoolArgs& pl, int32_t phys, int32_t h, int32_t lp) {
-  return (((int64_t)phys * pl.hkv + h) * pl.r + lp) * (int64_t)(2 * kHeadDim);
+__device__ __forceinline__ int64_t summ_page(const PoolArgs& pl, int32_t phys, int32_t hsl, int32_t lp) {
+  return (((int64_t)phys * pl.hs + hsl) * pl.r + lp) * (int64_t)(2 * kHeadDim);
+}
+// Slot of KV head h in its physical page: h, or, when pages hold fewer slots
+// than heads (compact layout), its rank among the heads of its kind.
+// dyn_below: dynamic heads with an index below h.
+__device__ __forceinline__ int32_t head_slot(const PoolArgs& pl, int32_t h, int32_t dyn_below, bool dynamic) {
+  return pl.hs == pl.hkv ? h : (dynamic ? dyn_below : h - dyn_below);
+}
+// Dynamic heads below h in an ascending head list.
+__device__ __forceinline__ int32_t dyn_rank(const HeadList& dyn, int32_t h) {
+  int32_t n = 0;
+  for (int32_t d = 0; d < dyn.n; ++d) n += dyn.id[d] < h;
+  return n;
 }
 __device__ __forceinline__ int32_t clamp_len(const BatchArgs& bt, int32_t b, int32_t P) {
   int32_t L = bt.lens[b];
@@ -54,10 +67,10 @@ __device__ __forceinline__ uint16_t from_key(uint32_t k) {
 // l owns channels 2l and 2l+1. With `summary`, the same wave rebuilds the
 // summary of the logical page receiving the token: min and max over the
 // page's earlier tokens (read from the pool, 16 rows per batch of loads) and
-// the new key. `in_ring`: a streaming head kept in the sequence's ring.
-// k_new / v_new: bf16 [B][H_kv][D].
+// the new key. `in_ring`: a streaming head kept in the sequence's ring; hsl:
+// the head's slot in its page. k_new / v_new: bf16 [B][H_kv][D].
 __device__ __forceinline__ void append_token(const PoolArgs& pl, const BatchArgs& bt, int32_t b, int32_t h,
-                                             const uint32_t* __restrict__ k_new,
+                                             int32_t hsl, const uint32_t* __restrict__ k_new,
                                              const uint16_t* __restrict__ v_new, bool summary, bool in_ring) {
   const int32_t L = clamp_len(bt, b, pl.P);
   if (L < 1) return;
@@ -68,9 +81,9 @@ __device__ __forceinline__ void append_token(const PoolArgs& pl, const BatchArgs
   const int lane = threadIdx.x & 63;
   const int64_t src = ((int64_t)b * pl.hkv + h) * kHeadDim;
   const uint32_t kw = k_new[src / 2 + lane];
-  uint16_t* krow0 = pl.k + k_row(pl, phys, h, lp * pl.p) * kHeadDim;   // first token of the page
+  uint16_t* krow0 = pl.k + k_row(pl, phys, hsl, lp * pl.p) * kHeadDim;   // first token of the page
   reinterpret_cast<uint32_t*>(krow0 + (int64_t)i * kHeadDim)[lane] = kw;
-  uint16_t* vp = pl.v + v_page(pl, phys, h, lp);
+  uint16_t* vp = pl.v + v_page(pl, phys, hsl, lp);
   vp[(2 * lane) * pl.p + i] = v_new[src + 2 * lane];
   vp[(2 * lane + 1) * pl.p + i] = v_new[src + 2 * lane + 1];
   if (!summary) return;
@@ -88,7 +101,7 @@ __device__ __forceinline__ void append_token(const PoolArgs& pl, const BatchArgs
       lo1 = min(lo1, c); hi1 = max(hi1, c);
     }
   }
-  uint32_t* sp = reinterpret_cast<uint32_t*>(pl.summ + summ_page(pl, phys, h, lp));
+  uint32_t* sp = reinterpret_cast<uint32_t*>(pl.summ + summ_page(pl, phys, hsl, lp));
   sp[lane] = (uint32_t)from_key(lo0) | ((uint32_t)from_key(lo1) << 16);
   sp[kHeadDim / 2 + lane] = (uint32_t)from_key(hi0) | ((uint32_t)from_key(hi1) << 16);
 }

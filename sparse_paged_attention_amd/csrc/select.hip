@@ -198,12 +198,14 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
     const int32_t ab = w / pl.hkv, ah = w - ab * pl.hkv;
     bool is_dyn = false;
     for (int32_t d = 0; d < dyn.n; ++d) is_dyn |= dyn.id[d] == ah;
-    append_token(pl, bt, ab, ah, k_new, v_new, is_dyn, bt.ring != nullptr && !is_dyn);
+    append_token(pl, bt, ab, ah, head_slot(pl, ah, dyn_rank(dyn, ah), is_dyn), k_new, v_new, is_dyn,
+                 bt.ring != nullptr && !is_dyn);
     return;
   }
   static_assert(S::OFFS <= 192, "three page offsets per lane");
   __shared__ uint32_t offs[S::OFFS];
   const int32_t b = blockIdx.y / dyn.n, h = dyn.id[blockIdx.y % dyn.n];
+  const int32_t hsl = head_slot(pl, h, blockIdx.y % dyn.n, true);   // (the list is in ascending head order)
   const int32_t L = clamp_len(bt, b, pl.P);
   const int32_t n = (L + pl.p - 1) / pl.p;
   const int32_t base = blockIdx.x * S::RANGE;
@@ -223,7 +225,7 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
     if (i < S::OFFS) {
       const int32_t phys = pt_row[min(j / pl.r, bt.max_pp - 1)];
       const bool ok = j < n && phys >= 0 && phys < pl.N;
-      offs[i] = ok ? (uint32_t)(((int64_t)phys * pl.hkv + h) * pl.r + j % pl.r) : ~0u;
+      offs[i] = ok ? (uint32_t)(((int64_t)phys * pl.hs + hsl) * pl.r + j % pl.r) : ~0u;
     }
   }
 

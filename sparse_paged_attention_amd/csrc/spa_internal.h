@@ -14,13 +14,15 @@ constexpr int kMaxKvHeads = 128;
 // Pool geometry and base pointers, passed by value to every kernel.
 struct PoolArgs {
   int32_t hkv;      // KV heads
+  int32_t hs;       // head slots per physical page: hkv, or fewer when the page table's pages hold the
+                    // dynamic heads and the streaming heads' rings the streaming heads (slot = rank in kind)
   int32_t p;        // logical page (tokens)
   int32_t P;        // physical page (tokens)
   int32_t r;        // P / p
   int32_t N;        // physical pages
-  uint16_t* k;      // [N][hkv][P][D]
-  uint16_t* v;      // [N][hkv][r][D][p]
-  uint16_t* summ;   // [N][hkv][r][2][D]
+  uint16_t* k;      // [N][hs][P][D]
+  uint16_t* v;      // [N][hs][r][D][p]
+  uint16_t* summ;   // [N][hs][r][2][D]
 };
 
 struct BatchArgs {

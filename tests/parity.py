@@ -41,7 +41,8 @@ class ParityRun:
     """A workload on the GPU plus the oracle state needed to check it."""
 
     def __init__(self, wl: W.Workload, check_heads=None, threads: int = 16, strict_ties: bool = False,
-                 resolve_at_selection: bool = True, fused: bool = False, window_only: bool = False):
+                 resolve_at_selection: bool = True, fused: bool = False, window_only: bool = False,
+                 compact: bool = False):
         self.wl = wl
         self.fused = fused               # the append runs inside the selection / attention launches
         self.strict_ties = strict_ties
@@ -51,7 +52,7 @@ class ParityRun:
         self.layer = DecodeLayer(hq=wl.hq, hkv=wl.hkv, p=wl.p, P=wl.P, kind=wl.kind, sink=wl.sink,
                                  window=wl.window, page_table=pt, num_phys_pages=wl.num_phys_pages,
                                  k_max=wl.k_max, resolve_at_selection=resolve_at_selection,
-                                 window_only=window_only)
+                                 window_only=window_only or compact, compact=compact)
         self.K, self.V = {}, {}          # host bits of the checked (b, h) slices
         self.new_k, self.new_v = [], []  # per sequence: [H_kv][steps][D] appended tokens
         need = {(b, h) for b, h in self.check}

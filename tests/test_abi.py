@@ -200,6 +200,29 @@ def test_window_only_storage_validation(spa):
                                FAKE, None) == 0
 
 
+def test_compact_pool_validation(spa):
+    """head_slots: 0 or H_kv (one slot per head), or a compact layout holding
+    the larger of the two head kinds, which needs the head kinds and rings."""
+    L = spa.lib()
+    heads = mkheads(spa)                                     # 4 streaming + 4 dynamic heads
+    plain = mkbatch(spa)
+    ringed = spa.c_batch(1, 4, FAKE, FAKE, FAKE)
+    assert attn(spa, mkpool(spa, head_slots=9), heads, plain) == 1          # more slots than heads
+    assert attn(spa, mkpool(spa, head_slots=-1), heads, plain) == 1
+    assert attn(spa, mkpool(spa, num_phys_pages=100, head_slots=3), heads, ringed) == 1   # 4 heads of a kind
+    assert attn(spa, mkpool(spa, num_phys_pages=100, head_slots=4), heads, plain) == 1    # no rings
+    assert L.spa_kv_pool_append(ctypes.byref(mkpool(spa, num_phys_pages=100, head_slots=4)), None,
+                                ctypes.byref(ringed), FAKE, FAKE, None) == 1               # no head kinds
+    compact = mkpool(spa, num_phys_pages=100, head_slots=4)
+    assert L.spa_kv_pool_write(ctypes.byref(compact), ctypes.byref(heads), FAKE, 4, -1, 0, 1, FAKE, FAKE,
+                               None) == 1                                                  # no ring base
+    assert L.spa_kv_pool_write(ctypes.byref(compact), ctypes.byref(heads), FAKE, 4, 50, 0, 0, FAKE, FAKE,
+                               None) == 0
+    all_dyn = mkheads(spa, kind=(1,) * 8)                    # no streaming head: no rings needed
+    assert L.spa_kv_pool_write(ctypes.byref(mkpool(spa, head_slots=8)), ctypes.byref(all_dyn), FAKE, 4, -1, 0, 0,
+                               FAKE, FAKE, None) == 0
+
+
 def test_attn_blocks_per_item_setting(spa):
     """Accepted item sizes round-trip; anything else is rejected up front."""
     lib = spa.lib()

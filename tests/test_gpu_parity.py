@@ -20,10 +20,11 @@ def gpu():
     oracle.build()
 
 
-def run(wl, steps=None, check=None, fused=False, window_only=False):
+def run(wl, steps=None, check=None, fused=False, window_only=False, compact=False):
     log(f"[parity] {wl.name} B={wl.batch} hq={wl.hq} hkv={wl.hkv} p={wl.p} P={wl.P} "
-        f"contexts={wl.contexts[:4]} steps={wl.steps if steps is None else steps} window_only={window_only}")
-    pr = ParityRun(wl, check_heads=check, fused=fused, window_only=window_only)
+        f"contexts={wl.contexts[:4]} steps={wl.steps if steps is None else steps} window_only={window_only} "
+        f"compact={compact}")
+    pr = ParityRun(wl, check_heads=check, fused=fused, window_only=window_only, compact=compact)
     reps = pr.run(steps)
     assert_reports(reps)
     return pr, reps
@@ -298,6 +299,38 @@ def test_window_only_matches_page_table_layout():
     k = b.layer.pool.k[torch.from_numpy(used).cuda()][:, stream]
     v = b.layer.pool.v[torch.from_numpy(used).cuda()][:, stream]
     assert not k.view(torch.int16).any() and not v.view(torch.int16).any()
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("case", list(WINDOW_ONLY_CASES))
+def test_compact_pool(case, fused):
+    """The compact layout of window-only storage: the page table's pages hold
+    only the dynamic heads and the rings only the streaming heads (each in its
+    rank among the heads of its kind); the same results as the oracle."""
+    run(WINDOW_ONLY_CASES[case](), fused=fused, compact=True)
+
+
+def test_compact_pool_matches_page_table_layout():
+    """The compact pool gives, step by step, the page-table layout's outputs,
+    lse and selections bit for bit, with half the head slots per page."""
+    wl = W.WORKLOADS["llama3_128k"].scaled(contexts=(4100, 3001, 1000, 17), steps=9, budget=512, window=300)
+    log(f"[parity] compact vs page table {wl.name} contexts={wl.contexts}")
+    a = ParityRun(wl, check_heads=[], fused=True)
+    b = ParityRun(wl, check_heads=[], fused=True, compact=True)
+    assert b.layer.pool.k.shape[1] * 2 == a.layer.pool.k.shape[1]
+    for i in range(wl.steps):
+        a.run_step(i)
+        b.run_step(i)
+        for x, y, what in ((a.layer.out, b.layer.out, "out"), (a.layer.lse, b.layer.lse, "lse"),
+                           (a.layer.sel_pages, b.layer.sel_pages, "sel_pages"),
+                           (a.layer.sel_count, b.layer.sel_count, "sel_count")):
+            assert torch.equal(x, y), f"step {i}: {what} differs"
+
+
+def test_compact_pool_128k_full_size_sampled():
+    """The benchmark's configuration at full size in the compact layout (half
+    the pool), the benchmark's launches, sampled heads."""
+    run(W.WORKLOADS["llama3_128k"], check=[(0, 1), (1, 6), (2, 4), (3, 3)], fused=True, compact=True)
 
 
 def test_window_only_128k_full_size_sampled():

@@ -122,9 +122,10 @@ def main() -> int:
     ap.add_argument("--replicas", type=int, default=8, help="layer replicas the steps cycle over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--threads", type=int, default=16)
-    ap.add_argument("--storage", choices=("ring", "table"), default="table",
-                    help="streaming heads' tokens: in a ring of sink + window pages per sequence "
-                         "(window-only storage), or in the page table's pages like the dynamic heads")
+    ap.add_argument("--storage", choices=("table", "ring", "compact"), default="table",
+                    help="streaming heads' tokens: in the page table's pages like the dynamic heads, in a "
+                         "ring of sink + window pages per sequence (window-only storage), or in rings with "
+                         "the compact pool (page-table pages hold the dynamic heads only)")
     ap.add_argument("--probe", action="store_true",
                     help="counter-collection mode: run the steps eagerly, then a plain copy of "
                          "COPY_BYTES for calibration; prints no result line")
@@ -153,7 +154,8 @@ def main() -> int:
     pt = W.page_table(wl)
     layers = [DecodeLayer(hq=wl.hq, hkv=wl.hkv, p=wl.p, P=wl.P, kind=wl.kind, sink=wl.sink,
                           window=wl.window, page_table=pt, num_phys_pages=wl.num_phys_pages,
-                          k_max=wl.k_max, window_only=args.storage == "ring") for _ in range(R)]
+                          k_max=wl.k_max, window_only=args.storage != "table",
+                          compact=args.storage == "compact") for _ in range(R)]
     host_kv = []
     write_events = []
     newk = np.zeros((wl.steps, wl.batch, wl.hkv, wl.d), np.uint16)
@@ -309,8 +311,10 @@ def main() -> int:
                                f"(sink 64 + window 2048), kv 4-7 dynamic budget 4096, select every 4 "
                                f"steps, {R} layer replicas",
                    "batch": wl.batch, "context": wl.contexts[0], "replicas": R,
-                   "streaming_storage": "ring of sink + window pages per sequence" if args.storage == "ring"
-                   else "page table"},
+                   "streaming_storage": {"table": "page table", "ring": "ring of sink + window pages per sequence",
+                                         "compact": "rings, page-table pages holding the dynamic heads only"}[
+                       args.storage],
+                   "pool_gib_per_layer": round(layers[0].pool.k.numel() * 2 * 2 / 2**30, 3)},
         "achieved_GBps": round(gbps, 1),
         "hbm_frac": round(gbps / PEAK_GBPS, 4),
         "bytes_per_step": int(bytes_per_step),

@@ -1,0 +1,41 @@
+"""The algorithmic byte counts the benchmark divides by its times, against the
+closed form of the 128K workload (4 sequences, 32 query / 8 KV heads, d 128,
+logical pages of 16 in physical pages of 64, 4 streaming heads with sink 64 +
+window 2048, 4 dynamic heads keeping 256 pages of 16 tokens), written out here
+term by term."""
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import workloads as W  # noqa: E402
+
+ROW = 128 * 2            # one bf16 key or value row
+
+
+def test_attention_bytes_at_128k():
+    wl = W.WORKLOADS["llama3_128k"]
+    L = 131072 + 15                                    # the last decode step's length
+    kv = 4 * (4 * (64 + 2048) + 4 * 256 * 16) * 2 * ROW  # streaming and dynamic tokens, K and V rows
+    q = 4 * 32 * ROW
+    out = 4 * 32 * (128 * 4 + 4)                       # fp32 output rows and lse
+    sel = 4 * 4 * 256 * 4                              # selected page ids
+    pt = 4 * (L // 64 + 1) * 4                         # page-table entries
+    assert bench.algorithmic_bytes(wl, L, False)["attn"] == kv + q + out + sel + pt == 51003920
+
+
+def test_selection_and_write_bytes_at_128k():
+    wl = W.WORKLOADS["llama3_128k"]
+    L = 131072
+    n = L // 16                                        # logical pages (L is a multiple of 16 here)
+    summaries = 4 * 4 * n * 2 * ROW                    # min and max rows of every page of each dynamic head
+    scores = 4 * 4 * n * 4 * 2                         # fp32 scores written and read back
+    sel = bench.algorithmic_bytes(wl, L, True)["select"]
+    assert sel == summaries + 4 * 32 * ROW + scores + 4 * 4 * 256 * 4
+    count = 131071                                     # one prompt
+    rows = 2 * 2 * 8 * count * ROW                     # K and V rows of 8 heads, read and written
+    summaries_written = 4 * 8192 * 2 * ROW             # 8192 logical pages of each dynamic head
+    page_table = 2048 * 4                              # physical pages of the prompt
+    assert bench.bulk_write_bytes(wl, count) == rows + summaries_written + page_table == 1090519040

@@ -42,13 +42,13 @@ class ParityRun:
 
     def __init__(self, wl: W.Workload, check_heads=None, threads: int = 16, strict_ties: bool = False,
                  resolve_at_selection: bool = True, fused: bool = False, window_only: bool = False,
-                 compact: bool = False):
+                 compact: bool = False, page_table=None):
         self.wl = wl
         self.fused = fused               # the append runs inside the selection / attention launches
         self.strict_ties = strict_ties
         self.check = check_heads if check_heads is not None else \
             [(b, h) for b in range(wl.batch) for h in range(wl.hkv)]
-        pt = W.page_table(wl)
+        pt = W.page_table(wl) if page_table is None else page_table
         self.layer = DecodeLayer(hq=wl.hq, hkv=wl.hkv, p=wl.p, P=wl.P, kind=wl.kind, sink=wl.sink,
                                  window=wl.window, page_table=pt, num_phys_pages=wl.num_phys_pages,
                                  k_max=wl.k_max, resolve_at_selection=resolve_at_selection,

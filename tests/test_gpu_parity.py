@@ -254,6 +254,39 @@ def test_graph_replay_matches_eager():
     assert_reports(pr2.run())
 
 
+def test_pages_mapped_from_the_free_list_as_sequences_grow():
+    """The serving flow: each sequence's prompt pages come from the host free
+    list (spa_alloc_*), and a new physical page is taken and entered into the
+    device page table exactly when a step's token opens it (every sequence
+    crosses a page boundary during the steps; the entries of earlier pages,
+    which selections refer to, never change). Checked against the oracle every
+    step; all pages go back to the free list at the end."""
+    import sparse_paged_attention_amd as spa
+    wl = W.WORKLOADS["llama3_128k"].scaled(contexts=(1020, 126, 2047, 64), steps=12, budget=512, window=300,
+                                           permute=False)
+    P = wl.P
+    alloc = spa.Allocator(wl.num_phys_pages)
+    pt = np.full((wl.batch, wl.max_pages), -1, np.int32)
+    for b in range(wl.batch):
+        n = -(-(wl.contexts[b] - 1) // P)
+        pt[b, :n] = alloc.alloc(n)
+    log(f"[parity] pages from the free list {wl.name} contexts={wl.contexts}")
+    pr = ParityRun(wl, fused=True, page_table=pt)
+    opened = 0
+    for i in range(wl.steps):
+        for b in range(wl.batch):
+            t = wl.seq_len(b, i) - 1
+            if t % P == 0:                       # the token opens a physical page
+                assert pt[b, t // P] == -1
+                pt[b, t // P] = alloc.alloc(1)[0]
+                pr.layer.page_table[b, t // P] = int(pt[b, t // P])
+                opened += 1
+        assert_reports([pr.run_step(i)])
+    assert opened == wl.batch
+    alloc.free([int(x) for x in pt[pt >= 0]])
+    assert alloc.num_free == wl.num_phys_pages
+
+
 # ------------------------------------------ window-only streaming storage
 
 WINDOW_ONLY_CASES = {

@@ -5,7 +5,7 @@ Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 never does, and the two share no code.
 
 This module is a thin ctypes layer over ``spa_oracle.c`` (plain C, fp64
-attention, exact page scores). Each wrapper takes and returns numpy arrays in
+attention, exact page scores, the E4M3 quantizer of fp8 pages). Each wrapper takes and returns numpy arrays in
 logical (position) order; bf16 values travel as uint16 bit patterns.
 """
 from __future__ import annotations
@@ -74,8 +74,19 @@ def lib():
         L.orc_decode_heads.argtypes = [i32, ctypes.POINTER(OrcJob)]
         L.orc_decode_heads.restype = i32
         L.orc_num_threads.restype = i32
+        L.orc_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_value.restype = ctypes.c_double
+        L.orc_e4m3_encode.argtypes = [vp, i64, vp]
+        L.orc_quantize_rows.argtypes = [vp, i64, i32, vp, vp]
+        L.orc_bf16_round_outward.argtypes = [vp, i64, i32, vp]
+        L.orc_page_summary_q8.argtypes = [vp, vp, i64, i32, i32, vp, vp]
+        L.orc_attend_q8.argtypes = [vp, vp, vp, vp, vp, i64, i32, vp, vp, vp]
+        L.orc_decode_head_q8.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32,
+                                         i32, i64, i32, vp, i64, vp, vp, vp, vp, vp]
         for name in ("orc_page_summary", "orc_page_scores", "orc_topk", "orc_attend",
-                     "orc_decode_head"):
+                     "orc_decode_head", "orc_e4m3_encode", "orc_quantize_rows",
+                     "orc_bf16_round_outward", "orc_page_summary_q8", "orc_attend_q8",
+                     "orc_decode_head_q8"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -224,6 +235,97 @@ def decode_heads(jobs: list[dict]) -> list[tuple[np.ndarray, np.ndarray]]:
         bad = [(i, arr[i].rc) for i in range(len(jobs)) if arr[i].rc]
         raise OracleError(f"{failed} oracle jobs failed: {bad[:4]}")
     return results
+
+
+# ------------------------------------------------------------------ fp8 pages
+
+def e4m3_value(code: int) -> float:
+    """Value of one OCP E4M3 code (NaN for 0x7F and 0xFF)."""
+    return lib().orc_e4m3_value(code)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """float32 array -> uint8 E4M3 codes (nearest, ties to even, saturating at 448)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint8)
+    _check(lib().orc_e4m3_encode(_ptr(x), x.size, _ptr(out)), "e4m3_encode")
+    return out
+
+
+def quantize_rows(X: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """X: uint16 bf16 [L][D] -> (codes uint8 [L][D], scales float32 [L])."""
+    X = _u16(X)
+    L, D = X.shape
+    codes = np.empty((L, D), np.uint8)
+    scales = np.empty(max(L, 1), np.float32)
+    _check(lib().orc_quantize_rows(_ptr(X), L, D, _ptr(codes), _ptr(scales)), "quantize_rows")
+    return codes, scales[:L].copy()
+
+
+def dequantize_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """codes uint8 [L][D], scales [L] -> fp64 [L][D] (code value x scale, exact)."""
+    table = np.array([e4m3_value(c) for c in range(256)], np.float64)
+    return table[np.asarray(codes)] * np.asarray(scales, np.float64)[:, None]
+
+
+def bf16_round_outward(x, down: bool) -> np.ndarray:
+    """fp64 array -> uint16 bf16 patterns, the largest bf16 <= x (down) or the smallest >= x."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, np.uint16)
+    _check(lib().orc_bf16_round_outward(_ptr(x), x.size, -1 if down else 1, _ptr(out)),
+           "bf16_round_outward")
+    return out
+
+
+def page_summary_q8(Kc: np.ndarray, Ks: np.ndarray, p: int):
+    """Kc uint8 [L][D], Ks float32 [L] -> (kmin, kmax) uint16 bf16 [ceil(L/p)][D]."""
+    Kc = np.ascontiguousarray(Kc, dtype=np.uint8)
+    Ks = np.ascontiguousarray(Ks, dtype=np.float32)
+    L, D = Kc.shape
+    n = -(-L // p)
+    kmin = np.empty((n, D), np.uint16)
+    kmax = np.empty((n, D), np.uint16)
+    _check(lib().orc_page_summary_q8(_ptr(Kc), _ptr(Ks), L, D, p, _ptr(kmin), _ptr(kmax)),
+           "page_summary_q8")
+    return kmin, kmax
+
+
+def attend_q8(q, Kc, Ks, Vc, Vs, mask) -> tuple[np.ndarray, float]:
+    """attend() over fp8 rows: q uint16 [D]; Kc, Vc uint8 [L][D]; Ks, Vs float32 [L]."""
+    q = _u16(q)
+    Kc, Vc = (np.ascontiguousarray(a, dtype=np.uint8) for a in (Kc, Vc))
+    Ks, Vs = (np.ascontiguousarray(a, dtype=np.float32) for a in (Ks, Vs))
+    L, D = Kc.shape
+    m = np.ascontiguousarray(mask, dtype=np.uint8)
+    out = np.empty(D, np.float64)
+    lse = np.empty(1, np.float64)
+    _check(lib().orc_attend_q8(_ptr(q), _ptr(Kc), _ptr(Ks), _ptr(Vc), _ptr(Vs), L, D, _ptr(m),
+                               _ptr(out), _ptr(lse)), "attend_q8")
+    return out, float(lse[0])
+
+
+def decode_head_q8(Kc, Ks, Vc, Vs, q, *, dynamic: bool, sink: int, window: int, p: int,
+                   budget: int, do_select: bool, state: HeadState | None = None,
+                   want_scores: bool = False):
+    """decode_head() over fp8 rows (codes uint8 [L][D], scales float32 [L])."""
+    q = _u16(q)
+    Kc, Vc = (np.ascontiguousarray(a, dtype=np.uint8) for a in (Kc, Vc))
+    Ks, Vs = (np.ascontiguousarray(a, dtype=np.float32) for a in (Ks, Vs))
+    L, D = Kc.shape
+    G = q.shape[0]
+    n = -(-L // p)
+    if state is None:
+        state = HeadState(n)
+    scores = np.full(n, np.nan, np.float32) if (want_scores and dynamic and do_select) else None
+    out = np.empty((G, D), np.float64)
+    lse = np.empty(G, np.float64)
+    rc = lib().orc_decode_head_q8(_ptr(Kc), _ptr(Ks), _ptr(Vc), _ptr(Vs), _ptr(q), L, D, G,
+                                  int(dynamic), sink, window, p, budget, int(do_select),
+                                  _ptr(state.sel), state.sel.size, _ptr(state.nsel),
+                                  _ptr(state.Ls), _ptr(scores) if scores is not None else None,
+                                  _ptr(out), _ptr(lse))
+    _check(rc, "decode_head_q8")
+    return out, lse, scores
 
 
 def num_threads() -> int:

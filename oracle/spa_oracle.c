@@ -26,6 +26,9 @@
  *   LCI "2.3 分组查询注意力 (GQA)": query head i uses KV head i/G; logits are
  *       divided by sqrt(head_dim); softmax over the keys.
  *   LCI sparse-method table (StreamingLLM row): attention sink + local window.
+ *   PAGE "5.2 参数调优指南" and the long-text article at lshu.cn, "4.2 KV Cache
+ *       Quantization（INT8/FP8）": K and V kept in fp8 (E4M3); the scale
+ *       convention is this file's reading (see the fp8 section).
  */
 #include <math.h>
 #include <stdint.h>
@@ -330,6 +333,207 @@ int orc_decode_head(const uint16_t* K, const uint16_t* V, const uint16_t* q,
                        dynamic ? *Ls : L, mask) < 0) rc = ORC_ERR_ARG;
   for (int32_t g = 0; g < G && !rc; g++)
     rc = orc_attend(q + (int64_t)g * D, K, V, L, D, mask, out + (int64_t)g * D, lse + g);
+  free(mask);
+  return rc;
+}
+
+/* ------------------------------------------------------------ fp8 pages */
+
+/* PAGE "5.2 参数调优指南" sets the KV cache precision to fp8, and the
+ * long-text article at lshu.cn ("4.2 KV Cache Quantization（INT8/FP8）")
+ * keeps K and V in the FP8 E4M3 format; neither fixes the scale. The reading
+ * taken here: OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; no infinities, S.1111.111 is NaN, largest finite 448), one fp32 scale
+ * per (token, head) row, scale = amax / 448 in fp32, code = the value x / scale
+ * (fp32 division) rounded to the nearest E4M3 value, ties to even, saturating
+ * at +-448. A row of zeros has scale 0 and all codes +0. The dequantized value
+ * is code value x scale. */
+
+/* Value of an E4M3 code (NaN for the two NaN codes). */
+double orc_e4m3_value(uint8_t code) {
+  int32_t e = (code >> 3) & 15, m = code & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m, -9);          /* subnormal: m/8 * 2^-6 */
+  else v = ldexp((double)(8 + m), e - 10);      /* (1 + m/8) * 2^(e-7) */
+  return (code & 0x80) ? -v : v;
+}
+
+/* Nearest E4M3 code of a finite x, ties to even, saturating. */
+static uint8_t e4m3_encode(double x) {
+  uint8_t sign = signbit(x) ? 0x80 : 0;
+  double a = fabs(x);
+  if (a >= 448.0) return sign | 0x7E;
+  if (a < ldexp(1.0, -6)) {
+    /* subnormal range: integer multiples of 2^-9; 8 * 2^-9 is the smallest
+     * normal, whose code is also 8 */
+    return sign | (uint8_t)nearbyint(ldexp(a, 9));
+  }
+  int32_t k;
+  frexp(a, &k);                                  /* a = f * 2^k, f in [0.5, 1) */
+  int32_t E = k - 1;                             /* a in [2^E, 2^(E+1)) */
+  int32_t m = (int32_t)nearbyint((ldexp(a, -E) - 1.0) * 8.0);
+  if (m == 8) { E += 1; m = 0; }
+  return sign | (uint8_t)(((E + 7) << 3) | m);
+}
+
+/* Codes of n fp32 values; a non-finite value is an error. */
+int orc_e4m3_encode(const float* x, int64_t n, uint8_t* out) {
+  if (!x || !out || n < 0) return ORC_ERR_ARG;
+  for (int64_t i = 0; i < n; i++) {
+    if (!isfinite(x[i])) return ORC_ERR_NONFINITE;
+    out[i] = e4m3_encode((double)x[i]);
+  }
+  return ORC_OK;
+}
+
+/* Quantizes L rows of D bf16 values (X [L][D]) into codes [L][D] and one
+ * scale per row, as stated above. */
+int orc_quantize_rows(const uint16_t* X, int64_t L, int32_t D, uint8_t* codes,
+                      float* scales) {
+  if (!X || !codes || !scales || L < 0 || D < 1) return ORC_ERR_ARG;
+  for (int64_t t = 0; t < L; t++) {
+    float amax = 0.0f;
+    for (int32_t c = 0; c < D; c++) {
+      uint16_t b = X[t * D + c];
+      if (!bf16_finite(b)) return ORC_ERR_NONFINITE;
+      float a = (float)fabs(orc_bf16_value(b));  /* exact: a bf16 is an fp32 */
+      if (a > amax) amax = a;
+    }
+    volatile float s = amax / 448.0f;            /* one fp32 division */
+    scales[t] = s;
+    for (int32_t c = 0; c < D; c++) {
+      if (s == 0.0f) { codes[t * D + c] = 0; continue; }
+      volatile float y = (float)orc_bf16_value(X[t * D + c]) / s;
+      codes[t * D + c] = e4m3_encode((double)y);
+    }
+  }
+  return ORC_OK;
+}
+
+/* Largest bf16 <= x (x finite, within the bf16 range). */
+static uint16_t bf16_down(double x) {
+  float f = (float)x;
+  if ((double)f > x) f = nextafterf(f, -INFINITY);   /* largest fp32 <= x */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  uint16_t b = (uint16_t)(u >> 16);                  /* toward zero */
+  if ((u & 0xFFFF) && (u & 0x80000000u)) b += 1;     /* negative: one more step down */
+  return b;
+}
+
+/* Smallest bf16 >= x. */
+static uint16_t bf16_up(double x) { return bf16_down(-x) ^ 0x8000; }
+
+/* Bit patterns of bf16_down / bf16_up of n doubles (dir < 0: down, else up). */
+int orc_bf16_round_outward(const double* x, int64_t n, int32_t dir, uint16_t* out) {
+  if (!x || !out || n < 0) return ORC_ERR_ARG;
+  for (int64_t i = 0; i < n; i++) {
+    if (!isfinite(x[i])) return ORC_ERR_NONFINITE;
+    out[i] = dir < 0 ? bf16_down(x[i]) : bf16_up(x[i]);
+  }
+  return ORC_OK;
+}
+
+/* Dequantized element t, c of a code matrix [L][D] with row scales. */
+static double q8_value(const uint8_t* codes, const float* scales, int64_t t, int32_t D,
+                       int32_t c) {
+  return orc_e4m3_value(codes[t * D + c]) * (double)scales[t];   /* exact in fp64 */
+}
+
+/* PAGE "2.1" min-max pooling over the dequantized keys of fp8 pages: the
+ * channel-wise min and max of each logical page, computed exactly, then
+ * rounded outward to bf16 (min down, max up), so that a bf16 summary still
+ * bounds every key of its page. */
+int orc_page_summary_q8(const uint8_t* Kc, const float* Ks, int64_t L, int32_t D,
+                        int32_t p, uint16_t* kmin, uint16_t* kmax) {
+  if (!Kc || !Ks || !kmin || !kmax || L < 0 || D < 1 || p < 1) return ORC_ERR_ARG;
+  int64_t n = (L + p - 1) / p;
+  for (int64_t j = 0; j < n; j++) {
+    int64_t t0 = j * p, t1 = t0 + p < L ? t0 + p : L;
+    for (int32_t c = 0; c < D; c++) {
+      double lo = INFINITY, hi = -INFINITY;
+      for (int64_t t = t0; t < t1; t++) {
+        double v = q8_value(Kc, Ks, t, D, c);
+        if (!isfinite(v)) return ORC_ERR_NONFINITE;
+        if (v < lo) lo = v;
+        if (v > hi) hi = v;
+      }
+      kmin[j * D + c] = bf16_down(lo);
+      kmax[j * D + c] = bf16_up(hi);
+    }
+  }
+  return ORC_OK;
+}
+
+/* orc_attend over fp8 pages: the same softmax attention, with K_t and V_t the
+ * dequantized rows. */
+int orc_attend_q8(const uint16_t* q, const uint8_t* Kc, const float* Ks,
+                  const uint8_t* Vc, const float* Vs, int64_t L, int32_t D,
+                  const uint8_t* mask, double* out, double* lse) {
+  if (!q || !Kc || !Ks || !Vc || !Vs || !mask || !out || !lse || L < 0 || D < 1)
+    return ORC_ERR_ARG;
+  double* x = (double*)malloc(sizeof(double) * (size_t)(L ? L : 1));
+  if (!x) return ORC_ERR_ARG;
+  double m = -INFINITY;
+  for (int64_t t = 0; t < L; t++) {
+    if (!mask[t]) continue;
+    double dot = 0.0;
+    for (int32_t c = 0; c < D; c++) dot += orc_bf16_value(q[c]) * q8_value(Kc, Ks, t, D, c);
+    x[t] = dot / sqrt((double)D);
+    if (x[t] > m) m = x[t];
+  }
+  for (int32_t c = 0; c < D; c++) out[c] = 0.0;
+  if (m == -INFINITY) { *lse = -INFINITY; free(x); return ORC_OK; }
+  double den = 0.0;
+  for (int64_t t = 0; t < L; t++) {
+    if (!mask[t]) continue;
+    double w = exp(x[t] - m);
+    den += w;
+    for (int32_t c = 0; c < D; c++) out[c] += w * q8_value(Vc, Vs, t, D, c);
+  }
+  for (int32_t c = 0; c < D; c++) out[c] /= den;
+  *lse = m + log(den);
+  free(x);
+  return ORC_OK;
+}
+
+/* orc_decode_head over fp8 pages: summaries from orc_page_summary_q8, then the
+ * same scores, top-k, token set and attention (orc_attend_q8). */
+int orc_decode_head_q8(const uint8_t* Kc, const float* Ks, const uint8_t* Vc,
+                       const float* Vs, const uint16_t* q, int64_t L, int32_t D,
+                       int32_t G, int32_t dynamic, int32_t sink, int32_t window,
+                       int32_t p, int64_t budget, int32_t do_select, int32_t* sel,
+                       int64_t sel_cap, int64_t* nsel, int64_t* Ls, float* scores,
+                       double* out, double* lse) {
+  if (!Kc || !Ks || !Vc || !Vs || !q || !out || !lse || L < 1 || D < 1 || G < 1 || p < 1)
+    return ORC_ERR_ARG;
+  int rc = ORC_OK;
+  if (dynamic && do_select) {
+    if (!sel || !nsel || !Ls) return ORC_ERR_ARG;
+    int64_t n = (L + p - 1) / p;
+    uint16_t* kmin = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(n * D));
+    uint16_t* kmax = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(n * D));
+    float* s = scores ? scores : (float*)malloc(sizeof(float) * (size_t)n);
+    if (!kmin || !kmax || !s) rc = ORC_ERR_ARG;
+    if (!rc) rc = orc_page_summary_q8(Kc, Ks, L, D, p, kmin, kmax);
+    if (!rc) rc = orc_page_scores(q, G, D, kmin, kmax, n, s);
+    int64_t k = orc_pages_to_select(n, budget, p);
+    if (!rc && k > sel_cap) rc = ORC_ERR_ARG;
+    if (!rc) rc = orc_topk(s, n, k, sel);
+    if (!rc) { *nsel = k; *Ls = L; }
+    free(kmin);
+    free(kmax);
+    if (!scores) free(s);
+    if (rc) return rc;
+  }
+  uint8_t* mask = (uint8_t*)malloc((size_t)L);
+  if (!mask) return ORC_ERR_ARG;
+  if (orc_attended_set(dynamic, L, sink, window, p, sel, dynamic ? *nsel : 0,
+                       dynamic ? *Ls : L, mask) < 0) rc = ORC_ERR_ARG;
+  for (int32_t g = 0; g < G && !rc; g++)
+    rc = orc_attend_q8(q + (int64_t)g * D, Kc, Ks, Vc, Vs, L, D, mask,
+                       out + (int64_t)g * D, lse + g);
   free(mask);
   return rc;
 }

@@ -75,8 +75,8 @@ typedef struct spa_pool {
   int32_t logical_page;   /* p, tokens per logical page: 16, 32 or 64 (the write-up caps it at 64, "5.3") */
   int32_t physical_page;  /* P, tokens per physical page: a multiple of p, P/p <= 64 */
   int32_t num_phys_pages; /* N >= 1 */
-  void* k_pool;           /* device bf16 [N][S][P][D] */
-  void* v_pool;           /* device bf16 [N][S][P/p][D][p] */
+  void* k_pool;           /* device bf16 (or fp8 codes, see kv_format) [N][S][P][D] */
+  void* v_pool;           /* device bf16 (or fp8 codes) [N][S][P/p][D][p] */
   void* summary;          /* device bf16 [N][S][P/p][2][D]; may be NULL when no head is dynamic */
   /* S, head slots per physical page. 0 (or H_kv): every page holds every KV
    * head, head h in slot h. Fewer (at least the number of dynamic and of
@@ -87,7 +87,29 @@ typedef struct spa_pool {
    * the rings whenever a head is streaming. With half the heads streaming this
    * halves the pool. */
   int32_t head_slots;
+  /* Storage format of k_pool and v_pool. SPA_KV_BF16 (0): bf16 elements.
+   * SPA_KV_FP8 (1): fp8 pages -- the same layouts with one-byte OCP E4M3
+   * codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; largest
+   * finite 448) and one fp32 scale per row in k_scale / v_scale; a row's
+   * value is code value x scale. The LServe write-up ("5.2 参数调优指南")
+   * sets the KV cache to fp8 and the long-text article at lshu.cn ("4.2 KV
+   * Cache Quantization（INT8/FP8）") keeps K and V in E4M3; the scale rule is
+   * this library's: scale = amax / 448 over the row's D values (one fp32
+   * division), code = x / scale (fp32 division) rounded to the nearest E4M3
+   * value, ties to even; a row of zeros has scale 0 and codes 0. The writes
+   * (spa_kv_pool_write, spa_kv_pool_append) quantize the caller's bf16 rows;
+   * summaries stay bf16: the exact min / max of the dequantized keys rounded
+   * outward (min down, max up), so each still bounds every q.k of its page.
+   * On fp8 pools the append entry points run the append as a launch of its
+   * own ahead of the selection or the attention. Non-finite inputs give
+   * unspecified codes. */
+  int32_t kv_format;
+  float* k_scale;         /* SPA_KV_FP8: device fp32 [N][S][P], one scale per key row; else unused */
+  float* v_scale;         /* SPA_KV_FP8: device fp32 [N][S][P], one scale per value row (token); else unused */
 } spa_pool;
+
+#define SPA_KV_BF16 0
+#define SPA_KV_FP8 1
 
 /* Which KV heads are streaming and which are dynamic, and the streaming
  * pattern. The `kind` array is read on the host during the call only. */

@@ -40,7 +40,11 @@ class c_pool(ctypes.Structure):
                 ("logical_page", ctypes.c_int32), ("physical_page", ctypes.c_int32),
                 ("num_phys_pages", ctypes.c_int32), ("k_pool", ctypes.c_void_p),
                 ("v_pool", ctypes.c_void_p), ("summary", ctypes.c_void_p),
-                ("head_slots", ctypes.c_int32)]
+                ("head_slots", ctypes.c_int32), ("kv_format", ctypes.c_int32),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+
+
+SPA_KV_BF16, SPA_KV_FP8 = 0, 1
 
 
 class c_heads(ctypes.Structure):
@@ -155,7 +159,9 @@ class Pool:
     """A physical-page pool of one attention layer (device tensors).
 
     k: bf16 [N][S][P][D]; v: bf16 [N][S][P/p][D][p];
-    summary: bf16 [N][S][P/p][2][D] or None; S = head_slots or H_kv."""
+    summary: bf16 [N][S][P/p][2][D] or None; S = head_slots or H_kv.
+    kv_format "fp8": k and v hold E4M3 codes (uint8, same shapes) and
+    k_scale / v_scale the fp32 row scales [N][S][P]."""
     num_kv_heads: int
     logical_page: int
     physical_page: int
@@ -165,31 +171,49 @@ class Pool:
     summary: object = None
     head_dim: int = HEAD_DIM
     head_slots: int = 0
+    kv_format: str = "bf16"
+    k_scale: object = None
+    v_scale: object = None
 
     @classmethod
     def empty(cls, num_kv_heads: int, logical_page: int, physical_page: int, num_phys_pages: int,
-              with_summary: bool = True, device="cuda", zero: bool = True, head_slots: int = 0) -> "Pool":
+              with_summary: bool = True, device="cuda", zero: bool = True, head_slots: int = 0,
+              kv_format: str = "bf16") -> "Pool":
         import torch
+        if kv_format not in ("bf16", "fp8"):
+            raise SpaError(SPA_ERR_INVALID, f"kv_format {kv_format!r}: 'bf16' or 'fp8'")
         mk = torch.zeros if zero else torch.empty
         r = physical_page // logical_page
         S = head_slots or num_kv_heads
-        k = mk((num_phys_pages, S, physical_page, HEAD_DIM), dtype=torch.bfloat16, device=device)
-        v = mk((num_phys_pages, S, r, HEAD_DIM, logical_page), dtype=torch.bfloat16, device=device)
+        el = torch.bfloat16 if kv_format == "bf16" else torch.uint8
+        k = mk((num_phys_pages, S, physical_page, HEAD_DIM), dtype=el, device=device)
+        v = mk((num_phys_pages, S, r, HEAD_DIM, logical_page), dtype=el, device=device)
         s = mk((num_phys_pages, S, r, 2, HEAD_DIM), dtype=torch.bfloat16, device=device) \
             if with_summary else None
-        return cls(num_kv_heads, logical_page, physical_page, num_phys_pages, k, v, s, head_slots=head_slots)
+        ks = vs = None
+        if kv_format == "fp8":
+            ks = mk((num_phys_pages, S, physical_page), dtype=torch.float32, device=device)
+            vs = mk((num_phys_pages, S, physical_page), dtype=torch.float32, device=device)
+        return cls(num_kv_heads, logical_page, physical_page, num_phys_pages, k, v, s, head_slots=head_slots,
+                   kv_format=kv_format, k_scale=ks, v_scale=vs)
 
     def check(self) -> None:
         r = self.physical_page // max(self.logical_page, 1)
         N, S, P, p = self.num_phys_pages, self.head_slots or self.num_kv_heads, self.physical_page, self.logical_page
-        _need(self.k, (N, S, P, HEAD_DIM), "bf16", "pool.k")
-        _need(self.v, (N, S, r, HEAD_DIM, p), "bf16", "pool.v")
+        el = "bf16" if self.kv_format == "bf16" else "u8"
+        _need(self.k, (N, S, P, HEAD_DIM), el, "pool.k")
+        _need(self.v, (N, S, r, HEAD_DIM, p), el, "pool.v")
         _need(self.summary, (N, S, r, 2, HEAD_DIM), "bf16", "pool.summary", optional=True)
+        if self.kv_format == "fp8":
+            _need(self.k_scale, (N, S, P), "f32", "pool.k_scale")
+            _need(self.v_scale, (N, S, P), "f32", "pool.v_scale")
 
     def c(self) -> c_pool:
         self.check()
+        fmt = SPA_KV_FP8 if self.kv_format == "fp8" else SPA_KV_BF16
         return c_pool(self.num_kv_heads, self.head_dim, self.logical_page, self.physical_page,
-                      self.num_phys_pages, _ptr(self.k), _ptr(self.v), _ptr(self.summary), self.head_slots)
+                      self.num_phys_pages, _ptr(self.k), _ptr(self.v), _ptr(self.summary), self.head_slots,
+                      fmt, _ptr(self.k_scale), _ptr(self.v_scale))
 
 
 @dataclass

@@ -116,6 +116,12 @@ spa_status check_pool(const spa_pool* pool, spa::PoolArgs* out) {
   out->k = static_cast<uint16_t*>(pool->k_pool);
   out->v = static_cast<uint16_t*>(pool->v_pool);
   out->summ = static_cast<uint16_t*>(pool->summary);
+  if (pool->kv_format != SPA_KV_BF16 && pool->kv_format != SPA_KV_FP8)
+    return fail(SPA_ERR_INVALID, "kv_format %d is neither SPA_KV_BF16 nor SPA_KV_FP8", pool->kv_format);
+  out->q8 = pool->kv_format == SPA_KV_FP8;
+  out->ks = out->q8 ? pool->k_scale : nullptr;
+  out->vs = out->q8 ? pool->v_scale : nullptr;
+  if (out->q8 && (!out->ks || !out->vs)) return fail(SPA_ERR_INVALID, "an fp8 pool needs k_scale and v_scale");
   return SPA_OK;
 }
 
@@ -432,8 +438,19 @@ spa_status select_pages(const spa_pool* pool, const spa_heads* heads, const spa_
                 (long long)kMaxScoredPages);
   if ((int64_t)bt.B * dyn.n > 2147483647LL / 1) return fail(SPA_ERR_INVALID, "too many heads");
   if (bt.B == 0) return ok();
-  const bool fresh = k_new != nullptr || v_new != nullptr;
+  bool fresh = k_new != nullptr || v_new != nullptr;
   if (fresh && (!k_new || !v_new)) return fail(SPA_ERR_INVALID, "k_new / v_new is NULL");
+  if (fresh && pl.q8) {             // fp8 pools: the append as a launch of its own, first
+    if (!q || !budget_tokens || !sel_pages || !sel_count || !sel_len) {
+      if (dyn.n > 0) return fail(SPA_ERR_INVALID, "q / budget_tokens / sel_pages / sel_count / sel_len is NULL");
+    }
+    const spa_status a = hip_status(spa::launch_append(pl, bt, static_cast<const uint16_t*>(k_new),
+                                                       static_cast<const uint16_t*>(v_new), &dyn, stream),
+                                    what);
+    if (a != SPA_OK) return a;
+    k_new = v_new = nullptr;
+    fresh = false;
+  }
   if (dyn.n == 0)                   // nothing to select: the append alone
     return fresh ? hip_status(spa::launch_select(pl, bt, dyn, G, nullptr, nullptr, k_max, nullptr, nullptr,
                                                  nullptr, nullptr, nullptr, n_max,
@@ -514,6 +531,13 @@ spa_status decode_attn(const spa_pool* pool, const spa_heads* heads, const spa_b
   size_t ml_off;
   const size_t need = attn_bytes(pl, plan, bt.B, G, &ml_off);
   if (!ws || ws_bytes < need) return fail(SPA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
+  if (k_new && pl.q8) {             // fp8 pools: the append as a launch of its own, first
+    const spa_status a = hip_status(spa::launch_append(pl, bt, static_cast<const uint16_t*>(k_new),
+                                                       static_cast<const uint16_t*>(v_new), &dyn, stream),
+                                    what);
+    if (a != SPA_OK) return a;
+    k_new = v_new = nullptr;
+  }
   float* part_o = static_cast<float*>(ws);
   float* part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + ml_off);
   return hip_status(spa::launch_attn(pl, bt, plan, G, static_cast<const uint16_t*>(q), sel_pages, sel_count,

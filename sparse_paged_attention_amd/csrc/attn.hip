@@ -91,6 +91,62 @@ __device__ __forceinline__ void issue_half(const PoolArgs& pl, int32_t h, const 
   }
 }
 
+// fp8 pages: the same tiles as E4M3 codes (half the bytes), with each
+// token's key and value scale. A lane's four score rows (tokens 4*quad .. +3
+// of a block) are also the four tokens of its probabilities, so one f32x4 of
+// key scales and one of value scales per block cover both uses.
+struct PairTile8 {
+  uint4 ka[2], kb[2];       // K codes: this lane's 32 bytes of token (lane & 15) of a / b
+  uint32_t va[8], vb[8];    // V codes: tokens 4*quad .. +3 of channel 16c + (lane & 15), block a / b
+  f32x4 ksa, ksb, vsa, vsb; // key / value scales of tokens 4*quad .. +3 of block a / b
+};
+
+template <int PG>
+__device__ __forceinline__ void issue_half8(const PoolArgs& pl, int32_t h, const Block& blk, PairTile8& t,
+                                            int half, bool real) {
+  uint4* kd = half ? t.kb : t.ka;
+  uint32_t* vd = half ? t.vb : t.va;
+  f32x4& ks = half ? t.ksb : t.ksa;
+  f32x4& vs = half ? t.vsb : t.vsa;
+  if (!real) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) kd[i] = uint4{0, 0, 0, 0};
+#pragma unroll
+    for (int ch = 0; ch < 8; ++ch) vd[ch] = 0;
+    ks = f32x4{0.f, 0.f, 0.f, 0.f};
+    vs = f32x4{0.f, 0.f, 0.f, 0.f};
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  const int row = lane & 15, quad = lane >> 4;
+  const int64_t head = (int64_t)blk.phys * pl.hs + h;     // h: the head's slot in its page
+  const int32_t in_page = blk.t0 & (PG - 1);
+  const int64_t row0 = head * pl.P + blk.lp * PG + in_page; // the block's first token row
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(pl.k) + row0 * kHeadDim;
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(pl.v) + (head * pl.r + blk.lp) * (int64_t)(kHeadDim * PG) + in_page;
+  const uint32_t koff = row * kHeadDim + 32 * quad, voff = row * PG + 4 * quad;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) kd[i] = *reinterpret_cast<const uint4*>(kbase + koff + 16 * i);
+#pragma unroll
+  for (int ch = 0; ch < 8; ++ch) vd[ch] = *reinterpret_cast<const uint32_t*>(vbase + voff + 16 * ch * PG);
+  ks = *reinterpret_cast<const f32x4*>(pl.ks + row0 + 4 * quad);
+  vs = *reinterpret_cast<const f32x4*>(pl.vs + row0 + 4 * quad);
+}
+
+// Two E4M3 codes (bytes 0-1 or 2-3 of w) as a bf16 pair: the hardware
+// conversion to fp32, then the upper halves, which is exact because an E4M3
+// value has at most four significant bits.
+template <bool HIGH>
+__device__ __forceinline__ uint32_t codes_bf16x2(uint32_t w) {
+  const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HIGH);
+  return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
+}
+
+// Four codes (tokens or channels in byte order) as two bf16 words.
+__device__ __forceinline__ uint2 codes_bf16x4(uint32_t w) {
+  return uint2{codes_bf16x2<false>(w), codes_bf16x2<true>(w)};
+}
+
 struct State {
   float m;          // running reference (near the maximum) of this lane's query, log2 units
   float l;          // running sum over this lane's tokens
@@ -125,6 +181,22 @@ __device__ __forceinline__ f32x4 qk_block(const uint4 (&k)[4], const bf16x8 (&qb
   return s;
 }
 
+// qk_block over E4M3 key codes: the codes become bf16 operands exactly; the
+// key scale is applied to the scores afterwards.
+__device__ __forceinline__ f32x4 qk_block8(const uint4 (&k)[2], const bf16x8 (&qb)[4]) {
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4& w = k[i / 2];
+    const uint2 lo = codes_bf16x4(i % 2 ? w.z : w.x), hi = codes_bf16x4(i % 2 ? w.w : w.y);
+    const uint4 u = {lo.x, lo.y, hi.x, hi.y};
+    bf16x8 a;
+    __builtin_memcpy(&a, &u, 16);
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[i], s, 0, 0, 0);
+  }
+  return s;
+}
+
 // The running reference of the online softmax is raised only when a block's
 // maximum exceeds it by more than this (log2 units): probabilities then stay
 // below 2^kRescaleSlack, and the rescale of the accumulators (which live in
@@ -143,16 +215,22 @@ struct PairProbs {
 // the running reference and sum, rescales the accumulators when the
 // reference rises, and returns this lane's 8 probabilities (K-slot j of lane
 // row q: token 4q + j of block a for j < 4, token 4q + j - 4 of block b).
+// Q8 (fp8 pages): the scores are multiplied by their key scales first, and
+// the probabilities by their value scales after the running sum has taken
+// them (the sum is over softmax weights, the value scale belongs to V).
+template <bool Q8 = false>
 __device__ __forceinline__ PairProbs softmax_pair(const Block& ba, const Block& bb, const f32x4& sa,
-                                                  const f32x4& sb, State& st) {
+                                                  const f32x4& sb, State& st, const f32x4* ksa = nullptr,
+                                                  const f32x4* ksb = nullptr, const f32x4* vsa = nullptr,
+                                                  const f32x4* vsb = nullptr) {
   PairProbs pp;
   const int quad = (threadIdx.x & 63) >> 4;
   pp.full = ba.lo <= ba.t0 && ba.hi >= ba.t0 + kBlockTokens && bb.lo <= bb.t0 && bb.hi >= bb.t0 + kBlockTokens;
   float s[8];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    s[r] = sa[r];
-    s[4 + r] = sb[r];
+    s[r] = Q8 ? sa[r] * (*ksa)[r] : sa[r];
+    s[4 + r] = Q8 ? sb[r] * (*ksb)[r] : sb[r];
   }
   if (!pp.full) {                                  // mask the invalid tokens (uniform branch)
     bool valid[8];
@@ -190,6 +268,13 @@ __device__ __forceinline__ PairProbs softmax_pair(const Block& ba, const Block& 
     psum += pr[r];
   }
   st.l += psum;
+  if (Q8) {                                       // masked tokens keep 0 whatever their (stale) scale
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pr[r] = pr[r] != 0.f ? pr[r] * (*vsa)[r] : 0.f;
+      pr[4 + r] = pr[4 + r] != 0.f ? pr[4 + r] * (*vsb)[r] : 0.f;
+    }
+  }
 #pragma unroll
   for (int r = 0; r < 8; r += 2) {                // native round-to-nearest-even conversions
     const f32x2 v = {pr[r], pr[r + 1]};
@@ -208,6 +293,25 @@ __device__ __forceinline__ void pv_pair(const PairTile& t, const PairProbs& pp, 
 #pragma unroll
   for (int ch = 0; ch < 8; ++ch) {
     uint4 w = t.v[ch];
+    if (!pp.full) {                                // stale pool bytes must not reach the MFMA
+      w.x &= pp.mk[0];
+      w.y &= pp.mk[1];
+      w.z &= pp.mk[2];
+      w.w &= pp.mk[3];
+    }
+    bf16x8 a;
+    __builtin_memcpy(&a, &w, 16);
+    st.o[ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pp.hi, st.o[ch], 0, 0, 0);
+    st.o[ch] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pp.lo, st.o[ch], 0, 0, 0);
+  }
+}
+
+// pv_pair over E4M3 value codes (the value scales are already in P).
+__device__ __forceinline__ void pv_pair8(const PairTile8& t, const PairProbs& pp, State& st) {
+#pragma unroll
+  for (int ch = 0; ch < 8; ++ch) {
+    const uint2 a2 = codes_bf16x4(t.va[ch]), b2 = codes_bf16x4(t.vb[ch]);
+    uint4 w = {a2.x, a2.y, b2.x, b2.y};
     if (!pp.full) {                                // stale pool bytes must not reach the MFMA
       w.x &= pp.mk[0];
       w.y &= pp.mk[1];
@@ -302,7 +406,10 @@ struct BlockSource {
 // the caller before the lengths arrive). The kernel has a single call site,
 // so one copy of the pipeline serves every kind of item (instruction-cache
 // footprint).
-template <int PG, int BPI, int DEPTH, bool RING>
+template <bool Q8> struct TileOf { using T = PairTile; };
+template <> struct TileOf<true> { using T = PairTile8; };
+
+template <int PG, int BPI, int DEPTH, bool RING, bool Q8>
 __device__ __forceinline__ void run_blocks(const PoolArgs& pl, const BatchArgs& bt, const int32_t* pt_row,
                                            int32_t max_pp, int32_t h, const BlockSource& src,
                                            const int32_t (&page)[(BPI + 1) & ~1],
@@ -375,25 +482,40 @@ __device__ __forceinline__ void run_blocks(const PoolArgs& pl, const BatchArgs& 
   static_assert(DEPTH % 2 == 0, "blocks are processed in pairs");
   constexpr int D = DEPTH < NB ? DEPTH : NB;
   constexpr int NT = D / 2;
-  PairTile t[NT];
+  using Tile = typename TileOf<Q8>::T;
+  Tile t[NT];
+  auto issue = [&](const Block& bk, Tile& tile, int half, bool real) {
+    if constexpr (Q8) issue_half8<PG>(pl, h, bk, tile, half, real);
+    else issue_half<PG>(pl, h, bk, tile, half, real);
+  };
+  auto qk = [&](const Tile& tile, int half) {
+    if constexpr (Q8) return qk_block8(half ? tile.kb : tile.ka, qb);
+    else return qk_block(half ? tile.kb : tile.ka, qb);
+  };
 #pragma unroll
   for (int u = 0; u < D; u += 2) {
-    issue_half<PG>(pl, h, blk[u], t[u / 2], 0, u < BPI);
-    issue_half<PG>(pl, h, blk[u + 1], t[u / 2], 1, u + 1 < BPI);
+    issue(blk[u], t[u / 2], 0, u < BPI);
+    issue(blk[u + 1], t[u / 2], 1, u + 1 < BPI);
   }
-  f32x4 sa = qk_block(t[0].ka, qb), sb = qk_block(t[0].kb, qb);
+  f32x4 sa = qk(t[0], 0), sb = qk(t[0], 1);
 #pragma unroll
   for (int u = 0; u < NB; u += 2) {
-    const PairProbs pp = softmax_pair(blk[u], blk[u + 1], sa, sb, st);
+    const Tile& tc = t[(u / 2) % NT];
+    PairProbs pp;
+    if constexpr (Q8) pp = softmax_pair<true>(blk[u], blk[u + 1], sa, sb, st, &tc.ksa, &tc.ksb, &tc.vsa, &tc.vsb);
+    else pp = softmax_pair(blk[u], blk[u + 1], sa, sb, st);
     if (u + 2 < NB) {
-      const PairTile& tn = t[((u + 2) / 2) % NT];
-      sa = qk_block(tn.ka, qb);
-      sb = qk_block(tn.kb, qb);
+      const Tile& tn = t[((u + 2) / 2) % NT];
+      sa = qk(tn, 0);
+      sb = qk(tn, 1);
     }
-    if (pp.any) pv_pair(t[(u / 2) % NT], pp, st);
+    if (pp.any) {
+      if constexpr (Q8) pv_pair8(tc, pp, st);
+      else pv_pair(tc, pp, st);
+    }
     if (u + D < NB) {
-      issue_half<PG>(pl, h, blk[u + D], t[(u / 2) % NT], 0, u + D < BPI);
-      issue_half<PG>(pl, h, blk[u + 1 + D], t[(u / 2) % NT], 1, u + 1 + D < BPI);
+      issue(blk[u + D], t[(u / 2) % NT], 0, u + D < BPI);
+      issue(blk[u + 1 + D], t[(u / 2) % NT], 1, u + 1 + D < BPI);
     }
   }
 }
@@ -423,7 +545,7 @@ struct HeadMask {
 // a partial (max, sum, unnormalised output) per query head.
 // FRESH: the step's token is appended in this launch (k_new / v_new given);
 // a separate instantiation, so plain attention carries none of its code.
-template <int PG, int BPI, int DEPTH, bool FRESH, bool RING>
+template <int PG, int BPI, int DEPTH, bool FRESH, bool RING, bool Q8 = false>
 __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, AttnPlan plan, int32_t G,
                                                   const uint16_t* q, const int32_t* sel_pages,
                                                   const int32_t* sel_count, const int32_t* sel_len,
@@ -443,6 +565,7 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
                "s"(sel_len), "s"(sel_phys), "s"(q), "s"(part_o), "s"(part_ml),
                "s"(k_new), "s"(v_new), "s"(n_append), "s"(bt.B));
   if (RING) asm volatile("" ::"s"(bt.ring), "s"(bt.ring_sink), "s"(bt.ring_win));
+  if (Q8) asm volatile("" ::"s"(pl.ks), "s"(pl.vs));
   // work-group -> (sequence, head, item): head h's first item within the
   // sequence is h * items_stream + (dynamic heads below h) * (items_dyn - items_stream)
   const HeadMask mask(plan);
@@ -555,7 +678,7 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
     v_end = (L - src.ls_floor + kBlockTokens - 1) / kBlockTokens;   // any length: chunks of BPI
   }
   for (int32_t v0 = v_begin; v0 < v_end; v0 += BPI)
-    run_blocks<PG, BPI, DEPTH, RING>(pl, bt, pt_row, bt.max_pp, head_slot(pl, h, mask.below(h), dynamic), src, page, page_phys, plan.use_phys != 0, v0, v_end,
+    run_blocks<PG, BPI, DEPTH, RING, Q8>(pl, bt, pt_row, bt.max_pp, head_slot(pl, h, mask.below(h), dynamic), src, page, page_phys, plan.use_phys != 0, v0, v_end,
                                qb, st);
 
   // fold the four token quads of the running sum, store the partial
@@ -651,12 +774,15 @@ hipError_t launch_attn_t(const PoolArgs& pool, const BatchArgs& batch, const Att
   // kernel variants: the token appended in the launch (FRESH) and streaming
   // heads kept in rings (RING) are template flags, so launches without them
   // carry none of their code
-#define SPA_ATTN_LAUNCH(FRESH, RING)                                                                         \
-  hipLaunchKernelGGL((attn_kernel<PG, BPI, DEPTH, FRESH, RING>), dim3((unsigned)grid), dim3(64), 0, s, pool, \
-                     batch, plan, G, q, sel_pages, sel_count, sel_len, sel_phys, part_o, part_ml,           \
+#define SPA_ATTN_LAUNCH(FRESH, RING, ...)                                                                    \
+  hipLaunchKernelGGL((attn_kernel<PG, BPI, DEPTH, FRESH, RING, ##__VA_ARGS__>), dim3((unsigned)grid), dim3(64), \
+                     0, s, pool, batch, plan, G, q, sel_pages, sel_count, sel_len, sel_phys, part_o, part_ml,  \
                      reinterpret_cast<const uint32_t*>(k_new), v_new, n_append)
   const bool ring = batch.ring != nullptr;
-  if (k_new) {
+  if (pool.q8) {                  // fp8 pages: the append (if any) ran as a launch of its own
+    if (k_new) return hipErrorInvalidValue;
+    if (ring) SPA_ATTN_LAUNCH(false, true, true); else SPA_ATTN_LAUNCH(false, false, true);
+  } else if (k_new) {
     if (ring) SPA_ATTN_LAUNCH(true, true); else SPA_ATTN_LAUNCH(true, false);
   } else {
     if (ring) SPA_ATTN_LAUNCH(false, true); else SPA_ATTN_LAUNCH(false, false);

@@ -24,8 +24,12 @@ __global__ void __launch_bounds__(64) append_kernel(PoolArgs pl, BatchArgs bt,
   const int32_t b = blockIdx.x / pl.hkv, h = blockIdx.x % pl.hkv;
   bool is_dyn = false;
   for (int32_t d = 0; d < dyn.n; ++d) is_dyn |= dyn.id[d] == h;
-  append_token(pl, bt, b, h, head_slot(pl, h, dyn_rank(dyn, h), is_dyn), k_new, v_new, with_summary && is_dyn,
-               bt.ring != nullptr && !is_dyn);
+  const int32_t hsl = head_slot(pl, h, dyn_rank(dyn, h), is_dyn);
+  if (pl.q8)
+    append_token_q8(pl, bt, b, h, hsl, k_new, reinterpret_cast<const uint32_t*>(v_new), with_summary && is_dyn,
+                    bt.ring != nullptr && !is_dyn);
+  else
+    append_token(pl, bt, b, h, hsl, k_new, v_new, with_summary && is_dyn, bt.ring != nullptr && !is_dyn);
 }
 
 // Bulk write of tokens [start, start + count) of one sequence (prefill), one
@@ -124,6 +128,82 @@ __global__ void __launch_bounds__(64) write_kernel(PoolArgs pl, const int32_t* _
   sp[kHeadDim / 2 + lane] = (uint32_t)from_key(hi0) | ((uint32_t)from_key(hi1) << 16);
 }
 
+// write_kernel for fp8 pages: each token's key and value rows are quantized
+// (one wave reduction for the row's scale), codes and scales are written, and
+// the summary of a dynamic head's page is the min / max of the dequantized
+// keys in position order (tokens before `start` read back from the pool),
+// rounded outward to bf16.
+template <int PG>
+__global__ void __launch_bounds__(64) write_kernel_q8(PoolArgs pl, const int32_t* __restrict__ pt, int64_t start,
+                                                      int64_t count, const uint32_t* __restrict__ k,
+                                                      const uint32_t* __restrict__ v, DynMask dyn,
+                                                      int32_t ring_base, int32_t ring_sink, int32_t ring_win) {
+  const int32_t h = blockIdx.y;
+  const int64_t j = start / PG + blockIdx.x;       // logical page
+  const int64_t t0 = j * PG, end = start + count;
+  const int64_t lo = t0 > start ? t0 : start, hi = t0 + PG < end ? t0 + PG : end;
+  if (lo >= hi) return;
+  const bool dynamic = (dyn.w[h >> 5] >> (h & 31)) & 1u;
+  int32_t phys;
+  if (ring_base >= 0 && !dynamic) {
+    const int64_t pg = j / pl.r, last = (end - 1) / pl.P;
+    if (pg >= ring_sink && pg < last - (ring_win - 1)) return;   // overwritten later in this range
+    phys = ring_base + (int32_t)(pg < ring_sink ? pg : ring_sink + (pg - ring_sink) % ring_win);
+  } else {
+    phys = pt[j / pl.r];
+  }
+  if (phys < 0 || phys >= pl.N) return;
+  const int32_t lp = (int32_t)(j % pl.r);
+  int32_t below = 0;
+#pragma unroll
+  for (int w = 0; w < kMaxKvHeads / 32; ++w) below += __popc(dyn.w[w] & (32 * w + 32 <= h ? ~0u : 32 * w >= h ? 0u : (1u << (h - 32 * w)) - 1u));
+  const int32_t hsl = head_slot(pl, h, below, dynamic);
+  const int lane = threadIdx.x;
+  const int64_t row0 = k_row(pl, phys, hsl, lp * PG);
+  uint8_t* kd = reinterpret_cast<uint8_t*>(pl.k) + row0 * kHeadDim;                 // [PG][D] codes
+  uint8_t* vd = reinterpret_cast<uint8_t*>(pl.v) + v_page(pl, phys, hsl, lp);        // [D][PG] codes
+  MinMax2 mm;
+  if (dynamic)
+    for (int64_t t = t0; t < lo; ++t)               // the page's tokens before `start`, from the pool
+      mm.add(reinterpret_cast<const uint16_t*>(kd + (t - t0) * kHeadDim)[lane], pl.ks[row0 + (t - t0)]);
+  const bool full = lo == t0 && hi == t0 + PG;
+  uint32_t a[PG / 4], c[PG / 4];                    // value codes of channels 2l / 2l + 1, 4 tokens a word
+#pragma unroll
+  for (int i = 0; i < PG / 4; ++i) { a[i] = 0; c[i] = 0; }
+#pragma unroll
+  for (int u = 0; u < PG; ++u) {
+    const int64_t t = t0 + u;
+    if (t < lo || t >= hi) continue;                // wave-uniform
+    const int64_t row = (int64_t)h * count + t - start;
+    float ks, vs;
+    const uint32_t kc = quantize_pair(k[row * 64 + lane], ks);
+    const uint32_t vc = quantize_pair(v[row * 64 + lane], vs);
+    reinterpret_cast<uint16_t*>(kd + u * kHeadDim)[lane] = (uint16_t)kc;
+    if (lane == 0) {
+      pl.ks[row0 + u] = ks;
+      pl.vs[row0 + u] = vs;
+    }
+    if (full) {
+      a[u / 4] |= (vc & 0xFFu) << (8 * (u % 4));
+      c[u / 4] |= ((vc >> 8) & 0xFFu) << (8 * (u % 4));
+    } else {
+      vd[(2 * lane) * PG + u] = (uint8_t)vc;
+      vd[(2 * lane + 1) * PG + u] = (uint8_t)(vc >> 8);
+    }
+    if (dynamic) mm.add(kc, ks);
+  }
+  if (full) {
+    uint4* d0 = reinterpret_cast<uint4*>(vd + (2 * lane) * PG);
+    uint4* d1 = reinterpret_cast<uint4*>(vd + (2 * lane + 1) * PG);
+#pragma unroll
+    for (int i = 0; i < PG / 16; ++i) {
+      d0[i] = uint4{a[4 * i], a[4 * i + 1], a[4 * i + 2], a[4 * i + 3]};
+      d1[i] = uint4{c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]};
+    }
+  }
+  if (dynamic) mm.store(pl.summ + summ_page(pl, phys, hsl, lp), lane);
+}
+
 // Summaries rebuilt from the pool: grid (pages in range, B * dyn.n), one wave
 // per (logical page, dynamic head); lane l takes channels 2l and 2l + 1 of the
 // page's valid tokens, each load instruction one 256-byte key row.
@@ -162,6 +242,35 @@ __global__ void __launch_bounds__(64) summary_kernel(PoolArgs pl, BatchArgs bt, 
   sp[kHeadDim / 2 + lane] = (uint32_t)from_key(hi0) | ((uint32_t)from_key(hi1) << 16);
 }
 
+// summary_kernel for fp8 pages: min / max of the dequantized keys in position
+// order, rounded outward to bf16.
+template <int PG>
+__global__ void __launch_bounds__(64) summary_kernel_q8(PoolArgs pl, BatchArgs bt, HeadList dyn,
+                                                        const int32_t* __restrict__ first_pos,
+                                                        int32_t max_tokens) {
+  const int32_t b = blockIdx.y / dyn.n, k = blockIdx.y % dyn.n, h = dyn.id[k];
+  const int32_t hsl = head_slot(pl, h, k, true);     // (the list is in ascending head order)
+  const int32_t L = clamp_len(bt, b, pl.P);
+  if (L < 1) return;
+  int32_t f = first_pos ? first_pos[b] : L - 1;
+  if (f < 0) f = 0;
+  if (f < L - max_tokens) f = L - max_tokens;      // pages beyond the bound are not refreshed
+  if (f >= L) return;
+  const int32_t j = f / PG + blockIdx.x;            // logical page to rebuild
+  if ((int64_t)j * PG >= L) return;
+  const int32_t phys = bt.pt[(int64_t)b * bt.max_pp + j / pl.r];
+  if (phys < 0 || phys >= pl.N) return;
+  const int32_t lp = j % pl.r;
+  const int32_t n = min(PG, L - j * PG);            // valid tokens of the page
+  const int lane = threadIdx.x;
+  const int64_t row0 = k_row(pl, phys, hsl, lp * PG);
+  const uint8_t* kr = reinterpret_cast<const uint8_t*>(pl.k) + row0 * kHeadDim;
+  MinMax2 mm;
+  for (int32_t u = 0; u < n; ++u)
+    mm.add(reinterpret_cast<const uint16_t*>(kr + (int64_t)u * kHeadDim)[lane], pl.ks[row0 + u]);
+  mm.store(pl.summ + summ_page(pl, phys, hsl, lp), lane);
+}
+
 }  // namespace
 
 hipError_t launch_append(const PoolArgs& pool, const BatchArgs& batch, const uint16_t* k_new,
@@ -186,6 +295,15 @@ hipError_t launch_write(const PoolArgs& pool, const int32_t* pt_row, int64_t sta
   const dim3 grid((unsigned)pages, pool.hkv);
   const uint32_t* k32 = reinterpret_cast<const uint32_t*>(k);
   const uint32_t* v32 = reinterpret_cast<const uint32_t*>(v);
+  if (pool.q8) {
+    switch (pool.p) {
+      case 16: hipLaunchKernelGGL(write_kernel_q8<16>, grid, dim3(64), 0, s, pool, pt_row, start, count, k32, v32, m, ring_base, ring_sink, ring_win); break;
+      case 32: hipLaunchKernelGGL(write_kernel_q8<32>, grid, dim3(64), 0, s, pool, pt_row, start, count, k32, v32, m, ring_base, ring_sink, ring_win); break;
+      case 64: hipLaunchKernelGGL(write_kernel_q8<64>, grid, dim3(64), 0, s, pool, pt_row, start, count, k32, v32, m, ring_base, ring_sink, ring_win); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (pool.p) {
     case 16: hipLaunchKernelGGL(write_kernel<16>, grid, dim3(64), 0, s, pool, pt_row, start, count, k32, v32, m, ring_base, ring_sink, ring_win); break;
     case 32: hipLaunchKernelGGL(write_kernel<32>, grid, dim3(64), 0, s, pool, pt_row, start, count, k32, v32, m, ring_base, ring_sink, ring_win); break;
@@ -201,6 +319,15 @@ hipError_t launch_summary(const PoolArgs& pool, const BatchArgs& batch, const He
   // pages overlapping a range of max_tokens positions
   const int32_t pages = (max_tokens + pool.p - 1) / pool.p + 1;
   const dim3 grid(pages, batch.B * dyn.n);
+  if (pool.q8) {
+    switch (pool.p) {
+      case 16: hipLaunchKernelGGL(summary_kernel_q8<16>, grid, dim3(64), 0, s, pool, batch, dyn, first_pos, max_tokens); break;
+      case 32: hipLaunchKernelGGL(summary_kernel_q8<32>, grid, dim3(64), 0, s, pool, batch, dyn, first_pos, max_tokens); break;
+      case 64: hipLaunchKernelGGL(summary_kernel_q8<64>, grid, dim3(64), 0, s, pool, batch, dyn, first_pos, max_tokens); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (pool.p) {
     case 16: hipLaunchKernelGGL(summary_kernel<16>, grid, dim3(64), 0, s, pool, batch, dyn, first_pos, max_tokens); break;
     case 32: hipLaunchKernelGGL(summary_kernel<32>, grid, dim3(64), 0, s, pool, batch, dyn, first_pos, max_tokens); break;

@@ -63,6 +63,113 @@ __device__ __forceinline__ uint16_t from_key(uint32_t k) {
   return (k & 0x8000u) ? (uint16_t)(k & 0x7FFFu) : (uint16_t)(~k & 0xFFFFu);
 }
 
+// ---- fp8 pages -------------------------------------------------------------
+// OCP E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, largest
+// finite 448). A row is quantized with one fp32 scale, amax / 448; each code
+// is the nearest E4M3 value of x / scale, ties to even.
+
+// Code of a finite fp32 value, from its bit pattern: nearest, ties to even,
+// saturating at 448.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u, a = u & 0x7FFFFFFFu;
+  uint32_t c;
+  if (a >= 0x43E00000u) {                          // |y| >= 448
+    c = 0x7Eu;
+  } else if (a < 0x3C800000u) {                    // |y| < 2^-6: multiples of 2^-9 (8 * 2^-9 is code 8)
+    c = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.f);
+  } else {                                         // exponent field 1..15, 3 mantissa bits kept
+    const uint32_t m = (a >> 20) & 7u, rest = a & 0xFFFFFu;
+    c = ((((a >> 23) - 120u)) << 3) | m;
+    if (rest > 0x80000u || (rest == 0x80000u && (m & 1u))) c += 1;   // a carry moves into the exponent
+    c = c > 0x7Eu ? 0x7Eu : c;
+  }
+  return sign | c;
+}
+
+// Value of a code (never one of the NaN codes), exact in fp32.
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+  return (c & 0x80u) ? -v : v;
+}
+
+// Largest bf16 <= x and smallest bf16 >= x, as bit patterns.
+__device__ __forceinline__ uint32_t bf16_down(double x) {
+  const uint32_t u = __float_as_uint(__double2float_rd(x));   // largest fp32 <= x
+  uint32_t b = u >> 16;                                         // toward zero
+  if ((u & 0xFFFFu) && (u >> 31)) b += 1;                       // negative: one step further down
+  return b;
+}
+__device__ __forceinline__ uint32_t bf16_up(double x) { return bf16_down(-x) ^ 0x8000u; }
+
+// Quantizes one D = 128 row held by a wave as bf16 pairs (lane l: channels 2l
+// and 2l + 1, in w). Returns the lane's two codes (bits 0-7 and 8-15) and sets
+// the row's scale. Every lane of the wave must take part (cross-lane max).
+__device__ __forceinline__ uint32_t quantize_pair(uint32_t w, float& scale) {
+  const float x0 = __uint_as_float(w << 16), x1 = __uint_as_float(w & 0xFFFF0000u);
+  float a = fmaxf(fabsf(x0), fabsf(x1));
+#pragma unroll
+  for (int o = 32; o; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
+  scale = a / 448.f;
+  if (scale == 0.f) return 0;
+  return e4m3_code(x0 / scale) | (e4m3_code(x1 / scale) << 8);
+}
+
+// Running min / max, in position order, of the dequantized values of the
+// lane's two channels (codes in bits 0-7 / 8-15 of c2).
+struct MinMax2 {
+  double lo0 = INFINITY, hi0 = -INFINITY, lo1 = INFINITY, hi1 = -INFINITY;
+  __device__ __forceinline__ void add(uint32_t c2, float scale) {
+    const double v0 = (double)e4m3_value(c2 & 0xFFu) * (double)scale;   // exact
+    const double v1 = (double)e4m3_value((c2 >> 8) & 0xFFu) * (double)scale;
+    if (v0 < lo0) lo0 = v0;
+    if (v0 > hi0) hi0 = v0;
+    if (v1 < lo1) lo1 = v1;
+    if (v1 > hi1) hi1 = v1;
+  }
+  // the summary rows of the page, rounded outward to bf16
+  __device__ __forceinline__ void store(uint16_t* summ_page_base, int lane) const {
+    uint32_t* sp = reinterpret_cast<uint32_t*>(summ_page_base);
+    sp[lane] = bf16_down(lo0) | (bf16_down(lo1) << 16);
+    sp[kHeadDim / 2 + lane] = bf16_up(hi0) | (bf16_up(hi1) << 16);
+  }
+};
+
+// append_token for fp8 pages: the key and value rows are quantized (one scale
+// each), and the summary is rebuilt from the page's dequantized keys.
+__device__ __forceinline__ void append_token_q8(const PoolArgs& pl, const BatchArgs& bt, int32_t b, int32_t h,
+                                                int32_t hsl, const uint32_t* __restrict__ k_new,
+                                                const uint32_t* __restrict__ v_new, bool summary, bool in_ring) {
+  const int32_t L = clamp_len(bt, b, pl.P);
+  if (L < 1) return;
+  const int32_t t = L - 1;
+  const int32_t phys = in_ring ? ring_page(bt, bt.ring[b], t, pl.P, pl.N) : bt.pt[(int64_t)b * bt.max_pp + t / pl.P];
+  if (phys < 0 || phys >= pl.N) return;
+  const int32_t slot = t % pl.P, lp = slot / pl.p, i = slot % pl.p;
+  const int lane = threadIdx.x & 63;
+  const int64_t src = ((int64_t)b * pl.hkv + h) * (kHeadDim / 2);
+  float ks, vs;
+  const uint32_t kc = quantize_pair(k_new[src + lane], ks);
+  const uint32_t vc = quantize_pair(v_new[src + lane], vs);
+  const int64_t row0 = k_row(pl, phys, hsl, lp * pl.p);               // the page's first token row
+  uint8_t* krow0 = reinterpret_cast<uint8_t*>(pl.k) + row0 * kHeadDim;
+  reinterpret_cast<uint16_t*>(krow0 + (int64_t)i * kHeadDim)[lane] = (uint16_t)kc;
+  uint8_t* vp = reinterpret_cast<uint8_t*>(pl.v) + v_page(pl, phys, hsl, lp);
+  vp[(2 * lane) * pl.p + i] = (uint8_t)vc;
+  vp[(2 * lane + 1) * pl.p + i] = (uint8_t)(vc >> 8);
+  if (lane == 0) {
+    pl.ks[row0 + i] = ks;
+    pl.vs[row0 + i] = vs;
+  }
+  if (!summary) return;
+  MinMax2 mm;
+  for (int32_t r = 0; r < i; ++r)                   // the page's earlier tokens, in order
+    mm.add(reinterpret_cast<const uint16_t*>(krow0 + (int64_t)r * kHeadDim)[lane], pl.ks[row0 + r]);
+  mm.add(kc, ks);
+  mm.store(pl.summ + summ_page(pl, phys, hsl, lp), lane);
+}
+
 // One wave writes token L-1 of sequence b, KV head h into its pool slot; lane
 // l owns channels 2l and 2l+1. With `summary`, the same wave rebuilds the
 // summary of the logical page receiving the token: min and max over the

@@ -23,6 +23,9 @@ struct PoolArgs {
   uint16_t* k;      // [N][hs][P][D]
   uint16_t* v;      // [N][hs][r][D][p]
   uint16_t* summ;   // [N][hs][r][2][D]
+  int32_t q8;       // 1: k and v hold E4M3 codes (bytes, same layouts) with row scales ks / vs
+  float* ks;        // [N][hs][P] key row scales (q8)
+  float* vs;        // [N][hs][P] value row scales (q8)
 };
 
 struct BatchArgs {

@@ -24,7 +24,8 @@ from . import (Batch, Heads, Pool, kv_pool_append, kv_pool_write, page_summary_u
 class DecodeLayer:
     def __init__(self, *, hq: int, hkv: int, p: int, P: int, kind, sink: int, window: int,
                  page_table: np.ndarray, num_phys_pages: int, k_max: int, device="cuda",
-                 resolve_at_selection: bool = True, window_only: bool = False, compact: bool = False):
+                 resolve_at_selection: bool = True, window_only: bool = False, compact: bool = False,
+                 kv_format: str = "bf16"):
         self.hq, self.hkv, self.p, self.P = hq, hkv, p, P
         self.k_max = int(k_max)
         self.device = device
@@ -45,7 +46,8 @@ class DecodeLayer:
         slots = max(n_dyn, hkv - n_dyn) if compact else 0
         if compact and not window_only:
             raise ValueError("the compact layout keeps streaming heads in rings: needs window_only")
-        self.pool = Pool.empty(hkv, p, P, n_pages, with_summary=any(kind), device=device, head_slots=slots)
+        self.pool = Pool.empty(hkv, p, P, n_pages, with_summary=any(kind), device=device, head_slots=slots,
+                               kv_format=kv_format)
         self.stream_pages = None
         if window_only:
             self.stream_pages = torch.arange(self.B, dtype=torch.int32, device=device) * self.ring_pages \

@@ -42,8 +42,9 @@ class ParityRun:
 
     def __init__(self, wl: W.Workload, check_heads=None, threads: int = 16, strict_ties: bool = False,
                  resolve_at_selection: bool = True, fused: bool = False, window_only: bool = False,
-                 compact: bool = False, page_table=None):
+                 compact: bool = False, page_table=None, kv_format: str = "bf16"):
         self.wl = wl
+        self.q8 = kv_format == "fp8"     # fp8 pages: the oracle quantizes the same bf16 rows
         self.fused = fused               # the append runs inside the selection / attention launches
         self.strict_ties = strict_ties
         self.check = check_heads if check_heads is not None else \
@@ -52,7 +53,7 @@ class ParityRun:
         self.layer = DecodeLayer(hq=wl.hq, hkv=wl.hkv, p=wl.p, P=wl.P, kind=wl.kind, sink=wl.sink,
                                  window=wl.window, page_table=pt, num_phys_pages=wl.num_phys_pages,
                                  k_max=wl.k_max, resolve_at_selection=resolve_at_selection,
-                                 window_only=window_only or compact, compact=compact)
+                                 window_only=window_only or compact, compact=compact, kv_format=kv_format)
         self.K, self.V = {}, {}          # host bits of the checked (b, h) slices
         self.new_k, self.new_v = [], []  # per sequence: [H_kv][steps][D] appended tokens
         need = {(b, h) for b, h in self.check}
@@ -68,6 +69,9 @@ class ParityRun:
                 if (b, h) in need:
                     self.K[(b, h)] = Kb[h]
                     self.V[(b, h)] = Vb[h]
+                    if self.q8:          # rows are quantized one by one: once for every length
+                        self.K[(b, h)] = oracle.quantize_rows(Kb[h])
+                        self.V[(b, h)] = oracle.quantize_rows(Vb[h])
             del Kb, Vb
         self.layer.set_lengths([c - 1 for c in wl.contexts])
         if any(wl.kind):
@@ -116,8 +120,12 @@ class ParityRun:
             dyn = bool(wl.kind[h])
             st = self.state[(b, h)]
             qg = q[b, h * G:(h + 1) * G]
-            K, V = self.K[(b, h)][:L], self.V[(b, h)][:L]
-            o_out, o_lse, o_scores = oracle.decode_head(
+            if self.q8:
+                (Kc, Ks), (Vc, Vs) = self.K[(b, h)], self.V[(b, h)]
+                K, V = (Kc[:L], Ks[:L]), (Vc[:L], Vs[:L])
+            else:
+                K, V = self.K[(b, h)][:L], self.V[(b, h)][:L]
+            o_out, o_lse, o_scores = self._oracle_head(
                 K, V, qg, dynamic=dyn, sink=wl.sink, window=wl.window, p=wl.p,
                 budget=wl.budget_at(L), do_select=select, state=st, want_scores=True)
             if dyn and select:
@@ -139,7 +147,7 @@ class ParityRun:
                     report["ties"] += 1
                     st.sel[:gsel.size] = gsel
                     st.nsel[0] = gsel.size
-                    o_out, o_lse, _ = oracle.decode_head(
+                    o_out, o_lse, _ = self._oracle_head(
                         K, V, qg, dynamic=True, sink=wl.sink, window=wl.window, p=wl.p,
                         budget=wl.budget_at(L), do_select=False, state=st)
             err = float(np.abs(out[b, h * G:(h + 1) * G] - o_out).max())
@@ -147,6 +155,11 @@ class ParityRun:
             report["max_err"] = max(report["max_err"], err)
             report["max_lse_err"] = max(report["max_lse_err"], lerr)
         return report
+
+    def _oracle_head(self, K, V, q, **kw):
+        if self.q8:
+            return oracle.decode_head_q8(K[0], K[1], V[0], V[1], q, **kw)
+        return oracle.decode_head(K, V, q, **kw)
 
     def run(self, steps: int | None = None) -> list:
         reps = []

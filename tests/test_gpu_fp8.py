@@ -1,0 +1,115 @@
+"""GPU parity for fp8 pages (E4M3 codes with one fp32 scale per row, bf16
+summaries of the dequantized keys rounded outward): the pool bytes the HIP
+writes produce against the oracle's quantizer bit for bit, and whole decode
+steps against the oracle's fp8 decode step. Every test needs an MI355X and the
+built library."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity import ParityRun, assert_reports, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_paged_attention_amd as spa
+    spa.lib()
+    oracle.build()
+
+
+def run(wl, steps=None, fused=False, window_only=False, compact=False):
+    log(f"[fp8 parity] {wl.name} B={wl.batch} hq={wl.hq} hkv={wl.hkv} p={wl.p} P={wl.P} "
+        f"contexts={wl.contexts[:4]} steps={wl.steps if steps is None else steps} fused={fused} "
+        f"window_only={window_only} compact={compact}")
+    pr = ParityRun(wl, fused=fused, window_only=window_only, compact=compact, kv_format="fp8")
+    reps = pr.run(steps)
+    assert_reports(reps)
+    return pr, reps
+
+
+@pytest.mark.parametrize("p,P", [(16, 64), (32, 256), (64, 64)])
+def test_fp8_pool_bytes_bit_exact(p, P):
+    """Prompt write (spa_kv_pool_write) then appended tokens (spa_kv_pool_append):
+    every code, every scale and every summary equal the oracle's quantization of
+    the same bf16 rows; then the summaries rebuilt from the pool
+    (spa_page_summary_update) are the same bytes."""
+    wl = W.Workload(f"fp8_bytes_p{p}", 3100 + p, 2, 8, 2, p, P, (1500, 333), 5, 2, (0, 1), 8, 400,
+                    256, True)
+    pr = ParityRun(wl, kv_format="fp8")
+    for i in range(wl.steps):
+        pr.layer.set_lengths([wl.seq_len(b, i) for b in range(wl.batch)])
+        _, kn, vn = pr.step_inputs(i)
+        from parity import bits_to_bf16
+        pr.layer.append(bits_to_bf16(kn), bits_to_bf16(vn))
+    torch.cuda.synchronize()
+    pool = pr.layer.pool
+
+    def check(where):
+        k, v = pool.k.cpu().numpy(), pool.v.cpu().numpy()
+        ks, vs = pool.k_scale.cpu().numpy(), pool.v_scale.cpu().numpy()
+        summ = pool.summary.view(torch.int16).cpu().numpy().view(np.uint16)
+        pt = pr.layer.page_table.cpu().numpy()
+        for b in range(wl.batch):
+            L = wl.seq_len(b, wl.steps - 1)
+            t = np.arange(L)
+            phys, slot = pt[b, t // P], t % P
+            lp, i = slot // p, slot % p
+            for h in range(wl.hkv):
+                (Kc, Ks), (Vc, Vs) = pr.K[(b, h)], pr.V[(b, h)]
+                assert np.array_equal(k[phys, h, slot], Kc[:L]), (where, b, h, "key codes")
+                assert np.array_equal(ks[phys, h, slot], Ks[:L]), (where, b, h, "key scales")
+                assert np.array_equal(v[phys, h, lp, :, i], Vc[:L]), (where, b, h, "value codes")
+                assert np.array_equal(vs[phys, h, slot], Vs[:L]), (where, b, h, "value scales")
+                if wl.kind[h]:
+                    kmin, kmax = oracle.page_summary_q8(Kc[:L], Ks[:L], p)
+                    j = np.arange(kmin.shape[0])
+                    jp = pt[b, (j * p) // P]
+                    jl = ((j * p) % P) // p
+                    assert np.array_equal(summ[jp, h, jl, 0], kmin), (where, b, h, "summary min")
+                    assert np.array_equal(summ[jp, h, jl, 1], kmax), (where, b, h, "summary max")
+
+    check("written")
+    pool.summary.zero_()
+    pr.layer.rebuild_summaries()
+    torch.cuda.synchronize()
+    check("rebuilt")
+
+
+def test_fp8_toy_4k():
+    run(W.WORKLOADS["toy_4k"])
+
+
+def test_fp8_llama3_32k_massive_activations():
+    run(W.WORKLOADS["llama3_32k"])
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_fp8_llama3_128k_reuse_small(fused):
+    """Batch 4, shuffled pool, selection every 4 steps; fused: the append entry
+    points (on fp8 pools the append runs as a launch of its own first)."""
+    wl = W.WORKLOADS["llama3_128k"].scaled(contexts=(4100, 3001, 1000, 17), steps=9, budget=512,
+                                           window=300)
+    run(wl, fused=fused)
+
+
+def test_fp8_ragged_mha_small():
+    wl = W.WORKLOADS["ragged_mha"].scaled(contexts=(2500, 40, 1800, 3333, 700, 16, 1, 2049),
+                                          batch=8, steps=6)
+    run(wl)
+
+
+def test_fp8_p32_P256():
+    run(W.WORKLOADS["single_256k"].scaled(contexts=(9000,), steps=5, window=700, sink=40))
+
+
+@pytest.mark.parametrize("compact", [False, True])
+def test_fp8_window_only_storage(compact):
+    wl = W.WORKLOADS["llama3_128k"].scaled(contexts=(4100, 3001, 1000, 17), steps=9, budget=512,
+                                           window=300)
+    run(wl, window_only=True, compact=compact)

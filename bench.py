@@ -37,17 +37,21 @@ METRIC = "sparse decode-attn µs/step + achieved HBM GB/s (% peak) at 128K ctx"
 PEAK_GBPS = 8000.0
 COPY_BYTES = 1 << 30          # calibration copy for the HBM byte counters
 WORKLOAD = "llama3_128k"
-ATTN_KERNELS = "attn_kernel<16, 5, 4, false, false>|combine_kernel"    # one spa_sparse_decode_attn call
+ATTN_KERNELS = "attn_kernel<16, 5, 4, false, false, false>|combine_kernel"    # one spa_sparse_decode_attn call
 WRITE_KERNELS = "write_kernel<16>"                               # one spa_kv_pool_write call
+ATTN_KERNELS_FP8 = "attn_kernel<16, 5, 4, false, false, true>|combine_kernel"
+WRITE_KERNELS_FP8 = "write_kernel_q8<16>"
+ROW_BYTES = {"bf16": 256, "fp8": 128 + 4}     # one stored key or value row: elements (+ its fp32 scale)
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(wl, L: int, select: bool) -> dict:
+def algorithmic_bytes(wl, L: int, select: bool, row: int = 256) -> dict:
     """Bytes the method must move in one layer-step, per part (all sequences
-    at length L). K/V rows are 256 B each, summaries 512 B per page."""
+    at length L). A stored K or V row is `row` bytes (256 for bf16; 128 codes +
+    a 4-byte scale for fp8 pages), summaries 512 B per page."""
     D2 = wl.d * 2
     n_dyn = sum(wl.kind)
     n_str = wl.hkv - n_dyn
@@ -60,9 +64,9 @@ def algorithmic_bytes(wl, L: int, select: bool) -> dict:
     t_dyn = k * wl.p                        # selected pages are full pages here
     q_bytes = B * wl.hq * D2
     out_bytes = B * wl.hq * (wl.d * 4 + 4)
-    attn = B * (n_str * t_stream + n_dyn * t_dyn) * 2 * D2 + q_bytes + out_bytes \
+    attn = B * (n_str * t_stream + n_dyn * t_dyn) * 2 * row + q_bytes + out_bytes \
         + B * n_dyn * k * 4 + B * (L // wl.P + 1) * 4
-    append = B * wl.hkv * D2 * 2 * 2                       # read new rows, write them
+    append = B * wl.hkv * 2 * (D2 + row)                   # read new bf16 rows, write them
     summary = B * n_dyn * (D2 + 2 * 2 * D2)                 # new key + read/write min/max
     sel = 0
     if select:
@@ -71,13 +75,14 @@ def algorithmic_bytes(wl, L: int, select: bool) -> dict:
                 total=attn + append + summary + sel)
 
 
-def bulk_write_bytes(wl, count: int) -> int:
+def bulk_write_bytes(wl, count: int, row: int = 256) -> int:
     """Bytes one prompt write of `count` tokens must move: read the caller's
-    K and V rows, write them into the pool, write the min/max summary of every
-    logical page of the dynamic heads, read the page-table row."""
+    bf16 K and V rows, write them into the pool (`row` bytes each stored),
+    write the min/max summary of every logical page of the dynamic heads, read
+    the page-table row."""
     n_dyn = sum(wl.kind)
-    rows = wl.hkv * count * wl.d * 2
-    return 2 * 2 * rows + n_dyn * (-(-count // wl.p)) * 2 * wl.d * 2 + (-(-count // wl.P)) * 4
+    rows = wl.hkv * count
+    return 2 * rows * (wl.d * 2 + row) + n_dyn * (-(-count // wl.p)) * 2 * wl.d * 2 + (-(-count // wl.P)) * 4
 
 
 def cpu_baseline(wl, host_kv, replicas: int, sample_steps: int = 16) -> dict:
@@ -126,6 +131,8 @@ def main() -> int:
                     help="streaming heads' tokens: in the page table's pages like the dynamic heads, in a "
                          "ring of sink + window pages per sequence (window-only storage), or in rings with "
                          "the compact pool (page-table pages hold the dynamic heads only)")
+    ap.add_argument("--kv", choices=("bf16", "fp8"), default="bf16",
+                    help="pool format: bf16 rows, or fp8 pages (E4M3 codes with one fp32 scale per row)")
     ap.add_argument("--probe", action="store_true",
                     help="counter-collection mode: run the steps eagerly, then a plain copy of "
                          "COPY_BYTES for calibration; prints no result line")
@@ -155,7 +162,8 @@ def main() -> int:
     layers = [DecodeLayer(hq=wl.hq, hkv=wl.hkv, p=wl.p, P=wl.P, kind=wl.kind, sink=wl.sink,
                           window=wl.window, page_table=pt, num_phys_pages=wl.num_phys_pages,
                           k_max=wl.k_max, window_only=args.storage != "table",
-                          compact=args.storage == "compact") for _ in range(R)]
+                          compact=args.storage == "compact", kv_format=args.kv) for _ in range(R)]
+    row = ROW_BYTES[args.kv]
     host_kv = []
     write_events = []
     newk = np.zeros((wl.steps, wl.batch, wl.hkv, wl.d), np.uint16)
@@ -184,7 +192,7 @@ def main() -> int:
     torch.cuda.synchronize()
     write_us = sorted(1e3 * e0.elapsed_time(e1) for e0, e1, _ in write_events)
     write_med = write_us[len(write_us) // 2]
-    write_bytes = bulk_write_bytes(wl, write_events[0][2])
+    write_bytes = bulk_write_bytes(wl, write_events[0][2], row)
 
     def dev(a, dtype=torch.bfloat16):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(dtype)
@@ -196,8 +204,10 @@ def main() -> int:
     vn = [dev(newv[t]) for t in range(n_decode)]
     qs = [dev(np.stack([W.query(wl, b, t * R + r) for b in range(wl.batch)]))
           for t in range(n_decode) for r in range(R)]
-    log(f"[bench] setup {time.time() - t_setup:.1f}s; {R} replicas x "
-        f"{layers[0].pool.k.numel() * 2 * 2 / 2**30:.2f} GiB K+V")
+    pool0 = layers[0].pool
+    pool_bytes = sum(t.numel() * t.element_size() for t in (pool0.k, pool0.v, pool0.k_scale, pool0.v_scale)
+                     if t is not None)
+    log(f"[bench] setup {time.time() - t_setup:.1f}s; {R} replicas x {pool_bytes / 2**30:.2f} GiB K+V")
 
     def layer_step(s: int):
         t, r = divmod(s, R)
@@ -266,13 +276,13 @@ def main() -> int:
     ea1.record()
     torch.cuda.synchronize()
     attn_avg_us = 1e3 * ea0.elapsed_time(ea1) / args.steps
-    attn_bytes_call = algorithmic_bytes(wl, wl.seq_len(0, t_last), False)["attn"]
+    attn_bytes_call = algorithmic_bytes(wl, wl.seq_len(0, t_last), False, row)["attn"]
 
     # algorithmic bytes over the timed steps
     tot = 0
     for s in range(args.warmup, total_steps):
         t = s // R
-        tot += algorithmic_bytes(wl, wl.seq_len(0, t), wl.selects_at(t))["total"]
+        tot += algorithmic_bytes(wl, wl.seq_len(0, t), wl.selects_at(t), row)["total"]
     bytes_per_step = tot / args.steps
     gbps = bytes_per_step / (ms_per_step * 1e-3) / 1e9
     attn_gbps = attn_bytes_call / (attn_avg_us * 1e-6) / 1e9
@@ -290,8 +300,12 @@ def main() -> int:
         tr = json.load(open(tpath))
         return tr.get("bytes_per_launch") if tr.get("kernel_source_hash") == source_hash(kernels) else None
 
-    traffic = stored_traffic("attn_llama3_128k_traffic.json", ATTN_KERNELS)
-    write_traffic = stored_traffic("bulk_write_llama3_128k_traffic.json", WRITE_KERNELS)
+    fp8 = args.kv == "fp8"
+    attn_kernels = ATTN_KERNELS_FP8 if fp8 else ATTN_KERNELS
+    write_kernels = WRITE_KERNELS_FP8 if fp8 else WRITE_KERNELS
+    tag = "fp8_" if fp8 else ""
+    traffic = stored_traffic(f"attn_{tag}llama3_128k_traffic.json", attn_kernels)
+    write_traffic = stored_traffic(f"bulk_write_{tag}llama3_128k_traffic.json", write_kernels)
 
     res = {
         "metric": METRIC,
@@ -314,12 +328,14 @@ def main() -> int:
                    "streaming_storage": {"table": "page table", "ring": "ring of sink + window pages per sequence",
                                          "compact": "rings, page-table pages holding the dynamic heads only"}[
                        args.storage],
-                   "pool_gib_per_layer": round(layers[0].pool.k.numel() * 2 * 2 / 2**30, 3)},
+                   "kv_format": {"bf16": "bf16 rows", "fp8": "fp8 pages: E4M3 codes + one fp32 scale per row"}[
+                       args.kv],
+                   "pool_gib_per_layer": round(pool_bytes / 2**30, 3)},
         "achieved_GBps": round(gbps, 1),
         "hbm_frac": round(gbps / PEAK_GBPS, 4),
         "bytes_per_step": int(bytes_per_step),
         "wall_s_timed": round(wall, 4),
-        "roofline": {"bound": "hbm", "kernel": "spa_sparse_decode_attn (attn_kernel + combine_kernel)",
+        "roofline": {"bound": "hbm", "kernel": f"spa_sparse_decode_attn ({attn_kernels.replace('|', ' + ')})",
                      "achieved": round(attn_gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attn_gbps / PEAK_GBPS, 4), "traffic": traffic,
                      "avg_launch_us": round(attn_avg_us, 2), "bytes_per_launch": int(attn_bytes_call)},

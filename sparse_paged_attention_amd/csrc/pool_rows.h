@@ -164,8 +164,19 @@ __device__ __forceinline__ void append_token_q8(const PoolArgs& pl, const BatchA
   }
   if (!summary) return;
   MinMax2 mm;
-  for (int32_t r = 0; r < i; ++r)                   // the page's earlier tokens, in order
-    mm.add(reinterpret_cast<const uint16_t*>(krow0 + (int64_t)r * kHeadDim)[lane], pl.ks[row0 + r]);
+  for (int32_t r0 = 0; r0 < i; r0 += 16) {          // the page's earlier tokens, in order, 16 rows a batch
+    uint32_t w[16];
+    float sc[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {                  // rows past i - 1 re-read row i - 1 and are not added
+      const int32_t r = min(r0 + u, i - 1);
+      w[u] = reinterpret_cast<const uint16_t*>(krow0 + (int64_t)r * kHeadDim)[lane];
+      sc[u] = pl.ks[row0 + r];
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (r0 + u < i) mm.add(w[u], sc[u]);
+  }
   mm.add(kc, ks);
   mm.store(pl.summ + summ_page(pl, phys, hsl, lp), lane);
 }

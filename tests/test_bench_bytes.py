@@ -39,3 +39,17 @@ def test_selection_and_write_bytes_at_128k():
     summaries_written = 4 * 8192 * 2 * ROW             # 8192 logical pages of each dynamic head
     page_table = 2048 * 4                              # physical pages of the prompt
     assert bench.bulk_write_bytes(wl, count) == rows + summaries_written + page_table == 1090519040
+
+
+def test_fp8_bytes_at_128k():
+    """fp8 pages: a stored row is 128 one-byte codes and its 4-byte fp32 scale;
+    the query, output, selection and page-table terms are those of bf16."""
+    wl = W.WORKLOADS["llama3_128k"]
+    L = 131072 + 15
+    ROW8 = 128 + 4
+    kv = 4 * (4 * (64 + 2048) + 4 * 256 * 16) * 2 * ROW8
+    rest = 4 * 32 * ROW + 4 * 32 * (128 * 4 + 4) + 4 * 4 * 256 * 4 + 4 * (L // 64 + 1) * 4
+    assert bench.algorithmic_bytes(wl, L, False, ROW8)["attn"] == kv + rest == 26370576
+    count = 131071
+    written = 2 * 8 * count * (ROW + ROW8)              # bf16 rows read, fp8 rows written, K and V
+    assert bench.bulk_write_bytes(wl, count, ROW8) == written + 4 * 8192 * 2 * ROW + 2048 * 4

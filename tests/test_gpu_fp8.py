@@ -92,7 +92,7 @@ def test_fp8_llama3_32k_massive_activations():
 @pytest.mark.parametrize("fused", [False, True])
 def test_fp8_llama3_128k_reuse_small(fused):
     """Batch 4, shuffled pool, selection every 4 steps; fused: the append entry
-    points (on fp8 pools the append runs as a launch of its own first)."""
+    points (on fp8 pools they run the append as a launch of its own first)."""
     wl = W.WORKLOADS["llama3_128k"].scaled(contexts=(4100, 3001, 1000, 17), steps=9, budget=512,
                                            window=300)
     run(wl, fused=fused)
@@ -108,8 +108,26 @@ def test_fp8_p32_P256():
     run(W.WORKLOADS["single_256k"].scaled(contexts=(9000,), steps=5, window=700, sink=40))
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("compact", [False, True])
-def test_fp8_window_only_storage(compact):
+def test_fp8_window_only_storage(compact, fused):
     wl = W.WORKLOADS["llama3_128k"].scaled(contexts=(4100, 3001, 1000, 17), steps=9, budget=512,
                                            window=300)
-    run(wl, window_only=True, compact=compact)
+    run(wl, window_only=True, compact=compact, fused=fused)
+
+
+def test_fp8_append_inside_attention_pool_bytes():
+    """spa_append_decode_attn and spa_append_select_pages on fp8 pages write the
+    same codes, scales and summaries as spa_kv_pool_append followed by the
+    plain calls, and give results within the tolerances."""
+    wl = W.WORKLOADS["llama3_128k"].scaled(contexts=(1000, 333, 64, 17), steps=3, budget=256, window=200,
+                                           reuse=100)
+    a = ParityRun(wl, kv_format="fp8")
+    b = ParityRun(wl, kv_format="fp8", fused=True)
+    for i in range(wl.steps):
+        assert_reports([a.run_step(i)])
+        assert_reports([b.run_step(i)])
+    torch.cuda.synchronize()
+    for name in ("k", "v", "k_scale", "v_scale", "summary"):
+        x, y = getattr(a.layer.pool, name), getattr(b.layer.pool, name)
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), name

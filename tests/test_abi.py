@@ -269,3 +269,23 @@ def test_append_select_pages_validation(spa):
     assert call(mkbatch(spa, mp=20000), ws_bytes=1 << 40) == 2
     assert call(mkbatch(spa, B=0, pt=None, lens=None), k_new=None, v_new=None) == 0
 
+
+
+def test_fp8_pool_validation(spa):
+    """kv_format: SPA_KV_BF16 or SPA_KV_FP8; fp8 pages need both row-scale
+    arrays. Checked on the host before anything is launched (a zero-token write
+    launches nothing)."""
+    L = spa.lib()
+    heads = mkheads(spa)
+
+    def write(pool):
+        return L.spa_kv_pool_write(ctypes.byref(pool), ctypes.byref(heads), FAKE, 4, -1, 0, 0, FAKE, FAKE, None)
+
+    assert write(mkpool(spa, kv_format=spa.SPA_KV_FP8, k_scale=FAKE, v_scale=FAKE)) == 0
+    assert write(mkpool(spa, kv_format=spa.SPA_KV_BF16)) == 0          # scales unused
+    for bad in (dict(kv_format=2), dict(kv_format=-1),
+                dict(kv_format=spa.SPA_KV_FP8), dict(kv_format=spa.SPA_KV_FP8, k_scale=FAKE),
+                dict(kv_format=spa.SPA_KV_FP8, v_scale=FAKE)):
+        assert write(mkpool(spa, **bad)) == 1, bad
+        assert b"kv_format" in L.spa_last_error() or b"scale" in L.spa_last_error()
+    assert attn(spa, mkpool(spa, kv_format=spa.SPA_KV_FP8), heads, mkbatch(spa)) == 1

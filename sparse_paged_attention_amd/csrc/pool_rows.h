@@ -141,19 +141,40 @@ struct MinMax2 {
 __device__ __forceinline__ void append_token_q8(const PoolArgs& pl, const BatchArgs& bt, int32_t b, int32_t h,
                                                 int32_t hsl, const uint32_t* __restrict__ k_new,
                                                 const uint32_t* __restrict__ v_new, bool summary, bool in_ring) {
+  // the new rows do not depend on the length or the page: loaded with the length
+  const int lane = threadIdx.x & 63;
+  const int64_t src = ((int64_t)b * pl.hkv + h) * (kHeadDim / 2);
+  const uint32_t kin = k_new[src + lane], vin = v_new[src + lane];
   const int32_t L = clamp_len(bt, b, pl.P);
   if (L < 1) return;
   const int32_t t = L - 1;
   const int32_t phys = in_ring ? ring_page(bt, bt.ring[b], t, pl.P, pl.N) : bt.pt[(int64_t)b * bt.max_pp + t / pl.P];
   if (phys < 0 || phys >= pl.N) return;
   const int32_t slot = t % pl.P, lp = slot / pl.p, i = slot % pl.p;
-  const int lane = threadIdx.x & 63;
-  const int64_t src = ((int64_t)b * pl.hkv + h) * (kHeadDim / 2);
-  float ks, vs;
-  const uint32_t kc = quantize_pair(k_new[src + lane], ks);
-  const uint32_t vc = quantize_pair(v_new[src + lane], vs);
   const int64_t row0 = k_row(pl, phys, hsl, lp * pl.p);               // the page's first token row
   uint8_t* krow0 = reinterpret_cast<uint8_t*>(pl.k) + row0 * kHeadDim;
+  // the page's earlier key rows (never the row written below), read before
+  // the quantization so that their loads go out with nothing ahead of them;
+  // added in position order, 16 rows a batch
+  MinMax2 mm;
+  if (summary) {
+    for (int32_t r0 = 0; r0 < i; r0 += 16) {
+      uint32_t w[16];
+      float sc[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {                // rows past i - 1 re-read row i - 1 and are not added
+        const int32_t r = min(r0 + u, i - 1);
+        w[u] = reinterpret_cast<const uint16_t*>(krow0 + (int64_t)r * kHeadDim)[lane];
+        sc[u] = pl.ks[row0 + r];
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (r0 + u < i) mm.add(w[u], sc[u]);
+    }
+  }
+  float ks, vs;
+  const uint32_t kc = quantize_pair(kin, ks);
+  const uint32_t vc = quantize_pair(vin, vs);
   reinterpret_cast<uint16_t*>(krow0 + (int64_t)i * kHeadDim)[lane] = (uint16_t)kc;
   uint8_t* vp = reinterpret_cast<uint8_t*>(pl.v) + v_page(pl, phys, hsl, lp);
   vp[(2 * lane) * pl.p + i] = (uint8_t)vc;
@@ -163,20 +184,6 @@ __device__ __forceinline__ void append_token_q8(const PoolArgs& pl, const BatchA
     pl.vs[row0 + i] = vs;
   }
   if (!summary) return;
-  MinMax2 mm;
-  for (int32_t r0 = 0; r0 < i; r0 += 16) {          // the page's earlier tokens, in order, 16 rows a batch
-    uint32_t w[16];
-    float sc[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {                  // rows past i - 1 re-read row i - 1 and are not added
-      const int32_t r = min(r0 + u, i - 1);
-      w[u] = reinterpret_cast<const uint16_t*>(krow0 + (int64_t)r * kHeadDim)[lane];
-      sc[u] = pl.ks[row0 + r];
-    }
-#pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (r0 + u < i) mm.add(w[u], sc[u]);
-  }
   mm.add(kc, ks);
   mm.store(pl.summ + summ_page(pl, phys, hsl, lp), lane);
 }

@@ -23,11 +23,12 @@ def gpu():
     oracle.build()
 
 
-def run(wl, steps=None, fused=False, window_only=False, compact=False):
+def run(wl, steps=None, fused=False, window_only=False, compact=False, check=None):
     log(f"[fp8 parity] {wl.name} B={wl.batch} hq={wl.hq} hkv={wl.hkv} p={wl.p} P={wl.P} "
         f"contexts={wl.contexts[:4]} steps={wl.steps if steps is None else steps} fused={fused} "
         f"window_only={window_only} compact={compact}")
-    pr = ParityRun(wl, fused=fused, window_only=window_only, compact=compact, kv_format="fp8")
+    pr = ParityRun(wl, check_heads=check, fused=fused, window_only=window_only, compact=compact,
+                   kv_format="fp8")
     reps = pr.run(steps)
     assert_reports(reps)
     return pr, reps
@@ -96,6 +97,13 @@ def test_fp8_llama3_128k_reuse_small(fused):
     wl = W.WORKLOADS["llama3_128k"].scaled(contexts=(4100, 3001, 1000, 17), steps=9, budget=512,
                                            window=300)
     run(wl, fused=fused)
+
+
+def test_fp8_llama3_128k_full_size_sampled():
+    """The benchmark's configuration at full size on fp8 pages: 4 x 131072 + 16
+    steps, shuffled pool, reuse every 4 steps, the benchmark's launches (the
+    append entry points); checked on sampled heads of both kinds."""
+    run(W.WORKLOADS["llama3_128k"], check=[(0, 0), (0, 4), (1, 5), (2, 3), (3, 7)], fused=True)
 
 
 def test_fp8_ragged_mha_small():

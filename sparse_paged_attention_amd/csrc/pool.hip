@@ -162,6 +162,14 @@ __global__ void __launch_bounds__(64) write_kernel_q8(PoolArgs pl, const int32_t
   const int64_t row0 = k_row(pl, phys, hsl, lp * PG);
   uint8_t* kd = reinterpret_cast<uint8_t*>(pl.k) + row0 * kHeadDim;                 // [PG][D] codes
   uint8_t* vd = reinterpret_cast<uint8_t*>(pl.v) + v_page(pl, phys, hsl, lp);        // [D][PG] codes
+  uint32_t kw[PG], vw[PG];                          // all of the page's rows in flight at once
+#pragma unroll
+  for (int u = 0; u < PG; ++u) {                    // rows outside the range re-read row lo
+    const int64_t t = t0 + u;
+    const int64_t row = (int64_t)h * count + ((t >= lo && t < hi) ? t : lo) - start;
+    kw[u] = k[row * 64 + lane];
+    vw[u] = v[row * 64 + lane];
+  }
   MinMax2 mm;
   if (dynamic)
     for (int64_t t = t0; t < lo; ++t)               // the page's tokens before `start`, from the pool
@@ -174,10 +182,9 @@ __global__ void __launch_bounds__(64) write_kernel_q8(PoolArgs pl, const int32_t
   for (int u = 0; u < PG; ++u) {
     const int64_t t = t0 + u;
     if (t < lo || t >= hi) continue;                // wave-uniform
-    const int64_t row = (int64_t)h * count + t - start;
     float ks, vs;
-    const uint32_t kc = quantize_pair(k[row * 64 + lane], ks);
-    const uint32_t vc = quantize_pair(v[row * 64 + lane], vs);
+    const uint32_t kc = quantize_pair(kw[u], ks);
+    const uint32_t vc = quantize_pair(vw[u], vs);
     reinterpret_cast<uint16_t*>(kd + u * kHeadDim)[lane] = (uint16_t)kc;
     if (lane == 0) {
       pl.ks[row0 + u] = ks;

@@ -139,3 +139,49 @@ def test_fp8_append_inside_attention_pool_bytes():
     for name in ("k", "v", "k_scale", "v_scale", "summary"):
         x, y = getattr(a.layer.pool, name), getattr(b.layer.pool, name)
         assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), name
+
+
+def test_fp8_degenerate_rows_bit_exact():
+    """Rows that exercise the quantizer's edges, through the prompt write of a
+    fp8 pool: all zeros, all -0, a lone smallest bf16 subnormal, subnormals only
+    (the scale is then an fp32 subnormal), a row reaching the largest bf16,
+    mixed signs across 60 decades; codes, scales and summaries equal the
+    oracle's quantization of the same rows."""
+    import sparse_paged_attention_amd as spa
+    rng = np.random.default_rng(77)
+    p, P, count = 16, 64, 64
+    X = np.empty((2, 2, count, 128), np.uint16)          # [K/V][head][token][channel]
+    for kv in range(2):
+        for h in range(2):
+            x = (rng.standard_normal((count, 128)) * 10.0 ** rng.integers(-30, 30, (count, 1))).astype(np.float32)
+            rows = W.to_bf16_bits(x)
+            rows[0] = 0
+            rows[1] = 0x8000
+            rows[2] = 0
+            rows[2, 5] = 0x0001
+            rows[3] = rng.integers(1, 0x80, 128).astype(np.uint16) | (rng.integers(0, 2, 128).astype(np.uint16) << 15)
+            rows[4, 9] = 0x7F7F                           # the largest finite bf16
+            X[kv, h] = rows
+    pool = spa.Pool.empty(2, p, P, 4, kv_format="fp8")
+    heads = spa.Heads(8, (0, 1), 8, 64)
+    row = torch.arange(4, dtype=torch.int32, device="cuda")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    spa.kv_pool_write(pool, row, 0, dev(X[0]), dev(X[1]), heads=heads)
+    torch.cuda.synchronize()
+    k, v = pool.k.cpu().numpy(), pool.v.cpu().numpy()
+    ks, vs = pool.k_scale.cpu().numpy(), pool.v_scale.cpu().numpy()
+    summ = pool.summary.view(torch.int16).cpu().numpy().view(np.uint16)
+    t = np.arange(count)
+    phys, slot = t // P, t % P
+    for h in range(2):
+        Kc, Ks = oracle.quantize_rows(X[0, h])
+        Vc, Vs = oracle.quantize_rows(X[1, h])
+        assert np.array_equal(ks[phys, h, slot].view(np.uint32), Ks.view(np.uint32)), (h, "key scales")
+        assert np.array_equal(k[phys, h, slot], Kc), (h, "key codes")
+        assert np.array_equal(vs[phys, h, slot].view(np.uint32), Vs.view(np.uint32)), (h, "value scales")
+        assert np.array_equal(v[phys, h, slot // p, :, slot % p], Vc), (h, "value codes")
+        if h == 1:
+            kmin, kmax = oracle.page_summary_q8(Kc, Ks, p)
+            j = np.arange(count // p)
+            assert np.array_equal(summ[(j * p) // P, h, ((j * p) % P) // p, 0], kmin), "summary min"
+            assert np.array_equal(summ[(j * p) // P, h, ((j * p) % P) // p, 1], kmax), "summary max"

@@ -62,7 +62,9 @@ extern "C" {
 typedef enum spa_status {
   SPA_OK = 0,
   SPA_ERR_INVALID = 1,        /* bad argument: null pointer, size out of range, shapes that disagree */
-  SPA_ERR_UNSUPPORTED = 2,    /* well-formed but not built: head_dim != 128, p not 16/32/64, G > 16 */
+  SPA_ERR_UNSUPPORTED = 2,    /* well-formed but not built: head_dim != 128, p not 16/32/64, G not
+                                 1/2/4/8/16, a selection over more than 32768 logical pages per
+                                 sequence (max_pages * P / p > 32768), 2^32 or more summary records */
   SPA_ERR_POOL_EXHAUSTED = 3, /* page allocator has fewer free pages than requested */
   SPA_ERR_WORKSPACE = 4,      /* workspace missing or smaller than spa_workspace_bytes() */
   SPA_ERR_HIP = 5             /* a HIP runtime call failed (kernel launch) */
@@ -228,6 +230,9 @@ spa_status spa_page_summary_update(const spa_pool* pool, const spa_heads* heads,
  *                  given, receives s_j for dynamic heads (entries j >= n_b
  *                  unspecified)
  *   ws, ws_bytes:  device workspace of at least spa_workspace_bytes() bytes
+ * Limit: a page-table row may address at most 32768 logical pages
+ * (max_pages * P / p <= 32768, e.g. 524288 tokens at p = 16); larger rows
+ * return SPA_ERR_UNSUPPORTED before anything is enqueued.
  * Reuse across steps (write-up "3.2": rerun selection every C tokens) is the
  * caller's: call this only on steps that select and keep the outputs. */
 spa_status spa_select_pages(const spa_pool* pool, const spa_heads* heads,

@@ -210,14 +210,17 @@ def decode_head(K, V, q, *, dynamic: bool, sink: int, window: int, p: int, budge
     return out, lse, scores
 
 
-def decode_heads(jobs: list[dict]) -> list[tuple[np.ndarray, np.ndarray]]:
+def decode_heads(jobs: list[dict]) -> list[tuple]:
     """Runs many independent decode_head jobs in parallel (OpenMP).
 
     Each job dict holds K, V, q, dynamic, sink, window, p, budget, do_select,
-    state (HeadState). Returns [(out, lse)] in job order."""
+    state (HeadState), and optionally want_scores. Returns [(out, lse)] in job
+    order, or [(out, lse, scores)] for every job when any job asks for scores
+    (scores None where the job does not select)."""
     arr = (OrcJob * len(jobs))()
     keep = []
     results = []
+    any_scores = any(j.get("want_scores") for j in jobs)
     for i, j in enumerate(jobs):
         K, V, q = _u16(j["K"]), _u16(j["V"]), _u16(j["q"])
         L, D = K.shape
@@ -225,11 +228,16 @@ def decode_heads(jobs: list[dict]) -> list[tuple[np.ndarray, np.ndarray]]:
         st = j["state"]
         out = np.empty((G, D), np.float64)
         lse = np.empty(G, np.float64)
+        sc = None
+        if j.get("want_scores") and j["dynamic"] and j["do_select"]:
+            sc = np.full(-(-L // j["p"]), np.nan, np.float32)
+            keep.append(sc)
         keep += [K, V, q, out, lse]
-        results.append((out, lse))
+        results.append((out, lse, sc) if any_scores else (out, lse))
         arr[i] = OrcJob(_ptr(K), _ptr(V), _ptr(q), L, D, G, int(j["dynamic"]), j["sink"],
                         j["window"], j["p"], j["budget"], int(j["do_select"]), _ptr(st.sel),
-                        st.sel.size, _ptr(st.nsel), _ptr(st.Ls), None, _ptr(out), _ptr(lse), 0)
+                        st.sel.size, _ptr(st.nsel), _ptr(st.Ls), _ptr(sc) if sc is not None else None,
+                        _ptr(out), _ptr(lse), 0)
     failed = lib().orc_decode_heads(len(jobs), arr)
     if failed:
         bad = [(i, arr[i].rc) for i in range(len(jobs)) if arr[i].rc]

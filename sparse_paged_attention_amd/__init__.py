@@ -17,7 +17,9 @@ import os
 from dataclasses import dataclass
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libspa.so")
+# SPA_LIB_PATH may name another build of the same C ABI (the tests load a
+# host-only AddressSanitizer build of the argument checks that way)
+LIB_PATH = os.environ.get("SPA_LIB_PATH") or os.path.join(_HERE, "libspa.so")
 
 SPA_OK, SPA_ERR_INVALID, SPA_ERR_UNSUPPORTED, SPA_ERR_POOL_EXHAUSTED, SPA_ERR_WORKSPACE, SPA_ERR_HIP = range(6)
 

@@ -440,10 +440,19 @@ spa_status select_pages(const spa_pool* pool, const spa_heads* heads, const spa_
   if (bt.B == 0) return ok();
   bool fresh = k_new != nullptr || v_new != nullptr;
   if (fresh && (!k_new || !v_new)) return fail(SPA_ERR_INVALID, "k_new / v_new is NULL");
-  if (fresh && pl.q8) {             // fp8 pools: the append as a launch of its own, first
-    if (!q || !budget_tokens || !sel_pages || !sel_count || !sel_len) {
-      if (dyn.n > 0) return fail(SPA_ERR_INVALID, "q / budget_tokens / sel_pages / sel_count / sel_len is NULL");
+  // every check before anything is enqueued (the fp8 append below launches)
+  float* sc = scores;
+  if (dyn.n > 0) {
+    if (!q || !budget_tokens || !sel_pages || !sel_count || !sel_len)
+      return fail(SPA_ERR_INVALID, "q / budget_tokens / sel_pages / sel_count / sel_len is NULL");
+    if (!sc) {
+      const size_t need = select_bytes(pl, bt.B, bt.max_pp);
+      if (!ws || ws_bytes < need)
+        return fail(SPA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
+      sc = static_cast<float*>(ws);
     }
+  }
+  if (fresh && pl.q8) {             // fp8 pools: the append as a launch of its own, first
     const spa_status a = hip_status(spa::launch_append(pl, bt, static_cast<const uint16_t*>(k_new),
                                                        static_cast<const uint16_t*>(v_new), &dyn, stream),
                                     what);
@@ -458,15 +467,6 @@ spa_status select_pages(const spa_pool* pool, const spa_heads* heads, const spa_
                                                  static_cast<const uint16_t*>(v_new), stream),
                               what)
                  : ok();
-  if (!q || !budget_tokens || !sel_pages || !sel_count || !sel_len)
-    return fail(SPA_ERR_INVALID, "q / budget_tokens / sel_pages / sel_count / sel_len is NULL");
-  float* sc = scores;
-  if (!sc) {
-    const size_t need = select_bytes(pl, bt.B, bt.max_pp);
-    if (!ws || ws_bytes < need)
-      return fail(SPA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
-    sc = static_cast<float*>(ws);
-  }
   return hip_status(spa::launch_select(pl, bt, dyn, G, static_cast<const uint16_t*>(q), budget_tokens, k_max,
                                        sel_pages, sel_count, sel_len, sel_phys, sc, n_max,
                                        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),

@@ -289,3 +289,73 @@ def test_fp8_pool_validation(spa):
         assert write(mkpool(spa, **bad)) == 1, bad
         assert b"kv_format" in L.spa_last_error() or b"scale" in L.spa_last_error()
     assert attn(spa, mkpool(spa, kv_format=spa.SPA_KV_FP8), heads, mkbatch(spa)) == 1
+
+
+def launches(spa):
+    """Kernel launches so far when the host-only stub build is loaded (see
+    tests/asan/launch_stubs.cpp), else None."""
+    f = getattr(spa.lib(), "spa_test_launch_count", None)
+    return f() if f is not None else None
+
+
+def test_fp8_append_select_checks_workspace_before_any_launch(spa):
+    """On fp8 pools spa_append_select_pages runs the append as a launch of its
+    own; a missing or short workspace (scores NULL) and missing selection
+    outputs must be reported before that launch, so a failing call leaves the
+    pool untouched."""
+    L = spa.lib()
+    pool = mkpool(spa, kv_format=spa.SPA_KV_FP8, k_scale=FAKE, v_scale=FAKE)
+    heads = mkheads(spa)
+    before = launches(spa)
+
+    def call(ws=FAKE, ws_bytes=8, q=FAKE, sel=FAKE):
+        return L.spa_append_select_pages(ctypes.byref(pool), ctypes.byref(heads), ctypes.byref(mkbatch(spa)), FAKE,
+                                         FAKE, q, FAKE, 8, sel, FAKE, FAKE, None, None, ws, ws_bytes, None)
+    assert call() == spa.SPA_ERR_WORKSPACE
+    assert call(ws=None, ws_bytes=1 << 30) == spa.SPA_ERR_WORKSPACE
+    assert call(ws_bytes=1 << 30, q=None) == spa.SPA_ERR_INVALID
+    assert call(ws_bytes=1 << 30, sel=None) == spa.SPA_ERR_INVALID
+    assert launches(spa) == before
+
+
+def test_every_failing_call_launches_nothing(spa):
+    """With the stub build loaded, the validation failures of the calls above
+    enqueue nothing, and a call that passes its checks launches."""
+    if launches(spa) is None:
+        pytest.skip("needs the host-only stub build (SPA_LIB_PATH)")
+    before = launches(spa)
+    test_batch_and_buffer_validation(spa)
+    test_select_and_summary_validation(spa)
+    test_append_decode_attn_validation(spa)
+    test_append_select_pages_validation(spa)
+    test_compact_pool_validation(spa)
+    test_window_only_storage_validation(spa)
+    assert launches(spa) == before
+    assert attn(spa, mkpool(spa), mkheads(spa), mkbatch(spa)) == 0      # passes: one launch
+    assert launches(spa) == before + 1
+
+
+def test_sparse_config_of_the_write_up(spa):
+    """The sparse configuration the LServe write-up gives as its example
+    ("5.2 参数调优指南"; page sizes "2.2", largest logical page "5.3"), read
+    from tests/golden/sparse_config.json: both page-size pairs and the largest
+    logical page are accepted, a logical page past the largest is rejected,
+    the static sparsity ratio maps onto half the KV heads streaming, and the
+    token budget and reuse interval are those of the benchmark workload."""
+    import workloads as W
+    cfg = json.load(open(os.path.join(ROOT, "tests", "golden", "sparse_config.json")))
+    L = spa.lib()
+    heads = mkheads(spa)
+
+    def ws(p, P):
+        pool = mkpool(spa, logical_page=p, physical_page=P)
+        return L.spa_workspace_bytes(ctypes.byref(pool), ctypes.byref(heads), 4, 256, 128)
+    assert ws(cfg["logical_page_size"], cfg["physical_page_size"]) > 0
+    assert ws(cfg["alt_logical_page_size"], cfg["alt_physical_page_size"]) > 0
+    assert ws(cfg["max_logical_page_size"], 4 * cfg["max_logical_page_size"]) > 0
+    assert ws(2 * cfg["max_logical_page_size"], 4 * cfg["max_logical_page_size"]) == 0
+    wl = W.WORKLOADS["llama3_128k"]
+    assert sum(1 for k in wl.kind if k == 0) == int(cfg["static_sparsity_ratio"] * wl.hkv)
+    assert wl.budget == cfg["dynamic_token_budget"]
+    assert wl.reuse == cfg["reuse_interval"]
+    assert (wl.p, wl.P) == (cfg["alt_logical_page_size"], cfg["alt_physical_page_size"])

@@ -171,24 +171,119 @@ def test_short_sequences_streaming_dense():
 
 
 @pytest.mark.parametrize("fused", [True, False])
-def test_llama3_128k_full_size_sampled(fused):
+def test_llama3_128k_full_size(fused):
     """The configuration the benchmark times, at full size: 4 x 131072 + 16
-    steps, shuffled pool, reuse every 4 steps; checked on sampled heads. With
-    `fused` the steps run the benchmark's launches (the append inside the
-    selection / attention launches), without it the separate entry points
-    (the attention call the roofline is timed on)."""
+    steps, shuffled pool, reuse every 4 steps. With `fused` the steps run the
+    benchmark's launches (the append inside the selection / attention
+    launches), checked on every (sequence, KV head); without it the separate
+    entry points (the attention call the roofline is timed on), checked on
+    sampled heads."""
     wl = W.WORKLOADS["llama3_128k"]
-    run(wl, check=[(0, 0), (0, 4), (1, 5), (2, 3), (3, 7)], fused=fused)
+    run(wl, check=None if fused else [(0, 0), (0, 4), (1, 5), (2, 3), (3, 7)], fused=fused)
 
 
-def test_ragged_mha_full_size_sampled():
+def test_ragged_mha_full_size():
     """The ragged continuous batch at full size: 16 sequences of 24842 ..
     127144 tokens, 32 KV heads (MHA) over one shuffled 20.5 GB pool, 16 steps
-    with selection every 4, the benchmark's launches; checked on sampled
-    heads of the shortest and the longest sequences and others, streaming
-    (0-15) and dynamic (16-31)."""
+    with selection every 4, the benchmark's launches; checked on every head of
+    the shortest and the longest sequences and of two others (128 of the 512
+    (sequence, head) pairs, streaming 0-15 and dynamic 16-31)."""
     wl = W.WORKLOADS["ragged_mha"]
-    run(wl, check=[(6, 0), (6, 31), (0, 15), (0, 16), (9, 3), (13, 24), (15, 30)], fused=True)
+    short, long_ = int(np.argmin(wl.contexts)), int(np.argmax(wl.contexts))
+    seqs = sorted({short, long_, 9, 13})
+    run(wl, check=[(b, h) for b in seqs for h in range(wl.hkv)], fused=True)
+
+
+# Top-k holds E scores per thread of a 1024-thread group, E the fewest of 8,
+# 9, 12, 16, 24 and 32 that hold a row of n_max = max_pages * P / p scores.
+# One context per band of E above 9 (p = 16, P = 64), planted pages, and an
+# integer-valued case whose rows are full of exact score ties.
+TOPK_BANDS = {
+    "E12": (150_000, 9216, 12288, False),
+    "E16": (200_000, 12288, 16384, False),
+    "E24": (300_000, 16384, 24576, False),
+    "E32": (500_000, 24576, 32768, False),
+    "E32_ties": (520_000, 24576, 32768, True),
+}
+
+
+@pytest.mark.parametrize("band", list(TOPK_BANDS))
+def test_topk_row_sizes(band):
+    """Selections over rows of 9376 .. 32500 logical pages (contexts of 150K
+    to 520K tokens): every top-k row size above the benchmark's, checked id for
+    id against the oracle (strict: the scores are bit-identical), with the
+    outputs; two selecting steps each."""
+    L, lo, hi, quantized = TOPK_BANDS[band]
+    wl = W.Workload(f"topk_{band}", 2950 + L // 1000, 1, 8, 2, 16, 64, (L,), 2, 1, (0, 1), 64, 512, 4096,
+                    True, planted=None if quantized else "aligned3", quantized=quantized)
+    n_max = wl.max_pages * (wl.P // wl.p)
+    assert lo < n_max <= hi, (band, n_max)
+    log(f"[parity] top-k band {band}: n_max {n_max}")
+    reps = ParityRun(wl, strict_ties=True).run()
+    assert_reports(reps)
+    assert all(r["sel_checked"] == 1 for r in reps)
+
+
+def test_sparse_config_of_the_write_up():
+    """The LServe write-up's example sparse configuration ("5.2 参数调优指南",
+    tests/golden/sparse_config.json): logical pages of 32 tokens inside
+    physical pages of 512, half the KV heads streaming, a 4096-token budget,
+    selection reused for 4 steps; the benchmark's launches against the
+    oracle."""
+    import json
+    import os
+    cfg = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "sparse_config.json")))
+    hkv = 8
+    n_stream = int(cfg["static_sparsity_ratio"] * hkv)
+    kind = (0,) * n_stream + (1,) * (hkv - n_stream)
+    wl = W.Workload("write_up_config", 3100, 3, 32, hkv, cfg["logical_page_size"], cfg["physical_page_size"],
+                    (140_000, 9000, 33_000), 9, cfg["reuse_interval"], kind, 64, 2048,
+                    cfg["dynamic_token_budget"], True)
+    run(wl, fused=True)
+
+
+def test_outputs_stay_inside_their_buffers():
+    """Canary words around every buffer the library writes (out, lse,
+    workspace, selection outputs, scores): a few decode steps of the 128K
+    shape at small contexts, on both the separate and the append entry points,
+    leave every guard word as it was, and the results still match the
+    oracle."""
+    GUARD = 1024
+
+    def guarded(t, fill):
+        n = t.numel()
+        buf = torch.empty(n + 2 * GUARD, dtype=t.dtype, device=t.device)
+        if t.dtype == torch.float32:
+            buf.view(torch.int32).fill_(fill)
+        else:
+            buf.fill_(fill)
+        return buf, buf[GUARD:GUARD + n].view(t.shape)
+
+    for fused in (False, True):
+        wl = W.WORKLOADS["llama3_128k"].scaled(contexts=(4100, 3001, 1000, 17), steps=6, budget=512, window=300)
+        pr = ParityRun(wl, fused=fused)
+        layer = pr.layer
+        bufs = {}
+        for name, fill in (("out", 0x7FC0DEAD), ("lse", 0x7FC0BEEF), ("workspace", 0xA5),
+                           ("sel_pages", 0x5A5A5A5A), ("sel_count", 0x5A5A5A5B), ("sel_len", 0x5A5A5A5C),
+                           ("sel_phys", 0x5A5A5A5D)):
+            t = getattr(layer, name)
+            full, view = guarded(t, fill if t.dtype != torch.uint8 else fill)
+            view.copy_(t)
+            setattr(layer, name, view)
+            bufs[name] = (full, full.clone())
+        full, view = guarded(pr.scores, 0x7FC0F00D)
+        view.copy_(pr.scores)
+        pr.scores = view
+        bufs["scores"] = (full, full.clone())
+        assert_reports(pr.run())
+        torch.cuda.synchronize()
+        for name, (full, before) in bufs.items():
+            for part in (slice(0, GUARD), slice(full.numel() - GUARD, full.numel())):
+                a, b = full[part], before[part]
+                if a.dtype == torch.float32:
+                    a, b = a.view(torch.int32), b.view(torch.int32)
+                assert torch.equal(a, b), f"fused={fused}: a guard word of {name} was overwritten"
 
 
 def test_graph_replay_matches_eager():

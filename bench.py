@@ -1,21 +1,35 @@
-"""Benchmark: sparse paged decode attention at 128K context on one MI355X.
+"""Benchmark: sparse paged decode attention on one MI355X.
 
-Workload (the 128K decode configuration of the LServe write-up's latency
-table, bqwf.cn "3.2", at Llama-3-8B attention shape): 4 sequences of 131072
-tokens, 32 query / 8 KV heads, head_dim 128, logical pages of 16 inside
+Default workload (the 128K decode configuration of the LServe write-up's
+latency table, bqwf.cn "3.2", at Llama-3-8B attention shape): 4 sequences of
+131072 tokens, 32 query / 8 KV heads, head_dim 128, logical pages of 16 inside
 physical pages of 64 shuffled over the pool, KV heads 0-3 streaming (sink 64 +
-window 2048), 4-7 dynamic with a 4096-token budget, page selection every 4
-decode steps. Inputs are synthetic (seeded N(0,1) bf16) and resident in HBM.
+window 2048), 4-7 dynamic with a 4096-token budget, page selection every C = 4
+decode steps. `--workload single_256k` (one 262144-token sequence, logical
+pages of 32 in physical pages of 256, selection every step) and `--workload
+ragged_mha` (16 sequences of 16K-128K tokens, 32 KV heads, budget
+min(4096, L/32), C = 4) time the other two long-context configurations.
+Inputs are synthetic (seeded N(0,1) bf16) and resident in HBM.
 
 A step is one pass of the whole hot path for one attention layer: append the
-new token, refresh its page summary, select pages (every 4th decode step),
+new token, refresh its page summary, select pages (on steps t with t % C == 0),
 sparse decode attention for all heads. The append runs inside the attention
 launch on steps without selection (spa_append_decode_attn) and inside the
-selection's scoring launch on the others (spa_append_select_pages). To keep the timing honest about HBM
-(a step touches 51-118 MB, less than the 256 MB last-level cache), the layer
-is replicated R times with separate pools and consecutive steps cycle through
-the replicas, as the layers of a model do; the timed steps are replayed from
-a HIP graph.
+selection's scoring launch on the others (spa_append_select_pages). To keep
+the timing honest about HBM (a step of the 128K configuration touches 51-118
+MB, less than the 256 MB last-level cache), the layer is replicated R times
+with separate pools and consecutive steps cycle through the replicas, as the
+layers of a model do.
+
+Timing: one whole reuse cycle (C decode steps of every replica, R x C
+layer-steps, exactly one in C of them selecting) is captured in a HIP graph
+and replayed N >= 20 times, each replay between two events on the stream it
+runs on; `value` is the median over the replays of the time per layer-step
+(p10 / p90 beside it). The same is done for a graph of R selecting steps and
+a graph of R non-selecting steps (select_step_us, plain_step_us), and for a
+graph of R attention calls, the dominant kernel, for the roofline. A read
+probe with the attention's access shape (whole 4 KiB pieces at scattered
+places, each read once) gives the same GPU's measured ceiling.
 
 Prints one JSON line.
 """
@@ -36,41 +50,64 @@ sys.path.insert(0, ROOT)
 METRIC = "sparse decode-attn µs/step + achieved HBM GB/s (% peak) at 128K ctx"
 PEAK_GBPS = 8000.0
 COPY_BYTES = 1 << 30          # calibration copy for the HBM byte counters
-WORKLOAD = "llama3_128k"
 ATTN_KERNELS = "attn_kernel<16, 5, 4, false, false, false>|combine_kernel"    # one spa_sparse_decode_attn call
 WRITE_KERNELS = "write_kernel<16>"                               # one spa_kv_pool_write call
 ATTN_KERNELS_FP8 = "attn_kernel<16, 5, 4, false, false, true>|combine_kernel"
 WRITE_KERNELS_FP8 = "write_kernel_q8<16>"
 ROW_BYTES = {"bf16": 256, "fp8": 128 + 4}     # one stored key or value row: elements (+ its fp32 scale)
+MIN_REPLAYS = 20
+
+# per workload: layer replicas (each step's working set times R must exceed
+# the 256 MB last-level cache), decode steps generated, a description
+WORKLOADS = {
+    "llama3_128k": dict(replicas=8, steps=16,
+                        text="batch 4 x 131072 ctx (+1 token/step), 32 q / 8 kv heads, d 128, logical page 16 / "
+                             "physical 64 shuffled, kv 0-3 streaming (sink 64 + window 2048), kv 4-7 dynamic "
+                             "budget 4096, select every 4 steps"),
+    "single_256k": dict(replicas=12, steps=2,
+                        text="batch 1 x 262144 ctx (+1 token/step), 32 q / 8 kv heads, d 128, logical page 32 / "
+                             "physical 256, kv 0-3 streaming (sink 64 + window 4096), kv 4-7 dynamic budget "
+                             "4096, select every step, 32 planted pages"),
+    "ragged_mha": dict(replicas=2, steps=8,
+                       text="batch 16 x U[16384, 131072] ctx (+1 token/step), 32 q / 32 kv heads (MHA), d 128, "
+                            "logical page 16 / physical 64 shuffled, kv 0-15 streaming (sink 64 + window 1024), "
+                            "kv 16-31 dynamic budget min(4096, L/32), select every 4 steps"),
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(wl, L: int, select: bool, row: int = 256) -> dict:
-    """Bytes the method must move in one layer-step, per part (all sequences
-    at length L). A stored K or V row is `row` bytes (256 for bf16; 128 codes +
-    a 4-byte scale for fp8 pages), summaries 512 B per page."""
+def algorithmic_bytes(wl, L, select: bool, row: int = 256, tail: int = 0) -> dict:
+    """Bytes the method must move in one layer-step, per part. L: the length
+    of every sequence (an int) or one length per sequence. A stored K or V row
+    is `row` bytes (256 for bf16; 128 codes + a 4-byte scale for fp8 pages),
+    summaries 512 B per page; `tail`: tokens appended since the selection,
+    which dynamic heads attend besides their selected pages."""
+    lens = [int(L)] * wl.batch if np.isscalar(L) else [int(x) for x in L]
     D2 = wl.d * 2
     n_dyn = sum(wl.kind)
     n_str = wl.hkv - n_dyn
     B = wl.batch
-    s0 = min(wl.sink, L)
-    w0 = max(wl.sink, L - wl.window)
-    t_stream = s0 + max(0, L - w0)
-    n = -(-L // wl.p)
-    k = min(n, max(1, wl.budget_at(L) // wl.p))
-    t_dyn = k * wl.p                        # selected pages are full pages here
+    attn = sel = 0
+    for Lb in lens:
+        s0 = min(wl.sink, Lb)
+        w0 = max(wl.sink, Lb - wl.window)
+        t_stream = s0 + max(0, Lb - w0)
+        n = -(-Lb // wl.p)
+        k = min(n, max(1, wl.budget_at(Lb) // wl.p))
+        t_dyn = k * wl.p + tail                 # selected pages are full pages here
+        attn += (n_str * t_stream + n_dyn * t_dyn) * 2 * row + n_dyn * k * 4 + (Lb // wl.P + 1) * 4
+        if select:
+            sel += n_dyn * n * 2 * D2 + n_dyn * n * 4 * 2 + n_dyn * k * 4
     q_bytes = B * wl.hq * D2
     out_bytes = B * wl.hq * (wl.d * 4 + 4)
-    attn = B * (n_str * t_stream + n_dyn * t_dyn) * 2 * row + q_bytes + out_bytes \
-        + B * n_dyn * k * 4 + B * (L // wl.P + 1) * 4
+    attn += q_bytes + out_bytes
+    if select:
+        sel += q_bytes
     append = B * wl.hkv * 2 * (D2 + row)                   # read new bf16 rows, write them
     summary = B * n_dyn * (D2 + 2 * 2 * D2)                 # new key + read/write min/max
-    sel = 0
-    if select:
-        sel = B * n_dyn * n * 2 * D2 + q_bytes + B * n_dyn * n * 4 * 2 + B * n_dyn * k * 4
     return dict(attn=attn, append=append, summary=summary, select=sel,
                 total=attn + append + summary + sel)
 
@@ -85,11 +122,25 @@ def bulk_write_bytes(wl, count: int, row: int = 256) -> int:
     return 2 * rows * (wl.d * 2 + row) + n_dyn * (-(-count // wl.p)) * 2 * wl.d * 2 + (-(-count // wl.P)) * 4
 
 
-def cpu_baseline(wl, host_kv, replicas: int, sample_steps: int = 16) -> dict:
-    """The CPU oracle on a bounded sample of the same job: the first
-    `sample_steps` decode steps (selections and reuse as scheduled) of every
-    layer replica, sequence and KV head, with the queries the GPU steps use,
-    scaled to microseconds per layer-step."""
+def host_info() -> dict:
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"nproc": os.cpu_count(), "affinity": aff, "cpu_model": model}
+
+
+def cpu_baseline(wl, host_kv, replicas: int, budget_s: float = 15.0) -> dict:
+    """The CPU oracle on a bounded sample of the same job: decode steps in the
+    GPU's order (selections and reuse as scheduled, the queries the GPU steps
+    use) over every layer replica, sequence and KV head, until about
+    `budget_s` seconds of CPU work are done; scaled to microseconds per
+    layer-step."""
     import oracle
     import workloads as W
     oracle.build()
@@ -97,7 +148,8 @@ def cpu_baseline(wl, host_kv, replicas: int, sample_steps: int = 16) -> dict:
     states = {(r, b, h): oracle.HeadState(wl.k_max)
               for r in range(replicas) for b in range(wl.batch) for h in range(wl.hkv)}
     t0 = time.perf_counter()
-    for i in range(sample_steps):
+    n = n_sel = 0
+    for i in range(wl.steps):
         for r in range(replicas):
             jobs = []
             for b in range(wl.batch):
@@ -109,23 +161,80 @@ def cpu_baseline(wl, host_kv, replicas: int, sample_steps: int = 16) -> dict:
                                      sink=wl.sink, window=wl.window, p=wl.p, budget=wl.budget_at(L),
                                      do_select=wl.selects_at(i), state=states[(r, b, h)]))
             oracle.decode_heads(jobs)
+            n += 1
+            n_sel += wl.selects_at(i)
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
     dt = time.perf_counter() - t0
-    n = sample_steps * replicas
-    n_sel = sum(1 for i in range(sample_steps) if wl.selects_at(i))
+    info = host_info()
     return {"value": round(dt / n * 1e6, 1), "unit": "us/step", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{sample_steps} decode steps ({n_sel} with selection) x {replicas} layer replicas = "
-                      f"{n} layer-steps over all {wl.batch} sequences x {wl.hkv} KV heads, fp64 oracle, "
-                      f"{dt:.1f} s total"}
+            "kind": "oracle", **info,
+            "sample": f"{n} layer-steps ({n_sel} with selection) in the GPU's step order over {replicas} layer "
+                      f"replicas, all {wl.batch} sequences x {wl.hkv} KV heads each, fp64 oracle on "
+                      f"{oracle.num_threads()} OpenMP threads, {dt:.1f} s total"}
+
+
+def percentiles(xs) -> dict:
+    a = np.sort(np.asarray(xs, np.float64))
+    return {"median": round(float(np.median(a)), 3), "p10": round(float(np.percentile(a, 10)), 3),
+            "p90": round(float(np.percentile(a, 90)), 3), "n": int(a.size)}
+
+
+def time_graph(torch, build, replays: int, per: int) -> list:
+    """Captures build() in a HIP graph, replays it once untimed, then `replays`
+    times, each between two events on the current stream; returns the time
+    of each timed replay divided by `per`, in microseconds."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        build()
+    g.replay()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(replays)]
+    for e0, e1 in evs:
+        e0.record()
+        g.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    return [1e3 * e0.elapsed_time(e1) / per for e0, e1 in evs]
+
+
+def read_ceiling(torch, spa, chunks: int, replicas: int, replays: int) -> dict:
+    """The read probe: `replicas` disjoint random sets of `chunks` 4 KiB
+    pieces of a 2 GiB buffer (one set per launch, cycling like the layer
+    replicas), for 4, 8 and 16 pieces per wave; the best is the ceiling.
+    A launch over consecutive pieces gives the sequential figure."""
+    total = (2 << 30) // 4096
+    buf = torch.ones(2 << 30, dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(7)
+    perm = rng.permutation(total)[:chunks * replicas].astype(np.int32)
+    sets = [torch.from_numpy(perm[i * chunks:(i + 1) * chunks].copy()).cuda() for i in range(replicas)]
+    seq = [torch.arange(i * chunks, (i + 1) * chunks, dtype=torch.int32, device="cuda") for i in range(replicas)]
+    sink = torch.empty(chunks, dtype=torch.int32, device="cuda")
+    res = {}
+    for name, ids in (("random", sets), ("sequential", seq)):
+        for cpw in (4, 8, 16):
+            us = time_graph(torch, lambda: [spa.probe_read_chunks(buf, i, cpw, sink) for i in ids], replays,
+                            replicas)
+            med = float(np.median(us))
+            res[f"{name}_{cpw}"] = round(chunks * 4096 / (med * 1e-6) / 1e9, 1)
+    del buf
+    best = max(v for k, v in res.items() if k.startswith("random"))
+    return {"GBps": best, "per_wave": res, "bytes_per_launch": chunks * 4096}
 
 
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=64, help="timed layer-steps")
-    ap.add_argument("--warmup", type=int, default=16, help="untimed layer-steps before")
-    ap.add_argument("--replicas", type=int, default=8, help="layer replicas the steps cycle over")
+    ap.add_argument("--steps", type=int, default=64,
+                    help="layer-steps to time at least (rounded up to whole reuse cycles of every replica, "
+                         "and to at least 20 replays of one cycle)")
+    ap.add_argument("--warmup", type=int, default=16, help="untimed layer-steps before (at least one cycle)")
+    ap.add_argument("--workload", choices=tuple(WORKLOADS), default="llama3_128k")
+    ap.add_argument("--replicas", type=int, default=0, help="layer replicas the steps cycle over (0: per workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the read-ceiling probe")
     ap.add_argument("--threads", type=int, default=16)
     ap.add_argument("--storage", choices=("table", "ring", "compact"), default="table",
                     help="streaming heads' tokens: in the page table's pages like the dynamic heads, in a "
@@ -138,8 +247,8 @@ def main() -> int:
                          "COPY_BYTES for calibration; prints no result line")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path keeps every "
-              f"head on its own GPU and has no multi-GPU run.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no multi-GPU "
+              f"path; the sharding by KV head it would use moves no data between GPUs.", file=sys.stderr)
         return 2
 
     import torch
@@ -150,12 +259,13 @@ def main() -> int:
 
     spa.lib()
     torch.cuda.set_device(0)
-    wl = W.WORKLOADS[WORKLOAD]
-    R = args.replicas
-    total_steps = args.warmup + args.steps
-    n_decode = -(-total_steps // R)
-    if n_decode > wl.steps:
-        raise SystemExit(f"at most {wl.steps * R} layer-steps with {R} replicas")
+    spec = WORKLOADS[args.workload]
+    wl = W.WORKLOADS[args.workload].scaled(steps=spec["steps"])
+    R = args.replicas or spec["replicas"]
+    C = wl.reuse
+    cycle = R * C                                # layer-steps in one reuse cycle of every replica
+    if wl.steps < 2 * C:
+        raise SystemExit("the workload needs two reuse cycles of decode steps")
 
     t_setup = time.time()
     pt = W.page_table(wl)
@@ -190,28 +300,29 @@ def main() -> int:
         layer.set_lengths([c - 1 for c in wl.contexts])
         layer.set_budget([wl.budget_at(c) for c in wl.contexts])
     torch.cuda.synchronize()
-    write_us = sorted(1e3 * e0.elapsed_time(e1) for e0, e1, _ in write_events)
+    write_sel = [(e0, e1, n) for e0, e1, n in write_events if n == write_events[0][2]]
+    write_us = sorted(1e3 * e0.elapsed_time(e1) for e0, e1, _ in write_sel)
     write_med = write_us[len(write_us) // 2]
-    write_bytes = bulk_write_bytes(wl, write_events[0][2], row)
+    write_bytes = bulk_write_bytes(wl, write_sel[0][2], row)
 
     def dev(a, dtype=torch.bfloat16):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(dtype)
 
     # per decode step: lengths, new tokens; per layer-step: q
     lens = [torch.tensor([wl.seq_len(b, t) for b in range(wl.batch)], dtype=torch.int32, device="cuda")
-            for t in range(n_decode)]
-    kn = [dev(newk[t]) for t in range(n_decode)]
-    vn = [dev(newv[t]) for t in range(n_decode)]
+            for t in range(wl.steps)]
+    kn = [dev(newk[t]) for t in range(wl.steps)]
+    vn = [dev(newv[t]) for t in range(wl.steps)]
     qs = [dev(np.stack([W.query(wl, b, t * R + r) for b in range(wl.batch)]))
-          for t in range(n_decode) for r in range(R)]
+          for t in range(wl.steps) for r in range(R)]
     pool0 = layers[0].pool
     pool_bytes = sum(t.numel() * t.element_size() for t in (pool0.k, pool0.v, pool0.k_scale, pool0.v_scale)
                      if t is not None)
     log(f"[bench] setup {time.time() - t_setup:.1f}s; {R} replicas x {pool_bytes / 2**30:.2f} GiB K+V")
 
-    def layer_step(s: int):
-        t, r = divmod(s, R)
+    def layer_step(t: int, r: int):
         layer = layers[r]
+        s = t * R + r
         layer.use_lengths(lens[t])
         if wl.selects_at(t):                    # append inside the scoring launch
             layer.append_select(qs[s], kn[t], vn[t])
@@ -219,73 +330,87 @@ def main() -> int:
         else:                                   # append inside the attention launch
             layer.append_attend(qs[s], kn[t], vn[t])
 
-    # warm-up (eager, also compiles nothing: kernels are prebuilt)
-    for s in range(args.warmup):
-        layer_step(s)
+    # warm-up: the first reuse cycle of every replica, eagerly (decode steps
+    # 0 .. C-1); the timed cycle is the next one (steps C .. 2C-1)
+    for t in range(C):
+        for r in range(R):
+            layer_step(t, r)
     torch.cuda.synchronize()
+    t0 = C
 
     if args.probe:
-        for s in range(args.warmup, total_steps):
-            layer_step(s)
+        for t in range(t0, t0 + C):
+            for r in range(R):
+                layer_step(t, r)
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-        log(f"[bench] probe done: {args.steps} steps, copy of {COPY_BYTES} bytes")
+        log(f"[bench] probe done: {cycle} steps, copy of {COPY_BYTES} bytes")
         return 0
 
-    # capture the timed steps once; a replay re-appends the same tokens at the
-    # same positions and does the same work per step (a selection can differ
-    # where a scoring wave reads the summary of the page receiving the token,
-    # which an earlier run already filled further; the attention reads k
-    # pages per dynamic head whichever they are)
+    replays = max(MIN_REPLAYS, -(-args.steps // cycle))
+    warm_replays = max(1, -(-max(args.warmup - cycle, 0) // cycle))
+
+    def run_cycle():
+        for t in range(t0, t0 + C):
+            for r in range(R):
+                layer_step(t, r)
+
+    # the cycle graph: warm replays untimed, then the timed replays. A replay
+    # re-appends the same tokens at the same positions and does the same work
+    # (a selection can differ where a scoring wave reads the summary of the
+    # page receiving the token, which an earlier replay already filled
+    # further; the attention reads k pages per dynamic head whichever they are)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for s in range(args.warmup, total_steps):
-            layer_step(s)
-    g.replay()                                  # one untimed replay
+        run_cycle()
+    for _ in range(warm_replays):
+        g.replay()
     torch.cuda.synchronize()
-
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(replays)]
     wall0 = time.perf_counter()
-    ev0.record()
-    g.replay()
-    ev1.record()
+    for e0, e1 in evs:
+        e0.record()
+        g.replay()
+        e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    gpu_ms = ev0.elapsed_time(ev1)
-    ms_per_step = gpu_ms / args.steps
+    step_us = [1e3 * e0.elapsed_time(e1) / cycle for e0, e1 in evs]
+    cyc = percentiles(step_us)
+    del g
 
-    # per-call time of the attention entry point (attn_kernel + combine_kernel):
-    # a graph of `steps` attention calls cycling over the replicas at the
-    # state the timed steps left (last decode step's lengths and selections),
-    # replayed between two events on the capturing stream
-    t_last = (total_steps - 1) // R
-    ga = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(ga):
-        for i in range(args.steps):
-            r = i % R
+    # selecting steps alone and non-selecting steps alone (R layer-steps each)
+    sel_us = percentiles(time_graph(torch, lambda: [layer_step(t0, r) for r in range(R)], replays, R))
+    plain_us = None
+    if C > 1:
+        plain_us = percentiles(time_graph(torch, lambda: [layer_step(t0 + 1, r) for r in range(R)], replays, R))
+    weighted = (sel_us["median"] + (C - 1) * plain_us["median"]) / C if plain_us else sel_us["median"]
+
+    # the dominant kernel: spa_sparse_decode_attn (attn_kernel + combine_kernel)
+    # over the replicas at the last decode step of the cycle, R calls a replay
+    t_last = t0 + C - 1
+
+    def attn_calls():
+        for r in range(R):
             layers[r].use_lengths(lens[t_last])
             layers[r].attend(qs[t_last * R + r])
-    ga.replay()
-    torch.cuda.synchronize()
-    ea0, ea1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ea0.record()
-    ga.replay()
-    ea1.record()
-    torch.cuda.synchronize()
-    attn_avg_us = 1e3 * ea0.elapsed_time(ea1) / args.steps
-    attn_bytes_call = algorithmic_bytes(wl, wl.seq_len(0, t_last), False, row)["attn"]
+    attn = percentiles(time_graph(torch, attn_calls, replays, R))
+    lens_last = [wl.seq_len(b, t_last) for b in range(wl.batch)]
+    attn_bytes_call = algorithmic_bytes(wl, lens_last, False, row, tail=C - 1)["attn"]
 
-    # algorithmic bytes over the timed steps
+    # algorithmic bytes per layer-step over the timed cycle
     tot = 0
-    for s in range(args.warmup, total_steps):
-        t = s // R
-        tot += algorithmic_bytes(wl, wl.seq_len(0, t), wl.selects_at(t), row)["total"]
-    bytes_per_step = tot / args.steps
-    gbps = bytes_per_step / (ms_per_step * 1e-3) / 1e9
-    attn_gbps = attn_bytes_call / (attn_avg_us * 1e-6) / 1e9
+    for t in range(t0, t0 + C):
+        tot += R * algorithmic_bytes(wl, [wl.seq_len(b, t) for b in range(wl.batch)], wl.selects_at(t), row,
+                                     tail=t % C)["total"]
+    bytes_per_step = tot / cycle
+    gbps = bytes_per_step / (cyc["median"] * 1e-6) / 1e9
+    attn_gbps = attn_bytes_call / (attn["median"] * 1e-6) / 1e9
+
+    ceiling = None
+    if not args.no_ceiling:
+        ceiling = read_ceiling(torch, spa, max(1, attn_bytes_call // 4096), R, replays)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -303,34 +428,37 @@ def main() -> int:
     fp8 = args.kv == "fp8"
     attn_kernels = ATTN_KERNELS_FP8 if fp8 else ATTN_KERNELS
     write_kernels = WRITE_KERNELS_FP8 if fp8 else WRITE_KERNELS
-    tag = "fp8_" if fp8 else ""
-    traffic = stored_traffic(f"attn_{tag}llama3_128k_traffic.json", attn_kernels)
-    write_traffic = stored_traffic(f"bulk_write_{tag}llama3_128k_traffic.json", write_kernels)
+    tag = ("fp8_" if fp8 else "") + args.workload
+    traffic = stored_traffic(f"attn_{tag}_traffic.json", attn_kernels)
+    write_traffic = stored_traffic(f"bulk_write_{tag}_traffic.json", write_kernels)
 
     res = {
         "metric": METRIC,
-        "value": round(ms_per_step * 1e3, 2),
+        "value": round(cyc["median"], 2),
         "unit": "us/step",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "steps": replays * cycle,
+        "warmup": cycle + warm_replays * cycle,
+        "ms_per_step": round(cyc["median"] * 1e-3, 5),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3 pages (bf16 q, fp32 accumulate)" if fp8 else "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{WORKLOAD}: batch 4 x 131072 ctx (+1 token/step), 32 q / 8 kv heads, "
-                               f"d 128, logical page 16 / physical 64 shuffled, kv 0-3 streaming "
-                               f"(sink 64 + window 2048), kv 4-7 dynamic budget 4096, select every 4 "
-                               f"steps, {R} layer replicas",
-                   "batch": wl.batch, "context": wl.contexts[0], "replicas": R,
+        "config": {"workload": f"{args.workload}: {spec['text']}, {R} layer replicas",
+                   "batch": wl.batch, "context": list(wl.contexts) if wl.batch > 1 and len(set(wl.contexts)) > 1
+                   else wl.contexts[0], "replicas": R, "reuse": C,
                    "streaming_storage": {"table": "page table", "ring": "ring of sink + window pages per sequence",
                                          "compact": "rings, page-table pages holding the dynamic heads only"}[
                        args.storage],
                    "kv_format": {"bf16": "bf16 rows", "fp8": "fp8 pages: E4M3 codes + one fp32 scale per row"}[
                        args.kv],
                    "pool_gib_per_layer": round(pool_bytes / 2**30, 3)},
+        "timing": {"what": f"{replays} replays of a graph of one reuse cycle ({C} decode steps x {R} replicas = "
+                           f"{cycle} layer-steps, one in {C} selecting); per replay: time / {cycle}",
+                   "step_us": cyc, "select_step_us": sel_us, "plain_step_us": plain_us,
+                   "c_weighted_us": round(weighted, 3), "steps_requested": args.steps,
+                   "warmup_requested": args.warmup},
         "achieved_GBps": round(gbps, 1),
         "hbm_frac": round(gbps / PEAK_GBPS, 4),
         "bytes_per_step": int(bytes_per_step),
@@ -338,9 +466,12 @@ def main() -> int:
         "roofline": {"bound": "hbm", "kernel": f"spa_sparse_decode_attn ({attn_kernels.replace('|', ' + ')})",
                      "achieved": round(attn_gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attn_gbps / PEAK_GBPS, 4), "traffic": traffic,
-                     "avg_launch_us": round(attn_avg_us, 2), "bytes_per_launch": int(attn_bytes_call)},
+                     "avg_launch_us": attn["median"], "launch_us": attn, "bytes_per_launch": int(attn_bytes_call),
+                     "measured_ceiling_GBps": ceiling["GBps"] if ceiling else None,
+                     "frac_of_measured_ceiling": round(attn_gbps / ceiling["GBps"], 4) if ceiling else None},
+        "read_ceiling": ceiling,
         "cpu_baseline": cpu,
-        "bulk_write": {"what": f"spa_kv_pool_write of one {write_events[0][2]}-token prompt (all {wl.hkv} KV heads, "
+        "bulk_write": {"what": f"spa_kv_pool_write of one {write_sel[0][2]}-token prompt (all {wl.hkv} KV heads, "
                                f"summaries of the {sum(wl.kind)} dynamic heads in the same pass)",
                        "median_us": round(write_med, 1), "bytes": int(write_bytes),
                        "achieved": round(write_bytes / (write_med * 1e-6) / 1e9, 1), "unit": "GB/s",

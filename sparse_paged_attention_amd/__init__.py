@@ -65,7 +65,7 @@ EXPORTS = ("spa_kv_pool_append", "spa_kv_pool_write", "spa_page_summary_update",
            "spa_workspace_bytes",
            "spa_default_budget", "spa_stream_ring_pages", "spa_alloc_create", "spa_alloc_pages", "spa_alloc_free",
            "spa_alloc_num_free", "spa_alloc_destroy", "spa_status_string", "spa_last_error",
-           "spa_set_attn_blocks_per_item")
+           "spa_set_attn_blocks_per_item", "spa_probe_read_chunks")
 
 _lib = None
 
@@ -101,6 +101,7 @@ def lib() -> ctypes.CDLL:
             "spa_alloc_destroy": ([vp], None),
             "spa_status_string": ([ctypes.c_int], ctypes.c_char_p),
             "spa_last_error": ([], ctypes.c_char_p),
+            "spa_probe_read_chunks": ([vp, sz, vp, i32, i32, vp, vp], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -375,6 +376,22 @@ def sparse_decode_attn(pool: Pool, heads: Heads, batch: Batch, q, sel_pages, sel
                                         _ptr(v_new), _ptr(q), _ptr(sel_pages), _ptr(sel_count), _ptr(sel_len),
                                         _ptr(sel_phys), k_max, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                         _stream(stream)))
+
+
+def probe_read_chunks(base, chunk_ids, chunks_per_wave: int, sink, stream=None) -> None:
+    """spa_probe_read_chunks (include/spa_probe.h): reads the 4 KiB chunks
+    chunk_ids (int32, device) of the device tensor `base` once each; a
+    measurement aid for the benchmark's read ceiling."""
+    _need(chunk_ids, (None,), "i32", "chunk_ids")
+    n = chunk_ids.numel()
+    nbytes = base.numel() * base.element_size()
+    _need(sink, (None,), "i32", "sink")
+    if sink.numel() < -(-n // chunks_per_wave):
+        raise SpaError(SPA_ERR_INVALID, "sink holds fewer words than waves")
+    rc = lib().spa_probe_read_chunks(_ptr(base), nbytes, _ptr(chunk_ids), n, chunks_per_wave, _ptr(sink),
+                                     _stream(stream))
+    if rc != SPA_OK:
+        raise SpaError(rc, "probe_read_chunks failed")
 
 
 def set_attn_blocks_per_item(blocks: int) -> None:

@@ -23,9 +23,13 @@ def spa():
 
 
 def header_functions():
-    src = open(os.path.join(ROOT, "include", "spa.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(spa_[a-z_]+)\s*\(", src)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", h)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(spa_[a-z_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_exports_every_declared_function(spa):
@@ -359,3 +363,4 @@ def test_sparse_config_of_the_write_up(spa):
     assert wl.budget == cfg["dynamic_token_budget"]
     assert wl.reuse == cfg["reuse_interval"]
     assert (wl.p, wl.P) == (cfg["alt_logical_page_size"], cfg["alt_physical_page_size"])
+

@@ -287,6 +287,27 @@ spa_status spa_sparse_decode_attn(const spa_pool* pool, const spa_heads* heads,
                                   float* out, float* lse, void* ws, size_t ws_bytes,
                                   hipStream_t stream);
 
+/* ---- a6 + a7 + a8 for callers that cannot allocate ----------------------
+ * For callers that cannot call hipMalloc or hand in a workspace: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * The same results as spa_sparse_decode_attn with the same arguments (the
+ * same kernels), but the split partials live in a static scratch array of the
+ * library instead of a caller's workspace: SPA_NOALLOC_SCRATCH_BYTES (32 MiB)
+ * per GPU, held from the first call on that GPU until the process ends. Shapes
+ * whose partials need more return SPA_ERR_WORKSPACE before anything is
+ * enqueued (the benchmark's 4 x 131072-token batch at 32 / 8 heads needs
+ * about 3.6 MB). The first call on a device looks the array's device address
+ * up, with that device current. Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (other streams, other threads) race
+ * and give unspecified results. Allocates nothing: no hipMalloc, hipFree or
+ * allocating library routine, and needs no zeroed memory. */
+#define SPA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+spa_status spa_sparse_decode_attn_noalloc(const spa_pool* pool, const spa_heads* heads,
+                                          const spa_batch* batch, const void* q,
+                                          const int32_t* sel_pages, const int32_t* sel_count,
+                                          const int32_t* sel_len, const int32_t* sel_phys,
+                                          int32_t k_max, float* out, float* lse, hipStream_t stream);
+
 /* ---- a1 + a2 + a6 + a7 + a8 in one launch -------------------------------
  * The same pool state and outputs as spa_kv_pool_append(pool, heads, batch,
  * k_new, v_new) followed by spa_sparse_decode_attn with the other arguments:

@@ -65,7 +65,8 @@ EXPORTS = ("spa_kv_pool_append", "spa_kv_pool_write", "spa_page_summary_update",
            "spa_workspace_bytes",
            "spa_default_budget", "spa_stream_ring_pages", "spa_alloc_create", "spa_alloc_pages", "spa_alloc_free",
            "spa_alloc_num_free", "spa_alloc_destroy", "spa_status_string", "spa_last_error",
-           "spa_set_attn_blocks_per_item", "spa_probe_read_chunks")
+           "spa_set_attn_blocks_per_item", "spa_probe_read_chunks",
+           "spa_sparse_decode_attn_noalloc")
 
 _lib = None
 
@@ -102,6 +103,7 @@ def lib() -> ctypes.CDLL:
             "spa_status_string": ([ctypes.c_int], ctypes.c_char_p),
             "spa_last_error": ([], ctypes.c_char_p),
             "spa_probe_read_chunks": ([vp, sz, vp, i32, i32, vp, vp], ctypes.c_int),
+            "spa_sparse_decode_attn_noalloc": ([P, H, B, vp, vp, vp, vp, vp, i32, vp, vp, vp], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -392,6 +394,26 @@ def probe_read_chunks(base, chunk_ids, chunks_per_wave: int, sink, stream=None) 
                                      _stream(stream))
     if rc != SPA_OK:
         raise SpaError(rc, "probe_read_chunks failed")
+
+
+def sparse_decode_attn_noalloc(pool: Pool, heads: Heads, batch: Batch, q, sel_pages, sel_count, sel_len,
+                               k_max: int, out, lse=None, stream=None, sel_phys=None) -> None:
+    """spa_sparse_decode_attn_noalloc: spa_sparse_decode_attn without a
+    workspace (the library's static per-GPU scratch holds the split partials;
+    calls overlapping on one GPU race). Allocates nothing."""
+    p, h, b = pool.c(), _heads_for(heads, pool), batch.c()
+    B, H, HQ = b.batch, pool.num_kv_heads, heads.num_q_heads
+    _need(q, (B, HQ, HEAD_DIM), "bf16", "q")
+    dyn = any(heads.kind)
+    _need(sel_pages, (B, H, k_max), "i32", "sel_pages", optional=not dyn)
+    _need(sel_count, (B, H), "i32", "sel_count", optional=not dyn)
+    _need(sel_len, (B,), "i32", "sel_len", optional=not dyn)
+    _need(sel_phys, (B, H, k_max), "i32", "sel_phys", optional=True)
+    _need(out, (B, HQ, HEAD_DIM), "f32", "out")
+    _need(lse, (B, HQ), "f32", "lse", optional=True)
+    _check(lib().spa_sparse_decode_attn_noalloc(ctypes.byref(p), ctypes.byref(h), ctypes.byref(b), _ptr(q),
+                                                _ptr(sel_pages), _ptr(sel_count), _ptr(sel_len), _ptr(sel_phys),
+                                                k_max, _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def set_attn_blocks_per_item(blocks: int) -> None:

@@ -500,7 +500,8 @@ namespace {
 spa_status decode_attn(const spa_pool* pool, const spa_heads* heads, const spa_batch* batch, const void* k_new,
                        const void* v_new, const void* q, const int32_t* sel_pages, const int32_t* sel_count,
                        const int32_t* sel_len, const int32_t* sel_phys, int32_t k_max, float* out, float* lse,
-                       void* ws, size_t ws_bytes, hipStream_t stream, const char* what) {
+                       void* ws, size_t ws_bytes, hipStream_t stream, const char* what,
+                       bool use_scratch = false) {
   spa::PoolArgs pl;
   spa::BatchArgs bt;
   spa::HeadList dyn;
@@ -530,6 +531,13 @@ spa_status decode_attn(const spa_pool* pool, const spa_heads* heads, const spa_b
   if (!plan.use_phys) sel_phys = sel_pages;     // read alongside the ids, never used
   size_t ml_off;
   const size_t need = attn_bytes(pl, plan, bt.B, G, &ml_off);
+  if (use_scratch) {                // the library's static scratch in place of a workspace
+    const hipError_t e = spa::scratch_area(&ws, &ws_bytes);
+    if (e != hipSuccess) return hip_status(e, "scratch address");
+    if (ws_bytes < need)
+      return fail(SPA_ERR_WORKSPACE, "these shapes need %zu bytes of scratch; the library's static scratch "
+                  "holds %zu (use spa_sparse_decode_attn with a workspace)", need, ws_bytes);
+  }
   if (!ws || ws_bytes < need) return fail(SPA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
   if (k_new && pl.q8) {             // fp8 pools: the append as a launch of its own, first
     const spa_status a = hip_status(spa::launch_append(pl, bt, static_cast<const uint16_t*>(k_new),
@@ -555,6 +563,14 @@ spa_status spa_sparse_decode_attn(const spa_pool* pool, const spa_heads* heads, 
                                   float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
   return decode_attn(pool, heads, batch, nullptr, nullptr, q, sel_pages, sel_count, sel_len, sel_phys, k_max, out,
                      lse, ws, ws_bytes, stream, "sparse_decode_attn launch");
+}
+
+spa_status spa_sparse_decode_attn_noalloc(const spa_pool* pool, const spa_heads* heads, const spa_batch* batch,
+                                          const void* q, const int32_t* sel_pages, const int32_t* sel_count,
+                                          const int32_t* sel_len, const int32_t* sel_phys, int32_t k_max,
+                                          float* out, float* lse, hipStream_t stream) {
+  return decode_attn(pool, heads, batch, nullptr, nullptr, q, sel_pages, sel_count, sel_len, sel_phys, k_max, out,
+                     lse, nullptr, 0, stream, "sparse_decode_attn_noalloc launch", true);
 }
 
 spa_status spa_append_decode_attn(const spa_pool* pool, const spa_heads* heads, const spa_batch* batch,

@@ -20,6 +20,8 @@
 // into bf16 high and low parts so the products keep ~16 significant bits.
 // Keys are stored token-major and values channel-major per logical page, so
 // both tiles load straight from HBM into operand registers.
+#include <atomic>
+
 #include "pool_rows.h"
 
 namespace spa {
@@ -813,6 +815,34 @@ hipError_t launch_attn_p(const PoolArgs& pool, const BatchArgs& batch, const Att
 }
 
 }  // namespace
+
+// Scratch of spa_sparse_decode_attn_noalloc, for callers that cannot
+// allocate: the split partials of one call live in this array instead of a
+// caller's workspace. One copy per GPU, held until the process ends; calls
+// that overlap on one GPU share it and race.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+hipError_t scratch_area(void** ptr, size_t* bytes) {
+  // The array's name is a host-side stand-in, not a device address: the
+  // device address comes from the runtime, once per device (each GPU holds
+  // its own copy at its own address), with that device current.
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> cache[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = cache[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    cache[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  *bytes = kScratchBytes;
+  return hipSuccess;
+}
 
 hipError_t launch_attn(const PoolArgs& pool, const BatchArgs& batch, const AttnPlan& plan, int32_t G,
                        const uint16_t* q, const int32_t* sel_pages, const int32_t* sel_count,

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/spa.h"
+
 namespace spa {
 
 constexpr int kHeadDim = 128;       // D
@@ -65,6 +67,14 @@ struct AttnPlan {
   int32_t extra_partial;                 // 1: slot items_* of each head holds an appended token's partial
   int64_t sel_mask;                      // ~0 with dynamic heads, 0 without (selection unused)
 };
+
+// Bytes of the static scratch array of the attention entry point that
+// allocates nothing (spa_sparse_decode_attn_noalloc), per GPU.
+constexpr size_t kScratchBytes = SPA_NOALLOC_SCRATCH_BYTES;
+
+// Device address of that array on the current device (looked up once per
+// device) and its size.
+hipError_t scratch_area(void** ptr, size_t* bytes);
 
 // ---- launchers (return hipError_t of the launch) -------------------------
 hipError_t launch_append(const PoolArgs& pool, const BatchArgs& batch,

@@ -364,3 +364,27 @@ def test_sparse_config_of_the_write_up(spa):
     assert wl.reuse == cfg["reuse_interval"]
     assert (wl.p, wl.P) == (cfg["alt_logical_page_size"], cfg["alt_physical_page_size"])
 
+
+def test_noalloc_attention_scratch_limit(spa):
+    """spa_sparse_decode_attn_noalloc checks its arguments like
+    spa_sparse_decode_attn and rejects shapes whose partials exceed the
+    static scratch (SPA_NOALLOC_SCRATCH_BYTES) before anything is enqueued
+    (the scratch size check needs the stub build here: on a machine without a
+    GPU the real library cannot look the scratch's address up)."""
+    L = spa.lib()
+    pool, heads = mkpool(spa), mkheads(spa)
+
+    def call(batch, q=FAKE, k_max=256):
+        return L.spa_sparse_decode_attn_noalloc(ctypes.byref(pool), ctypes.byref(heads), ctypes.byref(batch), q,
+                                                FAKE, FAKE, FAKE, None, k_max, FAKE, None, None)
+    assert call(mkbatch(spa), q=None) == spa.SPA_ERR_INVALID
+    assert call(mkbatch(spa), k_max=0) == spa.SPA_ERR_INVALID
+    assert call(mkbatch(spa, B=0, pt=None, lens=None)) == 0
+    if launches(spa) is None:
+        return
+    before = launches(spa)
+    assert call(mkbatch(spa, B=64)) == spa.SPA_ERR_WORKSPACE
+    assert b"scratch" in L.spa_last_error()
+    assert launches(spa) == before
+    assert call(mkbatch(spa, B=4)) == 0
+    assert launches(spa) == before + 1

@@ -5,7 +5,9 @@ Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 never does, and the two share no code.
 
 This module is a thin ctypes layer over ``spa_oracle.c`` (plain C, fp64
-attention, exact page scores, the E4M3 quantizer of fp8 pages). Each wrapper takes and returns numpy arrays in
+attention, exact page scores, the E4M3 quantizer of fp8 pages) and
+``prefill_oracle.c`` (prefill block-sparse attention: low-rank block scores,
+block selection, exact attention on the selected blocks; fp64). Each wrapper takes and returns numpy arrays in
 logical (position) order; bf16 values travel as uint16 bit patterns.
 """
 from __future__ import annotations
@@ -18,6 +20,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "spa_oracle.c")
+_SRCS = [_SRC, os.path.join(_HERE, "prefill_oracle.c")]
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 ORC_OK, ORC_ERR_ARG, ORC_ERR_NONFINITE, ORC_ERR_RANGE = 0, 1, 2, 3
@@ -25,10 +28,10 @@ ORC_OK, ORC_ERR_ARG, ORC_ERR_NONFINITE, ORC_ERR_RANGE = 0, 1, 2, 3
 
 def build(force: bool = False) -> str:
     """Compile spa_oracle.c with gcc (OpenMP) into oracle/liboracle.so."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < max(os.path.getmtime(f) for f in _SRCS):
         tmp = _LIB + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-std=gnu11", "-fopenmp", "-fPIC", "-shared",
-                               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+                               "-Wall", "-Wextra", "-o", tmp, *_SRCS, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -83,6 +86,14 @@ def lib():
         L.orc_attend_q8.argtypes = [vp, vp, vp, vp, vp, i64, i32, vp, vp, vp]
         L.orc_decode_head_q8.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32,
                                          i32, i64, i32, vp, i64, vp, vp, vp, vp, vp]
+        L.orc_prefill_block_scores.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, vp]
+        L.orc_prefill_select.argtypes = [vp, i64, i64, vp, vp, i64]
+        L.orc_prefill_attend.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, i32, vp, vp, i64, vp, vp]
+        L.orc_prefill_attend_rows.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, i32, vp, vp, i64, vp, i64,
+                                              vp, vp]
+        for name in ("orc_prefill_block_scores", "orc_prefill_select", "orc_prefill_attend",
+                     "orc_prefill_attend_rows"):
+            getattr(L, name).restype = ctypes.c_int
         for name in ("orc_page_summary", "orc_page_scores", "orc_topk", "orc_attend",
                      "orc_decode_head", "orc_e4m3_encode", "orc_quantize_rows",
                      "orc_bf16_round_outward", "orc_page_summary_q8", "orc_attend_q8",
@@ -338,3 +349,76 @@ def decode_head_q8(Kc, Ks, Vc, Vs, q, *, dynamic: bool, sink: int, window: int, 
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+# ------------------------------------------------------- prefill (prefill_oracle.c)
+
+PREFILL_STREAMING, PREFILL_DENSE, PREFILL_SPARSE = 0, 1, 2
+
+
+def prefill_block_scores(Q, K, Wq, Wk, b: int) -> np.ndarray:
+    """One query head's block scores against its KV head: Q, K uint16 [L][D],
+    Wq, Wk uint16 [D][R] -> float32 [nb][nb], S[j][i] for i < j (NaN elsewhere)."""
+    Q, K, Wq, Wk = _u16(Q), _u16(K), _u16(Wq), _u16(Wk)
+    L, D = Q.shape
+    R = Wq.shape[1]
+    nb = -(-L // b)
+    S = np.empty((nb, nb), np.float32)
+    _check(lib().orc_prefill_block_scores(_ptr(Q), _ptr(K), _ptr(Wq), _ptr(Wk), L, D, R, b, _ptr(S)),
+           "prefill_block_scores")
+    return S
+
+
+def prefill_select(S: np.ndarray, kb: int):
+    """Selected key blocks per query block: (sel int32 [nb][kb] ascending ids,
+    cnt int32 [nb]); block j keeps itself and the min(j, kb - 1) best earlier
+    blocks."""
+    S = np.ascontiguousarray(S, dtype=np.float32)
+    nb = S.shape[0]
+    sel = np.full((nb, kb), -1, np.int32)
+    cnt = np.zeros(nb, np.int32)
+    _check(lib().orc_prefill_select(_ptr(S), nb, kb, _ptr(sel), _ptr(cnt), kb), "prefill_select")
+    return sel, cnt
+
+
+def prefill_attend(Q, K, V, b: int, mode: int, sink: int = 0, window: int = 1, sel=None, cnt=None,
+                   rows=None):
+    """One query head's prefill attention (mode PREFILL_STREAMING, _DENSE or
+    _SPARSE with sel / cnt from prefill_select): (out fp64 [L][D], lse fp64
+    [L]), or only the query positions `rows` when given."""
+    Q, K, V = _u16(Q), _u16(K), _u16(V)
+    L, D = Q.shape
+    cap = 1
+    sp = cp = None
+    if mode == PREFILL_SPARSE:
+        sel = np.ascontiguousarray(sel, dtype=np.int32)
+        cnt = np.ascontiguousarray(cnt, dtype=np.int32)
+        cap, sp, cp = sel.shape[1], _ptr(sel), _ptr(cnt)
+    if rows is None:
+        out = np.empty((L, D), np.float64)
+        lse = np.empty(L, np.float64)
+        _check(lib().orc_prefill_attend(_ptr(Q), _ptr(K), _ptr(V), L, D, b, mode, sink, window, sp, cp, cap,
+                                        _ptr(out), _ptr(lse)), "prefill_attend")
+        return out, lse
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((rows.size, D), np.float64)
+    lse = np.empty(max(rows.size, 1), np.float64)
+    _check(lib().orc_prefill_attend_rows(_ptr(Q), _ptr(K), _ptr(V), L, D, b, mode, sink, window, sp, cp, cap,
+                                         _ptr(rows), rows.size, _ptr(out), _ptr(lse)), "prefill_attend_rows")
+    return out, lse[:rows.size]
+
+
+def prefill_head(Q, K, V, Wq, Wk, *, b: int, dynamic: bool, dense: bool, budget: int, sink: int = 0,
+                 window: int = 1, rows=None):
+    """The whole prefill step for one query head: returns (out, lse, sel, cnt, S)
+    (sel / cnt / S None unless the head selects)."""
+    if not dynamic:
+        out, lse = prefill_attend(Q, K, V, b, PREFILL_STREAMING, sink, window, rows=rows)
+        return out, lse, None, None, None
+    if dense:
+        out, lse = prefill_attend(Q, K, V, b, PREFILL_DENSE, rows=rows)
+        return out, lse, None, None, None
+    S = prefill_block_scores(Q, K, Wq, Wk, b)
+    sel, cnt = prefill_select(S, max(1, budget // b))
+    out, lse = prefill_attend(Q, K, V, b, PREFILL_SPARSE, sel=sel, cnt=cnt, rows=rows)
+    return out, lse, sel, cnt, S

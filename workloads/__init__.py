@@ -33,6 +33,7 @@ import numpy as np
 
 # stream tags
 _K, _V, _Q, _PLANT, _OUTLIER, _PERM, _LENS = 1, 2, 3, 4, 5, 6, 7
+_PQ, _PK, _PV, _PW = 11, 12, 13, 14
 
 
 @dataclasses.dataclass(frozen=True)
@@ -235,3 +236,96 @@ def page_table(wl: Workload) -> np.ndarray:
     for b, ids in enumerate(physical_pages(wl)):
         pt[b, :ids.size] = ids
     return pt
+
+
+# ---------------------------------------------------------------- prefill
+
+@dataclasses.dataclass(frozen=True)
+class Prefill:
+    """A prompt's attention inputs for prefill: queries [H_q][L][D], keys and
+    values [H_kv][L][D] in position order, and the low-rank projections W_q,
+    W_k [D][D / 8] of the block-importance estimate. No trained projections
+    exist here: W is a seeded random sketch with N(0, 1 / r) entries (r = D / 8,
+    so E[W W^T] = I), and with `tied` the same W serves as W_q and W_k, which
+    makes the low-rank score an unbiased estimate of the block pair's mean
+    logit, the role the trained pair plays; untied, W_k has its own seed."""
+    name: str
+    seed: int
+    L: int
+    hq: int
+    hkv: int
+    kind: tuple
+    sink: int
+    window: int
+    budget: int              # tokens of key blocks per query block (the diagonal block included)
+    dense_below: int         # dense attention for dynamic heads when L < dense_below
+    block: int = 64
+    planted: int = 0         # key blocks per dynamic head pulled along the queries' shared direction
+    tied: bool = True
+    d: int = 128
+
+    @property
+    def rank(self) -> int:
+        return self.d // 8
+
+    @property
+    def G(self) -> int:
+        return self.hq // self.hkv
+
+    @property
+    def n_blocks(self) -> int:
+        return -(-self.L // self.block)
+
+    def scaled(self, **changes) -> "Prefill":
+        return dataclasses.replace(self, **changes)
+
+
+PREFILLS = {
+    # the 128K prompt of the LServe write-up's prefill figure ("3.1": 17 s -> 9 s at
+    # 128K) at Llama-3-8B attention shape, heads split as in the decode workloads
+    "prefill_128k": Prefill("prefill_128k", 1101, 131072, 32, 8, (0, 0, 0, 0, 1, 1, 1, 1), 64, 2048, 4096,
+                            32768, planted=16),
+    # below the write-up's 32K threshold: dense attention for the dynamic heads
+    "prefill_16k": Prefill("prefill_16k", 1102, 16384, 32, 8, (0, 0, 0, 0, 1, 1, 1, 1), 64, 1024, 4096, 32768),
+}
+
+QUERY_BIAS = 0.5          # queries: + 0.5 u, a shared direction (unit vector u)
+PLANT_GAIN = 2.0          # planted key blocks: + 2 u
+
+
+def _shared_direction(pf: Prefill) -> np.ndarray:
+    u = _gen(pf.seed, _PLANT, 999).standard_normal(pf.d).astype(np.float64)
+    return (u / np.linalg.norm(u)).astype(np.float32)
+
+
+def prefill_planted_blocks(pf: Prefill, h: int) -> np.ndarray:
+    """Key blocks of KV head h carrying the shared direction (dynamic heads)."""
+    nb = pf.n_blocks
+    if not pf.planted or pf.kind[h] != 1 or nb < 2:
+        return np.zeros(0, np.int64)
+    g = _gen(pf.seed, _PLANT, h)
+    return np.sort(g.choice(np.arange(nb - 1), size=min(pf.planted, nb - 1), replace=False))
+
+
+def prefill_rows(pf: Prefill, which: str, h: int) -> np.ndarray:
+    """bf16 bits [L][D] of the queries ('q', query head h) or keys / values
+    ('k' / 'v', KV head h) of a prefill input, N(0, 1) draws; with planted
+    blocks, every query also carries QUERY_BIAS along a shared direction and
+    the planted key blocks PLANT_GAIN along it."""
+    tag = {"q": _PQ, "k": _PK, "v": _PV}[which]
+    x = _gen(pf.seed, tag, h).standard_normal((pf.L, pf.d), dtype=np.float32)
+    if pf.planted:
+        u = _shared_direction(pf)
+        if which == "q":
+            x += np.float32(QUERY_BIAS) * u
+        elif which == "k":
+            for i in prefill_planted_blocks(pf, h):
+                x[i * pf.block:(i + 1) * pf.block] += np.float32(PLANT_GAIN) * u
+    return to_bf16_bits(x)
+
+
+def prefill_projection(pf: Prefill, which: str) -> np.ndarray:
+    """bf16 bits [D][D / 8] of W_q ('q') or W_k ('k')."""
+    g = _gen(pf.seed, _PW, 1 if (which == "q" or pf.tied) else 2)
+    x = g.standard_normal((pf.d, pf.rank), dtype=np.float32) / np.float32(math.sqrt(pf.rank))
+    return to_bf16_bits(x)

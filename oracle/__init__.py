@@ -86,7 +86,7 @@ def lib():
         L.orc_attend_q8.argtypes = [vp, vp, vp, vp, vp, i64, i32, vp, vp, vp]
         L.orc_decode_head_q8.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32,
                                          i32, i64, i32, vp, i64, vp, vp, vp, vp, vp]
-        L.orc_prefill_block_scores.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, vp]
+        L.orc_prefill_block_scores.argtypes = [vp, i32, vp, vp, vp, i64, i32, i32, i32, vp]
         L.orc_prefill_select.argtypes = [vp, i64, i64, vp, vp, i64]
         L.orc_prefill_attend.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, i32, vp, vp, i64, vp, vp]
         L.orc_prefill_attend_rows.argtypes = [vp, vp, vp, i64, i32, i32, i32, i32, i32, vp, vp, i64, vp, i64,
@@ -357,14 +357,17 @@ PREFILL_STREAMING, PREFILL_DENSE, PREFILL_SPARSE = 0, 1, 2
 
 
 def prefill_block_scores(Q, K, Wq, Wk, b: int) -> np.ndarray:
-    """One query head's block scores against its KV head: Q, K uint16 [L][D],
-    Wq, Wk uint16 [D][R] -> float32 [nb][nb], S[j][i] for i < j (NaN elsewhere)."""
+    """One KV head's block scores for its query group: Q uint16 [G][L][D] (or
+    [L][D] for G = 1), K uint16 [L][D], Wq, Wk uint16 [D][R] -> float32
+    [nb][nb], S[j][i] for i < j (NaN elsewhere)."""
     Q, K, Wq, Wk = _u16(Q), _u16(K), _u16(Wq), _u16(Wk)
-    L, D = Q.shape
+    if Q.ndim == 2:
+        Q = Q[None]
+    G, L, D = Q.shape
     R = Wq.shape[1]
     nb = -(-L // b)
     S = np.empty((nb, nb), np.float32)
-    _check(lib().orc_prefill_block_scores(_ptr(Q), _ptr(K), _ptr(Wq), _ptr(Wk), L, D, R, b, _ptr(S)),
+    _check(lib().orc_prefill_block_scores(_ptr(Q), G, _ptr(K), _ptr(Wq), _ptr(Wk), L, D, R, b, _ptr(S)),
            "prefill_block_scores")
     return S
 
@@ -410,15 +413,25 @@ def prefill_attend(Q, K, V, b: int, mode: int, sink: int = 0, window: int = 1, s
 
 def prefill_head(Q, K, V, Wq, Wk, *, b: int, dynamic: bool, dense: bool, budget: int, sink: int = 0,
                  window: int = 1, rows=None):
-    """The whole prefill step for one query head: returns (out, lse, sel, cnt, S)
-    (sel / cnt / S None unless the head selects)."""
-    if not dynamic:
-        out, lse = prefill_attend(Q, K, V, b, PREFILL_STREAMING, sink, window, rows=rows)
-        return out, lse, None, None, None
-    if dense:
-        out, lse = prefill_attend(Q, K, V, b, PREFILL_DENSE, rows=rows)
-        return out, lse, None, None, None
-    S = prefill_block_scores(Q, K, Wq, Wk, b)
-    sel, cnt = prefill_select(S, max(1, budget // b))
-    out, lse = prefill_attend(Q, K, V, b, PREFILL_SPARSE, sel=sel, cnt=cnt, rows=rows)
-    return out, lse, sel, cnt, S
+    """The whole prefill step for one KV head and its query group: Q uint16
+    [G][L][D] (or [L][D]), K, V [L][D]. Returns (out fp64 [G][n][D], lse fp64
+    [G][n], sel, cnt, S) with n = L or len(rows) (sel / cnt / S None unless
+    the head selects)."""
+    Q = _u16(Q)
+    if Q.ndim == 2:
+        Q = Q[None]
+    sel = cnt = S = None
+    if dynamic and not dense:
+        S = prefill_block_scores(Q, K, Wq, Wk, b)
+        sel, cnt = prefill_select(S, max(1, budget // b))
+    outs, lses = [], []
+    for g in range(Q.shape[0]):
+        if not dynamic:
+            o, l_ = prefill_attend(Q[g], K, V, b, PREFILL_STREAMING, sink, window, rows=rows)
+        elif dense:
+            o, l_ = prefill_attend(Q[g], K, V, b, PREFILL_DENSE, rows=rows)
+        else:
+            o, l_ = prefill_attend(Q[g], K, V, b, PREFILL_SPARSE, sel=sel, cnt=cnt, rows=rows)
+        outs.append(o)
+        lses.append(l_)
+    return np.stack(outs), np.stack(lses), sel, cnt, S

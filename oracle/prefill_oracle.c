@@ -25,8 +25,12 @@
  *     By linearity that is (qbar_j W_q) . (kbar_i W_k) / sqrt(d) with qbar_j,
  *     kbar_i the mean query / key of each block; it is computed in fp64 in
  *     that order (mean, projection, dot product) and rounded once to fp32.
- *   - Each query head selects for itself (one W_q, W_k pair per layer,
- *     shared by the heads). Query block j always attends its own block j
+ *   - Selection is per KV head, for its whole group of G query heads
+ *     (grouped-query attention; the decode path selects per KV head too):
+ *     the score averages the low-rank logits over the group's G heads as
+ *     well, i.e. qbar_j is the mean query of block j over the G heads and
+ *     the block's tokens. One W_q, W_k pair per layer, shared by the heads.
+ *     Query block j always attends its own block j
  *     (causally, so every query sees at least itself) and, of the earlier
  *     blocks 0..j-1, the min(j, kb - 1) best ones in the order (score
  *     descending, block id ascending), kb = max(1, budget / b) blocks per
@@ -71,20 +75,27 @@ static void project(const double* x, const uint16_t* W, int32_t D, int32_t R, do
   }
 }
 
-/* Block scores of one query head against its KV head: S[j][i] for
- * 0 <= i < j < nb (other entries NaN), nb = ceil(L / b). Q, K: [L][D]. */
-int orc_prefill_block_scores(const uint16_t* Q, const uint16_t* K, const uint16_t* Wq, const uint16_t* Wk,
-                             int64_t L, int32_t D, int32_t R, int32_t b, float* S) {
-  if (!Q || !K || !Wq || !Wk || !S || L < 1 || D < 1 || R < 1 || b < 1) return PF_ERR_ARG;
+/* Block scores of one KV head for its group of G query heads: S[j][i] for
+ * 0 <= i < j < nb (other entries NaN), nb = ceil(L / b). Q: [G][L][D] (the
+ * group's queries), K: [L][D]. */
+int orc_prefill_block_scores(const uint16_t* Q, int32_t G, const uint16_t* K, const uint16_t* Wq,
+                             const uint16_t* Wk, int64_t L, int32_t D, int32_t R, int32_t b, float* S) {
+  if (!Q || !K || !Wq || !Wk || !S || G < 1 || L < 1 || D < 1 || R < 1 || b < 1) return PF_ERR_ARG;
   const int64_t nb = (L + b - 1) / b;
   double* qp = malloc(sizeof(double) * nb * R);
   double* kp = malloc(sizeof(double) * nb * R);
   double* m = malloc(sizeof(double) * D);
-  if (!qp || !kp || !m) { free(qp); free(kp); free(m); return PF_ERR_ARG; }
+  double* mg = malloc(sizeof(double) * D);
+  if (!qp || !kp || !m || !mg) { free(qp); free(kp); free(m); free(mg); return PF_ERR_ARG; }
   for (int64_t j = 0; j < nb; j++) {
     const int64_t t0 = j * b, t1 = t0 + b < L ? t0 + b : L;
-    block_mean(Q, D, t0, t1, m);
-    project(m, Wq, D, R, qp + j * R);
+    for (int32_t c = 0; c < D; c++) mg[c] = 0.0;
+    for (int32_t g = 0; g < G; g++) {                    /* the group's mean query of the block */
+      block_mean(Q + (int64_t)g * L * D, D, t0, t1, m);
+      for (int32_t c = 0; c < D; c++) mg[c] += m[c];
+    }
+    for (int32_t c = 0; c < D; c++) mg[c] /= (double)G;
+    project(mg, Wq, D, R, qp + j * R);
     block_mean(K, D, t0, t1, m);
     project(m, Wk, D, R, kp + j * R);
   }
@@ -99,6 +110,7 @@ int orc_prefill_block_scores(const uint16_t* Q, const uint16_t* K, const uint16_
   free(qp);
   free(kp);
   free(m);
+  free(mg);
   return PF_OK;
 }
 

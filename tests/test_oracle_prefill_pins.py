@@ -3,8 +3,9 @@ LServe write-up's "3.1 预填充阶段优化" and the mathematics fix, each comp
 here another way:
 
   - the block score is the mean over a block pair of the low-rank logits
-    (Q W_q)(K_i W_k)^T / sqrt(d): numpy forms the whole token-by-token matrix
-    and averages its blocks (the oracle pools first, then projects);
+    (Q W_q)(K_i W_k)^T / sqrt(d), over every query head of the KV head's group:
+    numpy forms the whole token-by-token matrix of each head and averages its
+    blocks (the oracle pools first, then projects);
   - selection: numpy.lexsort on (score descending, block id ascending), the
     query's own block always kept, min(j + 1, budget / b) blocks in all;
   - attention: torch's scaled_dot_product_attention in fp64 with the mask
@@ -25,9 +26,15 @@ B = 64
 
 
 def inputs(L, seed=5, tied=False, planted=0, D=128):
+    """One query head (head 3, of KV head 1) and its KV head."""
     pf = W.Prefill("pin", seed, L, 4, 2, (0, 1), 16, 100, 512, 1 << 30, planted=planted, tied=tied)
     return (pf, W.prefill_rows(pf, "q", 3), W.prefill_rows(pf, "k", 1), W.prefill_rows(pf, "v", 1),
             W.prefill_projection(pf, "q"), W.prefill_projection(pf, "k"))
+
+
+def group(pf):
+    """The queries of KV head 1's group (query heads 2 and 3): [2][L][D]."""
+    return np.stack([W.prefill_rows(pf, "q", h) for h in (2, 3)])
 
 
 def f64(bits):
@@ -50,18 +57,20 @@ def causal(L):
 
 @pytest.mark.parametrize("L", [300, 512, 64 * 7 + 1])
 def test_block_score_is_the_mean_low_rank_logit_of_the_pair(L):
+    """Over every query row of the block in every query head of the group and
+    every key row of the key block."""
     pf, Q, K, V, Wq, Wk = inputs(L)
-    S = orc.prefill_block_scores(Q, K, Wq, Wk, B)
-    A = f64(Q) @ f64(Wq)
+    Qg = group(pf)
+    S = orc.prefill_block_scores(Qg, K, Wq, Wk, B)
     C = f64(K) @ f64(Wk)
-    logits = A @ C.T / np.sqrt(128)
+    logits = np.stack([(f64(q) @ f64(Wq)) @ C.T / np.sqrt(128) for q in Qg])     # [G][L][L]
     nb = -(-L // B)
     for j in range(nb):
         for i in range(nb):
             if i >= j:
                 assert np.isnan(S[j, i])
                 continue
-            want = logits[j * B:(j + 1) * B, i * B:(i + 1) * B].mean()
+            want = logits[:, j * B:(j + 1) * B, i * B:(i + 1) * B].mean()
             got = float(S[j, i])
             assert abs(got - want) <= 2 ** -23 * abs(want) + 1e-12, (j, i, got, want)
 
@@ -112,33 +121,37 @@ def test_dense_mode_is_causal_attention(L):
 def test_budget_covering_the_sequence_is_dense_attention():
     L = 64 * 9 + 20
     pf, Q, K, V, Wq, Wk = inputs(L)
-    out, lse, sel, cnt, S = orc.prefill_head(Q, K, V, Wq, Wk, b=B, dynamic=True, dense=False, budget=L + B)
+    Qg = group(pf)
+    out, lse, sel, cnt, S = orc.prefill_head(Qg, K, V, Wq, Wk, b=B, dynamic=True, dense=False, budget=L + B)
     assert (cnt == np.arange(1, cnt.size + 1)).all()
-    want, wlse = sdpa(Q, K, V, causal(L))
-    np.testing.assert_allclose(out, want, atol=1e-12, rtol=1e-10)
-    np.testing.assert_allclose(lse, wlse, atol=1e-12, rtol=1e-10)
+    for g in range(2):
+        want, wlse = sdpa(Qg[g], K, V, causal(L))
+        np.testing.assert_allclose(out[g], want, atol=1e-12, rtol=1e-10)
+        np.testing.assert_allclose(lse[g], wlse, atol=1e-12, rtol=1e-10)
 
 
 def test_one_block_sequence_is_dense_whatever_the_budget():
     pf, Q, K, V, Wq, Wk = inputs(50)
     out, lse, sel, cnt, S = orc.prefill_head(Q, K, V, Wq, Wk, b=B, dynamic=True, dense=False, budget=B)
     want, _ = sdpa(Q, K, V, causal(50))
-    np.testing.assert_allclose(out, want, atol=1e-12, rtol=1e-10)
+    np.testing.assert_allclose(out[0], want, atol=1e-12, rtol=1e-10)
 
 
 @pytest.mark.parametrize("budget", [64, 192, 320])
 def test_sparse_attention_is_causal_attention_inside_the_selected_blocks(budget):
     L = 64 * 11 + 33
     pf, Q, K, V, Wq, Wk = inputs(L, planted=2)
-    out, lse, sel, cnt, S = orc.prefill_head(Q, K, V, Wq, Wk, b=B, dynamic=True, dense=False, budget=budget)
+    Qg = group(pf)
+    out, lse, sel, cnt, S = orc.prefill_head(Qg, K, V, Wq, Wk, b=B, dynamic=True, dense=False, budget=budget)
     mask = np.zeros((L, L), bool)
     for t in range(L):
         for i in sel[t // B, :cnt[t // B]]:
             mask[t, i * B:min((i + 1) * B, t + 1)] = True
     assert (mask <= causal(L)).all() and mask[np.arange(L), np.arange(L)].all()
-    want, wlse = sdpa(Q, K, V, mask)
-    np.testing.assert_allclose(out, want, atol=1e-12, rtol=1e-10)
-    np.testing.assert_allclose(lse, wlse, atol=1e-12, rtol=1e-10)
+    for g in range(2):                       # both heads of the group use the KV head's selection
+        want, wlse = sdpa(Qg[g], K, V, mask)
+        np.testing.assert_allclose(out[g], want, atol=1e-12, rtol=1e-10)
+        np.testing.assert_allclose(lse[g], wlse, atol=1e-12, rtol=1e-10)
 
 
 @pytest.mark.parametrize("sink,window", [(16, 100), (0, 1), (64, 64), (3, 500)])
@@ -180,7 +193,7 @@ def test_planted_blocks_are_selected():
     """Sanity (not parity): with the tied random sketch, key blocks pulled along
     the queries' shared direction are among the last query block's choices."""
     pf = W.Prefill("plant", 9, 64 * 40, 4, 2, (0, 1), 16, 100, 640, 1 << 30, planted=4, tied=True)
-    Q, K = W.prefill_rows(pf, "q", 2), W.prefill_rows(pf, "k", 1)
+    Q, K = group(pf), W.prefill_rows(pf, "k", 1)
     Wq, Wk = W.prefill_projection(pf, "q"), W.prefill_projection(pf, "k")
     S = orc.prefill_block_scores(Q, K, Wq, Wk, B)
     sel, cnt = orc.prefill_select(S, 10)

@@ -326,6 +326,54 @@ spa_status spa_append_decode_attn(const spa_pool* pool, const spa_heads* heads,
                                   const int32_t* sel_phys, int32_t k_max, float* out, float* lse,
                                   void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---- prefill: block-sparse attention over a whole prompt ----------------
+ * LServe write-up "3.1 预填充阶段优化": for every query head i (KV head
+ * h = i / G) and position t of a sequence of L tokens,
+ *     out[i][t] = sum_{s in T(t)} softmax_s(q_i,t . k_h,s / sqrt(D)) v_h,s,
+ *     lse[i][t] = natural log of the softmax denominator,
+ * with blocks of b = 64 tokens and T(t) depending on the head's kind:
+ *   streaming head: s <= t with s < sink or s > t - window (sink + window);
+ *   dynamic head, L < dense_below: every s <= t (the write-up's dense
+ *       fallback below 32K tokens);
+ *   dynamic head otherwise: s <= t inside the key blocks selected for t's
+ *       block j: block j itself and the kb - 1 (kb = max(1, budget / 64)) best
+ *       earlier blocks by the low-rank importance score
+ *           S(j, i) = RN32( (qbar_j W_q) . (kbar_i W_k) / sqrt(D) ),
+ *       qbar_j the mean query of block j over the KV head's G query heads and
+ *       the block's tokens, kbar_i the mean key of block i, the projections
+ *       W_q, W_k bf16 [D][D / 8], evaluated in fp64 (the mean of the low-rank
+ *       logits (q W_q)(k W_k)^T / sqrt(D) over the block pair); best = score
+ *       descending, block id ascending; one selection per KV head serves its
+ *       whole query group.
+ * Inputs are the prompt's activations in position order (before they are
+ * written into the page pool): q bf16 [H_q][L][D], k and v bf16 [H_kv][L][D].
+ *   out: device fp32 [H_q][L][D]; lse: device fp32 [H_q][L] or NULL;
+ *   sel_blocks, sel_count: NULL, or device int32 [H_kv][nb][kb] and
+ *       [H_kv][nb] (nb = ceil(L / 64)) receiving each dynamic head's attended
+ *       blocks, ascending (written only when the heads select);
+ *   block_scores: NULL, or device fp32 [H_kv][nb][nb] receiving S(j, i) for
+ *       i < j of the dynamic heads (other entries unspecified);
+ *   ws, ws_bytes: workspace of spa_prefill_workspace_bytes() bytes.
+ * head_dim 128 and blocks of 64 only; with selection L <= 524288 (longer:
+ * SPA_ERR_UNSUPPORTED). L == 0 is a no-op. */
+typedef struct spa_prefill {
+  int32_t head_dim;      /* D, 128 */
+  int32_t block;         /* b, 64 */
+  int32_t budget;        /* tokens of key blocks per query block, the diagonal block included, >= 1 */
+  int32_t dense_below;   /* dynamic heads attend densely when L < dense_below (the write-up: 32768) */
+} spa_prefill;
+
+spa_status spa_prefill_attn(const spa_heads* heads, int32_t num_kv_heads, const spa_prefill* cfg,
+                            int64_t seq_len, const void* q, const void* k, const void* v,
+                            const void* w_q, const void* w_k, float* out, float* lse,
+                            int32_t* sel_blocks, int32_t* sel_count, float* block_scores,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes of spa_prefill_attn for these shapes (0 for invalid
+ * arguments). Needs no initialisation; calls sharing it must not overlap. */
+size_t spa_prefill_workspace_bytes(const spa_heads* heads, int32_t num_kv_heads, const spa_prefill* cfg,
+                                   int64_t seq_len);
+
 /* Workspace bytes needed by spa_select_pages and spa_sparse_decode_attn for
  * these shapes (one buffer serves both). Returns 0 for invalid arguments.
  * The workspace needs no initialisation and holds nothing between calls;

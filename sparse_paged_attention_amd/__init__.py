@@ -54,6 +54,11 @@ class c_heads(ctypes.Structure):
                 ("window", ctypes.c_int32), ("kind", ctypes.POINTER(ctypes.c_uint8))]
 
 
+class c_prefill(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("block", ctypes.c_int32), ("budget", ctypes.c_int32),
+                ("dense_below", ctypes.c_int32)]
+
+
 class c_batch(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("max_pages", ctypes.c_int32),
                 ("page_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
@@ -66,7 +71,7 @@ EXPORTS = ("spa_kv_pool_append", "spa_kv_pool_write", "spa_page_summary_update",
            "spa_default_budget", "spa_stream_ring_pages", "spa_alloc_create", "spa_alloc_pages", "spa_alloc_free",
            "spa_alloc_num_free", "spa_alloc_destroy", "spa_status_string", "spa_last_error",
            "spa_set_attn_blocks_per_item", "spa_probe_read_chunks",
-           "spa_sparse_decode_attn_noalloc")
+           "spa_sparse_decode_attn_noalloc", "spa_prefill_attn", "spa_prefill_workspace_bytes")
 
 _lib = None
 
@@ -104,6 +109,9 @@ def lib() -> ctypes.CDLL:
             "spa_last_error": ([], ctypes.c_char_p),
             "spa_probe_read_chunks": ([vp, sz, vp, i32, i32, vp, vp], ctypes.c_int),
             "spa_sparse_decode_attn_noalloc": ([P, H, B, vp, vp, vp, vp, vp, i32, vp, vp, vp], ctypes.c_int),
+            "spa_prefill_attn": ([H, i32, ctypes.POINTER(c_prefill), i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                  vp, sz, vp], ctypes.c_int),
+            "spa_prefill_workspace_bytes": ([H, i32, ctypes.POINTER(c_prefill), i64], sz),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -414,6 +422,56 @@ def sparse_decode_attn_noalloc(pool: Pool, heads: Heads, batch: Batch, q, sel_pa
     _check(lib().spa_sparse_decode_attn_noalloc(ctypes.byref(p), ctypes.byref(h), ctypes.byref(b), _ptr(q),
                                                 _ptr(sel_pages), _ptr(sel_count), _ptr(sel_len), _ptr(sel_phys),
                                                 k_max, _ptr(out), _ptr(lse), _stream(stream)))
+
+
+@dataclass
+class Prefill:
+    """Configuration of spa_prefill_attn: blocks of 64 tokens, `budget` tokens
+    of key blocks per query block (its own block included), dense attention
+    for the dynamic heads below `dense_below` tokens."""
+    budget: int = 4096
+    dense_below: int = 32768
+    block: int = 64
+    head_dim: int = HEAD_DIM
+
+    def c(self) -> c_prefill:
+        return c_prefill(self.head_dim, self.block, self.budget, self.dense_below)
+
+
+def prefill_workspace_bytes(heads: Heads, num_kv_heads: int, cfg: Prefill, seq_len: int) -> int:
+    h = heads.c()
+    n = lib().spa_prefill_workspace_bytes(ctypes.byref(h), num_kv_heads, ctypes.byref(cfg.c()), seq_len)
+    if n == 0:
+        raise SpaError(SPA_ERR_INVALID, "prefill_workspace_bytes: invalid shapes")
+    return n
+
+
+def prefill_attn(heads: Heads, cfg: Prefill, q, k, v, w_q, w_k, out, lse=None, sel_blocks=None, sel_count=None,
+                 block_scores=None, workspace=None, stream=None) -> None:
+    """spa_prefill_attn: q bf16 [H_q][L][D], k, v bf16 [H_kv][L][D], w_q, w_k bf16
+    [D][D / 8]; out fp32 [H_q][L][D], lse fp32 [H_q][L] or None; optional
+    sel_blocks int32 [H_kv][nb][kb], sel_count int32 [H_kv][nb], block_scores
+    fp32 [H_kv][nb][nb] (nb = ceil(L / 64), kb = max(1, budget / 64) capped at nb)."""
+    hkv = len(heads.kind)
+    _need(q, (heads.num_q_heads, None, HEAD_DIM), "bf16", "q")
+    L = q.shape[1]
+    _need(k, (hkv, L, HEAD_DIM), "bf16", "k")
+    _need(v, (hkv, L, HEAD_DIM), "bf16", "v")
+    _need(w_q, (HEAD_DIM, HEAD_DIM // 8), "bf16", "w_q", optional=True)
+    _need(w_k, (HEAD_DIM, HEAD_DIM // 8), "bf16", "w_k", optional=True)
+    _need(out, (heads.num_q_heads, L, HEAD_DIM), "f32", "out")
+    _need(lse, (heads.num_q_heads, L), "f32", "lse", optional=True)
+    nb = -(-L // 64)
+    kb = min(max(1, cfg.budget // 64), max(nb, 1))
+    _need(sel_blocks, (hkv, nb, kb), "i32", "sel_blocks", optional=True)
+    _need(sel_count, (hkv, nb), "i32", "sel_count", optional=True)
+    _need(block_scores, (hkv, nb, nb), "f32", "block_scores", optional=True)
+    _need(workspace, (None,), "u8", "workspace", optional=True)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    h = heads.c()
+    _check(lib().spa_prefill_attn(ctypes.byref(h), hkv, ctypes.byref(cfg.c()), L, _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(w_q), _ptr(w_k), _ptr(out), _ptr(lse), _ptr(sel_blocks), _ptr(sel_count),
+                                  _ptr(block_scores), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def set_attn_blocks_per_item(blocks: int) -> None:

@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libspa.so")
-SOURCES = ["api.cpp", "pool.hip", "select.hip", "attn.hip", "probe.hip"]
+SOURCES = ["api.cpp", "pool.hip", "select.hip", "attn.hip", "prefill.hip", "probe.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -583,6 +583,114 @@ spa_status spa_append_decode_attn(const spa_pool* pool, const spa_heads* heads, 
                      lse, ws, ws_bytes, stream, "append_decode_attn launch");
 }
 
+// ------------------------------------------------------------- prefill
+
+namespace {
+
+struct PrefillPlan {
+  int32_t G, nb, kb, sparse, any_dynamic;
+  uint32_t dyn_mask[spa::kMaxKvHeads / 32];
+  size_t qp_off, kp_off, sel_off, cnt_off, bytes;
+};
+
+spa_status check_prefill(const spa_heads* heads, int32_t hkv, const spa_prefill* cfg, int64_t L,
+                         PrefillPlan* pp) {
+  if (!cfg) return fail(SPA_ERR_INVALID, "cfg is NULL");
+  if (hkv < 1 || hkv > spa::kMaxKvHeads) return fail(SPA_ERR_INVALID, "num_kv_heads %d outside [1, %d]", hkv,
+                                                     spa::kMaxKvHeads);
+  if (cfg->head_dim != spa::kHeadDim)
+    return fail(cfg->head_dim < 1 ? SPA_ERR_INVALID : SPA_ERR_UNSUPPORTED, "head_dim %d: only 128 is built",
+                cfg->head_dim);
+  if (cfg->block != spa::kPrefillBlock)
+    return fail(cfg->block < 1 ? SPA_ERR_INVALID : SPA_ERR_UNSUPPORTED, "block %d: only 64 is built",
+                cfg->block);
+  if (cfg->budget < 1) return fail(SPA_ERR_INVALID, "budget %d < 1", cfg->budget);
+  if (L < 0) return fail(SPA_ERR_INVALID, "seq_len %lld < 0", (long long)L);
+  if (L > ((int64_t)1 << 31) / spa::kHeadDim) return fail(SPA_ERR_UNSUPPORTED, "seq_len %lld too long", (long long)L);
+  spa::PoolArgs pl{};
+  pl.hkv = hkv;
+  pl.hs = hkv;
+  pl.summ = reinterpret_cast<uint16_t*>(1);       // summaries are not used here
+  spa::HeadList dyn;
+  uint8_t kind[spa::kMaxKvHeads];
+  int32_t G;
+  spa_status s;
+  if ((s = check_heads(heads, pl, &G, &dyn, kind)) != SPA_OK) return s;
+  std::memset(pp, 0, sizeof *pp);
+  pp->G = G;
+  pp->nb = (int32_t)((L + spa::kPrefillBlock - 1) / spa::kPrefillBlock);
+  pp->kb = std::max(1, cfg->budget / spa::kPrefillBlock);
+  pp->kb = std::min(pp->kb, std::max(pp->nb, 1));
+  pp->any_dynamic = dyn.n > 0;
+  for (int32_t h = 0; h < hkv; ++h)
+    if (kind[h]) pp->dyn_mask[h / 32] |= 1u << (h % 32);
+  pp->sparse = dyn.n > 0 && L >= cfg->dense_below;
+  if (pp->sparse && pp->nb > spa::kPrefillMaxBlocks)
+    return fail(SPA_ERR_UNSUPPORTED, "seq_len %lld: selection rows hold at most %d blocks of 64", (long long)L,
+                spa::kPrefillMaxBlocks);
+  size_t o = 0;
+  if (pp->sparse) {
+    const size_t proj = (size_t)hkv * pp->nb * (spa::kHeadDim / 8) * sizeof(double);
+    pp->qp_off = o; o = align_up(o + proj);
+    pp->kp_off = o; o = align_up(o + proj);
+    pp->sel_off = o; o = align_up(o + (size_t)hkv * pp->nb * pp->kb * sizeof(int32_t));
+    pp->cnt_off = o; o = align_up(o + (size_t)hkv * pp->nb * sizeof(int32_t));
+  }
+  pp->bytes = std::max<size_t>(o, 256);
+  return SPA_OK;
+}
+
+}  // namespace
+
+size_t spa_prefill_workspace_bytes(const spa_heads* heads, int32_t num_kv_heads, const spa_prefill* cfg,
+                                   int64_t seq_len) {
+  const std::string keep = g_last_error;
+  PrefillPlan pp;
+  const size_t n = check_prefill(heads, num_kv_heads, cfg, seq_len, &pp) == SPA_OK ? pp.bytes : 0;
+  g_last_error = keep;
+  return n;
+}
+
+spa_status spa_prefill_attn(const spa_heads* heads, int32_t num_kv_heads, const spa_prefill* cfg, int64_t seq_len,
+                            const void* q, const void* k, const void* v, const void* w_q, const void* w_k,
+                            float* out, float* lse, int32_t* sel_blocks, int32_t* sel_count, float* block_scores,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+  PrefillPlan pp;
+  spa_status s;
+  if ((s = check_prefill(heads, num_kv_heads, cfg, seq_len, &pp)) != SPA_OK) return s;
+  if (seq_len == 0) return ok();
+  if (!q || !k || !v || !out) return fail(SPA_ERR_INVALID, "q / k / v / out is NULL");
+  if (pp.sparse && (!w_q || !w_k)) return fail(SPA_ERR_INVALID, "w_q / w_k is NULL (the dynamic heads select)");
+  if (!ws || ws_bytes < pp.bytes) return fail(SPA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes,
+                                              pp.bytes);
+  spa::PrefillArgs a{};
+  a.hq = heads->num_q_heads;
+  a.hkv = num_kv_heads;
+  a.G = pp.G;
+  a.L = seq_len;
+  a.nb = pp.nb;
+  a.kb = pp.kb;
+  a.sink = heads->sink;
+  a.window = heads->window;
+  a.dense = !pp.sparse;
+  a.any_dynamic = pp.any_dynamic;
+  std::memcpy(a.dyn_mask, pp.dyn_mask, sizeof a.dyn_mask);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.wq = static_cast<const uint16_t*>(w_q);
+  a.wk = static_cast<const uint16_t*>(w_k);
+  char* w = static_cast<char*>(ws);
+  a.qp = reinterpret_cast<double*>(w + pp.qp_off);
+  a.kp = reinterpret_cast<double*>(w + pp.kp_off);
+  a.sel = sel_blocks ? sel_blocks : reinterpret_cast<int32_t*>(w + pp.sel_off);
+  a.cnt = sel_count ? sel_count : reinterpret_cast<int32_t*>(w + pp.cnt_off);
+  a.scores = block_scores;
+  a.out = out;
+  a.lse = lse;
+  return hip_status(spa::launch_prefill(a, stream), "prefill_attn launch");
+}
+
 // ------------------------------------------------------------- allocator
 
 struct spa_allocator {

@@ -68,6 +68,36 @@ struct AttnPlan {
   int64_t sel_mask;                      // ~0 with dynamic heads, 0 without (selection unused)
 };
 
+// Prefill block-sparse attention (spa_prefill_attn): a sequence's queries
+// [H_q][L][D] and keys / values [H_kv][L][D] in position order.
+constexpr int kPrefillBlock = 64;              // tokens per query / key block
+constexpr int kPrefillMaxBlocks = 8192;        // blocks a selection row holds (L <= 524288)
+
+struct PrefillArgs {
+  int32_t hq, hkv, G;
+  int64_t L;
+  int32_t nb;                 // blocks: ceil(L / 64)
+  int32_t kb;                 // key blocks per query block, the diagonal one included
+  int32_t sink, window;       // streaming heads
+  int32_t dense;              // 1: dynamic heads attend every earlier token (no selection)
+  int32_t any_dynamic;
+  uint32_t dyn_mask[kMaxKvHeads / 32];
+  const uint16_t* q;          // [H_q][L][D]
+  const uint16_t* k;          // [H_kv][L][D]
+  const uint16_t* v;
+  const uint16_t* wq;         // [D][D / 8]
+  const uint16_t* wk;
+  double* qp;                 // [H_kv][nb][D / 8]: projected group-mean queries of each block
+  double* kp;                 // [H_kv][nb][D / 8]: projected mean keys
+  int32_t* sel;               // [H_kv][nb][kb]: attended key blocks of each query block, ascending
+  int32_t* cnt;               // [H_kv][nb]
+  float* scores;              // NULL or [H_kv][nb][nb]: block scores (entries i < j)
+  float* out;                 // [H_q][L][D]
+  float* lse;                 // NULL or [H_q][L]
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+
 // Bytes of the static scratch array of the attention entry point that
 // allocates nothing (spa_sparse_decode_attn_noalloc), per GPU.
 constexpr size_t kScratchBytes = SPA_NOALLOC_SCRATCH_BYTES;

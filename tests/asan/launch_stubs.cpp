@@ -55,6 +55,10 @@ hipError_t launch_attn(const PoolArgs&, const BatchArgs&, const AttnPlan&, int32
   ++g_launches;
   return hipSuccess;
 }
+hipError_t launch_prefill(const PrefillArgs&, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
 }  // namespace spa
 
 // The read probe lives in its own kernel file; a stand-in keeps the export list whole.

@@ -1,0 +1,172 @@
+"""GPU parity of prefill block-sparse attention (spa_prefill_attn, through the
+C ABI) against the prefill oracle on the same seeded inputs (LServe write-up
+"3.1 预填充阶段优化"):
+  - block scores within 1e-6 relative of the oracle's (both fp64, one
+    rounding to fp32; the summation orders differ);
+  - selected blocks identical, except where the oracle's k-th and (k+1)-th
+    scores of a row are within 1e-6 relative (then the GPU's blocks must still
+    be a valid choice: each scores at least the oracle's k-th less 1e-6
+    relative), and the oracle's attention is recomputed with the GPU's blocks;
+  - outputs within 2e-3 max-abs, lse within 1e-3."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity import LSE_TOL, OUT_TOL, TIE_REL, bits_to_bf16, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_paged_attention_amd as spa
+    spa.lib()
+    oracle.build()
+
+
+def run_gpu(pf: W.Prefill, Qb, Kb, Vb, Wq, Wk):
+    import sparse_paged_attention_amd as spa
+    heads = spa.Heads(pf.hq, pf.kind, pf.sink, pf.window)
+    cfg = spa.Prefill(budget=pf.budget, dense_below=pf.dense_below, block=pf.block)
+    L = pf.L
+    nb = -(-L // 64)
+    kb = min(max(1, pf.budget // 64), nb)
+    q, k, v = bits_to_bf16(Qb), bits_to_bf16(Kb), bits_to_bf16(Vb)
+    wq, wk = bits_to_bf16(Wq), bits_to_bf16(Wk)
+    out = torch.full((pf.hq, L, 128), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((pf.hq, L), float("nan"), dtype=torch.float32, device="cuda")
+    sel = torch.full((pf.hkv, nb, kb), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((pf.hkv, nb), dtype=torch.int32, device="cuda")
+    scores = torch.full((pf.hkv, nb, nb), float("nan"), dtype=torch.float32, device="cuda") if nb <= 4096 else None
+    ws = torch.empty(spa.prefill_workspace_bytes(heads, pf.hkv, cfg, L), dtype=torch.uint8, device="cuda")
+    spa.prefill_attn(heads, cfg, q, k, v, wq, wk, out, lse, sel, cnt, scores, ws)
+    torch.cuda.synchronize()
+    return (out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), sel.cpu().numpy(),
+            cnt.cpu().numpy(), None if scores is None else scores.cpu().numpy())
+
+
+def inputs(pf: W.Prefill):
+    Qb = np.stack([W.prefill_rows(pf, "q", i) for i in range(pf.hq)])
+    Kb = np.stack([W.prefill_rows(pf, "k", h) for h in range(pf.hkv)])
+    Vb = np.stack([W.prefill_rows(pf, "v", h) for h in range(pf.hkv)])
+    return Qb, Kb, Vb, W.prefill_projection(pf, "q"), W.prefill_projection(pf, "k")
+
+
+def check(pf: W.Prefill, rows=None) -> dict:
+    """Runs the prefill on the GPU and checks it against the oracle (every row,
+    or the query positions `rows` of every head). Returns a small report."""
+    log(f"[prefill] {pf.name} L={pf.L} hq={pf.hq} hkv={pf.hkv} kind={pf.kind} budget={pf.budget} "
+        f"dense_below={pf.dense_below} rows={'all' if rows is None else len(rows)}")
+    Qb, Kb, Vb, Wq, Wk = inputs(pf)
+    out, lse, gsel, gcnt, gscores = run_gpu(pf, Qb, Kb, Vb, Wq, Wk)
+    G, b = pf.G, pf.block
+    dense = pf.L < pf.dense_below
+    rep = dict(max_err=0.0, max_lse_err=0.0, ties=0, rows_checked=0, sel_rows=0)
+    for h in range(pf.hkv):
+        dyn = bool(pf.kind[h])
+        Qg = Qb[h * G:(h + 1) * G]
+        o_out, o_lse, osel, ocnt, oS = oracle.prefill_head(Qg, Kb[h], Vb[h], Wq, Wk, b=b, dynamic=dyn, dense=dense,
+                                                           budget=pf.budget, sink=pf.sink, window=pf.window,
+                                                           rows=rows)
+        if dyn and not dense:
+            nb = oS.shape[0]
+            if gscores is not None:
+                gs, os_ = gscores[h], oS
+                low = np.tril(np.ones((nb, nb), bool), -1)
+                rel = np.abs(gs[low].astype(np.float64) - os_[low]) / np.maximum(np.abs(os_[low]), 1e-30)
+                assert (rel <= 1e-6).all() or (np.abs(gs[low] - os_[low]) <= 1e-12).all(), \
+                    f"head {h}: block scores differ by up to {rel.max():.2e} relative"
+            redo = False
+            for j in range(nb):
+                rep["sel_rows"] += 1
+                gj = gsel[h, j, :gcnt[h, j]]
+                oj = osel[j, :ocnt[j]]
+                if np.array_equal(gj, oj):
+                    continue
+                k = int(ocnt[j]) - 1
+                srt = np.sort(oS[j, :j])[::-1]
+                kth = float(srt[k - 1])
+                near = k < srt.size and abs(kth - float(srt[k])) <= TIE_REL * abs(kth)
+                ok = (gj.size == oj.size and gj[-1] == j and np.unique(gj).size == gj.size
+                      and bool((oS[j, gj[:-1]] >= kth - TIE_REL * abs(kth)).all()))
+                assert near and ok, (f"head {h} block {j}: selection differs (gpu {gj.tolist()[:8]}..., "
+                                     f"oracle {oj.tolist()[:8]}...)")
+                rep["ties"] += 1
+                osel[j, :gj.size] = gj
+                redo = True
+            if redo:
+                res = [oracle.prefill_attend(Qg[g], Kb[h], Vb[h], b, oracle.PREFILL_SPARSE, sel=osel, cnt=ocnt,
+                                             rows=rows) for g in range(G)]
+                o_out = np.stack([r[0] for r in res])
+                o_lse = np.stack([r[1] for r in res])
+        for g in range(G):
+            i = h * G + g
+            go = out[i] if rows is None else out[i][rows]
+            gl = lse[i] if rows is None else lse[i][rows]
+            err = float(np.abs(go - o_out[g]).max())
+            lerr = float(np.abs(gl - o_lse[g]).max())
+            rep["max_err"] = max(rep["max_err"], err)
+            rep["max_lse_err"] = max(rep["max_lse_err"], lerr)
+            rep["rows_checked"] += go.shape[0]
+    log(f"  {pf.name}: max_err={rep['max_err']:.2e} lse_err={rep['max_lse_err']:.2e} ties={rep['ties']} "
+        f"rows={rep['rows_checked']} selection rows={rep['sel_rows']}")
+    assert rep["max_err"] <= OUT_TOL and rep["max_lse_err"] <= LSE_TOL, rep
+    return rep
+
+
+SMALL = W.Prefill("prefill_small", 3001, 64 * 20 + 37, 8, 2, (0, 1), 16, 100, 320, 1000, planted=3)
+
+
+def test_sparse_small():
+    """Selection on (L above the threshold), 21 blocks with a ragged last one,
+    5 key blocks per query block, a planted block, one streaming head."""
+    rep = check(SMALL)
+    assert rep["sel_rows"] == 21
+
+
+def test_dense_below_the_threshold():
+    check(SMALL.scaled(name="prefill_dense", L=900))
+
+
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2), (16, 2), (32, 2)])
+def test_group_sizes(hq, hkv):
+    """G = 1, 2, 8, 16 (the 4-head work-groups split larger groups)."""
+    check(SMALL.scaled(name=f"prefill_g{hq // hkv}", hq=hq, hkv=hkv, L=64 * 9 + 5, budget=192, dense_below=100))
+
+
+@pytest.mark.parametrize("L", [1, 63, 64, 65, 129])
+def test_short_sequences(L):
+    check(SMALL.scaled(name=f"prefill_L{L}", L=L, dense_below=1, budget=64))
+
+
+def test_budget_covering_the_sequence():
+    check(SMALL.scaled(name="prefill_full_budget", L=64 * 12 + 1, budget=64 * 13, dense_below=1))
+
+
+def test_untied_projections_and_mha():
+    check(W.Prefill("prefill_untied", 3002, 64 * 16, 4, 4, (1, 0, 1, 1), 8, 70, 256, 512, planted=2, tied=False))
+
+
+def test_streaming_windows_and_sinks():
+    """Windows shorter than, equal to and longer than a block; sinks inside one
+    block and across two."""
+    for sink, window in ((5, 30), (64, 64), (100, 200)):
+        check(SMALL.scaled(name=f"prefill_stream_{sink}_{window}", kind=(0, 0), sink=sink, window=window,
+                           L=64 * 7 + 11))
+
+
+def test_128k_full_size_sampled_rows():
+    """The 128K prompt at Llama-3-8B attention shape (32 q / 8 KV heads, 4
+    dynamic, budget 4096, threshold 32K): every dynamic head's selection row
+    against the oracle's, and 48 sampled positions of every query head
+    (first, ragged and last blocks among them) against the oracle's rows."""
+    pf = W.PREFILLS["prefill_128k"]
+    rng = np.random.default_rng(17)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 4095, 32768, pf.L - 64, pf.L - 1],
+                                     rng.integers(0, pf.L, 40)])).astype(np.int64)
+    rep = check(pf, rows=rows)
+    assert rep["sel_rows"] == 4 * 2048

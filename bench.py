@@ -224,6 +224,146 @@ def read_ceiling(torch, spa, chunks: int, replicas: int, replays: int) -> dict:
     return {"GBps": best, "per_wave": res, "bytes_per_launch": chunks * 4096}
 
 
+def prefill_flops(pf, dense: bool) -> int:
+    """Algorithmic flops of one prefill call: 4 D per attended (query, key)
+    pair (the q.k product and the weighted sum of v), summed over the query
+    heads; the dynamic heads attend causally inside min(j + 1, kb) key blocks
+    of query block j (dense: all of them), the streaming heads their sink and
+    window."""
+    L, b, D = pf.L, pf.block, pf.d
+    t = np.arange(L, dtype=np.int64)
+    s0 = np.minimum(pf.sink, t + 1)
+    w_lo = np.maximum(pf.sink, t + 1 - pf.window)
+    stream_pairs = int((s0 + np.maximum(0, t + 1 - w_lo)).sum())
+    nb = -(-L // b)
+    kb = nb if dense else min(max(1, pf.budget // b), nb)
+    dyn_pairs = 0
+    for j in range(nb):
+        rows = min(b, L - j * b)
+        earlier = min(j + 1, kb) - 1                       # full earlier key blocks
+        dyn_pairs += rows * earlier * b + rows * (rows + 1) // 2
+    n_dyn = sum(pf.kind)
+    return 4 * D * pf.G * (n_dyn * dyn_pairs + (pf.hkv - n_dyn) * stream_pairs)
+
+
+def bench_prefill(args) -> int:
+    """spa_prefill_attn on a whole prompt: the time per call (median of
+    timed calls with HIP events), the same prompt in dense mode, algorithmic
+    MFMA throughput, and the oracle on sampled rows as the CPU baseline."""
+    import torch
+    import workloads as W
+    import sparse_paged_attention_amd as spa
+    spa.lib()
+    torch.cuda.set_device(0)
+    pf = W.PREFILLS[args.workload]
+    t_setup = time.time()
+    Qb = np.stack([W.prefill_rows(pf, "q", i) for i in range(pf.hq)])
+    Kb = np.stack([W.prefill_rows(pf, "k", h) for h in range(pf.hkv)])
+    Vb = np.stack([W.prefill_rows(pf, "v", h) for h in range(pf.hkv)])
+    Wq, Wk = W.prefill_projection(pf, "q"), W.prefill_projection(pf, "k")
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    q, k, v, wq, wk = dev(Qb), dev(Kb), dev(Vb), dev(Wq), dev(Wk)
+    heads = spa.Heads(pf.hq, pf.kind, pf.sink, pf.window)
+    out = torch.empty((pf.hq, pf.L, pf.d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((pf.hq, pf.L), dtype=torch.float32, device="cuda")
+    log(f"[bench] prefill setup {time.time() - t_setup:.1f}s")
+    reps = max(5, min(args.steps, 20))
+
+    def timed(cfg) -> dict:
+        ws = torch.empty(spa.prefill_workspace_bytes(heads, pf.hkv, cfg, pf.L), dtype=torch.uint8, device="cuda")
+        for _ in range(2):
+            spa.prefill_attn(heads, cfg, q, k, v, wq, wk, out, lse, workspace=ws)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in evs:
+            e0.record()
+            spa.prefill_attn(heads, cfg, q, k, v, wq, wk, out, lse, workspace=ws)
+            e1.record()
+        torch.cuda.synchronize()
+        return percentiles([e0.elapsed_time(e1) for e0, e1 in evs])
+
+    dense_mode = pf.L < pf.dense_below
+    cfg = spa.Prefill(budget=pf.budget, dense_below=pf.dense_below)
+    t = timed(cfg)
+    flops = prefill_flops(pf, dense_mode)
+    tflops = flops / (t["median"] * 1e-3) / 1e12
+    dense = None
+    if not dense_mode:
+        td = timed(spa.Prefill(budget=pf.budget, dense_below=pf.L + 1))
+        dflops = prefill_flops(pf, True)
+        dense = {"ms": td, "flops": dflops, "TFLOPs": round(dflops / (td["median"] * 1e-3) / 1e12, 1),
+                 "speedup_of_sparse": round(td["median"] / t["median"], 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build()
+        rng = np.random.default_rng(3)
+        G = pf.G
+        sel_s = 0.0
+        modes = []
+        for h in range(pf.hkv):                     # the selection of every dynamic head (whole)
+            dyn = bool(pf.kind[h])
+            ts = time.perf_counter()
+            if dyn and not dense_mode:
+                S = oracle.prefill_block_scores(Qb[h * G:(h + 1) * G], Kb[h], Wq, Wk, pf.block)
+                sel, cnt = oracle.prefill_select(S, max(1, pf.budget // pf.block))
+                sel_s += time.perf_counter() - ts
+                modes.append((oracle.PREFILL_SPARSE, dict(sel=sel, cnt=cnt)))
+            else:
+                modes.append((oracle.PREFILL_DENSE, {}) if dyn else
+                             (oracle.PREFILL_STREAMING, dict(sink=pf.sink, window=pf.window)))
+        t0 = time.perf_counter()
+        n_rows = 0
+        while time.perf_counter() - t0 < 10.0:       # uniformly sampled rows of every query head
+            rows = np.sort(rng.integers(0, pf.L, 64)).astype(np.int64)
+            for h in range(pf.hkv):
+                mode, kw = modes[h]
+                for g in range(G):
+                    oracle.prefill_attend(Qb[h * G + g], Kb[h], Vb[h], pf.block, mode, rows=rows, **kw)
+                    n_rows += rows.size
+        row_s = (time.perf_counter() - t0) / n_rows
+        dt = time.perf_counter() - t0
+        est = sel_s + row_s * pf.L * pf.hq
+        cpu = {"value": round(est * 1e3, 1), "unit": "ms", "cores": oracle.num_threads(), "kind": "oracle",
+               **host_info(),
+               "sample": f"block scores and selection of all {sum(pf.kind)} dynamic KV heads ({sel_s:.1f} s) and "
+                         f"{n_rows} sampled query rows over all {pf.hq} query heads ({dt - sel_s:.1f} s), fp64 "
+                         f"oracle, scaled to all {pf.L * pf.hq} rows"}
+
+    res = {
+        "metric": f"prefill block-sparse attention ms at {pf.L // 1024}K ctx (one layer, LServe write-up 3.1)",
+        "value": t["median"],
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": reps,
+        "warmup": 2,
+        "ms_per_step": t["median"],
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 (fp32 accumulate, fp64 block scores)",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: one sequence of {pf.L} tokens, {pf.hq} q / {pf.hkv} kv heads, "
+                               f"d {pf.d}, blocks of {pf.block}, kv heads "
+                               f"{[h for h in range(pf.hkv) if not pf.kind[h]]} streaming (sink {pf.sink} + window "
+                               f"{pf.window}), the others dynamic with {pf.budget} key tokens per query block, "
+                               f"dense below {pf.dense_below} tokens ({'dense' if dense_mode else 'sparse'} here), "
+                               f"random low-rank sketch d -> d/8 as W_q = W_k"},
+        "timing": {"call_ms": t},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(tflops / 2500.0, 4), "traffic": None, "flops_per_call": int(flops),
+                     "kernel": "spa_prefill_attn (pool_kernel + select_kernel + attn_kernel), algorithmic flops "
+                               "(4 d per attended query-key pair)"},
+        "dense_mode": dense,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -231,7 +371,8 @@ def main() -> int:
                     help="layer-steps to time at least (rounded up to whole reuse cycles of every replica, "
                          "and to at least 20 replays of one cycle)")
     ap.add_argument("--warmup", type=int, default=16, help="untimed layer-steps before (at least one cycle)")
-    ap.add_argument("--workload", choices=tuple(WORKLOADS), default="llama3_128k")
+    ap.add_argument("--workload", choices=tuple(WORKLOADS) + ("prefill_128k", "prefill_16k"), default="llama3_128k",
+                    help="decode workloads, or prefill_128k / prefill_16k: block-sparse prefill attention")
     ap.add_argument("--replicas", type=int, default=0, help="layer replicas the steps cycle over (0: per workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the read-ceiling probe")
@@ -250,6 +391,9 @@ def main() -> int:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no multi-GPU "
               f"path; the sharding by KV head it would use moves no data between GPUs.", file=sys.stderr)
         return 2
+
+    if args.workload.startswith("prefill"):
+        return bench_prefill(args)
 
     import torch
     import workloads as W

@@ -442,9 +442,12 @@ static double q8_value(const uint8_t* codes, const float* scales, int64_t t, int
 }
 
 /* PAGE "2.1" min-max pooling over the dequantized keys of fp8 pages: the
- * channel-wise min and max of each logical page, computed exactly, then
- * rounded outward to bf16 (min down, max up), so that a bf16 summary still
- * bounds every key of its page. */
+ * channel-wise min and max of each logical page, computed exactly in IEEE
+ * totalOrder (-0 below +0, the order of the bf16 summaries), then rounded
+ * outward to bf16 (min down, max up), so that a bf16 summary still bounds
+ * every key of its page. Rounding outward is monotone in that order, so a
+ * page's summary after one more key is the min / max of its summary before
+ * and the new key rounded outward. */
 int orc_page_summary_q8(const uint8_t* Kc, const float* Ks, int64_t L, int32_t D,
                         int32_t p, uint16_t* kmin, uint16_t* kmax) {
   if (!Kc || !Ks || !kmin || !kmax || L < 0 || D < 1 || p < 1) return ORC_ERR_ARG;
@@ -456,8 +459,8 @@ int orc_page_summary_q8(const uint8_t* Kc, const float* Ks, int64_t L, int32_t D
       for (int64_t t = t0; t < t1; t++) {
         double v = q8_value(Kc, Ks, t, D, c);
         if (!isfinite(v)) return ORC_ERR_NONFINITE;
-        if (v < lo) lo = v;
-        if (v > hi) hi = v;
+        if (v < lo || (v == lo && signbit(v))) lo = v;        /* -0 below +0 */
+        if (v > hi || (v == hi && !signbit(v))) hi = v;
       }
       kmin[j * D + c] = bf16_down(lo);
       kmax[j * D + c] = bf16_up(hi);

@@ -214,12 +214,75 @@ def pow2_scaled(orc, rng, L):
 
 
 def test_page_summary_q8_exact_keys_equal_bf16_summary(orc):
+    """With every dequantized key exactly a bf16 value, the fp8 summary is the
+    bf16 summary of those keys bit for bit (the same totalOrder, -0 < +0)."""
     Kc, Ks, Kb = pow2_scaled(orc, np.random.default_rng(4), 100)
+    Kc[5, :7] = 0x80                                  # -0 codes next to +0 ones
+    Kc[6, :7] = 0x00
+    Kc[21, 3] = 0x80
+    Kb = bf16_bits(dequant(Kc, Ks))
     a = orc.page_summary_q8(Kc, Ks, 16)
     b = orc.page_summary(Kb, 16)
-    # the same values; a page minimum of -0 and +0 may differ in sign only
     for x, y in zip(a, b):
-        assert np.array_equal(bf16_values(x), bf16_values(y))
+        assert np.array_equal(x, y)
+
+
+def _order(bits):
+    """bf16 patterns -> keys ordered like IEEE totalOrder (-0 < +0)."""
+    b = np.asarray(bits, np.uint32)
+    return np.where(b & 0x8000, (~b) & 0xFFFF, b | 0x8000)
+
+
+def test_page_summary_q8_grows_by_merging_the_new_key(orc):
+    """Appending a key to a page changes its summary to the min / max (in
+    totalOrder) of the old summary and the new key rounded outward -- what an
+    append may do without re-reading the page. Pages mixing -0 and +0 keys,
+    keys below the smallest bf16 subnormal, both signs."""
+    rng = np.random.default_rng(31)
+    for trial in range(12):
+        p = 16
+        rows = rand_rows(rng, p)
+        if trial % 3 == 0:
+            rows[rng.random((p, 128)) < 0.3] = 0x8000          # -0
+        if trial % 3 == 1:
+            rows[rng.random((p, 128)) < 0.3] = 0x0000
+        Kc, Ks = orc.quantize_rows(rows)
+        if trial % 4 == 2:                                      # scales far below the bf16 range
+            Ks = (Ks * np.float32(2.0 ** -140)).astype(np.float32)
+            Kc[rng.random((p, 128)) < 0.2] = 0x80
+        vals = dequant(Kc, Ks)
+        for i in range(1, p):
+            old_min, old_max = orc.page_summary_q8(Kc[:i], Ks[:i], p)
+            new_min, new_max = orc.page_summary_q8(Kc[:i + 1], Ks[:i + 1], p)
+            dn = orc.bf16_round_outward(vals[i], True)
+            up = orc.bf16_round_outward(vals[i], False)
+            want_min = np.where(_order(dn) < _order(old_min[0]), dn, old_min[0])
+            want_max = np.where(_order(up) > _order(old_max[0]), up, old_max[0])
+            assert np.array_equal(new_min[0], want_min), (trial, i)
+            assert np.array_equal(new_max[0], want_max), (trial, i)
+
+
+def test_page_summary_q8_signed_zeros(orc):
+    """-0 sorts below +0 whatever the position: a page of +0 keys then a -0 key
+    has minimum -0 and maximum +0, and so does a page of -0 then +0; a key
+    below the smallest bf16 subnormal rounds down to +0 (positive) or to the
+    negative smallest subnormal."""
+    X = np.zeros((4, 128), np.uint16)
+    X[1, :] = 0x8000
+    Kc, Ks = orc.quantize_rows(X)                 # zero rows: scale 0, codes +0
+    Kc[1, :] = 0x80                               # -0 codes
+    Ks[:] = 1.0
+    for order in ([0, 1], [1, 0], [0, 0, 1, 0]):
+        kmin, kmax = orc.page_summary_q8(Kc[order], Ks[order], 16)
+        assert (kmin[0] == 0x8000).all() and (kmax[0] == 0x0000).all(), order
+    kmin, kmax = orc.page_summary_q8(Kc[[0, 0]], Ks[[0, 0]], 16)
+    assert (kmin[0] == 0x0000).all() and (kmax[0] == 0x0000).all()
+    tiny = np.zeros((1, 128), np.uint8)
+    tiny[0, :] = 0x01                              # smallest positive code, 2^-9
+    kmin, kmax = orc.page_summary_q8(tiny, np.array([2.0 ** -140], np.float32), 16)
+    assert (kmin[0] == 0x0000).all() and (kmax[0] == 0x0001).all()
+    kmin, kmax = orc.page_summary_q8(tiny | 0x80, np.array([2.0 ** -140], np.float32), 16)
+    assert (kmin[0] == 0x8001).all() and (kmax[0] == 0x8000).all()
 
 
 # ------------------------------------------------------------ attention

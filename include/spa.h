@@ -100,10 +100,13 @@ typedef struct spa_pool {
    * division), code = x / scale (fp32 division) rounded to the nearest E4M3
    * value, ties to even; a row of zeros has scale 0 and codes 0. The writes
    * (spa_kv_pool_write, spa_kv_pool_append) quantize the caller's bf16 rows;
-   * summaries stay bf16: the exact min / max of the dequantized keys rounded
-   * outward (min down, max up), so each still bounds every q.k of its page.
-   * On fp8 pools the append entry points run the append as a launch of its
-   * own ahead of the selection or the attention. Non-finite inputs give
+   * summaries stay bf16: the exact min / max of the dequantized keys in IEEE
+   * totalOrder (-0 below +0) rounded outward (min down, max up), so each
+   * still bounds every q.k of its page; an append merges its key rounded
+   * outward into the stored summary (the same result, rounding outward being
+   * monotone). spa_append_decode_attn appends inside the attention launch on
+   * fp8 pools as on bf16 ones; spa_append_select_pages runs the append as a
+   * launch of its own ahead of the selection. Non-finite inputs give
    * unspecified codes. */
   int32_t kv_format;
   float* k_scale;         /* SPA_KV_FP8: device fp32 [N][S][P], one scale per key row; else unused */

@@ -539,13 +539,6 @@ spa_status decode_attn(const spa_pool* pool, const spa_heads* heads, const spa_b
                   "holds %zu (use spa_sparse_decode_attn with a workspace)", need, ws_bytes);
   }
   if (!ws || ws_bytes < need) return fail(SPA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
-  if (k_new && pl.q8) {             // fp8 pools: the append as a launch of its own, first
-    const spa_status a = hip_status(spa::launch_append(pl, bt, static_cast<const uint16_t*>(k_new),
-                                                       static_cast<const uint16_t*>(v_new), &dyn, stream),
-                                    what);
-    if (a != SPA_OK) return a;
-    k_new = v_new = nullptr;
-  }
   float* part_o = static_cast<float*>(ws);
   float* part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + ml_off);
   return hip_status(spa::launch_attn(pl, bt, plan, G, static_cast<const uint16_t*>(q), sel_pages, sel_count,

@@ -379,6 +379,64 @@ __device__ __forceinline__ void token_partial(const PoolArgs& pl, const BatchArg
   }
 }
 
+// token_partial on fp8 pages, from the token's rows as the append quantizes
+// them (kc / vc: lane l holds the codes of channels 2l and 2l + 1; ks / vs the
+// row scales; the same codes the pool receives): the score over the key codes
+// times the key scale, the output the dequantized value row -- the arithmetic
+// the items apply to every stored token. Each lane fetches the codes of its
+// channels from the lanes that quantized them.
+__device__ __forceinline__ void token_partial_q8(const PoolArgs& pl, const BatchArgs& bt, int32_t b, int32_t h,
+                                                 int32_t G, int32_t item_stride, int32_t it, const uint16_t* q,
+                                                 uint32_t kc, float ks, uint32_t vc, float vs, float* part_o,
+                                                 float* part_ml, bool in_ring) {
+  const int lane = threadIdx.x & 63, g = lane & 15, quad = lane >> 4;
+  const int32_t L = clamp_len(bt, b, pl.P);
+  bool valid = L >= 1;
+  if (valid) {
+    const int32_t phys = in_ring ? ring_page(bt, bt.ring[b], L - 1, pl.P, pl.N)
+                                 : bt.pt[(int64_t)b * bt.max_pp + (L - 1) / pl.P];
+    valid = phys >= 0 && phys < pl.N;
+  }
+  const int64_t bh = (int64_t)b * pl.hkv + h;
+  const int32_t gq = g < G ? g : 0;
+  const uint4* q4 = reinterpret_cast<const uint4*>(q + (bh * G + gq) * kHeadDim + 32 * quad);
+  // q channels 32 quad + 8 i + j; their key codes sit in lane 16 quad + 4 i + j / 2
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 qw = q4[i];
+    bf16x8 qv;
+    __builtin_memcpy(&qv, &qw, 16);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t c2 = (uint32_t)__shfl((int)kc, 16 * quad + 4 * i + m, 64);
+      s = __builtin_fmaf((float)qv[2 * m], e4m3_value(c2 & 0xFFu), s);
+      s = __builtin_fmaf((float)qv[2 * m + 1], e4m3_value((c2 >> 8) & 0xFFu), s);
+    }
+  }
+  const float t = sum_over_rows(s) * ks * kScaleLog2;
+  // output channels 16 c + 4 quad + r; their value codes sit in lane 8 c + 2 quad + r / 2
+  f32x4 v[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const uint32_t c2 = (uint32_t)__shfl((int)vc, 8 * c + 2 * quad + m, 64);
+      v[c][2 * m] = e4m3_value(c2 & 0xFFu) * vs;
+      v[c][2 * m + 1] = e4m3_value((c2 >> 8) & 0xFFu) * vs;
+    }
+  if (g >= G) return;
+  const int64_t slot = (bh * item_stride + it) * G + g;
+  float* o = part_o + slot * kHeadDim + 4 * quad;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    *reinterpret_cast<f32x4*>(o + 16 * c) = valid ? v[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+  if (quad == 0) {
+    part_ml[slot * 2 + 0] = valid ? t : -INFINITY;
+    part_ml[slot * 2 + 1] = valid ? 1.f : 0.f;
+  }
+}
+
 // Which blocks an item covers. Blocks are numbered per head:
 //   streaming: the sink blocks, then the window blocks;
 //   dynamic:   block (i, s) = 16-token block s of the i-th selected page,
@@ -579,10 +637,21 @@ __global__ void __launch_bounds__(64) attn_kernel(PoolArgs pl, BatchArgs bt, Att
     const int32_t w = (int32_t)blockIdx.x - n_items_all;
     const int32_t ab = w / pl.hkv, ah = w - ab * pl.hkv;
     const int32_t n_it = mask.dynamic(ah) ? plan.items_dyn : plan.items_stream;
-    token_partial(pl, bt, ab, ah, G, plan.item_stride, n_it, q, reinterpret_cast<const uint16_t*>(k_new), v_new,
-                  part_o, part_ml, RING && !mask.dynamic(ah));
-    append_token(pl, bt, ab, ah, head_slot(pl, ah, mask.below(ah), mask.dynamic(ah)), k_new, v_new,
-                 mask.dynamic(ah), RING && !mask.dynamic(ah));
+    const int32_t hsl_a = head_slot(pl, ah, mask.below(ah), mask.dynamic(ah));
+    if constexpr (Q8) {                 // the rows quantized once, shared by the partial and the append
+      const int lane = threadIdx.x & 63;
+      const int64_t src = ((int64_t)ab * pl.hkv + ah) * (kHeadDim / 2);
+      const uint32_t kin = k_new[src + lane], vin = reinterpret_cast<const uint32_t*>(v_new)[src + lane];
+      float ks, vs;
+      const uint32_t kc = quantize_pair(kin, ks), vc = quantize_pair(vin, vs);
+      token_partial_q8(pl, bt, ab, ah, G, plan.item_stride, n_it, q, kc, ks, vc, vs, part_o, part_ml,
+                       RING && !mask.dynamic(ah));
+      store_token_q8(pl, bt, ab, hsl_a, kc, ks, vc, vs, mask.dynamic(ah), RING && !mask.dynamic(ah));
+    } else {
+      token_partial(pl, bt, ab, ah, G, plan.item_stride, n_it, q, reinterpret_cast<const uint16_t*>(k_new), v_new,
+                    part_o, part_ml, RING && !mask.dynamic(ah));
+      append_token(pl, bt, ab, ah, hsl_a, k_new, v_new, mask.dynamic(ah), RING && !mask.dynamic(ah));
+    }
     return;
   }
   const int32_t item = (int32_t)blockIdx.x;
@@ -781,9 +850,12 @@ hipError_t launch_attn_t(const PoolArgs& pool, const BatchArgs& batch, const Att
                      0, s, pool, batch, plan, G, q, sel_pages, sel_count, sel_len, sel_phys, part_o, part_ml,  \
                      reinterpret_cast<const uint32_t*>(k_new), v_new, n_append)
   const bool ring = batch.ring != nullptr;
-  if (pool.q8) {                  // fp8 pages: the append (if any) ran as a launch of its own
-    if (k_new) return hipErrorInvalidValue;
-    if (ring) SPA_ATTN_LAUNCH(false, true, true); else SPA_ATTN_LAUNCH(false, false, true);
+  if (pool.q8) {
+    if (k_new) {
+      if (ring) SPA_ATTN_LAUNCH(true, true, true); else SPA_ATTN_LAUNCH(true, false, true);
+    } else {
+      if (ring) SPA_ATTN_LAUNCH(false, true, true); else SPA_ATTN_LAUNCH(false, false, true);
+    }
   } else if (k_new) {
     if (ring) SPA_ATTN_LAUNCH(true, true); else SPA_ATTN_LAUNCH(true, false);
   } else {

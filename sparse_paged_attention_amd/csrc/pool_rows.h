@@ -116,17 +116,18 @@ __device__ __forceinline__ uint32_t quantize_pair(uint32_t w, float& scale) {
   return e4m3_code(x0 / scale) | (e4m3_code(x1 / scale) << 8);
 }
 
-// Running min / max, in position order, of the dequantized values of the
-// lane's two channels (codes in bits 0-7 / 8-15 of c2).
+// Running min / max in IEEE totalOrder (-0 below +0, the order of the bf16
+// summaries) of the dequantized values of the lane's two channels (codes in
+// bits 0-7 / 8-15 of c2).
 struct MinMax2 {
   double lo0 = INFINITY, hi0 = -INFINITY, lo1 = INFINITY, hi1 = -INFINITY;
+  __device__ __forceinline__ static void fold(double v, double& lo, double& hi) {
+    if (v < lo || (v == lo && __signbit(v))) lo = v;
+    if (v > hi || (v == hi && !__signbit(v))) hi = v;
+  }
   __device__ __forceinline__ void add(uint32_t c2, float scale) {
-    const double v0 = (double)e4m3_value(c2 & 0xFFu) * (double)scale;   // exact
-    const double v1 = (double)e4m3_value((c2 >> 8) & 0xFFu) * (double)scale;
-    if (v0 < lo0) lo0 = v0;
-    if (v0 > hi0) hi0 = v0;
-    if (v1 < lo1) lo1 = v1;
-    if (v1 > hi1) hi1 = v1;
+    fold((double)e4m3_value(c2 & 0xFFu) * (double)scale, lo0, hi0);     // products exact in fp64
+    fold((double)e4m3_value((c2 >> 8) & 0xFFu) * (double)scale, lo1, hi1);
   }
   // the summary rows of the page, rounded outward to bf16
   __device__ __forceinline__ void store(uint16_t* summ_page_base, int lane) const {
@@ -136,15 +137,45 @@ struct MinMax2 {
   }
 };
 
-// append_token for fp8 pages: the key and value rows are quantized (one scale
-// each), and the summary is rebuilt from the page's dequantized keys.
-__device__ __forceinline__ void append_token_q8(const PoolArgs& pl, const BatchArgs& bt, int32_t b, int32_t h,
-                                                int32_t hsl, const uint32_t* __restrict__ k_new,
-                                                const uint32_t* __restrict__ v_new, bool summary, bool in_ring) {
-  // the new rows do not depend on the length or the page: loaded with the length
+// The outward-rounded bf16 min / max words (channels 2 lane and 2 lane + 1)
+// of one quantized key row merged into a stored summary record: channel-wise
+// totalOrder min of the stored minimum and the new key rounded down, max of
+// the stored maximum and the new key rounded up; the new key alone when it
+// opens the page. Rounding outward is monotone, so this equals the rebuild
+// over all of the page's keys.
+__device__ __forceinline__ void merge_q8_summary(uint16_t* summ_rec, int lane, uint32_t c2, float scale,
+                                                 bool opens) {
+  uint32_t* sp = reinterpret_cast<uint32_t*>(summ_rec);
+  const double v0 = (double)e4m3_value(c2 & 0xFFu) * (double)scale;
+  const double v1 = (double)e4m3_value((c2 >> 8) & 0xFFu) * (double)scale;
+  const uint32_t dn0 = bf16_down(v0), dn1 = bf16_down(v1), up0 = bf16_up(v0), up1 = bf16_up(v1);
+  uint32_t lo = dn0 | (dn1 << 16), hi = up0 | (up1 << 16);
+  if (!opens) {
+    const uint32_t smin = sp[lane], smax = sp[kHeadDim / 2 + lane];
+    uint32_t l2 = 0, h2 = 0;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const uint32_t a = order_key((uint16_t)(smin >> (16 * half))), n = order_key((uint16_t)(lo >> (16 * half)));
+      const uint32_t c = order_key((uint16_t)(smax >> (16 * half))), m = order_key((uint16_t)(hi >> (16 * half)));
+      l2 |= (uint32_t)from_key(min(a, n)) << (16 * half);
+      h2 |= (uint32_t)from_key(max(c, m)) << (16 * half);
+    }
+    lo = l2;
+    hi = h2;
+  }
+  sp[lane] = lo;
+  sp[kHeadDim / 2 + lane] = hi;
+}
+
+// Writes token L-1 of sequence b, KV head h into an fp8 pool from its
+// quantized rows (lane l: the codes of channels 2l, 2l + 1 in bits 0-15 of kc
+// / vc; ks / vs the row scales); with `summary`, the new key is merged into
+// the stored summary of its logical page (merge_q8_summary), so the page's
+// earlier rows are not read again.
+__device__ __forceinline__ void store_token_q8(const PoolArgs& pl, const BatchArgs& bt, int32_t b, int32_t hsl,
+                                               uint32_t kc, float ks, uint32_t vc, float vs, bool summary,
+                                               bool in_ring) {
   const int lane = threadIdx.x & 63;
-  const int64_t src = ((int64_t)b * pl.hkv + h) * (kHeadDim / 2);
-  const uint32_t kin = k_new[src + lane], vin = v_new[src + lane];
   const int32_t L = clamp_len(bt, b, pl.P);
   if (L < 1) return;
   const int32_t t = L - 1;
@@ -153,28 +184,6 @@ __device__ __forceinline__ void append_token_q8(const PoolArgs& pl, const BatchA
   const int32_t slot = t % pl.P, lp = slot / pl.p, i = slot % pl.p;
   const int64_t row0 = k_row(pl, phys, hsl, lp * pl.p);               // the page's first token row
   uint8_t* krow0 = reinterpret_cast<uint8_t*>(pl.k) + row0 * kHeadDim;
-  // the page's earlier key rows (never the row written below), read before
-  // the quantization so that their loads go out with nothing ahead of them;
-  // added in position order, 16 rows a batch
-  MinMax2 mm;
-  if (summary) {
-    for (int32_t r0 = 0; r0 < i; r0 += 16) {
-      uint32_t w[16];
-      float sc[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {                // rows past i - 1 re-read row i - 1 and are not added
-        const int32_t r = min(r0 + u, i - 1);
-        w[u] = reinterpret_cast<const uint16_t*>(krow0 + (int64_t)r * kHeadDim)[lane];
-        sc[u] = pl.ks[row0 + r];
-      }
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        if (r0 + u < i) mm.add(w[u], sc[u]);
-    }
-  }
-  float ks, vs;
-  const uint32_t kc = quantize_pair(kin, ks);
-  const uint32_t vc = quantize_pair(vin, vs);
   reinterpret_cast<uint16_t*>(krow0 + (int64_t)i * kHeadDim)[lane] = (uint16_t)kc;
   uint8_t* vp = reinterpret_cast<uint8_t*>(pl.v) + v_page(pl, phys, hsl, lp);
   vp[(2 * lane) * pl.p + i] = (uint8_t)vc;
@@ -183,9 +192,22 @@ __device__ __forceinline__ void append_token_q8(const PoolArgs& pl, const BatchA
     pl.ks[row0 + i] = ks;
     pl.vs[row0 + i] = vs;
   }
-  if (!summary) return;
-  mm.add(kc, ks);
-  mm.store(pl.summ + summ_page(pl, phys, hsl, lp), lane);
+  if (summary) merge_q8_summary(pl.summ + summ_page(pl, phys, hsl, lp), lane, kc, ks, i == 0);
+}
+
+// append_token for fp8 pages: the key and value rows are quantized (one scale
+// each) and stored (store_token_q8). k_new / v_new: bf16 [B][H_kv][D] as
+// 32-bit pairs.
+__device__ __forceinline__ void append_token_q8(const PoolArgs& pl, const BatchArgs& bt, int32_t b, int32_t h,
+                                                int32_t hsl, const uint32_t* __restrict__ k_new,
+                                                const uint32_t* __restrict__ v_new, bool summary, bool in_ring) {
+  const int lane = threadIdx.x & 63;
+  const int64_t src = ((int64_t)b * pl.hkv + h) * (kHeadDim / 2);
+  const uint32_t kin = k_new[src + lane], vin = v_new[src + lane];
+  float ks, vs;
+  const uint32_t kc = quantize_pair(kin, ks);     // every lane takes part (cross-lane max)
+  const uint32_t vc = quantize_pair(vin, vs);
+  store_token_q8(pl, bt, b, hsl, kc, ks, vc, vs, summary, in_ring);
 }
 
 // One wave writes token L-1 of sequence b, KV head h into its pool slot; lane

@@ -71,7 +71,10 @@ __device__ __forceinline__ float xchg(float x) {
 template <int G_>
 struct ScoreShape {
   static constexpr int G = G_;
-  static constexpr int LPP = G <= 4 ? 16 : 4 * G;   // lanes per page
+  // lanes per page: 32 for G <= 4 (4 channels per lane: the lane's q+ / q-
+  // in fp64 take 64 registers, and the kernel fits three waves per SIMD; with
+  // 16 lanes per page it needed 282 registers and ran one wave per SIMD)
+  static constexpr int LPP = G <= 4 ? 32 : 4 * G;
   static constexpr int CPL = kHeadDim / LPP;        // channels per lane
   static constexpr int NP = 4;                      // pages per group per pass
   static constexpr int V = NP * G;                  // partial sums per lane

@@ -104,9 +104,8 @@ typedef struct spa_pool {
    * totalOrder (-0 below +0) rounded outward (min down, max up), so each
    * still bounds every q.k of its page; an append merges its key rounded
    * outward into the stored summary (the same result, rounding outward being
-   * monotone). spa_append_decode_attn appends inside the attention launch on
-   * fp8 pools as on bf16 ones; spa_append_select_pages runs the append as a
-   * launch of its own ahead of the selection. Non-finite inputs give
+   * monotone). The append entry points append inside the attention and
+   * scoring launches on fp8 pools as on bf16 ones. Non-finite inputs give
    * unspecified codes. */
   int32_t kv_format;
   float* k_scale;         /* SPA_KV_FP8: device fp32 [N][S][P], one scale per key row; else unused */

@@ -438,9 +438,8 @@ spa_status select_pages(const spa_pool* pool, const spa_heads* heads, const spa_
                 (long long)kMaxScoredPages);
   if ((int64_t)bt.B * dyn.n > 2147483647LL / 1) return fail(SPA_ERR_INVALID, "too many heads");
   if (bt.B == 0) return ok();
-  bool fresh = k_new != nullptr || v_new != nullptr;
+  const bool fresh = k_new != nullptr || v_new != nullptr;
   if (fresh && (!k_new || !v_new)) return fail(SPA_ERR_INVALID, "k_new / v_new is NULL");
-  // every check before anything is enqueued (the fp8 append below launches)
   float* sc = scores;
   if (dyn.n > 0) {
     if (!q || !budget_tokens || !sel_pages || !sel_count || !sel_len)
@@ -451,14 +450,6 @@ spa_status select_pages(const spa_pool* pool, const spa_heads* heads, const spa_
         return fail(SPA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
       sc = static_cast<float*>(ws);
     }
-  }
-  if (fresh && pl.q8) {             // fp8 pools: the append as a launch of its own, first
-    const spa_status a = hip_status(spa::launch_append(pl, bt, static_cast<const uint16_t*>(k_new),
-                                                       static_cast<const uint16_t*>(v_new), &dyn, stream),
-                                    what);
-    if (a != SPA_OK) return a;
-    k_new = v_new = nullptr;
-    fresh = false;
   }
   if (dyn.n == 0)                   // nothing to select: the append alone
     return fresh ? hip_status(spa::launch_select(pl, bt, dyn, G, nullptr, nullptr, k_max, nullptr, nullptr,

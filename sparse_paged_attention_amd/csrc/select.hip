@@ -122,21 +122,23 @@ __device__ __forceinline__ void widen(const Raw<CPL>& r, double (&out)[CPL]) {
 
 // The summary of the page receiving a token appended in the same launch, as
 // the append leaves it: the channel-wise min / max of the stored summary and
-// the new key, or the new key alone when it opens the page. Taking min / max
-// with the new key again changes nothing, so the stored record may be read
-// before or after the append wave rewrites it.
+// the new key (on fp8 pages the key as quantized, rounded outward: kn_lo down,
+// kn_hi up; on bf16 pages both are the key), or the new key alone when it
+// opens the page. Taking min / max with the new key again changes nothing, so
+// the stored record may be read before or after the append wave rewrites it.
 template <int CPL>
-__device__ __forceinline__ void merge_new_key(Raw<CPL>& mn, Raw<CPL>& mx, const Raw<CPL>& kn, bool opens) {
+__device__ __forceinline__ void merge_new_key(Raw<CPL>& mn, Raw<CPL>& mx, const Raw<CPL>& kn_lo,
+                                              const Raw<CPL>& kn_hi, bool opens) {
 #pragma unroll
   for (int w = 0; w < CPL / 2; ++w) {
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const uint16_t a = (uint16_t)(mn.w[w] >> (16 * half)), c = (uint16_t)(mx.w[w] >> (16 * half));
-      const uint16_t k = (uint16_t)(kn.w[w] >> (16 * half));
-      const uint32_t ka = order_key(a), kc = order_key(c), kk = order_key(k);
-      const uint16_t l = opens ? k : from_key(min(ka, kk));
-      const uint16_t u = opens ? k : from_key(max(kc, kk));
+      const uint16_t kl = (uint16_t)(kn_lo.w[w] >> (16 * half)), kh = (uint16_t)(kn_hi.w[w] >> (16 * half));
+      const uint32_t ka = order_key(a), kc = order_key(c);
+      const uint16_t l = opens ? kl : from_key(min(ka, order_key(kl)));
+      const uint16_t u = opens ? kh : from_key(max(kc, order_key(kh)));
       lo |= (uint32_t)l << (16 * half);
       hi |= (uint32_t)u << (16 * half);
     }
@@ -201,8 +203,12 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
     const int32_t ab = w / pl.hkv, ah = w - ab * pl.hkv;
     bool is_dyn = false;
     for (int32_t d = 0; d < dyn.n; ++d) is_dyn |= dyn.id[d] == ah;
-    append_token(pl, bt, ab, ah, head_slot(pl, ah, dyn_rank(dyn, ah), is_dyn), k_new, v_new, is_dyn,
-                 bt.ring != nullptr && !is_dyn);
+    const int32_t hsl_a = head_slot(pl, ah, dyn_rank(dyn, ah), is_dyn);
+    if (pl.q8)
+      append_token_q8(pl, bt, ab, ah, hsl_a, k_new, reinterpret_cast<const uint32_t*>(v_new), is_dyn,
+                      bt.ring != nullptr && !is_dyn);
+    else
+      append_token(pl, bt, ab, ah, hsl_a, k_new, v_new, is_dyn, bt.ring != nullptr && !is_dyn);
     return;
   }
   static_assert(S::OFFS <= 192, "three page offsets per lane");
@@ -248,10 +254,39 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
     }
   }
   // the new key's channels of this lane, and where the token lands
-  Raw<S::CPL> kn;
+  Raw<S::CPL> kn, kn_hi;
   const int32_t j_new = FRESH && L >= 1 ? (L - 1) / pl.p : -1;
   const bool opens = FRESH && L >= 1 && (L - 1) % pl.p == 0;
-  if (FRESH) load_raw<S::CPL>(reinterpret_cast<const uint16_t*>(k_new) + ((int64_t)b * pl.hkv + h) * kHeadDim + c0, kn);
+  if (FRESH) {
+    load_raw<S::CPL>(reinterpret_cast<const uint16_t*>(k_new) + ((int64_t)b * pl.hkv + h) * kHeadDim + c0, kn);
+    kn_hi = kn;
+    if (pl.q8) {          // the key as the append quantizes it (the group's lanes hold the whole row), rounded outward
+      float x[S::CPL];
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < S::CPL / 2; ++i) {
+        x[2 * i] = bf16_lo(kn.w[i]);
+        x[2 * i + 1] = bf16_hi(kn.w[i]);
+        amax = fmaxf(amax, fmaxf(fabsf(x[2 * i]), fabsf(x[2 * i + 1])));
+      }
+#pragma unroll
+      for (int o = 1; o < S::LPP; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+      const float scale = amax / 448.f;
+#pragma unroll
+      for (int i = 0; i < S::CPL / 2; ++i) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint32_t code = scale == 0.f ? 0u : e4m3_code(x[2 * i + e] / scale);
+          const double v = (double)e4m3_value(code) * (double)scale;
+          lo |= bf16_down(v) << (16 * e);
+          hi |= bf16_up(v) << (16 * e);
+        }
+        kn.w[i] = lo;
+        kn_hi.w[i] = hi;
+      }
+    }
+  }
   __syncthreads();
 
   // summary location of page slot pp of pass it (page 0 of the pool if invalid)
@@ -279,7 +314,8 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
     if (FRESH && j_new >= base + it * S::PASS && j_new < base + (it + 1) * S::PASS) {
 #pragma unroll
       for (int pp = 0; pp < S::NP; ++pp)
-        if (base + it * S::PASS + pp * S::GPW + group == j_new) merge_new_key<S::CPL>(ps.mn[pp], ps.mx[pp], kn, opens);
+        if (base + it * S::PASS + pp * S::GPW + group == j_new)
+          merge_new_key<S::CPL>(ps.mn[pp], ps.mx[pp], kn, kn_hi, opens);
     }
     double v[S::V];                                       // [page slot][query]
 #pragma unroll

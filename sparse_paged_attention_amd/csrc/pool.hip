@@ -129,10 +129,11 @@ __global__ void __launch_bounds__(64) write_kernel(PoolArgs pl, const int32_t* _
 }
 
 // write_kernel for fp8 pages: each token's key and value rows are quantized
-// (one wave reduction for the row's scale), codes and scales are written, and
-// the summary of a dynamic head's page is the min / max of the dequantized
-// keys in position order (tokens before `start` read back from the pool),
-// rounded outward to bf16.
+// (the row maxima of 16 rows at a time reduced across the wave two rows per
+// word; each code from a reciprocal bracket of the quotient, codes_in_row),
+// codes and scales are written, and the summary of a dynamic head's page is
+// the min / max of the dequantized keys (tokens before `start` read back
+// from the pool), rounded outward to bf16.
 template <int PG>
 __global__ void __launch_bounds__(64) write_kernel_q8(PoolArgs pl, const int32_t* __restrict__ pt, int64_t start,
                                                       int64_t count, const uint32_t* __restrict__ k,
@@ -162,14 +163,6 @@ __global__ void __launch_bounds__(64) write_kernel_q8(PoolArgs pl, const int32_t
   const int64_t row0 = k_row(pl, phys, hsl, lp * PG);
   uint8_t* kd = reinterpret_cast<uint8_t*>(pl.k) + row0 * kHeadDim;                 // [PG][D] codes
   uint8_t* vd = reinterpret_cast<uint8_t*>(pl.v) + v_page(pl, phys, hsl, lp);        // [D][PG] codes
-  uint32_t kw[PG], vw[PG];                          // all of the page's rows in flight at once
-#pragma unroll
-  for (int u = 0; u < PG; ++u) {                    // rows outside the range re-read row lo
-    const int64_t t = t0 + u;
-    const int64_t row = (int64_t)h * count + ((t >= lo && t < hi) ? t : lo) - start;
-    kw[u] = k[row * 64 + lane];
-    vw[u] = v[row * 64 + lane];
-  }
   MinMax2 mm;
   if (dynamic)
     for (int64_t t = t0; t < lo; ++t)               // the page's tokens before `start`, from the pool
@@ -178,26 +171,50 @@ __global__ void __launch_bounds__(64) write_kernel_q8(PoolArgs pl, const int32_t
   uint32_t a[PG / 4], c[PG / 4];                    // value codes of channels 2l / 2l + 1, 4 tokens a word
 #pragma unroll
   for (int i = 0; i < PG / 4; ++i) { a[i] = 0; c[i] = 0; }
+  // chunks of 16 rows: all of a chunk's rows in flight at once
+  constexpr int CH = PG < 16 ? PG : 16;
 #pragma unroll
-  for (int u = 0; u < PG; ++u) {
-    const int64_t t = t0 + u;
-    if (t < lo || t >= hi) continue;                // wave-uniform
-    float ks, vs;
-    const uint32_t kc = quantize_pair(kw[u], ks);
-    const uint32_t vc = quantize_pair(vw[u], vs);
-    reinterpret_cast<uint16_t*>(kd + u * kHeadDim)[lane] = (uint16_t)kc;
-    if (lane == 0) {
-      pl.ks[row0 + u] = ks;
-      pl.vs[row0 + u] = vs;
+  for (int c0 = 0; c0 < PG; c0 += CH) {
+    if (t0 + c0 >= hi || t0 + c0 + CH <= lo) continue;     // wave-uniform
+    uint32_t kw[CH], vw[CH];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {                  // rows outside the range re-read row lo
+      const int64_t t = t0 + c0 + u;
+      const int64_t row = (int64_t)h * count + ((t >= lo && t < hi) ? t : lo) - start;
+      kw[u] = k[row * 64 + lane];
+      vw[u] = v[row * 64 + lane];
     }
-    if (full) {
-      a[u / 4] |= (vc & 0xFFu) << (8 * (u % 4));
-      c[u / 4] |= ((vc >> 8) & 0xFFu) << (8 * (u % 4));
-    } else {
-      vd[(2 * lane) * PG + u] = (uint8_t)vc;
-      vd[(2 * lane + 1) * PG + u] = (uint8_t)(vc >> 8);
+    // every row's maximum magnitude, two rows per word (16-bit halves), the
+    // reductions of the chunk's rows in flight together
+    uint32_t km[CH / 2], vm[CH / 2];
+#pragma unroll
+    for (int i = 0; i < CH / 2; ++i) {
+      km[i] = wave_max_u16x2(pair_max_u16(kw[2 * i], kw[2 * i + 1]));
+      vm[i] = wave_max_u16x2(pair_max_u16(vw[2 * i], vw[2 * i + 1]));
     }
-    if (dynamic) mm.add(kc, ks);
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int64_t t = t0 + c0 + u;
+      if (t < lo || t >= hi) continue;              // wave-uniform
+      const RowScale rk = row_scale_of((km[u / 2] >> (16 * (u & 1))) & 0xFFFFu);
+      const RowScale rv = row_scale_of((vm[u / 2] >> (16 * (u & 1))) & 0xFFFFu);
+      const uint32_t kc = codes_in_row(kw[u], rk);
+      const uint32_t vc = codes_in_row(vw[u], rv);
+      const int r = c0 + u;                         // row in the page
+      reinterpret_cast<uint16_t*>(kd + r * kHeadDim)[lane] = (uint16_t)kc;
+      if (lane == 0) {
+        pl.ks[row0 + r] = rk.s;
+        pl.vs[row0 + r] = rv.s;
+      }
+      if (full) {
+        a[r / 4] |= (vc & 0xFFu) << (8 * (r % 4));
+        c[r / 4] |= ((vc >> 8) & 0xFFu) << (8 * (r % 4));
+      } else {
+        vd[(2 * lane) * PG + r] = (uint8_t)vc;
+        vd[(2 * lane + 1) * PG + r] = (uint8_t)(vc >> 8);
+      }
+      if (dynamic) mm.add(kc, rk.s);
+    }
   }
   if (full) {
     uint4* d0 = reinterpret_cast<uint4*>(vd + (2 * lane) * PG);

@@ -87,6 +87,14 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
   return sign | c;
 }
 
+// Codes of two fp32 values with |y| <= 464 (bits 0-7: y0, bits 8-15: y1) by
+// the hardware conversion, which on this GPU writes OCP E4M3 rounded to
+// nearest, ties to even: for every such fp32 value its code equals
+// e4m3_code's (checked over all of them, both signs).
+__device__ __forceinline__ uint32_t e4m3_code2(float y0, float y1) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false) & 0xFFFFu;
+}
+
 // Value of a code (never one of the NaN codes), exact in fp32.
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
   const uint32_t e = (c >> 3) & 15u, m = c & 7u;
@@ -94,46 +102,194 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
   return (c & 0x80u) ? -v : v;
 }
 
+// fp32 bit pattern -> largest bf16 <= it (bit pattern): truncation, one step
+// further down for a negative value with bits cut off.
+__device__ __forceinline__ uint32_t bf16_down_bits(uint32_t u) {
+  return (u >> 16) + (((u & 0xFFFFu) != 0u) & (u >> 31));
+}
 // Largest bf16 <= x and smallest bf16 >= x, as bit patterns.
 __device__ __forceinline__ uint32_t bf16_down(double x) {
-  const uint32_t u = __float_as_uint(__double2float_rd(x));   // largest fp32 <= x
-  uint32_t b = u >> 16;                                         // toward zero
-  if ((u & 0xFFFFu) && (u >> 31)) b += 1;                       // negative: one step further down
-  return b;
+  return bf16_down_bits(__float_as_uint(__double2float_rd(x)));   // largest fp32 <= x first
 }
 __device__ __forceinline__ uint32_t bf16_up(double x) { return bf16_down(-x) ^ 0x8000u; }
+
+// Values of the two codes in bits 0-7 / 8-15 of c2 by the hardware
+// conversion (exact: every E4M3 value is an fp32 value; equal to e4m3_value
+// for every code but the NaN ones, checked over all of them).
+typedef float e4m3_pair_values __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ e4m3_pair_values e4m3_value2(uint32_t c2) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)c2, false);
+}
+
+// Key of an fp32 bit pattern that orders like IEEE totalOrder, with
+// consecutive fp32 values on consecutive keys (-0 just below +0), and back.
+__device__ __forceinline__ uint32_t f32_key(uint32_t u) { return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u); }
+__device__ __forceinline__ uint32_t f32_unkey(uint32_t k) { return k ^ ((k >> 31) ? 0x80000000u : 0xFFFFFFFFu); }
+
+// Keys of the largest fp32 <= v * scale (kd) and the smallest fp32 >= it (ku),
+// v the value of a code. The product has at most 4 + 24 significant bits:
+// p = RN(v s) and its residual e = fma(v, s, -p), exact while p is a normal
+// number (scales from 2^-100 up: |v| >= 2^-9 unless v = 0), put the product
+// one key below p when e < 0 and one above when e > 0. Smaller scales take
+// the fp64 product, which is exact, rounded each way.
+__device__ __forceinline__ void product_keys(float v, float scale, uint32_t& kd, uint32_t& ku) {
+  if (!(scale >= 0x1p-100f)) {
+    const double x = (double)v * (double)scale;
+    kd = f32_key(__float_as_uint(__double2float_rd(x)));
+    ku = f32_key(__float_as_uint(__double2float_ru(x)));
+    return;
+  }
+  const float p = v * scale;
+  const float e = __builtin_fmaf(v, scale, -p);
+  const uint32_t k = f32_key(__float_as_uint(p));
+  kd = k - (e < 0.f ? 1u : 0u);
+  ku = k + (e > 0.f ? 1u : 0u);
+}
+
+// bf16 bit patterns from such keys: the largest bf16 <= the fp32 of kd, the
+// smallest bf16 >= the fp32 of ku (up(x) = -down(-x)). For the product of a
+// code's value and a scale these equal bf16_down / bf16_up of the exact fp64
+// product, for every code and every scale a bf16 row can have (checked).
+__device__ __forceinline__ uint32_t bf16_below_key(uint32_t kd) { return bf16_down_bits(f32_unkey(kd)); }
+__device__ __forceinline__ uint32_t bf16_above_key(uint32_t ku) {
+  return bf16_down_bits(f32_unkey(ku) ^ 0x80000000u) ^ 0x8000u;
+}
+
+// Wave-wide maximum of unsigned values (every lane of the wave active): DPP
+// within each 16-lane row (neighbours, pairs, mirrored halves, mirrored rows),
+// then the cross-row lane swaps; every lane ends with the result.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));   // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max(b[0], b[1]);
+}
+
+// Whether the fp32 value q lies within 4 ulp of a rounding boundary of E4M3
+// (a midpoint between two codes): there a quotient rounded another way
+// could take the other code. (Both ranges tested, then one picked: no
+// branch.)
+__device__ __forceinline__ bool near_e4m3_boundary(float q) {
+  const uint32_t a = __float_as_uint(q) & 0x7FFFFFFFu;
+  const bool normal = ((a & 0xFFFFFu) - 0x7FFFCu) <= 8u;          // the 20 bits below the 3 kept
+  const float y = __uint_as_float(a) * 512.f;                     // below 2^-6: multiples of 2^-9
+  const bool sub = fabsf((y - truncf(y)) - 0.5f) <= 0x1p-19f;
+  return a >= 0x3C800000u ? normal : sub;
+}
+
+// The row scale RN(amax / 448) of a bf16 row maximum: amax times the fp32
+// nearest 1/448, corrected once by the exact residual (an FMA); equal to the
+// IEEE division for every bf16 value (checked over all of them).
+__device__ __forceinline__ float row_scale(float amax) {
+  constexpr float kInv448 = 1.f / 448.f;
+  const float q = amax * kInv448;
+  return __builtin_fmaf(__builtin_fmaf(-q, 448.f, amax), kInv448, q);
+}
 
 // Quantizes one D = 128 row held by a wave as bf16 pairs (lane l: channels 2l
 // and 2l + 1, in w). Returns the lane's two codes (bits 0-7 and 8-15) and sets
 // the row's scale. Every lane of the wave must take part (cross-lane max).
+// Each code is that of the correctly rounded quotient x / scale: x times the
+// reciprocal of the scale is within 3 ulp of it, and within 4 ulp of a
+// rounding boundary the division decides; for every bf16 row maximum and
+// every bf16 x up to it this gives the division's code (checked over all
+// pairs). Scales below 2^-100 divide; a row of zeros has scale 0 and codes 0.
 __device__ __forceinline__ uint32_t quantize_pair(uint32_t w, float& scale) {
   const float x0 = __uint_as_float(w << 16), x1 = __uint_as_float(w & 0xFFFF0000u);
-  float a = fmaxf(fabsf(x0), fabsf(x1));
-#pragma unroll
-  for (int o = 32; o; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
-  scale = a / 448.f;
-  if (scale == 0.f) return 0;
-  return e4m3_code(x0 / scale) | (e4m3_code(x1 / scale) << 8);
+  const uint32_t amax = wave_max_u32(max(__float_as_uint(x0) & 0x7FFFFFFFu, __float_as_uint(x1) & 0x7FFFFFFFu));
+  scale = row_scale(__uint_as_float(amax));
+  const bool tiny = !(scale >= 0x1p-100f);
+  const float r = __builtin_amdgcn_rcpf(scale);
+  float q0 = x0 * r, q1 = x1 * r;
+  const bool n0 = tiny | near_e4m3_boundary(q0), n1 = tiny | near_e4m3_boundary(q1);
+  if (n0 | n1) {                                   // rare (and rows of zeros: 0 / 0, masked below)
+    if (n0) q0 = x0 / scale;
+    if (n1) q1 = x1 / scale;
+  }
+  const uint32_t c = e4m3_code2(q0, q1);
+  return scale == 0.f ? 0u : c;
 }
 
-// Running min / max in IEEE totalOrder (-0 below +0, the order of the bf16
-// summaries) of the dequantized values of the lane's two channels (codes in
-// bits 0-7 / 8-15 of c2).
+// Unsigned 16-bit maximum of the two halves of two words (one packed
+// instruction).
+typedef unsigned short u16_pair __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16_pair, a),
+                                                                __builtin_bit_cast(u16_pair, b)));
+}
+// Wave-wide maximum of each 16-bit half (every lane of the wave active), by
+// the steps of wave_max_u32.
+__device__ __forceinline__ uint32_t wave_max_u16x2(uint32_t v) {
+  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
+  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
+  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));
+  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = pk_max_u16(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return pk_max_u16(b[0], b[1]);
+}
+// The magnitudes (bf16 bits less the sign) of two rows' bf16 pairs w0, w1
+// folded into one word: low half the larger of w0's two, high half w1's.
+__device__ __forceinline__ uint32_t pair_max_u16(uint32_t w0, uint32_t w1) {
+  const uint32_t a = w0 & 0x7FFF7FFFu, b = w1 & 0x7FFF7FFFu;
+  return pk_max_u16(__builtin_amdgcn_perm(b, a, 0x05040100u), __builtin_amdgcn_perm(b, a, 0x07060302u));
+}
+
+// A row's scale RN(amax / 448) with the reciprocal bracket used to code its
+// elements: x lo and x hi lie below and above the correctly rounded quotient
+// x / s (the reciprocal is within 1 ulp; the bracket is 2^-20 either side of
+// it, the products' rounding adds 2^-24 each), scales from 2^-100 up.
+struct RowScale {
+  float s, lo, hi;
+  bool divide;                      // scales below 2^-100 (and 0): the division codes every element
+};
+__device__ __forceinline__ RowScale row_scale_of(uint32_t amax_bf16) {
+  const float s = row_scale(__uint_as_float(amax_bf16 << 16));
+  const float r = __builtin_amdgcn_rcpf(s);
+  return RowScale{s, r * (1.f - 0x1p-20f), r * (1.f + 0x1p-20f), !(s >= 0x1p-100f)};
+}
+// Codes of the bf16 pair w (bits 0-7: the low channel) in a row of scale rs:
+// rounding to E4M3 is monotone, so when x lo and x hi take the same code the
+// correctly rounded quotient between them takes it too; otherwise (within
+// 2^-20 of a rounding boundary: rare) the division decides. A row of zeros
+// codes to 0. Equal to e4m3_code(x / s) for every bf16 row maximum and every
+// bf16 x up to it (checked over all pairs).
+__device__ __forceinline__ uint32_t codes_in_row(uint32_t w, const RowScale& rs) {
+  const float x0 = __uint_as_float(w << 16), x1 = __uint_as_float(w & 0xFFFF0000u);
+  const uint32_t a = e4m3_code2(x0 * rs.lo, x1 * rs.lo), b = e4m3_code2(x0 * rs.hi, x1 * rs.hi);
+  uint32_t c = a;
+  if ((a != b) | rs.divide) c = e4m3_code2(x0 / rs.s, x1 / rs.s);
+  return rs.s == 0.f ? 0u : c;
+}
+
+// Running channel-wise min / max of the dequantized keys of the lane's two
+// channels (codes in bits 0-7 / 8-15 of c2), in IEEE totalOrder (-0 below
+// +0, the order of the bf16 summaries): the fp32 neighbours of each exact
+// product as keys (product_keys), rounded outward to bf16 once, when stored.
+// Both roundings are monotone in that order, so this is the exact min / max
+// rounded outward.
 struct MinMax2 {
-  double lo0 = INFINITY, hi0 = -INFINITY, lo1 = INFINITY, hi1 = -INFINITY;
-  __device__ __forceinline__ static void fold(double v, double& lo, double& hi) {
-    if (v < lo || (v == lo && __signbit(v))) lo = v;
-    if (v > hi || (v == hi && !__signbit(v))) hi = v;
-  }
+  uint32_t lo0 = 0xFFFFFFFFu, hi0 = 0u, lo1 = 0xFFFFFFFFu, hi1 = 0u;
   __device__ __forceinline__ void add(uint32_t c2, float scale) {
-    fold((double)e4m3_value(c2 & 0xFFu) * (double)scale, lo0, hi0);     // products exact in fp64
-    fold((double)e4m3_value((c2 >> 8) & 0xFFu) * (double)scale, lo1, hi1);
+    const e4m3_pair_values v = e4m3_value2(c2);
+    uint32_t kd, ku;
+    product_keys(v[0], scale, kd, ku);
+    lo0 = min(lo0, kd);
+    hi0 = max(hi0, ku);
+    product_keys(v[1], scale, kd, ku);
+    lo1 = min(lo1, kd);
+    hi1 = max(hi1, ku);
   }
-  // the summary rows of the page, rounded outward to bf16
+  // the summary rows of the page
   __device__ __forceinline__ void store(uint16_t* summ_page_base, int lane) const {
     uint32_t* sp = reinterpret_cast<uint32_t*>(summ_page_base);
-    sp[lane] = bf16_down(lo0) | (bf16_down(lo1) << 16);
-    sp[kHeadDim / 2 + lane] = bf16_up(hi0) | (bf16_up(hi1) << 16);
+    sp[lane] = bf16_below_key(lo0) | (bf16_below_key(lo1) << 16);
+    sp[kHeadDim / 2 + lane] = bf16_above_key(hi0) | (bf16_above_key(hi1) << 16);
   }
 };
 
@@ -146,9 +302,12 @@ struct MinMax2 {
 __device__ __forceinline__ void merge_q8_summary(uint16_t* summ_rec, int lane, uint32_t c2, float scale,
                                                  bool opens) {
   uint32_t* sp = reinterpret_cast<uint32_t*>(summ_rec);
-  const double v0 = (double)e4m3_value(c2 & 0xFFu) * (double)scale;
-  const double v1 = (double)e4m3_value((c2 >> 8) & 0xFFu) * (double)scale;
-  const uint32_t dn0 = bf16_down(v0), dn1 = bf16_down(v1), up0 = bf16_up(v0), up1 = bf16_up(v1);
+  const e4m3_pair_values v = e4m3_value2(c2);
+  uint32_t kd0, ku0, kd1, ku1;
+  product_keys(v[0], scale, kd0, ku0);
+  product_keys(v[1], scale, kd1, ku1);
+  const uint32_t dn0 = bf16_below_key(kd0), up0 = bf16_above_key(ku0);
+  const uint32_t dn1 = bf16_below_key(kd1), up1 = bf16_above_key(ku1);
   uint32_t lo = dn0 | (dn1 << 16), hi = up0 | (up1 << 16);
   if (!opens) {
     const uint32_t smin = sp[lane], smax = sp[kHeadDim / 2 + lane];

@@ -1,0 +1,143 @@
+// Exhaustive check of the fp8 quantizer's fast steps in
+// sparse_paged_attention_amd/csrc/pool_rows.h against their plain forms, on the
+// GPU they run on (test program; the product library does not contain it):
+//   1. e4m3_code2 (the hardware conversion) vs e4m3_code (from the fp32 bit
+//      pattern), every fp32 value of magnitude <= 464, both signs, both bytes;
+//   2. for every bf16 row maximum a and every bf16 x with |x| <= a, both signs:
+//      row_scale_of(a) vs the IEEE division a / 448, codes_in_row (reciprocal
+//      bracket) and quantize_pair (whole-wave row) vs e4m3_code(x / s);
+//   3. product_keys + bf16_below_key / bf16_above_key vs bf16_down / bf16_up of
+//      the fp64 product, every code and every such scale; e4m3_value2 vs
+//      e4m3_value, every code;
+//   4. wave_max_u32, pair_max_u16 + wave_max_u16x2 vs serial maxima on seeded rows.
+// Prints one line per check with its mismatch count; exit status 0 when all are 0.
+#include <hip/hip_runtime.h>
+#include <cstdio>
+#include <cstdint>
+#include "pool_rows.h"
+using namespace spa;
+
+constexpr int kChecks = 9;
+
+__device__ void report(unsigned long long* cnt, uint32_t* first, int which, uint32_t a, uint32_t b, uint32_t c) {
+  const unsigned long long k = atomicAdd(&cnt[which], 1ull);
+  if (k < 4) {
+    uint32_t* f = first + (which * 4 + k) * 3;
+    f[0] = a; f[1] = b; f[2] = c;
+  }
+}
+
+__global__ void check_conversion(uint32_t n, unsigned long long* cnt, uint32_t* first) {
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const float y = __uint_as_float(i), z = -y;
+    const uint32_t hw = e4m3_code2(y, z), sw = e4m3_code(y) | (e4m3_code(z) << 8);
+    if (hw != sw) report(cnt, first, 0, i, hw, sw);
+  }
+}
+
+// one block per row maximum a (bf16 bits 0 .. 0x7F7F; 0: a row of zeros)
+__global__ void __launch_bounds__(256) check_rows(unsigned long long* cnt, uint32_t* first) {
+  const uint32_t abits = blockIdx.x;
+  const float a = __uint_as_float(abits << 16);
+  const float s = a / 448.f;
+  const RowScale rs = row_scale_of(abits);
+  if (threadIdx.x == 0 && __float_as_uint(rs.s) != __float_as_uint(s)) report(cnt, first, 1, abits, __float_as_uint(rs.s), __float_as_uint(s));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t n = abits + 1;                     // x patterns 0 .. abits
+  // codes_in_row: any thread, any x
+  for (uint32_t xb = threadIdx.x; xb < n; xb += blockDim.x) {
+    const uint32_t w = (xb << 16) | (xb | 0x8000u);  // channel 0: -x, channel 1: +x
+    const float x = __uint_as_float(xb << 16);
+    const uint32_t want = s == 0.f ? 0u : (e4m3_code(-x / s) | (e4m3_code(x / s) << 8));
+    const uint32_t got = codes_in_row(w, rs);
+    if (got != want) report(cnt, first, 2, abits, xb, got);
+  }
+  // quantize_pair: whole waves; lane 0 carries the maximum, lanes 1-63 the x values
+  for (uint32_t base = wave * 63; base < n; base += 4 * 63) {
+    const uint32_t xb = lane == 0 ? abits : min(base + (uint32_t)lane - 1u, abits);
+    const uint32_t w = (xb << 16) | (xb | 0x8000u);
+    float sq;
+    const uint32_t got = quantize_pair(w, sq);
+    const float x = __uint_as_float(xb << 16);
+    const uint32_t want = s == 0.f ? 0u : (e4m3_code(-x / s) | (e4m3_code(x / s) << 8));
+    if (got != want || __float_as_uint(sq) != __float_as_uint(s)) report(cnt, first, 3, abits, xb, got);
+  }
+}
+
+__global__ void check_products(unsigned long long* cnt, uint32_t* first) {
+  const uint32_t abits = blockIdx.x;
+  const float s = __uint_as_float(abits << 16) / 448.f;
+  for (uint32_t c = threadIdx.x; c < 256; c += blockDim.x) {
+    if ((c & 0x7Fu) == 0x7Fu) continue;             // the NaN codes
+    const float v = e4m3_value(c);
+    const float v2 = e4m3_value2(c | (c << 8))[1];
+    if (__float_as_uint(v2) != __float_as_uint(v)) report(cnt, first, 4, abits, c, __float_as_uint(v2));
+    const double x = (double)v * (double)s;
+    uint32_t kd, ku;
+    product_keys(v, s, kd, ku);
+    if (bf16_below_key(kd) != bf16_down(x)) report(cnt, first, 5, abits, c, bf16_below_key(kd));
+    if (bf16_above_key(ku) != bf16_up(x)) report(cnt, first, 6, abits, c, bf16_above_key(ku));
+  }
+}
+
+__global__ void __launch_bounds__(64) check_maxima(unsigned long long* cnt, uint32_t* first) {
+  uint32_t st = blockIdx.x * 2654435761u + threadIdx.x * 40503u + 12345u;
+  st ^= st << 13; st ^= st >> 17; st ^= st << 5;
+  const uint32_t w0 = st >> (blockIdx.x & 7);
+  st ^= st << 13; st ^= st >> 17; st ^= st << 5;
+  const uint32_t w1 = st >> (blockIdx.x & 15);
+  const uint32_t m32 = wave_max_u32(w0);
+  const uint32_t m16 = wave_max_u16x2(pair_max_u16(w0, w1));
+  __shared__ uint32_t sh[128];
+  sh[threadIdx.x] = w0;
+  sh[64 + threadIdx.x] = w1;
+  __syncthreads();
+  uint32_t r = 0, r0 = 0, r1 = 0;
+  for (int i = 0; i < 64; ++i) {
+    r = max(r, sh[i]);
+    r0 = max(r0, max(sh[i] & 0x7FFFu, (sh[i] >> 16) & 0x7FFFu));
+    r1 = max(r1, max(sh[64 + i] & 0x7FFFu, (sh[64 + i] >> 16) & 0x7FFFu));
+  }
+  if (m32 != r) report(cnt, first, 7, blockIdx.x, threadIdx.x, m32);
+  if (m16 != (r0 | (r1 << 16))) report(cnt, first, 8, blockIdx.x, threadIdx.x, m16);
+}
+
+int main() {
+  unsigned long long* cnt;
+  uint32_t* first;
+  if (hipMalloc(&cnt, kChecks * sizeof(unsigned long long)) != hipSuccess) return 2;
+  if (hipMalloc(&first, kChecks * 4 * 3 * sizeof(uint32_t)) != hipSuccess) return 2;
+  if (hipMemset(cnt, 0, kChecks * sizeof(unsigned long long)) != hipSuccess) return 2;
+  if (hipMemset(first, 0, kChecks * 4 * 3 * sizeof(uint32_t)) != hipSuccess) return 2;
+  hipLaunchKernelGGL(check_conversion, dim3(8192), dim3(256), 0, 0, 0x43E80001u, cnt, first);   // |y| <= 464
+  hipLaunchKernelGGL(check_rows, dim3(0x7F80), dim3(256), 0, 0, cnt, first);
+  hipLaunchKernelGGL(check_products, dim3(0x7F80), dim3(256), 0, 0, cnt, first);
+  hipLaunchKernelGGL(check_maxima, dim3(65536), dim3(64), 0, 0, cnt, first);
+  const hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    printf("hip error: %s\n", hipGetErrorString(e));
+    return 2;
+  }
+  unsigned long long h[kChecks];
+  uint32_t f[kChecks * 4 * 3];
+  if (hipMemcpy(h, cnt, sizeof h, hipMemcpyDeviceToHost) != hipSuccess) return 2;
+  if (hipMemcpy(f, first, sizeof f, hipMemcpyDeviceToHost) != hipSuccess) return 2;
+  const char* names[kChecks] = {
+      "hardware E4M3 conversion vs e4m3_code, all fp32 |y| <= 464",
+      "row_scale_of vs a / 448, all bf16 a",
+      "codes_in_row vs e4m3_code(x / s), all bf16 pairs",
+      "quantize_pair vs e4m3_code(x / s), all bf16 pairs",
+      "e4m3_value2 vs e4m3_value, all codes",
+      "bf16 below the product vs fp64, all codes x scales",
+      "bf16 above the product vs fp64, all codes x scales",
+      "wave_max_u32, seeded rows",
+      "pair_max_u16 + wave_max_u16x2, seeded rows"};
+  int bad = 0;
+  for (int w = 0; w < kChecks; ++w) {
+    printf("%s: %llu mismatches\n", names[w], h[w]);
+    bad |= h[w] != 0;
+    for (unsigned k = 0; k < 4 && k < h[w]; ++k)
+      printf("  %08x %08x %08x\n", f[(w * 4 + k) * 3], f[(w * 4 + k) * 3 + 1], f[(w * 4 + k) * 3 + 2]);
+  }
+  return bad;
+}

@@ -185,7 +185,7 @@ __global__ void __launch_bounds__(64) select_kernel(PrefillArgs a) {
 // next key block's global loads are in flight while the current one is
 // computed, so one barrier per key block suffices.
 constexpr int kKStride = 136;              // bf16 per K row in LDS
-constexpr int kVStride = 72;               // bf16 per V^T row in LDS
+constexpr int kVStride = 68;               // bf16 per V^T row in LDS (136 B: 16 rows read as 8-byte pieces fall on distinct banks)
 constexpr int kKBytes = kB * kKStride * 2;
 constexpr int kVBytes = kHeadDim * kVStride * 2;
 constexpr int kBufBytes = kKBytes + kVBytes;
@@ -194,8 +194,8 @@ template <int NT>
 struct Stage {
   static constexpr int KP = 1024 / NT;   // 16-byte pieces of K per thread
   static constexpr int VU = 512 / NT;    // V units (channel pair x 8 keys) per thread
-  uint4 k[KP];
-  uint32_t v[VU][8];
+  uint32_t k[KP][4];                     // (32-bit words: held as 16-byte vectors, the pieces
+  uint32_t v[VU][8];                     // went to scratch memory, whose store waited for the loads)
 };
 
 // Which key blocks a query block attends: [0, n1) then [w0, j] (the second
@@ -266,7 +266,8 @@ __global__ void __launch_bounds__(NH * 128) attn_kernel(PrefillArgs a) {
     for (int x = 0; x < St::KP; ++x) {
       const int p = tid + NT * x;                       // < 1024
       const int64_t row = min(base + p / 16, L - 1);
-      st.k[x] = *reinterpret_cast<const uint4*>(kh + row * kHeadDim + 8 * (p % 16));
+      const uint4 kv4 = *reinterpret_cast<const uint4*>(kh + row * kHeadDim + 8 * (p % 16));
+      st.k[x][0] = kv4.x; st.k[x][1] = kv4.y; st.k[x][2] = kv4.z; st.k[x][3] = kv4.w;
     }
 #pragma unroll
     for (int x = 0; x < St::VU; ++x) {
@@ -285,7 +286,7 @@ __global__ void __launch_bounds__(NH * 128) attn_kernel(PrefillArgs a) {
 #pragma unroll
     for (int x = 0; x < St::KP; ++x) {
       const int p = tid + NT * x;
-      *reinterpret_cast<uint4*>(kl_ + ((p / 16) * kKStride + 8 * (p % 16)) * 2) = st.k[x];
+      *reinterpret_cast<uint4*>(kl_ + ((p / 16) * kKStride + 8 * (p % 16)) * 2) = uint4{st.k[x][0], st.k[x][1], st.k[x][2], st.k[x][3]};
     }
 #pragma unroll
     for (int x = 0; x < St::VU; ++x) {
@@ -301,8 +302,12 @@ __global__ void __launch_bounds__(NH * 128) attn_kernel(PrefillArgs a) {
       hi.y = (v[2] >> 16) | (v[3] & 0xFFFF0000u);
       hi.z = (v[4] >> 16) | (v[5] & 0xFFFF0000u);
       hi.w = (v[6] >> 16) | (v[7] & 0xFFFF0000u);
-      *reinterpret_cast<uint4*>(vl + ((2 * cp) * kVStride + 8 * kg) * 2) = lo;
-      *reinterpret_cast<uint4*>(vl + ((2 * cp + 1) * kVStride + 8 * kg) * 2) = hi;
+      uint2* d0 = reinterpret_cast<uint2*>(vl + ((2 * cp) * kVStride + 8 * kg) * 2);      // 8-byte aligned rows
+      uint2* d1 = reinterpret_cast<uint2*>(vl + ((2 * cp + 1) * kVStride + 8 * kg) * 2);
+      d0[0] = uint2{lo.x, lo.y};
+      d0[1] = uint2{lo.z, lo.w};
+      d1[0] = uint2{hi.x, hi.y};
+      d1[1] = uint2{hi.z, hi.w};
     }
   };
 
@@ -341,20 +346,25 @@ __global__ void __launch_bounds__(NH * 128) attn_kernel(PrefillArgs a) {
       }
     }
 
-    // mask: causal, the sequence's end, and the streaming pattern
-    const int64_t kpos0 = (int64_t)kbk * kB + 4 * quad;
-    const bool full = dynamic && kbk < j;
+    // mask: causal, the sequence's end, and the streaming pattern. A key
+    // block below the diagonal needs none when the head is dynamic, or when
+    // it lies wholly in the sink or wholly inside every row's window (its
+    // first key at or after the last row's window start)
+    const int32_t kpos0 = kbk * kB + 4 * quad;      // positions fit 32 bits (L <= 2^24)
+    const bool full = kbk < j && (dynamic || (kbk + 1) * kB <= a.sink ||
+                                  (int64_t)kbk * kB >= (int64_t)(j + 1) * kB - a.window);
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      const int64_t tq = (int64_t)j * kB + 32 * rh + 16 * qt + col;
+      const int32_t tq = j * kB + 32 * rh + 16 * qt + col;
       if (!full) {
+        const int32_t Li = (int32_t)L, sink = a.sink, wlo = tq + 1 - a.window;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int64_t sp = kpos0 + 16 * t + r;
-            bool ok = sp <= tq && sp < L;
-            if (!dynamic) ok = ok && (sp < a.sink || sp >= tq + 1 - a.window);
+            const int32_t sp = kpos0 + 16 * t + r;
+            bool ok = sp <= tq && sp < Li;
+            if (!dynamic) ok = ok && (sp < sink || sp >= wlo);
             s[qt][t][r] = ok ? s[qt][t][r] : -INFINITY;
           }
       }

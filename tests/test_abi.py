@@ -322,6 +322,50 @@ def test_fp8_append_select_checks_workspace_before_any_launch(spa):
     assert launches(spa) == before
 
 
+def prefill(spa, heads=None, hkv=8, cfg=None, L=40000, q=FAKE, k=FAKE, v=FAKE, wq=FAKE, wk=FAKE, out=FAKE,
+            ws=FAKE, ws_bytes=1 << 30, cfg_ptr=True):
+    heads = heads or mkheads(spa)
+    cfg = cfg or spa.Prefill().c()
+    c = ctypes.byref(cfg) if cfg_ptr else None
+    return spa.lib().spa_prefill_attn(ctypes.byref(heads), hkv, c, L, q, k, v, wq, wk, out, None, None, None,
+                                      None, ws, ws_bytes, None)
+
+
+def test_prefill_validation(spa):
+    """spa_prefill_attn and spa_prefill_workspace_bytes reject bad arguments on
+    the host: configuration, head shapes, lengths, pointers, workspace."""
+    L = spa.lib()
+    c = lambda **kw: spa.Prefill(**kw).c()
+    assert prefill(spa, cfg_ptr=False) == 1                         # no configuration
+    assert prefill(spa, hkv=0) == 1 and prefill(spa, hkv=200) == 1
+    assert prefill(spa, cfg=c(head_dim=64)) == 2 and prefill(spa, cfg=c(head_dim=0)) == 1
+    assert prefill(spa, cfg=c(block=32)) == 2 and prefill(spa, cfg=c(block=0)) == 1
+    assert prefill(spa, cfg=c(budget=0)) == 1
+    assert prefill(spa, L=-1) == 1
+    assert prefill(spa, L=(1 << 24) + 1) == 2                       # positions past 2^24
+    assert prefill(spa, heads=mkheads(spa, hq=12)) == 1             # H_q not a multiple of H_kv
+    assert prefill(spa, heads=mkheads(spa, hq=8 * 32)) == 2         # a group of 32 is not built
+    # a selection row holds at most 8192 blocks (sparse mode only; the dense
+    # mode's acceptance is checked with the launch stubs below)
+    assert prefill(spa, L=8193 * 64) == 2
+    for name in ("q", "k", "v", "out"):
+        assert prefill(spa, **{name: None}) == 1, name
+    assert prefill(spa, wq=None) == 1 and prefill(spa, wk=None) == 1   # the dynamic heads select
+    assert prefill(spa, ws=None) == 4
+    hs = mkheads(spa)
+    need = L.spa_prefill_workspace_bytes(ctypes.byref(hs), 8, ctypes.byref(c()), 40000)
+    assert need > 0
+    assert prefill(spa, ws_bytes=need - 1) == 4
+    assert spa.lib().spa_last_error()
+    # sizes: 0 for invalid shapes; the dense mode needs no selection workspace
+    assert L.spa_prefill_workspace_bytes(ctypes.byref(hs), 0, ctypes.byref(c()), 40000) == 0
+    assert L.spa_prefill_workspace_bytes(ctypes.byref(hs), 8, ctypes.byref(c(head_dim=64)), 40000) == 0
+    dense = L.spa_prefill_workspace_bytes(ctypes.byref(hs), 8, ctypes.byref(c()), 1000)
+    assert 0 < dense < need
+    streaming = mkheads(spa, kind=(0,) * 8)
+    assert L.spa_prefill_workspace_bytes(ctypes.byref(streaming), 8, ctypes.byref(c()), 40000) == dense
+
+
 def test_every_failing_call_launches_nothing(spa):
     """With the stub build loaded, the validation failures of the calls above
     enqueue nothing, and a call that passes its checks launches."""
@@ -337,6 +381,14 @@ def test_every_failing_call_launches_nothing(spa):
     assert launches(spa) == before
     assert attn(spa, mkpool(spa), mkheads(spa), mkbatch(spa)) == 0      # passes: one launch
     assert launches(spa) == before + 1
+    test_prefill_validation(spa)
+    assert launches(spa) == before + 1
+    assert prefill(spa, L=0) == 0                                       # an empty prompt: nothing to do
+    assert launches(spa) == before + 1
+    assert prefill(spa) == 0                                            # sparse: passes, launches
+    assert launches(spa) == before + 2
+    assert prefill(spa, L=8193 * 64, cfg=spa.Prefill(dense_below=1 << 30).c()) == 0   # dense past 8192 blocks
+    assert launches(spa) == before + 3
 
 
 def test_sparse_config_of_the_write_up(spa):

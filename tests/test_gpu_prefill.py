@@ -170,3 +170,49 @@ def test_128k_full_size_sampled_rows():
                                      rng.integers(0, pf.L, 40)])).astype(np.int64)
     rep = check(pf, rows=rows)
     assert rep["sel_rows"] == 4 * 2048
+
+
+def test_graph_replay_and_workspace_selection():
+    """spa_prefill_attn captured in a HIP graph and replayed three times (eager
+    work in between) gives the eager call's outputs bit for bit; with the
+    selection left in the workspace (sel_blocks / sel_count / block_scores not
+    requested) the outputs are the same bytes too."""
+    import sparse_paged_attention_amd as spa
+    pf = SMALL
+    Qb, Kb, Vb, Wq, Wk = inputs(pf)
+    heads = spa.Heads(pf.hq, pf.kind, pf.sink, pf.window)
+    cfg = spa.Prefill(budget=pf.budget, dense_below=pf.dense_below, block=pf.block)
+    L = pf.L
+    nb = -(-L // 64)
+    kb = min(max(1, pf.budget // 64), nb)
+    q, k, v = bits_to_bf16(Qb), bits_to_bf16(Kb), bits_to_bf16(Vb)
+    wq, wk = bits_to_bf16(Wq), bits_to_bf16(Wk)
+    ws = torch.empty(spa.prefill_workspace_bytes(heads, pf.hkv, cfg, L), dtype=torch.uint8, device="cuda")
+
+    def outputs():
+        return (torch.full((pf.hq, L, 128), float("nan"), dtype=torch.float32, device="cuda"),
+                torch.full((pf.hq, L), float("nan"), dtype=torch.float32, device="cuda"))
+
+    out0, lse0 = outputs()
+    sel = torch.full((pf.hkv, nb, kb), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((pf.hkv, nb), dtype=torch.int32, device="cuda")
+    spa.prefill_attn(heads, cfg, q, k, v, wq, wk, out0, lse0, sel, cnt, None, ws)
+    out1, lse1 = outputs()
+    spa.prefill_attn(heads, cfg, q, k, v, wq, wk, out1, lse1, None, None, None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1) and torch.equal(lse0, lse1)
+
+    out2, lse2 = outputs()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        spa.prefill_attn(heads, cfg, q, k, v, wq, wk, out2, lse2, None, None, None, ws)
+    for rep in range(3):
+        out2.fill_(float("nan"))
+        lse2.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        x = (q.float() * 2).sum()                      # eager work between the replays
+        assert torch.isfinite(x)
+        assert torch.equal(out2, out0) and torch.equal(lse2, lse0), f"replay {rep}"
+    log(f"  prefill graph: 3 replays bit-identical, L={L}")

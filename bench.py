@@ -182,6 +182,18 @@ def percentiles(xs) -> dict:
             "p90": round(float(np.percentile(a, 90)), 3), "n": int(a.size)}
 
 
+def timing_plan(steps: int, warmup: int, replicas: int, reuse: int) -> tuple:
+    """Replays of the one-cycle graph (reuse decode steps of every replica, the
+    first of them selecting) that cover at least `steps` layer-steps and at
+    least MIN_REPLAYS, and untimed replays after the eager first cycle that
+    cover `warmup`. Every timed replay is a whole cycle, so the timed mix of
+    selecting and plain steps is 1 : reuse - 1 whatever the arguments."""
+    cycle = replicas * reuse
+    replays = max(MIN_REPLAYS, -(-steps // cycle))
+    warm_replays = max(1, -(-max(warmup - cycle, 0) // cycle))
+    return replays, warm_replays
+
+
 def time_graph(torch, build, replays: int, per: int) -> list:
     """Captures build() in a HIP graph, replays it once untimed, then `replays`
     times, each between two events on the current stream; returns the time
@@ -493,8 +505,7 @@ def main() -> int:
         log(f"[bench] probe done: {cycle} steps, copy of {COPY_BYTES} bytes")
         return 0
 
-    replays = max(MIN_REPLAYS, -(-args.steps // cycle))
-    warm_replays = max(1, -(-max(args.warmup - cycle, 0) // cycle))
+    replays, warm_replays = timing_plan(args.steps, args.warmup, R, C)
 
     def run_cycle():
         for t in range(t0, t0 + C):

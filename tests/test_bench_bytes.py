@@ -53,3 +53,18 @@ def test_fp8_bytes_at_128k():
     count = 131071
     written = 2 * 8 * count * (ROW + ROW8)              # bf16 rows read, fp8 rows written, K and V
     assert bench.bulk_write_bytes(wl, count, ROW8) == written + 4 * 8192 * 2 * ROW + 2048 * 4
+
+
+def test_timed_steps_are_whole_reuse_cycles():
+    """Whatever --steps / --warmup say, the timed region is whole reuse cycles
+    of every layer replica (one selecting step in C), at least 20 of them, so
+    the headline is the C-weighted step."""
+    for steps, warmup in ((20, 5), (64, 16), (1, 0), (640, 64), (33, 100)):
+        for R, C in ((8, 4), (12, 1), (2, 4)):
+            replays, warm = bench.timing_plan(steps, warmup, R, C)
+            assert replays >= bench.MIN_REPLAYS and replays * R * C >= steps
+            assert warm >= 1 and (warm + 1) * R * C >= warmup
+            timed_select = replays * R                    # the first step of each cycle selects
+            assert timed_select * C == replays * R * C
+    # 20 / 5 and 64 / 16 time the same work at the benchmark shape
+    assert bench.timing_plan(20, 5, 8, 4)[0] == bench.timing_plan(64, 16, 8, 4)[0] == 20

@@ -485,7 +485,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
   __shared__ int32_t sh_wave[kTopkWaves];
   __shared__ uint32_t sh_min[kTopkWaves], sh_max[kTopkWaves];
   __shared__ int32_t sh_cnt[kTopkWaves];
-  __shared__ int32_t sh_pick[2];
+  __shared__ int32_t sh_pick[3];
   __shared__ int32_t sh_nc;
   __shared__ uint64_t cand_key[kMaxCand];
   __shared__ uint32_t sel_bits[kTopkThreads];
@@ -512,27 +512,33 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
   }
   int32_t need = k;
   int32_t rank[E];
+  int32_t known = -1;       // candidates left by the previous round's pick (its bin's count)
 
   for (int round = 0; round < 8 && need > 0; ++round) {
-    // candidate count and key range; the histogram is cleared meanwhile
     uint32_t lo = 0xFFFFFFFFu, hi = 0;
+    int32_t total = known;
+    // when the candidates the last pick left are all kept, or few enough to
+    // rank exactly, their key range is not needed (block-uniform)
+    if (!(known >= 0 && (known <= need || known <= kMaxCand))) {
+      // candidate count and key range; the histogram is cleared meanwhile
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (cand >> e & 1) { lo = min(lo, ord[e]); hi = max(hi, ord[e]); }
-    lo = wave_reduce(lo, [](uint32_t x, uint32_t y) { return min(x, y); });
-    hi = wave_reduce(hi, [](uint32_t x, uint32_t y) { return max(x, y); });
-    const int32_t c = (int32_t)wave_reduce((uint32_t)__popc(cand), [](uint32_t x, uint32_t y) { return x + y; });
-    if (lane == 0) { sh_min[wave] = lo; sh_max[wave] = hi; sh_cnt[wave] = c; }
+      for (int e = 0; e < E; ++e)
+        if (cand >> e & 1) { lo = min(lo, ord[e]); hi = max(hi, ord[e]); }
+      lo = wave_reduce(lo, [](uint32_t x, uint32_t y) { return min(x, y); });
+      hi = wave_reduce(hi, [](uint32_t x, uint32_t y) { return max(x, y); });
+      const int32_t c = (int32_t)wave_reduce((uint32_t)__popc(cand), [](uint32_t x, uint32_t y) { return x + y; });
+      if (lane == 0) { sh_min[wave] = lo; sh_max[wave] = hi; sh_cnt[wave] = c; }
 #pragma unroll
-    for (int i = 0; i < PER; ++i) hist[tid * PER + i] = 0;
-    sel_bits[tid] = 0;
-    if (tid == 0) sh_nc = 0;
-    __syncthreads();
-    lo = 0xFFFFFFFFu;
-    hi = 0;
-    int32_t total = 0;
+      for (int i = 0; i < PER; ++i) hist[tid * PER + i] = 0;
+      sel_bits[tid] = 0;                             // (untouched until the exact ranking)
+      if (tid == 0) sh_nc = 0;
+      __syncthreads();
+      lo = 0xFFFFFFFFu;
+      hi = 0;
+      total = 0;
 #pragma unroll
-    for (int w = 0; w < kTopkWaves; ++w) { lo = min(lo, sh_min[w]); hi = max(hi, sh_max[w]); total += sh_cnt[w]; }
+      for (int w = 0; w < kTopkWaves; ++w) { lo = min(lo, sh_min[w]); hi = max(hi, sh_max[w]); total += sh_cnt[w]; }
+    }
     if (total <= need) { sel |= cand; cand = 0; break; }
     if (total <= kMaxCand) {
       // exact ranks by (key descending, page id ascending) among the few left
@@ -588,12 +594,13 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
     for (int i = 0; i < PER; ++i) { cnt[i] = hist[BINS - 1 - (tid * PER + i)]; sum += cnt[i]; }
     int32_t tot2;
     int32_t run = block_exclusive_scan(sum, sh_wave, tot2);       // keys in higher bins
-    int32_t hit = -1, hit_run = 0;                // the owned bin where the count reaches `need`
+    int32_t hit = -1, hit_run = 0, hit_cnt = 0;   // the owned bin where the count reaches `need`
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const bool here = run < need && run + cnt[i] >= need;
       hit = here ? i : hit;
       hit_run = here ? run : hit_run;
+      hit_cnt = here ? cnt[i] : hit_cnt;
       run += cnt[i];
     }
     if (hit >= 0) {
@@ -604,10 +611,12 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
       asm volatile("" : "+v"(t));
       sh_pick[0] = BINS - 1 - (t * PER + hit);
       sh_pick[1] = hit_run;
+      sh_pick[2] = hit_cnt;
     }
     __syncthreads();
     const uint32_t pick = (uint32_t)sh_pick[0];
     const int32_t above = sh_pick[1];
+    known = sh_pick[2];
 #pragma unroll
     for (int e = 0; e < E; ++e)
       if (cand >> e & 1) {

@@ -381,11 +381,9 @@ __global__ void __launch_bounds__(NH * 128) attn_kernel(PrefillArgs a) {
         bm = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
       }
       bm *= kScaleLog2;
-      if (bm == -INFINITY) {                         // nothing of this block for this tile's queries
-#pragma unroll
-        for (int t = 0; t < 4; ++t) s[qt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        continue;
-      }
+      // a column with nothing of this block (bm = -inf) keeps its reference;
+      // its scores are -inf and their probabilities come out 0 against any
+      // finite reference (0 while the column has none yet): no branch
       const bool first = m_ref[qt] == -INFINITY;
       const bool raise = bm > m_ref[qt] + kRescaleSlack;
       const float mn = raise ? bm : m_ref[qt];
@@ -396,11 +394,12 @@ __global__ void __launch_bounds__(NH * 128) attn_kernel(PrefillArgs a) {
         for (int c = 0; c < 8; ++c) o[qt][c] *= alpha;
       }
       m_ref[qt] = mn;
+      const float mx = mn == -INFINITY ? 0.f : mn;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][t][r], kScaleLog2, -mn));
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][t][r], kScaleLog2, -mx));
           l_sum[qt] += p;
           s[qt][t][r] = p;
         }

@@ -363,8 +363,7 @@ __global__ void __launch_bounds__(NH * 128) attn_kernel(PrefillArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int32_t sp = kpos0 + 16 * t + r;
-            bool ok = sp <= tq && sp < Li;
-            if (!dynamic) ok = ok && (sp < sink || sp >= wlo);
+            const bool ok = (sp <= tq) & (sp < Li) & (dynamic | (sp < sink) | (sp >= wlo));   // no branches
             s[qt][t][r] = ok ? s[qt][t][r] : -INFINITY;
           }
       }

@@ -56,6 +56,7 @@ ATTN_KERNELS_FP8 = "attn_kernel<16, 5, 4, false, false, true>|combine_kernel"
 WRITE_KERNELS_FP8 = "write_kernel_q8<16>"
 ROW_BYTES = {"bf16": 256, "fp8": 128 + 4}     # one stored key or value row: elements (+ its fp32 scale)
 MIN_REPLAYS = 20
+WRITE_REPS = 10                       # warm prompt writes timed
 
 # per workload: layer replicas (each step's working set times R must exceed
 # the 256 MB last-level cache), decode steps generated, a description
@@ -112,13 +113,23 @@ def algorithmic_bytes(wl, L, select: bool, row: int = 256, tail: int = 0) -> dic
                 total=attn + append + summary + sel)
 
 
-def bulk_write_bytes(wl, count: int, row: int = 256) -> int:
-    """Bytes one prompt write of `count` tokens must move: read the caller's
-    bf16 K and V rows, write them into the pool (`row` bytes each stored),
-    write the min/max summary of every logical page of the dynamic heads, read
-    the page-table row."""
+def bulk_write_bytes(wl, count: int, row: int = 256, ring: bool = False) -> int:
+    """Bytes one prompt write of `count` tokens from position 0 must move: read
+    the caller's bf16 K and V rows, write them into the pool (`row` bytes each
+    stored), write the min/max summary of every logical page of the dynamic
+    heads, read the page-table row. With `ring`, a streaming head keeps only
+    the tokens of its sink pages and of the last ceil(window / P) + 1 physical
+    pages (the rest would be overwritten within the same write), and only those
+    are read and written."""
     n_dyn = sum(wl.kind)
-    rows = wl.hkv * count
+    n_str = wl.hkv - n_dyn
+    kept = count
+    if ring and count > 0:
+        sink_pages = -(-wl.sink // wl.P)
+        win_pages = -(-wl.window // wl.P) + 1
+        last = (count - 1) // wl.P
+        kept = min(sink_pages * wl.P, count) + max(0, count - max(sink_pages, last - win_pages + 1) * wl.P)
+    rows = n_dyn * count + n_str * kept
     return 2 * rows * (wl.d * 2 + row) + n_dyn * (-(-count // wl.p)) * 2 * wl.d * 2 + (-(-count // wl.P)) * 4
 
 
@@ -447,6 +458,8 @@ def main() -> int:
             layer.write_tokens(b, 0, Kd, Vd)
             e1.record()
             write_events.append((e0, e1, pre))
+        if b == 0:
+            first_prompt = (Kd, Vd, pre)        # kept for the warm timing of the write below
         del Kd, Vd
         newk[:, b] = K[:, pre:pre + wl.steps].transpose(1, 0, 2)
         newv[:, b] = V[:, pre:pre + wl.steps].transpose(1, 0, 2)
@@ -456,10 +469,24 @@ def main() -> int:
         layer.set_lengths([c - 1 for c in wl.contexts])
         layer.set_budget([wl.budget_at(c) for c in wl.contexts])
     torch.cuda.synchronize()
-    write_sel = [(e0, e1, n) for e0, e1, n in write_events if n == write_events[0][2]]
-    write_us = sorted(1e3 * e0.elapsed_time(e1) for e0, e1, _ in write_sel)
+    # the set-up writes are the first into freshly allocated pools; the prompt
+    # write is timed warm, as the steps are: sequence 0's prompt written again
+    # into layer 0 (the same bytes, so the pool does not change)
+    cold_sel = [(e0, e1, n) for e0, e1, n in write_events if n == write_events[0][2]]
+    cold_us = sorted(1e3 * e0.elapsed_time(e1) for e0, e1, _ in cold_sel)
+    Kd, Vd, pre0 = first_prompt
+    write_us = []
+    for _ in range(WRITE_REPS):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        layers[0].write_tokens(0, 0, Kd, Vd)
+        e1.record()
+        write_us.append((e0, e1))
+    torch.cuda.synchronize()
+    write_us = sorted(1e3 * e0.elapsed_time(e1) for e0, e1 in write_us)
+    del Kd, Vd, first_prompt
     write_med = write_us[len(write_us) // 2]
-    write_bytes = bulk_write_bytes(wl, write_sel[0][2], row)
+    write_bytes = bulk_write_bytes(wl, pre0, row, ring=args.storage != "table")
 
     def dev(a, dtype=torch.bfloat16):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(dtype)
@@ -626,12 +653,17 @@ def main() -> int:
                      "frac_of_measured_ceiling": round(attn_gbps / ceiling["GBps"], 4) if ceiling else None},
         "read_ceiling": ceiling,
         "cpu_baseline": cpu,
-        "bulk_write": {"what": f"spa_kv_pool_write of one {write_sel[0][2]}-token prompt (all {wl.hkv} KV heads, "
-                               f"summaries of the {sum(wl.kind)} dynamic heads in the same pass)",
+        "bulk_write": {"what": f"spa_kv_pool_write of one {pre0}-token prompt (all {wl.hkv} KV heads"
+                               + (", the streaming heads' sink and last window pages only"
+                                  if args.storage != "table" else "")
+                               + f", summaries of the {sum(wl.kind)} dynamic heads in the same pass)",
                        "median_us": round(write_med, 1), "bytes": int(write_bytes),
                        "achieved": round(write_bytes / (write_med * 1e-6) / 1e9, 1), "unit": "GB/s",
                        "frac": round(write_bytes / (write_med * 1e-6) / 1e9 / PEAK_GBPS, 4),
-                       "traffic": write_traffic, "calls": len(write_us)},
+                       "traffic": write_traffic, "calls": len(write_us),
+                       "first_writes_median_us": round(cold_us[len(cold_us) // 2], 1),
+                       "timing": "median of warm rewrites of sequence 0's prompt into one layer (the same bytes); "
+                                 "first_writes_median_us: the set-up's first writes into the fresh pools"},
     }
     print(json.dumps(res), flush=True)
     return 0

@@ -68,3 +68,19 @@ def test_timed_steps_are_whole_reuse_cycles():
             assert timed_select * C == replays * R * C
     # 20 / 5 and 64 / 16 time the same work at the benchmark shape
     assert bench.timing_plan(20, 5, 8, 4)[0] == bench.timing_plan(64, 16, 8, 4)[0] == 20
+
+
+def test_ring_write_bytes_at_128k():
+    """Ring storage: a streaming head's prompt write keeps the sink's page
+    (tokens 0-63) and the last ceil(2048 / 64) + 1 = 33 physical pages of the
+    131071-token prompt (pages 2015-2047: tokens 128960-131070); the dynamic
+    heads write every token."""
+    wl = W.WORKLOADS["llama3_128k"]
+    count = 131071
+    kept = 64 + (count - 2015 * 64)
+    assert kept == 2175
+    rows = 2 * (4 * count + 4 * kept) * 2 * ROW
+    assert bench.bulk_write_bytes(wl, count, ring=True) == rows + 4 * 8192 * 2 * ROW + 2048 * 4
+    # a prompt shorter than sink + window is kept whole
+    assert bench.bulk_write_bytes(wl, 2000, ring=True) == bench.bulk_write_bytes(wl, 2000)
+    assert bench.bulk_write_bytes(wl, 0, ring=True) == 0

@@ -129,11 +129,14 @@ __global__ void __launch_bounds__(64) write_kernel(PoolArgs pl, const int32_t* _
 }
 
 // write_kernel for fp8 pages: each token's key and value rows are quantized
-// (the row maxima of 16 rows at a time reduced across the wave two rows per
-// word; each code from a reciprocal bracket of the quotient, codes_in_row),
-// codes and scales are written, and the summary of a dynamic head's page is
+// and codes and scales are written; the summary of a dynamic head's page is
 // the min / max of the dequantized keys (tokens before `start` read back
-// from the pool), rounded outward to bf16.
+// from the pool), rounded outward to bf16. Per chunk of 16 tokens, the 32
+// key and value row maxima are reduced across the wave together, two rows
+// per word, by a reduce-scatter that leaves each lane with two of them; the
+// lanes compute those rows' scales and reciprocal brackets in parallel and
+// store the scales, and each row's bracket is read from its lane into scalar
+// registers for coding the row (codes_bracketed).
 template <int PG>
 __global__ void __launch_bounds__(64) write_kernel_q8(PoolArgs pl, const int32_t* __restrict__ pt, int64_t start,
                                                       int64_t count, const uint32_t* __restrict__ k,
@@ -169,51 +172,69 @@ __global__ void __launch_bounds__(64) write_kernel_q8(PoolArgs pl, const int32_t
       mm.add(reinterpret_cast<const uint16_t*>(kd + (t - t0) * kHeadDim)[lane], pl.ks[row0 + (t - t0)]);
   const bool full = lo == t0 && hi == t0 + PG;
   uint32_t a[PG / 4], c[PG / 4];                    // value codes of channels 2l / 2l + 1, 4 tokens a word
+  static_assert(PG % 16 == 0, "pages of 16, 32 or 64 tokens");
 #pragma unroll
-  for (int i = 0; i < PG / 4; ++i) { a[i] = 0; c[i] = 0; }
-  // chunks of 16 rows: all of a chunk's rows in flight at once
-  constexpr int CH = PG < 16 ? PG : 16;
+  for (int c0 = 0; c0 < PG; c0 += 16) {             // chunks of 16 rows, all in flight at once
+    if (t0 + c0 >= hi || t0 + c0 + 16 <= lo) continue;     // wave-uniform
+    uint32_t kw[16], vw[16];
 #pragma unroll
-  for (int c0 = 0; c0 < PG; c0 += CH) {
-    if (t0 + c0 >= hi || t0 + c0 + CH <= lo) continue;     // wave-uniform
-    uint32_t kw[CH], vw[CH];
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {                  // rows outside the range re-read row lo
+    for (int u = 0; u < 16; ++u) {                  // rows outside the range re-read row lo
       const int64_t t = t0 + c0 + u;
       const int64_t row = (int64_t)h * count + ((t >= lo && t < hi) ? t : lo) - start;
       kw[u] = k[row * 64 + lane];
       vw[u] = v[row * 64 + lane];
     }
-    // every row's maximum magnitude, two rows per word (16-bit halves), the
-    // reductions of the chunk's rows in flight together
-    uint32_t km[CH / 2], vm[CH / 2];
+    // the 32 rows' maxima spread over the lanes (chunk_row_maxima), each
+    // lane's two rows' scales and brackets computed where they lie
+    uint32_t kp[8], vp[8];
 #pragma unroll
-    for (int i = 0; i < CH / 2; ++i) {
-      km[i] = wave_max_u16x2(pair_max_u16(kw[2 * i], kw[2 * i + 1]));
-      vm[i] = wave_max_u16x2(pair_max_u16(vw[2 * i], vw[2 * i + 1]));
+    for (int i = 0; i < 8; ++i) {
+      kp[i] = pair_max_u16(kw[2 * i], kw[2 * i + 1]);
+      vp[i] = pair_max_u16(vw[2 * i], vw[2 * i + 1]);
     }
+    const uint32_t m = chunk_row_maxima(kp, vp);
+    float s0, lo0, hi0, s1, lo1, hi1;               // rows 2i (low half) and 2i + 1 (high half)
+    row_bracket(m & 0xFFFFu, s0, lo0, hi0);
+    row_bracket(m >> 16, s1, lo1, hi1);
+    {                                               // the scales: one lane of each 4 stores its two rows'
+      const int i = 4 * ((lane >> 3) & 1) + fold_row(lane >> 4), r = c0 + 2 * i;
+      float* dst = ((lane >> 2) & 1 ? pl.vs : pl.ks) + row0 + r;
+      if ((lane & 3) == 0) {
+        if (full) {
+          *reinterpret_cast<float2*>(dst) = make_float2(s0, s1);
+        } else {
+          if (t0 + r >= lo && t0 + r < hi) dst[0] = s0;
+          if (t0 + r + 1 >= lo && t0 + r + 1 < hi) dst[1] = s1;
+        }
+      }
+    }
+    uint32_t vcs[16];
 #pragma unroll
-    for (int u = 0; u < CH; ++u) {
+    for (int u = 0; u < 16; ++u) {
       const int64_t t = t0 + c0 + u;
+      vcs[u] = 0;
       if (t < lo || t >= hi) continue;              // wave-uniform
-      const RowScale rk = row_scale_of((km[u / 2] >> (16 * (u & 1))) & 0xFFFFu);
-      const RowScale rv = row_scale_of((vm[u / 2] >> (16 * (u & 1))) & 0xFFFFu);
-      const uint32_t kc = codes_in_row(kw[u], rk);
-      const uint32_t vc = codes_in_row(vw[u], rv);
+      const int lk = fold_lane(false, u >> 1), lv = fold_lane(true, u >> 1);
+      const float sl = u & 1 ? s1 : s0, bl = u & 1 ? lo1 : lo0, bh = u & 1 ? hi1 : hi0;
+      const uint32_t kc = codes_bracketed(kw[u], lane_value(bl, lk), lane_value(bh, lk), sl, lk);
+      const uint32_t vc = codes_bracketed(vw[u], lane_value(bl, lv), lane_value(bh, lv), sl, lv);
       const int r = c0 + u;                         // row in the page
       reinterpret_cast<uint16_t*>(kd + r * kHeadDim)[lane] = (uint16_t)kc;
-      if (lane == 0) {
-        pl.ks[row0 + r] = rk.s;
-        pl.vs[row0 + r] = rv.s;
-      }
-      if (full) {
-        a[r / 4] |= (vc & 0xFFu) << (8 * (r % 4));
-        c[r / 4] |= ((vc >> 8) & 0xFFu) << (8 * (r % 4));
-      } else {
+      vcs[u] = vc;
+      if (!full) {
         vd[(2 * lane) * PG + r] = (uint8_t)vc;
         vd[(2 * lane + 1) * PG + r] = (uint8_t)(vc >> 8);
       }
-      if (dynamic) mm.add(kc, rk.s);
+      if (dynamic) mm.add(kc, lane_value(sl, lk));
+    }
+    if (full) {                                     // 4 rows' codes to one word per channel
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t t01 = __builtin_amdgcn_perm(vcs[4 * g + 1], vcs[4 * g], 0x05010400u);
+        const uint32_t t23 = __builtin_amdgcn_perm(vcs[4 * g + 3], vcs[4 * g + 2], 0x05010400u);
+        a[c0 / 4 + g] = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+        c[c0 / 4 + g] = __builtin_amdgcn_perm(t23, t01, 0x07060302u);
+      }
     }
   }
   if (full) {

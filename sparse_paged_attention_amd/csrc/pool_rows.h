@@ -221,18 +221,6 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16_pair, a),
                                                                 __builtin_bit_cast(u16_pair, b)));
 }
-// Wave-wide maximum of each 16-bit half (every lane of the wave active), by
-// the steps of wave_max_u32.
-__device__ __forceinline__ uint32_t wave_max_u16x2(uint32_t v) {
-  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
-  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
-  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));
-  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));
-  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  v = pk_max_u16(a[0], a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return pk_max_u16(b[0], b[1]);
-}
 // The magnitudes (bf16 bits less the sign) of two rows' bf16 pairs w0, w1
 // folded into one word: low half the larger of w0's two, high half w1's.
 __device__ __forceinline__ uint32_t pair_max_u16(uint32_t w0, uint32_t w1) {
@@ -240,31 +228,86 @@ __device__ __forceinline__ uint32_t pair_max_u16(uint32_t w0, uint32_t w1) {
   return pk_max_u16(__builtin_amdgcn_perm(b, a, 0x05040100u), __builtin_amdgcn_perm(b, a, 0x07060302u));
 }
 
-// A row's scale RN(amax / 448) with the reciprocal bracket used to code its
+// Steps of a reduce-scatter over the wave: two words in, one out, each lane
+// keeping the maximum of a pair of lanes for one of the two words.
+// Lane-half swap: lanes 0-31 end with x over {l, l + 32}, lanes 32-63 with y.
+__device__ __forceinline__ uint32_t fold32(uint32_t x, uint32_t y) {
+  const auto s = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+  return pk_max_u16(s[0], s[1]);
+}
+// 16-lane row swap: rows 0 and 2 end with x over {l, l + 16}, rows 1 and 3
+// with y.
+__device__ __forceinline__ uint32_t fold16(uint32_t x, uint32_t y) {
+  const auto s = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+  return pk_max_u16(s[0], s[1]);
+}
+// Within each 16-lane row, by a DPP lane pattern CTRL (a mirror): the 4-lane
+// banks in XB keep x folded with its mirror lanes, the other banks y.
+template <int CTRL, int XB>
+__device__ __forceinline__ uint32_t fold_banks(uint32_t x, uint32_t y) {
+  const uint32_t a = (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)y, CTRL, 0xF, 0xF ^ XB, false);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_update_dpp((int)y, (int)x, CTRL, 0xF, XB, false);
+  return pk_max_u16(a, b);
+}
+
+// Row maxima of a chunk of 16 key rows and 16 value rows, from their pair
+// words (kp[i], vp[i]: pair_max_u16 of rows 2i and 2i + 1, every lane of the
+// wave active), by a reduce-scatter instead of one all-reduce per word: two
+// lane-half swaps, one row swap, two bank folds and a 4-lane all-reduce for
+// the 16 words, after which lane 16 rho + 4 beta + q (q = 0..3) holds the
+// wave maxima of pair i = 4 (beta >> 1) + fold_row(rho) of the keys (beta
+// even) or values (beta odd): low half row 2i, high half row 2i + 1.
+// fold_row: 0, 2, 1, 3 (the row swap's order; its own inverse).
+__device__ __forceinline__ int fold_row(int rho) { return ((rho & 1) << 1) | (rho >> 1); }
+__device__ __forceinline__ int fold_lane(bool value, int i) { return 16 * fold_row(i & 3) + 8 * (i >> 2) + 4 * value; }
+__device__ __forceinline__ uint32_t chunk_row_maxima(const uint32_t (&kp)[8], const uint32_t (&vp)[8]) {
+  uint32_t bk[2], bv[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    bk[j] = fold16(fold32(kp[4 * j], kp[4 * j + 1]), fold32(kp[4 * j + 2], kp[4 * j + 3]));
+    bv[j] = fold16(fold32(vp[4 * j], vp[4 * j + 1]), fold32(vp[4 * j + 2], vp[4 * j + 3]));
+  }
+  // rows of bk[j] / bv[j]: pairs 4j + (0, 2, 1, 3), each still over 16 lanes
+  const uint32_t ck = fold_banks<0x140, 0x3>(bk[0], bk[1]);    // row_mirror: lanes 0-7 bk[0], 8-15 bk[1]
+  const uint32_t cv = fold_banks<0x140, 0x3>(bv[0], bv[1]);
+  uint32_t d = fold_banks<0x141, 0x5>(ck, cv);                 // row_half_mirror: banks 0, 2 keys, 1, 3 values
+  d = pk_max_u16(d, (uint32_t)__builtin_amdgcn_mov_dpp((int)d, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  return pk_max_u16(d, (uint32_t)__builtin_amdgcn_mov_dpp((int)d, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+}
+
+// A row's scale RN(amax / 448) and the reciprocal bracket used to code its
 // elements: x lo and x hi lie below and above the correctly rounded quotient
 // x / s (the reciprocal is within 1 ulp; the bracket is 2^-20 either side of
-// it, the products' rounding adds 2^-24 each), scales from 2^-100 up.
-struct RowScale {
-  float s, lo, hi;
-  bool divide;                      // scales below 2^-100 (and 0): the division codes every element
-};
-__device__ __forceinline__ RowScale row_scale_of(uint32_t amax_bf16) {
-  const float s = row_scale(__uint_as_float(amax_bf16 << 16));
+// it, the products' rounding adds 2^-24 each), scales from 2^-100 up. Rows
+// with smaller scales (and rows of zeros, scale 0) get lo = -1: every element
+// of theirs is coded by the division.
+__device__ __forceinline__ void row_bracket(uint32_t amax_bf16, float& s, float& lo, float& hi) {
+  s = row_scale(__uint_as_float(amax_bf16 << 16));
   const float r = __builtin_amdgcn_rcpf(s);
-  return RowScale{s, r * (1.f - 0x1p-20f), r * (1.f + 0x1p-20f), !(s >= 0x1p-100f)};
+  lo = s >= 0x1p-100f ? r * (1.f - 0x1p-20f) : -1.f;
+  hi = r * (1.f + 0x1p-20f);
 }
-// Codes of the bf16 pair w (bits 0-7: the low channel) in a row of scale rs:
-// rounding to E4M3 is monotone, so when x lo and x hi take the same code the
-// correctly rounded quotient between them takes it too; otherwise (within
-// 2^-20 of a rounding boundary: rare) the division decides. A row of zeros
-// codes to 0. Equal to e4m3_code(x / s) for every bf16 row maximum and every
-// bf16 x up to it (checked over all pairs).
-__device__ __forceinline__ uint32_t codes_in_row(uint32_t w, const RowScale& rs) {
+// Codes of the bf16 pair w (bits 0-7: the low channel) in a row with bracket
+// lo / hi (row_bracket; wave-uniform values) whose scale is s_lanes in lane
+// `src`: rounding to E4M3 is monotone, so when x lo and x hi take the same
+// code the correctly rounded quotient between them takes it too; otherwise
+// (within 2^-20 of a rounding boundary: rare), and in rows with lo < 0, the
+// division decides. A row of zeros codes to 0. Equal to e4m3_code(x / s)
+// for every bf16 row maximum and every bf16 x up to it (checked over all
+// pairs).
+__device__ __forceinline__ uint32_t codes_bracketed(uint32_t w, float lo, float hi, float s_lanes, int src) {
   const float x0 = __uint_as_float(w << 16), x1 = __uint_as_float(w & 0xFFFF0000u);
-  const uint32_t a = e4m3_code2(x0 * rs.lo, x1 * rs.lo), b = e4m3_code2(x0 * rs.hi, x1 * rs.hi);
+  const uint32_t a = e4m3_code2(x0 * lo, x1 * lo), b = e4m3_code2(x0 * hi, x1 * hi);
   uint32_t c = a;
-  if ((a != b) | rs.divide) c = e4m3_code2(x0 / rs.s, x1 / rs.s);
-  return rs.s == 0.f ? 0u : c;
+  if ((a != b) | (__float_as_int(lo) < 0)) {
+    const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s_lanes), src));
+    c = s == 0.f ? 0u : e4m3_code2(x0 / s, x1 / s);
+  }
+  return c;
+}
+// A wave-uniform copy of lane `src`'s value.
+__device__ __forceinline__ float lane_value(float x, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), src));
 }
 
 // Running channel-wise min / max of the dequantized keys of the lane's two

@@ -4,12 +4,15 @@
 //   1. e4m3_code2 (the hardware conversion) vs e4m3_code (from the fp32 bit
 //      pattern), every fp32 value of magnitude <= 464, both signs, both bytes;
 //   2. for every bf16 row maximum a and every bf16 x with |x| <= a, both signs:
-//      row_scale_of(a) vs the IEEE division a / 448, codes_in_row (reciprocal
-//      bracket) and quantize_pair (whole-wave row) vs e4m3_code(x / s);
+//      row_bracket(a)'s scale vs the IEEE division a / 448, codes_bracketed
+//      (reciprocal bracket) and quantize_pair (whole-wave row) vs
+//      e4m3_code(x / s);
 //   3. product_keys + bf16_below_key / bf16_above_key vs bf16_down / bf16_up of
 //      the fp64 product, every code and every such scale; e4m3_value2 vs
 //      e4m3_value, every code;
-//   4. wave_max_u32, pair_max_u16 + wave_max_u16x2 vs serial maxima on seeded rows.
+//   4. wave_max_u32, and pair_max_u16 + chunk_row_maxima (the reduce-scatter of
+//      16 key and 16 value rows, with its lane map fold_lane) vs serial maxima
+//      on seeded rows.
 // Prints one line per check with its mismatch count; exit status 0 when all are 0.
 #include <hip/hip_runtime.h>
 #include <cstdio>
@@ -40,16 +43,18 @@ __global__ void __launch_bounds__(256) check_rows(unsigned long long* cnt, uint3
   const uint32_t abits = blockIdx.x;
   const float a = __uint_as_float(abits << 16);
   const float s = a / 448.f;
-  const RowScale rs = row_scale_of(abits);
-  if (threadIdx.x == 0 && __float_as_uint(rs.s) != __float_as_uint(s)) report(cnt, first, 1, abits, __float_as_uint(rs.s), __float_as_uint(s));
+  float rs, lo, hi;                                 // the same in every lane (one maximum per block)
+  row_bracket(abits, rs, lo, hi);
+  if (threadIdx.x == 0 && __float_as_uint(rs) != __float_as_uint(s)) report(cnt, first, 1, abits, __float_as_uint(rs), __float_as_uint(s));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t n = abits + 1;                     // x patterns 0 .. abits
-  // codes_in_row: any thread, any x
-  for (uint32_t xb = threadIdx.x; xb < n; xb += blockDim.x) {
+  // codes_bracketed: any thread, any x (the scale read from lane 0)
+  for (uint32_t xb0 = wave * 64; xb0 < n; xb0 += blockDim.x) {
+    const uint32_t xb = min(xb0 + (uint32_t)lane, abits);
     const uint32_t w = (xb << 16) | (xb | 0x8000u);  // channel 0: -x, channel 1: +x
     const float x = __uint_as_float(xb << 16);
     const uint32_t want = s == 0.f ? 0u : (e4m3_code(-x / s) | (e4m3_code(x / s) << 8));
-    const uint32_t got = codes_in_row(w, rs);
+    const uint32_t got = codes_bracketed(w, lane_value(lo, 0), lane_value(hi, 0), rs, 0);
     if (got != want) report(cnt, first, 2, abits, xb, got);
   }
   // quantize_pair: whole waves; lane 0 carries the maximum, lanes 1-63 the x values
@@ -84,22 +89,40 @@ __global__ void __launch_bounds__(64) check_maxima(unsigned long long* cnt, uint
   uint32_t st = blockIdx.x * 2654435761u + threadIdx.x * 40503u + 12345u;
   st ^= st << 13; st ^= st >> 17; st ^= st << 5;
   const uint32_t w0 = st >> (blockIdx.x & 7);
-  st ^= st << 13; st ^= st >> 17; st ^= st << 5;
-  const uint32_t w1 = st >> (blockIdx.x & 15);
   const uint32_t m32 = wave_max_u32(w0);
-  const uint32_t m16 = wave_max_u16x2(pair_max_u16(w0, w1));
-  __shared__ uint32_t sh[128];
-  sh[threadIdx.x] = w0;
-  sh[64 + threadIdx.x] = w1;
-  __syncthreads();
-  uint32_t r = 0, r0 = 0, r1 = 0;
-  for (int i = 0; i < 64; ++i) {
-    r = max(r, sh[i]);
-    r0 = max(r0, max(sh[i] & 0x7FFFu, (sh[i] >> 16) & 0x7FFFu));
-    r1 = max(r1, max(sh[64 + i] & 0x7FFFu, (sh[64 + i] >> 16) & 0x7FFFu));
+  // 16 key rows and 16 value rows of seeded bf16 pairs, magnitudes of a
+  // different range in each row
+  uint32_t rows[32];
+  for (int u = 0; u < 32; ++u) {
+    st ^= st << 13; st ^= st >> 17; st ^= st << 5;
+    rows[u] = st >> ((u * 7 + blockIdx.x) & 15);
   }
+  uint32_t kp[8], vp[8];
+  for (int i = 0; i < 8; ++i) {
+    kp[i] = pair_max_u16(rows[2 * i], rows[2 * i + 1]);
+    vp[i] = pair_max_u16(rows[16 + 2 * i], rows[16 + 2 * i + 1]);
+  }
+  const uint32_t m = chunk_row_maxima(kp, vp);
+  __shared__ uint32_t sh[33][64];
+  sh[0][threadIdx.x] = w0;
+  for (int u = 0; u < 32; ++u) sh[1 + u][threadIdx.x] = rows[u];
+  __syncthreads();
+  uint32_t r = 0;
+  for (int i = 0; i < 64; ++i) r = max(r, sh[0][i]);
   if (m32 != r) report(cnt, first, 7, blockIdx.x, threadIdx.x, m32);
-  if (m16 != (r0 | (r1 << 16))) report(cnt, first, 8, blockIdx.x, threadIdx.x, m16);
+  // the pair this lane holds, and the lane the kernel reads it from
+  const int lane = threadIdx.x, rho = lane >> 4, beta = (lane >> 2) & 3;
+  const int tau = beta & 1, i = 4 * (beta >> 1) + fold_row(rho);
+  uint32_t want = 0;
+  for (int hh = 0; hh < 2; ++hh) {
+    uint32_t mx = 0;
+    for (int l = 0; l < 64; ++l) {
+      const uint32_t x = sh[1 + 16 * tau + 2 * i + hh][l];
+      mx = max(mx, max(x & 0x7FFFu, (x >> 16) & 0x7FFFu));
+    }
+    want |= mx << (16 * hh);
+  }
+  if (m != want || fold_lane(tau != 0, i) != (lane & ~3)) report(cnt, first, 8, blockIdx.x, threadIdx.x, m);
 }
 
 int main() {
@@ -124,14 +147,14 @@ int main() {
   if (hipMemcpy(f, first, sizeof f, hipMemcpyDeviceToHost) != hipSuccess) return 2;
   const char* names[kChecks] = {
       "hardware E4M3 conversion vs e4m3_code, all fp32 |y| <= 464",
-      "row_scale_of vs a / 448, all bf16 a",
-      "codes_in_row vs e4m3_code(x / s), all bf16 pairs",
+      "row_bracket's scale vs a / 448, all bf16 a",
+      "codes_bracketed vs e4m3_code(x / s), all bf16 pairs",
       "quantize_pair vs e4m3_code(x / s), all bf16 pairs",
       "e4m3_value2 vs e4m3_value, all codes",
       "bf16 below the product vs fp64, all codes x scales",
       "bf16 above the product vs fp64, all codes x scales",
       "wave_max_u32, seeded rows",
-      "pair_max_u16 + wave_max_u16x2, seeded rows"};
+      "pair_max_u16 + chunk_row_maxima and its lane map, seeded rows"};
   int bad = 0;
   for (int w = 0; w < kChecks; ++w) {
     printf("%s: %llu mismatches\n", names[w], h[w]);

@@ -185,3 +185,55 @@ def test_fp8_degenerate_rows_bit_exact():
             j = np.arange(count // p)
             assert np.array_equal(summ[(j * p) // P, h, ((j * p) % P) // p, 0], kmin), "summary min"
             assert np.array_equal(summ[(j * p) // P, h, ((j * p) % P) // p, 1], kmax), "summary max"
+
+
+@pytest.mark.parametrize("p,P", [(16, 64), (32, 256), (64, 128)])
+def test_fp8_bulk_write_in_chunks_bit_exact(p, P):
+    """spa_kv_pool_write into fp8 pages in chunks whose edges fall inside
+    logical pages (and inside the 16-row groups the kernel quantizes together):
+    every code and scale equals the oracle's quantization of the whole rows,
+    and each dynamic head's summaries, built across the chunks (tokens before
+    a chunk's start read back from the pool), equal the oracle's outward-rounded
+    min / max of the dequantized keys."""
+    from parity import bits_to_bf16
+    from sparse_paged_attention_amd.runner import DecodeLayer
+    wl = W.WORKLOADS["toy_4k"].scaled(contexts=(300, 77, 1, 2 * P + 3), batch=4, steps=1, permute=True,
+                                      p=p, P=P, hkv=4, hq=8, kind=(1, 0, 1, 0), planted=None,
+                                      name="fp8_bulk_write_chunks")
+    log(f"[fp8 parity] chunked write p={p} P={P} contexts={wl.contexts}")
+    pt = W.page_table(wl)
+    layer = DecodeLayer(hq=wl.hq, hkv=wl.hkv, p=p, P=P, kind=wl.kind, sink=wl.sink, window=wl.window,
+                        page_table=pt, num_phys_pages=wl.num_phys_pages, k_max=wl.k_max, kv_format="fp8")
+    src = []
+    for b in range(wl.batch):
+        L = wl.contexts[b]
+        K = np.stack([W.kv(wl, b, h, "k")[:L] for h in range(wl.hkv)])
+        V = np.stack([W.kv(wl, b, h, "v")[:L] for h in range(wl.hkv)])
+        src.append((K, V))
+        edges = sorted({0, L, *[e for e in (5, 37, 38, 38 + p, 2 * P + 1) if e < L]})
+        for a, e in zip(edges[:-1], edges[1:]):
+            layer.write_tokens(b, a, bits_to_bf16(np.ascontiguousarray(K[:, a:e])).cuda(),
+                               bits_to_bf16(np.ascontiguousarray(V[:, a:e])).cuda())
+    torch.cuda.synchronize()
+    pool = layer.pool
+    k, v = pool.k.cpu().numpy(), pool.v.cpu().numpy()
+    ks, vs = pool.k_scale.cpu().numpy(), pool.v_scale.cpu().numpy()
+    summ = pool.summary.view(torch.int16).cpu().numpy().view(np.uint16)
+    r = P // p
+    for b in range(wl.batch):
+        K, V = src[b]
+        L = wl.contexts[b]
+        t = np.arange(L)
+        phys, slot = pt[b, t // P], t % P
+        for h in range(wl.hkv):
+            Kc, Ks = oracle.quantize_rows(K[h])
+            Vc, Vs = oracle.quantize_rows(V[h])
+            assert np.array_equal(k[phys, h, slot], Kc), (b, h, "key codes")
+            assert np.array_equal(ks[phys, h, slot].view(np.uint32), Ks[:L].view(np.uint32)), (b, h, "key scales")
+            assert np.array_equal(v[phys, h, slot // p, :, slot % p], Vc), (b, h, "value codes")
+            assert np.array_equal(vs[phys, h, slot].view(np.uint32), Vs[:L].view(np.uint32)), (b, h, "value scales")
+            if wl.kind[h]:
+                kmin, kmax = oracle.page_summary_q8(Kc, Ks[:L], p)
+                j = np.arange(kmin.shape[0])
+                assert np.array_equal(summ[pt[b, j // r], h, j % r, 0], kmin), (b, h, "summary min")
+                assert np.array_equal(summ[pt[b, j // r], h, j % r, 1], kmax), (b, h, "summary max")

@@ -81,7 +81,11 @@ struct ScoreShape {
   static constexpr int R = LPP / V;                 // lanes holding each total
   static constexpr int GPW = 64 / LPP;              // groups per wave
   static constexpr int PASS = GPW * NP;             // pages per pass
-  static constexpr int PASSES = 8;
+  // passes per wave: for G <= 4 (three waves per SIMD) 6, so that a 128K
+  // row's ranges (2736 waves for 16 heads) are still all resident at once and
+  // each wave's chain of dependent load rounds is shorter (20.3 against 21.2
+  // us for 8 passes at the 128K benchmark shape; 7 passes: 21.0 us)
+  static constexpr int PASSES = G <= 4 ? 6 : 8;
   static constexpr int RING = 2;                    // passes in flight
   static constexpr int RANGE = PASS * PASSES;       // pages per wave
   // the last range of a head takes up to one pass more, so that a length just

@@ -81,17 +81,20 @@ struct ScoreShape {
   static constexpr int R = LPP / V;                 // lanes holding each total
   static constexpr int GPW = 64 / LPP;              // groups per wave
   static constexpr int PASS = GPW * NP;             // pages per pass
-  // passes per wave: for G <= 4 (three waves per SIMD) 6, so that a 128K
-  // row's ranges (2736 waves for 16 heads) are still all resident at once and
-  // each wave's chain of dependent load rounds is shorter (20.3 against 21.2
-  // us for 8 passes at the 128K benchmark shape; 7 passes: 21.0 us)
+  // most passes per wave: for G <= 4 (three waves per SIMD) 6, so that a
+  // 128K row's ranges (2736 waves for 16 heads) are still all resident at
+  // once and each wave's chain of dependent load rounds is shorter (20.3
+  // against 21.2 us for 8 passes at the 128K benchmark shape; 7 passes: 21.0
+  // us). Launches with fewer pages take fewer passes per wave (score_passes).
   static constexpr int PASSES = G <= 4 ? 6 : 8;
   static constexpr int RING = 2;                    // passes in flight
-  static constexpr int RANGE = PASS * PASSES;       // pages per wave
+  // waves a launch can keep resident with room to spare (three per SIMD for
+  // G <= 4, one or two above)
+  static constexpr int WAVES = G <= 4 ? 2048 : 1024;
   // the last range of a head takes up to one pass more, so that a length just
-  // past a multiple of RANGE needs no extra wave (which would wait for a free
-  // slot until every other wave of the launch has finished); not for G > 4,
-  // whose registers the extra pass would push past two waves per SIMD
+  // past a multiple of the range needs no extra wave (which would wait for a
+  // free slot until every other wave of the launch has finished); not for
+  // G > 4, whose registers the extra pass would push past two waves per SIMD
   static constexpr int XPASS = G <= 4 ? 1 : 0;
   static constexpr int MAXP = PASSES + XPASS;
   static constexpr int OFFS = PASS * MAXP;          // pages of the longest range
@@ -198,7 +201,7 @@ template <int G, bool FRESH>
 __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, HeadList dyn,
                                                    const uint16_t* __restrict__ q,
                                                    float* __restrict__ scores, int32_t n_max,
-                                                   const uint32_t* __restrict__ k_new,
+                                                   int32_t passes, const uint32_t* __restrict__ k_new,
                                                    const uint16_t* __restrict__ v_new) {
   using S = ScoreShape<G>;
   if (FRESH && (int32_t)blockIdx.y >= bt.B * dyn.n) {
@@ -221,7 +224,7 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
   const int32_t hsl = head_slot(pl, h, blockIdx.y % dyn.n, true);   // (the list is in ascending head order)
   const int32_t L = clamp_len(bt, b, pl.P);
   const int32_t n = (L + pl.p - 1) / pl.p;
-  const int32_t base = blockIdx.x * S::RANGE;
+  const int32_t base = blockIdx.x * passes * S::PASS;    // a range of `passes` passes
   if (base >= n) return;
 
   const int lane = threadIdx.x & 63;
@@ -358,7 +361,7 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
   // at run time; deeper rings measured slower)
   // Passes past the head's last page are skipped (wave-uniform): the last
   // range of a head is often nearly empty.
-  const int32_t cap = blockIdx.x + 1 == gridDim.x ? S::MAXP : S::PASSES;
+  const int32_t cap = blockIdx.x + 1 == gridDim.x ? passes + S::XPASS : passes;
   const int32_t live = min(cap, (n - base + S::PASS - 1) / S::PASS);
   Pass ring[S::RING];
 #pragma unroll
@@ -370,7 +373,8 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
     compute(it, ring[it % S::RING]);
     if (it + S::RING < live) issue(it + S::RING, ring[it % S::RING]);
   }
-  // the extra pass of a head's last range (issued by the loop above)
+  // the extra pass of a head's last range when it follows S::PASSES passes
+  // (issued by the loop above; after fewer passes the loop computes it)
   if constexpr (S::XPASS > 0)
     if (live > S::PASSES) compute(S::PASSES, ring[S::PASSES % S::RING]);
 }
@@ -662,15 +666,22 @@ hipError_t launch_score_g(const PoolArgs& pool, const BatchArgs& batch, const He
                           const uint16_t* q, float* scores, int32_t n_max, const uint16_t* k_new,
                           const uint16_t* v_new, hipStream_t s) {
   using S = ScoreShape<G>;
-  // ranges of RANGE pages; the last one also takes up to PASS more
-  const int32_t ranges = std::max(1, (n_max - S::XPASS * S::PASS + S::RANGE - 1) / S::RANGE);
+  // passes per wave: S::PASSES when the rows fill the GPU, fewer when there
+  // are few pages in all (small batches), so that about S::WAVES waves share
+  // them and each wave's chain of dependent load rounds is short
+  const int64_t pages = (int64_t)batch.B * dyn.n * n_max;
+  const int64_t per = (int64_t)S::WAVES * S::PASS;
+  const int32_t passes = (int32_t)std::min<int64_t>(S::PASSES, std::max<int64_t>(1, (pages + per - 1) / per));
+  // ranges of passes * PASS pages; the last one also takes up to PASS more
+  const int32_t range = passes * S::PASS;
+  const int32_t ranges = std::max(1, (n_max - S::XPASS * S::PASS + range - 1) / range);
   if (k_new) {          // extra rows for the append waves
     const int32_t rows = (batch.B * pool.hkv + ranges - 1) / ranges;
     hipLaunchKernelGGL((score_kernel<G, true>), dim3(ranges, batch.B * dyn.n + rows), dim3(64), 0, s, pool, batch,
-                       dyn, q, scores, n_max, reinterpret_cast<const uint32_t*>(k_new), v_new);
+                       dyn, q, scores, n_max, passes, reinterpret_cast<const uint32_t*>(k_new), v_new);
   } else {
     hipLaunchKernelGGL((score_kernel<G, false>), dim3(ranges, batch.B * dyn.n), dim3(64), 0, s, pool, batch, dyn,
-                       q, scores, n_max, nullptr, nullptr);
+                       q, scores, n_max, passes, nullptr, nullptr);
   }
   return hipGetLastError();
 }

@@ -43,7 +43,11 @@ spa_status hip_status(hipError_t e, const char* what) {
 // Attention blocks per work item (16 tokens each). All work-groups of a
 // launch are resident at once and the dispatcher spreads them evenly over
 // the compute units, so the launch lasts as long as the busiest unit: the
-// item size is picked to minimise ceil(items / CUs) * blocks per item.
+// item size is picked to minimise max(ceil(items / CUs), 2) * blocks per
+// item. The floor of 2: one wave's own chain of dependent tile loads lasts
+// about as long as two items' share of a unit's bandwidth, so below two
+// items per unit shorter items win (256K single sequence: 9 blocks, one item
+// per unit, 14.8 us per call; 5 or 6 blocks, two per unit, 12.7-13.0 us).
 // spa_set_attn_blocks_per_item() or the SPA_ATTN_BLOCKS_PER_ITEM environment
 // variable (one of kBpiChoices) fixes it instead.
 constexpr int32_t kBpiChoices[] = {4, 5, 6, 7, 8, 9, 10, 12, 16};
@@ -248,7 +252,7 @@ void plan_attention(const spa::PoolArgs& pl, const spa_heads* heads, int32_t k_m
       size_items(pl, heads, k_max, c, &t);
       const int64_t items = (int64_t)std::max(batch, 1) * (n_str * (int64_t)t.items_stream +
                                                            n_dyn * (int64_t)(t.items_dyn - 1));
-      const int64_t cost = (items + cus - 1) / cus * c;
+      const int64_t cost = std::max<int64_t>((items + cus - 1) / cus, 2) * c;
       if (best < 0 || cost <= best) {      // ties go to the larger item
         best = cost;
         bpi = c;

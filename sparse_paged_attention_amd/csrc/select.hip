@@ -428,6 +428,8 @@ __device__ __forceinline__ int32_t group8_sum(int32_t v) {
 }
 
 // Exclusive prefix over the block (thread order) of one value per thread.
+// The caller puts a barrier between this call's reads of sh_wave and the next
+// call (the pick that follows each use does).
 __device__ int32_t block_exclusive_scan(int32_t x, int32_t* sh_wave, int32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int32_t incl = x;
@@ -436,7 +438,13 @@ __device__ int32_t block_exclusive_scan(int32_t x, int32_t* sh_wave, int32_t& to
     const int32_t y = __shfl_up(incl, d, 64);
     if (lane >= d) incl += y;
   }
-  if (lane == 63) sh_wave[wave] = incl;
+  if (lane == 63) {
+    // the slot's address formed here: left to itself the compiler computes it
+    // before the rounds and, with 16 scores per thread, parks it in scratch
+    int32_t w = wave;
+    asm volatile("" : "+v"(w));
+    sh_wave[w] = incl;
+  }
   __syncthreads();
   int32_t before = 0, all = 0;
 #pragma unroll
@@ -445,16 +453,18 @@ __device__ int32_t block_exclusive_scan(int32_t x, int32_t* sh_wave, int32_t& to
     before += w < wave ? t : 0;
     all += t;
   }
-  __syncthreads();
   total = all;
   return incl - x + before;
 }
 
 // For a per-thread element mask: the position of every set element among all
 // set elements in page-id order (ids e * kTopkThreads + thread); returns the
-// number of set elements.
+// number of set elements. The E * waves per-(element, wave) counts are
+// scanned by wave 0 alone (a few per lane), between two barriers; `again`:
+// the block calls it once more later (block-uniform).
 template <int E>
-__device__ int32_t id_order_ranks(uint32_t mask, int32_t (&rank)[E], int32_t* table, int32_t* sh_wave) {
+__device__ int32_t id_order_ranks(uint32_t mask, int32_t (&rank)[E], int32_t* table, int32_t* sh_total,
+                                  bool again) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -462,11 +472,32 @@ __device__ int32_t id_order_ranks(uint32_t mask, int32_t (&rank)[E], int32_t* ta
     if (lane == 0) table[e * kTopkWaves + wave] = __popcll(ball);
   }
   __syncthreads();
-  static_assert(E * kTopkWaves <= kTopkThreads, "one table entry per thread");
-  const int32_t x = tid < E * kTopkWaves ? table[tid] : 0;
-  int32_t total;
-  const int32_t excl = block_exclusive_scan(x, sh_wave, total);
-  if (tid < E * kTopkWaves) table[tid] = excl;
+  constexpr int N = E * kTopkWaves, PL = (N + 63) / 64;   // entries, entries per lane of wave 0
+  if (wave == 0) {
+    int32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int idx = lane * PL + i;
+      sum += idx < N ? table[idx] : 0;
+    }
+    int32_t incl = sum;
+#pragma unroll
+    for (int d = 1; d < 64; d *= 2) {
+      const int32_t y = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += y;
+    }
+    int32_t run = incl - sum;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {                  // (the lane's entries read again: fewer live registers)
+      const int idx = lane * PL + i;
+      if (idx < N) {
+        const int32_t c = table[idx];
+        table[idx] = run;
+        run += c;
+      }
+    }
+    if (lane == 63) *sh_total = incl;
+  }
   __syncthreads();
   const uint64_t below = (1ull << lane) - 1;
 #pragma unroll
@@ -474,7 +505,8 @@ __device__ int32_t id_order_ranks(uint32_t mask, int32_t (&rank)[E], int32_t* ta
     const uint64_t ball = __ballot((mask >> e) & 1);
     rank[e] = table[e * kTopkWaves + wave] + __popcll(ball & below);
   }
-  __syncthreads();
+  const int32_t total = *sh_total;
+  if (again) __syncthreads();                       // table and sh_total free for the next call
   return total;
 }
 
@@ -494,7 +526,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
   __shared__ uint32_t sh_min[kTopkWaves], sh_max[kTopkWaves];
   __shared__ int32_t sh_cnt[kTopkWaves];
   __shared__ int32_t sh_pick[3];
-  __shared__ int32_t sh_nc;
+  __shared__ int32_t sh_nc, sh_total;
   __shared__ uint64_t cand_key[kMaxCand];
   __shared__ uint32_t sel_bits[kTopkThreads];
   __shared__ int32_t table[E * kTopkWaves];
@@ -582,7 +614,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
     }
     if (lo == hi) {
       // more than kMaxCand candidates share one key: keep the `need` lowest page ids
-      id_order_ranks<E>(cand, rank, table, sh_wave);
+      id_order_ranks<E>(cand, rank, table, &sh_total, true);
 #pragma unroll
       for (int e = 0; e < E; ++e)
         if ((cand >> e & 1) && rank[e] < need) sel |= 1u << e;
@@ -636,7 +668,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
   }
 
   // kept ids in ascending order
-  const int32_t total = id_order_ranks<E>(sel, rank, table, sh_wave);
+  const int32_t total = id_order_ranks<E>(sel, rank, table, &sh_total, false);
   int32_t* out = sel_pages + ((int64_t)b * hkv + h) * k_max;
 #pragma unroll
   for (int e = 0; e < E; ++e)

@@ -62,8 +62,8 @@ extern "C" {
 typedef enum spa_status {
   SPA_OK = 0,
   SPA_ERR_INVALID = 1,        /* bad argument: null pointer, size out of range, shapes that disagree */
-  SPA_ERR_UNSUPPORTED = 2,    /* well-formed but not built: head_dim != 128, p not 16/32/64, G not
-                                 1/2/4/8/16, a selection over more than 32768 logical pages per
+  SPA_ERR_UNSUPPORTED = 2,    /* well-formed but not built: head_dim != 128, p not 16/32/64, G above
+                                 16, a selection over more than 32768 logical pages per
                                  sequence (max_pages * P / p > 32768), 2^32 or more summary records */
   SPA_ERR_POOL_EXHAUSTED = 3, /* page allocator has fewer free pages than requested */
   SPA_ERR_WORKSPACE = 4,      /* workspace missing or smaller than spa_workspace_bytes() */
@@ -118,7 +118,7 @@ typedef struct spa_pool {
 /* Which KV heads are streaming and which are dynamic, and the streaming
  * pattern. The `kind` array is read on the host during the call only. */
 typedef struct spa_heads {
-  int32_t num_q_heads;    /* H_q: a multiple of H_kv with G = H_q / H_kv in {1, 2, 4, 8, 16} */
+  int32_t num_q_heads;    /* H_q: a multiple of H_kv with G = H_q / H_kv from 1 to 16 */
   int32_t sink;           /* streaming heads attend tokens [0, min(sink, L)), sink >= 0 */
   int32_t window;         /* ... and tokens [max(sink, L - window), L), window >= 1 */
   const uint8_t* kind;    /* host [H_kv]: 0 = streaming head, 1 = dynamic head */

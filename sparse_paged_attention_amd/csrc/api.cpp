@@ -136,8 +136,7 @@ spa_status check_heads(const spa_heads* heads, const spa::PoolArgs& pl, int32_t*
     return fail(SPA_ERR_INVALID, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
                 heads->num_q_heads, pl.hkv);
   const int32_t g = heads->num_q_heads / pl.hkv;
-  if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16)
-    return fail(SPA_ERR_UNSUPPORTED, "query group size %d: only 1, 2, 4, 8, 16 are built", g);
+  if (g > 16) return fail(SPA_ERR_UNSUPPORTED, "query group size %d: groups of up to 16 are built", g);
   if (heads->sink < 0) return fail(SPA_ERR_INVALID, "sink %d < 0", heads->sink);
   if (heads->window < 1) return fail(SPA_ERR_INVALID, "window %d < 1", heads->window);
   if (!heads->kind) return fail(SPA_ERR_INVALID, "heads->kind is NULL");

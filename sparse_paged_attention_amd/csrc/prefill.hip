@@ -468,7 +468,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     else hipLaunchKernelGGL(select_kernel<128>, grid, dim3(64), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const int nh = a.G < 4 ? a.G : 4;
+  // query heads per work-group: the largest of 4, 2, 1 that divides G
+  const int nh = a.G % 4 == 0 ? 4 : a.G % 2 == 0 ? 2 : 1;
   const dim3 grid(a.nb, a.hkv, a.G / nh);
   switch (nh) {
     case 1: hipLaunchKernelGGL(attn_kernel<1>, grid, dim3(128), 0, s, a); break;

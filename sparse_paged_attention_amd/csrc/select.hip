@@ -201,8 +201,12 @@ template <int G, bool FRESH>
 __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, HeadList dyn,
                                                    const uint16_t* __restrict__ q,
                                                    float* __restrict__ scores, int32_t n_max,
-                                                   int32_t passes, const uint32_t* __restrict__ k_new,
+                                                   int32_t passes, int32_t gq,
+                                                   const uint32_t* __restrict__ k_new,
                                                    const uint16_t* __restrict__ v_new) {
+  // G: the group size the kernel is built for; gq <= G the heads of the
+  // caller's group (query columns g >= gq repeat query gq - 1: a page's score
+  // is the maximum over the group, which a repeated query leaves unchanged)
   using S = ScoreShape<G>;
   if (FRESH && (int32_t)blockIdx.y >= bt.B * dyn.n) {
     const int32_t w = ((int32_t)blockIdx.y - bt.B * dyn.n) * (int32_t)gridDim.x + (int32_t)blockIdx.x;
@@ -247,11 +251,11 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
 
   // q+ and q- of this lane's channels, fp64 (exact for bf16)
   double qp[G][S::CPL], qn[G][S::CPL];
-  const int32_t hq = pl.hkv * G;
+  const int32_t hq = pl.hkv * gq;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     Raw<S::CPL> rq;
-    load_raw<S::CPL>(q + ((int64_t)b * hq + h * G + g) * kHeadDim + c0, rq);
+    load_raw<S::CPL>(q + ((int64_t)b * hq + h * gq + min(g, gq - 1)) * kHeadDim + c0, rq);
     double qv[S::CPL];
     widen<S::CPL>(rq, qv);
 #pragma unroll
@@ -694,7 +698,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(BatchArgs bt, int32_
 }
 
 template <int G>
-hipError_t launch_score_g(const PoolArgs& pool, const BatchArgs& batch, const HeadList& dyn,
+hipError_t launch_score_g(const PoolArgs& pool, const BatchArgs& batch, const HeadList& dyn, int32_t gq,
                           const uint16_t* q, float* scores, int32_t n_max, const uint16_t* k_new,
                           const uint16_t* v_new, hipStream_t s) {
   using S = ScoreShape<G>;
@@ -710,10 +714,10 @@ hipError_t launch_score_g(const PoolArgs& pool, const BatchArgs& batch, const He
   if (k_new) {          // extra rows for the append waves
     const int32_t rows = (batch.B * pool.hkv + ranges - 1) / ranges;
     hipLaunchKernelGGL((score_kernel<G, true>), dim3(ranges, batch.B * dyn.n + rows), dim3(64), 0, s, pool, batch,
-                       dyn, q, scores, n_max, passes, reinterpret_cast<const uint32_t*>(k_new), v_new);
+                       dyn, q, scores, n_max, passes, gq, reinterpret_cast<const uint32_t*>(k_new), v_new);
   } else {
     hipLaunchKernelGGL((score_kernel<G, false>), dim3(ranges, batch.B * dyn.n), dim3(64), 0, s, pool, batch, dyn,
-                       q, scores, n_max, passes, nullptr, nullptr);
+                       q, scores, n_max, passes, gq, nullptr, nullptr);
   }
   return hipGetLastError();
 }
@@ -728,17 +732,19 @@ hipError_t launch_select(const PoolArgs& pool, const BatchArgs& batch, const Hea
   if (batch.B == 0) return hipSuccess;
   if (dyn.n == 0) return k_new ? launch_append(pool, batch, k_new, v_new, nullptr, s) : hipSuccess;
   hipError_t e;
-  if (k_new && G >= 8) {      // no room in those scoring kernels' registers: append first
+  // the scoring kernel built for the next power of two holds the group
+  const int32_t gk = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16;
+  if (G > 16) return hipErrorInvalidValue;
+  if (k_new && gk >= 8) {     // no room in those scoring kernels' registers: append first
     if ((e = launch_append(pool, batch, k_new, v_new, &dyn, s)) != hipSuccess) return e;
     k_new = v_new = nullptr;
   }
-  switch (G) {
-    case 1: e = launch_score_g<1>(pool, batch, dyn, q, scores, n_max, k_new, v_new, s); break;
-    case 2: e = launch_score_g<2>(pool, batch, dyn, q, scores, n_max, k_new, v_new, s); break;
-    case 4: e = launch_score_g<4>(pool, batch, dyn, q, scores, n_max, k_new, v_new, s); break;
-    case 8: e = launch_score_g<8>(pool, batch, dyn, q, scores, n_max, k_new, v_new, s); break;
-    case 16: e = launch_score_g<16>(pool, batch, dyn, q, scores, n_max, k_new, v_new, s); break;
-    default: return hipErrorInvalidValue;
+  switch (gk) {
+    case 1: e = launch_score_g<1>(pool, batch, dyn, G, q, scores, n_max, k_new, v_new, s); break;
+    case 2: e = launch_score_g<2>(pool, batch, dyn, G, q, scores, n_max, k_new, v_new, s); break;
+    case 4: e = launch_score_g<4>(pool, batch, dyn, G, q, scores, n_max, k_new, v_new, s); break;
+    case 8: e = launch_score_g<8>(pool, batch, dyn, G, q, scores, n_max, k_new, v_new, s); break;
+    default: e = launch_score_g<16>(pool, batch, dyn, G, q, scores, n_max, k_new, v_new, s); break;
   }
   if (e != hipSuccess) return e;
 #define SPA_TOPK(E)                                                                                     \

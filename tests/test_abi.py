@@ -120,7 +120,7 @@ def test_pool_validation(spa, bad, status):
 
 
 @pytest.mark.parametrize("bad,status", [
-    (dict(hq=20), 1), (dict(hq=8 * 3), 2), (dict(hq=8 * 32), 2), (dict(hq=0), 1), (dict(sink=-1), 1),
+    (dict(hq=20), 1), (dict(hq=8 * 17), 2), (dict(hq=8 * 32), 2), (dict(hq=0), 1), (dict(sink=-1), 1),
     (dict(window=0), 1), (dict(kind=(0, 0, 0, 0, 1, 1, 1, 2)), 1),
 ])
 def test_heads_validation(spa, bad, status):

@@ -117,6 +117,14 @@ def test_fp8_p32_P256():
 
 
 @pytest.mark.parametrize("fused", [False, True])
+def test_fp8_group_of_7(fused):
+    """A group of 7 query heads per KV head (28 / 4), scored by the kernel built
+    for 8, on fp8 pages."""
+    run(W.Workload("fp8_g7", 3207, 2, 28, 4, 16, 64, (1500, 999), 5, 2, (1, 0, 1, 0), 32, 200, 256, True),
+        fused=fused)
+
+
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("compact", [False, True])
 def test_fp8_window_only_storage(compact, fused):
     wl = W.WORKLOADS["llama3_128k"].scaled(contexts=(4100, 3001, 1000, 17), steps=9, budget=512,

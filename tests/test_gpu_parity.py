@@ -146,11 +146,14 @@ def test_ragged_mha_small():
 
 
 @pytest.mark.parametrize("fused", [False, True])
-@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (64, 8), (32, 2)])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (64, 8), (32, 2), (24, 8), (40, 8), (12, 2), (56, 8),
+                                    (24, 2)])
 def test_group_sizes(hq, hkv, fused):
-    """Query groups of 1, 2, 8 and 16 heads (the benchmark's 4 elsewhere), on the
-    separate entry points and on the launches with the append inside (for
-    groups of 8 and 16 the selection entry point runs the append first)."""
+    """Query groups of 1, 2, 8 and 16 heads (the benchmark's 4 elsewhere) and of
+    3, 5, 6, 7 and 12 (scored by the kernel built for the next power of two,
+    the extra query columns repeating the group's last query), on the separate
+    entry points and on the launches with the append inside (for groups above
+    4 the selection entry point runs the append first)."""
     kind = tuple(h % 2 for h in range(hkv))
     wl = W.Workload(f"g{hq // hkv}", 2000 + hq, 2, hq, hkv, 16, 64, (1500, 999), 5, 2, kind, 32, 200,
                     256, True)

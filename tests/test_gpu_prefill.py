@@ -132,9 +132,10 @@ def test_dense_below_the_threshold():
     check(SMALL.scaled(name="prefill_dense", L=900))
 
 
-@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2), (16, 2), (32, 2)])
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2), (16, 2), (32, 2), (6, 2), (10, 2), (14, 2), (24, 2)])
 def test_group_sizes(hq, hkv):
-    """G = 1, 2, 8, 16 (the 4-head work-groups split larger groups)."""
+    """G = 1, 2, 8, 16, and 3, 5, 7, 12 (work-groups of the largest of 4, 2, 1
+    heads that divides G)."""
     check(SMALL.scaled(name=f"prefill_g{hq // hkv}", hq=hq, hkv=hkv, L=64 * 9 + 5, budget=192, dense_below=100))
 
 

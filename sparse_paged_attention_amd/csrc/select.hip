@@ -264,40 +264,11 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
       qn[g][i] = qv[i] < 0.0 ? qv[i] : 0.0;
     }
   }
-  // the new key's channels of this lane, and where the token lands
-  Raw<S::CPL> kn, kn_hi;
+  // where the step's token lands (its key is taken below, by the one wave
+  // whose range holds that page, once the first summary loads are out)
+  Raw<S::CPL> kn = {}, kn_hi = {};
   const int32_t j_new = FRESH && L >= 1 ? (L - 1) / pl.p : -1;
   const bool opens = FRESH && L >= 1 && (L - 1) % pl.p == 0;
-  if (FRESH) {
-    load_raw<S::CPL>(reinterpret_cast<const uint16_t*>(k_new) + ((int64_t)b * pl.hkv + h) * kHeadDim + c0, kn);
-    kn_hi = kn;
-    if (pl.q8) {          // the key as the append quantizes it (the group's lanes hold the whole row), rounded outward
-      float x[S::CPL];
-      float amax = 0.f;
-#pragma unroll
-      for (int i = 0; i < S::CPL / 2; ++i) {
-        x[2 * i] = bf16_lo(kn.w[i]);
-        x[2 * i + 1] = bf16_hi(kn.w[i]);
-        amax = fmaxf(amax, fmaxf(fabsf(x[2 * i]), fabsf(x[2 * i + 1])));
-      }
-#pragma unroll
-      for (int o = 1; o < S::LPP; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-      const float scale = amax / 448.f;
-#pragma unroll
-      for (int i = 0; i < S::CPL / 2; ++i) {
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const uint32_t code = scale == 0.f ? 0u : e4m3_code(x[2 * i + e] / scale);
-          const double v = (double)e4m3_value(code) * (double)scale;
-          lo |= bf16_down(v) << (16 * e);
-          hi |= bf16_up(v) << (16 * e);
-        }
-        kn.w[i] = lo;
-        kn_hi.w[i] = hi;
-      }
-    }
-  }
   __syncthreads();
 
   // summary location of page slot pp of pass it (page 0 of the pool if invalid)
@@ -371,6 +342,38 @@ __global__ void __launch_bounds__(64) score_kernel(PoolArgs pl, BatchArgs bt, He
 #pragma unroll
   for (int it = 0; it < S::RING; ++it)
     if (it < live) issue(it, ring[it]);
+  // the new key's channels of this lane (on fp8 pages as the append
+  // quantizes it, rounded outward), for the wave whose range holds its page
+  if (FRESH && j_new >= base && j_new < base + live * S::PASS) {   // wave-uniform
+    load_raw<S::CPL>(reinterpret_cast<const uint16_t*>(k_new) + ((int64_t)b * pl.hkv + h) * kHeadDim + c0, kn);
+    kn_hi = kn;
+    if (pl.q8) {          // the key as the append quantizes it (the group's lanes hold the whole row), rounded outward
+      float x[S::CPL];
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < S::CPL / 2; ++i) {
+        x[2 * i] = bf16_lo(kn.w[i]);
+        x[2 * i + 1] = bf16_hi(kn.w[i]);
+        amax = fmaxf(amax, fmaxf(fabsf(x[2 * i]), fabsf(x[2 * i + 1])));
+      }
+#pragma unroll
+      for (int o = 1; o < S::LPP; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+      const float scale = amax / 448.f;
+#pragma unroll
+      for (int i = 0; i < S::CPL / 2; ++i) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint32_t code = scale == 0.f ? 0u : e4m3_code(x[2 * i + e] / scale);
+          const double v = (double)e4m3_value(code) * (double)scale;
+          lo |= bf16_down(v) << (16 * e);
+          hi |= bf16_up(v) << (16 * e);
+        }
+        kn.w[i] = lo;
+        kn_hi.w[i] = hi;
+      }
+    }
+  }
 #pragma unroll
   for (int it = 0; it < S::PASSES; ++it) {
     if (it >= live) break;

@@ -85,7 +85,7 @@ struct ScoreShape {
   // 128K row's ranges (2736 waves for 16 heads) are still all resident at
   // once and each wave's chain of dependent load rounds is shorter (20.3
   // against 21.2 us for 8 passes at the 128K benchmark shape; 7 passes: 21.0
-  // us). Launches with fewer pages take fewer passes per wave (score_passes).
+  // us). Launches with fewer pages take fewer passes per wave (launch_score_g).
   static constexpr int PASSES = G <= 4 ? 6 : 8;
   static constexpr int RING = 2;                    // passes in flight
   // waves a launch can keep resident with room to spare (three per SIMD for

@@ -589,3 +589,40 @@ def test_selection_exact_ties_go_to_lowest_page_id():
     log(f"[parity] {wl.name}")
     pr = ParityRun(wl, strict_ties=True)
     assert_reports(pr.run())
+
+
+def random_workload(seed: int):
+    """A seeded random small configuration: KV heads, group size, page sizes,
+    batch and lengths, head kinds, sink and window, budget, reuse interval,
+    page layout, pool format, storage and launch path."""
+    rng = np.random.default_rng(seed)
+    hkv = int(rng.choice([1, 2, 3, 4, 8]))
+    G = int(rng.integers(1, 9))
+    p = int(rng.choice([16, 32, 64]))
+    P = p * int(rng.choice([1, 2, 4]))
+    batch = int(rng.integers(1, 5))
+    contexts = tuple(int(x) for x in rng.integers(1, 3000, batch))
+    kind = tuple(int(x) for x in rng.integers(0, 2, hkv))
+    sink = int(rng.integers(0, 100))
+    window = int(rng.integers(1, 600))
+    budget = int(rng.integers(p, 1025))
+    wl = W.Workload(f"random{seed}", 7000 + seed, batch, hkv * G, hkv, p, P, contexts, int(rng.integers(3, 7)),
+                    int(rng.integers(1, 5)), kind, sink, window, budget, bool(rng.integers(0, 2)),
+                    quantized=bool(rng.random() < 0.2))
+    storage = str(rng.choice(["table", "ring", "compact"]))
+    return wl, dict(kv_format=str(rng.choice(["bf16", "fp8"])), fused=bool(rng.integers(0, 2)),
+                    window_only=storage != "table", compact=storage == "compact")
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_configurations(seed):
+    """Forty-eight seeded random small configurations (random_workload) through
+    the whole step against the oracle: every step's outputs, scores and
+    selections, on whichever pool format, storage and launch path the seed
+    draws."""
+    wl, opts = random_workload(seed)
+    log(f"[parity] random {seed}: B={wl.batch} hq={wl.hq} hkv={wl.hkv} p={wl.p} P={wl.P} kind={wl.kind} "
+        f"contexts={wl.contexts} sink={wl.sink} window={wl.window} budget={wl.budget} reuse={wl.reuse} "
+        f"permute={wl.permute} quantized={wl.quantized} {opts}")
+    pr = ParityRun(wl, **opts)
+    assert_reports(pr.run())

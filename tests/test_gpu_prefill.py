@@ -217,3 +217,24 @@ def test_graph_replay_and_workspace_selection():
         assert torch.isfinite(x)
         assert torch.equal(out2, out0) and torch.equal(lse2, lse0), f"replay {rep}"
     log(f"  prefill graph: 3 replays bit-identical, L={L}")
+
+
+def random_prefill(seed: int) -> W.Prefill:
+    """A seeded random small prefill: length (ragged last block), KV heads,
+    group size, head kinds, sink and window, budget, dense threshold, planted
+    blocks, tied or untied projections."""
+    rng = np.random.default_rng(seed)
+    hkv = int(rng.choice([1, 2, 3]))
+    G = int(rng.integers(1, 9))
+    L = int(rng.integers(1, 64 * 24))
+    return W.Prefill(f"prefill_random{seed}", 9000 + seed, L, hkv * G, hkv,
+                     tuple(int(x) for x in rng.integers(0, 2, hkv)), int(rng.integers(0, 150)),
+                     int(rng.integers(1, 400)), int(rng.integers(1, 16)) * 64, int(rng.choice([1, 2 * L, L // 2 + 1])),
+                     planted=int(rng.integers(0, 3)), tied=bool(rng.integers(0, 2)))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_configurations(seed):
+    """Twenty-four seeded random small prefills (random_prefill) against the
+    oracle: block scores, every selection row, outputs and lse."""
+    check(random_prefill(seed))

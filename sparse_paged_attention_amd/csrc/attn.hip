@@ -135,20 +135,6 @@ __device__ __forceinline__ void issue_half8(const PoolArgs& pl, int32_t h, const
   vs = *reinterpret_cast<const f32x4*>(pl.vs + row0 + 4 * quad);
 }
 
-// Two E4M3 codes (bytes 0-1 or 2-3 of w) as a bf16 pair: the hardware
-// conversion to fp32, then the upper halves, which is exact because an E4M3
-// value has at most four significant bits.
-template <bool HIGH>
-__device__ __forceinline__ uint32_t codes_bf16x2(uint32_t w) {
-  const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HIGH);
-  return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
-}
-
-// Four codes (tokens or channels in byte order) as two bf16 words.
-__device__ __forceinline__ uint2 codes_bf16x4(uint32_t w) {
-  return uint2{codes_bf16x2<false>(w), codes_bf16x2<true>(w)};
-}
-
 struct State {
   float m;          // running reference (near the maximum) of this lane's query, log2 units
   float l;          // running sum over this lane's tokens

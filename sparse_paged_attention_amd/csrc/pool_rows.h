@@ -121,6 +121,23 @@ __device__ __forceinline__ e4m3_pair_values e4m3_value2(uint32_t c2) {
   return __builtin_amdgcn_cvt_pk_f32_fp8((int)c2, false);
 }
 
+// Two codes (bytes 0-1 of w, or 2-3 with HIGH) as a bf16 pair, by gfx950's
+// scaled conversion with scale 1. Exact: an E4M3 value has at most four
+// significant bits and an exponent inside bf16's range (equal to e4m3_value
+// for every pair of codes but the NaN ones, checked over all of them).
+template <bool HIGH>
+__device__ __forceinline__ uint32_t codes_bf16x2(uint32_t w) {
+  const auto p = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH);
+  uint32_t u;
+  __builtin_memcpy(&u, &p, 4);
+  return u;
+}
+
+// Four codes (tokens or channels in byte order) as two bf16 words.
+__device__ __forceinline__ uint2 codes_bf16x4(uint32_t w) {
+  return uint2{codes_bf16x2<false>(w), codes_bf16x2<true>(w)};
+}
+
 // Key of an fp32 bit pattern that orders like IEEE totalOrder, with
 // consecutive fp32 values on consecutive keys (-0 just below +0), and back.
 __device__ __forceinline__ uint32_t f32_key(uint32_t u) { return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u); }

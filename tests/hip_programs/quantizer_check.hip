@@ -12,7 +12,10 @@
 //      e4m3_value, every code;
 //   4. wave_max_u32, and pair_max_u16 + chunk_row_maxima (the reduce-scatter of
 //      16 key and 16 value rows, with its lane map fold_lane) vs serial maxima
-//      on seeded rows.
+//      on seeded rows;
+//   5. codes_bf16x2 (the scaled conversion the attention kernels decode codes
+//      with) vs the bf16 bits of e4m3_value, every pair of codes, both halves
+//      of the word.
 // Prints one line per check with its mismatch count; exit status 0 when all are 0.
 #include <hip/hip_runtime.h>
 #include <cstdio>
@@ -20,7 +23,7 @@
 #include "pool_rows.h"
 using namespace spa;
 
-constexpr int kChecks = 9;
+constexpr int kChecks = 10;
 
 __device__ void report(unsigned long long* cnt, uint32_t* first, int which, uint32_t a, uint32_t b, uint32_t c) {
   const unsigned long long k = atomicAdd(&cnt[which], 1ull);
@@ -125,6 +128,19 @@ __global__ void __launch_bounds__(64) check_maxima(unsigned long long* cnt, uint
   if (m != want || fold_lane(tau != 0, i) != (lane & ~3)) report(cnt, first, 8, blockIdx.x, threadIdx.x, m);
 }
 
+// one thread per pair of codes (bits 0-15); NaN codes skipped
+__global__ void check_decode(unsigned long long* cnt, uint32_t* first) {
+  const uint32_t c2 = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c2 > 0xFFFFu) return;
+  const uint32_t c0 = c2 & 0xFFu, c1 = c2 >> 8;
+  if ((c0 & 0x7Fu) == 0x7Fu || (c1 & 0x7Fu) == 0x7Fu) return;
+  const uint32_t want = (__float_as_uint(e4m3_value(c0)) >> 16) | (__float_as_uint(e4m3_value(c1)) & 0xFFFF0000u);
+  const uint32_t lo = codes_bf16x2<false>(c2 | 0xA5A50000u);   // the other half holds codes that must not leak in
+  const uint32_t hi = codes_bf16x2<true>((c2 << 16) | 0x5A5Au);
+  if (lo != want) report(cnt, first, 9, c2, lo, want);
+  if (hi != want) report(cnt, first, 9, c2 | 0x10000u, hi, want);
+}
+
 int main() {
   unsigned long long* cnt;
   uint32_t* first;
@@ -136,6 +152,7 @@ int main() {
   hipLaunchKernelGGL(check_rows, dim3(0x7F80), dim3(256), 0, 0, cnt, first);
   hipLaunchKernelGGL(check_products, dim3(0x7F80), dim3(256), 0, 0, cnt, first);
   hipLaunchKernelGGL(check_maxima, dim3(65536), dim3(64), 0, 0, cnt, first);
+  hipLaunchKernelGGL(check_decode, dim3(256), dim3(256), 0, 0, cnt, first);
   const hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     printf("hip error: %s\n", hipGetErrorString(e));
@@ -154,7 +171,8 @@ int main() {
       "bf16 below the product vs fp64, all codes x scales",
       "bf16 above the product vs fp64, all codes x scales",
       "wave_max_u32, seeded rows",
-      "pair_max_u16 + chunk_row_maxima and its lane map, seeded rows"};
+      "pair_max_u16 + chunk_row_maxima and its lane map, seeded rows",
+      "codes_bf16x2 (scaled conversion) vs e4m3_value, all code pairs, both halves"};
   int bad = 0;
   for (int w = 0; w < kChecks; ++w) {
     printf("%s: %llu mismatches\n", names[w], h[w]);

@@ -23,6 +23,7 @@
 #include <atomic>
 
 #include "pool_rows.h"
+#include "psplit.h"
 
 namespace spa {
 namespace {
@@ -30,7 +31,6 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // log2(e) / sqrt(128): scores are kept in the log2 domain
@@ -264,11 +264,9 @@ __device__ __forceinline__ PairProbs softmax_pair(const Block& ba, const Block& 
     }
   }
 #pragma unroll
-  for (int r = 0; r < 8; r += 2) {                // native round-to-nearest-even conversions
-    const f32x2 v = {pr[r], pr[r + 1]};
-    const bf16x2 h = __builtin_convertvector(v, bf16x2);
-    const f32x2 rest = v - __builtin_convertvector(h, f32x2);
-    const bf16x2 lo = __builtin_convertvector(rest, bf16x2);
+  for (int r = 0; r < 8; r += 2) {
+    bf16x2 h, lo;
+    split_pair(pr[r], pr[r + 1], h, lo);
     pp.hi[r] = h[0]; pp.hi[r + 1] = h[1];
     pp.lo[r] = lo[0]; pp.lo[r + 1] = lo[1];
   }

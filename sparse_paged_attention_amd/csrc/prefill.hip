@@ -24,6 +24,7 @@
 //                  group's heads, S^T = K Q^T and O^T += V^T P^T on
 //                  v_mfma_f32_16x16x32_bf16 (P split into bf16 high and low
 //                  parts, as in the decode kernel).
+#include "psplit.h"
 #include "spa_internal.h"
 
 namespace spa {
@@ -31,7 +32,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kB = kPrefillBlock;          // 64 tokens per block
@@ -258,26 +258,42 @@ __global__ void __launch_bounds__(NH * 128) attn_kernel(PrefillArgs a) {
   // staging assignment: K piece p (of 1024 16-byte pieces) = row p / 16, cols
   // 8 (p % 16) .. +8; V unit u (of 512) = channel pair u % 64, keys 8 (u / 64) .. +8
   using St = Stage<NT>;
+  // byte offsets of this thread's staged pieces inside a key block
+  const uint32_t kcol = 16u * (tid % 16), vcol = 4u * (tid % 64);
+  uint32_t koff[St::KP], voff[St::VU];
+#pragma unroll
+  for (int x = 0; x < St::KP; ++x) koff[x] = (uint32_t)((tid + NT * x) / 16) * 256u + kcol;
+#pragma unroll
+  for (int x = 0; x < St::VU; ++x) voff[x] = (uint32_t)(8 * ((tid + NT * x) / 64)) * 256u + vcol;
   auto load_block = [&](int32_t kbk, St& st) {
     const int64_t base = (int64_t)kbk * kB;
-    const uint16_t* kh = a.k + (int64_t)h * L * kHeadDim;
-    const uint16_t* vh = a.v + (int64_t)h * L * kHeadDim;
+    const char* kb = reinterpret_cast<const char*>(a.k + ((int64_t)h * L + base) * kHeadDim);
+    const char* vb = reinterpret_cast<const char*>(a.v + ((int64_t)h * L + base) * kHeadDim);
+    if (base + kB <= L) {                               // block-uniform
 #pragma unroll
-    for (int x = 0; x < St::KP; ++x) {
-      const int p = tid + NT * x;                       // < 1024
-      const int64_t row = min(base + p / 16, L - 1);
-      const uint4 kv4 = *reinterpret_cast<const uint4*>(kh + row * kHeadDim + 8 * (p % 16));
-      st.k[x][0] = kv4.x; st.k[x][1] = kv4.y; st.k[x][2] = kv4.z; st.k[x][3] = kv4.w;
-    }
-#pragma unroll
-    for (int x = 0; x < St::VU; ++x) {
-      const int un = tid + NT * x;                      // < 512
-      const int cp = un % 64, kg = un / 64;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t row = min(base + 8 * kg + u, L - 1);
-        st.v[x][u] = reinterpret_cast<const uint32_t*>(vh + row * kHeadDim)[cp];
+      for (int x = 0; x < St::KP; ++x) {
+        const uint4 kv4 = *reinterpret_cast<const uint4*>(kb + koff[x]);
+        st.k[x][0] = kv4.x; st.k[x][1] = kv4.y; st.k[x][2] = kv4.z; st.k[x][3] = kv4.w;
       }
+#pragma unroll
+      for (int x = 0; x < St::VU; ++x)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) st.v[x][u] = *reinterpret_cast<const uint32_t*>(vb + voff[x] + 256u * u);
+    } else {
+      // the prompt's last block: rows past its end repeat its last row (no
+      // query attends them)
+      asm volatile("");                                 // a real branch: the loads above need no clamp
+      const uint32_t last = (uint32_t)(L - 1 - base) * 256u;
+#pragma unroll
+      for (int x = 0; x < St::KP; ++x) {
+        const uint4 kv4 = *reinterpret_cast<const uint4*>(kb + min(koff[x] - kcol, last) + kcol);
+        st.k[x][0] = kv4.x; st.k[x][1] = kv4.y; st.k[x][2] = kv4.z; st.k[x][3] = kv4.w;
+      }
+#pragma unroll
+      for (int x = 0; x < St::VU; ++x)
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          st.v[x][u] = *reinterpret_cast<const uint32_t*>(vb + min(voff[x] - vcol + 256u * u, last) + vcol);
     }
   };
   auto store_block = [&](int buf, const St& st) {
@@ -293,15 +309,15 @@ __global__ void __launch_bounds__(NH * 128) attn_kernel(PrefillArgs a) {
       const int un = tid + NT * x;
       const int cp = un % 64, kg = un / 64;
       const uint32_t* v = st.v[x];
-      uint4 lo, hi;                 // channel 2cp / 2cp + 1, keys 8kg .. +8
-      lo.x = (v[0] & 0xFFFFu) | (v[1] << 16);
-      lo.y = (v[2] & 0xFFFFu) | (v[3] << 16);
-      lo.z = (v[4] & 0xFFFFu) | (v[5] << 16);
-      lo.w = (v[6] & 0xFFFFu) | (v[7] << 16);
-      hi.x = (v[0] >> 16) | (v[1] & 0xFFFF0000u);
-      hi.y = (v[2] >> 16) | (v[3] & 0xFFFF0000u);
-      hi.z = (v[4] >> 16) | (v[5] & 0xFFFF0000u);
-      hi.w = (v[6] >> 16) | (v[7] & 0xFFFF0000u);
+      uint4 lo, hi;                 // channel 2cp / 2cp + 1, keys 8kg .. +8: the low / high halves of pairs of words
+      lo.x = __builtin_amdgcn_perm(v[1], v[0], 0x05040100u);
+      lo.y = __builtin_amdgcn_perm(v[3], v[2], 0x05040100u);
+      lo.z = __builtin_amdgcn_perm(v[5], v[4], 0x05040100u);
+      lo.w = __builtin_amdgcn_perm(v[7], v[6], 0x05040100u);
+      hi.x = __builtin_amdgcn_perm(v[1], v[0], 0x07060302u);
+      hi.y = __builtin_amdgcn_perm(v[3], v[2], 0x07060302u);
+      hi.z = __builtin_amdgcn_perm(v[5], v[4], 0x07060302u);
+      hi.w = __builtin_amdgcn_perm(v[7], v[6], 0x07060302u);
       uint2* d0 = reinterpret_cast<uint2*>(vl + ((2 * cp) * kVStride + 8 * kg) * 2);      // 8-byte aligned rows
       uint2* d1 = reinterpret_cast<uint2*>(vl + ((2 * cp + 1) * kVStride + 8 * kg) * 2);
       d0[0] = uint2{lo.x, lo.y};
@@ -357,12 +373,14 @@ __global__ void __launch_bounds__(NH * 128) attn_kernel(PrefillArgs a) {
     for (int qt = 0; qt < 2; ++qt) {
       const int32_t tq = j * kB + 32 * rh + 16 * qt + col;
       if (!full) {
+        int32_t kp0 = kpos0;
+        asm volatile("" : "+v"(kp0));      // keeps the comparisons inside this branch
         const int32_t Li = (int32_t)L, sink = a.sink, wlo = tq + 1 - a.window;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int32_t sp = kpos0 + 16 * t + r;
+            const int32_t sp = kp0 + 16 * t + r;
             const bool ok = (sp <= tq) & (sp < Li) & (dynamic | (sp < sink) | (sp >= wlo));   // no branches
             s[qt][t][r] = ok ? s[qt][t][r] : -INFINITY;
           }
@@ -413,10 +431,8 @@ __global__ void __launch_bounds__(NH * 128) attn_kernel(PrefillArgs a) {
 #pragma unroll
         for (int x = 0; x < 8; x += 2) {
           const int t = 2 * pr + x / 4, r = x % 4;
-          const f32x2 v = {s[qt][t][r], s[qt][t][r + 1]};
-          const bf16x2 hv = __builtin_convertvector(v, bf16x2);
-          const f32x2 rest = v - __builtin_convertvector(hv, f32x2);
-          const bf16x2 lv = __builtin_convertvector(rest, bf16x2);
+          bf16x2 hv, lv;
+          split_pair(s[qt][t][r], s[qt][t][r + 1], hv, lv);
           ph[qt][x] = hv[0]; ph[qt][x + 1] = hv[1];
           pl[qt][x] = lv[0]; pl[qt][x + 1] = lv[1];
         }

@@ -15,15 +15,18 @@
 //      on seeded rows;
 //   5. codes_bf16x2 (the scaled conversion the attention kernels decode codes
 //      with) vs the bf16 bits of e4m3_value, every pair of codes, both halves
-//      of the word.
+//      of the word;
+//   6. split_pair (psplit.h: p - hi by one dot instruction) vs the plain
+//      subtraction, every normal fp32 p below 2^9 in both slots.
 // Prints one line per check with its mismatch count; exit status 0 when all are 0.
 #include <hip/hip_runtime.h>
 #include <cstdio>
 #include <cstdint>
 #include "pool_rows.h"
+#include "psplit.h"
 using namespace spa;
 
-constexpr int kChecks = 10;
+constexpr int kChecks = 11;
 
 __device__ void report(unsigned long long* cnt, uint32_t* first, int which, uint32_t a, uint32_t b, uint32_t c) {
   const unsigned long long k = atomicAdd(&cnt[which], 1ull);
@@ -141,6 +144,24 @@ __global__ void check_decode(unsigned long long* cnt, uint32_t* first) {
   if (hi != want) report(cnt, first, 9, c2 | 0x10000u, hi, want);
 }
 
+// every normal fp32 p in [2^-126, 2^9): in slot 0, and mirrored in slot 1
+__global__ void check_split(unsigned long long* cnt, uint32_t* first) {
+  constexpr uint32_t kLo = 0x00800000u, kHi = 0x44000000u;
+  for (uint32_t u = kLo + blockIdx.x * blockDim.x + threadIdx.x; u < kHi; u += gridDim.x * blockDim.x) {
+    const float p0 = __uint_as_float(u), p1 = __uint_as_float(kLo + (kHi - 1u - u));
+    bf16x2_t hi, lo;
+    split_pair(p0, p1, hi, lo);
+    const f32x2_t v = {p0, p1};
+    const bf16x2_t h = __builtin_convertvector(v, bf16x2_t);
+    const f32x2_t rest = v - __builtin_convertvector(h, f32x2_t);
+    const bf16x2_t l = __builtin_convertvector(rest, bf16x2_t);
+    uint32_t gh, gl, wh, wl;
+    __builtin_memcpy(&gh, &hi, 4); __builtin_memcpy(&gl, &lo, 4);
+    __builtin_memcpy(&wh, &h, 4); __builtin_memcpy(&wl, &l, 4);
+    if (gh != wh || gl != wl) report(cnt, first, 10, u, gl, wl);
+  }
+}
+
 int main() {
   unsigned long long* cnt;
   uint32_t* first;
@@ -153,6 +174,7 @@ int main() {
   hipLaunchKernelGGL(check_products, dim3(0x7F80), dim3(256), 0, 0, cnt, first);
   hipLaunchKernelGGL(check_maxima, dim3(65536), dim3(64), 0, 0, cnt, first);
   hipLaunchKernelGGL(check_decode, dim3(256), dim3(256), 0, 0, cnt, first);
+  hipLaunchKernelGGL(check_split, dim3(8192), dim3(256), 0, 0, cnt, first);
   const hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     printf("hip error: %s\n", hipGetErrorString(e));
@@ -172,7 +194,8 @@ int main() {
       "bf16 above the product vs fp64, all codes x scales",
       "wave_max_u32, seeded rows",
       "pair_max_u16 + chunk_row_maxima and its lane map, seeded rows",
-      "codes_bf16x2 (scaled conversion) vs e4m3_value, all code pairs, both halves"};
+      "codes_bf16x2 (scaled conversion) vs e4m3_value, all code pairs, both halves",
+      "split_pair (dot instruction) vs the plain subtraction, all normal fp32 p < 2^9"};
   int bad = 0;
   for (int w = 0; w < kChecks; ++w) {
     printf("%s: %llu mismatches\n", names[w], h[w]);

@@ -66,7 +66,7 @@ def pmc_per_dispatch(db_path: str) -> dict:
 
 # Sources each kernel is built from (name part -> files).
 _KERNEL_SOURCES = (
-    (("attn_kernel", "combine_kernel"), ("attn.hip", "pool_rows.h", "spa_internal.h")),
+    (("attn_kernel", "combine_kernel"), ("attn.hip", "pool_rows.h", "psplit.h", "spa_internal.h")),
     (("write_kernel", "summary_kernel", "append_kernel"), ("pool.hip", "pool_rows.h", "spa_internal.h")),
     (("score_kernel", "topk_kernel"), ("select.hip", "pool_rows.h", "spa_internal.h")),
 )

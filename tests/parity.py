@@ -32,6 +32,17 @@ LSE_TOL = 1e-3
 TIE_REL = 1e-6
 
 
+def seed_range(var: str, default: int) -> range:
+    """Seeds of a random-configuration test: range(default), or the range
+    "a:b" that the environment variable `var` names (a wider sweep)."""
+    import os
+    v = os.environ.get(var)
+    if not v:
+        return range(default)
+    a, b = (int(x) for x in v.split(":"))
+    return range(a, b)
+
+
 def log(msg: str) -> None:
     print(msg, flush=True)
     sys.stdout.flush()

@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import workloads as W
-from parity import ParityRun, assert_reports, bits_to_bf16, log
+from parity import ParityRun, assert_reports, bits_to_bf16, log, seed_range
 
 pytestmark = pytest.mark.gpu
 
@@ -614,12 +614,13 @@ def random_workload(seed: int):
                     window_only=storage != "table", compact=storage == "compact")
 
 
-@pytest.mark.parametrize("seed", range(48))
+@pytest.mark.parametrize("seed", seed_range("SPA_RANDOM_SEEDS", 48))
 def test_random_configurations(seed):
     """Forty-eight seeded random small configurations (random_workload) through
     the whole step against the oracle: every step's outputs, scores and
     selections, on whichever pool format, storage and launch path the seed
-    draws."""
+    draws. SPA_RANDOM_SEEDS=a:b runs seeds a .. b - 1 instead (a wider
+    sweep)."""
     wl, opts = random_workload(seed)
     log(f"[parity] random {seed}: B={wl.batch} hq={wl.hq} hkv={wl.hkv} p={wl.p} P={wl.P} kind={wl.kind} "
         f"contexts={wl.contexts} sink={wl.sink} window={wl.window} budget={wl.budget} reuse={wl.reuse} "

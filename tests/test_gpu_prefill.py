@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import workloads as W
-from parity import LSE_TOL, OUT_TOL, TIE_REL, bits_to_bf16, log
+from parity import LSE_TOL, OUT_TOL, TIE_REL, bits_to_bf16, log, seed_range
 
 pytestmark = pytest.mark.gpu
 
@@ -233,8 +233,10 @@ def random_prefill(seed: int) -> W.Prefill:
                      planted=int(rng.integers(0, 3)), tied=bool(rng.integers(0, 2)))
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", seed_range("SPA_RANDOM_PREFILL_SEEDS", 24))
 def test_random_configurations(seed):
     """Twenty-four seeded random small prefills (random_prefill) against the
-    oracle: block scores, every selection row, outputs and lse."""
+    oracle: block scores, every selection row, outputs and lse.
+    SPA_RANDOM_PREFILL_SEEDS=a:b runs seeds a .. b - 1 instead (a wider
+    sweep)."""
     check(random_prefill(seed))

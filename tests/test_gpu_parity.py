@@ -591,13 +591,14 @@ def test_selection_exact_ties_go_to_lowest_page_id():
     assert_reports(pr.run())
 
 
-def random_workload(seed: int):
-    """A seeded random small configuration: KV heads, group size, page sizes,
-    batch and lengths, head kinds, sink and window, budget, reuse interval,
-    page layout, pool format, storage and launch path."""
+def random_workload(seed: int, groups=(1, 8)):
+    """A seeded random small configuration: KV heads, group size (in the range
+    `groups`), page sizes, batch and lengths, head kinds, sink and window,
+    budget, reuse interval, page layout, pool format, storage and launch
+    path."""
     rng = np.random.default_rng(seed)
     hkv = int(rng.choice([1, 2, 3, 4, 8]))
-    G = int(rng.integers(1, 9))
+    G = int(rng.integers(groups[0], groups[1] + 1))
     p = int(rng.choice([16, 32, 64]))
     P = p * int(rng.choice([1, 2, 4]))
     batch = int(rng.integers(1, 5))
@@ -627,3 +628,14 @@ def test_random_configurations(seed):
         f"permute={wl.permute} quantized={wl.quantized} {opts}")
     pr = ParityRun(wl, **opts)
     assert_reports(pr.run())
+
+
+@pytest.mark.parametrize("seed", seed_range("SPA_RANDOM_LARGE_GROUP_SEEDS", 12))
+def test_random_configurations_large_groups(seed):
+    """Twelve seeded random small configurations whose query groups hold 9 to
+    16 heads: the scoring kernel built for 16 queries with the group's last
+    query repeated, and the step's append launched before the selection."""
+    wl, opts = random_workload(5000 + seed, groups=(9, 16))
+    log(f"[parity] random large group {seed}: B={wl.batch} hq={wl.hq} hkv={wl.hkv} p={wl.p} P={wl.P} "
+        f"kind={wl.kind} contexts={wl.contexts} budget={wl.budget} {opts}")
+    assert_reports(ParityRun(wl, **opts).run())

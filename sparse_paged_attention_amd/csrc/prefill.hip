@@ -210,7 +210,7 @@ struct KeyList {
 
 template <int NH>
 __global__ void __launch_bounds__(NH * 128) attn_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBufBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kBufBytes];
   constexpr int NT = NH * 128;                 // threads
   const int32_t j = (int32_t)(gridDim.x - 1 - blockIdx.x);   // longest key lists first
   const int32_t h = blockIdx.y;
@@ -334,14 +334,8 @@ __global__ void __launch_bounds__(NH * 128) attn_kernel(PrefillArgs a) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) o[qt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  St st;
-  if (kl.count > 0) load_block(kl.at(0, sel_list), st);
-  for (int32_t e = 0; e < kl.count; ++e) {
-    const int32_t kbk = kl.at(e, sel_list);
-    const int buf = e & 1;
-    store_block(buf, st);
-    __syncthreads();
-    if (e + 1 < kl.count) load_block(kl.at(e + 1, sel_list), st);
+  // one key block staged in LDS buffer buf: scores, mask, online softmax, P V
+  auto block = [&](int32_t kbk, int buf) {
     const uint8_t* kl_ = lds + buf * kBufBytes;
     const uint8_t* vl = kl_ + kKBytes;
 
@@ -452,6 +446,25 @@ __global__ void __launch_bounds__(NH * 128) attn_kernel(PrefillArgs a) {
         }
       }
     }
+  };
+
+  // two key blocks per barrier: pair q sits in buffers 2 (q & 1) and
+  // 2 (q & 1) + 1 while the next pair's global loads are in flight (the
+  // buffers it overwrites were last read two pairs before, behind the last
+  // barrier)
+  St st0, st1;
+  const int32_t nk = kl.count;
+  if (nk > 0) load_block(kl.at(0, sel_list), st0);
+  if (nk > 1) load_block(kl.at(1, sel_list), st1);
+  for (int32_t e = 0; e < nk; e += 2) {
+    const int buf = 2 * ((e >> 1) & 1);
+    store_block(buf, st0);
+    if (e + 1 < nk) store_block(buf + 1, st1);
+    __syncthreads();
+    if (e + 2 < nk) load_block(kl.at(e + 2, sel_list), st0);
+    if (e + 3 < nk) load_block(kl.at(e + 3, sel_list), st1);
+    block(kl.at(e, sel_list), buf);
+    if (e + 1 < nk) block(kl.at(e + 1, sel_list), buf + 1);
   }
 
   // normalise and store the wave's rows

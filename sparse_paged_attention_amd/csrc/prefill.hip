@@ -181,9 +181,9 @@ __global__ void __launch_bounds__(64) select_kernel(PrefillArgs a) {
 // 2 * NH waves, wave w handles query head g0 + w / 2, rows 32 (w % 2) .. +32 of
 // the block as two 16-row column tiles of the MFMAs. Per key block, every
 // thread stages part of K (row-major, rows padded to 272 bytes) and of V^T
-// (channel-major, rows padded to 144 bytes) into one of two LDS buffers; the
-// next key block's global loads are in flight while the current one is
-// computed, so one barrier per key block suffices.
+// (channel-major, rows padded to 136 bytes) into one of four LDS block
+// buffers. Key blocks go in pairs: the next pair's global loads are in flight
+// while the current pair is computed, one barrier per pair.
 constexpr int kKStride = 136;              // bf16 per K row in LDS
 constexpr int kVStride = 68;               // bf16 per V^T row in LDS (136 B: 16 rows read as 8-byte pieces fall on distinct banks)
 constexpr int kKBytes = kB * kKStride * 2;

@@ -327,7 +327,9 @@ __global__ void __launch_bounds__(NH * 128) attn_kernel(PrefillArgs a) {
     }
   };
 
-  float m_ref[2] = {-INFINITY, -INFINITY}, l_sum[2] = {0.f, 0.f};
+  // running reference per query column (log2 units) and the value subtracted
+  // before exponentiation (0 while the column has no key yet)
+  float m_ref[2] = {-INFINITY, -INFINITY}, m_sub[2] = {0.f, 0.f}, l_sum[2] = {0.f, 0.f};
   f32x4 o[2][8];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt)
@@ -379,33 +381,38 @@ __global__ void __launch_bounds__(NH * 128) attn_kernel(PrefillArgs a) {
             s[qt][t][r] = ok ? s[qt][t][r] : -INFINITY;
           }
       }
-      // online softmax over the 64 keys of the block for this query column
+      // online softmax over the 64 keys of the block for this query column.
+      // A column's reference rises only when the block's maximum passes it
+      // by the slack. Scaling is monotone, so that happens for some column
+      // exactly when some lane's own maximum passes its column's reference:
+      // the cross-lane reduction runs only then, with the same outcome
       float bm = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) bm = fmaxf(bm, s[qt][t][r]);
-      {
+      if (__any(bm * kScaleLog2 > m_ref[qt] + kRescaleSlack)) {
         auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
         bm = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
         auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
         bm = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
-      }
-      bm *= kScaleLog2;
-      // a column with nothing of this block (bm = -inf) keeps its reference;
-      // its scores are -inf and their probabilities come out 0 against any
-      // finite reference (0 while the column has none yet): no branch
-      const bool first = m_ref[qt] == -INFINITY;
-      const bool raise = bm > m_ref[qt] + kRescaleSlack;
-      const float mn = raise ? bm : m_ref[qt];
-      if (__any(raise && !first)) {
-        const float alpha = raise && !first ? __builtin_amdgcn_exp2f(m_ref[qt] - mn) : 1.f;
-        l_sum[qt] *= alpha;
+        bm *= kScaleLog2;
+        // a column with nothing of this block (bm = -inf) keeps its reference;
+        // its scores are -inf and their probabilities come out 0 against any
+        // finite reference (0 while the column has none yet)
+        const bool first = m_ref[qt] == -INFINITY;
+        const bool raise = bm > m_ref[qt] + kRescaleSlack;
+        const float mn = raise ? bm : m_ref[qt];
+        if (__any(raise && !first)) {
+          const float alpha = raise && !first ? __builtin_amdgcn_exp2f(m_ref[qt] - mn) : 1.f;
+          l_sum[qt] *= alpha;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) o[qt][c] *= alpha;
+          for (int c = 0; c < 8; ++c) o[qt][c] *= alpha;
+        }
+        m_ref[qt] = mn;
+        m_sub[qt] = mn == -INFINITY ? 0.f : mn;
       }
-      m_ref[qt] = mn;
-      const float mx = mn == -INFINITY ? 0.f : mn;
+      const float mx = m_sub[qt];
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll

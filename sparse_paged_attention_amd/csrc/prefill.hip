@@ -64,8 +64,20 @@ __global__ void __launch_bounds__(64) pool_kernel(PrefillArgs a) {
   for (int32_t g = 0; g < heads; ++g) {
     const int64_t head = side == 0 ? (int64_t)h * a.G + g : h;
     const uint32_t* rows = src + (head * a.L) * (kHeadDim / 2) + lane;
+    // rows summed in order; the loads of 32 rows go out together
     double u0 = 0.0, u1 = 0.0;
-    for (int64_t t = t0; t < t1; ++t) {
+    int64_t t = t0;
+    for (; t + 32 <= t1; t += 32) {
+      uint32_t w[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) w[i] = rows[(t + i) * (kHeadDim / 2)];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        u0 += bfd(w[i] & 0xFFFFu);
+        u1 += bfd(w[i] >> 16);
+      }
+    }
+    for (; t < t1; ++t) {
       const uint32_t w = rows[t * (kHeadDim / 2)];
       u0 += bfd(w & 0xFFFFu);
       u1 += bfd(w >> 16);

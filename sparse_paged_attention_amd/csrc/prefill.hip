@@ -112,17 +112,32 @@ __device__ __forceinline__ uint32_t order32(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Wave-wide reduction on the VALU (DPP inside each 16-lane row: swap
+// neighbours, pairs, then mirror halves and rows; then the cross-row lane
+// swaps); every lane ends with the result.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_all(uint32_t v, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));   // row_mirror
+  auto x = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op(x[0], x[1]);
+  auto y = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return op(y[0], y[1]);
+}
+
 __device__ __forceinline__ int32_t wave_sum(int32_t v) {
-#pragma unroll
-  for (int o = 32; o; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  return (int32_t)wave_all((uint32_t)v, [](uint32_t p, uint32_t q) { return p + q; });
 }
 
 // One wave per (query block j, dynamic KV head h). Lane l holds the scores of
-// blocks l, l + 64, ... below j (M per lane). The k-th largest order key T is
-// found bit by bit from the top (the largest T with at least k keys >= T);
-// keys above T are kept, and of those equal to T the ones with the lowest
-// block ids. Kept ids go out ascending, then j itself.
+// blocks l, l + 64, ... below j (M slots per lane, the first mv of them in
+// use). The k-th largest order key T is found bit by bit from the top (the
+// largest T with at least k keys >= T), starting below the leading bits that
+// the smallest and the largest key share (T lies between them); keys above T
+// are kept, and of those equal to T the ones with the lowest block ids. Kept
+// ids go out ascending, then j itself.
 template <int M>
 __global__ void __launch_bounds__(64) select_kernel(PrefillArgs a) {
   const int32_t j = blockIdx.x, h = blockIdx.y;
@@ -130,24 +145,41 @@ __global__ void __launch_bounds__(64) select_kernel(PrefillArgs a) {
   const int lane = threadIdx.x;
   int32_t* sel = a.sel + ((int64_t)h * a.nb + j) * a.kb;
   const int32_t k = min(j, a.kb - 1);
+  const int32_t mv = (j + 63) >> 6;
   const double* qp = a.qp + ((int64_t)h * a.nb + j) * kR;
+  const double* kbase = a.kp + (int64_t)h * a.nb * kR;
   double qv[kR];
 #pragma unroll
   for (int r = 0; r < kR; ++r) qv[r] = qp[r];
   const double scale = 0.088388347648318440550;   // 1 / sqrt(128)
   uint32_t key[M];
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int32_t i = lane + 64 * m;
-    key[m] = 0;
-    if (i < j) {
-      const double* kp = a.kp + ((int64_t)h * a.nb + i) * kR;
-      double s = 0.0;
+  for (int m = 0; m < M; ++m) key[m] = 0;
+  // the loads of two slots go out together; a lane past j reads block
+  // j - 1 and drops the result. The dot product is a chain of fused
+  // multiply-adds in fp64
 #pragma unroll
-      for (int r = 0; r < kR; ++r) s = __dadd_rn(s, __dmul_rn(qv[r], kp[r]));
-      const float sc = (float)(s * scale);
-      key[m] = order32(sc);
-      if (a.scores) a.scores[((int64_t)h * a.nb + j) * a.nb + i] = sc;
+  for (int m = 0; m < M; m += 2) {
+    if (m < mv) {
+      double kv[2][kR];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const double* kp = kbase + (int64_t)min(lane + 64 * (m + u), j - 1) * kR;
+#pragma unroll
+        for (int r = 0; r < kR; ++r) kv[u][r] = kp[r];
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int32_t i = lane + 64 * (m + u);
+        double s = 0.0;
+#pragma unroll
+        for (int r = 0; r < kR; ++r) s = __builtin_fma(qv[r], kv[u][r], s);
+        const float sc = (float)(s * scale);
+        if (i < j) {
+          key[m + u] = order32(sc);
+          if (a.scores) a.scores[((int64_t)h * a.nb + j) * a.nb + i] = sc;
+        }
+      }
     }
   }
   if (k == j) {                                   // every earlier block is kept
@@ -156,14 +188,30 @@ __global__ void __launch_bounds__(64) select_kernel(PrefillArgs a) {
     return;
   }
   // the k-th largest key among the j valid ones (order keys of real scores are
-  // never 0, so 0 marks the invalid slots)
-  uint32_t T = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = T | (1u << bit);
-    int32_t c = 0;
+  // never 0, so 0 marks the invalid slots); with k = 0 nothing is kept
+  uint32_t T = 0xFFFFFFFFu;
+  if (k > 0) {
+    uint32_t lo = 0xFFFFFFFFu, hi = 0;
 #pragma unroll
-    for (int m = 0; m < M; ++m) c += key[m] >= cand;
-    if (wave_sum(c) >= k) T = cand;
+    for (int m = 0; m < M; ++m) {
+      lo = key[m] != 0 ? min(lo, key[m]) : lo;
+      hi = max(hi, key[m]);
+    }
+    lo = wave_all(lo, [](uint32_t p, uint32_t q) { return min(p, q); });
+    hi = wave_all(hi, [](uint32_t p, uint32_t q) { return max(p, q); });
+    T = hi;
+    const uint32_t diff = lo ^ hi;
+    if (diff != 0) {
+      const int top = 31 - __builtin_clz(diff);
+      T = hi & ~((2u << top) - 1u);
+      for (int bit = top; bit >= 0; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        int32_t c = 0;
+#pragma unroll
+        for (int m = 0; m < M; ++m) c += key[m] >= cand;     // unused slots hold 0 < cand
+        if (wave_sum(c) >= k) T = cand;
+      }
+    }
   }
   int32_t gt = 0;
 #pragma unroll

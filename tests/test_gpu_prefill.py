@@ -56,12 +56,13 @@ def inputs(pf: W.Prefill):
     return Qb, Kb, Vb, W.prefill_projection(pf, "q"), W.prefill_projection(pf, "k")
 
 
-def check(pf: W.Prefill, rows=None) -> dict:
+def check(pf: W.Prefill, rows=None, data=None) -> dict:
     """Runs the prefill on the GPU and checks it against the oracle (every row,
-    or the query positions `rows` of every head). Returns a small report."""
+    or the query positions `rows` of every head), on the workload's seeded
+    inputs or on `data` = (Q, K, V, W_q, W_k) bits. Returns a small report."""
     log(f"[prefill] {pf.name} L={pf.L} hq={pf.hq} hkv={pf.hkv} kind={pf.kind} budget={pf.budget} "
         f"dense_below={pf.dense_below} rows={'all' if rows is None else len(rows)}")
-    Qb, Kb, Vb, Wq, Wk = inputs(pf)
+    Qb, Kb, Vb, Wq, Wk = inputs(pf) if data is None else data
     out, lse, gsel, gcnt, gscores = run_gpu(pf, Qb, Kb, Vb, Wq, Wk)
     G, b = pf.G, pf.block
     dense = pf.L < pf.dense_below
@@ -142,6 +143,19 @@ def test_group_sizes(hq, hkv):
 @pytest.mark.parametrize("L", [1, 63, 64, 65, 129])
 def test_short_sequences(L):
     check(SMALL.scaled(name=f"prefill_L{L}", L=L, dense_below=1, budget=64))
+
+
+def test_equal_block_scores_keep_the_lowest_ids():
+    """Every key row the same, so every earlier block of a row scores the same
+    on both sides: each query block keeps the lowest kb - 1 earlier ids and
+    itself, id for id (no near-tie allowance is used). On the GPU the smallest
+    and the largest key of each row are then equal, so the threshold search
+    has no bit to decide."""
+    pf = SMALL.scaled(name="prefill_equal_scores", L=64 * 20 + 7, budget=256, dense_below=1)
+    Qb, Kb, Vb, Wq, Wk = inputs(pf)
+    Kb = np.repeat(Kb[:, :1], pf.L, axis=1)
+    rep = check(pf, data=(Qb, Kb, Vb, Wq, Wk))
+    assert rep["sel_rows"] > 0 and rep["ties"] == 0
 
 
 def test_budget_covering_the_sequence():

@@ -241,11 +241,14 @@ __global__ void __launch_bounds__(64) select_kernel(PrefillArgs a) {
 // 2 * NH waves, wave w handles query head g0 + w / 2, rows 32 (w % 2) .. +32 of
 // the block as two 16-row column tiles of the MFMAs. Per key block, every
 // thread stages part of K (row-major, rows padded to 272 bytes) and of V^T
-// (channel-major, rows padded to 136 bytes) into one of four LDS block
-// buffers. Key blocks go in pairs: the next pair's global loads are in flight
+// (channel-major, rows padded to 144 bytes) into one of four LDS block
+// buffers. In a V^T row the keys of each 32-key half of the block are
+// interleaved in groups of four: keys 4q .. 4q + 3 and 16 + 4q .. 19 + 4q
+// (q = 0 .. 3) sit side by side, the eight keys one lane of the P V MFMAs
+// takes, so it reads them as one 16-byte piece. Key blocks go in pairs: the next pair's global loads are in flight
 // while the current pair is computed, one barrier per pair.
 constexpr int kKStride = 136;              // bf16 per K row in LDS
-constexpr int kVStride = 68;               // bf16 per V^T row in LDS (136 B: 16 rows read as 8-byte pieces fall on distinct banks)
+constexpr int kVStride = 72;               // bf16 per V^T row in LDS (144 B: 16-byte aligned; 16 rows read as 16-byte pieces fall on distinct banks)
 constexpr int kKBytes = kB * kKStride * 2;
 constexpr int kVBytes = kHeadDim * kVStride * 2;
 constexpr int kBufBytes = kKBytes + kVBytes;
@@ -378,12 +381,14 @@ __global__ void __launch_bounds__(NH * 128) attn_kernel(PrefillArgs a) {
       hi.y = __builtin_amdgcn_perm(v[3], v[2], 0x07060302u);
       hi.z = __builtin_amdgcn_perm(v[5], v[4], 0x07060302u);
       hi.w = __builtin_amdgcn_perm(v[7], v[6], 0x07060302u);
-      uint2* d0 = reinterpret_cast<uint2*>(vl + ((2 * cp) * kVStride + 8 * kg) * 2);      // 8-byte aligned rows
-      uint2* d1 = reinterpret_cast<uint2*>(vl + ((2 * cp + 1) * kVStride + 8 * kg) * 2);
-      d0[0] = uint2{lo.x, lo.y};
-      d0[1] = uint2{lo.z, lo.w};
-      d1[0] = uint2{hi.x, hi.y};
-      d1[1] = uint2{hi.z, hi.w};
+      // keys 8kg .. 8kg + 3 and 8kg + 4 .. 8kg + 7 in the interleaved order
+      const int c0 = 32 * (kg / 4) + 16 * (kg % 2) + 4 * ((kg % 4) / 2);
+      uint8_t* r0 = vl + (2 * cp) * kVStride * 2;
+      uint8_t* r1 = vl + (2 * cp + 1) * kVStride * 2;
+      *reinterpret_cast<uint2*>(r0 + c0 * 2) = uint2{lo.x, lo.y};
+      *reinterpret_cast<uint2*>(r0 + (c0 + 8) * 2) = uint2{lo.z, lo.w};
+      *reinterpret_cast<uint2*>(r1 + c0 * 2) = uint2{hi.x, hi.y};
+      *reinterpret_cast<uint2*>(r1 + (c0 + 8) * 2) = uint2{hi.z, hi.w};
     }
   };
 
@@ -500,10 +505,8 @@ __global__ void __launch_bounds__(NH * 128) attn_kernel(PrefillArgs a) {
       }
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const uint8_t* vrow = vl + ((16 * c + col) * kVStride) * 2;
-        const uint2 va = *reinterpret_cast<const uint2*>(vrow + (32 * pr + 4 * quad) * 2);
-        const uint2 vb = *reinterpret_cast<const uint2*>(vrow + (32 * pr + 16 + 4 * quad) * 2);
-        const uint4 vv = {va.x, va.y, vb.x, vb.y};
+        // keys 32pr + 4quad .. +3, then 32pr + 16 + 4quad .. +3 (the interleaved order)
+        const uint4 vv = *reinterpret_cast<const uint4*>(vl + ((16 * c + col) * kVStride + 32 * pr + 8 * quad) * 2);
         bf16x8 av;
         __builtin_memcpy(&av, &vv, 16);
 #pragma unroll

@@ -245,8 +245,9 @@ __global__ void __launch_bounds__(64) select_kernel(PrefillArgs a) {
 // buffers. In a V^T row the keys of each 32-key half of the block are
 // interleaved in groups of four: keys 4q .. 4q + 3 and 16 + 4q .. 19 + 4q
 // (q = 0 .. 3) sit side by side, the eight keys one lane of the P V MFMAs
-// takes, so it reads them as one 16-byte piece. Key blocks go in pairs: the next pair's global loads are in flight
-// while the current pair is computed, one barrier per pair.
+// takes, so it reads them as one 16-byte piece. Key blocks go in pairs: the
+// next pair's global loads are in flight while the current pair is computed,
+// one barrier per pair.
 constexpr int kKStride = 136;              // bf16 per K row in LDS
 constexpr int kVStride = 72;               // bf16 per V^T row in LDS (144 B: 16-byte aligned; 16 rows read as 16-byte pieces fall on distinct banks)
 constexpr int kKBytes = kB * kKStride * 2;
